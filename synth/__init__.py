@@ -1,0 +1,206 @@
+"""Seeded synthetic inputs for the quantized matmul.
+
+Shared by the tests, the bench and the smoke check; imported by neither the
+HIP library nor the oracle.  It holds none of the method's arithmetic: only
+random code words (any bit string is a valid tail-biting trellis walk),
+random sign bits, N(0,1) values rounded to fp16, the textbook Lloyd-Max
+levels for N(0,1) (data, not computed here), random group scales, and the
+layer shapes of the workloads.
+
+Every array is a numpy array; fp16 values are carried as uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import hashlib
+from dataclasses import dataclass, field, replace
+from typing import List, Optional
+
+import numpy as np
+
+HYB, MAD1, INST3, NUQ, VQ = 1, 2, 3, 4, 5
+CODE_NAMES = {HYB: "HYB", MAD1: "1MAD", INST3: "3INST", NUQ: "NUQ", VQ: "VQ"}
+
+# Optimal 8-level quantizer for a unit Gaussian (J. Max, "Quantizing for
+# minimum distortion", IRE Trans. IT-6, 1960, the N = 8 Gaussian row):
+# output levels +/-0.2451, 0.7560, 1.344, 2.152.  Stored as data.
+LLOYD_MAX_8 = (-2.152, -1.344, -0.7560, -0.2451, 0.2451, 0.7560, 1.344, 2.152)
+
+
+def rng_for(*tags) -> np.random.Generator:
+    """A numpy Generator seeded by a hash of the tags (stable across runs)."""
+    h = hashlib.sha256("/".join(str(t) for t in tags).encode()).digest()
+    return np.random.default_rng(int.from_bytes(h[:8], "little"))
+
+
+def f16_bits(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64).astype(np.float16)).view(np.uint16)
+
+
+def normal_f16(rng: np.random.Generator, shape) -> np.ndarray:
+    return f16_bits(rng.standard_normal(shape))
+
+
+def random_words(rng: np.random.Generator, count: int) -> np.ndarray:
+    return rng.integers(0, 1 << 32, size=count, dtype=np.uint64).astype(np.uint32)
+
+
+def sign_words(rng: np.random.Generator, nbits: int) -> np.ndarray:
+    return random_words(rng, (nbits + 31) // 32)
+
+
+def largest_pow2_divisor(x: int) -> int:
+    return x & -x
+
+
+@dataclass
+class HostLayer:
+    """Host copy of one quantized linear layer (W_hat is m out x n in)."""
+    code: int
+    L: int
+    k: int
+    V: int
+    Q: int
+    m: int
+    n: int
+    codes: np.ndarray                   # uint32, m*n*k/32 words
+    lut: Optional[np.ndarray] = None    # uint32 table
+    gscale: Optional[np.ndarray] = None  # uint16 fp16 [m][n/group]
+    group: int = 0
+    scale: float = 1.0
+    sign_in: Optional[np.ndarray] = None
+    sign_out: Optional[np.ndarray] = None
+    had_in: int = 1
+    had_out: int = 1
+    name: str = ""
+
+    @property
+    def n_tiles(self) -> int:
+        return (self.m // 16) * (self.n // 16)
+
+    @property
+    def code_bytes(self) -> int:
+        return self.codes.size * 4
+
+    @property
+    def side_bytes(self) -> int:
+        b = 0
+        for a in (self.lut, self.gscale, self.sign_in, self.sign_out):
+            if a is not None:
+                b += a.nbytes
+        return b
+
+
+def make_layer(code: int, m: int, n: int, k: int, *, tag: str, V: Optional[int] = None,
+               Q: int = 9, scale: float = 0.02, signs: bool = True,
+               had_in: Optional[int] = None, had_out: Optional[int] = None,
+               group: int = 128, codes: Optional[np.ndarray] = None) -> HostLayer:
+    """A seeded random layer.  Trellis codes use L = 16; NUQ uses L = k, V = 1;
+    VQ uses L = 2k, V = 2 (one index per weight pair)."""
+    if code == HYB:
+        V = 2 if V is None else V
+        L = 16
+    elif code in (MAD1, INST3):
+        V = 1
+        L = 16
+    elif code == NUQ:
+        V, L = 1, k
+    elif code == VQ:
+        V, L = 2, 2 * k
+    else:
+        raise ValueError("unknown code %r" % code)
+    nwords = m * n * k // 32
+    if codes is None:
+        codes = random_words(rng_for(tag, "codes"), nwords)
+    assert codes.size == nwords
+    lut = gscale = None
+    grp = 0
+    if code == HYB:
+        lut = normal_f16(rng_for(tag, "lut"), (1 << Q) * 2).view(np.uint32).copy()
+    elif code == NUQ:
+        if k != 3:
+            raise ValueError("the textbook table here is the 8-level one (k = 3)")
+        lv = f16_bits(np.array(LLOYD_MAX_8)).astype(np.uint32)
+        lut = lv
+        grp = group
+        gscale = f16_bits(rng_for(tag, "gscale").uniform(0.01, 0.03, size=(m, n // group)))
+        scale = 1.0
+    elif code == VQ:
+        lut = normal_f16(rng_for(tag, "lut"), (1 << L) * 2).view(np.uint32).copy()
+    si = sign_words(rng_for(tag, "sign_in"), n) if signs else None
+    so = sign_words(rng_for(tag, "sign_out"), m) if signs else None
+    return HostLayer(code=code, L=L, k=k, V=V, Q=Q if code == HYB else 0, m=m, n=n,
+                     codes=codes, lut=lut, gscale=gscale, group=grp, scale=float(scale),
+                     sign_in=si, sign_out=so,
+                     had_in=largest_pow2_divisor(n) if had_in is None else had_in,
+                     had_out=largest_pow2_divisor(m) if had_out is None else had_out,
+                     name=tag)
+
+
+def activations(tag: str, b: int, n: int) -> np.ndarray:
+    """x ~ N(0,1) rounded to fp16, b x n bit patterns."""
+    return normal_f16(rng_for(tag, "x"), (b, n))
+
+
+# ---------------------------------------------------------------------------
+# Workloads: layer shapes and code settings of the five configurations.
+
+@dataclass
+class LayerSpec:
+    name: str
+    code: int
+    m: int
+    n: int
+    k: int
+    scale: float = 0.02
+    had_in: Optional[int] = None
+    had_out: Optional[int] = None
+
+    def build(self, tag: str) -> HostLayer:
+        return make_layer(self.code, self.m, self.n, self.k, tag=tag + "/" + self.name,
+                          scale=self.scale, had_in=self.had_in, had_out=self.had_out)
+
+
+@dataclass
+class Workload:
+    name: str
+    layers: List[LayerSpec]
+    batches: List[int]
+    description: str = ""
+
+    @property
+    def code_bytes(self) -> int:
+        return sum(s.m * s.n * s.k // 8 for s in self.layers)
+
+
+WORKLOADS = {
+    # 4096x4096, HYB k=2 V=2 Q=9, scale 0.02, RHT 4096 both sides, batch 1
+    "hyb4096": Workload("hyb4096", [LayerSpec("w", HYB, 4096, 4096, 2)], [1],
+                        "single 4096x4096 linear, 2-bit HYB trellis"),
+    # 4096x4096 with computed codes, k in {2,3,4}, V = 1, batch 1
+    "computed4096": Workload(
+        "computed4096",
+        [LayerSpec("%s_k%d" % (CODE_NAMES[c], k), c, 4096, 4096, k)
+         for c in (MAD1, INST3) for k in (2, 3, 4)],
+        [1], "4096x4096 with 1MAD and 3INST codes, k = 2, 3, 4"),
+    # Llama-3-8B-shaped decoder layer, HYB k=2, batch 1 and 8
+    "llama3_8b_layer": Workload(
+        "llama3_8b_layer",
+        [LayerSpec("q", HYB, 4096, 4096, 2), LayerSpec("k", HYB, 1024, 4096, 2),
+         LayerSpec("v", HYB, 1024, 4096, 2), LayerSpec("o", HYB, 4096, 4096, 2),
+         LayerSpec("gate", HYB, 14336, 4096, 2), LayerSpec("up", HYB, 14336, 4096, 2),
+         LayerSpec("down", HYB, 4096, 14336, 2)],
+        [1, 8], "Llama-3-8B-shaped decoder layer, 7 linears, HYB k=2"),
+    # scalar / vector LUT variants on the down-projection shape, batch 1
+    "down_nuq": Workload("down_nuq", [LayerSpec("down_nuq", NUQ, 4096, 14336, 3, scale=1.0)],
+                         [1], "4096x14336 NUQ 3-bit, fp16 scale per 128 weights"),
+    "down_vq": Workload("down_vq", [LayerSpec("down_vq", VQ, 4096, 14336, 4)],
+                        [1], "4096x14336 2-D VQ, 8-bit index per weight pair"),
+    # batched prefill on a 70B-class up-projection, HYB k=3, batch 64
+    "up70b_prefill": Workload(
+        "up70b_prefill", [LayerSpec("up", HYB, 28672, 8192, 3, had_in=8192, had_out=4096)],
+        [64], "28672x8192 HYB k=3, X 64x8192"),
+}
+
+
+def with_codes(layer: HostLayer, codes: np.ndarray) -> HostLayer:
+    return replace(layer, codes=codes)

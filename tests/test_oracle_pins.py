@@ -1,0 +1,459 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: the worked
+example printed on the pages, brute force on tiny trellises, closed forms,
+library routines (numpy's binary16 conversion, numpy matrix products,
+np.kron), invariants (H H^T = B I, Parseval, exact LUT coverage) and
+statistical properties the pages state for the computed codes.
+"""
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split("=", 1)
+            vals[k] = v
+    return vals
+
+
+def _bits(s):
+    return np.array([int(c) for c in s], dtype=np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# Bitshift trellis walk
+
+def test_worked_example_linear():
+    g = _read_golden("bitshift_trellis_example.txt")
+    L, kV = int(g["L"]), int(g["kV"])
+    want = [int(v) for v in g["states"].split(",")]
+    got = oracle.walk_bits(_bits(g["bits"]), L, kV, len(want), tailbiting=False)
+    assert list(got) == want
+
+
+def test_worked_example_tailbiting():
+    g = _read_golden("bitshift_trellis_example.txt")
+    L, kV = int(g["L"]), int(g["kV"])
+    want = [int(v) for v in g["tailbiting_states"].split(",")]
+    got = oracle.walk_bits(_bits(g["tailbiting_bits"]), L, kV, len(want), tailbiting=True)
+    assert list(got) == want
+
+
+def test_short_linear_stream_rejected():
+    with pytest.raises(ValueError):
+        oracle.walk_bits(_bits("001011"), 2, 1, 6, tailbiting=False)
+
+
+@pytest.mark.parametrize("L,kV,steps", [(4, 2, 4), (3, 1, 6), (4, 1, 8), (6, 3, 4)])
+def test_bijection_onto_cyclic_walks(L, kV, steps):
+    """Tail-biting: the map from the steps*kV-bit stream to state sequences
+    is a bijection onto the cyclic walks of the bitshift trellis (every state
+    shares its low L-kV bits with the high L-kV bits of the next, wrapping)."""
+    nbits = steps * kV
+    mask = (1 << (L - kV)) - 1
+    seen = set()
+    for v in range(1 << nbits):
+        bits = [(v >> (nbits - 1 - i)) & 1 for i in range(nbits)]
+        st = tuple(int(s) for s in oracle.walk_bits(np.array(bits, np.uint8), L, kV, steps, True))
+        for t in range(steps):
+            a, b = st[t], st[(t + 1) % steps]
+            assert (a & mask) == (b >> kV), (bits, st)
+        seen.add(st)
+    assert len(seen) == 1 << nbits  # injective
+    # brute force over all state sequences: the valid cyclic walks number
+    # exactly 2^nbits when L <= nbits (each step adds kV free bits)
+    if (1 << L) ** steps <= 1 << 20:
+        valid = 0
+        for st in itertools.product(range(1 << L), repeat=steps):
+            if all((st[t] & mask) == (st[(t + 1) % steps] >> kV) for t in range(steps)):
+                valid += 1
+                assert st in seen
+        assert valid == len(seen)
+
+
+@pytest.mark.parametrize("L,kV", [(16, 2), (16, 3), (16, 4), (16, 6), (12, 5), (16, 1)])
+def test_serial_walk_equals_random_access_window(L, kV):
+    rng = np.random.default_rng(L * 100 + kV)
+    steps = 64
+    nbits = steps * kV
+    bits = rng.integers(0, 2, size=nbits, dtype=np.uint8)
+    serial = oracle.walk_bits(bits, L, kV, steps, True)
+    for t in range(steps):
+        assert serial[t] == oracle.window_state(bits, L, kV, t)
+    # and a window by numpy's own bit handling: concatenate, slice, pack
+    ext = np.concatenate([bits, bits])
+    for t in range(0, steps, 7):
+        w = ext[t * kV:t * kV + L]
+        assert serial[t] == int("".join(str(int(b)) for b in w), 2)
+
+
+@pytest.mark.parametrize("kV", [3, 8])
+def test_L_equals_kV_is_plain_fields(kV):
+    """L = kV: the trellis becomes plain kV-bit VQ (no overlap), so state t is
+    field t of the stream ("Ablations and fast inference")."""
+    rng = np.random.default_rng(kV)
+    words = rng.integers(0, 1 << 32, size=24, dtype=np.uint64).astype(np.uint32)
+    bits = np.unpackbits(words.astype(">u4").view(np.uint8))  # MSB-first per word
+    steps = bits.size // kV
+    st = oracle.walk_bits(bits, kV, kV, steps, True)
+    fields = bits[:steps * kV].reshape(steps, kV)
+    want = fields.dot(1 << np.arange(kV - 1, -1, -1))
+    assert np.array_equal(st, want)
+
+
+# ---------------------------------------------------------------------------
+# fp16 rounding (own implementation) vs numpy's IEEE binary16 conversion
+
+def test_f16_rounding_matches_numpy():
+    rng = np.random.default_rng(0)
+    vals = [0.0, -0.0, 1.0, 65504.0, 65519.99, 65520.0, 1e9, -1e9, 5.96e-8, 2.98e-8,
+            2.9802322387695312e-08, 8.940696716308594e-08, 6.097555160522461e-05,
+            6.103515625e-05, float("inf"), -float("inf")]
+    # exact halfway points between neighbouring fp16 values, across binades
+    h = np.arange(0, 0x7BFF, 37, dtype=np.uint16)
+    a = h.view(np.float16).astype(np.float64)
+    b = (h + 1).view(np.float16).astype(np.float64)
+    mids = (a + b) / 2
+    x = np.concatenate([np.array(vals), mids, -mids, rng.standard_normal(3000) * 10,
+                        rng.standard_normal(2000) * 1e-5,
+                        np.exp(rng.uniform(-20, 12, 2000))])
+    got = oracle.f16_from_double(x)
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want)
+    back = oracle.f16_to_double(np.arange(0, 0x7C00, 13, dtype=np.uint16))
+    assert np.array_equal(back, np.arange(0, 0x7C00, 13, dtype=np.uint16).view(np.float16).astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
+# HYB code
+
+def test_hyb_covers_signed_codebook_uniformly():
+    """Over all 2^16 states the HYB decode yields only +/- LUT pairs, the sign
+    flips both halves, and each of the 2^(Q+1) = 1024 signed entries appears
+    exactly 64 times (the LUT of 512 words expands to 1024 entries at V = 2;
+    untitled ALU-op comment and "Bit Accounting (Q2)")."""
+    g = _read_golden("bit_accounting.txt")
+    Q = int(g["hyb_Q"])
+    lut = synth.normal_f16(synth.rng_for("pin", "hyb"), (1 << Q) * 2).view(np.uint32)
+    assert lut.size == int(g["hyb_lut_words"])
+    vals = oracle.state_values_all(oracle.HYB, 16, Q, lut)
+    words = vals[:, 0].astype(np.uint32) | (vals[:, 1].astype(np.uint32) << 16)
+    pos = {int(w): i for i, w in enumerate(lut)}
+    neg = {int(w) ^ 0x80008000: i for i, w in enumerate(lut)}
+    counts = {}
+    for w in words:
+        w = int(w)
+        key = ("+", pos[w]) if w in pos else ("-", neg[w])
+        counts[key] = counts.get(key, 0) + 1
+    assert len(counts) == int(g["hyb_signed_entries"])
+    assert set(counts.values()) == {64}
+    # codebook size from the bit accounting: 2^Q x V x 16 bits
+    assert (1 << Q) * int(g["hyb_V"]) * 16 // 8 == int(g["hyb_codebook_bytes"]) == lut.nbytes
+
+
+# ---------------------------------------------------------------------------
+# Computed codes: statistics the pages state (approximately Gaussian for
+# L >= 10, neighbouring trellis states not strongly correlated), and the
+# FP8-cast negative control of the computed-codes reply.
+
+def _neighbour_pairs(v, L, kV):
+    s = np.arange(1 << L, dtype=np.int64)
+    nxt = ((s[:, None] << kV) | np.arange(1 << kV)[None, :]) & ((1 << L) - 1)
+    return np.repeat(v, 1 << kV), v[nxt.ravel()]
+
+
+def _coverage(a, b, bins=12):
+    qa = np.quantile(a, np.linspace(0, 1, bins + 1)[1:-1])
+    qb = np.quantile(b, np.linspace(0, 1, bins + 1)[1:-1])
+    ia, ib = np.searchsorted(qa, a), np.searchsorted(qb, b)
+    occ = np.zeros((bins, bins), bool)
+    occ[ia, ib] = True
+    return occ.mean()
+
+
+@pytest.fixture(scope="module")
+def computed_values():
+    out = {}
+    for code in (oracle.MAD1, oracle.INST3):
+        h = oracle.state_values_all(code, 16)[:, 0]
+        out[code] = h.view(np.float16).astype(np.float64)
+    return out
+
+
+@pytest.mark.parametrize("code", [oracle.MAD1, oracle.INST3])
+def test_computed_code_near_gaussian(code, computed_values):
+    v = computed_values[code]
+    assert np.all(np.isfinite(v))
+    z = (v - v.mean()) / v.std()
+    assert abs(v.mean()) < 0.02 * v.std()
+    assert 2.5 < (z ** 4).mean() < 3.3        # kurtosis near 3
+    assert abs((z ** 3).mean()) < 0.05         # symmetric
+    assert len(np.unique(v)) > 200             # many distinct values
+
+
+@pytest.mark.parametrize("code", [oracle.MAD1, oracle.INST3])
+@pytest.mark.parametrize("kV", [1, 2, 3, 4])
+def test_computed_code_neighbours_decorrelated(code, kV, computed_values):
+    v = computed_values[code]
+    a, b = _neighbour_pairs(v, 16, kV)
+    rho = np.corrcoef(a, b)[0, 1]
+    assert abs(rho) < 0.01
+    assert _coverage(a, b) > 0.97
+
+
+def _predictability(v, L, kV, classes=4):
+    """Mean over states of the largest fraction of its 2^kV successors that
+    fall in one value class (classes = quantiles of v).  Near the i.i.d.
+    random-codebook value when the state does not predict its successor."""
+    q = np.quantile(v, np.linspace(0, 1, classes + 1)[1:-1])
+    cls = np.searchsorted(q, v, side="right")
+    s = np.arange(1 << L, dtype=np.int64)
+    nxt = ((s[:, None] << kV) | np.arange(1 << kV)[None, :]) & ((1 << L) - 1)
+    c = cls[nxt]
+    frac = np.stack([(c == i).mean(1) for i in range(classes)], 1)
+    return frac.max(1).mean()
+
+
+def _random_codebook_predictability(L, kV, seed=0):
+    v = np.random.default_rng(seed).standard_normal(1 << L)
+    return _predictability(v, L, kV)
+
+
+@pytest.mark.parametrize("code", [oracle.MAD1, oracle.INST3])
+@pytest.mark.parametrize("kV", [1, 2, 3, 4])
+def test_computed_code_successors_unpredictable(code, kV, computed_values):
+    """A one-multiply-add LCG code keeps a little of the shift structure of
+    the bitshift trellis (the successor's LCG output is about 2^kV times the
+    current one plus a d-dependent offset); an LCG with a full 32-bit
+    multiplier shows an excess of about 0.04 on this statistic.  Require the
+    excess over an i.i.d. Gaussian codebook to stay below 0.06."""
+    got = _predictability(computed_values[code], 16, kV)
+    ref = _random_codebook_predictability(16, kV)
+    assert got - ref < 0.06, (got, ref)
+
+
+def test_fp8_cast_negative_control():
+    """The direct FP8 (e5m2) cast of the state, the counter-example in the
+    computed-codes reply (L = 8, K = 4): the mantissa bits of a state become
+    sign and exponent bits of the next, so the successor's value class is
+    largely fixed by the state -- the same statistic must flag it."""
+    L, K = 8, 4
+    s = np.arange(1 << L)
+    # e5m2 is the upper byte of a binary16 pattern; drop the inf/nan states
+    v = (s.astype(np.uint16) << 8).view(np.float16).astype(np.float64)
+    v = np.where(np.isfinite(v), v, 0.0)
+    got = _predictability(v, L, K)
+    ref = _random_codebook_predictability(L, K)
+    assert got > ref + 0.25, (got, ref)
+
+
+def test_1mad_values_are_scaled_integers(computed_values):
+    """1MAD values are (integer in [-510, 510]) / sqrt(21845) up to fp16
+    rounding: a sum of four bytes, centred."""
+    v = computed_values[oracle.MAD1]
+    scaled = v * np.sqrt(21845.0)
+    assert np.all(np.abs(scaled) <= 510 * (1 + 2 ** -10))
+    assert np.all(np.abs(scaled - np.round(scaled)) <= np.abs(scaled) * 2 ** -10 + 1e-9)
+    assert abs(v.std() - 1.0) < 0.02           # unit variance by construction
+
+
+# ---------------------------------------------------------------------------
+# Hadamard
+
+@pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32, 64])
+def test_hadamard_orthogonal(B):
+    H = np.array([[oracle.hadamard_entry(i, j) for j in range(B)] for i in range(B)])
+    assert np.array_equal(H @ H.T, B * np.eye(B, dtype=np.int64))
+
+
+def test_hadamard_kronecker():
+    H = np.array([[1]])
+    for _ in range(6):
+        H = np.kron(np.array([[1, 1], [1, -1]]), H)
+    B = H.shape[0]
+    Ho = np.array([[oracle.hadamard_entry(i, j) for j in range(B)] for i in range(B)])
+    assert np.array_equal(H, Ho)
+
+
+def _kron_h(B):
+    H = np.array([[1.0]])
+    while H.shape[0] < B:
+        H = np.kron(np.array([[1.0, 1.0], [1.0, -1.0]]), H)
+    return H
+
+
+def _signs_pm(words, n):
+    if words is None:
+        return np.ones(n)
+    bits = (words[np.arange(n) >> 5] >> (np.arange(n) & 31).astype(np.uint32)) & 1
+    return np.where(bits == 1, -1.0, 1.0)
+
+
+@pytest.mark.parametrize("B,n", [(16, 64), (64, 192), (256, 256)])
+def test_rht_against_kron_matrix(B, n):
+    rng = np.random.default_rng(B + n)
+    x = rng.standard_normal((3, n))
+    sw = synth.sign_words(rng, n)
+    s = _signs_pm(sw, n)
+    H = _kron_h(B) / np.sqrt(B)
+    want0 = np.concatenate([(H @ (s[b:b + B, None] * x.T[b:b + B])) for b in range(0, n, B)]).T
+    got0 = oracle.rht(x, B, sw, mode=0)
+    assert np.allclose(got0, want0, atol=1e-12)
+    want1 = np.concatenate([s[b:b + B, None] * (H @ x.T[b:b + B]) for b in range(0, n, B)]).T
+    got1 = oracle.rht(x, B, sw, mode=1, scale=1.0)
+    assert np.allclose(got1, want1, atol=1e-12)
+    # Parseval and round trip (input transform undone by the output transform)
+    assert np.allclose((got0 ** 2).sum(1), (x ** 2).sum(1))
+    back = oracle.rht(got0, B, sw, mode=1)
+    assert np.allclose(back, x, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Layer geometry and sizes
+
+def test_tile_index_panel_order():
+    n = 16 * 5
+    seen = set()
+    for R in range(16):
+        for C in range(5):
+            i = oracle.tile_index(n, R, C)
+            assert oracle.tile_coords(n, i) == (R, C)
+            seen.add(i)
+    assert seen == set(range(16 * 5))
+    # the 8 tiles of one panel column sit next to each other
+    assert [oracle.tile_index(n, r, 3) for r in range(8, 16)] == list(range(5 * 8 + 24, 5 * 8 + 32))
+
+
+def test_bits_per_weight_and_side_info():
+    g = _read_golden("bit_accounting.txt")
+    for wl in synth.WORKLOADS.values():
+        for spec in wl.layers:
+            assert spec.m * spec.n * spec.k % 32 == 0
+    lay = synth.make_layer(synth.HYB, 4096, 4096, 2, tag="acct")
+    assert lay.code_bytes * 8 == 2 * 4096 * 4096           # exactly k bits per weight
+    side_bits = (lay.lut.nbytes * 8) + (4096 + 4096)          # codebook + n+m sign bits
+    assert side_bits / (4096 * 4096) < float(g["max_side_bits_per_weight"])
+
+
+def test_validate_rejects_bad_layers():
+    good = synth.make_layer(synth.HYB, 128, 64, 2, tag="val")
+    assert oracle.validate(good)
+    import dataclasses
+    for bad in [dict(m=100), dict(n=40), dict(k=0), dict(Q=0), dict(V=1),
+                dict(had_in=3), dict(had_out=256), dict(L=12)]:
+        assert not oracle.validate(dataclasses.replace(good, **bad)), bad
+
+
+# ---------------------------------------------------------------------------
+# Lloyd-Max
+
+def test_lloyd_max_textbook():
+    lv, mse = oracle.lloyd_max_gauss(8, 3000)
+    assert np.allclose(lv, synth.LLOYD_MAX_8, atol=6e-4)
+    assert abs(mse - 0.03454) < 5e-5
+    assert np.array_equal(synth.f16_bits(lv), synth.f16_bits(np.array(synth.LLOYD_MAX_8)))
+    lv2, mse2 = oracle.lloyd_max_gauss(2, 200)
+    # two levels: +/- sqrt(2/pi), MSE 1 - 2/pi
+    assert np.allclose(lv2, [-np.sqrt(2 / np.pi), np.sqrt(2 / np.pi)], atol=1e-12)
+    assert abs(mse2 - (1 - 2 / np.pi)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# The forward pass
+
+def _numpy_forward(layer, x16):
+    """Independent evaluation: dense W from tile decodes placed by hand,
+    Kronecker-built Hadamards, numpy matrix products."""
+    m, n = layer.m, layer.n
+    W = np.zeros((m, n))
+    for R in range(m // 16):
+        for C in range(n // 16):
+            t = oracle.decode_tile(layer, R, C).view(np.float16).astype(np.float64)
+            W[R * 16:(R + 1) * 16, C * 16:(C + 1) * 16] = t.reshape(16, 16)
+    W *= float(np.float32(layer.scale))   # the descriptor carries an fp32 scale
+    x = np.atleast_2d(x16).view(np.float16).astype(np.float64)
+    si, so = _signs_pm(layer.sign_in, n), _signs_pm(layer.sign_out, m)
+    Hi = _kron_h(layer.had_in) / np.sqrt(layer.had_in)
+    Ho = _kron_h(layer.had_out) / np.sqrt(layer.had_out)
+    Hin = np.kron(np.eye(n // layer.had_in), Hi)
+    Hout = np.kron(np.eye(m // layer.had_out), Ho)
+    xr = (Hin @ (si[:, None] * x.T))
+    z = W @ xr
+    return (so[:, None] * (Hout @ z)).T
+
+
+@pytest.mark.parametrize("code,k", [(synth.HYB, 2), (synth.MAD1, 3), (synth.INST3, 2),
+                                    (synth.VQ, 4), (synth.HYB, 3)])
+def test_forward_matches_numpy(code, k):
+    lay = synth.make_layer(code, 256, 96, k, tag="fwd%d%d" % (code, k), had_out=64)
+    x = synth.activations("fwdx", 2, 96)
+    got = oracle.forward(lay, x)
+    want = _numpy_forward(lay, x)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+    bi = lay.m // lay.had_out - 1
+    blk = oracle.forward_block(lay, x, [1], bi)
+    assert np.allclose(blk[0], want[1, bi * lay.had_out:(bi + 1) * lay.had_out],
+                       rtol=1e-12, atol=1e-12)
+
+
+def test_forward_nuq_matches_numpy_with_exact_products():
+    lay = synth.make_layer(synth.NUQ, 128, 256, 3, tag="fwdnuq")
+    x = synth.activations("fwdnuqx", 1, 256)
+    got = oracle.forward(lay, x)
+    # NUQ weights are level x group scale exactly; rebuild from the stream bits
+    lvl = np.array(lay.lut, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    gs = lay.gscale.view(np.float16).astype(np.float64)
+    W = np.zeros((128, 256))
+    for R in range(8):
+        for C in range(16):
+            i = oracle.tile_index(256, R, C)
+            words = lay.codes[i * 24:(i + 1) * 24]
+            bits = np.unpackbits(words.astype(">u4").view(np.uint8))
+            idx = bits.reshape(256, 3).dot([4, 2, 1])
+            for j in range(256):
+                r, c = R * 16 + j // 16, C * 16 + j % 16
+                W[r, c] = lvl[idx[j]] * gs[r, c // 128]
+    x64 = x.view(np.float16).astype(np.float64)
+    si, so = _signs_pm(lay.sign_in, 256), _signs_pm(lay.sign_out, 128)
+    xr = (_kron_h(256) / 16.0) @ (si * x64[0])
+    want = so * ((_kron_h(128) / np.sqrt(128)) @ (W @ xr))
+    assert np.allclose(got[0], want, rtol=1e-12, atol=1e-12)
+
+
+def test_forward_closed_form_constant_rows():
+    """A VQ layer whose codebook is (1, 0) everywhere has W[r][c] = scale for
+    even c and 0 for odd c.  With x = e_j the input RHT gives the column j of
+    H/sqrt(B) times s_in[j]; every row of z equals the sum of its even entries;
+    the output RHT of a constant block is sqrt(B) times that value in the
+    block's first row and 0 elsewhere, times the output signs."""
+    m, n, k = 256, 64, 4
+    lay = synth.make_layer(synth.VQ, m, n, k, tag="closed", scale=0.5)
+    lay.lut[:] = np.uint32(0x3C00)              # (1.0, 0.0)
+    j = 5
+    x = np.zeros((1, n), dtype=np.float64)
+    x[0, j] = 1.0
+    x16 = synth.f16_bits(x)
+    y = oracle.forward(lay, x16)[0]
+    si, so = _signs_pm(lay.sign_in, n), _signs_pm(lay.sign_out, m)
+    Bi, Bo = lay.had_in, lay.had_out
+    col = np.array([(-1) ** bin(i & j).count("1") for i in range(Bi)]) / np.sqrt(Bi) * si[j]
+    zval = 0.5 * col[0::2].sum()
+    want = np.zeros(m)
+    for b0 in range(0, m, Bo):
+        want[b0] = np.sqrt(Bo) * zval * so[b0]
+    assert np.allclose(y, want, atol=1e-12)
