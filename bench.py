@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused dequant-GEMV (batch 1) and the MFMA GEMM (batch 64).
+
+Headline (one JSON line on stdout): packed-code HBM GB/s of the fused GEMV
+on the 4096x4096 computed-code layer set -- 1MAD and 3INST, k = 2, 3, 4,
+V = 1, RHT 4096 with random signs, x ~ N(0,1) fp16, batch 1.  One step runs
+one fused GEMV per layer of the set (six launches); consecutive steps use
+different, equally random code buffers from a pool larger than the 256 MiB
+Infinity Cache, so every step reads its codes from HBM.  Inputs are resident
+in HBM before the timed region.  The line also carries:
+  roofline      the dominant kernel's achieved algorithmic bytes per launch
+                over its average launch duration (HIP events on its stream),
+                against the 8 TB/s HBM peak
+  cpu_baseline  the CPU oracle (decode, O(B^2) Hadamard, fp64 matvec) on a
+                bounded sample of the same workload, on the host cores
+  detail        per-variant kernel times, the Llama-3-8B-shaped decoder layer
+                (microseconds per layer at batch 1 and 8) and the batch-64
+                GEMM on the 28672x8192 up-projection (TFLOP/s vs fp16 MFMA peak)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+POOL_MIB = 1152
+METRIC = "fused dequant-GEMV HBM GB/s + µs/layer (b=1); GEMM TFLOP/s (b=64)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--pool-mib", type=int, default=POOL_MIB)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-detail", action="store_true")
+    ap.add_argument("--only", default="", help="restrict the step to one variant, e.g. 3INST_k4")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Launch:
+    """One pre-marshalled C call: avoids per-call Python work in timed loops."""
+
+    def __init__(self, q, fn, layer, x, y, b, ws, stream):
+        import ctypes
+        self.fn = getattr(q._lib, fn)
+        self.args = (ctypes.byref(layer.desc()), x.data_ptr(), y.data_ptr(), b, ws.data_ptr(),
+                     ws.numel(), stream)
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError("launch failed with status %d" % st)
+
+
+def algorithmic_bytes(m, n, k, b, lut_bytes=0, gscale_bytes=0):
+    """Minimal HBM bytes of one call: packed codes, fp16 x and y, the two sign
+    vectors, and the code tables."""
+    return m * n * k // 8 + 2 * b * n + 2 * b * m + (m + n) // 8 + lut_bytes + gscale_bytes
+
+
+def make_pool_layers(q, torch, dev, code, m, n, k, count, tag):
+    """`count` layers sharing signs/LUT but with distinct random codes."""
+    import synth
+    g = torch.Generator(device=dev)
+    g.manual_seed(int.from_bytes(tag.encode()[:8].ljust(8, b"\0"), "little") & 0x7FFFFFFF)
+    words = m * n * k // 32
+    pool = torch.randint(-(1 << 31), (1 << 31) - 1, (count, words), dtype=torch.int32, device=dev,
+                         generator=g)
+    host = synth.make_layer(code, m, n, k, tag=tag, codes=np.zeros(words, dtype=np.uint32))
+    base = q.upload_layer(host, dev)
+    layers = []
+    for i in range(count):
+        layers.append(q.Layer(code=base.code, L=base.L, k=base.k, V=base.V, Q=base.Q, m=m, n=n,
+                              codes=pool[i], lut=base.lut, group_scale=base.group_scale,
+                              group=base.group, layer_scale=base.layer_scale,
+                              sign_in=base.sign_in, sign_out=base.sign_out, had_in=base.had_in,
+                              had_out=base.had_out))
+    return layers, pool, base
+
+
+def time_events(torch, fn, reps):
+    """Average device time of fn() over reps launches, one event pair each."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3  # us
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU; this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import dequant_matmul_packed_amd as q
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    # ---- the headline workload: 4096x4096 computed codes, b = 1 -----------
+    wl = synth.WORKLOADS["computed4096"]
+    specs = [s for s in wl.layers if not args.only or s.name == args.only]
+    step_bytes = sum(s.m * s.n * s.k // 8 for s in specs)
+    P = max(2, int(args.pool_mib * 2 ** 20 // step_bytes))
+    log("workload %s: %d layers per step, %.1f MiB codes per step, pool of %d steps"
+        % (wl.name, len(specs), step_bytes / 2 ** 20, P))
+    x16 = synth.activations(wl.name + "/x", 1, 4096)
+    x = torch.from_numpy(x16.view(np.int16)).to(dev)
+    variants = []
+    keep = []
+    for s in specs:
+        layers, pool, base = make_pool_layers(q, torch, dev, s.code, s.m, s.n, s.k, P, wl.name + "/" + s.name)
+        keep.append(pool)
+        ws = q.workspace(base, 1, q.QDEC_OP_GEMV, dev)
+        y = torch.empty((1, s.m), dtype=torch.float16, device=dev)
+        launches = [Launch(q, "qdec_gemv", L, x, y, 1, ws, stream) for L in layers]
+        variants.append(dict(spec=s, launches=launches, y=y, ws=ws,
+                             bytes=algorithmic_bytes(s.m, s.n, s.k, 1)))
+    torch.cuda.synchronize()
+
+    def step(i):
+        for v in variants:
+            v["launches"][i % P]()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # dominant kernel: the variant with the longest average launch
+    per_variant = {}
+    for v in variants:
+        cnt = [0]
+
+        def one(v=v, cnt=cnt):
+            v["launches"][cnt[0] % P]()
+            cnt[0] += 1
+        per_variant[v["spec"].name] = time_events(torch, one, 50)
+    dom = max(variants, key=lambda v: per_variant[v["spec"].name])
+    log("per-variant kernel us:", {k: round(t, 2) for k, t in per_variant.items()})
+
+    # ---- timed region: exactly `steps` steps ---------------------------------
+    dom_events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for v in variants:
+            if v is dom:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                v["launches"][(i + args.warmup) % P]()
+                b.record()
+                dom_events.append((a, b))
+            else:
+                v["launches"][(i + args.warmup) % P]()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    gbs = step_bytes * args.steps / elapsed / 1e9
+    dom_us = sum(a.elapsed_time(b) for a, b in dom_events) / len(dom_events) * 1e3
+    dom_gbs = dom["bytes"] / (dom_us * 1e-6) / 1e9
+    log("timed %d steps in %.3f s: %.1f GB/s packed, %.2f us/layer; dominant %s %.2f us"
+        % (args.steps, elapsed, gbs, ms_per_step * 1e3 / len(variants), dom["spec"].name, dom_us))
+
+    # sanity: outputs are finite
+    for v in variants:
+        if not torch.isfinite(v["y"].float()).all():
+            raise RuntimeError("non-finite output in %s" % v["spec"].name)
+
+    detail = {"per_variant_kernel_us": {k: round(t, 3) for k, t in per_variant.items()},
+              "us_per_layer": round(ms_per_step * 1e3 / len(variants), 3),
+              "pool_steps": P}
+    if not args.no_detail and not args.only:
+        detail.update(bench_llama_layer(q, torch, dev, stream))
+        detail.update(bench_gemm(q, torch, dev, stream))
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(specs, x16)
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 (codes k=2,3,4 bit; fp32 accumulate)",
+        "data": "synthetic: seeded random code words, N(0,1) fp16 activations, random signs",
+        "config": {"workload": "4096x4096 linear, 1MAD and 3INST computed codes, k=2,3,4, V=1, "
+                               "RHT 4096/4096, batch 1 (six fused GEMVs per step)",
+                   "global_batch": 1, "layers_per_step": len(variants),
+                   "packed_bytes_per_step": step_bytes, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<%s, k=%d, b=1>"
+                     % (synth.CODE_NAMES[dom["spec"].code], dom["spec"].k),
+                     "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": dom["bytes"], "avg_launch_us": round(dom_us, 3)},
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_llama_layer(q, torch, dev, stream):
+    """Llama-3-8B-shaped decoder layer (7 fused GEMVs), microseconds per
+    layer at batch 1 and 8, rotating through distinct layer instances."""
+    import synth
+    wl = synth.WORKLOADS["llama3_8b_layer"]
+    layer_bytes = wl.code_bytes
+    P = max(2, int(1200 * 2 ** 20 // layer_bytes))
+    out = {}
+    pools = []
+    for b in wl.batches:
+        x = {}
+        calls = []
+        for s in wl.layers:
+            layers, pool, base = make_pool_layers(q, torch, dev, s.code, s.m, s.n, s.k, P,
+                                                  "bench/llama/" + s.name)
+            pools.append(pool)
+            if s.n not in x:
+                x[s.n] = torch.from_numpy(synth.activations("bench/llama/x", b, s.n).view(np.int16)).to(dev)
+            ws = q.workspace(base, b, q.QDEC_OP_GEMV, dev)
+            y = torch.empty((b, s.m), dtype=torch.float16, device=dev)
+            calls.append([Launch(q, "qdec_gemv", L, x[s.n], y, b, ws, stream) for L in layers])
+        for i in range(10):
+            for c in calls:
+                c[i % P]()
+        torch.cuda.synchronize()
+        reps = 60
+        t0 = time.perf_counter()
+        for i in range(reps):
+            for c in calls:
+                c[i % P]()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) / reps * 1e6
+        out["llama3_8b_layer_b%d" % b] = {"us_per_layer": round(us, 2),
+                                          "packed_GBps": round(layer_bytes / (us * 1e-6) / 1e9, 1)}
+        log("llama layer b=%d: %.2f us/layer" % (b, us))
+        del calls
+        pools.clear()
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_gemm(q, torch, dev, stream):
+    """28672x8192 HYB k=3 up-projection with X of 64x8192: TFLOP/s of the
+    three-launch batched path and of the MFMA kernel alone."""
+    import synth
+    wl = synth.WORKLOADS["up70b_prefill"]
+    s = wl.layers[0]
+    b = wl.batches[0]
+    P = 4
+    layers, pool, base = make_pool_layers(q, torch, dev, s.code, s.m, s.n, s.k, P, "bench/up70b")
+    x = torch.from_numpy(synth.activations("bench/up70b/x", b, s.n).view(np.int16)).to(dev)
+    ws = q.workspace(base, b, q.QDEC_OP_GEMM, dev)
+    y = torch.empty((b, s.m), dtype=torch.float16, device=dev)
+    calls = [Launch(q, "qdec_gemm", L, x, y, b, ws, stream) for L in layers]
+    for i in range(5):
+        calls[i % P]()
+    torch.cuda.synchronize()
+    cnt = [0]
+
+    def one():
+        calls[cnt[0] % P]()
+        cnt[0] += 1
+    us = time_events(torch, one, 30)
+    flops = 2.0 * s.m * s.n * b
+    tf = flops / (us * 1e-6) / 1e12
+    log("gemm b=64: %.1f us, %.1f TFLOP/s" % (us, tf))
+    del calls, pool
+    torch.cuda.empty_cache()
+    return {"gemm_b64_up70b": {"us_per_call": round(us, 2), "TFLOPs": round(tf, 1),
+                               "frac_of_fp16_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                               "launches": "rht_in + gemm + rht_out"}}
+
+
+def cpu_baseline(specs, x16):
+    """The oracle as it stands, on the host cores: one full forward per layer
+    of the step (decode of every tile, O(B^2) Hadamards, fp64 matvec)."""
+    import oracle
+    import synth
+    t_total = 0.0
+    nbytes = 0
+    for s in specs:
+        host = s.build("cpu_baseline")
+        t0 = time.perf_counter()
+        oracle.forward(host, x16)
+        t_total += time.perf_counter() - t0
+        nbytes += s.m * s.n * s.k // 8
+    gbs = nbytes / t_total / 1e9
+    log("cpu oracle: %.2f s for %d layers, %.4f GB/s" % (t_total, len(specs), gbs))
+    return {"value": round(gbs, 5), "unit": "GB/s", "cores": oracle.omp_threads(), "kind": "oracle",
+            "sample": "one full forward of each of the %d layers of one step (%.1f MiB of codes), "
+                      "%.2f s" % (len(specs), nbytes / 2 ** 20, t_total)}
+
+
+if __name__ == "__main__":
+    main()

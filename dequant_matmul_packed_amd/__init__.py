@@ -1,0 +1,228 @@
+"""qdec: weight-only quantized matmul for MI355X (gfx950), y = W_hat x.
+
+A thin ctypes binding over the C ABI of ``libqdec.so`` (``include/qdec.h``).
+The functions carry the C names (``qdec_gemv`` ...) and only marshal
+arguments: every step of the computation runs in the library's HIP kernels.
+PyTorch provides device memory and streams.  Importing this package fails
+loudly when the library has not been built (``__graft_entry__.build()``);
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqdec.so")
+
+QDEC_OK, QDEC_EINVAL, QDEC_EUNSUPPORTED, QDEC_EWORKSPACE, QDEC_EHIP, QDEC_ENODEV = 0, -1, -2, -3, -4, -5
+QDEC_CODE_HYB, QDEC_CODE_1MAD, QDEC_CODE_3INST, QDEC_CODE_NUQ, QDEC_CODE_VQ = 1, 2, 3, 4, 5
+QDEC_OP_GEMV, QDEC_OP_GEMM = 1, 2
+QDEC_ABI_VERSION = 1
+
+# The exported symbols, as declared in include/qdec.h.
+EXPORTS = ("qdec_abi_version", "qdec_status_string", "qdec_last_error", "qdec_workspace_bytes",
+           "qdec_rht", "qdec_gemv", "qdec_gemm", "qdec_decode_tile")
+
+
+class QdecError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        detail = ""
+        if status == QDEC_EHIP:
+            detail = ": " + _lib.qdec_last_error().decode()
+        super().__init__("%s failed: %s (%d)%s" % (what, _status_string(status), status, detail))
+
+
+class qdec_layer(ctypes.Structure):
+    """Mirror of ``struct qdec_layer`` (include/qdec.h)."""
+    _fields_ = [
+        ("abi_version", ctypes.c_uint32), ("code", ctypes.c_int32),
+        ("L", ctypes.c_int32), ("k", ctypes.c_int32), ("V", ctypes.c_int32), ("Q", ctypes.c_int32),
+        ("m", ctypes.c_int64), ("n", ctypes.c_int64),
+        ("codes", ctypes.c_void_p), ("lut", ctypes.c_void_p), ("group_scale", ctypes.c_void_p),
+        ("group", ctypes.c_int32), ("layer_scale", ctypes.c_float),
+        ("sign_in", ctypes.c_void_p), ("sign_out", ctypes.c_void_p),
+        ("had_in", ctypes.c_int32), ("had_out", ctypes.c_int32),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libqdec.so is not built (%s); run __graft_entry__.build() -- "
+                          "there is no fallback path" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.qdec_abi_version.restype = ctypes.c_uint32
+    lib.qdec_abi_version.argtypes = []
+    lib.qdec_status_string.restype = ctypes.c_char_p
+    lib.qdec_status_string.argtypes = [ctypes.c_int]
+    lib.qdec_last_error.restype = ctypes.c_char_p
+    lib.qdec_last_error.argtypes = []
+    lib.qdec_workspace_bytes.restype = ctypes.c_size_t
+    lib.qdec_workspace_bytes.argtypes = [P, i64, i32]
+    lib.qdec_rht.restype = ctypes.c_int
+    lib.qdec_rht.argtypes = [P, i32, P, i32, i64, i64, i32, P, i32, ctypes.c_float, P]
+    for fn in (lib.qdec_gemv, lib.qdec_gemm):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [P, P, P, i64, P, ctypes.c_size_t, P]
+    lib.qdec_decode_tile.restype = ctypes.c_int
+    lib.qdec_decode_tile.argtypes = [P, i64, i64, P, P]
+    if lib.qdec_abi_version() != QDEC_ABI_VERSION:
+        raise ImportError("libqdec.so ABI version mismatch")
+    return lib
+
+
+_lib = _load()
+
+
+def _status_string(status: int) -> str:
+    return _lib.qdec_status_string(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != QDEC_OK:
+        raise QdecError(status, what)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+@dataclass
+class Layer:
+    """A quantized layer whose buffers live in device tensors.  Holds the
+    tensors (so they outlive the descriptor) and the C descriptor."""
+    code: int
+    L: int
+    k: int
+    V: int
+    Q: int
+    m: int
+    n: int
+    codes: object
+    lut: object = None
+    group_scale: object = None
+    group: int = 0
+    layer_scale: float = 1.0
+    sign_in: object = None
+    sign_out: object = None
+    had_in: int = 1
+    had_out: int = 1
+    _desc: qdec_layer = field(default=None, repr=False)
+
+    def desc(self) -> qdec_layer:
+        if self._desc is None:
+            self._desc = qdec_layer(QDEC_ABI_VERSION, self.code, self.L, self.k, self.V, self.Q,
+                                    self.m, self.n, _ptr(self.codes), _ptr(self.lut),
+                                    _ptr(self.group_scale), self.group, self.layer_scale,
+                                    _ptr(self.sign_in), _ptr(self.sign_out), self.had_in, self.had_out)
+        return self._desc
+
+    @property
+    def n_tiles(self) -> int:
+        return (self.m // 16) * (self.n // 16)
+
+    @property
+    def code_bytes(self) -> int:
+        return self.m * self.n * self.k // 8
+
+
+def qdec_workspace_bytes(layer: Layer, batch: int, op: int) -> int:
+    return int(_lib.qdec_workspace_bytes(ctypes.byref(layer.desc()), batch, op))
+
+
+def qdec_rht(inp, in_dtype: int, out, out_dtype: int, rows: int, n: int, block: int,
+             signs=None, mode: int = 0, scale: float = 1.0, stream=None) -> None:
+    _check(_lib.qdec_rht(_ptr(inp), in_dtype, _ptr(out), out_dtype, rows, n, block, _ptr(signs),
+                         mode, scale, _stream(stream)), "qdec_rht")
+
+
+def qdec_gemv(layer: Layer, x, y, batch: int, ws, ws_bytes: int, stream=None) -> None:
+    _check(_lib.qdec_gemv(ctypes.byref(layer.desc()), _ptr(x), _ptr(y), batch, _ptr(ws), ws_bytes,
+                          _stream(stream)), "qdec_gemv")
+
+
+def qdec_gemm(layer: Layer, x, y, batch: int, ws, ws_bytes: int, stream=None) -> None:
+    _check(_lib.qdec_gemm(ctypes.byref(layer.desc()), _ptr(x), _ptr(y), batch, _ptr(ws), ws_bytes,
+                          _stream(stream)), "qdec_gemm")
+
+
+def qdec_decode_tile(layer: Layer, first_tile: int, n_tiles: int, out, stream=None) -> None:
+    _check(_lib.qdec_decode_tile(ctypes.byref(layer.desc()), first_tile, n_tiles, _ptr(out),
+                                 _stream(stream)), "qdec_decode_tile")
+
+
+def raw_status(fn_name: str, *args) -> int:
+    """Call an entry point with raw ctypes arguments and return its status
+    (for error-path tests)."""
+    return int(getattr(_lib, fn_name)(*args))
+
+
+# ---------------------------------------------------------------------------
+# Convenience wrappers over torch tensors (allocation is torch's).
+
+def upload_layer(host, device="cuda") -> Layer:
+    """Copy a host layer (numpy arrays: codes, lut, gscale, sign_in, sign_out)
+    to device tensors."""
+    import numpy as np
+    import torch
+
+    def t(a, dtype):
+        if a is None:
+            return None
+        return torch.from_numpy(np.ascontiguousarray(a).view(dtype)).to(device)
+
+    codes = t(host.codes, np.int32)
+    return Layer(code=host.code, L=host.L, k=host.k, V=host.V, Q=host.Q, m=host.m, n=host.n,
+                 codes=codes, lut=t(host.lut, np.int32), group_scale=t(host.gscale, np.int16),
+                 group=host.group, layer_scale=host.scale, sign_in=t(host.sign_in, np.int32),
+                 sign_out=t(host.sign_out, np.int32), had_in=host.had_in, had_out=host.had_out)
+
+
+def workspace(layer: Layer, batch: int, op: int, device="cuda"):
+    """A zero-filled workspace tensor for qdec_gemv / qdec_gemm."""
+    import torch
+    nbytes = qdec_workspace_bytes(layer, batch, op)
+    if nbytes == 0:
+        raise QdecError(QDEC_EINVAL, "qdec_workspace_bytes")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def gemv(layer: Layer, x, ws=None, y=None):
+    """y = layer(x) for x of shape [b, n] (fp16, b <= 8), one launch."""
+    import torch
+    b = x.shape[0]
+    if ws is None:
+        ws = workspace(layer, b, QDEC_OP_GEMV, x.device)
+    if y is None:
+        y = torch.empty((b, layer.m), dtype=torch.float16, device=x.device)
+    qdec_gemv(layer, x, y, b, ws, ws.numel())
+    return y
+
+
+def gemm(layer: Layer, x, ws=None, y=None):
+    """y = layer(x) for x of shape [b, n] (fp16, b <= 256), MFMA path."""
+    import torch
+    b = x.shape[0]
+    if ws is None:
+        ws = workspace(layer, b, QDEC_OP_GEMM, x.device)
+    if y is None:
+        y = torch.empty((b, layer.m), dtype=torch.float16, device=x.device)
+    qdec_gemm(layer, x, y, b, ws, ws.numel())
+    return y

@@ -1,0 +1,304 @@
+// C ABI of the qdec library: argument validation, workspace sizing, kernel
+// selection and launch on the caller's stream.  Everything a call can reject
+// is rejected here, on the host, before any device work is queued.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "qdec.h"
+#include "qdec_device.hpp"
+#include "qdec_internal.hpp"
+
+namespace qdec {
+hipError_t launch_gemv_hyb(const GemvArgs& a, hipStream_t stream);
+hipError_t launch_gemv_mad1(const GemvArgs& a, hipStream_t stream);
+hipError_t launch_gemv_inst3(const GemvArgs& a, hipStream_t stream);
+hipError_t launch_gemv_nuq(const GemvArgs& a, hipStream_t stream);
+hipError_t launch_gemv_vq(const GemvArgs& a, hipStream_t stream);
+
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
+  switch (a.L.code) {
+    case HYB: return launch_gemv_hyb(a, stream);
+    case MAD1: return launch_gemv_mad1(a, stream);
+    case INST3: return launch_gemv_inst3(a, stream);
+    case NUQ: return launch_gemv_nuq(a, stream);
+    case VQ: return launch_gemv_vq(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool gemv_supported(int code, int k, int b) {
+  return code >= HYB && code <= VQ && k >= 2 && k <= 4 && b >= 1 && b <= 8;
+}
+}  // namespace qdec
+
+using namespace qdec;
+
+namespace {
+
+constexpr int kMaxHadamard = 16384;
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Format-level validation; EUNSUPPORTED for valid combinations not built.
+int check_layer(const qdec_layer* L, LayerArgs* out) {
+  if (!L || L->abi_version != QDEC_ABI_VERSION) return QDEC_EINVAL;
+  if (L->m <= 0 || L->n <= 0 || (L->m % 128) || (L->n % 16)) return QDEC_EINVAL;
+  if (L->k < 1 || L->k > 8) return QDEC_EINVAL;
+  if (!L->codes || !aligned(L->codes, 16)) return QDEC_EINVAL;
+  if (!is_pow2(L->had_in) || L->n % L->had_in) return QDEC_EINVAL;
+  if (!is_pow2(L->had_out) || L->m % L->had_out) return QDEC_EINVAL;
+  if (!isfinite(L->layer_scale)) return QDEC_EINVAL;
+  switch (L->code) {
+    case QDEC_CODE_HYB:
+      if (L->L != 16 || L->V != 2 || L->Q < 1 || L->Q > 15 || !L->lut) return QDEC_EINVAL;
+      if (L->k * L->V > L->L) return QDEC_EINVAL;
+      if (L->Q > 11) return QDEC_EUNSUPPORTED;   // LDS table would exceed the budget
+      break;
+    case QDEC_CODE_1MAD:
+    case QDEC_CODE_3INST:
+      if (L->L != 16 || L->V != 1) return QDEC_EINVAL;
+      break;
+    case QDEC_CODE_NUQ:
+      if (L->V != 1 || L->L != L->k || !L->lut || !L->group_scale) return QDEC_EINVAL;
+      if (L->group < 16 || L->group % 16 || L->n % L->group) return QDEC_EINVAL;
+      break;
+    case QDEC_CODE_VQ:
+      if (L->V != 2 || L->L != 2 * L->k || !L->lut) return QDEC_EINVAL;
+      break;
+    default:
+      return QDEC_EINVAL;
+  }
+  if (L->k < 2 || L->k > 4) return QDEC_EUNSUPPORTED;
+  if (L->had_in > kMaxHadamard || L->had_out > kMaxHadamard) return QDEC_EUNSUPPORTED;
+  if (out) {
+    out->codes = L->codes;
+    out->lut = L->lut;
+    out->gscale = L->group_scale;
+    out->sign_in = L->sign_in;
+    out->sign_out = L->sign_out;
+    out->m = L->m;
+    out->n = L->n;
+    out->code = L->code;
+    out->k = L->k;
+    out->Q = L->code == QDEC_CODE_HYB ? L->Q : 0;
+    out->qshift = L->code == QDEC_CODE_HYB ? 15 - L->Q : 0;
+    out->group = L->code == QDEC_CODE_NUQ ? L->group : 1;
+    out->had_in = L->had_in;
+    out->had_out = L->had_out;
+    out->scale = L->layer_scale;
+  }
+  return QDEC_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// The current device must be a gfx950 part; checked once per device.
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return QDEC_ENODEV;
+  }
+  static int state[64];   // 0 unknown, 1 ok, -1 not gfx950
+  if (dev < 64 && state[dev]) return state[dev] > 0 ? QDEC_OK : QDEC_ENODEV;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return QDEC_ENODEV;
+  }
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) state[dev] = ok ? 1 : -1;
+  return ok ? QDEC_OK : QDEC_ENODEV;
+}
+
+thread_local char g_last_error[256] = "no error";
+
+int status_of(hipError_t e) {
+  if (e == hipSuccess) return QDEC_OK;
+  snprintf(g_last_error, sizeof g_last_error, "%s (%d)", hipGetErrorString(e), (int)e);
+  return QDEC_EHIP;
+}
+
+// Input-chunk width of the fused GEMV: enough (panel, chunk) workgroups to
+// cover the 256 CUs several times, chunks a power of two in [64, 512].
+int gemv_chunk(int64_t m, int64_t n) {
+  const int64_t npanels = m / 128;
+  int64_t want = (n * npanels) / 1024;
+  int kc = 64;
+  while (kc < 512 && kc * 2 <= want) kc *= 2;
+  return kc;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t qdec_abi_version(void) { return QDEC_ABI_VERSION; }
+
+const char* qdec_last_error(void) { return g_last_error; }
+
+const char* qdec_status_string(int status) {
+  switch (status) {
+    case QDEC_OK: return "ok";
+    case QDEC_EINVAL: return "invalid argument";
+    case QDEC_EUNSUPPORTED: return "unsupported configuration";
+    case QDEC_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case QDEC_EHIP: return "HIP runtime error";
+    case QDEC_ENODEV: return "no gfx950 device";
+    default: return "unknown status";
+  }
+}
+
+size_t qdec_workspace_bytes(const qdec_layer* layer, int64_t batch, int32_t op) {
+  LayerArgs L;
+  if (check_layer(layer, &L) != QDEC_OK) return 0;
+  if (op == QDEC_OP_GEMV) {
+    if (batch < 1 || batch > 8) return 0;
+    return gemv_ws_bytes(L.m, batch, L.had_out);
+  }
+  if (op == QDEC_OP_GEMM) {
+    if (batch < 1 || batch > 256) return 0;
+    return gemm_ws_bytes(L.m, L.n, batch);
+  }
+  return 0;
+}
+
+int qdec_rht(const void* in, int32_t in_dtype, void* out, int32_t out_dtype, int64_t rows,
+             int64_t n, int32_t block, const uint32_t* signs, int32_t mode, float scale,
+             void* stream) {
+  if (!in || !out || rows < 0 || n <= 0) return QDEC_EINVAL;
+  if ((in_dtype != 0 && in_dtype != 1) || (out_dtype != 0 && out_dtype != 1)) return QDEC_EINVAL;
+  if (mode != 0 && mode != 1) return QDEC_EINVAL;
+  if (!is_pow2(block) || n % block) return QDEC_EINVAL;
+  if (!isfinite(scale)) return QDEC_EINVAL;
+  if (block > kMaxHadamard) return QDEC_EUNSUPPORTED;
+  const size_t ib = (size_t)(rows * n) * (in_dtype ? 4 : 2);
+  const size_t ob = (size_t)(rows * n) * (out_dtype ? 4 : 2);
+  if (in != out && overlap(in, ib, out, ob)) return QDEC_EINVAL;
+  if (in == out && in_dtype != out_dtype) return QDEC_EINVAL;
+  const int d = check_device();
+  if (d) return d;
+  RhtArgs a;
+  a.in = in;
+  a.out = out;
+  a.in_f32 = in_dtype;
+  a.out_f32 = out_dtype;
+  a.rows = rows;
+  a.n = n;
+  a.block = block;
+  a.signs = signs;
+  a.mode = mode;
+  a.mult = (float)((double)scale / sqrt((double)block));
+  return status_of(launch_rht(a, (hipStream_t)stream));
+}
+
+int qdec_gemv(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t batch, void* ws,
+              size_t ws_bytes, void* stream) {
+  LayerArgs L;
+  int st = check_layer(layer, &L);
+  if (st) return st;
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 4)) return QDEC_EINVAL;
+  if (batch < 1) return QDEC_EINVAL;
+  if (batch > 8) return QDEC_EUNSUPPORTED;
+  if (overlap(x, (size_t)(batch * L.n) * 2, y, (size_t)(batch * L.m) * 2)) return QDEC_EINVAL;
+  const size_t need = gemv_ws_bytes(L.m, batch, L.had_out);
+  if (!ws || !aligned(ws, 256) || ws_bytes < need) return QDEC_EWORKSPACE;
+  if (overlap(ws, need, x, (size_t)(batch * L.n) * 2) || overlap(ws, need, y, (size_t)(batch * L.m) * 2))
+    return QDEC_EINVAL;
+  const int d = check_device();
+  if (d) return d;
+  GemvArgs a;
+  a.L = L;
+  a.x = x;
+  a.y = y;
+  a.b = (int)batch;
+  a.z = (float*)ws;
+  a.counters = (uint32_t*)((char*)ws + align256((size_t)(batch * L.m) * 4));
+  a.Kc = gemv_chunk(L.m, L.n);
+  a.nchunks = (int)((L.n + a.Kc - 1) / a.Kc);
+  a.U = gemv_unit_rows(L.had_out);
+  const double factor = L.code == QDEC_CODE_1MAD ? 1.0 / sqrt(21845.0) : 1.0;
+  // the 1MAD matmul path multiplies by the fp32 normaliser, as the decode does
+  const double f32norm = (double)(float)factor;
+  a.out_mult = (float)((double)L.scale * f32norm / sqrt((double)L.had_out));
+  return status_of(launch_gemv(a, (hipStream_t)stream));
+}
+
+int qdec_gemm(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t batch, void* ws,
+              size_t ws_bytes, void* stream) {
+  LayerArgs L;
+  int st = check_layer(layer, &L);
+  if (st) return st;
+  if (!x || !y || !aligned(x, 16) || !aligned(y, 4)) return QDEC_EINVAL;
+  if (batch < 1) return QDEC_EINVAL;
+  if (batch > 256) return QDEC_EUNSUPPORTED;
+  if (overlap(x, (size_t)(batch * L.n) * 2, y, (size_t)(batch * L.m) * 2)) return QDEC_EINVAL;
+  const size_t need = gemm_ws_bytes(L.m, L.n, batch);
+  if (!ws || !aligned(ws, 256) || ws_bytes < need) return QDEC_EWORKSPACE;
+  if (overlap(ws, need, x, (size_t)(batch * L.n) * 2) || overlap(ws, need, y, (size_t)(batch * L.m) * 2))
+    return QDEC_EINVAL;
+  const int d = check_device();
+  if (d) return d;
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t* xr = (uint16_t*)ws;
+  float* z = (float*)((char*)ws + align256((size_t)(batch * L.n) * 2));
+  // 1. X' = RHT_in(X), fp16
+  RhtArgs r;
+  r.in = x;
+  r.out = xr;
+  r.in_f32 = 0;
+  r.out_f32 = 0;
+  r.rows = batch;
+  r.n = L.n;
+  r.block = L.had_in;
+  r.signs = L.sign_in;
+  r.mode = 0;
+  r.mult = (float)(1.0 / sqrt((double)L.had_in));
+  hipError_t e = launch_rht(r, s);
+  if (e != hipSuccess) return status_of(e);
+  // 2. Z = W_hat X'^T (fp32, accumulated into the zeroed workspace)
+  GemmArgs g;
+  g.L = L;
+  g.xr = xr;
+  g.z = z;
+  g.b = (int)batch;
+  const int64_t npanels = L.m / 128, nbt = (batch + 63) / 64;
+  const int64_t niter = (L.n / 16 + 3) / 4;
+  int64_t ks = (512 + npanels * nbt - 1) / (npanels * nbt);
+  if (ks < 1) ks = 1;
+  if (ks > niter) ks = niter;
+  if (ks > 16) ks = 16;
+  g.ksplit = (int)ks;
+  e = launch_gemm(g, s);
+  if (e != hipSuccess) return status_of(e);
+  // 3. Y = s_out .* (scale/sqrt(B) H Z), fp16; Z re-zeroed
+  e = launch_rht_out_f32(z, y, batch, L.m, L.had_out, L.sign_out,
+                         (float)((double)L.scale / sqrt((double)L.had_out)), s);
+  return status_of(e);
+}
+
+int qdec_decode_tile(const qdec_layer* layer, int64_t first_tile, int64_t n_tiles, uint16_t* out,
+                     void* stream) {
+  LayerArgs L;
+  int st = check_layer(layer, &L);
+  if (st) return st;
+  const int64_t total = (L.m / 16) * (L.n / 16);
+  if (first_tile < 0 || n_tiles < 0 || first_tile + n_tiles > total) return QDEC_EINVAL;
+  if (n_tiles > 0 && (!out || !aligned(out, 16))) return QDEC_EINVAL;
+  if (n_tiles == 0) return QDEC_OK;
+  const int d = check_device();
+  if (d) return d;
+  DecodeArgs a;
+  a.L = L;
+  a.first = first_tile;
+  a.count = n_tiles;
+  a.out = out;
+  return status_of(launch_decode_tile(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,152 @@
+// qdec_decode_tile and qdec_rht kernels.
+#include "gemv_impl.hpp"
+#include "qdec_device.hpp"
+#include "qdec_internal.hpp"
+
+namespace qdec {
+
+// ---------------------------------------------------------------------------
+// Tile decode (the bit-exact parity surface).  32 tiles per workgroup, one
+// 8-lane group per tile, the same window extraction and value maps the
+// matmul kernels use.
+template <int CODE, int K>
+__global__ __launch_bounds__(256) void decode_tile_kernel(DecodeArgs a) {
+  constexpr int COPIES = GemvTable<CODE>::COPIES;
+  extern __shared__ __align__(16) uint32_t tab[];
+  const int tid = threadIdx.x, lane = tid & 63, q = tid & 7;
+  if constexpr (CODE == HYB) fill_signed_table<COPIES>(tab, a.L.lut, a.L.Q, tid, 256);
+  if constexpr (CODE == VQ) fill_plain_table<COPIES>(tab, a.L.lut, 1 << (2 * K), tid, 256);
+  if constexpr (CODE == NUQ) fill_plain_table<1>(tab, a.L.lut, 1 << K, tid, 256);
+  __syncthreads();
+
+  const int64_t tile = a.first + (int64_t)blockIdx.x * 32 + (tid >> 3);
+  const bool valid = tile < a.first + a.count;
+  uint32_t w[K + 1];
+#pragma unroll
+  for (int i = 0; i <= K; ++i) w[i] = 0u;
+  if (valid) load_words<K>(a.L.codes + tile * (8 * K) + q * K, w);
+  w[K] = next_lane_word(w[0], lane);
+  if (!valid) return;
+
+  float gs[2] = {0.f, 0.f};
+  if constexpr (CODE == NUQ) {
+    // storage index -> tile (R, C): panels of 8 tile rows, column by column
+    const int64_t per_row = a.L.n >> 4;
+    const int64_t r8 = tile & 7, rest = tile >> 3;
+    const int64_t C = rest % per_row, R = (rest / per_row) * 8 + r8;
+    const int64_t gstride = a.L.n / a.L.group;
+    const int64_t g = (C * 16) / a.L.group;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) gs[r] = h2f(a.L.gscale[(R * 16 + 2 * q + r) * gstride + g]);
+  }
+  uint32_t out[16];
+  lane_decode_exact<CODE, K, COPIES>(w, tab + (lane & (COPIES - 1)), a.L.qshift, gs, out);
+  uint4* dst = reinterpret_cast<uint4*>(a.out + (tile - a.first) * 256 + q * 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+}
+
+template <int CODE, int K>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int COPIES = GemvTable<CODE>::COPIES;
+  const size_t lds = (size_t)gemv_table_words<CODE, K>(a.L.Q) * 4 + 16;
+  (void)COPIES;
+  const unsigned grid = (unsigned)((a.count + 31) / 32);
+  hipLaunchKernelGGL((decode_tile_kernel<CODE, K>), dim3(grid), dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int CODE>
+static hipError_t launch_decode_code(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.L.k) {
+    case 2: return launch_decode_t<CODE, 2>(a, stream);
+    case 3: return launch_decode_t<CODE, 3>(a, stream);
+    case 4: return launch_decode_t<CODE, 4>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_tile(const DecodeArgs& a, hipStream_t stream) {
+  if (a.count <= 0) return hipSuccess;
+  switch (a.L.code) {
+    case HYB: return launch_decode_code<HYB>(a, stream);
+    case MAD1: return launch_decode_code<MAD1>(a, stream);
+    case INST3: return launch_decode_code<INST3>(a, stream);
+    case NUQ: return launch_decode_code<NUQ>(a, stream);
+    case VQ: return launch_decode_code<VQ>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool decode_supported(int code, int k) {
+  return code >= HYB && code <= VQ && k >= 2 && k <= 4;
+}
+
+// ---------------------------------------------------------------------------
+// Randomized Hadamard transform of independent row blocks: one workgroup per
+// (row, block), the block held in LDS in fp32.
+//   mode 0: out = mult * H (s .* in);   mode 1: out = s .* (mult * H in)
+// ("Incoherence Processing (W2)": the RHT is invertible up to rounding.)
+// zero_in clears the fp32 input after reading it (the batched path re-zeroes
+// its accumulator this way).
+__global__ __launch_bounds__(256) void rht_kernel(RhtArgs a, int zero_in) {
+  extern __shared__ __align__(16) float buf[];
+  const int tid = threadIdx.x;
+  const int B = a.block;
+  const int64_t nblk = a.n / B;
+  const int64_t row = blockIdx.x / nblk;
+  const int64_t c0 = (blockIdx.x % nblk) * B;
+  const int64_t off = row * a.n + c0;
+  for (int i = tid; i < B; i += 256) {
+    float v;
+    if (a.in_f32) {
+      float* p = (float*)a.in + off + i;
+      v = *p;
+      if (zero_in) *p = 0.f;
+    } else {
+      v = h2f(((const uint16_t*)a.in)[off + i]);
+    }
+    if (a.mode == 0) v *= sign_of(a.signs, c0 + i);
+    buf[i] = v;
+  }
+  __syncthreads();
+  if (B > 1) fwht_segments(buf, B, B, tid, 256);
+  for (int i = tid; i < B; i += 256) {
+    float v = buf[i] * a.mult;
+    if (a.mode == 1) v *= sign_of(a.signs, c0 + i);
+    if (a.out_f32) ((float*)a.out)[off + i] = v;
+    else ((uint16_t*)a.out)[off + i] = f2h_bits(v);
+  }
+}
+
+static hipError_t launch_rht_impl(const RhtArgs& a, int zero_in, hipStream_t stream) {
+  if (a.rows <= 0) return hipSuccess;
+  static size_t have = 0;
+  const hipError_t e =
+      ensure_dynamic_lds(reinterpret_cast<const void*>(&rht_kernel), (size_t)a.block * 4, &have);
+  if (e != hipSuccess) return e;
+  const int64_t blocks = a.rows * (a.n / a.block);
+  hipLaunchKernelGGL(rht_kernel, dim3((unsigned)blocks), dim3(256), (size_t)a.block * 4, stream, a,
+                     zero_in);
+  return hipGetLastError();
+}
+
+hipError_t launch_rht(const RhtArgs& a, hipStream_t stream) { return launch_rht_impl(a, 0, stream); }
+
+hipError_t launch_rht_out_f32(float* z, uint16_t* y, int64_t rows, int64_t m, int block,
+                              const uint32_t* signs, float mult, hipStream_t stream) {
+  RhtArgs a;
+  a.in = z;
+  a.out = y;
+  a.in_f32 = 1;
+  a.out_f32 = 0;
+  a.rows = rows;
+  a.n = m;
+  a.block = block;
+  a.signs = signs;
+  a.mode = 1;
+  a.mult = mult;
+  return launch_rht_impl(a, 1, stream);
+}
+
+}  // namespace qdec

@@ -1,0 +1,8 @@
+// qdec_gemv kernels for the VQ code (k = 2, 3, 4; batch tiles 1, 2, 4, 8).
+#include "gemv_impl.hpp"
+
+namespace qdec {
+hipError_t launch_gemv_vq(const GemvArgs& a, hipStream_t stream) {
+  return launch_gemv_code<VQ>(a, stream);
+}
+}  // namespace qdec

@@ -1,0 +1,219 @@
+// Device-side building blocks shared by the qdec kernels (gfx950, wave64).
+//
+// Packed format, lane layout and code rules are those of include/qdec.h:
+// a 16x16 tile is a 256*k-bit stream; 8 consecutive lanes handle one tile and
+// lane q of the group holds stream words [q*k, q*k + k), i.e. stream bits
+// [32kq, 32k(q+1)) = weights 32q .. 32q+31 = tile rows 2q and 2q+1.  The
+// state of a step is an L-bit window that may run into the first word of the
+// next lane (the last lane wraps to the first: the tail-biting stream), which
+// a cross-lane permute supplies ("QTIP: Quantization with Trellises and
+// Incoherence Processing", "Figure 2 (Q4)": the bitshift trellis decodes any
+// step from its own window, so all lanes decode in parallel).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qdec {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+enum { HYB = 1, MAD1 = 2, INST3 = 3, NUQ = 4, VQ = 5 };
+
+__host__ __device__ constexpr int code_V(int code) { return (code == HYB || code == VQ) ? 2 : 1; }
+__host__ __device__ constexpr int code_L(int code, int k) {
+  return code == NUQ ? k : (code == VQ ? 2 * k : 16);
+}
+
+// Computed-code constants (this library's own; the pages give none).
+constexpr uint32_t MAD1_A = 0x00EA4F79u, MAD1_C = 0xC2AA9973u;
+constexpr uint32_t INST3_A = 0x00E77B2Bu, INST3_C = 0xEACB81D7u;
+constexpr uint32_t INST3_MASK = 0x8FFF8FFFu, INST3_PATTERN = 0x30003000u;
+// fp32(1/sqrt(21845)): unit variance for a centred sum of four uniform bytes.
+constexpr uint32_t MAD1_NORM_BITS = 0x3BDDB446u;
+// 1MAD in the matmul paths: the byte sum sigma is formed as the fp16 number
+// 1024 + sigma (exponent 10 makes integers exact); the mean 1024 + 510 is
+// removed once per chunk through the sum of the activations.
+constexpr float MAD1_BIAS = 1534.0f;
+
+__device__ __forceinline__ float mad1_norm() { return __builtin_bit_cast(float, MAD1_NORM_BITS); }
+
+__device__ __forceinline__ uint16_t f2h_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ half2v as_h2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
+
+// L-bit window starting at bit offset o of the lane's word array (MSB first).
+// o and L are compile-time constants after unrolling, so this folds to one
+// shift/mask or one funnel shift (v_alignbit_b32) plus a mask.
+template <int L>
+__device__ __forceinline__ uint32_t window_at(const uint32_t* w, int o) {
+  const int i = o >> 5, r = o & 31;
+  const uint32_t mask = (L == 32) ? 0xFFFFFFFFu : ((1u << L) - 1u);
+  if (r + L <= 32) return (w[i] >> (32 - r - L)) & mask;
+  return __builtin_amdgcn_alignbit(w[i], w[i + 1], 64 - r - L) & mask;
+}
+
+// First word of the next lane of the same 8-lane tile group (lane 7 wraps to
+// lane 0: the tail-biting stream).
+__device__ __forceinline__ uint32_t next_lane_word(uint32_t v, int lane) {
+  const int src = (lane & ~7) | ((lane + 1) & 7);
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)v);
+}
+
+// HYB hash: h = s*s + s (mod 2^16); the signed table index is h >> (15 - Q)
+// (Q index bits plus the sign bit 15).
+__device__ __forceinline__ uint32_t hyb_signed_index(uint32_t s, int qshift) {
+  return ((s * s + s) & 0xFFFFu) >> qshift;
+}
+
+// 1MAD: LCG output for a state.
+__device__ __forceinline__ uint32_t mad1_lcg(uint32_t s) { return s * MAD1_A + MAD1_C; }
+// 3INST: LCG, then force the high exponent bits of both halves.
+__device__ __forceinline__ uint32_t inst3_bits(uint32_t s) {
+  return ((s * INST3_A + INST3_C) & INST3_MASK) | INST3_PATTERN;
+}
+
+// Exact fp16 value of 1MAD: fp16(fp32((sigma - 510) * fp32(1/sqrt(21845)))).
+__device__ __forceinline__ uint16_t mad1_value_bits(uint32_t s) {
+  const int sigma = (int)__builtin_amdgcn_sad_u8(mad1_lcg(s), 0u, 0u);
+  return f2h_bits((float)(sigma - 510) * mad1_norm());
+}
+// Exact fp16 value of 3INST: the fp16 sum of the two halves (one rounding).
+__device__ __forceinline__ uint16_t inst3_value_bits(uint32_t s) {
+  const uint32_t u = inst3_bits(s);
+  const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu));
+  const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+  return __builtin_bit_cast(uint16_t, (_Float16)(lo + hi));
+}
+
+// ---------------------------------------------------------------------------
+// LDS lookup tables.  HYB: the 2^Q-entry LUT expanded by the sign bit into
+// 2^(Q+1) signed entries (the sign flips both halves), replicated COPIES
+// times with entry e of copy c at word e*COPIES + c, so lanes that use
+// different copies fall in different banks.  VQ: 2^(2k) pairs, replicated
+// the same way.  NUQ: 2^k fp16 levels (one copy, broadcast reads).
+template <int COPIES>
+__device__ __forceinline__ void fill_signed_table(uint32_t* tab, const uint32_t* __restrict__ lut,
+                                                  int Q, int tid, int nthreads) {
+  const int E = 2 << Q;
+  for (int e = tid; e < E; e += nthreads) {
+    uint32_t v = lut[e & ((1 << Q) - 1)];
+    if (e >> Q) v ^= 0x80008000u;
+#pragma unroll
+    for (int c = 0; c < COPIES; ++c) tab[e * COPIES + c] = v;
+  }
+}
+
+template <int COPIES>
+__device__ __forceinline__ void fill_plain_table(uint32_t* tab, const uint32_t* __restrict__ lut,
+                                                 int entries, int tid, int nthreads) {
+  for (int e = tid; e < entries; e += nthreads) {
+    const uint32_t v = lut[e];
+#pragma unroll
+    for (int c = 0; c < COPIES; ++c) tab[e * COPIES + c] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Exact decode of a lane's 32 weights into 16 fp16 pairs:
+// out[i] = (weight 32q + 2i, weight 32q + 2i + 1), i.e. tile row 2q + (i >> 3),
+// columns 2(i & 7) and 2(i & 7) + 1.  w[0..K) are the lane's words and w[K]
+// the next lane's first word.  tabc points at this lane's copy of the table
+// (HYB/VQ) or at the NUQ levels; gs[r] is the NUQ group scale of the lane's
+// row 2q + r (unused otherwise).
+template <int CODE, int K, int COPIES>
+__device__ __forceinline__ void lane_decode_exact(const uint32_t* w, const uint32_t* tabc,
+                                                  int qshift, const float* gs, uint32_t* out) {
+  constexpr int V = code_V(CODE);
+  constexpr int L = code_L(CODE, K);
+  constexpr int KV = K * V;
+  if constexpr (V == 2) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint32_t s = window_at<L>(w, t * KV);
+      if constexpr (CODE == HYB) out[t] = tabc[hyb_signed_index(s, qshift) * COPIES];
+      else out[t] = tabc[s * COPIES];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t v[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = 2 * i + h;
+        const uint32_t s = window_at<L>(w, t * KV);
+        if constexpr (CODE == MAD1) v[h] = mad1_value_bits(s);
+        else if constexpr (CODE == INST3) v[h] = inst3_value_bits(s);
+        else {  // NUQ: fp16(level * group scale); the fp32 product is exact
+          const uint16_t lvl = (uint16_t)tabc[s];
+          v[h] = f2h_bits(h2f(lvl) * gs[i >> 3]);
+        }
+      }
+      out[i] = v[0] | (v[1] << 16);
+    }
+  }
+}
+
+}  // namespace qdec
+
+namespace qdec {
+
+// ---------------------------------------------------------------------------
+// Fast Walsh-Hadamard transform on an LDS float array, in place and
+// unnormalised: every segment of S consecutive entries (S a power of two,
+// `total` a multiple of S) is multiplied by the Sylvester-ordered H_S.  The
+// radix-2 stages act on distinct index bits and commute, so they run in
+// passes of up to 4 bits, 16 values per thread held in registers.  All
+// threads of the block must call it; it ends with a barrier.
+template <int E>
+__device__ __forceinline__ void fwht_pass(float* buf, int total, int b0, int tid, int nthreads) {
+  constexpr int G = 1 << E;
+  const int ngroups = total >> E;
+  for (int g = tid; g < ngroups; g += nthreads) {
+    const int lo = g & ((1 << b0) - 1);
+    const int hi = g >> b0;
+    const int base = (hi << (b0 + E)) | lo;
+    float v[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) v[i] = buf[base + (i << b0)];
+#pragma unroll
+    for (int h = 1; h < G; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        if (!(i & h)) {
+          const float a = v[i], b = v[i + h];
+          v[i] = a + b;
+          v[i + h] = a - b;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) buf[base + (i << b0)] = v[i];
+  }
+}
+
+__device__ inline void fwht_segments(float* buf, int total, int S, int tid, int nthreads) {
+  const int bits = 31 - __builtin_clz((unsigned)S);
+  for (int b0 = 0; b0 < bits; b0 += 4) {
+    const int e = (bits - b0) < 4 ? (bits - b0) : 4;
+    switch (e) {
+      case 1: fwht_pass<1>(buf, total, b0, tid, nthreads); break;
+      case 2: fwht_pass<2>(buf, total, b0, tid, nthreads); break;
+      case 3: fwht_pass<3>(buf, total, b0, tid, nthreads); break;
+      default: fwht_pass<4>(buf, total, b0, tid, nthreads); break;
+    }
+    __syncthreads();
+  }
+}
+
+// Sign of entry j of a packed sign vector (bit set = -1); NULL = all +1.
+__device__ __forceinline__ float sign_of(const uint32_t* __restrict__ s, int64_t j) {
+  if (!s) return 1.0f;
+  return ((s[j >> 5] >> (j & 31)) & 1u) ? -1.0f : 1.0f;
+}
+
+}  // namespace qdec

@@ -1,0 +1,98 @@
+// Host/device interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qdec.h"
+
+namespace qdec {
+
+// A validated layer, as the kernels see it.
+struct LayerArgs {
+  const uint32_t* codes;
+  const uint32_t* lut;
+  const uint16_t* gscale;
+  const uint32_t* sign_in;
+  const uint32_t* sign_out;
+  int64_t m, n;
+  int code, k, Q, qshift, group;
+  int had_in, had_out;
+  float scale;
+};
+
+struct GemvArgs {
+  LayerArgs L;
+  const uint16_t* x;   // [b][n] fp16
+  uint16_t* y;         // [b][m] fp16
+  int b;
+  float* z;            // [b][m] fp32 split-K accumulator (workspace, zero on entry)
+  uint32_t* counters;  // [m / U] arrival counters (workspace, zero on entry)
+  int Kc;              // columns per chunk (power of two, 64 .. 512)
+  int nchunks;         // ceil(n / Kc)
+  int U;               // rows per finalize unit = max(had_out, 128)
+  float out_mult;      // layer scale x code factor / sqrt(had_out)
+};
+
+struct DecodeArgs {
+  LayerArgs L;
+  int64_t first, count;
+  uint16_t* out;       // [count][256] fp16
+};
+
+struct RhtArgs {
+  const void* in;
+  void* out;
+  int in_f32, out_f32;
+  int64_t rows, n;
+  int block;
+  const uint32_t* signs;
+  int mode;
+  float mult;          // scale / sqrt(block)
+};
+
+struct GemmArgs {
+  LayerArgs L;
+  const uint16_t* xr;  // [b][n] fp16, input RHT already applied
+  float* z;            // [b][m] fp32 accumulator (zero on entry)
+  int b;
+  int ksplit;          // K split factor (fp32 atomics when > 1)
+};
+
+// Workspace layout of qdec_gemv: z then counters, each 256-byte aligned.
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+inline int gemv_unit_rows(int had_out) { return had_out > 128 ? had_out : 128; }
+inline size_t gemv_ws_bytes(int64_t m, int64_t b, int had_out) {
+  return align256((size_t)(b * m) * 4) + align256((size_t)(m / gemv_unit_rows(had_out)) * 4);
+}
+// Workspace layout of qdec_gemm: X' (fp16 [b][n]) then Z (fp32 [b][m]).
+inline size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t b) {
+  return align256((size_t)(b * n) * 2) + align256((size_t)(b * m) * 4);
+}
+
+// Raise a kernel's dynamic-LDS limit to `bytes` when a launch needs more than
+// the default 64 KiB; *have caches the largest limit set so far.
+inline hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes, size_t* have) {
+  if (bytes <= 65536 || bytes <= *have) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) *have = bytes;
+  return e;
+}
+
+// Kernel launchers (return hipSuccess or the launch error).
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
+hipError_t launch_decode_tile(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_rht(const RhtArgs& a, hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+// Output side of the batched path: y = fp16(s_out .* (mult * H z)); z zeroed.
+hipError_t launch_rht_out_f32(float* z, uint16_t* y, int64_t rows, int64_t m, int block,
+                              const uint32_t* signs, float mult, hipStream_t stream);
+
+// Which (code, k) pairs and batch sizes the kernels are built for.
+bool gemv_supported(int code, int k, int b);
+bool decode_supported(int code, int k);
+bool gemm_supported(int code, int k);
+
+}  // namespace qdec

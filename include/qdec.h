@@ -1,0 +1,189 @@
+/*
+ * qdec -- weight-only quantized matrix multiplication on AMD Instinct MI355X
+ * (gfx950): y = W_hat x, with W_hat decoded on the fly from packed low-bit
+ * codes and wrapped in incoherence processing.
+ *
+ * What is computed.  The weight matrix is stored as  W = S_out H_out W_hat
+ * H_in S_in  (randomized Hadamard transform, RHT, on both sides: "QTIP:
+ * Quantization with Trellises and Incoherence Processing", author response
+ * "Incoherence Processing (W2)" and "Bit Accounting (Q2)"; QuIP#, Fig. 2).
+ * A call computes, for every batch row x of X (fp16):
+ *
+ *     x' = (1/sqrt(B_in))  H_{B_in}  (s_in .* x)         block-diagonal over n
+ *     z  = W_hat x'                                        fp32 accumulate
+ *     y  = s_out .* ((1/sqrt(B_out)) H_{B_out} z)         block-diagonal over m
+ *
+ * and rounds y to fp16 (round to nearest even).  H_B is the Sylvester-ordered
+ * Hadamard matrix, H[i][j] = (-1)^popcount(i & j).  Small-batch inference is
+ * memory bound, so the codes are streamed from HBM once and decoded in
+ * registers ("QTIP's contribution (W1)"); the problem is weight-only
+ * quantized MatMul with activations kept in floating point (the quantized
+ * MatMul rate-distortion abstract, "WaterSIC").
+ *
+ * Codes (W_hat = layer_scale x value; see the packed format below):
+ *  - QDEC_CODE_HYB   bitshift trellis, L = 16, V = 2, k bits per weight; the
+ *                    state is hashed, h = s*s + s mod 2^16; Q index bits
+ *                    [15-Q, 15) of h pick a fp16 pair from a 2^Q-entry LUT
+ *                    and bit 15 of h flips the sign of both halves
+ *                    (untitled ALU-op comment, "HYB Uniqueness (Q2)").
+ *  - QDEC_CODE_1MAD  bitshift trellis, L = 16, V = 1; u = 0xEA4F79*s +
+ *                    0xC2AA9973 (mod 2^32); value = fp16(fp32((b0+b1+b2+b3
+ *                    - 510) * fp32(1/sqrt(21845)))), b_i the bytes of u.
+ *  - QDEC_CODE_3INST bitshift trellis, L = 16, V = 1; u = 0xE77B2B*s +
+ *                    0xEACB81D7; u = (u & 0x8FFF8FFF) | 0x30003000; value =
+ *                    fp16(lo16(u) + hi16(u)) with both halves read as fp16.
+ *                    (1MAD/3INST: computed codes with a fixed instruction
+ *                    count and no LUT, built on an LCG -- computed-codes reply
+ *                    and "LCG citation (O2)"; the constants are this
+ *                    library's own.)
+ *  - QDEC_CODE_NUQ   non-uniform scalar quantizer ("Q-Palette" summary):
+ *                    L = k, V = 1, a k-bit index into a 2^k-entry fp16 level
+ *                    table, times an fp16 scale per `group` weights of a row.
+ *  - QDEC_CODE_VQ    2-D vector quantizer ("Q-Palette" summary): L = 2k,
+ *                    V = 2, one 2k-bit index per weight pair into a 2^(2k)
+ *                    table of fp16 pairs.  With L = kV the trellis reduces to
+ *                    plain k-bit V-dim VQ ("Ablations and fast inference").
+ *
+ * Packed format (version 1).
+ *  - W_hat is cut into 16x16 tiles; tile (R, C) covers rows 16R..16R+15 and
+ *    columns 16C..16C+15; weight j of a tile sits at (j >> 4, j & 15).
+ *  - Each tile is a stream of 256*k bits held in 8k little-endian uint32
+ *    words; stream bit p is bit 31 - (p & 31) of word p >> 5 (MSB first).
+ *  - Step t (t = 0 .. 256/V - 1) covers weights tV .. tV+V-1.  Its state is
+ *    the L-bit window starting at stream bit t*kV, read MSB first, wrapping
+ *    around the end of the tile's stream (tail-biting): the last L-kV bits of
+ *    a state are the first L-kV bits of the next ("Figure 2 (Q4)"), so every
+ *    bit string is a valid walk and storage is exactly k bits per weight.
+ *  - Tiles are stored in panels of 8 tile-rows (128 output rows); inside a
+ *    panel, column by column: storage index of tile (R, C) is
+ *      ((R / 8) * (n / 16) + C) * 8 + (R % 8).
+ *  - HYB LUT: 2^Q uint32 words, each an fp16 pair (low half = first weight).
+ *    NUQ table: 2^k uint32 words, fp16 level in the low half.  VQ table:
+ *    2^(2k) uint32 words, fp16 pairs.  NUQ group scales: fp16 [m][n/group].
+ *  - Sign vectors: bit j (bit j & 31 of word j >> 5) set means s[j] = -1;
+ *    NULL means all +1.  They take n + m bits ("Bit Accounting (Q2)").
+ *
+ * Conventions.
+ *  - Every pointer is a DEVICE pointer owned by the caller; the library never
+ *    allocates, frees or synchronizes.  `stream` is a hipStream_t passed as
+ *    void* (NULL = the default stream); every call is asynchronous on it.
+ *  - Argument errors are found on the host before any launch and return a
+ *    negative status with no device work queued.  A failed launch returns
+ *    QDEC_EHIP.  No exception crosses this interface.
+ *  - Workspaces: size them with qdec_workspace_bytes; a workspace must be
+ *    zero-filled before its first use; every successful call leaves the
+ *    parts it relies on zero again, so it can be reused without clearing.
+ *    Calls that share one workspace must be ordered (same stream).
+ *  - x and y must not overlap.  The library is reentrant.
+ */
+#ifndef QDEC_H
+#define QDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QDEC_ABI_VERSION 1u
+
+typedef enum {
+  QDEC_OK = 0,
+  QDEC_EINVAL = -1,      /* bad argument or descriptor                     */
+  QDEC_EUNSUPPORTED = -2,/* valid but not built (a code/k/V/batch combo)    */
+  QDEC_EWORKSPACE = -3,  /* workspace missing, misaligned or too small      */
+  QDEC_EHIP = -4,        /* a HIP runtime call or launch failed             */
+  QDEC_ENODEV = -5       /* no usable gfx950 device                         */
+} qdec_status;
+
+typedef enum {
+  QDEC_CODE_HYB = 1,
+  QDEC_CODE_1MAD = 2,
+  QDEC_CODE_3INST = 3,
+  QDEC_CODE_NUQ = 4,
+  QDEC_CODE_VQ = 5
+} qdec_code;
+
+/* One quantized linear layer.  Plain data; all pointers are device pointers
+ * owned by the caller.  Supported combinations:
+ *   HYB    L = 16, V = 2, k in {2, 3, 4}, Q in [1, 11]
+ *   1MAD   L = 16, V = 1, k in {2, 3, 4}
+ *   3INST  L = 16, V = 1, k in {2, 3, 4}
+ *   NUQ    L = k,  V = 1, k in {2, 3, 4}, group a multiple of 16 dividing n
+ *   VQ     L = 2k, V = 2, k in {2, 3, 4}
+ * m % 128 == 0, n % 16 == 0; had_in (had_out) a power of two dividing n (m),
+ * at most 16384; codes 16-byte aligned.                                      */
+typedef struct qdec_layer {
+  uint32_t abi_version;          /* QDEC_ABI_VERSION                          */
+  int32_t code;                  /* qdec_code                                 */
+  int32_t L, k, V, Q;            /* state bits, bits/weight, weights/step, HYB index bits */
+  int64_t m, n;                  /* W_hat is m (out) x n (in)                 */
+  const uint32_t *codes;         /* m*n*k/32 words, packed format above       */
+  const uint32_t *lut;           /* HYB / NUQ / VQ table (see format), else NULL */
+  const uint16_t *group_scale;   /* NUQ: fp16 [m][n/group]; else NULL         */
+  int32_t group;                 /* NUQ group length along a row; else 0      */
+  float layer_scale;             /* multiplies every decoded value            */
+  const uint32_t *sign_in;       /* n bits or NULL                            */
+  const uint32_t *sign_out;      /* m bits or NULL                            */
+  int32_t had_in, had_out;       /* RHT block sizes (1 = no Hadamard)         */
+} qdec_layer;
+
+/* Operation selector for qdec_workspace_bytes.                               */
+#define QDEC_OP_GEMV 1
+#define QDEC_OP_GEMM 2
+
+/* Bytes of workspace qdec_gemv (op = QDEC_OP_GEMV) or qdec_gemm
+ * (op = QDEC_OP_GEMM) needs for this layer at this batch.  0 on a bad
+ * argument.                                                                  */
+size_t qdec_workspace_bytes(const qdec_layer *layer, int64_t batch, int32_t op);
+
+/* Randomized Hadamard transform of `rows` rows of length n, block-diagonal
+ * with block size `block` (a power of two dividing n, at most 16384):
+ *   mode 0 (input side):  out = scale/sqrt(block) * H (s .* in)
+ *   mode 1 (output side): out = s .* (scale/sqrt(block) * H in)
+ * in/out: row-major, dtype 0 = fp16, 1 = fp32; in-place allowed when the
+ * dtypes match.  signs: n bits or NULL.  ("Incoherence Processing (W2)";
+ * QuIP# abstract and Fig. 2.)                                                 */
+int qdec_rht(const void *in, int32_t in_dtype, void *out, int32_t out_dtype,
+             int64_t rows, int64_t n, int32_t block, const uint32_t *signs,
+             int32_t mode, float scale, void *stream);
+
+/* Fused decode-and-multiply for small batches, one launch:
+ * Y[b][m] = layer(X[b][n]) as defined above, 1 <= batch <= 8, fp16 in/out,
+ * fp32 accumulation.  ws: qdec_workspace_bytes(layer, batch, QDEC_OP_GEMV)
+ * bytes, 256-byte aligned, zero-filled before first use (left zeroed).      */
+int qdec_gemv(const qdec_layer *layer, const uint16_t *x, uint16_t *y,
+              int64_t batch, void *ws, size_t ws_bytes, void *stream);
+
+/* Batched decode-and-multiply (prefill): same result as qdec_gemv for
+ * 1 <= batch <= 256; decoded tiles are staged in LDS and fed to fp16 MFMA
+ * with fp32 accumulation.  Three launches on `stream` (input RHT, GEMM,
+ * output RHT).  ws: qdec_workspace_bytes(layer, batch, QDEC_OP_GEMM) bytes,
+ * 256-byte aligned, zero-filled before first use (left zeroed).             */
+int qdec_gemm(const qdec_layer *layer, const uint16_t *x, uint16_t *y,
+              int64_t batch, void *ws, size_t ws_bytes, void *stream);
+
+/* Decode tiles [first_tile, first_tile + n_tiles) in storage order into
+ * out[n_tiles][256] fp16, tile-local row-major.  Values are the code values
+ * before the layer scale (HYB/VQ pairs, 1MAD/3INST values), and for NUQ
+ * fp16(level * group scale).  Runs the same device decoders as the matmuls;
+ * it is the bit-exact parity surface.                                        */
+int qdec_decode_tile(const qdec_layer *layer, int64_t first_tile,
+                     int64_t n_tiles, uint16_t *out, void *stream);
+
+/* Human-readable name of a status code (static storage).                    */
+const char *qdec_status_string(int status);
+
+/* ABI version of the loaded library (QDEC_ABI_VERSION).                      */
+uint32_t qdec_abi_version(void);
+
+/* Text of the HIP error behind the calling thread's last QDEC_EHIP (static,
+ * per-thread storage; "no error" if there was none).                         */
+const char *qdec_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QDEC_H */

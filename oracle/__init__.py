@@ -79,6 +79,7 @@ def lib():
         L.orc_tile_coords.argtypes = [i64, i64, P, P]
         L.orc_decode_tile.argtypes = [P, i64, i64, P]
         L.orc_decode_dense.argtypes = [P, P]
+        L.orc_decode_storage.argtypes = [P, i64, i64, P]
         L.orc_hadamard_entry.argtypes = [i64, i64]
         L.orc_rht.argtypes = [P, P, i64, i64, i64, P, i32, ctypes.c_double]
         L.orc_forward.argtypes = [P, P, i64, P, P]
@@ -184,10 +185,10 @@ def decode_tile(layer, R: int, C: int) -> np.ndarray:
 
 def decode_tiles_storage(layer, first: int, count: int) -> np.ndarray:
     """Decode tiles by storage index (the order they sit in memory)."""
+    s, keep = _struct(layer)
     out = np.zeros((count, 256), dtype=np.uint16)
-    for i in range(count):
-        R, C = tile_coords(layer.n, first + i)
-        out[i] = decode_tile(layer, R, C)
+    if lib().orc_decode_storage(ctypes.byref(s), first, count, _ptr(out)):
+        raise ValueError("decode_storage: invalid layer or range")
     return out
 
 

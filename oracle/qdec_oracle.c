@@ -327,6 +327,23 @@ int orc_decode_tile(const orc_layer *Lr, int64_t R, int64_t C,
   return orc_tile_values(Lr, R, C, out, NULL);
 }
 
+/* Decode tiles [first, first+count) in storage order (each mapped back to its
+ * grid coordinates by orc_tile_coords) into out[count][256].                 */
+int orc_decode_storage(const orc_layer *Lr, int64_t first, int64_t count,
+                       uint16_t *out) {
+  if (orc_validate(Lr)) return -1;
+  const int64_t total = (Lr->m / 16) * (Lr->n / 16);
+  if (first < 0 || count < 0 || first + count > total) return -1;
+  int bad = 0;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < count; i++) {
+    int64_t R, C;
+    orc_tile_coords(Lr->n, first + i, &R, &C);
+    if (orc_tile_values(Lr, R, C, out + i * 256, NULL)) bad = 1;
+  }
+  return bad ? -1 : 0;
+}
+
 /* Rows [r0, r1) of the effective weight matrix W_hat in fp64 (row-major,
  * (r1-r0) x n): layer scale x exact code value.                              */
 static int orc_decode_rows(const orc_layer *Lr, int64_t r0, int64_t r1,

@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/qdec.h declares, sizes workspaces, and rejects bad
+arguments with a negative status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "qdec.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qdec_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def q():
+    import dequant_matmul_packed_amd as q
+    return q
+
+
+def test_header_functions_exported(q):
+    names = _header_functions()
+    assert set(names) == set(q.EXPORTS)
+    lib = ctypes.CDLL(q.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(q):
+    assert q._lib.qdec_abi_version() == q.QDEC_ABI_VERSION
+    for st in (0, -1, -2, -3, -4, -5):
+        assert q._status_string(st) not in ("", "unknown status")
+    assert q._status_string(7) == "unknown status"
+
+
+FAKE = 0x7F0000000000   # never dereferenced: every case below fails validation
+
+
+def _layer(q, **kw):
+    base = dict(code=q.QDEC_CODE_HYB, L=16, k=2, V=2, Q=9, m=256, n=128, codes=FAKE, lut=FAKE + 4096,
+                group_scale=None, group=0, layer_scale=0.02, sign_in=None, sign_out=None,
+                had_in=128, had_out=256)
+    base.update(kw)
+    return q.Layer(**base)
+
+
+def test_workspace_sizes(q):
+    lay = _layer(q)
+    gv = q.qdec_workspace_bytes(lay, 1, q.QDEC_OP_GEMV)
+    # z: b*m fp32, counters: m / max(had_out, 128), each 256-byte aligned
+    assert gv == 1024 + 256
+    assert q.qdec_workspace_bytes(lay, 8, q.QDEC_OP_GEMV) == 8192 + 256
+    gm = q.qdec_workspace_bytes(lay, 64, q.QDEC_OP_GEMM)
+    assert gm == 64 * 128 * 2 + 64 * 256 * 4
+    assert q.qdec_workspace_bytes(lay, 9, q.QDEC_OP_GEMV) == 0
+    assert q.qdec_workspace_bytes(lay, 0, q.QDEC_OP_GEMM) == 0
+    assert q.qdec_workspace_bytes(lay, 1, 99) == 0
+
+
+BAD_LAYERS = [
+    dict(m=100), dict(n=40), dict(m=0), dict(k=0), dict(k=9), dict(Q=0), dict(V=1), dict(L=12),
+    dict(had_in=3), dict(had_in=256), dict(had_out=512), dict(codes=FAKE + 8), dict(codes=None),
+    dict(lut=None), dict(code=9), dict(code=4, L=3, k=3, V=1, group=128, group_scale=None),
+    dict(code=4, L=3, k=3, V=1, group=24, group_scale=FAKE), dict(code=5, L=6, k=2, V=2),
+    dict(code=2, V=2), dict(layer_scale=float("nan")),
+]
+
+
+@pytest.mark.parametrize("kw", BAD_LAYERS, ids=[str(k) for k in BAD_LAYERS])
+def test_invalid_layers_rejected(q, kw):
+    lay = _layer(q, **kw)
+    d = ctypes.byref(lay.desc())
+    assert q.qdec_workspace_bytes(lay, 1, q.QDEC_OP_GEMV) == 0
+    ws = FAKE + (1 << 20)
+    for fn in ("qdec_gemv", "qdec_gemm"):
+        st = q.raw_status(fn, d, FAKE + (1 << 24), FAKE + (1 << 25), 1, ws, 1 << 20, None)
+        assert st in (q.QDEC_EINVAL, q.QDEC_EUNSUPPORTED), (fn, st)
+    assert q.raw_status("qdec_decode_tile", d, 0, 1, FAKE + (1 << 24), None) in (
+        q.QDEC_EINVAL, q.QDEC_EUNSUPPORTED)
+
+
+def test_unsupported_but_valid(q):
+    lay = _layer(q, k=5)
+    d = ctypes.byref(lay.desc())
+    assert q.raw_status("qdec_decode_tile", d, 0, 1, FAKE + (1 << 24), None) == q.QDEC_EUNSUPPORTED
+    lay = _layer(q, Q=13)
+    d = ctypes.byref(lay.desc())
+    assert q.raw_status("qdec_decode_tile", d, 0, 1, FAKE + (1 << 24), None) == q.QDEC_EUNSUPPORTED
+
+
+def test_call_argument_errors(q):
+    lay = _layer(q)
+    d = ctypes.byref(lay.desc())
+    X, Y, WS = FAKE + (1 << 24), FAKE + (1 << 25), FAKE + (1 << 26)
+    need = q.qdec_workspace_bytes(lay, 1, q.QDEC_OP_GEMV)
+    E = q.QDEC_EINVAL
+    assert q.raw_status("qdec_gemv", d, None, Y, 1, WS, need, None) == E
+    assert q.raw_status("qdec_gemv", d, X, None, 1, WS, need, None) == E
+    assert q.raw_status("qdec_gemv", d, X + 2, Y, 1, WS, need, None) == E         # misaligned x
+    assert q.raw_status("qdec_gemv", d, X, Y, 0, WS, need, None) == E
+    assert q.raw_status("qdec_gemv", d, X, Y, 9, WS, need, None) == q.QDEC_EUNSUPPORTED
+    assert q.raw_status("qdec_gemv", d, X, X + 64, 1, WS, need, None) == E        # x and y overlap
+    assert q.raw_status("qdec_gemv", d, X, Y, 1, None, need, None) == q.QDEC_EWORKSPACE
+    assert q.raw_status("qdec_gemv", d, X, Y, 1, WS, need - 4, None) == q.QDEC_EWORKSPACE
+    assert q.raw_status("qdec_gemv", d, X, Y, 1, WS + 16, need, None) == q.QDEC_EWORKSPACE
+    assert q.raw_status("qdec_gemv", d, X, Y, 1, X, need, None) == E              # ws overlaps x
+    assert q.raw_status("qdec_gemm", d, X, Y, 257, WS, 1 << 30, None) == q.QDEC_EUNSUPPORTED
+    ntiles = (256 // 16) * (128 // 16)
+    assert q.raw_status("qdec_decode_tile", d, -1, 1, Y, None) == E
+    assert q.raw_status("qdec_decode_tile", d, ntiles - 1, 2, Y, None) == E
+    assert q.raw_status("qdec_decode_tile", d, 0, 1, None, None) == E
+    assert q.raw_status("qdec_decode_tile", d, 0, 0, None, None) == q.QDEC_OK    # nothing to do
+    R = q.raw_status
+    assert R("qdec_rht", X, 0, Y, 0, 1, 96, 64, None, 0, ctypes.c_float(1.0), None) == E  # block
+    assert R("qdec_rht", X, 2, Y, 0, 1, 64, 64, None, 0, ctypes.c_float(1.0), None) == E  # dtype
+    assert R("qdec_rht", X, 0, Y, 0, 1, 64, 64, None, 2, ctypes.c_float(1.0), None) == E  # mode
+    assert R("qdec_rht", X, 0, X + 2, 0, 1, 64, 64, None, 0, ctypes.c_float(1.0), None) == E
+    assert R("qdec_rht", X, 0, X, 1, 1, 64, 64, None, 0, ctypes.c_float(1.0), None) == E
+    assert R("qdec_rht", X, 0, Y, 0, 1, 1 << 15, 1 << 15, None, 0, ctypes.c_float(1.0),
+             None) == q.QDEC_EUNSUPPORTED
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_has_gpu(), reason="a valid call would launch on a real device")
+def test_valid_call_without_device_reports_enodev(q):
+    lay = _layer(q)
+    d = ctypes.byref(lay.desc())
+    need = q.qdec_workspace_bytes(lay, 1, q.QDEC_OP_GEMV)
+    st = q.raw_status("qdec_gemv", d, FAKE + (1 << 24), FAKE + (1 << 25), 1, FAKE + (1 << 26), need, None)
+    assert st == q.QDEC_ENODEV

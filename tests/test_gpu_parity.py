@@ -1,0 +1,292 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+the same seeded inputs.
+
+Bars: decoded weights bit-exact (qdec_decode_tile, every tile); outputs of
+qdec_rht / qdec_gemv / qdec_gemm within ||y - y_ref|| / ||y_ref|| <= 2e-3 per
+batch column (fp32 accumulation, fp16 in and out).  Small layers are checked
+whole (several tiles, ragged chunking, odd shapes); the full-size workloads
+are checked on every tile for the decode and on sampled output blocks (whole
+Hadamard blocks the oracle computes from their own rows) for the matmuls.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 2e-3
+
+
+def _say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def q(dev):
+    import dequant_matmul_packed_amd as q
+    return q
+
+
+def _f16_tensor(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+
+def _to_f64(t):
+    import torch
+    return t.cpu().view(torch.int16).numpy().view(np.float16).astype(np.float64)
+
+
+def _rel(y, ref):
+    y = np.atleast_2d(y)
+    ref = np.atleast_2d(ref)
+    errs = []
+    for c in range(ref.shape[0]):
+        d = np.linalg.norm(ref[c])
+        errs.append(np.linalg.norm(y[c] - ref[c]) / (d if d > 0 else 1.0))
+    return max(errs)
+
+
+# ---------------------------------------------------------------------------
+# decode: bit-exact
+
+DECODE_CASES = [
+    (synth.HYB, 2), (synth.HYB, 3), (synth.HYB, 4),
+    (synth.MAD1, 2), (synth.MAD1, 3), (synth.MAD1, 4),
+    (synth.INST3, 2), (synth.INST3, 3), (synth.INST3, 4),
+    (synth.NUQ, 3), (synth.VQ, 2), (synth.VQ, 3), (synth.VQ, 4),
+]
+
+
+@pytest.mark.parametrize("code,k", DECODE_CASES)
+def test_decode_tile_bit_exact_small(q, dev, code, k):
+    import torch
+    m, n = 384, 160 if code != synth.NUQ else 256
+    _say("decode small", synth.CODE_NAMES[code], k, m, n)
+    host = synth.make_layer(code, m, n, k, tag="dec%d_%d" % (code, k))
+    lay = q.upload_layer(host, dev)
+    want = oracle.decode_tiles_storage(host, 0, host.n_tiles)
+    out = torch.zeros((host.n_tiles, 256), dtype=torch.int16, device=dev)
+    q.qdec_decode_tile(lay, 0, host.n_tiles, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    # a sub-range that is not a multiple of the 32 tiles of a workgroup
+    first, cnt = 7, 45
+    out2 = torch.zeros((cnt, 256), dtype=torch.int16, device=dev)
+    q.qdec_decode_tile(lay, first, cnt, out2)
+    torch.cuda.synchronize()
+    assert np.array_equal(out2.cpu().numpy().view(np.uint16), want[first:first + cnt])
+
+
+def _full_layers():
+    out = []
+    for wl in synth.WORKLOADS.values():
+        for spec in wl.layers:
+            out.append((wl.name, spec))
+    return out
+
+
+@pytest.mark.parametrize("wname,spec", _full_layers(), ids=[w + "/" + s.name for w, s in _full_layers()])
+def test_decode_tile_bit_exact_full_size(q, dev, wname, spec):
+    """Every tile of every layer of the five workloads."""
+    import torch
+    _say("decode full", wname, spec.name, spec.m, spec.n, spec.k)
+    host = spec.build(wname)
+    lay = q.upload_layer(host, dev)
+    want = oracle.decode_tiles_storage(host, 0, host.n_tiles)
+    out = torch.empty((host.n_tiles, 256), dtype=torch.int16, device=dev)
+    q.qdec_decode_tile(lay, 0, host.n_tiles, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    bad = np.nonzero((got != want).any(1))[0]
+    assert bad.size == 0, "first mismatching tiles %s" % bad[:8]
+
+
+# ---------------------------------------------------------------------------
+# RHT
+
+@pytest.mark.parametrize("B,n,rows", [(1, 64, 3), (16, 592, 2), (256, 1024, 5), (4096, 4096, 2),
+                                      (2048, 14336, 1), (8192, 8192, 2), (16384, 16384, 1)])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_rht_matches_oracle(q, dev, B, n, rows, mode):
+    import torch
+    _say("rht", B, n, rows, mode)
+    rng = synth.rng_for("rht", B, n, mode)
+    x16 = synth.normal_f16(rng, (rows, n))
+    sg = synth.sign_words(rng, n)
+    xt = _f16_tensor(x16, dev)
+    st = torch.from_numpy(sg.view(np.int32)).to(dev)
+    ref = oracle.rht(x16.view(np.float16).astype(np.float64), B, sg, mode=mode, scale=0.5)
+    out32 = torch.empty((rows, n), dtype=torch.float32, device=dev)
+    q.qdec_rht(xt, 0, out32, 1, rows, n, B, st, mode, 0.5)
+    out16 = torch.empty((rows, n), dtype=torch.int16, device=dev)
+    q.qdec_rht(xt, 0, out16, 0, rows, n, B, st, mode, 0.5)
+    # fp32 in place, back to the input
+    inplace = out32.clone()
+    q.qdec_rht(inplace, 1, inplace, 1, rows, n, B, st, 1 - mode, 2.0)
+    torch.cuda.synchronize()
+    assert _rel(out32.cpu().numpy().astype(np.float64), ref) < 1e-5
+    assert _rel(_to_f64(out16), ref) < REL_TOL
+    back = inplace.cpu().numpy().astype(np.float64)
+    assert _rel(back, x16.view(np.float16).astype(np.float64)) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# GEMV (fused, batch <= 8)
+
+GEMV_SHAPES = [(256, 96), (384, 592), (1024, 1024), (128, 16), (640, 2048)]
+
+
+@pytest.mark.parametrize("code,k", [(synth.HYB, 2), (synth.HYB, 3), (synth.MAD1, 2), (synth.MAD1, 4),
+                                    (synth.INST3, 3), (synth.NUQ, 3), (synth.VQ, 4), (synth.HYB, 4),
+                                    (synth.INST3, 2), (synth.MAD1, 3)])
+@pytest.mark.parametrize("b", [1, 3, 8])
+def test_gemv_small_matches_oracle(q, dev, code, k, b):
+    import torch
+    for (m, n) in GEMV_SHAPES:
+        if code == synth.NUQ and n % 128:
+            continue
+        _say("gemv small", synth.CODE_NAMES[code], k, b, m, n)
+        host = synth.make_layer(code, m, n, k, tag="gv%d_%d_%d_%d" % (code, k, m, n))
+        x16 = synth.activations("gvx%d" % n, b, n)
+        ref = oracle.forward(host, x16)
+        lay = q.upload_layer(host, dev)
+        y = q.gemv(lay, _f16_tensor(x16, dev))
+        torch.cuda.synchronize()
+        err = _rel(_to_f64(y), ref)
+        assert err < REL_TOL, (m, n, err)
+
+
+def test_gemv_edge_cases(q, dev):
+    import torch
+    import dataclasses
+    m, n = 512, 256
+    host = synth.make_layer(synth.HYB, m, n, 2, tag="edge")
+    x16 = synth.activations("edgex", 2, n)
+    # no Hadamard at all (isolates the decoder), no signs, small blocks
+    for kw in (dict(had_in=1, had_out=1), dict(sign_in=None, sign_out=None),
+               dict(had_in=16, had_out=128), dict(had_in=64, had_out=512)):
+        h2 = dataclasses.replace(host, **kw)
+        _say("gemv edge", kw)
+        lay = q.upload_layer(h2, dev)
+        y = q.gemv(lay, _f16_tensor(x16, dev))
+        torch.cuda.synchronize()
+        assert _rel(_to_f64(y), oracle.forward(h2, x16)) < REL_TOL, kw
+    # zero input gives exactly zero output
+    lay = q.upload_layer(host, dev)
+    z = q.gemv(lay, torch.zeros((1, n), dtype=torch.float16, device=dev))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(z).item() == 0
+    # a workspace is left clean: reuse it for many calls, results stay right
+    ws = q.workspace(lay, 2, q.QDEC_OP_GEMV, dev)
+    ref = oracle.forward(host, x16)
+    xt = _f16_tensor(x16, dev)
+    for rep in range(5):
+        y = q.gemv(lay, xt, ws=ws)
+    torch.cuda.synchronize()
+    assert _rel(_to_f64(y), ref) < REL_TOL
+    assert torch.count_nonzero(ws).item() == 0
+
+
+def _full_gemv_cases():
+    cases = []
+    for wname in ("hyb4096", "computed4096", "llama3_8b_layer", "down_nuq", "down_vq"):
+        wl = synth.WORKLOADS[wname]
+        for spec in wl.layers:
+            for b in wl.batches:
+                cases.append((wname, spec, b))
+    return cases
+
+
+@pytest.mark.parametrize("wname,spec,b", _full_gemv_cases(),
+                         ids=["%s/%s/b%d" % (w, s.name, b) for w, s, b in _full_gemv_cases()])
+def test_gemv_full_size_sampled(q, dev, wname, spec, b):
+    """Full-size layer in the launch configuration the bench times; the
+    oracle computes the first and last output Hadamard blocks for the first
+    and last batch column from their own rows."""
+    import torch
+    _say("gemv full", wname, spec.name, b)
+    host = spec.build(wname)
+    x16 = synth.activations(wname + "/x", b, spec.n)
+    lay = q.upload_layer(host, dev)
+    y = _to_f64(q.gemv(lay, _f16_tensor(x16, dev)))
+    torch.cuda.synchronize()
+    nblk = host.m // host.had_out
+    cols = sorted({0, b - 1})
+    for blk in sorted({0, nblk - 1}):
+        ref = oracle.forward_block(host, x16, cols, blk)
+        got = y[cols][:, blk * host.had_out:(blk + 1) * host.had_out]
+        err = _rel(got, ref)
+        assert err < REL_TOL, (blk, err)
+
+
+# ---------------------------------------------------------------------------
+# GEMM (MFMA path)
+
+@pytest.mark.parametrize("code,k,m,n,b", [
+    (synth.HYB, 3, 256, 512, 64), (synth.HYB, 2, 384, 592, 5), (synth.HYB, 3, 128, 80, 70),
+    (synth.MAD1, 2, 256, 256, 64), (synth.INST3, 4, 256, 256, 33), (synth.NUQ, 3, 256, 512, 64),
+    (synth.VQ, 4, 256, 256, 64), (synth.HYB, 4, 1024, 1024, 64)])
+def test_gemm_small_matches_oracle(q, dev, code, k, m, n, b):
+    import torch
+    _say("gemm small", synth.CODE_NAMES[code], k, m, n, b)
+    host = synth.make_layer(code, m, n, k, tag="gm%d_%d_%d_%d" % (code, k, m, n))
+    x16 = synth.activations("gmx%d_%d" % (n, b), b, n)
+    ref = oracle.forward(host, x16)
+    lay = q.upload_layer(host, dev)
+    ws = q.workspace(lay, b, q.QDEC_OP_GEMM, dev)
+    xt = _f16_tensor(x16, dev)
+    y = q.gemm(lay, xt, ws=ws)
+    torch.cuda.synchronize()
+    assert _rel(_to_f64(y), ref) < REL_TOL
+    # the workspace accumulator is left zeroed: a second call agrees
+    y2 = q.gemm(lay, xt, ws=ws)
+    torch.cuda.synchronize()
+    assert _rel(_to_f64(y2), ref) < REL_TOL
+
+
+def test_gemm_full_size_sampled(q, dev):
+    """70B-class up-projection, X 64 x 8192: sampled batch columns and
+    output blocks against the oracle."""
+    import torch
+    wl = synth.WORKLOADS["up70b_prefill"]
+    spec = wl.layers[0]
+    b = wl.batches[0]
+    _say("gemm full", spec.m, spec.n, b)
+    host = spec.build(wl.name)
+    x16 = synth.activations(wl.name + "/x", b, spec.n)
+    lay = q.upload_layer(host, dev)
+    y = _to_f64(q.gemm(lay, _f16_tensor(x16, dev)))
+    torch.cuda.synchronize()
+    cols = [0, 31, 63]
+    for blk in (0, host.m // host.had_out - 1):
+        ref = oracle.forward_block(host, x16, cols, blk)
+        got = y[cols][:, blk * host.had_out:(blk + 1) * host.had_out]
+        assert _rel(got, ref) < REL_TOL, blk
+
+
+def test_gemm_agrees_with_gemv(q, dev):
+    import torch
+    host = synth.make_layer(synth.HYB, 512, 1024, 2, tag="gmgv")
+    x16 = synth.activations("gmgvx", 8, 1024)
+    lay = q.upload_layer(host, dev)
+    xt = _f16_tensor(x16, dev)
+    a = _to_f64(q.gemv(lay, xt))
+    g = _to_f64(q.gemm(lay, xt))
+    torch.cuda.synchronize()
+    assert _rel(g, a) < REL_TOL
