@@ -67,6 +67,21 @@ class Launch:
             raise RuntimeError("launch failed with status %d" % st)
 
 
+class LazyLaunch(Launch):
+    """A Launch that picks up the current stream at call time (so it can be
+    captured into a graph on torch's capture stream)."""
+
+    def __init__(self, q, fn, layer, x, y, b, ws):
+        super().__init__(q, fn, layer, x, y, b, ws, None)
+
+    def __call__(self):
+        import torch
+        args = self.args[:-1] + (torch.cuda.current_stream().cuda_stream,)
+        st = self.fn(*args)
+        if st != 0:
+            raise RuntimeError("launch failed with status %d" % st)
+
+
 def algorithmic_bytes(m, n, k, b, lut_bytes=0, gscale_bytes=0):
     """Minimal HBM bytes of one call: packed codes, fp16 x and y, the two sign
     vectors, and the code tables."""
@@ -135,45 +150,69 @@ def main():
         keep.append(pool)
         ws = q.workspace(base, 1, q.QDEC_OP_GEMV, dev)
         y = torch.empty((1, s.m), dtype=torch.float16, device=dev)
-        launches = [Launch(q, "qdec_gemv", L, x, y, 1, ws, stream) for L in layers]
-        variants.append(dict(spec=s, launches=launches, y=y, ws=ws,
+        launches = [LazyLaunch(q, "qdec_gemv", L, x, y, 1, ws) for L in layers]
+        variants.append(dict(spec=s, launches=launches, layers=layers, y=y, ws=ws,
                              bytes=algorithmic_bytes(s.m, s.n, s.k, 1)))
     torch.cuda.synchronize()
 
-    def step(i):
-        for v in variants:
-            v["launches"][i % P]()
+    # One step = the six fused GEMVs on one pool slot.  Launches of a few
+    # microseconds are host-bound when issued one by one, so each slot's step
+    # is captured once in a HIP graph and replayed.  The dominant variant is
+    # kept out of the graphs and launched eagerly between two HIP events
+    # while the GPU is still busy with the rest of the step: the events then
+    # bracket exactly that call's kernels on the stream it runs on.
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    for v in variants:          # warm the launch paths once, eagerly
+        v["launches"][0]()
+    torch.cuda.synchronize()
+    per_variant = {}
+    for v in variants:          # per-variant GEMV time, graph of 20 calls
+        g = capture(lambda v=v: [v["launches"][j % P]() for j in range(20)])
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(5):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per_variant[v["spec"].name] = e0.elapsed_time(e1) * 1e3 / 100
+        del g
+    dom = max(variants, key=lambda v: per_variant[v["spec"].name])
+    log("per-variant us per GEMV (graph replay):", {k: round(t, 2) for k, t in per_variant.items()})
+    others = [v for v in variants if v is not dom]
+    graphs = [capture(lambda i=i: [v["launches"][i]() for v in others]) for i in range(P)] if others else None
+    dom_launch = [Launch(q, "qdec_gemv", L, x, dom["y"], 1, dom["ws"], stream)
+                  for L in dom["layers"]]
+
+    def step(i, evs=None):
+        if graphs is not None:
+            graphs[i % P].replay()
+        if evs is not None:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            dom_launch[i % P]()
+            b.record()
+            evs.append((a, b))
+        else:
+            dom_launch[i % P]()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # dominant kernel: the variant with the longest average launch
-    per_variant = {}
-    for v in variants:
-        cnt = [0]
-
-        def one(v=v, cnt=cnt):
-            v["launches"][cnt[0] % P]()
-            cnt[0] += 1
-        per_variant[v["spec"].name] = time_events(torch, one, 50)
-    dom = max(variants, key=lambda v: per_variant[v["spec"].name])
-    log("per-variant kernel us:", {k: round(t, 2) for k, t in per_variant.items()})
 
     # ---- timed region: exactly `steps` steps ---------------------------------
     dom_events = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        for v in variants:
-            if v is dom:
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record()
-                v["launches"][(i + args.warmup) % P]()
-                b.record()
-                dom_events.append((a, b))
-            else:
-                v["launches"][(i + args.warmup) % P]()
+        step(i + args.warmup, dom_events)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
@@ -181,7 +220,7 @@ def main():
     gbs = step_bytes * args.steps / elapsed / 1e9
     dom_us = sum(a.elapsed_time(b) for a, b in dom_events) / len(dom_events) * 1e3
     dom_gbs = dom["bytes"] / (dom_us * 1e-6) / 1e9
-    log("timed %d steps in %.3f s: %.1f GB/s packed, %.2f us/layer; dominant %s %.2f us"
+    log("timed %d steps in %.4f s: %.1f GB/s packed, %.2f us/layer; dominant %s %.2f us"
         % (args.steps, elapsed, gbs, ms_per_step * 1e3 / len(variants), dom["spec"].name, dom_us))
 
     # sanity: outputs are finite
@@ -215,7 +254,7 @@ def main():
                                "RHT 4096/4096, batch 1 (six fused GEMVs per step)",
                    "global_batch": 1, "layers_per_step": len(variants),
                    "packed_bytes_per_step": step_bytes, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<%s, k=%d, b=1>"
+        "roofline": {"bound": "hbm", "kernel": "qdec_gemv %s k=%d b=1 (gemv_kernel + gemv_finish_kernel)"
                      % (synth.CODE_NAMES[dom["spec"].code], dom["spec"].k),
                      "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
@@ -246,18 +285,27 @@ def bench_llama_layer(q, torch, dev, stream):
                 x[s.n] = torch.from_numpy(synth.activations("bench/llama/x", b, s.n).view(np.int16)).to(dev)
             ws = q.workspace(base, b, q.QDEC_OP_GEMV, dev)
             y = torch.empty((b, s.m), dtype=torch.float16, device=dev)
-            calls.append([Launch(q, "qdec_gemv", L, x[s.n], y, b, ws, stream) for L in layers])
-        for i in range(10):
-            for c in calls:
-                c[i % P]()
+            calls.append([LazyLaunch(q, "qdec_gemv", L, x[s.n], y, b, ws) for L in layers])
+        for c in calls:
+            c[0]()
+        torch.cuda.synchronize()
+        graphs = []
+        for i in range(P):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in calls:
+                    c[i]()
+            graphs.append(g)
+        for i in range(P):
+            graphs[i].replay()
         torch.cuda.synchronize()
         reps = 60
         t0 = time.perf_counter()
         for i in range(reps):
-            for c in calls:
-                c[i % P]()
+            graphs[i % P].replay()
         torch.cuda.synchronize()
         us = (time.perf_counter() - t0) / reps * 1e6
+        del graphs
         out["llama3_8b_layer_b%d" % b] = {"us_per_layer": round(us, 2),
                                           "packed_GBps": round(layer_bytes / (us * 1e-6) / 1e9, 1)}
         log("llama layer b=%d: %.2f us/layer" % (b, us))
@@ -279,16 +327,23 @@ def bench_gemm(q, torch, dev, stream):
     x = torch.from_numpy(synth.activations("bench/up70b/x", b, s.n).view(np.int16)).to(dev)
     ws = q.workspace(base, b, q.QDEC_OP_GEMM, dev)
     y = torch.empty((b, s.m), dtype=torch.float16, device=dev)
-    calls = [Launch(q, "qdec_gemm", L, x, y, b, ws, stream) for L in layers]
-    for i in range(5):
-        calls[i % P]()
+    calls = [LazyLaunch(q, "qdec_gemm", L, x, y, b, ws) for L in layers]
+    calls[0]()
     torch.cuda.synchronize()
-    cnt = [0]
-
-    def one():
-        calls[cnt[0] % P]()
-        cnt[0] += 1
-    us = time_events(torch, one, 30)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(8):
+            calls[i % P]()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for r in range(4):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 32
+    del g
     flops = 2.0 * s.m * s.n * b
     tf = flops / (us * 1e-6) / 1e12
     log("gemm b=64: %.1f us, %.1f TFLOP/s" % (us, tf))

@@ -3,6 +3,7 @@
 // is rejected here, on the host, before any device work is queued.
 #include <math.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "qdec.h"
@@ -124,17 +125,37 @@ int status_of(hipError_t e) {
   return QDEC_EHIP;
 }
 
-// Input-chunk width of the fused GEMV: enough (panel, chunk) workgroups to
-// cover the 256 CUs several times, chunks a power of two in [64, 512].
-int gemv_chunk(int64_t m, int64_t n) {
+}  // namespace
+
+namespace qdec {
+// Tuning override for measurements: QDEC_GEMV_RHT=1 computes x' with the RHT
+// kernel before the GEMV instead of inside every GEMV workgroup.
+bool gemv_separate_rht() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("QDEC_GEMV_RHT");
+    v = (e && atoi(e) == 1) ? 1 : 0;
+  }
+  return v == 1;
+}
+
+int gemv_chunk(int64_t m, int64_t n, int64_t b) {
+  static int forced = -1;
+  if (forced < 0) {
+    // tuning override for measurements: QDEC_GEMV_KC = 64 .. 512
+    const char* e = getenv("QDEC_GEMV_KC");
+    const int v = e ? atoi(e) : 0;
+    forced = (v >= 64 && v <= 512 && (v & (v - 1)) == 0) ? v : 0;
+  }
+  if (forced > 0) return forced;
+  (void)b;
   const int64_t npanels = m / 128;
-  int64_t want = (n * npanels) / 1024;
+  const int64_t want = (n * npanels) / 1024;
   int kc = 64;
   while (kc < 512 && kc * 2 <= want) kc *= 2;
   return kc;
 }
-
-}  // namespace
+}  // namespace qdec
 
 extern "C" {
 
@@ -159,7 +180,7 @@ size_t qdec_workspace_bytes(const qdec_layer* layer, int64_t batch, int32_t op) 
   if (check_layer(layer, &L) != QDEC_OK) return 0;
   if (op == QDEC_OP_GEMV) {
     if (batch < 1 || batch > 8) return 0;
-    return gemv_ws_bytes(L.m, batch, L.had_out);
+    return gemv_ws_layout(L.m, L.n, batch).total;
   }
   if (op == QDEC_OP_GEMM) {
     if (batch < 1 || batch > 256) return 0;
@@ -206,7 +227,9 @@ int qdec_gemv(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
   if (batch < 1) return QDEC_EINVAL;
   if (batch > 8) return QDEC_EUNSUPPORTED;
   if (overlap(x, (size_t)(batch * L.n) * 2, y, (size_t)(batch * L.m) * 2)) return QDEC_EINVAL;
-  const size_t need = gemv_ws_bytes(L.m, batch, L.had_out);
+  const int Kc = gemv_chunk(L.m, L.n, batch);
+  const GemvWs wl = gemv_ws_layout(L.m, L.n, batch);
+  const size_t need = wl.total;
   if (!ws || !aligned(ws, 256) || ws_bytes < need) return QDEC_EWORKSPACE;
   if (overlap(ws, need, x, (size_t)(batch * L.n) * 2) || overlap(ws, need, y, (size_t)(batch * L.m) * 2))
     return QDEC_EINVAL;
@@ -217,15 +240,33 @@ int qdec_gemv(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
   a.x = x;
   a.y = y;
   a.b = (int)batch;
-  a.z = (float*)ws;
-  a.counters = (uint32_t*)((char*)ws + align256((size_t)(batch * L.m) * 4));
-  a.Kc = gemv_chunk(L.m, L.n);
+  a.z = (float*)((char*)ws + wl.z);
+  a.xr = nullptr;
+  a.Kc = Kc;
   a.nchunks = (int)((L.n + a.Kc - 1) / a.Kc);
   a.U = gemv_unit_rows(L.had_out);
   const double factor = L.code == QDEC_CODE_1MAD ? 1.0 / sqrt(21845.0) : 1.0;
   // the 1MAD matmul path multiplies by the fp32 normaliser, as the decode does
   const double f32norm = (double)(float)factor;
   a.out_mult = (float)((double)L.scale * f32norm / sqrt((double)L.had_out));
+  if (gemv_separate_rht()) {
+    // x' = RHT_in(x) by the RHT kernel into the workspace, then the GEMV
+    uint16_t* xr = (uint16_t*)((char*)ws + wl.xr);
+    RhtArgs r;
+    r.in = x;
+    r.out = xr;
+    r.in_f32 = 0;
+    r.out_f32 = 0;
+    r.rows = batch;
+    r.n = L.n;
+    r.block = L.had_in;
+    r.signs = L.sign_in;
+    r.mode = 0;
+    r.mult = (float)(1.0 / sqrt((double)L.had_in));
+    const hipError_t e = launch_rht(r, (hipStream_t)stream);
+    if (e != hipSuccess) return status_of(e);
+    a.xr = xr;
+  }
   return status_of(launch_gemv(a, (hipStream_t)stream));
 }
 

@@ -12,10 +12,14 @@
 //   4. stream the tiles: each 8-lane group decodes one 16x16 tile per step,
 //      each lane 32 weights of two rows, accumulating with v_dot2_f32_f16;
 //   5. reduce the four waves in LDS and add the panel's partial sums into
-//      the fp32 workspace with device-scope atomics;
-//   6. count arrivals per output unit (max(B_out, 128) rows); the last
-//      workgroup of a unit applies the output RHT, the scale and the signs,
-//      writes fp16 y, and re-zeroes the workspace it used.
+//      the fp32 accumulator z with device-scope atomic adds.
+// A second, small kernel (gemv_finish_kernel) then applies the output RHT,
+// the scale and the signs to z, writes fp16 y and re-zeroes z.  Splitting
+// there keeps every cross-workgroup dependency at a kernel boundary: an
+// in-kernel "last workgroup finishes" scheme needs an agent-scope release
+// (an L2 write-back) in every workgroup, which measured far more expensive
+// than the second launch.  With a precomputed x' (args.xr, written by the
+// RHT kernel) step 2 is replaced by a plain load of the chunk's slice.
 // Small-batch inference is memory bound ("QTIP: Quantization with Trellises
 // and Incoherence Processing", "QTIP's contribution (W1)"), so the codes are
 // read from HBM exactly once and every other operand stays on chip.
@@ -48,13 +52,12 @@ __host__ __device__ constexpr int gemv_table_words(int Q) {
 template <int CODE, int K, int NB>
 __host__ __device__ inline size_t gemv_regA_bytes(int Q, int Kc, int U) {
   size_t tab = (size_t)gemv_table_words<CODE, K>(Q) * 4;
-  size_t rht = (size_t)(GEMV_THREADS * 8 + NB * Kc) * 4;
-  size_t red = (size_t)4 * 128 * NB * 4;
-  size_t fin = (size_t)U * 4;
+  size_t rht = (size_t)(GEMV_THREADS * 8 + NB * padded_words(Kc)) * 4;
+  size_t red = ((size_t)4 * 128 * NB + padded_words(128 * NB)) * 4;
+  (void)U;
   size_t r = tab;
   if (rht > r) r = rht;
   if (red > r) r = red;
-  if (fin > r) r = fin;
   return (r + 15) & ~(size_t)15;
 }
 
@@ -102,14 +105,40 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   tc_count = tc_count < 0 ? 0 : (tc_count > tpw ? tpw : tc_count);
 
   // LDS carve-up
-  const int U = a.U;
-  const size_t regA_words = gemv_regA_bytes<CODE, K, NB>(a.L.Q, Kc, U) / 4;
+  const size_t regA_words = gemv_regA_bytes<CODE, K, NB>(a.L.Q, Kc, a.U) / 4;
   uint32_t* regA = smem;
   float* fA = reinterpret_cast<float*>(smem);
   uint32_t* xh = smem + regA_words;                 // [NB][Kc/2] fp16 pairs
   uint32_t* xd = xh + (size_t)NB * Kc / 2;           // [NB][Kc] duplicated (3INST)
   __shared__ float sx_sum[NB];
-  __shared__ int last_flag;
+
+  // ---- 0. activations of the first batch column for the input RHT: issued
+  // first, so the RHT's wait on them does not also wait on the (older,
+  // slower) code loads -- vector-memory counters drain in issue order.
+  const int Bi = a.L.had_in;
+  const int arows = Kc < Bi ? Bi / Kc : 1;
+  const int64_t rbase = Kc < Bi ? (c0 / Bi) * Bi : c0;
+  const int jhi = Kc < Bi ? (int)((c0 - rbase) / Kc) : 0;
+  const int CG = kcols >> 3;                       // groups of 8 columns
+  const int RG = CG >= GEMV_THREADS ? 1 : GEMV_THREADS / CG;
+  constexpr int MAXR = 8;   // arows / RG <= 8 (B_in <= 16384, RG = 2048 / kcols)
+  const uint32_t* __restrict__ sgn = a.L.sign_in;
+  uint4 xraw[MAXR];
+  uint32_t xsb[MAXR];
+  auto load_x_rows = [&](int c, int idx) {
+    const int cg = idx % CG, rg = idx / CG;
+    const uint16_t* __restrict__ xc = a.x + (int64_t)c * n;
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+      const int ih = rg + r * RG;
+      const int ihc = ih < arows ? ih : 0;   // row 0 is always in bounds
+      const int64_t col = rbase + (int64_t)ihc * Kc + cg * 8;
+      xraw[r] = *reinterpret_cast<const uint4*>(xc + col);
+      xsb[r] = sgn ? (sgn[col >> 5] >> (col & 31)) : 0u;
+    }
+  };
+  const bool x_hoisted = !a.xr && tid < CG * RG;
+  if (x_hoisted) load_x_rows(0, tid);
 
   // ---- 1. issue the code loads ------------------------------------------
   const int64_t tiles_row = n >> 4;
@@ -124,36 +153,44 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
     }
   }
 
-  // ---- 2. input RHT of the chunk ------------------------------------------
-  {
-    const int Bi = a.L.had_in;
-    const int arows = Kc < Bi ? Bi / Kc : 1;
-    const int64_t base = Kc < Bi ? (c0 / Bi) * Bi : c0;
-    const int jhi = Kc < Bi ? (int)((c0 - base) / Kc) : 0;
-    const int CG = kcols >> 3;                       // groups of 8 columns
-    const int RG = CG >= GEMV_THREADS ? 1 : GEMV_THREADS / CG;
+  // ---- 2. input RHT of the chunk (or load the precomputed x') -------------
+  if (a.xr) {
+    for (int idx = tid; idx < NB * (Kc / 2); idx += GEMV_THREADS) {
+      const int c = idx / (Kc / 2), p = idx % (Kc / 2);
+      uint32_t v = 0;
+      if (2 * p < kcols && c < a.b)
+        v = *reinterpret_cast<const uint32_t*>(a.xr + (int64_t)c * n + c0 + 2 * p);
+      xh[idx] = v;
+      if constexpr (CODE == INST3) {
+        xd[c * Kc + 2 * p] = (v & 0xFFFFu) * 0x10001u;
+        xd[c * Kc + 2 * p + 1] = (v >> 16) * 0x10001u;
+      }
+    }
+    __syncthreads();
+  } else {
     float* red = fA;                                 // [RG][kcols]
-    float* u = fA + GEMV_THREADS * 8;                // [NB][Kc]
-    const uint32_t* __restrict__ sgn = a.L.sign_in;
+    float* u = fA + GEMV_THREADS * 8;                // [NB][padded Kc]
+    const int ustride = padded_words(Kc);
     for (int c = 0; c < NB; ++c) {
       if (c < a.b) {
-        const uint16_t* __restrict__ xc = a.x + (int64_t)c * n;
         for (int idx = tid; idx < CG * RG; idx += GEMV_THREADS) {
-          const int cg = idx % CG, rg = idx / CG;
+          if (!(c == 0 && idx == tid && x_hoisted)) load_x_rows(c, idx);
+          const int rg = idx / CG, cg = idx % CG;
           float part[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) part[e] = 0.f;
-          for (int ih = rg; ih < arows; ih += RG) {
-            const int64_t col = base + (int64_t)ih * Kc + cg * 8;
-            const uint4 raw = *reinterpret_cast<const uint4*>(xc + col);
-            const uint32_t sb = sgn ? (sgn[col >> 5] >> (col & 31)) : 0u;
-            const uint32_t chi = (uint32_t)__builtin_popcount((unsigned)(jhi & ih)) & 1u;
-            const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float v = h2f((uint16_t)(rw[e >> 1] >> (16 * (e & 1))));
-              const uint32_t neg = ((sb >> e) & 1u) ^ chi;
-              part[e] += neg ? -v : v;
+          for (int r = 0; r < MAXR; ++r) {
+            const int ih = rg + r * RG;
+            if (ih < arows) {
+              const uint32_t chi = (uint32_t)__builtin_popcount((unsigned)(jhi & ih)) & 1u;
+              const uint32_t rw[4] = {xraw[r].x, xraw[r].y, xraw[r].z, xraw[r].w};
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float v = h2f((uint16_t)(rw[e >> 1] >> (16 * (e & 1))));
+                const uint32_t neg = ((xsb[r] >> e) & 1u) ^ chi;
+                part[e] += neg ? -v : v;
+              }
             }
           }
 #pragma unroll
@@ -163,26 +200,26 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
         for (int col = tid; col < kcols; col += GEMV_THREADS) {
           float s = 0.f;
           for (int rg = 0; rg < RG; ++rg) s += red[rg * kcols + col];
-          u[c * Kc + col] = s;
+          u[c * ustride + pad_index(col)] = s;
         }
         __syncthreads();
       } else {
-        for (int col = tid; col < Kc; col += GEMV_THREADS) u[c * Kc + col] = 0.f;
+        for (int col = tid; col < Kc; col += GEMV_THREADS) u[c * ustride + pad_index(col)] = 0.f;
       }
     }
     __syncthreads();
     const int S = Kc < Bi ? Kc : Bi;
     // transform each batch column's slice: segments of S within [0, kcols)
     for (int c = 0; c < NB; ++c) {
-      if (c < a.b) fwht_segments(u + c * Kc, kcols, S, tid, GEMV_THREADS);
+      if (c < a.b) fwht_segments(u + c * ustride, kcols, S, tid, GEMV_THREADS);
     }
     const float rs = 1.0f / sqrtf((float)Bi);
     for (int idx = tid; idx < NB * (Kc / 2); idx += GEMV_THREADS) {
       const int c = idx / (Kc / 2), p = idx % (Kc / 2);
       uint32_t v = 0;
       if (2 * p < kcols && c < a.b) {
-        const uint32_t lo = f2h_bits(u[c * Kc + 2 * p] * rs);
-        const uint32_t hi = f2h_bits(u[c * Kc + 2 * p + 1] * rs);
+        const uint32_t lo = f2h_bits(u[c * ustride + pad_index(2 * p)] * rs);
+        const uint32_t hi = f2h_bits(u[c * ustride + pad_index(2 * p + 1)] * rs);
         v = lo | (hi << 16);
       }
       xh[idx] = v;
@@ -192,17 +229,17 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
       }
     }
     __syncthreads();
-    if constexpr (CODE == MAD1) {
-      // sum of the fp16 x' of the chunk, per batch column (bias removal)
-      for (int c = wave; c < NB; c += 4) {
-        float s = 0.f;
-        for (int p = lane; p < Kc / 2; p += 64) {
-          const uint32_t v = xh[c * (Kc / 2) + p];
-          s += h2f((uint16_t)(v & 0xFFFFu)) + h2f((uint16_t)(v >> 16));
-        }
-        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-        if (lane == 0) sx_sum[c] = s;
+  }
+  if constexpr (CODE == MAD1) {
+    // sum of the fp16 x' of the chunk, per batch column (bias removal)
+    for (int c = wave; c < NB; c += 4) {
+      float s = 0.f;
+      for (int p = lane; p < Kc / 2; p += 64) {
+        const uint32_t v = xh[c * (Kc / 2) + p];
+        s += h2f((uint16_t)(v & 0xFFFFu)) + h2f((uint16_t)(v >> 16));
       }
+      for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+      if (lane == 0) sx_sum[c] = s;
     }
   }
 
@@ -305,7 +342,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
     }
   }
 
-  // ---- 5. reduce the waves, add into the workspace ------------------------
+  // ---- 5. reduce the waves, add into the fp32 accumulator -----------------
   __syncthreads();   // table region becomes the reduction buffer
   float* red = fA;   // [4 waves][128 rows][NB]
 #pragma unroll
@@ -313,46 +350,25 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int c = 0; c < NB; ++c) red[(wave * 128 + tl * 16 + 2 * q + r) * NB + c] = acc[r][c];
   __syncthreads();
+  // the panel's sums, scaled, then the output Hadamard stages that stay
+  // inside the panel (H_min(Bo,128) on 128 rows); the rest is the finisher's
+  float* pv = fA + 4 * 128 * NB;   // entry (c, row) at pad_index(c * 128 + row)
   for (int idx = tid; idx < 128 * NB; idx += GEMV_THREADS) {
     const int row = idx / NB, c = idx % NB;
-    if (c < a.b) {
-      float s = red[(0 * 128 + row) * NB + c] + red[(1 * 128 + row) * NB + c] +
-                red[(2 * 128 + row) * NB + c] + red[(3 * 128 + row) * NB + c];
-      if constexpr (CODE == MAD1) s -= MAD1_BIAS * sx_sum[c];
-      float* dst = a.z + (int64_t)c * m + (int64_t)panel * 128 + row;
-      __hip_atomic_fetch_add(dst, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-
-  // ---- 6. last workgroup of the output unit: output RHT -------------------
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  const int unit = (int)(((int64_t)panel * 128) / U);
-  if (tid == 0) {
-    const uint32_t expected = (uint32_t)a.nchunks * (uint32_t)(U / 128);
-    const uint32_t old = __hip_atomic_fetch_add(a.counters + unit, 1u, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = (old == expected - 1) ? 1 : 0;
+    float s = red[(0 * 128 + row) * NB + c] + red[(1 * 128 + row) * NB + c] +
+              red[(2 * 128 + row) * NB + c] + red[(3 * 128 + row) * NB + c];
+    if constexpr (CODE == MAD1) s -= MAD1_BIAS * sx_sum[c];
+    pv[pad_index(c * 128 + row)] = s * a.out_mult;
   }
   __syncthreads();
-  if (!last_flag) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int64_t r0 = (int64_t)unit * U;
   const int Bo = a.L.had_out;
-  for (int c = 0; c < a.b; ++c) {
-    float* zc = a.z + (int64_t)c * m + r0;
-    for (int i = tid; i < U; i += GEMV_THREADS) {
-      fA[i] = __hip_atomic_load(zc + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      zc[i] = 0.f;
-    }
-    __syncthreads();
-    if (Bo > 1) fwht_segments(fA, U, Bo, tid, GEMV_THREADS);
-    uint16_t* yc = a.y + (int64_t)c * m + r0;
-    for (int i = tid; i < U; i += GEMV_THREADS)
-      yc[i] = f2h_bits(fA[i] * a.out_mult * sign_of(a.L.sign_out, r0 + i));
-    __syncthreads();
+  if (Bo > 1) fwht_bits(pv, 128 * NB, 0, Bo >= 128 ? 7 : 31 - __builtin_clz((unsigned)Bo), tid, GEMV_THREADS);
+  for (int idx = tid; idx < 128 * NB; idx += GEMV_THREADS) {
+    const int c = idx >> 7, row = idx & 127;
+    if (c < a.b)
+      __hip_atomic_fetch_add(a.z + (int64_t)c * m + (int64_t)panel * 128 + row, pv[pad_index(c * 128 + row)],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (tid == 0) __hip_atomic_store(a.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int CODE, int K, int NB>
@@ -364,7 +380,9 @@ hipError_t launch_gemv_t(const GemvArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((a.L.m / 128) * a.nchunks);
   hipLaunchKernelGGL((gemv_kernel<CODE, K, NB>), dim3(grid), dim3(GEMV_THREADS), lds, stream, a);
-  return hipGetLastError();
+  const hipError_t e1 = hipGetLastError();
+  if (e1 != hipSuccess) return e1;
+  return launch_gemv_finish(a, stream);
 }
 
 template <int CODE, int K>

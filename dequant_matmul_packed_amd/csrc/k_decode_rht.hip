@@ -91,28 +91,67 @@ bool decode_supported(int code, int k) {
 // its accumulator this way).
 __global__ __launch_bounds__(256) void rht_kernel(RhtArgs a, int zero_in) {
   extern __shared__ __align__(16) float buf[];
+  constexpr int MAXJ = 8;            // 256 threads x 8 chunks x 8 values = 16384
   const int tid = threadIdx.x;
   const int B = a.block;
   const int64_t nblk = a.n / B;
   const int64_t row = blockIdx.x / nblk;
   const int64_t c0 = (blockIdx.x % nblk) * B;
   const int64_t off = row * a.n + c0;
-  for (int i = tid; i < B; i += 256) {
-    float v;
-    if (a.in_f32) {
-      float* p = (float*)a.in + off + i;
-      v = *p;
-      if (zero_in) *p = 0.f;
-    } else {
-      v = h2f(((const uint16_t*)a.in)[off + i]);
+  if (B < 8) {                       // tiny blocks: one value per thread
+    for (int i = tid; i < B; i += 256) {
+      float v = a.in_f32 ? ((const float*)a.in)[off + i] : h2f(((const uint16_t*)a.in)[off + i]);
+      if (a.in_f32 && zero_in) ((float*)a.in)[off + i] = 0.f;
+      if (a.mode == 0) v *= sign_of(a.signs, c0 + i);
+      buf[pad_index(i)] = v;
     }
-    if (a.mode == 0) v *= sign_of(a.signs, c0 + i);
-    buf[i] = v;
+  } else {
+    // chunks of 8 consecutive values; every load is issued before any is
+    // used (addresses clamped in bounds, unused results dropped)
+    const int nch = B >> 3;
+    float v[MAXJ][8];
+    uint32_t sw[MAXJ];
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const int ch = tid + 256 * j;
+      const int chc = ch < nch ? ch : 0;
+      const int64_t e0 = off + 8 * (int64_t)chc;
+      if (a.in_f32) {
+        const float4 p0 = *reinterpret_cast<const float4*>((const float*)a.in + e0);
+        const float4 p1 = *reinterpret_cast<const float4*>((const float*)a.in + e0 + 4);
+        v[j][0] = p0.x; v[j][1] = p0.y; v[j][2] = p0.z; v[j][3] = p0.w;
+        v[j][4] = p1.x; v[j][5] = p1.y; v[j][6] = p1.z; v[j][7] = p1.w;
+      } else {
+        const uint4 p = *reinterpret_cast<const uint4*>((const uint16_t*)a.in + e0);
+        const uint32_t r[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j][e] = h2f((uint16_t)(r[e >> 1] >> (16 * (e & 1))));
+      }
+      const int64_t g = c0 + 8 * (int64_t)chc;
+      sw[j] = a.signs ? (a.signs[g >> 5] >> (g & 31)) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const int ch = tid + 256 * j;
+      if (ch < nch) {
+        if (a.in_f32 && zero_in) {
+          float* p = (float*)a.in + off + 8 * (int64_t)ch;
+          *reinterpret_cast<float4*>(p) = make_float4(0.f, 0.f, 0.f, 0.f);
+          *reinterpret_cast<float4*>(p + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float x = v[j][e];
+          if (a.mode == 0 && ((sw[j] >> e) & 1u)) x = -x;
+          buf[pad_index(8 * ch + e)] = x;
+        }
+      }
+    }
   }
   __syncthreads();
   if (B > 1) fwht_segments(buf, B, B, tid, 256);
   for (int i = tid; i < B; i += 256) {
-    float v = buf[i] * a.mult;
+    float v = buf[pad_index(i)] * a.mult;
     if (a.mode == 1) v *= sign_of(a.signs, c0 + i);
     if (a.out_f32) ((float*)a.out)[off + i] = v;
     else ((uint16_t*)a.out)[off + i] = f2h_bits(v);
@@ -123,10 +162,10 @@ static hipError_t launch_rht_impl(const RhtArgs& a, int zero_in, hipStream_t str
   if (a.rows <= 0) return hipSuccess;
   static size_t have = 0;
   const hipError_t e =
-      ensure_dynamic_lds(reinterpret_cast<const void*>(&rht_kernel), (size_t)a.block * 4, &have);
+      ensure_dynamic_lds(reinterpret_cast<const void*>(&rht_kernel), (size_t)padded_words(a.block) * 4, &have);
   if (e != hipSuccess) return e;
   const int64_t blocks = a.rows * (a.n / a.block);
-  hipLaunchKernelGGL(rht_kernel, dim3((unsigned)blocks), dim3(256), (size_t)a.block * 4, stream, a,
+  hipLaunchKernelGGL(rht_kernel, dim3((unsigned)blocks), dim3(256), (size_t)padded_words(a.block) * 4, stream, a,
                      zero_in);
   return hipGetLastError();
 }
@@ -149,4 +188,60 @@ hipError_t launch_rht_out_f32(float* z, uint16_t* y, int64_t rows, int64_t m, in
   return launch_rht_impl(a, 1, stream);
 }
 
+}  // namespace qdec
+
+namespace qdec {
+// Output side of qdec_gemv.  z (fp32 [b][m]) holds, for every 128-row panel,
+// the scaled sums already multiplied by H_min(Bo,128) (the stages inside a
+// panel, done by the GEMV workgroups).  With Sylvester ordering
+// H_Bo = H_P (x) H_128 for P = Bo/128, so the stages left are P-point
+// transforms across the P panels of a block at a fixed row offset i: one
+// thread per (block, i, batch column), the P values in registers.  The
+// thread then applies the output signs, writes fp16 y and re-zeroes z.
+template <int P>
+__global__ __launch_bounds__(128) void gemv_finish_kernel(float* z, uint16_t* y, int64_t m,
+                                                        const uint32_t* sign_out) {
+  const int i = threadIdx.x;
+  const int64_t blk = blockIdx.x;
+  const int64_t c = blockIdx.y;
+  const int64_t row0 = blk * (P * 128) + i;
+  float* zc = z + c * m + row0;
+  float v[P];
+  uint32_t sg[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int64_t r = row0 + j * 128;
+    sg[j] = sign_out ? (sign_out[r >> 5] >> (r & 31)) & 1u : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < P; ++j) v[j] = zc[j * 128];
+#pragma unroll
+  for (int j = 0; j < P; ++j) zc[j * 128] = 0.f;
+  fwht_regs<P>(v);
+  uint16_t* yc = y + c * m + row0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) yc[j * 128] = f2h_bits(sg[j] ? -v[j] : v[j]);
+}
+
+template <int P>
+static hipError_t launch_finish_p(const GemvArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)(a.L.m / (P * 128)), (unsigned)a.b);
+  hipLaunchKernelGGL((gemv_finish_kernel<P>), grid, dim3(128), 0, stream, a.z, a.y, a.L.m, a.L.sign_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_finish(const GemvArgs& a, hipStream_t stream) {
+  const int P = a.L.had_out > 128 ? a.L.had_out / 128 : 1;
+  switch (P) {
+    case 1: return launch_finish_p<1>(a, stream);
+    case 2: return launch_finish_p<2>(a, stream);
+    case 4: return launch_finish_p<4>(a, stream);
+    case 8: return launch_finish_p<8>(a, stream);
+    case 16: return launch_finish_p<16>(a, stream);
+    case 32: return launch_finish_p<32>(a, stream);
+    case 64: return launch_finish_p<64>(a, stream);
+    case 128: return launch_finish_p<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 }  // namespace qdec

@@ -167,8 +167,13 @@ namespace qdec {
 // unnormalised: every segment of S consecutive entries (S a power of two,
 // `total` a multiple of S) is multiplied by the Sylvester-ordered H_S.  The
 // radix-2 stages act on distinct index bits and commute, so they run in
-// passes of up to 4 bits, 16 values per thread held in registers.  All
-// threads of the block must call it; it ends with a barrier.
+// passes of up to 4 bits, 16 values per thread held in registers.  Entry i
+// lives at word pad_index(i) = i + i/32: with one spare word per 32 the
+// strided accesses of every pass fall in distinct banks.  All threads of
+// the block must call these; they end with a barrier.
+__device__ __forceinline__ int pad_index(int i) { return i + (i >> 5); }
+__host__ __device__ constexpr int padded_words(int n) { return n + (n >> 5) + 1; }
+
 template <int E>
 __device__ __forceinline__ void fwht_pass(float* buf, int total, int b0, int tid, int nthreads) {
   constexpr int G = 1 << E;
@@ -179,7 +184,7 @@ __device__ __forceinline__ void fwht_pass(float* buf, int total, int b0, int tid
     const int base = (hi << (b0 + E)) | lo;
     float v[G];
 #pragma unroll
-    for (int i = 0; i < G; ++i) v[i] = buf[base + (i << b0)];
+    for (int i = 0; i < G; ++i) v[i] = buf[pad_index(base + (i << b0))];
 #pragma unroll
     for (int h = 1; h < G; h <<= 1) {
 #pragma unroll
@@ -192,14 +197,14 @@ __device__ __forceinline__ void fwht_pass(float* buf, int total, int b0, int tid
       }
     }
 #pragma unroll
-    for (int i = 0; i < G; ++i) buf[base + (i << b0)] = v[i];
+    for (int i = 0; i < G; ++i) buf[pad_index(base + (i << b0))] = v[i];
   }
 }
 
-__device__ inline void fwht_segments(float* buf, int total, int S, int tid, int nthreads) {
-  const int bits = 31 - __builtin_clz((unsigned)S);
-  for (int b0 = 0; b0 < bits; b0 += 4) {
-    const int e = (bits - b0) < 4 ? (bits - b0) : 4;
+// Stages on index bits [bit_lo, bit_hi) only; `total` a multiple of 2^bit_hi.
+__device__ inline void fwht_bits(float* buf, int total, int bit_lo, int bit_hi, int tid, int nthreads) {
+  for (int b0 = bit_lo; b0 < bit_hi; b0 += 4) {
+    const int e = (bit_hi - b0) < 4 ? (bit_hi - b0) : 4;
     switch (e) {
       case 1: fwht_pass<1>(buf, total, b0, tid, nthreads); break;
       case 2: fwht_pass<2>(buf, total, b0, tid, nthreads); break;
@@ -207,6 +212,26 @@ __device__ inline void fwht_segments(float* buf, int total, int S, int tid, int 
       default: fwht_pass<4>(buf, total, b0, tid, nthreads); break;
     }
     __syncthreads();
+  }
+}
+
+__device__ inline void fwht_segments(float* buf, int total, int S, int tid, int nthreads) {
+  fwht_bits(buf, total, 0, 31 - __builtin_clz((unsigned)S), tid, nthreads);
+}
+
+// In-register FWHT of P values (P a power of two).
+template <int P>
+__device__ __forceinline__ void fwht_regs(float* v) {
+#pragma unroll
+  for (int h = 1; h < P; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      if (!(i & h)) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
   }
 }
 

@@ -27,11 +27,11 @@ struct GemvArgs {
   const uint16_t* x;   // [b][n] fp16
   uint16_t* y;         // [b][m] fp16
   int b;
-  float* z;            // [b][m] fp32 split-K accumulator (workspace, zero on entry)
-  uint32_t* counters;  // [m / U] arrival counters (workspace, zero on entry)
+  const uint16_t* xr;  // precomputed x' = RHT_in(x), fp16 [b][n], or NULL
+  float* z;            // [b][m] fp32 split-K accumulator (workspace; zero on entry, left zero)
   int Kc;              // columns per chunk (power of two, 64 .. 512)
   int nchunks;         // ceil(n / Kc)
-  int U;               // rows per finalize unit = max(had_out, 128)
+  int U;               // rows per output block = max(had_out, 128)
   float out_mult;      // layer scale x code factor / sqrt(had_out)
 };
 
@@ -60,11 +60,23 @@ struct GemmArgs {
   int ksplit;          // K split factor (fp32 atomics when > 1)
 };
 
-// Workspace layout of qdec_gemv: z then counters, each 256-byte aligned.
+// Workspace layout of qdec_gemv: the fp32 accumulator z [b][m] (must start
+// at zero; left zero), then the fp16 x' [b][n] of the separate-RHT path.
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 inline int gemv_unit_rows(int had_out) { return had_out > 128 ? had_out : 128; }
-inline size_t gemv_ws_bytes(int64_t m, int64_t b, int had_out) {
-  return align256((size_t)(b * m) * 4) + align256((size_t)(m / gemv_unit_rows(had_out)) * 4);
+// Input-chunk width of the fused GEMV: enough (panel, chunk) workgroups to
+// cover the 256 CUs several times, chunks a power of two in [64, 512].
+int gemv_chunk(int64_t m, int64_t n, int64_t b);
+bool gemv_separate_rht();
+struct GemvWs {
+  size_t z, xr, total;
+};
+inline GemvWs gemv_ws_layout(int64_t m, int64_t n, int64_t b) {
+  GemvWs l;
+  l.z = 0;
+  l.xr = align256((size_t)(b * m) * 4);
+  l.total = l.xr + align256((size_t)(b * n) * 2);
+  return l;
 }
 // Workspace layout of qdec_gemm: X' (fp16 [b][n]) then Z (fp32 [b][m]).
 inline size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t b) {
@@ -83,6 +95,7 @@ inline hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes, size_t* h
 
 // Kernel launchers (return hipSuccess or the launch error).
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
+hipError_t launch_gemv_finish(const GemvArgs& a, hipStream_t stream);
 hipError_t launch_decode_tile(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_rht(const RhtArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);

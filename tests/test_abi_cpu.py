@@ -51,9 +51,9 @@ def _layer(q, **kw):
 def test_workspace_sizes(q):
     lay = _layer(q)
     gv = q.qdec_workspace_bytes(lay, 1, q.QDEC_OP_GEMV)
-    # z: b*m fp32, counters: m / max(had_out, 128), each 256-byte aligned
-    assert gv == 1024 + 256
-    assert q.qdec_workspace_bytes(lay, 8, q.QDEC_OP_GEMV) == 8192 + 256
+    # fp32 accumulator b x m, then fp16 x' b x n; each 256-byte aligned
+    assert gv == 1 * 256 * 4 + 1 * 128 * 2
+    assert q.qdec_workspace_bytes(lay, 8, q.QDEC_OP_GEMV) == 8 * 256 * 4 + 8 * 128 * 2
     gm = q.qdec_workspace_bytes(lay, 64, q.QDEC_OP_GEMM)
     assert gm == 64 * 128 * 2 + 64 * 256 * 4
     assert q.qdec_workspace_bytes(lay, 9, q.QDEC_OP_GEMV) == 0
