@@ -167,6 +167,7 @@ def main():
             fn()
         return g
 
+
     for v in variants:          # warm the launch paths once, eagerly
         v["launches"][0]()
     torch.cuda.synchronize()

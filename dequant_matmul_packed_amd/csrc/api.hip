@@ -139,6 +139,24 @@ bool gemv_separate_rht() {
   return v == 1;
 }
 
+// K-split factor of the batched path: about two workgroups per CU.
+int gemm_ksplit(int64_t m, int64_t n, int64_t b) {
+  static int forced = -1;
+  if (forced < 0) {
+    // tuning override for measurements: QDEC_GEMM_KSPLIT = 1 .. 16
+    const char* ev = getenv("QDEC_GEMM_KSPLIT");
+    forced = ev ? atoi(ev) : 0;
+    if (forced > 16) forced = 16;
+  }
+  const int64_t npanels = m / 128, nbt = (b + 63) / 64;
+  const int64_t niter = (n / 16 + 3) / 4;
+  int64_t ks = forced > 0 ? forced : (512 + npanels * nbt - 1) / (npanels * nbt);
+  if (ks > niter) ks = niter;
+  if (ks > 16) ks = 16;
+  if (ks < 1) ks = 1;
+  return (int)ks;
+}
+
 int gemv_chunk(int64_t m, int64_t n, int64_t b) {
   static int forced = -1;
   if (forced < 0) {
@@ -302,23 +320,18 @@ int qdec_gemm(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
   r.mult = (float)(1.0 / sqrt((double)L.had_in));
   hipError_t e = launch_rht(r, s);
   if (e != hipSuccess) return status_of(e);
-  // 2. Z = W_hat X'^T (fp32, accumulated into the zeroed workspace)
+  // 2. Z[split] = W_hat X'^T over each K split (fp32 slices, plain stores)
   GemmArgs g;
   g.L = L;
   g.xr = xr;
   g.z = z;
   g.b = (int)batch;
-  const int64_t npanels = L.m / 128, nbt = (batch + 63) / 64;
-  const int64_t niter = (L.n / 16 + 3) / 4;
-  int64_t ks = (512 + npanels * nbt - 1) / (npanels * nbt);
-  if (ks < 1) ks = 1;
-  if (ks > niter) ks = niter;
-  if (ks > 16) ks = 16;
+  const int64_t ks = gemm_ksplit(L.m, L.n, batch);
   g.ksplit = (int)ks;
   e = launch_gemm(g, s);
   if (e != hipSuccess) return status_of(e);
-  // 3. Y = s_out .* (scale/sqrt(B) H Z), fp16; Z re-zeroed
-  e = launch_rht_out_f32(z, y, batch, L.m, L.had_out, L.sign_out,
+  // 3. Y = s_out .* (scale/sqrt(B) H sum_split Z[split]), fp16
+  e = launch_rht_out_f32(z, g.ksplit, y, batch, L.m, L.had_out, L.sign_out,
                          (float)((double)L.scale / sqrt((double)L.had_out)), s);
   return status_of(e);
 }

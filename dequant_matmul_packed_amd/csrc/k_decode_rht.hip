@@ -87,9 +87,9 @@ bool decode_supported(int code, int k) {
 // (row, block), the block held in LDS in fp32.
 //   mode 0: out = mult * H (s .* in);   mode 1: out = s .* (mult * H in)
 // ("Incoherence Processing (W2)": the RHT is invertible up to rounding.)
-// zero_in clears the fp32 input after reading it (the batched path re-zeroes
-// its accumulator this way).
-__global__ __launch_bounds__(256) void rht_kernel(RhtArgs a, int zero_in) {
+// An fp32 input may be the sum of `nsum` slices `sum_stride` apart (the
+// K-split partial sums of the batched path).
+__global__ __launch_bounds__(256) void rht_kernel(RhtArgs a) {
   extern __shared__ __align__(16) float buf[];
   constexpr int MAXJ = 8;            // 256 threads x 8 chunks x 8 values = 16384
   const int tid = threadIdx.x;
@@ -100,8 +100,12 @@ __global__ __launch_bounds__(256) void rht_kernel(RhtArgs a, int zero_in) {
   const int64_t off = row * a.n + c0;
   if (B < 8) {                       // tiny blocks: one value per thread
     for (int i = tid; i < B; i += 256) {
-      float v = a.in_f32 ? ((const float*)a.in)[off + i] : h2f(((const uint16_t*)a.in)[off + i]);
-      if (a.in_f32 && zero_in) ((float*)a.in)[off + i] = 0.f;
+      float v = 0.f;
+      if (a.in_f32) {
+        for (int sl = 0; sl < a.nsum; ++sl) v += ((const float*)a.in)[sl * a.sum_stride + off + i];
+      } else {
+        v = h2f(((const uint16_t*)a.in)[off + i]);
+      }
       if (a.mode == 0) v *= sign_of(a.signs, c0 + i);
       buf[pad_index(i)] = v;
     }
@@ -117,10 +121,15 @@ __global__ __launch_bounds__(256) void rht_kernel(RhtArgs a, int zero_in) {
       const int chc = ch < nch ? ch : 0;
       const int64_t e0 = off + 8 * (int64_t)chc;
       if (a.in_f32) {
-        const float4 p0 = *reinterpret_cast<const float4*>((const float*)a.in + e0);
-        const float4 p1 = *reinterpret_cast<const float4*>((const float*)a.in + e0 + 4);
-        v[j][0] = p0.x; v[j][1] = p0.y; v[j][2] = p0.z; v[j][3] = p0.w;
-        v[j][4] = p1.x; v[j][5] = p1.y; v[j][6] = p1.z; v[j][7] = p1.w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+        for (int sl = 0; sl < a.nsum; ++sl) {     // K-split slices of a GEMM
+          const float* src = (const float*)a.in + sl * a.sum_stride + e0;
+          const float4 p0 = *reinterpret_cast<const float4*>(src);
+          const float4 p1 = *reinterpret_cast<const float4*>(src + 4);
+          v[j][0] += p0.x; v[j][1] += p0.y; v[j][2] += p0.z; v[j][3] += p0.w;
+          v[j][4] += p1.x; v[j][5] += p1.y; v[j][6] += p1.z; v[j][7] += p1.w;
+        }
       } else {
         const uint4 p = *reinterpret_cast<const uint4*>((const uint16_t*)a.in + e0);
         const uint32_t r[4] = {p.x, p.y, p.z, p.w};
@@ -134,11 +143,6 @@ __global__ __launch_bounds__(256) void rht_kernel(RhtArgs a, int zero_in) {
     for (int j = 0; j < MAXJ; ++j) {
       const int ch = tid + 256 * j;
       if (ch < nch) {
-        if (a.in_f32 && zero_in) {
-          float* p = (float*)a.in + off + 8 * (int64_t)ch;
-          *reinterpret_cast<float4*>(p) = make_float4(0.f, 0.f, 0.f, 0.f);
-          *reinterpret_cast<float4*>(p + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float x = v[j][e];
@@ -158,21 +162,24 @@ __global__ __launch_bounds__(256) void rht_kernel(RhtArgs a, int zero_in) {
   }
 }
 
-static hipError_t launch_rht_impl(const RhtArgs& a, int zero_in, hipStream_t stream) {
+static hipError_t launch_rht_impl(const RhtArgs& a, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
   static size_t have = 0;
   const hipError_t e =
       ensure_dynamic_lds(reinterpret_cast<const void*>(&rht_kernel), (size_t)padded_words(a.block) * 4, &have);
   if (e != hipSuccess) return e;
   const int64_t blocks = a.rows * (a.n / a.block);
-  hipLaunchKernelGGL(rht_kernel, dim3((unsigned)blocks), dim3(256), (size_t)padded_words(a.block) * 4, stream, a,
-                     zero_in);
+  hipLaunchKernelGGL(rht_kernel, dim3((unsigned)blocks), dim3(256), (size_t)padded_words(a.block) * 4, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_rht(const RhtArgs& a, hipStream_t stream) { return launch_rht_impl(a, 0, stream); }
+hipError_t launch_rht(const RhtArgs& a, hipStream_t stream) {
+  RhtArgs b = a;
+  if (b.nsum < 1) b.nsum = 1;
+  return launch_rht_impl(b, stream);
+}
 
-hipError_t launch_rht_out_f32(float* z, uint16_t* y, int64_t rows, int64_t m, int block,
+hipError_t launch_rht_out_f32(const float* z, int nsum, uint16_t* y, int64_t rows, int64_t m, int block,
                               const uint32_t* signs, float mult, hipStream_t stream) {
   RhtArgs a;
   a.in = z;
@@ -185,7 +192,9 @@ hipError_t launch_rht_out_f32(float* z, uint16_t* y, int64_t rows, int64_t m, in
   a.signs = signs;
   a.mode = 1;
   a.mult = mult;
-  return launch_rht_impl(a, 1, stream);
+  a.nsum = nsum;
+  a.sum_stride = rows * m;
+  return launch_rht_impl(a, stream);
 }
 
 }  // namespace qdec

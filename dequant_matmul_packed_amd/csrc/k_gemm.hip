@@ -1,15 +1,23 @@
-// Batched decode-and-multiply (qdec_gemm): decoded tiles staged in LDS and
-// fed to fp16 MFMA (v_mfma_f32_16x16x32_f16) with fp32 accumulation.
+// Batched decode-and-multiply (qdec_gemm): decoded weights feed fp16 MFMA
+// (v_mfma_f32_16x16x32_f16) with fp32 accumulation.
 //
 // A workgroup (4 waves) owns one panel of 128 output rows and 64 batch
-// columns; the K loop steps 64 input columns (4 tile columns) at a time:
-// wave w decodes tile column 4*it + w of the panel (8 tiles, 8 lanes each)
-// into the A tile, all threads stage the matching 64x64 slice of the
-// transformed activations X' in the B tile, and each wave then runs the MFMAs
-// for its 32 rows x 64 columns.  Both LDS tiles are [rows][64] fp16 with
-// 16-byte chunks XOR-swizzled by row, so the MFMA operand reads (16 rows x
-// one 16-byte chunk) hit distinct banks.  The dense contraction is where
-// MFMA belongs; the decode stays on the VALU and the LUT on the LDS.
+// columns and steps through K 64 input columns (4 tile columns) at a time.
+// Wave w owns tile rows 2w, 2w+1 of the panel; per step it decodes the 8
+// tiles (2 tile rows x 4 tile columns) with the same 8-lanes-per-tile layout
+// as the GEMV: lane q of tile t holds 32 weights, rows 2q and 2q+1 of the
+// tile, as four 8-weight chunks of one row each.  Placing tile t at
+// (tile row t % 2, tile column t / 2) makes lanes l, l+16, l+32, l+48 hold
+// the same weight row at four different k offsets -- exactly the shape of an
+// MFMA A fragment (lane l: row l % 16, k 8*(l/16) .. +8) under a fixed row
+// permutation.  So chunk a of every lane is an A operand as decoded: the
+// weights go from the code registers to the matrix cores without touching
+// LDS.  The transformed activations X' (the B operand) are staged once per
+// step in LDS (double buffered, 16-byte chunks XOR-swizzled by row) and read
+// as fragments by the four waves; the lookup table of HYB/VQ/NUQ also lives
+// in LDS.  The loop is software-pipelined: the code words of step i+2 and
+// the X' chunk of step i+2 are in flight while step i is decoded and
+// multiplied.
 #include "gemv_impl.hpp"
 #include "qdec_device.hpp"
 #include "qdec_internal.hpp"
@@ -22,22 +30,27 @@ __device__ __forceinline__ int gemm_swz(int r, int k) {
   return r * 128 + ((((k >> 3) ^ (r & 7)) << 4) | ((k & 7) << 1));
 }
 
+// LDS: lookup table, then B[2][64 batch][64 k] fp16 (double buffered).
+template <int CODE, int K>
+__host__ __device__ inline size_t gemm_table_bytes(int Q) {
+  return ((size_t)gemv_table_words<CODE, K>(Q) * 4 + 15) & ~(size_t)15;
+}
 template <int CODE, int K>
 __host__ __device__ inline size_t gemm_lds_bytes(int Q) {
-  const size_t tab = ((size_t)gemv_table_words<CODE, K>(Q) * 4 + 15) & ~(size_t)15;
-  return tab + 128 * 128 + 64 * 128;
+  return gemm_table_bytes<CODE, K>(Q) + 2 * (64 * 128);
 }
 
 template <int CODE, int K>
-__global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   constexpr int COPIES = GemvTable<CODE>::COPIES;
   extern __shared__ __align__(16) uint32_t smem[];
-  const size_t tab_bytes = ((size_t)gemv_table_words<CODE, K>(a.L.Q) * 4 + 15) & ~(size_t)15;
   uint32_t* tab = smem;
-  char* As = reinterpret_cast<char*>(smem) + tab_bytes;
-  char* Bs = As + 128 * 128;
+  char* Bs = reinterpret_cast<char*>(smem) + gemm_table_bytes<CODE, K>(a.L.Q);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = tid & 7, tl = lane >> 3;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane & 7, t = lane >> 3;           // tile t of the wave, lane q in it
+  const int tr = t & 1, tc = t >> 1;                 // tile row / column within the step
   const int64_t m = a.L.m, n = a.L.n;
   const int npanels = (int)(m / 128);
   const int panel = blockIdx.x % npanels;
@@ -52,30 +65,58 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   if constexpr (CODE == HYB) fill_signed_table<COPIES>(tab, a.L.lut, a.L.Q, tid, GEMM_THREADS);
   if constexpr (CODE == VQ) fill_plain_table<COPIES>(tab, a.L.lut, 1 << (2 * K), tid, GEMM_THREADS);
   if constexpr (CODE == NUQ) fill_plain_table<1>(tab, a.L.lut, 1 << K, tid, GEMM_THREADS);
-  __syncthreads();
-
   const uint32_t* tabc = tab + (lane & (COPIES - 1));
+
+  // code words of this lane: tile (row 2*wave + tr, column 4*it + tc)
+  const uint32_t* cbase = a.L.codes + ((int64_t)panel * ntc * 8 + 2 * wave + tr) * (8 * K) + q * K;
+  auto load_codes = [&](int64_t it, uint32_t* w) {
+    int64_t C = it * 4 + tc;
+    C = C < ntc ? C : ntc - 1;                        // in bounds; masked on use
+    load_words<K>(cbase + C * (8 * 8 * K), w);
+  };
+  // X' chunks of this thread: batch row n0 + (tid >> 3), k chunk tid & 7 (x2)
+  auto load_x = [&](int64_t it, uint4* xv) {
+#pragma unroll
+    for (int rep = 0; rep < 2; ++rep) {
+      const int c = tid + rep * GEMM_THREADS;
+      const int bb = c >> 3, ch = c & 7;
+      const int64_t row = (n0 + bb) < a.b ? (n0 + bb) : 0;
+      const int64_t kc = (it * 64 + ch * 8) < n ? (it * 64 + ch * 8) : 0;
+      xv[rep] = *reinterpret_cast<const uint4*>(a.xr + row * n + kc);
+    }
+  };
+  auto store_x = [&](int64_t it, const uint4* xv, int buf) {
+    char* Bt = Bs + buf * (64 * 128);
+#pragma unroll
+    for (int rep = 0; rep < 2; ++rep) {
+      const int c = tid + rep * GEMM_THREADS;
+      const int bb = c >> 3, ch = c & 7;
+      const bool ok = (n0 + bb) < a.b && (it * 64 + ch * 8) < n;
+      *reinterpret_cast<uint4*>(Bt + gemm_swz(bb, ch * 8)) = ok ? xv[rep] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+
   float4v acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t it = it0; it < it1; ++it) {
-    // ---- decode one tile column per wave into the A tile ----
-    const int64_t tc = it * 4 + wave;
-    uint32_t out[16];
+  // Decode step `it` (the lane's 32 weights) into the four A operands:
+  // operand 2*ra + h is the chunk (tile row 2q + ra, columns 8h .. 8h+7).
+  auto decode = [&](int64_t it, const uint32_t* wc, uint4* A) {
     uint32_t w[K + 1];
 #pragma unroll
-    for (int i = 0; i <= K; ++i) w[i] = 0u;
-    if (tc < ntc) load_words<K>(a.L.codes + ((panel * ntc + tc) * 8) * (8 * K) + lane * K, w);
+    for (int i = 0; i < K; ++i) w[i] = wc[i];
     w[K] = next_lane_word(w[0], lane);
-    if (tc < ntc) {
+    const int64_t C = it * 4 + tc;
+    uint32_t out[16];
+    if (C < ntc) {
       float gs[2] = {0.f, 0.f};
       if constexpr (CODE == NUQ) {
         const int64_t gstride = n / a.L.group;
-        const int64_t g = (tc * 16) / a.L.group;
-        const int64_t row0 = (int64_t)panel * 128 + tl * 16 + 2 * q;
+        const int64_t g = (C * 16) / a.L.group;
+        const int64_t row0 = (int64_t)panel * 128 + (2 * wave + tr) * 16 + 2 * q;
         gs[0] = h2f(a.L.gscale[row0 * gstride + g]);
         gs[1] = h2f(a.L.gscale[(row0 + 1) * gstride + g]);
       }
@@ -85,63 +126,86 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
       for (int i = 0; i < 16; ++i) out[i] = 0u;
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int row = tl * 16 + 2 * q + r;
+    for (int j = 0; j < 4; ++j) A[j] = make_uint4(out[4 * j], out[4 * j + 1], out[4 * j + 2], out[4 * j + 3]);
+  };
+  // B fragments of the step in LDS buffer `buf`, then the 16 MFMAs: the B
+  // operand for column half h holds X'[batch][16*(l/16) + 8h .. +8].
+  auto mma = [&](const uint4* A, int buf) {
+    const char* Bt = Bs + buf * (64 * 128);
+    half8v bf[2][4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        *reinterpret_cast<uint4*>(As + gemm_swz(row, wave * 16 + 8 * h)) =
-            make_uint4(out[8 * r + 4 * h], out[8 * r + 4 * h + 1], out[8 * r + 4 * h + 2],
-                       out[8 * r + 4 * h + 3]);
-      }
-    }
-    // ---- stage X' [n0 .. n0+64) x [it*64 .. it*64+64) in the B tile ----
-#pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      const int c = tid + rep * GEMM_THREADS;
-      const int bb = c >> 3, ch = c & 7;
-      const int64_t kcol = it * 64 + ch * 8;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (n0 + bb < a.b && kcol < n)
-        v = *reinterpret_cast<const uint4*>(a.xr + (int64_t)(n0 + bb) * n + kcol);
-      *reinterpret_cast<uint4*>(Bs + gemm_swz(bb, ch * 8)) = v;
-    }
-    __syncthreads();
-    // ---- MFMA: wave rows [32w, 32w+32) x 64 batch columns, K = 64 ----
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int kk = ks * 32 + 8 * (lane >> 4);
-      half8v af[2], bf[4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        af[mb] = *reinterpret_cast<const half8v*>(As + gemm_swz(wave * 32 + mb * 16 + (lane & 15), kk));
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        bf[nb] = *reinterpret_cast<const half8v*>(Bs + gemm_swz(nb * 16 + (lane & 15), kk));
+        bf[h][nb] = *reinterpret_cast<const half8v*>(Bt + gemm_swz(nb * 16 + (lane & 15), 16 * (lane >> 4) + 8 * h));
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+    for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const half8v af = __builtin_bit_cast(half8v, A[2 * ra + h]);
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
-    }
+          acc[ra][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[h][nb], acc[ra][nb], 0, 0, 0);
+      }
+  };
+
+  // Software pipeline, unrolled by 4.  At the top of step s: A[s % 2] holds
+  // the decoded weights of s, LDS buffer s % 2 holds X'(s), code set
+  // c[(s + j) % 4] holds the code words of step s + j (j = 1..3), and X' set
+  // x[(s + 1) % 2] holds X'(s + 1).  A step multiplies s, then decodes s+1
+  // (its VALU work overlaps the MFMAs in flight), stages X'(s+1) in the other
+  // LDS buffer and refills the freed registers with steps s+5 and s+3.
+  uint32_t c0[K], c1[K], c2[K], c3[K];
+  uint4 x0[2], x1[2];
+  uint4 A0[4], A1[4];
+  auto one = [&](int64_t s, const uint4* Acur, uint4* Anext, uint32_t* cnext, uint4* xnext, int buf) {
     __syncthreads();
+    mma(Acur, buf);
+    if (s + 1 < it1) {
+      decode(s + 1, cnext, Anext);
+      if (s + 5 < it1) load_codes(s + 5, cnext);
+      store_x(s + 1, xnext, buf ^ 1);
+      if (s + 3 < it1) load_x(s + 3, xnext);
+    }
+  };
+  if (it0 < it1) {
+    load_codes(it0, c0);
+    if (it0 + 1 < it1) load_codes(it0 + 1, c1);
+    if (it0 + 2 < it1) load_codes(it0 + 2, c2);
+    if (it0 + 3 < it1) load_codes(it0 + 3, c3);
+    load_x(it0, x0);
+    if (it0 + 1 < it1) load_x(it0 + 1, x1);
+    __syncthreads();                                  // lookup table ready
+    store_x(it0, x0, 0);
+    if (it0 + 2 < it1) load_x(it0 + 2, x0);
+    decode(it0, c0, A0);
+    if (it0 + 4 < it1) load_codes(it0 + 4, c0);
+    for (int64_t s = it0; s < it1; s += 4) {
+      one(s, A0, A1, c1, x1, 0);
+      if (s + 1 >= it1) break;
+      one(s + 1, A1, A0, c2, x0, 1);
+      if (s + 2 >= it1) break;
+      one(s + 2, A0, A1, c3, x1, 0);
+      if (s + 3 >= it1) break;
+      one(s + 3, A1, A0, c0, x0, 1);
+    }
   }
 
-  // ---- epilogue: D[i][j] with i = 4*(lane/16) + e, j = lane % 16 ----
+  // ---- epilogue.  acc[ra][nb] holds D[i][j], i = 4*(lane/16) + e, j = lane % 16:
+  // MFMA row i is weight row 16*(i/8) + 2*(i%8) + ra of the wave's 32 rows.
+  // Each K split writes its own slice of the workspace (no atomics); the
+  // output-RHT kernel sums the slices.
+  float* zs = a.z + (int64_t)split * a.b * m;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int nb = 0; nb < 4; ++nb) {
+    const int bb = n0 + nb * 16 + (lane & 15);
+    if (bb >= a.b) continue;
+    float* zrow = zs + (int64_t)bb * m + (int64_t)panel * 128 + 32 * wave;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int bb = n0 + nb * 16 + (lane & 15);
-      if (bb >= a.b) continue;
-      const int64_t row = (int64_t)panel * 128 + wave * 32 + mb * 16 + 4 * (lane >> 4);
-      float* dst = a.z + (int64_t)bb * m + row;
-      if (a.ksplit == 1) {
-        *reinterpret_cast<float4v*>(dst) = acc[mb][nb];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          __hip_atomic_fetch_add(dst + e, acc[mb][nb][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * (lane >> 4) + e;
+      const int r = 16 * (i >> 3) + 2 * (i & 7);
+      *reinterpret_cast<float2*>(zrow + r) = make_float2(acc[0][nb][e], acc[1][nb][e]);
     }
   }
 }

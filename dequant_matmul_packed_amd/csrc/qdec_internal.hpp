@@ -50,14 +50,16 @@ struct RhtArgs {
   const uint32_t* signs;
   int mode;
   float mult;          // scale / sqrt(block)
+  int nsum = 1;        // fp32 input: sum of nsum slices ...
+  int64_t sum_stride = 0;  // ... sum_stride elements apart
 };
 
 struct GemmArgs {
   LayerArgs L;
   const uint16_t* xr;  // [b][n] fp16, input RHT already applied
-  float* z;            // [b][m] fp32 accumulator (zero on entry)
+  float* z;            // [ksplit][b][m] fp32 partial sums, one slice per K split
   int b;
-  int ksplit;          // K split factor (fp32 atomics when > 1)
+  int ksplit;          // K split factor
 };
 
 // Workspace layout of qdec_gemv: the fp32 accumulator z [b][m] (must start
@@ -78,9 +80,11 @@ inline GemvWs gemv_ws_layout(int64_t m, int64_t n, int64_t b) {
   l.total = l.xr + align256((size_t)(b * n) * 2);
   return l;
 }
-// Workspace layout of qdec_gemm: X' (fp16 [b][n]) then Z (fp32 [b][m]).
+// Workspace layout of qdec_gemm: X' (fp16 [b][n]) then the K-split partial
+// sums Z (fp32 [ksplit][b][m]).  Nothing in it needs initialising.
+int gemm_ksplit(int64_t m, int64_t n, int64_t b);
 inline size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t b) {
-  return align256((size_t)(b * n) * 2) + align256((size_t)(b * m) * 4);
+  return align256((size_t)(b * n) * 2) + align256((size_t)(gemm_ksplit(m, n, b) * b * m) * 4);
 }
 
 // Raise a kernel's dynamic-LDS limit to `bytes` when a launch needs more than
@@ -100,7 +104,7 @@ hipError_t launch_decode_tile(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_rht(const RhtArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 // Output side of the batched path: y = fp16(s_out .* (mult * H z)); z zeroed.
-hipError_t launch_rht_out_f32(float* z, uint16_t* y, int64_t rows, int64_t m, int block,
+hipError_t launch_rht_out_f32(const float* z, int nsum, uint16_t* y, int64_t rows, int64_t m, int block,
                               const uint32_t* signs, float mult, hipStream_t stream);
 
 // Which (code, k) pairs and batch sizes the kernels are built for.

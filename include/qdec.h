@@ -160,7 +160,7 @@ int qdec_gemv(const qdec_layer *layer, const uint16_t *x, uint16_t *y,
  * 1 <= batch <= 256; decoded tiles are staged in LDS and fed to fp16 MFMA
  * with fp32 accumulation.  Three launches on `stream` (input RHT, GEMM,
  * output RHT).  ws: qdec_workspace_bytes(layer, batch, QDEC_OP_GEMM) bytes,
- * 256-byte aligned, zero-filled before first use (left zeroed).             */
+ * 256-byte aligned; its contents on entry do not matter.                    */
 int qdec_gemm(const qdec_layer *layer, const uint16_t *x, uint16_t *y,
               int64_t batch, void *ws, size_t ws_bytes, void *stream);
 

@@ -55,7 +55,8 @@ def test_workspace_sizes(q):
     assert gv == 1 * 256 * 4 + 1 * 128 * 2
     assert q.qdec_workspace_bytes(lay, 8, q.QDEC_OP_GEMV) == 8 * 256 * 4 + 8 * 128 * 2
     gm = q.qdec_workspace_bytes(lay, 64, q.QDEC_OP_GEMM)
-    assert gm == 64 * 128 * 2 + 64 * 256 * 4
+    # X' (b x n fp16), then one fp32 b x m slice per K split (here 2: n/64)
+    assert gm == 64 * 128 * 2 + 2 * 64 * 256 * 4
     assert q.qdec_workspace_bytes(lay, 9, q.QDEC_OP_GEMV) == 0
     assert q.qdec_workspace_bytes(lay, 0, q.QDEC_OP_GEMM) == 0
     assert q.qdec_workspace_bytes(lay, 1, 99) == 0
