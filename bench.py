@@ -45,6 +45,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--only", default="", help="restrict the step to one variant, e.g. 3INST_k4")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every GEMV directly (no graph replay), e.g. under counter collection")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed region, copy this many MiB device-to-device 5 times "
+                         "(a plain copy of known size to scale HBM counters by)")
     return ap.parse_args()
 
 
@@ -187,13 +192,23 @@ def main():
     dom = max(variants, key=lambda v: per_variant[v["spec"].name])
     log("per-variant us per GEMV (graph replay):", {k: round(t, 2) for k, t in per_variant.items()})
     others = [v for v in variants if v is not dom]
-    graphs = [capture(lambda i=i: [v["launches"][i]() for v in others]) for i in range(P)] if others else None
+    if args.eager:
+        graphs = None
+        dom_launch_all = others
+
+        def eager_others(i):
+            for v in dom_launch_all:
+                v["launches"][i % P]()
+    else:
+        graphs = [capture(lambda i=i: [v["launches"][i]() for v in others]) for i in range(P)] if others else None
     dom_launch = [Launch(q, "qdec_gemv", L, x, dom["y"], 1, dom["ws"], stream)
                   for L in dom["layers"]]
 
     def step(i, evs=None):
         if graphs is not None:
             graphs[i % P].replay()
+        elif args.eager:
+            eager_others(i)
         if evs is not None:
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
@@ -223,6 +238,16 @@ def main():
     dom_gbs = dom["bytes"] / (dom_us * 1e-6) / 1e9
     log("timed %d steps in %.4f s: %.1f GB/s packed, %.2f us/layer; dominant %s %.2f us"
         % (args.steps, elapsed, gbs, ms_per_step * 1e3 / len(variants), dom["spec"].name, dom_us))
+
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for r in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 5 device-to-device copies of %d MiB" % args.copy_calibration_mib)
+        del src, dst
 
     # sanity: outputs are finite
     for v in variants:
@@ -258,12 +283,34 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "qdec_gemv %s k=%d b=1 (gemv_kernel + gemv_finish_kernel)"
                      % (synth.CODE_NAMES[dom["spec"].code], dom["spec"].k),
                      "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(dom["spec"], dom_us),
                      "bytes_per_launch": dom["bytes"], "avg_launch_us": round(dom_us, 3)},
         "cpu_baseline": cpu,
         "detail": detail,
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(spec, us):
+    """HBM bytes per call of this variant from the committed counter summary
+    (profiles/gemv_hbm_traffic.json), as GB/s over the measured call time;
+    None when the kernels changed since the counters were taken."""
+    import synth
+    path = os.path.join(ROOT, "profiles", "gemv_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    import profile_traffic
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != profile_traffic.kernel_source_hash():
+        return None
+    v = rec["variants"].get("%s_k%d" % (synth.CODE_NAMES[spec.code], spec.k))
+    if v is None:
+        return None
+    return {"bytes_per_call": int(v["bytes_per_call"]), "GBps": round(v["bytes_per_call"] / (us * 1e-6) / 1e9, 2),
+            "over_algorithmic": round(v["bytes_per_call"] / v["algorithmic"], 3),
+            "source": "profiles/gemv_hbm_traffic.md (FETCH_SIZE, WRITE_SIZE scaled by a 256 MiB copy)"}
 
 
 def bench_llama_layer(q, torch, dev, stream):
