@@ -109,56 +109,86 @@ __global__ __launch_bounds__(256) void rht_kernel(RhtArgs a) {
       if (a.mode == 0) v *= sign_of(a.signs, c0 + i);
       buf[pad_index(i)] = v;
     }
-  } else {
-    // chunks of 8 consecutive values; every load is issued before any is
-    // used (addresses clamped in bounds, unused results dropped)
-    const int nch = B >> 3;
-    float v[MAXJ][8];
-    uint32_t sw[MAXJ];
-#pragma unroll
-    for (int j = 0; j < MAXJ; ++j) {
-      const int ch = tid + 256 * j;
-      const int chc = ch < nch ? ch : 0;
-      const int64_t e0 = off + 8 * (int64_t)chc;
-      if (a.in_f32) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
-        for (int sl = 0; sl < a.nsum; ++sl) {     // K-split slices of a GEMM
-          const float* src = (const float*)a.in + sl * a.sum_stride + e0;
-          const float4 p0 = *reinterpret_cast<const float4*>(src);
-          const float4 p1 = *reinterpret_cast<const float4*>(src + 4);
-          v[j][0] += p0.x; v[j][1] += p0.y; v[j][2] += p0.z; v[j][3] += p0.w;
-          v[j][4] += p1.x; v[j][5] += p1.y; v[j][6] += p1.z; v[j][7] += p1.w;
-        }
-      } else {
-        const uint4 p = *reinterpret_cast<const uint4*>((const uint16_t*)a.in + e0);
-        const uint32_t r[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[j][e] = h2f((uint16_t)(r[e >> 1] >> (16 * (e & 1))));
-      }
-      const int64_t g = c0 + 8 * (int64_t)chc;
-      sw[j] = a.signs ? (a.signs[g >> 5] >> (g & 31)) : 0u;
+    __syncthreads();
+    if (B > 1) fwht_segments(buf, B, B, tid, 256);
+    for (int i = tid; i < B; i += 256) {
+      float v = buf[pad_index(i)] * a.mult;
+      if (a.mode == 1) v *= sign_of(a.signs, c0 + i);
+      if (a.out_f32) ((float*)a.out)[off + i] = v;
+      else ((uint16_t*)a.out)[off + i] = f2h_bits(v);
     }
+    return;
+  }
+  // Chunks of 8 consecutive values.  Every global load (values and the
+  // chunk's sign word) is issued before any is used, with addresses clamped
+  // in bounds; the 3 butterfly stages inside a chunk run in registers, the
+  // rest in padded LDS.
+  const int nch = B >> 3;
+  float v[MAXJ][8];
+  uint32_t sw[MAXJ];
 #pragma unroll
-    for (int j = 0; j < MAXJ; ++j) {
-      const int ch = tid + 256 * j;
-      if (ch < nch) {
+  for (int j = 0; j < MAXJ; ++j) {
+    const int ch = tid + 256 * j;
+    const int chc = ch < nch ? ch : 0;
+    const int64_t e0 = off + 8 * (int64_t)chc;
+    if (a.in_f32) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float x = v[j][e];
-          if (a.mode == 0 && ((sw[j] >> e) & 1u)) x = -x;
-          buf[pad_index(8 * ch + e)] = x;
-        }
+      for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+      for (int sl = 0; sl < a.nsum; ++sl) {     // K-split slices of a GEMM
+        const float* src = (const float*)a.in + sl * a.sum_stride + e0;
+        const float4 p0 = *reinterpret_cast<const float4*>(src);
+        const float4 p1 = *reinterpret_cast<const float4*>(src + 4);
+        v[j][0] += p0.x; v[j][1] += p0.y; v[j][2] += p0.z; v[j][3] += p0.w;
+        v[j][4] += p1.x; v[j][5] += p1.y; v[j][6] += p1.z; v[j][7] += p1.w;
       }
+    } else {
+      const uint4 p = *reinterpret_cast<const uint4*>((const uint16_t*)a.in + e0);
+      const uint32_t r[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[j][e] = h2f((uint16_t)(r[e >> 1] >> (16 * (e & 1))));
+    }
+    const int64_t g = c0 + 8 * (int64_t)chc;
+    sw[j] = a.signs ? (a.signs[g >> 5] >> (g & 31)) : 0u;
+  }
+  const int lowbits = B >= 8 ? 3 : 0;
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int ch = tid + 256 * j;
+    if (ch < nch) {
+      if (a.mode == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if ((sw[j] >> e) & 1u) v[j][e] = -v[j][e];
+      }
+      fwht_regs<8>(v[j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) buf[pad_index(8 * ch + e)] = v[j][e];
     }
   }
   __syncthreads();
-  if (B > 1) fwht_segments(buf, B, B, tid, 256);
-  for (int i = tid; i < B; i += 256) {
-    float v = buf[pad_index(i)] * a.mult;
-    if (a.mode == 1) v *= sign_of(a.signs, c0 + i);
-    if (a.out_f32) ((float*)a.out)[off + i] = v;
-    else ((uint16_t*)a.out)[off + i] = f2h_bits(v);
+  fwht_bits(buf, B, lowbits, 31 - __builtin_clz((unsigned)B), tid, 256);
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int ch = tid + 256 * j;
+    if (ch < nch) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o[e] = buf[pad_index(8 * ch + e)] * a.mult;
+        if (a.mode == 1 && ((sw[j] >> e) & 1u)) o[e] = -o[e];
+      }
+      const int64_t e0 = off + 8 * (int64_t)ch;
+      if (a.out_f32) {
+        float* dst = (float*)a.out + e0;
+        *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+      } else {
+        uint32_t r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = f2h_bits(o[2 * e]) | ((uint32_t)f2h_bits(o[2 * e + 1]) << 16);
+        *reinterpret_cast<uint4*>((uint16_t*)a.out + e0) = make_uint4(r[0], r[1], r[2], r[3]);
+      }
+    }
   }
 }
 
