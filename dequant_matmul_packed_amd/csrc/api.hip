@@ -128,17 +128,6 @@ int status_of(hipError_t e) {
 }  // namespace
 
 namespace qdec {
-// Tuning override for measurements: QDEC_GEMV_RHT=1 computes x' with the RHT
-// kernel before the GEMV instead of inside every GEMV workgroup.
-bool gemv_separate_rht() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("QDEC_GEMV_RHT");
-    v = (e && atoi(e) == 1) ? 1 : 0;
-  }
-  return v == 1;
-}
-
 // K-split factor of the batched path: about two workgroups per CU.
 int gemm_ksplit(int64_t m, int64_t n, int64_t b) {
   static int forced = -1;
@@ -160,17 +149,24 @@ int gemm_ksplit(int64_t m, int64_t n, int64_t b) {
 int gemv_chunk(int64_t m, int64_t n, int64_t b) {
   static int forced = -1;
   if (forced < 0) {
-    // tuning override for measurements: QDEC_GEMV_KC = 64 .. 512
+    // tuning override for measurements: QDEC_GEMV_KC = 64 .. 2048
     const char* e = getenv("QDEC_GEMV_KC");
     const int v = e ? atoi(e) : 0;
-    forced = (v >= 64 && v <= 512 && (v & (v - 1)) == 0) ? v : 0;
+    forced = (v >= 64 && v <= 2048 && (v & (v - 1)) == 0) ? v : 0;
   }
-  if (forced > 0) return forced;
-  (void)b;
+  if (forced > 0) {
+    int kc = forced;
+    while (kc > 64 && kc * b > 4096) kc /= 2;
+    return kc;
+  }
+  // about two resident (panel, chunk) workgroups per CU; a chunk's x' slice
+  // (b x Kc fp32) must fit the LDS scratch: Kc * b <= 4096.  With one batch
+  // column every workgroup transforms its own chunk of x, which costs B_in
+  // loads whatever the chunk width: chunks start at 256 columns there (the
+  // widest that takes the wave-level transform).
   const int64_t npanels = m / 128;
-  const int64_t want = (n * npanels) / 1024;
-  int kc = 64;
-  while (kc < 512 && kc * 2 <= want) kc *= 2;
+  int kc = b == 1 ? 256 : 64;
+  while (kc < 2048 && kc * 2 * b <= 4096 && npanels * ((n + 2 * kc - 1) / (2 * kc)) >= 448) kc *= 2;
   return kc;
 }
 }  // namespace qdec
@@ -267,8 +263,10 @@ int qdec_gemv(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
   // the 1MAD matmul path multiplies by the fp32 normaliser, as the decode does
   const double f32norm = (double)(float)factor;
   a.out_mult = (float)((double)L.scale * f32norm / sqrt((double)L.had_out));
-  if (gemv_separate_rht()) {
-    // x' = RHT_in(x) by the RHT kernel into the workspace, then the GEMV
+  if (batch > 1) {
+    // x' = RHT_in(x) once, by the RHT kernel into the workspace, then the
+    // GEMV loads its slices (with one batch column the GEMV's workgroups
+    // transform their own chunks: no extra launch)
     uint16_t* xr = (uint16_t*)((char*)ws + wl.xr);
     RhtArgs r;
     r.in = x;

@@ -18,8 +18,12 @@
 // there keeps every cross-workgroup dependency at a kernel boundary: an
 // in-kernel "last workgroup finishes" scheme needs an agent-scope release
 // (an L2 write-back) in every workgroup, which measured far more expensive
-// than the second launch.  With a precomputed x' (args.xr, written by the
-// RHT kernel) step 2 is replaced by a plain load of the chunk's slice.
+// than the second launch.  With more than one batch column the input RHT
+// runs once, in the RHT kernel, and step 2 is a plain load of the chunk's
+// slice of x' (args.xr): the chunk transform costs b x B_in loads and adds
+// in every workgroup, which at b = 8 outweighs the extra launch.  All
+// global loads go through buffer resources and are issued unconditionally
+// (switched off by their offsets), so they stay in flight together.
 // Small-batch inference is memory bound ("QTIP: Quantization with Trellises
 // and Incoherence Processing", "QTIP's contribution (W1)"), so the codes are
 // read from HBM exactly once and every other operand stays on chip.
@@ -31,7 +35,12 @@
 namespace qdec {
 
 constexpr int GEMV_THREADS = 256;
-constexpr int GEMV_MAX_TPW = 8;   // tile columns per wave (Kc <= 512)
+// Every load slot costs address-unit issue time even when switched off, so
+// the kernel comes in variants sized to the layer: PF is the depth of the
+// code ring (tile columns in flight per wave: 2, 4 and 8 for chunks of at
+// most 128, 256 and more columns); SL ("small loads") sizes the activation
+// rows (2 per thread, enough for B_in <= 4096) and the table words (2 per
+// thread, 2^Q <= 512) instead of 8 and 8.
 
 template <int CODE>
 struct GemvTable {
@@ -53,7 +62,7 @@ template <int CODE, int K, int NB>
 __host__ __device__ inline size_t gemv_regA_bytes(int Q, int Kc, int U) {
   size_t tab = (size_t)gemv_table_words<CODE, K>(Q) * 4;
   size_t rht = (size_t)(GEMV_THREADS * 8 + NB * padded_words(Kc)) * 4;
-  size_t red = ((size_t)4 * 128 * NB + padded_words(128 * NB)) * 4;
+  size_t red = (size_t)4 * 128 * NB * 4;
   (void)U;
   size_t r = tab;
   if (rht > r) r = rht;
@@ -61,10 +70,17 @@ __host__ __device__ inline size_t gemv_regA_bytes(int Q, int Kc, int U) {
   return (r + 15) & ~(size_t)15;
 }
 
+// Chunks of at most this many columns (one batch column, no ragged tail)
+// take the wave-level input RHT, which needs 4 x Kc fp32 of its own.
+constexpr int GEMV_WAVE_RHT_MAX = 256;
+template <int NB>
+__host__ __device__ inline size_t gemv_wred_bytes(int Kc) {
+  return (NB == 1 && Kc <= GEMV_WAVE_RHT_MAX) ? (size_t)4 * Kc * 4 : 0;
+}
 template <int CODE, int K, int NB>
 __host__ __device__ inline size_t gemv_lds_bytes(int Q, int Kc, int U) {
   return gemv_regA_bytes<CODE, K, NB>(Q, Kc, U) + (size_t)NB * Kc * 2 +
-         (CODE == INST3 ? (size_t)NB * Kc * 4 : 0);
+         (CODE == INST3 ? (size_t)NB * Kc * 4 : 0) + gemv_wred_bytes<NB>(Kc);
 }
 
 // K consecutive code words of one lane (16-byte aligned tile blocks).
@@ -82,7 +98,7 @@ __device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint3
   }
 }
 
-template <int CODE, int K, int NB>
+template <int CODE, int K, int NB, int PF, bool SL>
 __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   constexpr int V = code_V(CODE);
   constexpr int L = code_L(CODE, K);
@@ -111,127 +127,278 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   float* fA = reinterpret_cast<float*>(smem);
   uint32_t* xh = smem + regA_words;                 // [NB][Kc/2] fp16 pairs
   uint32_t* xd = xh + (size_t)NB * Kc / 2;           // [NB][Kc] duplicated (3INST)
+  float* wred = reinterpret_cast<float*>(xd + (CODE == INST3 ? (size_t)NB * Kc : 0));   // [4][Kc]
   __shared__ float sx_sum[NB];
 
-  // ---- 0. activations of the first batch column for the input RHT: issued
-  // first, so the RHT's wait on them does not also wait on the (older,
-  // slower) code loads -- vector-memory counters drain in issue order.
+  // ---- 0. (b = 1) the activations of the input RHT: issued first, so the
+  // RHT's wait on them does not also wait on the (slower) code loads --
+  // vector-memory counters drain in issue order.  With b > 1, x' comes
+  // precomputed (args.xr) and step 2 loads the chunk's slice of it instead.
+  constexpr bool XR = NB > 1;
   const int Bi = a.L.had_in;
   const int arows = Kc < Bi ? Bi / Kc : 1;
   const int64_t rbase = Kc < Bi ? (c0 / Bi) * Bi : c0;
   const int jhi = Kc < Bi ? (int)((c0 - rbase) / Kc) : 0;
   const int CG = kcols >> 3;                       // groups of 8 columns
   const int RG = CG >= GEMV_THREADS ? 1 : GEMV_THREADS / CG;
-  constexpr int MAXR = 8;   // arows / RG <= 8 (B_in <= 16384, RG = 2048 / kcols)
-  const uint32_t* __restrict__ sgn = a.L.sign_in;
+  constexpr int MAXR = XR ? 1 : (SL ? 2 : 8);   // arows / RG = B_in / 2048 (B_in <= 16384)
   uint4 xraw[MAXR];
   uint32_t xsb[MAXR];
-  auto load_x_rows = [&](int c, int idx) {
-    const int cg = idx % CG, rg = idx / CG;
-    const uint16_t* __restrict__ xc = a.x + (int64_t)c * n;
+  // the lookup table's words, requested up front too: word tid + 256 i
+  // (HYB: 2^Q <= 256 TW words; VQ 2^(2k) <= 256; NUQ 2^k <= 16)
+  constexpr int TW = CODE == HYB ? (SL ? 2 : 8) : 1;
+  const int nlut = CODE == HYB ? (1 << a.L.Q) : CODE == VQ ? (1 << (2 * K)) : CODE == NUQ ? (1 << K) : 0;
+  uint32_t lw[TW];
+  {
+    const auto lrs = make_rsrc(a.L.lut, (uint32_t)nlut * 4u);
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+      const int e = tid + i * GEMV_THREADS;
+      lw[i] = buf_load_u32(lrs, e < nlut ? (uint32_t)e * 4u : BUF_OFF);
+    }
+  }
+  if constexpr (!XR) {
+    // x as a buffer of one row; the sign bits as a buffer that is empty when
+    // the layer has no input signs (its loads then read zero: all signs +1).
+    // xsb[r] is the whole sign word: the group's 8 signs start at bit
+    // (cg * 8) & 31, as rbase and Kc are multiples of 64.
+    const auto xrs = make_rsrc(a.x, (uint32_t)(n * 2));
+    const auto srs = make_rsrc(a.L.sign_in, a.L.sign_in ? (uint32_t)(((n + 31) >> 5) * 4) : 0u);
+    const int cg = tid % CG, rg = tid / CG;
 #pragma unroll
     for (int r = 0; r < MAXR; ++r) {
       const int ih = rg + r * RG;
-      const int ihc = ih < arows ? ih : 0;   // row 0 is always in bounds
-      const int64_t col = rbase + (int64_t)ihc * Kc + cg * 8;
-      xraw[r] = *reinterpret_cast<const uint4*>(xc + col);
-      xsb[r] = sgn ? (sgn[col >> 5] >> (col & 31)) : 0u;
+      const int64_t col = rbase + (int64_t)ih * Kc + cg * 8;
+      const bool ok = tid < CG * RG && ih < arows;
+      xraw[r] = buf_load_u4(xrs, ok ? (uint32_t)(col * 2) : BUF_OFF);
+      xsb[r] = buf_load_u32(srs, ok ? (uint32_t)((col >> 5) * 4) : BUF_OFF);
     }
-  };
-  const bool x_hoisted = !a.xr && tid < CG * RG;
-  if (x_hoisted) load_x_rows(0, tid);
+    __builtin_amdgcn_sched_barrier(0);   // keep these ahead of the code loads
+  }
 
   // ---- 1. issue the code loads ------------------------------------------
+  // A buffer over this panel's tile columns of the chunk (each 8 tiles x 8
+  // lanes x K words); the wave's tile columns tc_begin .. tc_begin+tc_count-1
+  // stream through an 8-deep ring of registers, the first 8 requested here.
   const int64_t tiles_row = n >> 4;
-  const uint32_t* __restrict__ codes = a.L.codes;
-  uint32_t buf[GEMV_MAX_TPW][K];
+  const uint32_t* pchunk = a.L.codes + ((int64_t)panel * tiles_row + (c0 >> 4)) * (64 * K);
+  const auto crs = make_rsrc(pchunk, (uint32_t)ntc * (256u * K));
+  const uint32_t lane_off = (uint32_t)lane * (4 * K);
+  auto code_off = [&](int j) -> uint32_t {
+    return j < tc_count ? (uint32_t)(tc_begin + j) * (256u * K) + lane_off : BUF_OFF;
+  };
+  uint32_t buf[PF][K];
 #pragma unroll
-  for (int j = 0; j < GEMV_MAX_TPW; ++j) {
-    if (j < tc_count) {
-      const int64_t tcg = (c0 >> 4) + tc_begin + j;
-      const uint32_t* src = codes + ((panel * tiles_row + tcg) * 8) * (8 * K) + lane * K;
-      load_words<K>(src, buf[j]);
+  for (int j = 0; j < PF; ++j) buf_load_words<K>(crs, code_off(j), buf[j]);
+  // NUQ: the fp16 group scales of the lane's two rows ride in the same ring
+  const int64_t gstride = CODE == NUQ ? n / a.L.group : 0;
+  const int64_t grow0 = (int64_t)panel * 128 + (lane >> 3) * 16 + 2 * (lane & 7);
+  const auto grs = make_rsrc(a.L.gscale, CODE == NUQ ? (uint32_t)(m * gstride * 2) : 0u);
+  uint32_t gsr[PF][2];
+  auto gs_load = [&](int j, uint32_t* g) {
+    if constexpr (CODE == NUQ) {
+      const bool ok = j < tc_count;
+      const int64_t gcol = (c0 + (int64_t)(tc_begin + j) * 16) / a.L.group;
+      g[0] = buf_load_u16(grs, ok ? (uint32_t)((grow0 * gstride + gcol) * 2) : BUF_OFF);
+      g[1] = buf_load_u16(grs, ok ? (uint32_t)(((grow0 + 1) * gstride + gcol) * 2) : BUF_OFF);
+    } else {
+      (void)j; g[0] = g[1] = 0u;
     }
-  }
+  };
+#pragma unroll
+  for (int j = 0; j < PF; ++j) gs_load(j, gsr[j]);
+  __builtin_amdgcn_sched_barrier(0);   // all requests out before any wait
 
-  // ---- 2. input RHT of the chunk (or load the precomputed x') -------------
-  if (a.xr) {
-    for (int idx = tid; idx < NB * (Kc / 2); idx += GEMV_THREADS) {
-      const int c = idx / (Kc / 2), p = idx % (Kc / 2);
-      uint32_t v = 0;
-      if (2 * p < kcols && c < a.b)
-        v = *reinterpret_cast<const uint32_t*>(a.xr + (int64_t)c * n + c0 + 2 * p);
-      xh[idx] = v;
-      if constexpr (CODE == INST3) {
-        xd[c * Kc + 2 * p] = (v & 0xFFFFu) * 0x10001u;
-        xd[c * Kc + 2 * p + 1] = (v >> 16) * 0x10001u;
-      }
-    }
-    __syncthreads();
-  } else {
-    float* red = fA;                                 // [RG][kcols]
-    float* u = fA + GEMV_THREADS * 8;                // [NB][padded Kc]
-    const int ustride = padded_words(Kc);
-    for (int c = 0; c < NB; ++c) {
-      if (c < a.b) {
-        for (int idx = tid; idx < CG * RG; idx += GEMV_THREADS) {
-          if (!(c == 0 && idx == tid && x_hoisted)) load_x_rows(c, idx);
-          const int rg = idx / CG, cg = idx % CG;
-          float part[8];
+  // The LDS lookup table: HYB entry e and its sign-flipped twin e + 2^Q;
+  // VQ / NUQ as stored; each replicated COPIES times (entry e of copy c at
+  // word e * COPIES + c).
+  auto fill_table = [&]() {
+    if constexpr (CODE == HYB || CODE == VQ || CODE == NUQ) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) part[e] = 0.f;
+      for (int i = 0; i < TW; ++i) {
+        const int e = tid + i * GEMV_THREADS;
+        if (e < nlut) {
 #pragma unroll
-          for (int r = 0; r < MAXR; ++r) {
-            const int ih = rg + r * RG;
-            if (ih < arows) {
-              const uint32_t chi = (uint32_t)__builtin_popcount((unsigned)(jhi & ih)) & 1u;
-              const uint32_t rw[4] = {xraw[r].x, xraw[r].y, xraw[r].z, xraw[r].w};
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const float v = h2f((uint16_t)(rw[e >> 1] >> (16 * (e & 1))));
-                const uint32_t neg = ((xsb[r] >> e) & 1u) ^ chi;
-                part[e] += neg ? -v : v;
-              }
-            }
+          for (int c = 0; c < COPIES; ++c) {
+            regA[e * COPIES + c] = lw[i];
+            if constexpr (CODE == HYB) regA[(e + nlut) * COPIES + c] = lw[i] ^ 0x80008000u;
           }
+        }
+      }
+    }
+  };
+
+  // ---- 2. input RHT of the chunk (b = 1), or load the precomputed x' ------
+  // A full chunk of at most 256 columns takes the wave-level transform:
+  // one barrier in all, and the table is filled before it.
+  const bool wave_rht = !XR && Kc <= GEMV_WAVE_RHT_MAX && kcols == Kc;
+  if constexpr (XR) {
+    // NB * Kc / 2 <= 2048 fp16 pairs: at most 8 per thread, all loads first
+    const auto xrr = make_rsrc(a.xr, (uint32_t)(a.b * n * 2));
+    const int hp = Kc >> 1, lhp = __builtin_ctz((unsigned)hp);
+    uint32_t v[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) red[rg * kcols + cg * 8 + e] = part[e];
+    for (int r = 0; r < 8; ++r) {
+      const int idx = tid + r * GEMV_THREADS;
+      const int c = idx >> lhp, p = idx & (hp - 1);
+      const bool ok = idx < NB * hp && 2 * p < kcols && c < a.b;
+      v[r] = buf_load_u32(xrr, ok ? (uint32_t)(((int64_t)c * n + c0 + 2 * p) * 2) : BUF_OFF);
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int idx = tid + r * GEMV_THREADS;
+      const int c = idx >> lhp, p = idx & (hp - 1);
+      if (idx < NB * hp) {
+        xh[idx] = v[r];
+        if constexpr (CODE == INST3) {
+          xd[c * Kc + 2 * p] = (v[r] & 0xFFFFu) * 0x10001u;
+          xd[c * Kc + 2 * p + 1] = (v[r] >> 16) * 0x10001u;
         }
-        __syncthreads();
-        for (int col = tid; col < kcols; col += GEMV_THREADS) {
-          float s = 0.f;
-          for (int rg = 0; rg < RG; ++rg) s += red[rg * kcols + col];
-          u[c * ustride + pad_index(col)] = s;
-        }
-        __syncthreads();
-      } else {
-        for (int col = tid; col < Kc; col += GEMV_THREADS) u[c * ustride + pad_index(col)] = 0.f;
       }
     }
     __syncthreads();
+  } else if (wave_rht) {
+    // u = the +/- combination of the arows strided rows, as below, but with
+    // lane = rgw * CG + cg: the row groups of a wave are summed with lane
+    // shuffles, the four waves through LDS, and H on segments of
+    // S = min(Kc, B_in) runs on the 8 values of a lane (index bits 0-2) and
+    // across the CG lanes (bits 3 and up).  Every wave ends with the whole
+    // x' of the chunk and stores the part its own tiles read.
+    fill_table();
+    const int cg = lane % CG;
+    float part[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[e] = 0.f;
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+      const int ih = tid / CG + r * RG;
+      const uint32_t chi = (uint32_t)__builtin_popcount((unsigned)(jhi & ih)) & 1u;
+      const uint32_t rw[4] = {xraw[r].x, xraw[r].y, xraw[r].z, xraw[r].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = h2f((uint16_t)(rw[e >> 1] >> (16 * (e & 1))));
+        const uint32_t neg = ((xsb[r] >> (((cg * 8) & 31) + e)) & 1u) ^ chi;
+        part[e] += neg ? -v : v;
+      }
+    }
+    for (int msk = CG; msk < 64; msk <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[e] += __shfl_xor(part[e], msk, 64);
+    }
+    if (lane < CG) {
+      float4* dst = reinterpret_cast<float4*>(wred + (wave * CG + cg) * 8);
+      dst[0] = make_float4(part[0], part[1], part[2], part[3]);
+      dst[1] = make_float4(part[4], part[5], part[6], part[7]);
+    }
+    __syncthreads();   // the partials of all waves, and the table
+    float u[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4* src = reinterpret_cast<const float4*>(wred + (w * CG + cg) * 8);
+      const float4 p0 = src[0], p1 = src[1];
+      u[0] += p0.x; u[1] += p0.y; u[2] += p0.z; u[3] += p0.w;
+      u[4] += p1.x; u[5] += p1.y; u[6] += p1.z; u[7] += p1.w;
+    }
     const int S = Kc < Bi ? Kc : Bi;
-    // transform each batch column's slice: segments of S within [0, kcols)
-    for (int c = 0; c < NB; ++c) {
-      if (c < a.b) fwht_segments(u + c * ustride, kcols, S, tid, GEMV_THREADS);
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+      if (h < S) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (!(e & h)) {
+            const float x0 = u[e], x1 = u[e + h];
+            u[e] = x0 + x1;
+            u[e + h] = x0 - x1;
+          }
+        }
+      }
+    }
+    for (int msk = 1; msk < (S >> 3); msk <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float o = __shfl_xor(u[e], msk, 64);
+        u[e] = (cg & msk) ? o - u[e] : u[e] + o;
+      }
     }
     const float rs = 1.0f / sqrtf((float)Bi);
-    for (int idx = tid; idx < NB * (Kc / 2); idx += GEMV_THREADS) {
-      const int c = idx / (Kc / 2), p = idx % (Kc / 2);
+    uint32_t hp[4];
+    float hsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = f2h_bits(u[2 * e] * rs), hi = f2h_bits(u[2 * e + 1] * rs);
+      hp[e] = lo | (hi << 16);
+      hsum += h2f((uint16_t)lo) + h2f((uint16_t)hi);
+    }
+    // this wave's tiles read column groups [2 tc_begin, 2 (tc_begin + tc_count))
+    if (lane < CG && cg >= 2 * tc_begin && cg < 2 * (tc_begin + tc_count)) {
+      *reinterpret_cast<uint4*>(xh + cg * 4) = make_uint4(hp[0], hp[1], hp[2], hp[3]);
+      if constexpr (CODE == INST3) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xd[cg * 8 + 2 * e] = (hp[e] & 0xFFFFu) * 0x10001u;
+          xd[cg * 8 + 2 * e + 1] = (hp[e] >> 16) * 0x10001u;
+        }
+      }
+    }
+    if constexpr (CODE == MAD1) {
+      for (int msk = 1; msk < CG; msk <<= 1) hsum += __shfl_xor(hsum, msk, 64);
+      if (wave == 0 && lane == 0) sx_sum[0] = hsum;   // read after the reduction's barriers
+    }
+  } else {
+    // u = the +/- combination of the arows strided rows (row ih enters with
+    // the sign H_arows[jhi][ih]), then H on segments of min(Kc, B_in)
+    // Every thread takes part: rows that do not exist were loaded as zeros,
+    // and thread tid writes red[8 tid .. 8 tid + 7] (rg * kcols + cg * 8 =
+    // 8 tid), inside the 2048 words of the region; rows rg >= RG are unread.
+    float* red = fA;                                 // [RG][kcols]
+    float* u = fA + GEMV_THREADS * 8;                // [padded Kc]
+    {
+      const int rg = tid / CG, cg = tid % CG;
+      float part[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[e] = 0.f;
+#pragma unroll
+      for (int r = 0; r < MAXR; ++r) {
+        const int ih = rg + r * RG;
+        const uint32_t chi = (uint32_t)__builtin_popcount((unsigned)(jhi & ih)) & 1u;
+        const uint32_t rw[4] = {xraw[r].x, xraw[r].y, xraw[r].z, xraw[r].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = h2f((uint16_t)(rw[e >> 1] >> (16 * (e & 1))));
+          const uint32_t neg = ((xsb[r] >> (((cg * 8) & 31) + e)) & 1u) ^ chi;
+          part[e] += neg ? -v : v;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[rg * kcols + cg * 8 + e] = part[e];
+    }
+    __syncthreads();
+    for (int col = tid; col < kcols; col += GEMV_THREADS) {
+      float sum = 0.f;
+      for (int rg = 0; rg < RG; ++rg) sum += red[rg * kcols + col];
+      u[pad_index(col)] = sum;
+    }
+    __syncthreads();
+    fwht_segments(u, kcols, Kc < Bi ? Kc : Bi, tid, GEMV_THREADS);
+    const float rs = 1.0f / sqrtf((float)Bi);
+    for (int p = tid; p < Kc / 2; p += GEMV_THREADS) {
       uint32_t v = 0;
-      if (2 * p < kcols && c < a.b) {
-        const uint32_t lo = f2h_bits(u[c * ustride + pad_index(2 * p)] * rs);
-        const uint32_t hi = f2h_bits(u[c * ustride + pad_index(2 * p + 1)] * rs);
+      if (2 * p < kcols) {
+        const uint32_t lo = f2h_bits(u[pad_index(2 * p)] * rs);
+        const uint32_t hi = f2h_bits(u[pad_index(2 * p + 1)] * rs);
         v = lo | (hi << 16);
       }
-      xh[idx] = v;
+      xh[p] = v;
       if constexpr (CODE == INST3) {
-        xd[c * Kc + 2 * p] = (v & 0xFFFFu) * 0x10001u;
-        xd[c * Kc + 2 * p + 1] = (v >> 16) * 0x10001u;
+        xd[2 * p] = (v & 0xFFFFu) * 0x10001u;
+        xd[2 * p + 1] = (v >> 16) * 0x10001u;
       }
     }
     __syncthreads();
   }
-  if constexpr (CODE == MAD1) {
+  if (CODE == MAD1 && !wave_rht) {
     // sum of the fp16 x' of the chunk, per batch column (bias removal)
     for (int c = wave; c < NB; c += 4) {
       float s = 0.f;
@@ -245,10 +412,10 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   }
 
   // ---- 3. lookup table --------------------------------------------------
-  if constexpr (CODE == HYB) fill_signed_table<COPIES>(regA, a.L.lut, a.L.Q, tid, GEMV_THREADS);
-  if constexpr (CODE == VQ) fill_plain_table<COPIES>(regA, a.L.lut, 1 << (2 * K), tid, GEMV_THREADS);
-  if constexpr (CODE == NUQ) fill_plain_table<1>(regA, a.L.lut, 1 << K, tid, GEMV_THREADS);
-  __syncthreads();
+  if (!wave_rht) {
+    fill_table();
+    __syncthreads();
+  }
 
   // ---- 4. stream the tiles ------------------------------------------------
   const int q = lane & 7, tl = lane >> 3;
@@ -260,13 +427,21 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int c = 0; c < NB; ++c) acc[r][c] = 0.f;
 
+  for (int j0 = 0; j0 < tc_count; j0 += PF) {
 #pragma unroll
-  for (int j = 0; j < GEMV_MAX_TPW; ++j) {
+  for (int jj = 0; jj < PF; ++jj) {
+    const int j = j0 + jj;
+    uint32_t w[K + 1];
+#pragma unroll
+    for (int i = 0; i < K; ++i) w[i] = buf[jj][i];
+    const uint32_t g0 = gsr[jj][0], g1 = gsr[jj][1];
+    (void)g0; (void)g1;
+    // refill this ring slot with the tile column 8 ahead (unconditionally:
+    // past the wave's last column the load is switched off by its offset)
+    buf_load_words<K>(crs, code_off(j + PF), buf[jj]);
+    gs_load(j + PF, gsr[jj]);
     if (j < tc_count) {
       const int tcl = tc_begin + j;   // tile column within the chunk
-      uint32_t w[K + 1];
-#pragma unroll
-      for (int i = 0; i < K; ++i) w[i] = buf[j][i];
       w[K] = next_lane_word(w[0], lane);
       if constexpr (CODE == INST3) {
 #pragma unroll
@@ -313,11 +488,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
                                                       acc[i >> 3][c], false);
           }
         } else {  // NUQ
-          const int64_t row0 = (int64_t)panel * 128 + tl * 16 + 2 * q;
-          const int64_t gcol = (c0 + tcl * 16) / a.L.group;
-          const int64_t gstride = n / a.L.group;
-          const float gs0 = h2f(a.L.gscale[row0 * gstride + gcol]);
-          const float gs1 = h2f(a.L.gscale[(row0 + 1) * gstride + gcol]);
+          const float gs0 = h2f((uint16_t)g0);
+          const float gs1 = h2f((uint16_t)g1);
           float part[2][NB];
 #pragma unroll
           for (int r = 0; r < 2; ++r)
@@ -342,48 +514,79 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
       }
     }
   }
+  }
 
   // ---- 5. reduce the waves, add into the fp32 accumulator -----------------
-  __syncthreads();   // table region becomes the reduction buffer
-  float* red = fA;   // [4 waves][128 rows][NB]
+  // Lane l of every wave holds partial sums of panel rows 2l and 2l + 1.
+  // One wave per batch column adds the four waves' partials, scales them and
+  // applies the output Hadamard stages that stay inside the panel
+  // (H_min(Bo,128) on the 128 rows: row bit 0 in registers, bits 1-6 across
+  // lanes), then adds the panel's sums into z; the cross-panel stages are
+  // the finisher's.
+  __syncthreads();   // the table region becomes the reduction buffer
+  float* red = fA;   // [4 waves][NB][128 rows]
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int c = 0; c < NB; ++c) red[(wave * 128 + tl * 16 + 2 * q + r) * NB + c] = acc[r][c];
-  __syncthreads();
-  // the panel's sums, scaled, then the output Hadamard stages that stay
-  // inside the panel (H_min(Bo,128) on 128 rows); the rest is the finisher's
-  float* pv = fA + 4 * 128 * NB;   // entry (c, row) at pad_index(c * 128 + row)
-  for (int idx = tid; idx < 128 * NB; idx += GEMV_THREADS) {
-    const int row = idx / NB, c = idx % NB;
-    float s = red[(0 * 128 + row) * NB + c] + red[(1 * 128 + row) * NB + c] +
-              red[(2 * 128 + row) * NB + c] + red[(3 * 128 + row) * NB + c];
-    if constexpr (CODE == MAD1) s -= MAD1_BIAS * sx_sum[c];
-    pv[pad_index(c * 128 + row)] = s * a.out_mult;
-  }
+  for (int c = 0; c < NB; ++c)
+    *reinterpret_cast<float2*>(red + (wave * NB + c) * 128 + 2 * lane) = make_float2(acc[0][c], acc[1][c]);
   __syncthreads();
   const int Bo = a.L.had_out;
-  if (Bo > 1) fwht_bits(pv, 128 * NB, 0, Bo >= 128 ? 7 : 31 - __builtin_clz((unsigned)Bo), tid, GEMV_THREADS);
-  for (int idx = tid; idx < 128 * NB; idx += GEMV_THREADS) {
-    const int c = idx >> 7, row = idx & 127;
-    if (c < a.b)
-      __hip_atomic_fetch_add(a.z + (int64_t)c * m + (int64_t)panel * 128 + row, pv[pad_index(c * 128 + row)],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int hbits = Bo >= 128 ? 7 : 31 - __builtin_clz((unsigned)Bo);
+  for (int c = wave; c < NB; c += 4) {
+    if (c < a.b) {
+      float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float2 p = *reinterpret_cast<const float2*>(red + (w * NB + c) * 128 + 2 * lane);
+        v0 += p.x;
+        v1 += p.y;
+      }
+      if constexpr (CODE == MAD1) {
+        v0 -= MAD1_BIAS * sx_sum[c];
+        v1 -= MAD1_BIAS * sx_sum[c];
+      }
+      v0 *= a.out_mult;
+      v1 *= a.out_mult;
+      if (hbits > 0) {
+        const float t = v0 + v1;
+        v1 = v0 - v1;
+        v0 = t;
+      }
+      for (int msk = 1; msk < (1 << (hbits > 0 ? hbits - 1 : 0)); msk <<= 1) {
+        const float o0 = __shfl_xor(v0, msk, 64), o1 = __shfl_xor(v1, msk, 64);
+        const bool hi = lane & msk;
+        v0 = hi ? o0 - v0 : v0 + o0;
+        v1 = hi ? o1 - v1 : v1 + o1;
+      }
+      float* zr = a.z + (int64_t)c * m + (int64_t)panel * 128 + 2 * lane;
+      __hip_atomic_fetch_add(zr, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(zr + 1, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
+}
+
+template <int CODE, int K, int NB, int PF, bool SL>
+hipError_t launch_gemv_v(const GemvArgs& a, hipStream_t stream) {
+  const size_t lds = gemv_lds_bytes<CODE, K, NB>(a.L.Q, a.Kc, a.U);
+  static size_t have = 0;
+  const hipError_t e =
+      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<CODE, K, NB, PF, SL>), lds, &have);
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)((a.L.m / 128) * a.nchunks);
+  hipLaunchKernelGGL((gemv_kernel<CODE, K, NB, PF, SL>), dim3(grid), dim3(GEMV_THREADS), lds, stream, a);
+  const hipError_t e1 = hipGetLastError();
+  if (e1 != hipSuccess) return e1;
+  return launch_gemv_finish(a, stream);
 }
 
 template <int CODE, int K, int NB>
 hipError_t launch_gemv_t(const GemvArgs& a, hipStream_t stream) {
-  const size_t lds = gemv_lds_bytes<CODE, K, NB>(a.L.Q, a.Kc, a.U);
-  static size_t have = 0;
-  const hipError_t e =
-      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<CODE, K, NB>), lds, &have);
-  if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)((a.L.m / 128) * a.nchunks);
-  hipLaunchKernelGGL((gemv_kernel<CODE, K, NB>), dim3(grid), dim3(GEMV_THREADS), lds, stream, a);
-  const hipError_t e1 = hipGetLastError();
-  if (e1 != hipSuccess) return e1;
-  return launch_gemv_finish(a, stream);
+  const bool sl = (NB > 1 || a.L.had_in <= 4096) && (CODE != HYB || a.L.Q <= 9);
+  if constexpr (NB == 1) {
+    if (a.Kc <= 128 && sl) return launch_gemv_v<CODE, K, NB, 2, true>(a, stream);
+    if (a.Kc <= 256 && sl) return launch_gemv_v<CODE, K, NB, 4, true>(a, stream);
+  }
+  if (sl) return launch_gemv_v<CODE, K, NB, 8, true>(a, stream);
+  return launch_gemv_v<CODE, K, NB, 8, false>(a, stream);
 }
 
 template <int CODE, int K>

@@ -247,13 +247,15 @@ __global__ __launch_bounds__(128) void gemv_finish_kernel(float* z, uint16_t* y,
   float* zc = z + c * m + row0;
   float v[P];
   uint32_t sg[P];
+  // sign words through a buffer that is empty without output signs (its
+  // loads read zero): no branch, so all 2P loads are in flight together
+  const auto srs = make_rsrc(sign_out, sign_out ? (uint32_t)(((m + 31) >> 5) * 4) : 0u);
 #pragma unroll
-  for (int j = 0; j < P; ++j) {
-    const int64_t r = row0 + j * 128;
-    sg[j] = sign_out ? (sign_out[r >> 5] >> (r & 31)) & 1u : 0u;
-  }
+  for (int j = 0; j < P; ++j) sg[j] = buf_load_u32(srs, (uint32_t)(((row0 + j * 128) >> 5) * 4));
 #pragma unroll
   for (int j = 0; j < P; ++j) v[j] = zc[j * 128];
+#pragma unroll
+  for (int j = 0; j < P; ++j) sg[j] = (sg[j] >> ((row0 + j * 128) & 31)) & 1u;
 #pragma unroll
   for (int j = 0; j < P; ++j) zc[j * 128] = 0.f;
   fwht_regs<P>(v);

@@ -67,32 +67,48 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   if constexpr (CODE == NUQ) fill_plain_table<1>(tab, a.L.lut, 1 << K, tid, GEMM_THREADS);
   const uint32_t* tabc = tab + (lane & (COPIES - 1));
 
-  // code words of this lane: tile (row 2*wave + tr, column 4*it + tc)
-  const uint32_t* cbase = a.L.codes + ((int64_t)panel * ntc * 8 + 2 * wave + tr) * (8 * K) + q * K;
+  // Every global load goes through a buffer resource and is issued
+  // unconditionally: a step beyond the split's range, a tile column beyond
+  // n, or a batch row beyond b gets an out-of-range offset and reads zeros
+  // without touching memory.  With no branch around them, the compiler
+  // waits for exactly the loads a step needs.
+  // Code words of this lane: tile (row 2*wave + tr, column 4*it + tc) of the
+  // panel; a panel's tile column is 8 tiles of 8K words.
+  const auto crs = make_rsrc(a.L.codes + (int64_t)panel * ntc * (64 * K), (uint32_t)(ntc * (256 * K)));
+  const uint32_t lane_code = (uint32_t)((2 * wave + tr) * (32 * K) + q * (4 * K));
+  // NUQ group scales of the lane's rows 2q, 2q+1 (fp16 [m][n/group])
+  const int64_t gstride = CODE == NUQ ? n / a.L.group : 0;
+  const int64_t grow0 = (int64_t)panel * 128 + (2 * wave + tr) * 16 + 2 * q;
+  const auto grs = make_rsrc(a.L.gscale, CODE == NUQ ? (uint32_t)(m * gstride * 2) : 0u);
   auto load_codes = [&](int64_t it, uint32_t* w) {
-    int64_t C = it * 4 + tc;
-    C = C < ntc ? C : ntc - 1;                        // in bounds; masked on use
-    load_words<K>(cbase + C * (8 * 8 * K), w);
+    const int64_t C = it * 4 + tc;
+    const bool ok = it < it1 && C < ntc;
+    buf_load_words<K>(crs, ok ? (uint32_t)C * (256u * K) + lane_code : BUF_OFF, w);
+    if constexpr (CODE == NUQ) {
+      const int64_t g = (C * 16) / a.L.group;
+      w[K] = buf_load_u16(grs, ok ? (uint32_t)((grow0 * gstride + g) * 2) : BUF_OFF);
+      w[K + 1] = buf_load_u16(grs, ok ? (uint32_t)(((grow0 + 1) * gstride + g) * 2) : BUF_OFF);
+    }
   };
   // X' chunks of this thread: batch row n0 + (tid >> 3), k chunk tid & 7 (x2)
+  const auto xrs = make_rsrc(a.xr, (uint32_t)(a.b * n * 2));
   auto load_x = [&](int64_t it, uint4* xv) {
 #pragma unroll
     for (int rep = 0; rep < 2; ++rep) {
       const int c = tid + rep * GEMM_THREADS;
       const int bb = c >> 3, ch = c & 7;
-      const int64_t row = (n0 + bb) < a.b ? (n0 + bb) : 0;
-      const int64_t kc = (it * 64 + ch * 8) < n ? (it * 64 + ch * 8) : 0;
-      xv[rep] = *reinterpret_cast<const uint4*>(a.xr + row * n + kc);
+      const int64_t row = n0 + bb, kc = it * 64 + ch * 8;
+      const bool ok = it < it1 && row < a.b && kc < n;
+      xv[rep] = buf_load_u4(xrs, ok ? (uint32_t)((row * n + kc) * 2) : BUF_OFF);
     }
   };
-  auto store_x = [&](int64_t it, const uint4* xv, int buf) {
+  auto store_x = [&](const uint4* xv, int buf) {
     char* Bt = Bs + buf * (64 * 128);
 #pragma unroll
     for (int rep = 0; rep < 2; ++rep) {
       const int c = tid + rep * GEMM_THREADS;
       const int bb = c >> 3, ch = c & 7;
-      const bool ok = (n0 + bb) < a.b && (it * 64 + ch * 8) < n;
-      *reinterpret_cast<uint4*>(Bt + gemm_swz(bb, ch * 8)) = ok ? xv[rep] : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(Bt + gemm_swz(bb, ch * 8)) = xv[rep];
     }
   };
 
@@ -104,26 +120,24 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
 
   // Decode step `it` (the lane's 32 weights) into the four A operands:
   // operand 2*ra + h is the chunk (tile row 2q + ra, columns 8h .. 8h+7).
+  // A tile column beyond n (only in the last step) is decoded from zero
+  // words and then zeroed, so no value of the table can leak into the sums.
   auto decode = [&](int64_t it, const uint32_t* wc, uint4* A) {
     uint32_t w[K + 1];
 #pragma unroll
     for (int i = 0; i < K; ++i) w[i] = wc[i];
     w[K] = next_lane_word(w[0], lane);
-    const int64_t C = it * 4 + tc;
+    float gs[2] = {0.f, 0.f};
+    if constexpr (CODE == NUQ) {
+      gs[0] = h2f((uint16_t)wc[K]);
+      gs[1] = h2f((uint16_t)wc[K + 1]);
+    }
     uint32_t out[16];
-    if (C < ntc) {
-      float gs[2] = {0.f, 0.f};
-      if constexpr (CODE == NUQ) {
-        const int64_t gstride = n / a.L.group;
-        const int64_t g = (C * 16) / a.L.group;
-        const int64_t row0 = (int64_t)panel * 128 + (2 * wave + tr) * 16 + 2 * q;
-        gs[0] = h2f(a.L.gscale[row0 * gstride + g]);
-        gs[1] = h2f(a.L.gscale[(row0 + 1) * gstride + g]);
-      }
-      lane_decode_exact<CODE, K, COPIES>(w, tabc, a.L.qshift, gs, out);
-    } else {
+    lane_decode_exact<CODE, K, COPIES>(w, tabc, a.L.qshift, gs, out);
+    if (it * 4 + 3 >= ntc) {                          // wave-uniform: the ragged step
+      const bool live = it * 4 + tc < ntc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) out[i] = 0u;
+      for (int i = 0; i < 16; ++i) out[i] = live ? out[i] : 0u;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) A[j] = make_uint4(out[4 * j], out[4 * j + 1], out[4 * j + 2], out[4 * j + 3]);
@@ -155,31 +169,30 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   // x[(s + 1) % 2] holds X'(s + 1).  A step multiplies s, then decodes s+1
   // (its VALU work overlaps the MFMAs in flight), stages X'(s+1) in the other
   // LDS buffer and refills the freed registers with steps s+5 and s+3.
-  uint32_t c0[K], c1[K], c2[K], c3[K];
+  constexpr int CW = CODE == NUQ ? K + 2 : K;        // code words (+ NUQ scales) per step
+  uint32_t c0[CW], c1[CW], c2[CW], c3[CW];
   uint4 x0[2], x1[2];
   uint4 A0[4], A1[4];
   auto one = [&](int64_t s, const uint4* Acur, uint4* Anext, uint32_t* cnext, uint4* xnext, int buf) {
     __syncthreads();
     mma(Acur, buf);
-    if (s + 1 < it1) {
-      decode(s + 1, cnext, Anext);
-      if (s + 5 < it1) load_codes(s + 5, cnext);
-      store_x(s + 1, xnext, buf ^ 1);
-      if (s + 3 < it1) load_x(s + 3, xnext);
-    }
+    decode(s + 1, cnext, Anext);          // past the range: decoded, never used
+    load_codes(s + 5, cnext);
+    store_x(xnext, buf ^ 1);
+    load_x(s + 3, xnext);
   };
   if (it0 < it1) {
     load_codes(it0, c0);
-    if (it0 + 1 < it1) load_codes(it0 + 1, c1);
-    if (it0 + 2 < it1) load_codes(it0 + 2, c2);
-    if (it0 + 3 < it1) load_codes(it0 + 3, c3);
+    load_codes(it0 + 1, c1);
+    load_codes(it0 + 2, c2);
+    load_codes(it0 + 3, c3);
     load_x(it0, x0);
-    if (it0 + 1 < it1) load_x(it0 + 1, x1);
+    load_x(it0 + 1, x1);
     __syncthreads();                                  // lookup table ready
-    store_x(it0, x0, 0);
-    if (it0 + 2 < it1) load_x(it0 + 2, x0);
+    store_x(x0, 0);
+    load_x(it0 + 2, x0);
     decode(it0, c0, A0);
-    if (it0 + 4 < it1) load_codes(it0 + 4, c0);
+    load_codes(it0 + 4, c0);
     for (int64_t s = it0; s < it1; s += 4) {
       one(s, A0, A1, c1, x1, 0);
       if (s + 1 >= it1) break;

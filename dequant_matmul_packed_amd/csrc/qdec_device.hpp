@@ -57,6 +57,47 @@ __device__ __forceinline__ uint32_t window_at(const uint32_t* w, int o) {
   return __builtin_amdgcn_alignbit(w[i], w[i + 1], 64 - r - L) & mask;
 }
 
+// ---------------------------------------------------------------------------
+// Raw buffer loads.  A buffer resource covers `bytes` bytes from a
+// wave-uniform base; a load whose byte offset lies at or beyond that size
+// returns zero and touches no memory.  Every load can therefore be issued
+// unconditionally and switched off through its offset: no branch around it,
+// so the compiler keeps exact counts of the loads in flight and waits only
+// for the one it needs (a load inside a branch ends in a wait for all of
+// them at the join).
+constexpr uint32_t BUF_OFF = 0x80000000u;   // an offset beyond every resource here
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <int K>
+__device__ __forceinline__ void buf_load_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* w) {
+  if constexpr (K == 1) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (K == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1];
+  } else if constexpr (K == 3) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
+  } else if constexpr (K == 4) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+  } else {
+#pragma unroll
+    for (int i = 0; i < K; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * i, 0, 0);
+  }
+}
+__device__ __forceinline__ uint4 buf_load_u4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t buf_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
 // First word of the next lane of the same 8-lane tile group (lane 7 wraps to
 // lane 0: the tail-biting stream).
 __device__ __forceinline__ uint32_t next_lane_word(uint32_t v, int lane) {
@@ -66,8 +107,11 @@ __device__ __forceinline__ uint32_t next_lane_word(uint32_t v, int lane) {
 
 // HYB hash: h = s*s + s (mod 2^16); the signed table index is h >> (15 - Q)
 // (Q index bits plus the sign bit 15).
+// Only bits below 16 of h are used, and they depend only on the low 16 bits
+// of s, so the 24-bit multiply-add (full rate) is exact here whatever the
+// bits of s above 16; a 32-bit product would be a quarter-rate instruction.
 __device__ __forceinline__ uint32_t hyb_signed_index(uint32_t s, int qshift) {
-  return ((s * s + s) & 0xFFFFu) >> qshift;
+  return ((__umul24(s, s) + s) & 0xFFFFu) >> qshift;
 }
 
 // 1MAD: LCG output for a state.

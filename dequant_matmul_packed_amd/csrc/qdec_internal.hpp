@@ -29,7 +29,7 @@ struct GemvArgs {
   int b;
   const uint16_t* xr;  // precomputed x' = RHT_in(x), fp16 [b][n], or NULL
   float* z;            // [b][m] fp32 split-K accumulator (workspace; zero on entry, left zero)
-  int Kc;              // columns per chunk (power of two, 64 .. 512)
+  int Kc;              // columns per chunk (power of two, 64 .. 2048; Kc * b <= 4096)
   int nchunks;         // ceil(n / Kc)
   int U;               // rows per output block = max(had_out, 128)
   float out_mult;      // layer scale x code factor / sqrt(had_out)
@@ -66,10 +66,9 @@ struct GemmArgs {
 // at zero; left zero), then the fp16 x' [b][n] of the separate-RHT path.
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 inline int gemv_unit_rows(int had_out) { return had_out > 128 ? had_out : 128; }
-// Input-chunk width of the fused GEMV: enough (panel, chunk) workgroups to
-// cover the 256 CUs several times, chunks a power of two in [64, 512].
+// Input-chunk width of the fused GEMV: about two (panel, chunk) workgroups
+// per CU, chunks a power of two in [64, 2048].
 int gemv_chunk(int64_t m, int64_t n, int64_t b);
-bool gemv_separate_rht();
 struct GemvWs {
   size_t z, xr, total;
 };

@@ -172,6 +172,32 @@ def test_gemv_small_matches_oracle(q, dev, code, k, b):
         assert err < REL_TOL, (m, n, err)
 
 
+@pytest.mark.parametrize("Q", [6, 10, 11])
+def test_hyb_table_sizes(q, dev, Q):
+    """HYB with lookup tables of 2^Q pairs other than the default 512: the
+    GEMV (one and three batch columns, fused and precomputed input RHT) and
+    the GEMM against the oracle, and the decode bit-exact."""
+    import torch
+    m, n = 384, 1024
+    host = synth.make_layer(synth.HYB, m, n, 2, Q=Q, tag="q%d" % Q)
+    lay = q.upload_layer(host, dev)
+    for b in (1, 3):
+        _say("hyb Q", Q, "gemv b", b)
+        x16 = synth.activations("qx%d" % b, b, n)
+        y = q.gemv(lay, _f16_tensor(x16, dev))
+        torch.cuda.synchronize()
+        assert _rel(_to_f64(y), oracle.forward(host, x16)) < REL_TOL, b
+    _say("hyb Q", Q, "gemm")
+    x16 = synth.activations("qx64", 64, n)
+    y = q.gemm(lay, _f16_tensor(x16, dev))
+    torch.cuda.synchronize()
+    assert _rel(_to_f64(y), oracle.forward(host, x16)) < REL_TOL
+    out = torch.zeros((host.n_tiles, 256), dtype=torch.int16, device=dev)
+    q.qdec_decode_tile(lay, 0, host.n_tiles, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), oracle.decode_tiles_storage(host, 0, host.n_tiles))
+
+
 def test_gemv_edge_cases(q, dev):
     import torch
     import dataclasses
@@ -180,13 +206,15 @@ def test_gemv_edge_cases(q, dev):
     x16 = synth.activations("edgex", 2, n)
     # no Hadamard at all (isolates the decoder), no signs, small blocks
     for kw in (dict(had_in=1, had_out=1), dict(sign_in=None, sign_out=None),
-               dict(had_in=16, had_out=128), dict(had_in=64, had_out=512)):
+               dict(had_in=16, had_out=128), dict(had_in=64, had_out=512),
+               dict(had_in=2, had_out=2), dict(had_in=4, had_out=8)):
         h2 = dataclasses.replace(host, **kw)
-        _say("gemv edge", kw)
         lay = q.upload_layer(h2, dev)
-        y = q.gemv(lay, _f16_tensor(x16, dev))
-        torch.cuda.synchronize()
-        assert _rel(_to_f64(y), oracle.forward(h2, x16)) < REL_TOL, kw
+        for b in (1, 2):     # the chunk transform in the workgroups, and the RHT kernel
+            _say("gemv edge", kw, "b", b)
+            y = q.gemv(lay, _f16_tensor(x16[:b], dev))
+            torch.cuda.synchronize()
+            assert _rel(_to_f64(y), oracle.forward(h2, x16[:b])) < REL_TOL, (kw, b)
     # zero input gives exactly zero output
     lay = q.upload_layer(host, dev)
     z = q.gemv(lay, torch.zeros((1, n), dtype=torch.float16, device=dev))
@@ -234,6 +262,31 @@ def test_gemv_full_size_sampled(q, dev, wname, spec, b):
         got = y[cols][:, blk * host.had_out:(blk + 1) * host.had_out]
         err = _rel(got, ref)
         assert err < REL_TOL, (blk, err)
+
+
+# Wide input chunks: 224 row panels make the GEMV pick 2048-column chunks at
+# b = 1, 2 (1024 at b = 3), so each wave streams 32 tile columns through its
+# prefetch ring; n = 5136 leaves a ragged 1040-column last chunk and a
+# 16-point input Hadamard block.
+WIDE_CASES = [(8192, 1, 3), (8192, 3, 3), (5136, 1, 2), (5136, 2, 2)]
+
+
+@pytest.mark.parametrize("n,b,k", WIDE_CASES, ids=["n%d_b%d_k%d" % c for c in WIDE_CASES])
+def test_gemv_wide_chunks_sampled(q, dev, n, b, k):
+    import torch
+    m = 28672
+    _say("gemv wide", m, n, b, k)
+    host = synth.make_layer(synth.HYB, m, n, k, tag="wide%d_%d" % (n, k))
+    x16 = synth.activations("widex%d" % n, b, n)
+    lay = q.upload_layer(host, dev)
+    y = _to_f64(q.gemv(lay, _f16_tensor(x16, dev)))
+    torch.cuda.synchronize()
+    nblk = host.m // host.had_out
+    cols = sorted({0, b - 1})
+    for blk in (0, nblk - 1):
+        ref = oracle.forward_block(host, x16, cols, blk)
+        got = y[cols][:, blk * host.had_out:(blk + 1) * host.had_out]
+        assert _rel(got, ref) < REL_TOL, blk
 
 
 # ---------------------------------------------------------------------------
