@@ -232,6 +232,28 @@ def test_gemv_edge_cases(q, dev):
     assert torch.count_nonzero(ws[:2 * m * 4]).item() == 0
 
 
+@pytest.mark.parametrize("m,had_out", [(1280, 256), (4096, 4096), (8192, 8192), (16384, 16384)])
+def test_gemv_output_blocks(q, dev, m, had_out):
+    """Output Hadamard blocks of 256 to 16384 rows (2 to 128 panels per block
+    in the finisher's cross-panel transform), at one and three batch
+    columns, twice on one workspace (left zeroed in between)."""
+    import torch
+    n = 256
+    host = synth.make_layer(synth.HYB, m, n, 2, had_out=had_out, tag="ob%d" % m)
+    lay = q.upload_layer(host, dev)
+    for b in (1, 3):
+        _say("gemv output blocks", m, had_out, "b", b)
+        x16 = synth.activations("obx%d" % b, b, n)
+        ref = oracle.forward(host, x16)
+        ws = q.workspace(lay, b, q.QDEC_OP_GEMV, dev)
+        xt = _f16_tensor(x16, dev)
+        for rep in range(2):
+            y = q.gemv(lay, xt, ws=ws)
+            torch.cuda.synchronize()
+            assert _rel(_to_f64(y), ref) < REL_TOL, (b, rep)
+        assert torch.count_nonzero(ws[:b * m * 4]).item() == 0
+
+
 def _full_gemv_cases():
     cases = []
     for wname in ("hyb4096", "computed4096", "llama3_8b_layer", "down_nuq", "down_vq"):
