@@ -89,70 +89,111 @@ bool decode_supported(int code, int k) {
 // ("Incoherence Processing (W2)": the RHT is invertible up to rounding.)
 // An fp32 input may be the sum of `nsum` slices `sum_stride` apart (the
 // K-split partial sums of the batched path).
-__global__ __launch_bounds__(256) void rht_kernel(RhtArgs a) {
+
+// Blocks of 1, 2 or 4 values: one value per thread.
+__global__ __launch_bounds__(256) void rht_tiny_kernel(RhtArgs a) {
   extern __shared__ __align__(16) float buf[];
-  constexpr int MAXJ = 8;            // 256 threads x 8 chunks x 8 values = 16384
   const int tid = threadIdx.x;
   const int B = a.block;
   const int64_t nblk = a.n / B;
   const int64_t row = blockIdx.x / nblk;
   const int64_t c0 = (blockIdx.x % nblk) * B;
   const int64_t off = row * a.n + c0;
-  if (B < 8) {                       // tiny blocks: one value per thread
-    for (int i = tid; i < B; i += 256) {
-      float v = 0.f;
-      if (a.in_f32) {
-        for (int sl = 0; sl < a.nsum; ++sl) v += ((const float*)a.in)[sl * a.sum_stride + off + i];
-      } else {
-        v = h2f(((const uint16_t*)a.in)[off + i]);
-      }
-      if (a.mode == 0) v *= sign_of(a.signs, c0 + i);
-      buf[pad_index(i)] = v;
-    }
-    __syncthreads();
-    if (B > 1) fwht_segments(buf, B, B, tid, 256);
-    for (int i = tid; i < B; i += 256) {
-      float v = buf[pad_index(i)] * a.mult;
-      if (a.mode == 1) v *= sign_of(a.signs, c0 + i);
-      if (a.out_f32) ((float*)a.out)[off + i] = v;
-      else ((uint16_t*)a.out)[off + i] = f2h_bits(v);
-    }
-    return;
-  }
-  // Chunks of 8 consecutive values.  Every global load (values and the
-  // chunk's sign word) is issued before any is used, with addresses clamped
-  // in bounds; the 3 butterfly stages inside a chunk run in registers, the
-  // rest in padded LDS.
-  const int nch = B >> 3;
-  float v[MAXJ][8];
-  uint32_t sw[MAXJ];
-#pragma unroll
-  for (int j = 0; j < MAXJ; ++j) {
-    const int ch = tid + 256 * j;
-    const int chc = ch < nch ? ch : 0;
-    const int64_t e0 = off + 8 * (int64_t)chc;
+  for (int i = tid; i < B; i += 256) {
+    float v = 0.f;
     if (a.in_f32) {
+      for (int sl = 0; sl < a.nsum; ++sl) v += ((const float*)a.in)[sl * a.sum_stride + off + i];
+    } else {
+      v = h2f(((const uint16_t*)a.in)[off + i]);
+    }
+    if (a.mode == 0) v *= sign_of(a.signs, c0 + i);
+    buf[pad_index(i)] = v;
+  }
+  __syncthreads();
+  if (B > 1) fwht_segments(buf, B, B, tid, 256);
+  for (int i = tid; i < B; i += 256) {
+    float v = buf[pad_index(i)] * a.mult;
+    if (a.mode == 1) v *= sign_of(a.signs, c0 + i);
+    if (a.out_f32) ((float*)a.out)[off + i] = v;
+    else ((uint16_t*)a.out)[off + i] = f2h_bits(v);
+  }
+}
+
+// Blocks of 8 or more: chunks of 8 consecutive values, chunk tid + 256 j for
+// j < J (J = B / 2048 rounded up to a power of two).  Every load goes
+// through a buffer resource and is issued unconditionally -- a chunk or a
+// slice that does not exist has an out-of-range offset and reads zeros --
+// so a thread's loads (all of them for fp16 input; SU slices at a time for
+// summed fp32 input) are in flight together.  The 3 butterfly stages inside
+// a chunk run in registers, the rest in padded LDS.
+template <bool IN_F32, int J>
+__global__ __launch_bounds__(256) void rht_kernel(RhtArgs a) {
+  extern __shared__ __align__(16) float buf[];
+  constexpr int SU = IN_F32 ? (J >= 4 ? 1 : 4 / J) : 1;   // fp32 slices per round
+  const int tid = threadIdx.x;
+  const int B = a.block;
+  const int64_t nblk = a.n / B;
+  const int64_t row = blockIdx.x / nblk;
+  const int64_t c0 = (blockIdx.x % nblk) * B;
+  const int64_t off = row * a.n + c0;
+  const int nch = B >> 3;
+  const auto srs = make_rsrc(a.signs, a.signs ? (uint32_t)(((a.n + 31) >> 5) * 4) : 0u);
+  uint32_t sw[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int ch = tid + 256 * j;
+    sw[j] = buf_load_u32(srs, ch < nch ? (uint32_t)(((c0 + 8 * ch) >> 5) * 4) : BUF_OFF);
+  }
+  float v[J][8];
+  if constexpr (IN_F32) {
+#pragma unroll
+    for (int j = 0; j < J; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
-      for (int sl = 0; sl < a.nsum; ++sl) {     // K-split slices of a GEMM
-        const float* src = (const float*)a.in + sl * a.sum_stride + e0;
-        const float4 p0 = *reinterpret_cast<const float4*>(src);
-        const float4 p1 = *reinterpret_cast<const float4*>(src + 4);
-        v[j][0] += p0.x; v[j][1] += p0.y; v[j][2] += p0.z; v[j][3] += p0.w;
-        v[j][4] += p1.x; v[j][5] += p1.y; v[j][6] += p1.z; v[j][7] += p1.w;
-      }
-    } else {
-      const uint4 p = *reinterpret_cast<const uint4*>((const uint16_t*)a.in + e0);
-      const uint32_t r[4] = {p.x, p.y, p.z, p.w};
+    const float* base = (const float*)a.in + off;
+    const auto irs = make_rsrc(base, (uint32_t)(((a.nsum - 1) * a.sum_stride + B) * 4));
+    for (int s0 = 0; s0 < a.nsum; s0 += SU) {
+      uint4 p[SU][J][2];
+#pragma unroll
+      for (int su = 0; su < SU; ++su)
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const int ch = tid + 256 * j;
+          const bool ok = ch < nch && s0 + su < a.nsum;
+          const uint32_t o = (uint32_t)(((s0 + su) * a.sum_stride + 8 * ch) * 4);
+          p[su][j][0] = buf_load_u4(irs, ok ? o : BUF_OFF);
+          p[su][j][1] = buf_load_u4(irs, ok ? o + 16u : BUF_OFF);
+        }
+#pragma unroll
+      for (int su = 0; su < SU; ++su)
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const uint32_t r[8] = {p[su][j][0].x, p[su][j][0].y, p[su][j][0].z, p[su][j][0].w,
+                                 p[su][j][1].x, p[su][j][1].y, p[su][j][1].z, p[su][j][1].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[j][e] += __builtin_bit_cast(float, r[e]);
+        }
+    }
+  } else {
+    const auto irs = make_rsrc((const uint16_t*)a.in + off, (uint32_t)B * 2u);
+    uint4 p[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int ch = tid + 256 * j;
+      p[j] = buf_load_u4(irs, ch < nch ? (uint32_t)ch * 16u : BUF_OFF);
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint32_t r[4] = {p[j].x, p[j].y, p[j].z, p[j].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[j][e] = h2f((uint16_t)(r[e >> 1] >> (16 * (e & 1))));
     }
-    const int64_t g = c0 + 8 * (int64_t)chc;
-    sw[j] = a.signs ? (a.signs[g >> 5] >> (g & 31)) : 0u;
   }
-  const int lowbits = B >= 8 ? 3 : 0;
+  // the chunk's 8 signs start at bit (c0 + 8 ch) & 31 of its word
 #pragma unroll
-  for (int j = 0; j < MAXJ; ++j) {
+  for (int j = 0; j < J; ++j) sw[j] >>= (c0 + 8 * (tid + 256 * j)) & 31;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
     const int ch = tid + 256 * j;
     if (ch < nch) {
       if (a.mode == 0) {
@@ -166,9 +207,9 @@ __global__ __launch_bounds__(256) void rht_kernel(RhtArgs a) {
     }
   }
   __syncthreads();
-  fwht_bits(buf, B, lowbits, 31 - __builtin_clz((unsigned)B), tid, 256);
+  fwht_bits(buf, B, 3, 31 - __builtin_clz((unsigned)B), tid, 256);
 #pragma unroll
-  for (int j = 0; j < MAXJ; ++j) {
+  for (int j = 0; j < J; ++j) {
     const int ch = tid + 256 * j;
     if (ch < nch) {
       float o[8];
@@ -192,15 +233,34 @@ __global__ __launch_bounds__(256) void rht_kernel(RhtArgs a) {
   }
 }
 
+template <bool IN_F32, int J>
+static hipError_t launch_rht_j(const RhtArgs& a, hipStream_t stream) {
+  static size_t have = 0;
+  const size_t lds = (size_t)padded_words(a.block) * 4;
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&rht_kernel<IN_F32, J>), lds, &have);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((rht_kernel<IN_F32, J>), dim3((unsigned)(a.rows * (a.n / a.block))), dim3(256), lds,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <bool IN_F32>
+static hipError_t launch_rht_in(const RhtArgs& a, hipStream_t stream) {
+  const int nch = a.block >> 3;
+  if (nch <= 256) return launch_rht_j<IN_F32, 1>(a, stream);
+  if (nch <= 512) return launch_rht_j<IN_F32, 2>(a, stream);
+  if (nch <= 1024) return launch_rht_j<IN_F32, 4>(a, stream);
+  return launch_rht_j<IN_F32, 8>(a, stream);
+}
+
 static hipError_t launch_rht_impl(const RhtArgs& a, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
-  static size_t have = 0;
-  const hipError_t e =
-      ensure_dynamic_lds(reinterpret_cast<const void*>(&rht_kernel), (size_t)padded_words(a.block) * 4, &have);
-  if (e != hipSuccess) return e;
-  const int64_t blocks = a.rows * (a.n / a.block);
-  hipLaunchKernelGGL(rht_kernel, dim3((unsigned)blocks), dim3(256), (size_t)padded_words(a.block) * 4, stream, a);
-  return hipGetLastError();
+  if (a.block < 8) {
+    const size_t lds = (size_t)padded_words(a.block) * 4;
+    hipLaunchKernelGGL(rht_tiny_kernel, dim3((unsigned)(a.rows * (a.n / a.block))), dim3(256), lds, stream, a);
+    return hipGetLastError();
+  }
+  return a.in_f32 ? launch_rht_in<true>(a, stream) : launch_rht_in<false>(a, stream);
 }
 
 hipError_t launch_rht(const RhtArgs& a, hipStream_t stream) {

@@ -56,11 +56,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   const int panel = blockIdx.x % npanels;
   const int split = blockIdx.x / npanels;
   const int n0 = blockIdx.y * 64;
-  const int64_t ntc = n >> 4;
-  const int64_t niter = (ntc + 3) >> 2;
-  const int64_t per = (niter + a.ksplit - 1) / a.ksplit;
-  const int64_t it0 = split * per;
-  const int64_t it1 = (it0 + per) < niter ? (it0 + per) : niter;
+  const int ntc = (int)(n >> 4);                    // tile columns (steps of 4)
+  const int niter = (ntc + 3) >> 2;
+  // steps per K split, a multiple of 4 (the loop's unroll) where possible
+  const int per = (((niter + a.ksplit - 1) / a.ksplit) + 3) & ~3;
+  const int it0 = split * per;
+  const int it1 = (it0 + per) < niter ? (it0 + per) : niter;
 
   if constexpr (CODE == HYB) fill_signed_table<COPIES>(tab, a.L.lut, a.L.Q, tid, GEMM_THREADS);
   if constexpr (CODE == VQ) fill_plain_table<COPIES>(tab, a.L.lut, 1 << (2 * K), tid, GEMM_THREADS);
@@ -71,36 +72,46 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   // unconditionally: a step beyond the split's range, a tile column beyond
   // n, or a batch row beyond b gets an out-of-range offset and reads zeros
   // without touching memory.  With no branch around them, the compiler
-  // waits for exactly the loads a step needs.
+  // waits for exactly the loads a step needs.  A load of step it is live
+  // while it is below the lane's limit (32-bit offsets: a panel's codes and
+  // X' stay far below 4 GiB).
   // Code words of this lane: tile (row 2*wave + tr, column 4*it + tc) of the
   // panel; a panel's tile column is 8 tiles of 8K words.
-  const auto crs = make_rsrc(a.L.codes + (int64_t)panel * ntc * (64 * K), (uint32_t)(ntc * (256 * K)));
-  const uint32_t lane_code = (uint32_t)((2 * wave + tr) * (32 * K) + q * (4 * K));
-  // NUQ group scales of the lane's rows 2q, 2q+1 (fp16 [m][n/group])
-  const int64_t gstride = CODE == NUQ ? n / a.L.group : 0;
-  const int64_t grow0 = (int64_t)panel * 128 + (2 * wave + tr) * 16 + 2 * q;
+  const auto crs = make_rsrc(a.L.codes + (int64_t)panel * ntc * (64 * K), (uint32_t)ntc * (256u * K));
+  const int itc = (ntc - tc + 3) >> 2 < it1 ? (ntc - tc + 3) >> 2 : it1;   // 4 it + tc < ntc
+  const uint32_t cbase = (uint32_t)tc * (256u * K) + (uint32_t)((2 * wave + tr) * (32 * K) + q * (4 * K));
+  // NUQ group scales of the lane's rows 2q, 2q+1 (fp16 [m][n/group]); a
+  // group spans gpt tile columns
+  const int gstride = CODE == NUQ ? (int)(n / a.L.group) : 0;
+  const int gpt = CODE == NUQ ? a.L.group >> 4 : 1;
+  const int grow0 = panel * 128 + (2 * wave + tr) * 16 + 2 * q;
   const auto grs = make_rsrc(a.L.gscale, CODE == NUQ ? (uint32_t)(m * gstride * 2) : 0u);
-  auto load_codes = [&](int64_t it, uint32_t* w) {
-    const int64_t C = it * 4 + tc;
-    const bool ok = it < it1 && C < ntc;
-    buf_load_words<K>(crs, ok ? (uint32_t)C * (256u * K) + lane_code : BUF_OFF, w);
+  auto load_codes = [&](int it, uint32_t* w) {
+    const bool ok = it < itc;
+    buf_load_words<K>(crs, ok ? cbase + (uint32_t)it * (1024u * K) : BUF_OFF, w);
     if constexpr (CODE == NUQ) {
-      const int64_t g = (C * 16) / a.L.group;
+      const int g = (it * 4 + tc) / gpt;
       w[K] = buf_load_u16(grs, ok ? (uint32_t)((grow0 * gstride + g) * 2) : BUF_OFF);
       w[K + 1] = buf_load_u16(grs, ok ? (uint32_t)(((grow0 + 1) * gstride + g) * 2) : BUF_OFF);
     }
   };
-  // X' chunks of this thread: batch row n0 + (tid >> 3), k chunk tid & 7 (x2)
+  // X' chunks of this thread: batch row n0 + (c >> 3), k chunk c & 7, for
+  // c = tid and tid + 256; chunk ch of step it is column 64 it + 8 ch
   const auto xrs = make_rsrc(a.xr, (uint32_t)(a.b * n * 2));
-  auto load_x = [&](int64_t it, uint4* xv) {
+  int itx[2];
+  uint32_t xbase[2];
 #pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      const int c = tid + rep * GEMM_THREADS;
-      const int bb = c >> 3, ch = c & 7;
-      const int64_t row = n0 + bb, kc = it * 64 + ch * 8;
-      const bool ok = it < it1 && row < a.b && kc < n;
-      xv[rep] = buf_load_u4(xrs, ok ? (uint32_t)((row * n + kc) * 2) : BUF_OFF);
-    }
+  for (int rep = 0; rep < 2; ++rep) {
+    const int c = tid + rep * GEMM_THREADS;
+    const int row = n0 + (c >> 3), ch = c & 7;
+    const int lim = (int)((n - ch * 8 + 63) >> 6);
+    itx[rep] = row < a.b ? (lim < it1 ? lim : it1) : 0;
+    xbase[rep] = (uint32_t)(((int64_t)(row < a.b ? row : 0) * n + ch * 8) * 2);
+  }
+  auto load_x = [&](int it, uint4* xv) {
+#pragma unroll
+    for (int rep = 0; rep < 2; ++rep)
+      xv[rep] = buf_load_u4(xrs, it < itx[rep] ? xbase[rep] + (uint32_t)it * 128u : BUF_OFF);
   };
   auto store_x = [&](const uint4* xv, int buf) {
     char* Bt = Bs + buf * (64 * 128);
@@ -122,7 +133,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   // operand 2*ra + h is the chunk (tile row 2q + ra, columns 8h .. 8h+7).
   // A tile column beyond n (only in the last step) is decoded from zero
   // words and then zeroed, so no value of the table can leak into the sums.
-  auto decode = [&](int64_t it, const uint32_t* wc, uint4* A) {
+  auto decode = [&](int it, const uint32_t* wc, uint4* A) {
     uint32_t w[K + 1];
 #pragma unroll
     for (int i = 0; i < K; ++i) w[i] = wc[i];
@@ -134,8 +145,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
     }
     uint32_t out[16];
     lane_decode_exact<CODE, K, COPIES>(w, tabc, a.L.qshift, gs, out);
-    if (it * 4 + 3 >= ntc) {                          // wave-uniform: the ragged step
-      const bool live = it * 4 + tc < ntc;
+    if (it * 4 + 3 >= ntc || it >= it1) {             // wave-uniform: the ragged or padding step
+      const bool live = it < it1 && it * 4 + tc < ntc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) out[i] = live ? out[i] : 0u;
     }
@@ -173,7 +184,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   uint32_t c0[CW], c1[CW], c2[CW], c3[CW];
   uint4 x0[2], x1[2];
   uint4 A0[4], A1[4];
-  auto one = [&](int64_t s, const uint4* Acur, uint4* Anext, uint32_t* cnext, uint4* xnext, int buf) {
+  auto one = [&](int s, const uint4* Acur, uint4* Anext, uint32_t* cnext, uint4* xnext, int buf) {
     __syncthreads();
     mma(Acur, buf);
     decode(s + 1, cnext, Anext);          // past the range: decoded, never used
@@ -193,13 +204,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
     load_x(it0 + 2, x0);
     decode(it0, c0, A0);
     load_codes(it0 + 4, c0);
-    for (int64_t s = it0; s < it1; s += 4) {
+    // whole groups of 4 steps; steps past it1 (at most 3) read zeros and
+    // add nothing
+    for (int s = it0; s < it1; s += 4) {
       one(s, A0, A1, c1, x1, 0);
-      if (s + 1 >= it1) break;
       one(s + 1, A1, A0, c2, x0, 1);
-      if (s + 2 >= it1) break;
       one(s + 2, A0, A1, c3, x1, 0);
-      if (s + 3 >= it1) break;
       one(s + 3, A1, A0, c0, x0, 1);
     }
   }
