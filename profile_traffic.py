@@ -67,7 +67,8 @@ def main():
     for k in sorted(fetch):
         if not k[0].startswith("qdec::gemv_kernel<"):
             continue
-        code, kk, nb = (int(v) for v in k[0][len("qdec::gemv_kernel<"):-1].split(","))
+        # template arguments: code, k, batch columns, code-ring depth, small loads
+        code, kk, nb = (int(v) for v in k[0][len("qdec::gemv_kernel<"):-1].split(",")[:3])
         fb = fetch[k][1] * 1024 * f_scale
         wb = write.get(k, (0, 0.0))[1] * 1024 * w_scale
         m = n = 4096
