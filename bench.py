@@ -259,6 +259,7 @@ def main():
               "pool_steps": P}
     if not args.no_detail and not args.only:
         detail.update(bench_llama_layer(q, torch, dev, stream))
+        detail.update(bench_llama_layer(q, torch, dev, stream, "llama3_8b_layer_fused"))
         detail.update(bench_gemm(q, torch, dev, stream))
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(specs, x16)
@@ -313,11 +314,12 @@ def measured_traffic(spec, us):
             "source": "profiles/gemv_hbm_traffic.md (FETCH_SIZE, WRITE_SIZE scaled by a 256 MiB copy)"}
 
 
-def bench_llama_layer(q, torch, dev, stream):
-    """Llama-3-8B-shaped decoder layer (7 fused GEMVs), microseconds per
-    layer at batch 1 and 8, rotating through distinct layer instances."""
+def bench_llama_layer(q, torch, dev, stream, name="llama3_8b_layer"):
+    """Llama-3-8B-shaped decoder layer (one fused GEMV per projection: 7, or
+    4 with QKV and gate+up fused), microseconds per layer at batch 1 and 8,
+    rotating through distinct layer instances."""
     import synth
-    wl = synth.WORKLOADS["llama3_8b_layer"]
+    wl = synth.WORKLOADS[name]
     layer_bytes = wl.code_bytes
     P = max(2, int(1200 * 2 ** 20 // layer_bytes))
     out = {}
@@ -354,9 +356,10 @@ def bench_llama_layer(q, torch, dev, stream):
         torch.cuda.synchronize()
         us = (time.perf_counter() - t0) / reps * 1e6
         del graphs
-        out["llama3_8b_layer_b%d" % b] = {"us_per_layer": round(us, 2),
-                                          "packed_GBps": round(layer_bytes / (us * 1e-6) / 1e9, 1)}
-        log("llama layer b=%d: %.2f us/layer" % (b, us))
+        out["%s_b%d" % (name, b)] = {"us_per_layer": round(us, 2),
+                                     "packed_GBps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
+                                     "gemv_calls": len(wl.layers)}
+        log("%s b=%d: %.2f us/layer" % (name, b, us))
         del calls
         pools.clear()
         torch.cuda.empty_cache()

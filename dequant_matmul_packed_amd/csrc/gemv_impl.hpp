@@ -70,12 +70,16 @@ __host__ __device__ inline size_t gemv_regA_bytes(int Q, int Kc, int U) {
   return (r + 15) & ~(size_t)15;
 }
 
-// Chunks of at most this many columns (one batch column, no ragged tail)
-// take the wave-level input RHT, which needs 4 x Kc fp32 of its own.
-constexpr int GEMV_WAVE_RHT_MAX = 256;
+// Full chunks of at most GEMV_WAVE_RHT_MAX columns (one batch column) take
+// the wave-level input RHT, whose exchange area holds 4 x Kc fp32.  Up to
+// GEMV_WRED_SEP_MAX columns that area has LDS of its own and the table is
+// filled before the transform; wider chunks borrow the table region and
+// fill the table after it.
+constexpr int GEMV_WAVE_RHT_MAX = 512;
+constexpr int GEMV_WRED_SEP_MAX = 256;
 template <int NB>
 __host__ __device__ inline size_t gemv_wred_bytes(int Kc) {
-  return (NB == 1 && Kc <= GEMV_WAVE_RHT_MAX) ? (size_t)4 * Kc * 4 : 0;
+  return (NB == 1 && Kc <= GEMV_WRED_SEP_MAX) ? (size_t)4 * Kc * 4 : 0;
 }
 template <int CODE, int K, int NB>
 __host__ __device__ inline size_t gemv_lds_bytes(int Q, int Kc, int U) {
@@ -127,7 +131,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   float* fA = reinterpret_cast<float*>(smem);
   uint32_t* xh = smem + regA_words;                 // [NB][Kc/2] fp16 pairs
   uint32_t* xd = xh + (size_t)NB * Kc / 2;           // [NB][Kc] duplicated (3INST)
-  float* wred = reinterpret_cast<float*>(xd + (CODE == INST3 ? (size_t)NB * Kc : 0));   // [4][Kc]
+  const bool wred_sep = NB == 1 && Kc <= GEMV_WRED_SEP_MAX;
+  float* wred = wred_sep ? reinterpret_cast<float*>(xd + (CODE == INST3 ? (size_t)NB * Kc : 0)) : fA;   // [4][Kc]
   __shared__ float sx_sum[NB];
 
   // ---- 0. (b = 1) the activations of the input RHT: issued first, so the
@@ -229,8 +234,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   };
 
   // ---- 2. input RHT of the chunk (b = 1), or load the precomputed x' ------
-  // A full chunk of at most 256 columns takes the wave-level transform:
-  // one barrier in all, and the table is filled before it.
+  // A full chunk of at most 512 columns takes the wave-level transform (one
+  // barrier; with a separate exchange area the table is filled before it).
   const bool wave_rht = !XR && Kc <= GEMV_WAVE_RHT_MAX && kcols == Kc;
   if constexpr (XR) {
     // NB * Kc / 2 <= 2048 fp16 pairs: at most 8 per thread, all loads first
@@ -264,7 +269,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
     // S = min(Kc, B_in) runs on the 8 values of a lane (index bits 0-2) and
     // across the CG lanes (bits 3 and up).  Every wave ends with the whole
     // x' of the chunk and stores the part its own tiles read.
-    fill_table();
+    if (wred_sep) fill_table();
     const int cg = lane % CG;
     float part[8];
 #pragma unroll
@@ -412,7 +417,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   }
 
   // ---- 3. lookup table --------------------------------------------------
-  if (!wave_rht) {
+  if (!wave_rht || !wred_sep) {
+    if (wave_rht) __syncthreads();   // every wave is done with the exchange area the table overwrites
     fill_table();
     __syncthreads();
   }

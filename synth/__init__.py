@@ -190,6 +190,15 @@ WORKLOADS = {
          LayerSpec("gate", HYB, 14336, 4096, 2), LayerSpec("up", HYB, 14336, 4096, 2),
          LayerSpec("down", HYB, 4096, 14336, 2)],
         [1, 8], "Llama-3-8B-shaped decoder layer, 7 linears, HYB k=2"),
+    # the same layer with the same-input projections fused: q, k, v as one
+    # 6144-row layer and gate, up as one 28672-row layer (each quantized as one
+    # matrix, so its output Hadamard block is the largest power of two
+    # dividing the fused m: 2048 and 4096); 4 GEMVs per layer instead of 7
+    "llama3_8b_layer_fused": Workload(
+        "llama3_8b_layer_fused",
+        [LayerSpec("qkv", HYB, 6144, 4096, 2), LayerSpec("o", HYB, 4096, 4096, 2),
+         LayerSpec("gate_up", HYB, 28672, 4096, 2), LayerSpec("down", HYB, 4096, 14336, 2)],
+        [1, 8], "Llama-3-8B-shaped layer with fused QKV and gate+up, HYB k=2"),
     # scalar / vector LUT variants on the down-projection shape, batch 1
     "down_nuq": Workload("down_nuq", [LayerSpec("down_nuq", NUQ, 4096, 14336, 3, scale=1.0)],
                          [1], "4096x14336 NUQ 3-bit, fp16 scale per 128 weights"),

@@ -103,7 +103,7 @@ def _full_layers():
 
 @pytest.mark.parametrize("wname,spec", _full_layers(), ids=[w + "/" + s.name for w, s in _full_layers()])
 def test_decode_tile_bit_exact_full_size(q, dev, wname, spec):
-    """Every tile of every layer of the five workloads."""
+    """Every tile of every layer of every workload."""
     import torch
     _say("decode full", wname, spec.name, spec.m, spec.n, spec.k)
     host = spec.build(wname)
@@ -256,7 +256,7 @@ def test_gemv_output_blocks(q, dev, m, had_out):
 
 def _full_gemv_cases():
     cases = []
-    for wname in ("hyb4096", "computed4096", "llama3_8b_layer", "down_nuq", "down_vq"):
+    for wname in ("hyb4096", "computed4096", "llama3_8b_layer", "llama3_8b_layer_fused", "down_nuq", "down_vq"):
         wl = synth.WORKLOADS[wname]
         for spec in wl.layers:
             for b in wl.batches:
