@@ -262,7 +262,17 @@ def main():
         detail.update(bench_llama_layer(q, torch, dev, stream, "llama3_8b_layer_fused"))
         detail.update(bench_gemm(q, torch, dev, stream))
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(specs, x16)
+    if not args.no_detail and not args.only:
+        ceil = measured_ceilings(torch, dev)
+        detail["measured_ceilings"] = ceil
+        g = detail.get("gemm_b64_up70b")
+        if g:
+            g["frac_of_measured_fp16_matmul"] = round(g["TFLOPs"] / ceil["fp16_matmul_8192_TFLOPs"], 4)
+        detail["headline_frac_of_measured_copy"] = round(dom_gbs / ceil["copy_GBps_read_plus_write"], 4)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu, cpu_detail = cpu_baseline(specs, x16)
+        detail["cpu_oracle"] = cpu_detail
 
     line = {
         "metric": METRIC,
@@ -407,22 +417,77 @@ def bench_gemm(q, torch, dev, stream):
 
 def cpu_baseline(specs, x16):
     """The oracle as it stands, on the host cores: one full forward per layer
-    of the step (decode of every tile, O(B^2) Hadamards, fp64 matvec)."""
+    of the step (decode of every tile, O(B^2) Hadamards, fp64 matvec) with
+    all threads; then, for the detail, decode-only on all threads and both
+    on one thread over the first layer.  It is a correctness reference, not
+    a tuned CPU competitor."""
     import oracle
     import synth
-    t_total = 0.0
-    nbytes = 0
-    for s in specs:
-        host = s.build("cpu_baseline")
+    threads = oracle.omp_threads()
+    hosts = [s.build("cpu_baseline") for s in specs]
+    nbytes = [s.m * s.n * s.k // 8 for s in specs]
+    nweights = [s.m * s.n for s in specs]
+
+    def timed(fn):
         t0 = time.perf_counter()
-        oracle.forward(host, x16)
-        t_total += time.perf_counter() - t0
-        nbytes += s.m * s.n * s.k // 8
-    gbs = nbytes / t_total / 1e9
-    log("cpu oracle: %.2f s for %d layers, %.4f GB/s" % (t_total, len(specs), gbs))
-    return {"value": round(gbs, 5), "unit": "GB/s", "cores": oracle.omp_threads(), "kind": "oracle",
+        fn()
+        return time.perf_counter() - t0
+    t_fwd = sum(timed(lambda h=h: oracle.forward(h, x16)) for h in hosts)
+    t_dec = sum(timed(lambda h=h: oracle.decode_tiles_storage(h, 0, h.n_tiles)) for h in hosts)
+    oracle.set_threads(1)
+    t_fwd1 = timed(lambda: oracle.forward(hosts[0], x16))
+    t_dec1 = timed(lambda: oracle.decode_tiles_storage(hosts[0], 0, hosts[0].n_tiles))
+    oracle.set_threads(threads)
+    gbs = sum(nbytes) / t_fwd / 1e9
+    log("cpu oracle: forward %.2f s for %d layers (%.4f GB/s, %d threads); one thread, one layer: "
+        "forward %.2f s, decode %.2f s" % (t_fwd, len(specs), gbs, threads, t_fwd1, t_dec1))
+    base = {"value": round(gbs, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "one full forward of each of the %d layers of one step (%.1f MiB of codes), "
-                      "%.2f s" % (len(specs), nbytes / 2 ** 20, t_total)}
+                      "%.2f s" % (len(specs), sum(nbytes) / 2 ** 20, t_fwd)}
+    detail = {"affinity_cores": len(os.sched_getaffinity(0)), "threads": threads,
+              "forward_GBps": round(gbs, 5),
+              "decode_Mweights_per_s": round(sum(nweights) / t_dec / 1e6, 2),
+              "one_thread_forward_GBps": round(nbytes[0] / t_fwd1 / 1e9, 5),
+              "one_thread_decode_Mweights_per_s": round(nweights[0] / t_dec1 / 1e6, 2),
+              "sample": "all threads: forward and decode-only of the %d layers; one thread: the first "
+                        "layer (%s)" % (len(specs), specs[0].name)}
+    return base, detail
+
+
+def measured_ceilings(torch, dev):
+    """What plain library kernels reach on this GPU: a device-to-device copy
+    (HBM read + write) and a large fp16 matmul (hipBLASLt, MFMA)."""
+    nbytes = 512 << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for r in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for r in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.float16, device=dev)
+    b = torch.randn(n, n, dtype=torch.float16, device=dev)
+    for r in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0.record()
+    for r in range(10):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    mm_tf = 2 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    log("measured ceilings: copy %.0f GB/s (read + write), fp16 matmul %d^3 %.0f TFLOP/s" % (copy_gbs, n, mm_tf))
+    return {"copy_GBps_read_plus_write": round(copy_gbs, 1),
+            "fp16_matmul_8192_TFLOPs": round(mm_tf, 1)}
 
 
 if __name__ == "__main__":

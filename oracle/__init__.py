@@ -87,6 +87,8 @@ def lib():
         L.orc_state_value.argtypes = [i32, i32, P, ctypes.c_uint32, P]
         L.orc_lloyd_max_gauss.argtypes = [i32, i32, P, P]
         L.orc_omp_threads.restype = i32
+        L.orc_set_threads.argtypes = [i32]
+        L.orc_set_threads.restype = None
         _lib = L
     return _lib
 
@@ -263,3 +265,8 @@ def lloyd_max_gauss(nlev: int, iters: int = 2000) -> tuple:
 
 def omp_threads() -> int:
     return int(lib().orc_omp_threads())
+
+
+def set_threads(n: int) -> None:
+    """Thread count of the oracle's OpenMP loops from now on."""
+    lib().orc_set_threads(int(n))

@@ -553,3 +553,14 @@ int orc_omp_threads(void) {
   return 1;
 #endif
 }
+
+/* Thread count of the OpenMP loops that follow (timing the oracle on one
+ * core and on all of them). */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
