@@ -1,0 +1,78 @@
+#!/usr/bin/env python3
+"""Summarise two rocprofv3 --pmc runs of the bench (SQ counters, eight per
+run) into profiles/sq_counters_bench.md.
+
+Usage (from the repository root R, after `cd /tmp && export TMPDIR=/tmp`):
+  rocprofv3 --pmc SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU \\
+      SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM SQ_VALU_MFMA_BUSY_CYCLES -d $R/gpurun_out/sq2/p1 -o run -- \\
+      python3 $R/bench.py --eager --steps 20 --warmup 5 --no-cpu-baseline
+  rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS \\
+      SQ_ACTIVE_INST_ANY SQ_INSTS_SALU SQ_LDS_ADDR_CONFLICT -d $R/gpurun_out/sq2/p2 -o run -- (same command)
+  python3 profile_counters.py gpurun_out/sq2/p1/run_results.db gpurun_out/sq2/p2/run_results.db
+
+Counters are per dispatch, summed over the chip; instruction counts are per
+wave (64 lanes).  For the two kernels the bench names (the 4096x4096 b=1
+GEMV of the headline, and the 28672x8192 b=64 GEMM) the script also gives
+VALU and LDS wave-instructions per weight.
+"""
+import os
+import sqlite3
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# (kernel name prefix, grid size in threads) -> weights per dispatch
+KNOWN = {("qdec::gemv_kernel<", 131072): 4096 * 4096,     # 4096x4096, b=1: 32 panels x 16 chunks
+         ("qdec::gemm_kernel<", 172032): 28672 * 8192}     # 28672x8192, b=64: 224 panels x 3 K splits
+
+
+def load(db):
+    c = sqlite3.connect(db)
+    rows = c.execute("select kernel_name, grid_size, counter_name, avg(value), count(*) "
+                     "from counters_collection group by kernel_name, grid_size, counter_name").fetchall()
+    out = {}
+    for kn, gs, cn, v, n in rows:
+        k = (kn.split("(")[0].replace("void ", ""), gs)
+        out.setdefault(k, {})[cn] = (v, n)
+    return out
+
+
+def main():
+    a, b = load(sys.argv[1]), load(sys.argv[2])
+    keys = [k for k in a if k in b and k[0].startswith("qdec::")]
+    keys.sort(key=lambda k: -a[k].get("SQ_WAVE_CYCLES", (0, 0))[0] * a[k].get("SQ_WAVE_CYCLES", (0, 1))[1])
+    lines = ["# SQ counters of the bench's kernels", "",
+             "Commands: two `rocprofv3 --pmc` runs of `python3 $R/bench.py --eager --steps 20 --warmup 5 "
+             "--no-cpu-baseline`, eight SQ counters each (the lists are in `profile_counters.py`), "
+             "summarised by `python3 profile_counters.py <pass 1 db> <pass 2 db>`.", "",
+             "Per dispatch, averaged over dispatches.  wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave time "
+             "waiting on a dependency); LDS wait = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES; bank = "
+             "SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS (conflict cycles per LDS issue cycle).", "",
+             "| kernel | grid | dispatches | VALU inst | LDS inst | MFMA inst | wait | LDS wait | bank | VALU/weight | LDS/weight |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in keys[:14]:
+        d = dict(a[k])
+        d.update(b[k])
+        g = lambda c: d.get(c, (0.0, 0))[0]
+        wc = g("SQ_WAVE_CYCLES") or 1.0
+        wts = None
+        for (pre, grid), w in KNOWN.items():
+            if k[0].startswith(pre) and k[1] == grid:
+                wts = w
+        vpw = "%.3f" % (g("SQ_INSTS_VALU") * 64 / wts) if wts else ""
+        lpw = "%.3f" % (g("SQ_INSTS_LDS") * 64 / wts) if wts else ""
+        lines.append("| `%s` | %d | %d | %.0f | %.0f | %.0f | %.2f | %.2f | %.2f | %s | %s |" % (
+            k[0], k[1], d.get("SQ_INSTS_VALU", (0, 0))[1], g("SQ_INSTS_VALU"), g("SQ_INSTS_LDS"),
+            g("SQ_INSTS_MFMA"), g("SQ_WAIT_INST_ANY") / wc, g("SQ_WAIT_INST_LDS") / wc,
+            g("SQ_LDS_BANK_CONFLICT") / (g("SQ_ACTIVE_INST_LDS") or 1.0), vpw, lpw))
+    lines += ["", "VALU/weight and LDS/weight are lane-instructions per weight (wave instructions x 64 / "
+              "weights) for the two dispatches whose shape is known from the grid: the b=1 GEMV counts "
+              "the decode and the dot products (v_dot2, one per two weights); the b=64 GEMM counts the "
+              "decode only (the products are MFMA instructions)."]
+    out = os.path.join(ROOT, "profiles", "sq_counters_bench.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()
