@@ -11,8 +11,13 @@ Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``
                              brute-force bijection on tiny trellises,
                              L = kV reduces to a direct table lookup
   f16_from_double            pinned: numpy's IEEE binary16 conversion
-  state_value (HYB)          pinned: every output is +/- a LUT pair; each of
-                             the 2^(Q+1) signed entries is hit equally often
+  state_value (HYB)          pinned: every output is +/- a LUT pair (V = 2)
+                             or value (V = 1); each of the 2^(Q+1) signed
+                             entries is hit equally often; hand-computed
+                             hashes of single states
+  state_value (LUT)          pinned: with a codebook whose entry e is the fp16
+                             pattern e, the decoded patterns are the states of
+                             the worked example of the bitshift trellis
   state_value (1MAD/3INST)   pinned by statistics only (near-Gaussian moments,
                              uncorrelated trellis neighbours) and closed forms
                              of single states; the exact constants of the
@@ -39,8 +44,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qdec_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-HYB, MAD1, INST3, NUQ, VQ = 1, 2, 3, 4, 5
-CODE_NAMES = {HYB: "HYB", MAD1: "1MAD", INST3: "3INST", NUQ: "NUQ", VQ: "VQ"}
+HYB, MAD1, INST3, NUQ, VQ, LUT = 1, 2, 3, 4, 5, 6
+CODE_NAMES = {HYB: "HYB", MAD1: "1MAD", INST3: "3INST", NUQ: "NUQ", VQ: "VQ", LUT: "LUT"}
 
 
 def build(force: bool = True) -> str:
@@ -84,7 +89,7 @@ def lib():
         L.orc_rht.argtypes = [P, P, i64, i64, i64, P, i32, ctypes.c_double]
         L.orc_forward.argtypes = [P, P, i64, P, P]
         L.orc_forward_block.argtypes = [P, P, i64, P, i64, i64, P]
-        L.orc_state_value.argtypes = [i32, i32, P, ctypes.c_uint32, P]
+        L.orc_state_value.argtypes = [i32, i32, i32, P, ctypes.c_uint32, P]
         L.orc_lloyd_max_gauss.argtypes = [i32, i32, P, P]
         L.orc_omp_threads.restype = i32
         L.orc_set_threads.argtypes = [i32]
@@ -240,18 +245,19 @@ def forward_block(layer, x_f16: np.ndarray, cols, block: int) -> np.ndarray:
     return y
 
 
-def state_value(code: int, s: int, Q: int = 9, lut=None) -> tuple:
+def state_value(code: int, s: int, Q: int = 9, lut=None, V: int = 2) -> tuple:
+    """fp16 bit patterns of the value(s) of state s (V matters for HYB only)."""
     lt = None if lut is None else np.ascontiguousarray(lut, dtype=np.uint32)
     out = np.zeros(2, dtype=np.uint16)
-    nv = lib().orc_state_value(code, Q, _ptr(lt), s, _ptr(out))
+    nv = lib().orc_state_value(code, V, Q, _ptr(lt), s, _ptr(out))
     if nv < 0:
         raise ValueError("state_value: bad code")
     return tuple(int(v) for v in out[:nv])
 
 
-def state_values_all(code: int, L: int = 16, Q: int = 9, lut=None) -> np.ndarray:
+def state_values_all(code: int, L: int = 16, Q: int = 9, lut=None, V: int = 2) -> np.ndarray:
     """Values of all 2^L states as fp16 bit patterns, shape (2^L, V)."""
-    rows = [state_value(code, s, Q, lut) for s in range(1 << L)]
+    rows = [state_value(code, s, Q, lut, V) for s in range(1 << L)]
     return np.array(rows, dtype=np.uint16)
 
 

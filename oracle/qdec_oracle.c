@@ -26,6 +26,10 @@
  *        a pseudo-Gaussian value, built on an LCG.
  *      "Incoherence Processing (W2)" -- the random Hadamard transform (RHT)
  *        on both sides, invertible up to rounding.
+ *      "Other hardware (e.g. ARM) (W3)" -- HYB with a one-dimensional
+ *        codebook (Q = 6, V = 1).
+ *      "Ablations and fast inference (W1 and W2)", Table A -- the pure-lookup
+ *        codebook of 2^L values (L = 16, V = 1: 16 * 2^L bits).
  *  - "Q-Palette" blog summary -- non-uniform scalar (NUQ) and vector (VQ)
  *    quantizers alongside TCQ.
  *  - QuIP# (arXiv 2402.04396) abstract and Fig. 2 -- RHT incoherence
@@ -40,7 +44,10 @@
  *    weights tV..tV+V-1; tiles stored in panels of 8 tile-rows, column-major
  *    inside a panel;
  *  - HYB hash h = s*s+s mod 2^16, index = bits [15-Q, 15) of h, sign = bit 15
- *    of h flipping both halves of the LUT pair;
+ *    of h flipping both halves of the LUT pair (V = 2) or the one value
+ *    (V = 1: the fp16 value is the low half of the LUT word);
+ *  - pure lookup: entry s of 2^L fp16 values packed two per LUT word (entry
+ *    e in the low half of word e/2 when e is even, the high half when odd);
  *  - 1MAD / 3INST constants are this library's own (not on the pages);
  *  - Sylvester-ordered Hadamard, 1/sqrt(B) normalisation, signs before H on
  *    the input and after H on the output, sign bit set means -1.
@@ -56,7 +63,7 @@
 
 /* ------------------------------------------------------------------------ */
 /* Code kinds (same numbering as the library's public header, restated).     */
-enum { ORC_HYB = 1, ORC_1MAD = 2, ORC_3INST = 3, ORC_NUQ = 4, ORC_VQ = 5 };
+enum { ORC_HYB = 1, ORC_1MAD = 2, ORC_3INST = 3, ORC_NUQ = 4, ORC_VQ = 5, ORC_LUT = 6 };
 
 /* Constants of the computed codes.  The pages name the codes and say they are
  * built on an LCG with a fixed instruction count; the numbers are this
@@ -191,6 +198,21 @@ static void orc_value_hyb(uint32_t s, int Q, const uint32_t *lut,
   out[1] = hi;
 }
 
+/* HYB at V = 1: the same hash and index; the value is the fp16 in the low
+ * half of the LUT word, its sign flipped by hash bit 15.                     */
+static uint16_t orc_value_hyb1(uint32_t s, int Q, const uint32_t *lut) {
+  uint32_t h = (s * s + s) & 0xFFFFu;
+  uint32_t idx = (h >> (15 - Q)) & ((1u << Q) - 1u);
+  uint16_t v = (uint16_t)(lut[idx] & 0xFFFFu);
+  return ((h >> 15) & 1u) ? (uint16_t)(v ^ 0x8000u) : v;
+}
+
+/* Pure lookup: the state itself indexes 2^L fp16 values, two per word.      */
+static uint16_t orc_value_lut(uint32_t s, const uint32_t *lut) {
+  uint32_t w = lut[s >> 1];
+  return (uint16_t)((s & 1u) ? (w >> 16) : (w & 0xFFFFu));
+}
+
 /* 1MAD: one LCG multiply-add on the state, then the sum of the four bytes of
  * the 32-bit result (a sum of four near-uniform bytes, mean 510, variance
  * 4*(256^2-1)/12 = 21845), centred and scaled to unit variance in fp32, then
@@ -226,8 +248,12 @@ int orc_validate(const orc_layer *Lr) {
   if (Lr->k < 1 || Lr->k > 8) return -1;
   switch (Lr->code) {
   case ORC_HYB:
-    if (Lr->V != 2 || Lr->L != 16 || Lr->Q < 1 || Lr->Q > 15 || !Lr->lut)
+    if ((Lr->V != 1 && Lr->V != 2) || Lr->L != 16 || Lr->Q < 1 || Lr->Q > 15 ||
+        !Lr->lut)
       return -1;
+    break;
+  case ORC_LUT:
+    if (Lr->V != 1 || Lr->L != 16 || !Lr->lut) return -1;
     break;
   case ORC_1MAD:
   case ORC_3INST:
@@ -291,7 +317,11 @@ static int orc_tile_values(const orc_layer *Lr, int64_t R, int64_t C,
     uint16_t v[2];
     double e[2];
     switch (Lr->code) {
-    case ORC_HYB: orc_value_hyb(s, Lr->Q, Lr->lut, v); break;
+    case ORC_HYB:
+      if (V == 2) orc_value_hyb(s, Lr->Q, Lr->lut, v);
+      else v[0] = orc_value_hyb1(s, Lr->Q, Lr->lut);
+      break;
+    case ORC_LUT: v[0] = orc_value_lut(s, Lr->lut); break;
     case ORC_1MAD: v[0] = orc_value_1mad(s); break;
     case ORC_3INST: v[0] = orc_value_3inst(s); break;
     case ORC_NUQ: {
@@ -493,10 +523,14 @@ int orc_forward_block(const orc_layer *Lr, const uint16_t *x, int64_t b,
 }
 
 /* Per-state value for statistics tests (V values as fp16 bit patterns).     */
-int orc_state_value(int code, int Q, const uint32_t *lut, uint32_t s,
+int orc_state_value(int code, int V, int Q, const uint32_t *lut, uint32_t s,
                     uint16_t out[2]) {
   switch (code) {
-  case ORC_HYB: orc_value_hyb(s, Q, lut, out); return 2;
+  case ORC_HYB:
+    if (V == 1) { out[0] = orc_value_hyb1(s, Q, lut); return 1; }
+    orc_value_hyb(s, Q, lut, out);
+    return 2;
+  case ORC_LUT: out[0] = orc_value_lut(s, lut); return 1;
   case ORC_1MAD: out[0] = orc_value_1mad(s); return 1;
   case ORC_3INST: out[0] = orc_value_3inst(s); return 1;
   default: return -1;

@@ -17,8 +17,8 @@ from typing import List, Optional
 
 import numpy as np
 
-HYB, MAD1, INST3, NUQ, VQ = 1, 2, 3, 4, 5
-CODE_NAMES = {HYB: "HYB", MAD1: "1MAD", INST3: "3INST", NUQ: "NUQ", VQ: "VQ"}
+HYB, MAD1, INST3, NUQ, VQ, LUT = 1, 2, 3, 4, 5, 6
+CODE_NAMES = {HYB: "HYB", MAD1: "1MAD", INST3: "3INST", NUQ: "NUQ", VQ: "VQ", LUT: "LUT"}
 
 # Optimal 8-level quantizer for a unit Gaussian (J. Max, "Quantizing for
 # minimum distortion", IRE Trans. IT-6, 1960, the N = 8 Gaussian row):
@@ -99,6 +99,8 @@ def make_layer(code: int, m: int, n: int, k: int, *, tag: str, V: Optional[int] 
     if code == HYB:
         V = 2 if V is None else V
         L = 16
+    elif code == LUT:
+        V, L = 1, 16
     elif code in (MAD1, INST3):
         V = 1
         L = 16
@@ -114,8 +116,12 @@ def make_layer(code: int, m: int, n: int, k: int, *, tag: str, V: Optional[int] 
     assert codes.size == nwords
     lut = gscale = None
     grp = 0
-    if code == HYB:
+    if code == HYB and V == 2:
         lut = normal_f16(rng_for(tag, "lut"), (1 << Q) * 2).view(np.uint32).copy()
+    elif code == HYB:        # V = 1: one fp16 value in the low half of each word
+        lut = normal_f16(rng_for(tag, "lut"), 1 << Q).astype(np.uint32)
+    elif code == LUT:        # 2^16 fp16 values, two per word
+        lut = normal_f16(rng_for(tag, "lut"), 1 << 16).view(np.uint32).copy()
     elif code == NUQ:
         if k != 3:
             raise ValueError("the textbook table here is the 8-level one (k = 3)")

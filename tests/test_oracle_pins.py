@@ -6,6 +6,7 @@ library routines (numpy's binary16 conversion, numpy matrix products,
 np.kron), invariants (H H^T = B I, Parseval, exact LUT coverage) and
 statistical properties the pages state for the computed codes.
 """
+import dataclasses
 import itertools
 import os
 
@@ -164,6 +165,68 @@ def test_hyb_covers_signed_codebook_uniformly():
     assert set(counts.values()) == {64}
     # codebook size from the bit accounting: 2^Q x V x 16 bits
     assert (1 << Q) * int(g["hyb_V"]) * 16 // 8 == int(g["hyb_codebook_bytes"]) == lut.nbytes
+
+
+@pytest.mark.parametrize("Q", [6, 9])
+def test_hyb_v1_covers_signed_codebook_uniformly(Q):
+    """HYB with a one-dimensional codebook ("Other hardware (W3)": Q = 6,
+    V = 1): every value is +/- the fp16 in the low half of a LUT word, and each
+    of the 2^(Q+1) signed entries is hit by exactly 2^16 / 2^(Q+1) states."""
+    # distinct positive fp16 values, in a seeded random order
+    lut = (synth.rng_for("pin", "hyb1_%d" % Q).permutation(1 << Q) + 0x2000).astype(np.uint32)
+    vals = oracle.state_values_all(oracle.HYB, 16, Q, lut, V=1)
+    assert vals.shape == (1 << 16, 1)
+    pos = {int(w): i for i, w in enumerate(lut)}
+    neg = {int(w) ^ 0x8000: i for i, w in enumerate(lut)}
+    counts = {}
+    for w in vals[:, 0]:
+        w = int(w)
+        key = ("+", pos[w]) if w in pos else ("-", neg[w])
+        counts[key] = counts.get(key, 0) + 1
+    assert len(counts) == 2 << Q
+    assert set(counts.values()) == {(1 << 16) >> (Q + 1)}
+
+
+# (state, Q, index, negative) worked out by hand from h = s*s + s mod 2^16,
+# index = bits [15-Q, 15) of h, sign = bit 15 of h:
+#   s = 0:      h = 0                                   -> index 0, +
+#   s = 0xFFFF: h = 0xFFFF * 0x10000 = 0 mod 2^16        -> index 0, +
+#   s = 0x00FF: h = 65025 + 255 = 65280 = 0xFF00         -> bit 15 set;
+#               Q = 6: 0xFF00 >> 9 = 127, & 63 = 63;  Q = 9: 0xFF00 >> 6 = 1020, & 511 = 508
+#   s = 0x0100: h = 65536 + 256 = 256 mod 2^16           -> Q = 6: 256 >> 9 = 0;  Q = 9: 256 >> 6 = 4
+#   s = 181:    h = 32761 + 181 = 32942 = 0x80AE         -> bit 15 set;
+#               Q = 6: 32942 >> 9 = 64, & 63 = 0;  Q = 9: 32942 >> 6 = 514, & 511 = 2
+HYB_HAND = [(0, 6, 0, False), (0xFFFF, 6, 0, False), (0x00FF, 6, 63, True), (0x0100, 6, 0, False),
+            (181, 6, 0, True), (0x00FF, 9, 508, True), (0x0100, 9, 4, False), (181, 9, 2, True)]
+
+
+@pytest.mark.parametrize("s,Q,idx,negative", HYB_HAND)
+def test_hyb_hash_of_single_states(s, Q, idx, negative):
+    lut1 = (np.arange(1 << Q, dtype=np.uint32) + 0x3C00)                  # distinct positive fp16
+    lut2 = lut1 | ((lut1 + 0x100) << 16)
+    (v1,) = oracle.state_value(oracle.HYB, s, Q, lut1, V=1)
+    assert v1 == (int(lut1[idx]) ^ (0x8000 if negative else 0))
+    lo, hi = oracle.state_value(oracle.HYB, s, Q, lut2, V=2)
+    flip = 0x8000 if negative else 0
+    assert (lo, hi) == (int(lut2[idx] & 0xFFFF) ^ flip, int(lut2[idx] >> 16) ^ flip)
+
+
+@pytest.mark.parametrize("k", [2, 3])
+def test_lut_code_decodes_the_states(k):
+    """Pure-lookup code (L = 16, V = 1; "Ablations and fast inference",
+    Table A): with a codebook whose entry e is the bit pattern e, a tile
+    decodes to its own trellis states, which the bit-serial walk (pinned by
+    the worked example) computes independently from the stream bits."""
+    lay = synth.make_layer(synth.LUT, 128, 32, k, tag="lutpin%d" % k)
+    ident = np.arange(1 << 16, dtype=np.uint32)
+    lay = dataclasses.replace(lay, lut=(ident[0::2] | (ident[1::2] << 16)).astype(np.uint32))
+    for R, C in [(0, 0), (3, 1), (7, 0)]:
+        got = oracle.decode_tile(lay, R, C)
+        i = oracle.tile_index(32, R, C)
+        words = lay.codes[i * 8 * k:(i + 1) * 8 * k]
+        bits = np.unpackbits(words.astype(">u4").view(np.uint8))
+        want = oracle.walk_bits(bits, 16, k, 256, True)
+        assert np.array_equal(got.astype(np.int64), want.astype(np.int64))
 
 
 # ---------------------------------------------------------------------------
@@ -354,7 +417,7 @@ def test_validate_rejects_bad_layers():
     good = synth.make_layer(synth.HYB, 128, 64, 2, tag="val")
     assert oracle.validate(good)
     import dataclasses
-    for bad in [dict(m=100), dict(n=40), dict(k=0), dict(Q=0), dict(V=1),
+    for bad in [dict(m=100), dict(n=40), dict(k=0), dict(Q=0), dict(V=3),
                 dict(had_in=3), dict(had_out=256), dict(L=12)]:
         assert not oracle.validate(dataclasses.replace(good, **bad)), bad
 
@@ -397,10 +460,12 @@ def _numpy_forward(layer, x16):
     return (so[:, None] * (Hout @ z)).T
 
 
-@pytest.mark.parametrize("code,k", [(synth.HYB, 2), (synth.MAD1, 3), (synth.INST3, 2),
-                                    (synth.VQ, 4), (synth.HYB, 3)])
-def test_forward_matches_numpy(code, k):
-    lay = synth.make_layer(code, 256, 96, k, tag="fwd%d%d" % (code, k), had_out=64)
+@pytest.mark.parametrize("code,k,V", [(synth.HYB, 2, 2), (synth.MAD1, 3, None), (synth.INST3, 2, None),
+                                      (synth.VQ, 4, None), (synth.HYB, 3, 2), (synth.HYB, 2, 1),
+                                      (synth.LUT, 3, None)])
+def test_forward_matches_numpy(code, k, V):
+    lay = synth.make_layer(code, 256, 96, k, tag="fwd%d%d" % (code, k), had_out=64, V=V,
+                           Q=6 if V == 1 else 9)
     x = synth.activations("fwdx", 2, 96)
     got = oracle.forward(lay, x)
     want = _numpy_forward(lay, x)
