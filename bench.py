@@ -93,15 +93,16 @@ def algorithmic_bytes(m, n, k, b, lut_bytes=0, gscale_bytes=0):
     return m * n * k // 8 + 2 * b * n + 2 * b * m + (m + n) // 8 + lut_bytes + gscale_bytes
 
 
-def make_pool_layers(q, torch, dev, code, m, n, k, count, tag):
-    """`count` layers sharing signs/LUT but with distinct random codes."""
+def make_pool_layers(q, torch, dev, code, m, n, k, count, tag, **kw):
+    """`count` layers sharing signs/LUT but with distinct random codes (extra
+    keyword arguments go to synth.make_layer, e.g. V and Q)."""
     import synth
     g = torch.Generator(device=dev)
     g.manual_seed(int.from_bytes(tag.encode()[:8].ljust(8, b"\0"), "little") & 0x7FFFFFFF)
     words = m * n * k // 32
     pool = torch.randint(-(1 << 31), (1 << 31) - 1, (count, words), dtype=torch.int32, device=dev,
                          generator=g)
-    host = synth.make_layer(code, m, n, k, tag=tag, codes=np.zeros(words, dtype=np.uint32))
+    host = synth.make_layer(code, m, n, k, tag=tag, codes=np.zeros(words, dtype=np.uint32), **kw)
     base = q.upload_layer(host, dev)
     layers = []
     for i in range(count):
@@ -261,6 +262,7 @@ def main():
         detail.update(bench_llama_layer(q, torch, dev, stream))
         detail.update(bench_llama_layer(q, torch, dev, stream, "llama3_8b_layer_fused"))
         detail.update(bench_gemm(q, torch, dev, stream))
+        detail.update(bench_code_variants(q, torch, dev))
 
     if not args.no_detail and not args.only:
         ceil = measured_ceilings(torch, dev)
@@ -374,6 +376,50 @@ def bench_llama_layer(q, torch, dev, stream, name="llama3_8b_layer"):
         pools.clear()
         torch.cuda.empty_cache()
     return out
+
+
+def bench_code_variants(q, torch, dev):
+    """The table-size knob of the trellis codes on one 4096x4096 k=2 layer at
+    b=1 and b=64: HYB with 2^9 pairs (V=2), HYB with a 2^6-value codebook
+    (V=1) and the pure lookup of 2^16 values (a 128 KiB table in LDS)."""
+    import synth
+    out = {}
+    for name, code, kw in (("HYB_V2_Q9", synth.HYB, dict(V=2, Q=9)), ("HYB_V1_Q6", synth.HYB, dict(V=1, Q=6)),
+                           ("LUT_L16", synth.LUT, {})):
+        layers, pool, base = make_pool_layers(q, torch, dev, code, 4096, 4096, 2, 16, "bench/var/" + name, **kw)
+        res = {}
+        for b in (1, 64):
+            x = torch.from_numpy(synth.activations("bench/var/x", b, 4096).view(np.int16)).to(dev)
+            y = torch.empty((b, 4096), dtype=torch.float16, device=dev)
+            op = q.QDEC_OP_GEMV if b == 1 else q.QDEC_OP_GEMM
+            ws = q.workspace(base, b, op, dev)
+            fn = "qdec_gemv" if b == 1 else "qdec_gemm"
+            calls = [LazyLaunch(q, fn, L, x, y, b, ws) for L in layers]
+            calls[0]()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(16):
+                    calls[i]()
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for r in range(5):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / 80
+            res["b%d_us" % b] = round(us, 2)
+            if b == 1:
+                res["b1_packed_GBps"] = round(4096 * 4096 * 2 / 8 / (us * 1e-6) / 1e9, 1)
+            else:
+                res["b64_TFLOPs"] = round(2 * 4096 * 4096 * 64 / (us * 1e-6) / 1e12, 1)
+            del g
+        out[name] = res
+        del layers, pool
+    log("code variants (4096x4096 k=2):", out)
+    return {"code_variants_4096_k2": out}
 
 
 def bench_gemm(q, torch, dev, stream):

@@ -18,7 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqdec.so")
 
 QDEC_OK, QDEC_EINVAL, QDEC_EUNSUPPORTED, QDEC_EWORKSPACE, QDEC_EHIP, QDEC_ENODEV = 0, -1, -2, -3, -4, -5
-QDEC_CODE_HYB, QDEC_CODE_1MAD, QDEC_CODE_3INST, QDEC_CODE_NUQ, QDEC_CODE_VQ = 1, 2, 3, 4, 5
+QDEC_CODE_HYB, QDEC_CODE_1MAD, QDEC_CODE_3INST, QDEC_CODE_NUQ, QDEC_CODE_VQ, QDEC_CODE_LUT = 1, 2, 3, 4, 5, 6
 QDEC_OP_GEMV, QDEC_OP_GEMM = 1, 2
 QDEC_ABI_VERSION = 1
 

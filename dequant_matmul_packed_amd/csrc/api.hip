@@ -16,6 +16,8 @@ hipError_t launch_gemv_mad1(const GemvArgs& a, hipStream_t stream);
 hipError_t launch_gemv_inst3(const GemvArgs& a, hipStream_t stream);
 hipError_t launch_gemv_nuq(const GemvArgs& a, hipStream_t stream);
 hipError_t launch_gemv_vq(const GemvArgs& a, hipStream_t stream);
+hipError_t launch_gemv_hyb1(const GemvArgs& a, hipStream_t stream);
+hipError_t launch_gemv_lut(const GemvArgs& a, hipStream_t stream);
 
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
   switch (a.L.code) {
@@ -24,12 +26,14 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
     case INST3: return launch_gemv_inst3(a, stream);
     case NUQ: return launch_gemv_nuq(a, stream);
     case VQ: return launch_gemv_vq(a, stream);
+    case HYB1: return launch_gemv_hyb1(a, stream);
+    case LUT: return launch_gemv_lut(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 bool gemv_supported(int code, int k, int b) {
-  return code >= HYB && code <= VQ && k >= 2 && k <= 4 && b >= 1 && b <= 8;
+  return code >= HYB && code <= HYB1 && k >= 2 && k <= 4 && b >= 1 && b <= 8;
 }
 }  // namespace qdec
 
@@ -53,9 +57,12 @@ int check_layer(const qdec_layer* L, LayerArgs* out) {
   if (!isfinite(L->layer_scale)) return QDEC_EINVAL;
   switch (L->code) {
     case QDEC_CODE_HYB:
-      if (L->L != 16 || L->V != 2 || L->Q < 1 || L->Q > 15 || !L->lut) return QDEC_EINVAL;
+      if (L->L != 16 || (L->V != 1 && L->V != 2) || L->Q < 1 || L->Q > 15 || !L->lut) return QDEC_EINVAL;
       if (L->k * L->V > L->L) return QDEC_EINVAL;
       if (L->Q > 11) return QDEC_EUNSUPPORTED;   // LDS table would exceed the budget
+      break;
+    case QDEC_CODE_LUT:
+      if (L->L != 16 || L->V != 1 || !L->lut) return QDEC_EINVAL;
       break;
     case QDEC_CODE_1MAD:
     case QDEC_CODE_3INST:
@@ -81,9 +88,9 @@ int check_layer(const qdec_layer* L, LayerArgs* out) {
     out->sign_out = L->sign_out;
     out->m = L->m;
     out->n = L->n;
-    out->code = L->code;
+    out->code = (L->code == QDEC_CODE_HYB && L->V == 1) ? HYB1 : L->code;
     out->k = L->k;
-    out->Q = L->code == QDEC_CODE_HYB ? L->Q : 0;
+    out->Q = L->code == QDEC_CODE_HYB ? L->Q : 0;   // both V = 1 and V = 2
     out->qshift = L->code == QDEC_CODE_HYB ? 15 - L->Q : 0;
     out->group = L->code == QDEC_CODE_NUQ ? L->group : 1;
     out->had_in = L->had_in;

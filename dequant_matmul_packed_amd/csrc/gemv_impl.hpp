@@ -45,14 +45,15 @@ constexpr int GEMV_THREADS = 256;
 template <int CODE>
 struct GemvTable {
   // LDS table copies (HYB, VQ); NUQ levels use one copy.
-  static constexpr int COPIES = (CODE == HYB || CODE == VQ) ? 8 : 1;
+  static constexpr int COPIES = (CODE == HYB || CODE == HYB1 || CODE == VQ) ? 8 : 1;
 };
 
 template <int CODE, int K>
 __host__ __device__ constexpr int gemv_table_words(int Q) {
-  return CODE == HYB ? (2 << Q) * GemvTable<CODE>::COPIES
+  return (CODE == HYB || CODE == HYB1) ? (2 << Q) * GemvTable<CODE>::COPIES
        : CODE == VQ ? (1 << (2 * K)) * GemvTable<CODE>::COPIES
-       : CODE == NUQ ? (1 << K) : 0;
+       : CODE == NUQ ? (1 << K)
+       : CODE == LUT ? (1 << 15) : 0;   // LUT: 2^16 fp16 values, two per word
 }
 
 // LDS of one workgroup: region A (lookup table; also the scratch of the
@@ -151,8 +152,9 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   uint32_t xsb[MAXR];
   // the lookup table's words, requested up front too: word tid + 256 i
   // (HYB: 2^Q <= 256 TW words; VQ 2^(2k) <= 256; NUQ 2^k <= 16)
-  constexpr int TW = CODE == HYB ? (SL ? 2 : 8) : 1;
-  const int nlut = CODE == HYB ? (1 << a.L.Q) : CODE == VQ ? (1 << (2 * K)) : CODE == NUQ ? (1 << K) : 0;
+  constexpr int TW = (CODE == HYB || CODE == HYB1) ? (SL ? 2 : 8) : 1;
+  const int nlut = (CODE == HYB || CODE == HYB1) ? (1 << a.L.Q)
+                 : CODE == VQ ? (1 << (2 * K)) : CODE == NUQ ? (1 << K) : 0;   // LUT: filled below
   uint32_t lw[TW];
   {
     const auto lrs = make_rsrc(a.L.lut, (uint32_t)nlut * 4u);
@@ -214,11 +216,14 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   for (int j = 0; j < PF; ++j) gs_load(j, gsr[j]);
   __builtin_amdgcn_sched_barrier(0);   // all requests out before any wait
 
-  // The LDS lookup table: HYB entry e and its sign-flipped twin e + 2^Q;
-  // VQ / NUQ as stored; each replicated COPIES times (entry e of copy c at
-  // word e * COPIES + c).
+  // The LDS lookup table: HYB entry e and its sign-flipped twin e + 2^Q
+  // (the flip covers both halves at V = 2, the low half at V = 1); VQ / NUQ
+  // as stored; each replicated COPIES times (entry e of copy c at word
+  // e * COPIES + c).  The pure lookup (LUT) copies its 128 KiB as it is, in
+  // rounds of 8 x 16 bytes per thread.
   auto fill_table = [&]() {
-    if constexpr (CODE == HYB || CODE == VQ || CODE == NUQ) {
+    if constexpr (CODE == HYB || CODE == HYB1 || CODE == VQ || CODE == NUQ) {
+      constexpr uint32_t FLIP = CODE == HYB ? 0x80008000u : 0x00008000u;
 #pragma unroll
       for (int i = 0; i < TW; ++i) {
         const int e = tid + i * GEMV_THREADS;
@@ -226,9 +231,19 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
 #pragma unroll
           for (int c = 0; c < COPIES; ++c) {
             regA[e * COPIES + c] = lw[i];
-            if constexpr (CODE == HYB) regA[(e + nlut) * COPIES + c] = lw[i] ^ 0x80008000u;
+            if constexpr (CODE == HYB || CODE == HYB1) regA[(e + nlut) * COPIES + c] = lw[i] ^ FLIP;
           }
         }
+      }
+    }
+    if constexpr (CODE == LUT) {
+      const auto trs = make_rsrc(a.L.lut, (1u << 15) * 4u);
+      for (int r0 = 0; r0 < (1 << 13); r0 += 8 * GEMV_THREADS) {   // 2^13 chunks of 16 bytes
+        uint4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = buf_load_u4(trs, (uint32_t)(r0 + tid + i * GEMV_THREADS) * 16u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) reinterpret_cast<uint4*>(regA)[r0 + tid + i * GEMV_THREADS] = v[i];
       }
     }
   };
@@ -493,6 +508,25 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
               acc[i >> 3][c] = __builtin_amdgcn_fdot2(as_h2(pv), as_h2(xp[c][i & 7]),
                                                       acc[i >> 3][c], false);
           }
+        } else if constexpr (CODE == HYB1 || CODE == LUT) {
+          // one table value per state (V = 1): two states per fp16 pair
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t s0 = window_at<L>(w, (2 * i) * KV);
+            const uint32_t s1 = window_at<L>(w, (2 * i + 1) * KV);
+            uint32_t pv;
+            if constexpr (CODE == HYB1) {
+              pv = (tabc[hyb_signed_index(s0, qshift) * COPIES] & 0xFFFFu) |
+                   (tabc[hyb_signed_index(s1, qshift) * COPIES] << 16);
+            } else {
+              const uint16_t* t16 = reinterpret_cast<const uint16_t*>(regA);
+              pv = (uint32_t)t16[s0] | ((uint32_t)t16[s1] << 16);
+            }
+#pragma unroll
+            for (int c = 0; c < NB; ++c)
+              acc[i >> 3][c] = __builtin_amdgcn_fdot2(as_h2(pv), as_h2(xp[c][i & 7]),
+                                                      acc[i >> 3][c], false);
+          }
         } else {  // NUQ
           const float gs0 = h2f((uint16_t)g0);
           const float gs1 = h2f((uint16_t)g1);
@@ -586,7 +620,7 @@ hipError_t launch_gemv_v(const GemvArgs& a, hipStream_t stream) {
 
 template <int CODE, int K, int NB>
 hipError_t launch_gemv_t(const GemvArgs& a, hipStream_t stream) {
-  const bool sl = (NB > 1 || a.L.had_in <= 4096) && (CODE != HYB || a.L.Q <= 9);
+  const bool sl = (NB > 1 || a.L.had_in <= 4096) && ((CODE != HYB && CODE != HYB1) || a.L.Q <= 9);
   if constexpr (NB == 1) {
     if (a.Kc <= 128 && sl) return launch_gemv_v<CODE, K, NB, 2, true>(a, stream);
     if (a.Kc <= 256 && sl) return launch_gemv_v<CODE, K, NB, 4, true>(a, stream);

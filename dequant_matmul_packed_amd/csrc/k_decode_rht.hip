@@ -15,6 +15,8 @@ __global__ __launch_bounds__(256) void decode_tile_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) uint32_t tab[];
   const int tid = threadIdx.x, lane = tid & 63, q = tid & 7;
   if constexpr (CODE == HYB) fill_signed_table<COPIES>(tab, a.L.lut, a.L.Q, tid, 256);
+  if constexpr (CODE == HYB1) fill_signed_table<COPIES, 0x8000u>(tab, a.L.lut, a.L.Q, tid, 256);
+  if constexpr (CODE == LUT) fill_plain_table<1>(tab, a.L.lut, 1 << 15, tid, 256);
   if constexpr (CODE == VQ) fill_plain_table<COPIES>(tab, a.L.lut, 1 << (2 * K), tid, 256);
   if constexpr (CODE == NUQ) fill_plain_table<1>(tab, a.L.lut, 1 << K, tid, 256);
   __syncthreads();
@@ -51,6 +53,9 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   constexpr int COPIES = GemvTable<CODE>::COPIES;
   const size_t lds = (size_t)gemv_table_words<CODE, K>(a.L.Q) * 4 + 16;
   (void)COPIES;
+  static size_t have = 0;
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&decode_tile_kernel<CODE, K>), lds, &have);
+  if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((a.count + 31) / 32);
   hipLaunchKernelGGL((decode_tile_kernel<CODE, K>), dim3(grid), dim3(256), lds, stream, a);
   return hipGetLastError();
@@ -74,12 +79,14 @@ hipError_t launch_decode_tile(const DecodeArgs& a, hipStream_t stream) {
     case INST3: return launch_decode_code<INST3>(a, stream);
     case NUQ: return launch_decode_code<NUQ>(a, stream);
     case VQ: return launch_decode_code<VQ>(a, stream);
+    case HYB1: return launch_decode_code<HYB1>(a, stream);
+    case LUT: return launch_decode_code<LUT>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 bool decode_supported(int code, int k) {
-  return code >= HYB && code <= VQ && k >= 2 && k <= 4;
+  return code >= HYB && code <= HYB1 && k >= 2 && k <= 4;
 }
 
 // ---------------------------------------------------------------------------

@@ -64,6 +64,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   const int it1 = (it0 + per) < niter ? (it0 + per) : niter;
 
   if constexpr (CODE == HYB) fill_signed_table<COPIES>(tab, a.L.lut, a.L.Q, tid, GEMM_THREADS);
+  if constexpr (CODE == HYB1) fill_signed_table<COPIES, 0x8000u>(tab, a.L.lut, a.L.Q, tid, GEMM_THREADS);
+  if constexpr (CODE == LUT) fill_plain_table<1>(tab, a.L.lut, 1 << 15, tid, GEMM_THREADS);
   if constexpr (CODE == VQ) fill_plain_table<COPIES>(tab, a.L.lut, 1 << (2 * K), tid, GEMM_THREADS);
   if constexpr (CODE == NUQ) fill_plain_table<1>(tab, a.L.lut, 1 << K, tid, GEMM_THREADS);
   const uint32_t* tabc = tab + (lane & (COPIES - 1));
@@ -262,10 +264,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     case INST3: return launch_gemm_code<INST3>(a, stream);
     case NUQ: return launch_gemm_code<NUQ>(a, stream);
     case VQ: return launch_gemm_code<VQ>(a, stream);
+    case HYB1: return launch_gemm_code<HYB1>(a, stream);
+    case LUT: return launch_gemm_code<LUT>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-bool gemm_supported(int code, int k) { return code >= HYB && code <= VQ && k >= 2 && k <= 4; }
+bool gemm_supported(int code, int k) { return code >= HYB && code <= HYB1 && k >= 2 && k <= 4; }
 
 }  // namespace qdec

@@ -20,7 +20,9 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
-enum { HYB = 1, MAD1 = 2, INST3 = 3, NUQ = 4, VQ = 5 };
+// Code kinds of the kernels: the public codes, with HYB split by V (HYB is
+// V = 2, HYB1 is V = 1, an internal number) and LUT the pure lookup.
+enum { HYB = 1, MAD1 = 2, INST3 = 3, NUQ = 4, VQ = 5, LUT = 6, HYB1 = 7 };
 
 __host__ __device__ constexpr int code_V(int code) { return (code == HYB || code == VQ) ? 2 : 1; }
 __host__ __device__ constexpr int code_L(int code, int k) {
@@ -140,13 +142,15 @@ __device__ __forceinline__ uint16_t inst3_value_bits(uint32_t s) {
 // times with entry e of copy c at word e*COPIES + c, so lanes that use
 // different copies fall in different banks.  VQ: 2^(2k) pairs, replicated
 // the same way.  NUQ: 2^k fp16 levels (one copy, broadcast reads).
-template <int COPIES>
+// FLIP is the sign flip of an entry: both halves (V = 2) or the low one
+// (V = 1, whose words carry one fp16 value in the low half).
+template <int COPIES, uint32_t FLIP = 0x80008000u>
 __device__ __forceinline__ void fill_signed_table(uint32_t* tab, const uint32_t* __restrict__ lut,
                                                   int Q, int tid, int nthreads) {
   const int E = 2 << Q;
   for (int e = tid; e < E; e += nthreads) {
     uint32_t v = lut[e & ((1 << Q) - 1)];
-    if (e >> Q) v ^= 0x80008000u;
+    if (e >> Q) v ^= FLIP;
 #pragma unroll
     for (int c = 0; c < COPIES; ++c) tab[e * COPIES + c] = v;
   }
@@ -192,6 +196,8 @@ __device__ __forceinline__ void lane_decode_exact(const uint32_t* w, const uint3
         const uint32_t s = window_at<L>(w, t * KV);
         if constexpr (CODE == MAD1) v[h] = mad1_value_bits(s);
         else if constexpr (CODE == INST3) v[h] = inst3_value_bits(s);
+        else if constexpr (CODE == HYB1) v[h] = tabc[hyb_signed_index(s, qshift) * COPIES] & 0xFFFFu;
+        else if constexpr (CODE == LUT) v[h] = reinterpret_cast<const uint16_t*>(tabc)[s];
         else {  // NUQ: fp16(level * group scale); the fp32 product is exact
           const uint16_t lvl = (uint16_t)tabc[s];
           v[h] = f2h_bits(h2f(lvl) * gs[i >> 3]);

@@ -26,6 +26,9 @@
  *                    [15-Q, 15) of h pick a fp16 pair from a 2^Q-entry LUT
  *                    and bit 15 of h flips the sign of both halves
  *                    (untitled ALU-op comment, "HYB Uniqueness (Q2)").
+ *                    With V = 1 the same index picks one fp16 value and bit
+ *                    15 flips its sign (a one-dimensional codebook, "Other
+ *                    hardware (e.g. ARM) (W3)": Q = 6, V = 1).
  *  - QDEC_CODE_1MAD  bitshift trellis, L = 16, V = 1; u = 0xEA4F79*s +
  *                    0xC2AA9973 (mod 2^32); value = fp16(fp32((b0+b1+b2+b3
  *                    - 510) * fp32(1/sqrt(21845)))), b_i the bytes of u.
@@ -43,6 +46,10 @@
  *                    V = 2, one 2k-bit index per weight pair into a 2^(2k)
  *                    table of fp16 pairs.  With L = kV the trellis reduces to
  *                    plain k-bit V-dim VQ ("Ablations and fast inference").
+ *  - QDEC_CODE_LUT   pure lookup ("Ablations and fast inference (W1 and
+ *                    W2)", Table A): bitshift trellis, L = 16, V = 1; the
+ *                    state itself indexes a table of 2^16 fp16 values
+ *                    (16 x 2^L bits = 128 KiB, held in LDS).
  *
  * Packed format (version 1).
  *  - W_hat is cut into 16x16 tiles; tile (R, C) covers rows 16R..16R+15 and
@@ -57,9 +64,12 @@
  *  - Tiles are stored in panels of 8 tile-rows (128 output rows); inside a
  *    panel, column by column: storage index of tile (R, C) is
  *      ((R / 8) * (n / 16) + C) * 8 + (R % 8).
- *  - HYB LUT: 2^Q uint32 words, each an fp16 pair (low half = first weight).
+ *  - HYB LUT: 2^Q uint32 words, each an fp16 pair (low half = first weight);
+ *    at V = 1, each word's low half is the value (the high half is ignored).
  *    NUQ table: 2^k uint32 words, fp16 level in the low half.  VQ table:
- *    2^(2k) uint32 words, fp16 pairs.  NUQ group scales: fp16 [m][n/group].
+ *    2^(2k) uint32 words, fp16 pairs.  LUT table: 2^15 uint32 words holding
+ *    the 2^16 fp16 values, entry e in the low half of word e/2 when e is
+ *    even, the high half when odd.  NUQ group scales: fp16 [m][n/group].
  *  - Sign vectors: bit j (bit j & 31 of word j >> 5) set means s[j] = -1;
  *    NULL means all +1.  They take n + m bits ("Bit Accounting (Q2)").
  *
@@ -102,16 +112,18 @@ typedef enum {
   QDEC_CODE_1MAD = 2,
   QDEC_CODE_3INST = 3,
   QDEC_CODE_NUQ = 4,
-  QDEC_CODE_VQ = 5
+  QDEC_CODE_VQ = 5,
+  QDEC_CODE_LUT = 6
 } qdec_code;
 
 /* One quantized linear layer.  Plain data; all pointers are device pointers
  * owned by the caller.  Supported combinations:
- *   HYB    L = 16, V = 2, k in {2, 3, 4}, Q in [1, 11]
+ *   HYB    L = 16, V = 2 or 1, k in {2, 3, 4}, Q in [1, 11]
  *   1MAD   L = 16, V = 1, k in {2, 3, 4}
  *   3INST  L = 16, V = 1, k in {2, 3, 4}
  *   NUQ    L = k,  V = 1, k in {2, 3, 4}, group a multiple of 16 dividing n
  *   VQ     L = 2k, V = 2, k in {2, 3, 4}
+ *   LUT    L = 16, V = 1, k in {2, 3, 4}
  * m % 128 == 0, n % 16 == 0; had_in (had_out) a power of two dividing n (m),
  * at most 16384; codes 16-byte aligned.                                      */
 typedef struct qdec_layer {
@@ -120,7 +132,7 @@ typedef struct qdec_layer {
   int32_t L, k, V, Q;            /* state bits, bits/weight, weights/step, HYB index bits */
   int64_t m, n;                  /* W_hat is m (out) x n (in)                 */
   const uint32_t *codes;         /* m*n*k/32 words, packed format above       */
-  const uint32_t *lut;           /* HYB / NUQ / VQ table (see format), else NULL */
+  const uint32_t *lut;           /* HYB / NUQ / VQ / LUT table (see format), else NULL */
   const uint16_t *group_scale;   /* NUQ: fp16 [m][n/group]; else NULL         */
   int32_t group;                 /* NUQ group length along a row; else 0      */
   float layer_scale;             /* multiplies every decoded value            */

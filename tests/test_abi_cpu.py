@@ -63,7 +63,9 @@ def test_workspace_sizes(q):
 
 
 BAD_LAYERS = [
-    dict(m=100), dict(n=40), dict(m=0), dict(k=0), dict(k=9), dict(Q=0), dict(V=1), dict(L=12),
+    dict(m=100), dict(n=40), dict(m=0), dict(k=0), dict(k=9), dict(Q=0), dict(V=3), dict(L=12),
+    dict(code=6, L=12, V=1), dict(code=6, L=16, V=2), dict(code=6, L=16, V=1, lut=None),
+    dict(code=1, V=1, k=9),
     dict(had_in=3), dict(had_in=256), dict(had_out=512), dict(codes=FAKE + 8), dict(codes=None),
     dict(lut=None), dict(code=9), dict(code=4, L=3, k=3, V=1, group=128, group_scale=None),
     dict(code=4, L=3, k=3, V=1, group=24, group_scale=FAKE), dict(code=5, L=6, k=2, V=2),

@@ -198,6 +198,51 @@ def test_hyb_table_sizes(q, dev, Q):
     assert np.array_equal(out.cpu().numpy().view(np.uint16), oracle.decode_tiles_storage(host, 0, host.n_tiles))
 
 
+# HYB with a one-dimensional codebook (V = 1) and the pure-lookup code (a
+# 128 KiB table of 2^16 fp16 values in LDS): decode, GEMV and GEMM.
+NEW_CODES = [(synth.HYB, 1, 6, 2), (synth.HYB, 1, 6, 3), (synth.HYB, 1, 9, 4),
+             (synth.LUT, None, 9, 2), (synth.LUT, None, 9, 3), (synth.LUT, None, 9, 4)]
+
+
+@pytest.mark.parametrize("code,V,Q,k", NEW_CODES, ids=["%s_V%s_Q%d_k%d" % (synth.CODE_NAMES[c], v, qq, kk)
+                                                      for c, v, qq, kk in NEW_CODES])
+def test_hyb1_and_lut_codes(q, dev, code, V, Q, k):
+    import torch
+    for (m, n) in [(384, 160), (256, 592), (1024, 1024)]:
+        host = synth.make_layer(code, m, n, k, V=V, Q=Q, tag="nc%d_%s_%d_%d_%d" % (code, V, Q, k, n))
+        lay = q.upload_layer(host, dev)
+        _say("new code decode", synth.CODE_NAMES[code], V, Q, k, m, n)
+        out = torch.zeros((host.n_tiles, 256), dtype=torch.int16, device=dev)
+        q.qdec_decode_tile(lay, 0, host.n_tiles, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), oracle.decode_tiles_storage(host, 0, host.n_tiles))
+        for b in (1, 3, 8):
+            _say("new code gemv", b)
+            x16 = synth.activations("ncx%d_%d" % (b, n), b, n)
+            y = q.gemv(lay, _f16_tensor(x16, dev))
+            torch.cuda.synchronize()
+            assert _rel(_to_f64(y), oracle.forward(host, x16)) < REL_TOL, (m, n, b)
+        _say("new code gemm")
+        x16 = synth.activations("ncx64_%d" % n, 70, n)
+        y = q.gemm(lay, _f16_tensor(x16, dev))
+        torch.cuda.synchronize()
+        assert _rel(_to_f64(y), oracle.forward(host, x16)) < REL_TOL, (m, n)
+
+
+@pytest.mark.parametrize("code,V,Q", [(synth.HYB, 1, 6), (synth.LUT, None, 9)])
+def test_hyb1_and_lut_full_size_sampled(q, dev, code, V, Q):
+    """4096 x 4096 at k = 2, b = 1 (the launch the bench would time)."""
+    import torch
+    host = synth.make_layer(code, 4096, 4096, 2, V=V, Q=Q, tag="ncfull%d" % code)
+    x16 = synth.activations("ncfullx", 1, 4096)
+    lay = q.upload_layer(host, dev)
+    _say("new code full", synth.CODE_NAMES[code], V)
+    y = _to_f64(q.gemv(lay, _f16_tensor(x16, dev)))
+    torch.cuda.synchronize()
+    ref = oracle.forward_block(host, x16, [0], 0)
+    assert _rel(y[[0]][:, :4096], ref) < REL_TOL
+
+
 def test_gemv_edge_cases(q, dev):
     import torch
     import dataclasses
