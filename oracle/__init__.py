@@ -23,6 +23,11 @@ Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``
                              of single states; the exact constants of the
                              original codes are not on the pages, so parity
                              with them is unpinned
+  fractional kV, half-TCQ    pinned: bits per weight of the Q-Palette
+                             examples (2.5; 2.5 and 3 giving 2.75); each
+                             tile the cyclic walk of its 128 kV-bit stream
+                             (numpy slicing); even kV equals the integer k;
+                             a two-part layer decodes as two layers stacked
   rht                        pinned: H H^T = B I, Kronecker recursion,
                              Parseval, round trip, numpy's matrix product
   forward / forward_block    pinned: a small layer against an independent
@@ -102,6 +107,7 @@ class _OrcLayer(ctypes.Structure):
     _fields_ = [
         ("code", ctypes.c_int32), ("L", ctypes.c_int32), ("k", ctypes.c_int32),
         ("V", ctypes.c_int32), ("Q", ctypes.c_int32),
+        ("kv", ctypes.c_int32), ("kv_b", ctypes.c_int32), ("m_a", ctypes.c_int64),
         ("m", ctypes.c_int64), ("n", ctypes.c_int64),
         ("codes", ctypes.c_void_p), ("lut", ctypes.c_void_p),
         ("gscale", ctypes.c_void_p), ("group", ctypes.c_int32),
@@ -135,8 +141,9 @@ def _struct(layer) -> tuple:
     gs = arr(layer.gscale, np.uint16)
     si = arr(layer.sign_in, np.uint32)
     so = arr(layer.sign_out, np.uint32)
-    s = _OrcLayer(layer.code, layer.L, layer.k, layer.V, layer.Q, layer.m,
-                  layer.n, _ptr(codes), _ptr(lut), _ptr(gs), layer.group,
+    s = _OrcLayer(layer.code, layer.L, layer.k, layer.V, layer.Q,
+                  getattr(layer, "kv", 0), getattr(layer, "kv_b", 0), getattr(layer, "m_a", 0),
+                  layer.m, layer.n, _ptr(codes), _ptr(lut), _ptr(gs), layer.group,
                   layer.scale, _ptr(si), _ptr(so), layer.had_in, layer.had_out)
     return s, keep
 

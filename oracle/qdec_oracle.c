@@ -30,6 +30,11 @@
  *        codebook (Q = 6, V = 1).
  *      "Ablations and fast inference (W1 and W2)", Table A -- the pure-lookup
  *        codebook of 2^L values (L = 16, V = 1: 16 * 2^L bits).
+ *  - "Q-Palette" blog summary -- fractional bit widths (2.5 bits and the
+ *    like) and half-TCQ, two trellis bit widths in one layer (2.5 and 3 bits
+ *    giving 2.75).  Here a trellis step may take any whole number kV of bits,
+ *    so V = 2 gives k = kV/2 (2.5 bits at kV = 5), and the rows of a layer
+ *    may be cut at a panel boundary into two parts of different kV.
  *  - "Q-Palette" blog summary -- non-uniform scalar (NUQ) and vector (VQ)
  *    quantizers alongside TCQ.
  *  - QuIP# (arXiv 2402.04396) abstract and Fig. 2 -- RHT incoherence
@@ -38,7 +43,11 @@
  * Readings where the pages are silent (each is also a format rule the HIP
  * library implements independently):
  *  - tail-biting per 256-weight tile: the state window wraps around the end of
- *    the tile's 256*k-bit stream, so storage is exactly k bits per weight;
+ *    the tile's (256/V)*kV-bit stream, so storage is exactly kV/V bits per
+ *    weight;
+ *  - half-TCQ: rows [0, m_a) at kv, rows [m_a, m) at kv_b, m_a a multiple of
+ *    128; the tiles of the first part are stored first (panel layout over its
+ *    own rows), then those of the second part;
  *  - stream bits are MSB-first in little-endian u32 words;
  *  - 16x16 tiles, weight j of a tile at (row j>>4, col j&15), step t covering
  *    weights tV..tV+V-1; tiles stored in panels of 8 tile-rows, column-major
@@ -78,6 +87,9 @@ enum { ORC_HYB = 1, ORC_1MAD = 2, ORC_3INST = 3, ORC_NUQ = 4, ORC_VQ = 5, ORC_LU
 
 typedef struct {
   int32_t code, L, k, V, Q;
+  int32_t kv;              /* bits per trellis step of rows [0, m_a); 0 = k*V */
+  int32_t kv_b;            /* bits per step of rows [m_a, m); 0 = one part */
+  int64_t m_a;             /* rows of the first part; 0 = all rows        */
   int64_t m, n;
   const uint32_t *codes;   /* packed tile streams                         */
   const uint32_t *lut;     /* HYB: 2^Q pairs; NUQ: 2^k levels; VQ: 2^(kV) */
@@ -242,10 +254,31 @@ static uint16_t orc_value_3inst(uint32_t s) {
 
 static int orc_is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
+static int orc_is_trellis(int code) {
+  return code == ORC_HYB || code == ORC_1MAD || code == ORC_3INST || code == ORC_LUT;
+}
+
+/* Bits per trellis step of the first part, of the second part, and the rows
+ * of the first part (a layer with one part: m_a = m, kv_b = kv).            */
+static int orc_kv_a(const orc_layer *Lr) { return Lr->kv ? Lr->kv : Lr->k * Lr->V; }
+static int orc_kv_b(const orc_layer *Lr) { return Lr->m_a ? Lr->kv_b : orc_kv_a(Lr); }
+static int64_t orc_m_a(const orc_layer *Lr) { return Lr->m_a ? Lr->m_a : Lr->m; }
+
 int orc_validate(const orc_layer *Lr) {
   if (!Lr || !Lr->codes) return -1;
   if (Lr->m <= 0 || Lr->n <= 0 || Lr->m % 128 || Lr->n % 16) return -1;
-  if (Lr->k < 1 || Lr->k > 8) return -1;
+  if (Lr->kv == 0) {
+    if (Lr->k < 1 || Lr->k > 8) return -1;
+  } else if (Lr->k != 0 || !orc_is_trellis(Lr->code)) {
+    return -1;
+  }
+  if (Lr->m_a) {
+    if (!orc_is_trellis(Lr->code) || Lr->m_a < 0 || Lr->m_a >= Lr->m || Lr->m_a % 128 ||
+        Lr->kv_b < 1)
+      return -1;
+  } else if (Lr->kv_b) {
+    return -1;
+  }
   switch (Lr->code) {
   case ORC_HYB:
     if ((Lr->V != 1 && Lr->V != 2) || Lr->L != 16 || Lr->Q < 1 || Lr->Q > 15 ||
@@ -269,7 +302,8 @@ int orc_validate(const orc_layer *Lr) {
   default:
     return -1;
   }
-  if (Lr->k * Lr->V > Lr->L) return -1;
+  if (orc_kv_a(Lr) < 1 || orc_kv_a(Lr) > Lr->L) return -1;
+  if (orc_kv_b(Lr) < 1 || orc_kv_b(Lr) > Lr->L) return -1;
   if (!orc_is_pow2(Lr->had_in) || Lr->n % Lr->had_in) return -1;
   if (!orc_is_pow2(Lr->had_out) || Lr->m % Lr->had_out) return -1;
   return 0;
@@ -291,14 +325,43 @@ void orc_tile_coords(int64_t n, int64_t index, int64_t *R, int64_t *C) {
   *R = (rest / tiles_per_row) * 8 + r8;
 }
 
-/* States of tile (R, C): the stream is the tile's 256*k bits, walked
+/* Where tile (R, C) lives: its step width kV and its first code word.  The
+ * tile stream holds 256/V steps of kV bits, (256/V)*kV/32 words.  Tiles of
+ * the second part (tile rows from m_a/16 on) follow all tiles of the first
+ * and are indexed over the second part's own rows.                           */
+static const uint32_t *orc_tile_words(const orc_layer *Lr, int64_t R, int64_t C, int *kV) {
+  const int64_t Ra = orc_m_a(Lr) / 16, tpr = Lr->n / 16;
+  const int64_t words_a = (256 / Lr->V) * (int64_t)orc_kv_a(Lr) / 32;
+  if (R < Ra) {
+    *kV = orc_kv_a(Lr);
+    return Lr->codes + orc_tile_index(Lr->n, R, C) * words_a;
+  }
+  *kV = orc_kv_b(Lr);
+  const int64_t words_b = (256 / Lr->V) * (int64_t)*kV / 32;
+  return Lr->codes + Ra * tpr * words_a + orc_tile_index(Lr->n, R - Ra, C) * words_b;
+}
+
+/* Grid coordinates of the tile at storage index `index` (both parts).      */
+static void orc_storage_coords(const orc_layer *Lr, int64_t index, int64_t *R, int64_t *C) {
+  const int64_t Ra = orc_m_a(Lr) / 16, tiles_a = Ra * (Lr->n / 16);
+  if (index < tiles_a) {
+    orc_tile_coords(Lr->n, index, R, C);
+  } else {
+    orc_tile_coords(Lr->n, index - tiles_a, R, C);
+    *R += Ra;
+  }
+}
+
+/* States of tile (R, C): the stream is the tile's (256/V)*kV bits, walked
  * bit-serially with wrap-around (tail-biting); 256/V states.                */
 static int orc_tile_states(const orc_layer *Lr, int64_t R, int64_t C,
                            uint32_t states[256]) {
-  const int k = Lr->k, V = Lr->V, L = Lr->L, kV = k * V;
-  const int64_t nbits = 256 * (int64_t)k;
-  const uint32_t *words = Lr->codes + orc_tile_index(Lr->n, R, C) * 8 * k;
-  uint8_t bits[2048];
+  const int V = Lr->V, L = Lr->L;
+  int kV;
+  const uint32_t *words = orc_tile_words(Lr, R, C, &kV);
+  const int64_t nbits = (256 / V) * (int64_t)kV;
+  uint8_t bits[4096];
+  if (nbits > 4096 || nbits % 32) return -1;
   for (int64_t p = 0; p < nbits; p++) bits[p] = (uint8_t)orc_bit(words, p);
   return orc_walk_bits(bits, nbits, L, kV, 256 / V, 1, states);
 }
@@ -358,7 +421,7 @@ int orc_decode_tile(const orc_layer *Lr, int64_t R, int64_t C,
 }
 
 /* Decode tiles [first, first+count) in storage order (each mapped back to its
- * grid coordinates by orc_tile_coords) into out[count][256].                 */
+ * grid coordinates, part by part) into out[count][256].                      */
 int orc_decode_storage(const orc_layer *Lr, int64_t first, int64_t count,
                        uint16_t *out) {
   if (orc_validate(Lr)) return -1;
@@ -368,7 +431,7 @@ int orc_decode_storage(const orc_layer *Lr, int64_t first, int64_t count,
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < count; i++) {
     int64_t R, C;
-    orc_tile_coords(Lr->n, first + i, &R, &C);
+    orc_storage_coords(Lr, first + i, &R, &C);
     if (orc_tile_values(Lr, R, C, out + i * 256, NULL)) bad = 1;
   }
   return bad ? -1 : 0;

@@ -72,6 +72,13 @@ class HostLayer:
     had_in: int = 1
     had_out: int = 1
     name: str = ""
+    kv: int = 0       # bits per trellis step of rows [0, m_a) (0: k * V)
+    kv_b: int = 0     # bits per step of rows [m_a, m) (half-TCQ), else 0
+    m_a: int = 0      # rows of the first part (half-TCQ), else 0
+
+    @property
+    def bits_per_weight(self) -> float:
+        return self.codes.size * 32 / (self.m * self.n)
 
     @property
     def n_tiles(self) -> int:
@@ -93,9 +100,12 @@ class HostLayer:
 def make_layer(code: int, m: int, n: int, k: int, *, tag: str, V: Optional[int] = None,
                Q: int = 9, scale: float = 0.02, signs: bool = True,
                had_in: Optional[int] = None, had_out: Optional[int] = None,
-               group: int = 128, codes: Optional[np.ndarray] = None) -> HostLayer:
+               group: int = 128, codes: Optional[np.ndarray] = None,
+               kv: int = 0, kv_b: int = 0, m_a: int = 0) -> HostLayer:
     """A seeded random layer.  Trellis codes use L = 16; NUQ uses L = k, V = 1;
-    VQ uses L = 2k, V = 2 (one index per weight pair)."""
+    VQ uses L = 2k, V = 2 (one index per weight pair).  Trellis codes may give
+    the bits per step kv instead of k (pass k = 0; V = 2 and kv = 5 is 2.5
+    bits per weight), and a second width kv_b for rows [m_a, m)."""
     if code == HYB:
         V = 2 if V is None else V
         L = 16
@@ -110,7 +120,12 @@ def make_layer(code: int, m: int, n: int, k: int, *, tag: str, V: Optional[int] 
         V, L = 2, 2 * k
     else:
         raise ValueError("unknown code %r" % code)
-    nwords = m * n * k // 32
+    spt = 256 // V                       # trellis steps (or indices) per tile
+    kva = kv if kv else k * V
+    rows_a = m_a if m_a else m
+    nwords = (rows_a // 16) * (n // 16) * spt * kva // 32
+    if m_a:
+        nwords += ((m - m_a) // 16) * (n // 16) * spt * kv_b // 32
     if codes is None:
         codes = random_words(rng_for(tag, "codes"), nwords)
     assert codes.size == nwords
@@ -139,7 +154,7 @@ def make_layer(code: int, m: int, n: int, k: int, *, tag: str, V: Optional[int] 
                      sign_in=si, sign_out=so,
                      had_in=largest_pow2_divisor(n) if had_in is None else had_in,
                      had_out=largest_pow2_divisor(m) if had_out is None else had_out,
-                     name=tag)
+                     name=tag, kv=kv, kv_b=kv_b, m_a=m_a)
 
 
 def activations(tag: str, b: int, n: int) -> np.ndarray:

@@ -522,3 +522,91 @@ def test_forward_closed_form_constant_rows():
     for b0 in range(0, m, Bo):
         want[b0] = np.sqrt(Bo) * zval * so[b0]
     assert np.allclose(y, want, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Fractional bit widths and half-TCQ
+
+def _frac_layer(kv, m=256, n=48, kv_b=0, m_a=0, tag="frac"):
+    return synth.make_layer(synth.HYB, m, n, 0, tag=tag, kv=kv, kv_b=kv_b, m_a=m_a, had_out=64)
+
+
+def test_fractional_bits_per_weight():
+    """kV = 5 at V = 2 stores 2.5 bits per weight; two equal halves at 2.5
+    and 3 bits store 2.75 on average (the Q-Palette half-TCQ example)."""
+    g = _read_golden("bit_accounting.txt")
+    lay = _frac_layer(5)
+    assert lay.bits_per_weight == float(g["fractional_example_bits"])
+    ka, kb = (float(v) for v in g["half_tcq_parts_bits"].split(","))
+    half = _frac_layer(int(2 * ka), kv_b=int(2 * kb), m_a=128)
+    assert half.bits_per_weight == float(g["half_tcq_average_bits"])
+    assert oracle.validate(lay) and oracle.validate(half)
+
+
+@pytest.mark.parametrize("kv", [5, 7])
+def test_fractional_tile_is_cyclic_walk_of_its_stream(kv):
+    """Each tile is a tail-biting stream of 128 kv bits (kv/2 bits per
+    weight) in storage order: its states are the cyclic kv-bit-shift windows
+    of that stream, taken here with numpy's own bit unpacking and slicing."""
+    lay = _frac_layer(kv)
+    tw = 128 * kv // 32
+    n = lay.n
+    for i in (0, 5, lay.n_tiles - 1):
+        R, C = oracle.tile_coords(n, i)
+        bits = np.unpackbits(lay.codes[i * tw:(i + 1) * tw].astype(">u4").view(np.uint8))
+        assert bits.size == 128 * kv
+        ext = np.concatenate([bits, bits[:16]])
+        want = []
+        for t in range(128):
+            s = int(ext[t * kv:t * kv + 16].dot(1 << np.arange(15, -1, -1)))
+            want.extend(oracle.state_value(synth.HYB, s, lay.Q, lay.lut, V=2))
+        assert np.array_equal(oracle.decode_tile(lay, R, C), np.array(want, dtype=np.uint16))
+
+
+def test_even_kv_equals_integer_k():
+    """kv = 2k given as bits per step decodes exactly as the integer width k."""
+    a = synth.make_layer(synth.HYB, 128, 64, 3, tag="evenkv")
+    b = dataclasses.replace(a, k=0, kv=6)
+    assert np.array_equal(oracle.decode_dense(a), oracle.decode_dense(b))
+
+
+@pytest.mark.parametrize("kv,kv_b,m_a", [(5, 6, 128), (7, 4, 256), (4, 5, 128)])
+def test_half_tcq_is_two_layers_stacked(kv, kv_b, m_a):
+    """Rows [0, m_a) at kv and [m_a, m) at kv_b, stored one part after the
+    other, decode as two separate layers (split at the part boundary of the
+    code words) stacked row-wise; the storage order lists the first part's
+    tiles, then the second's."""
+    m, n = 384, 48
+    lay = _frac_layer(kv, m=m, n=n, kv_b=kv_b, m_a=m_a, tag="half%d%d" % (kv, kv_b))
+    wa = (m_a // 16) * (n // 16) * 128 * kv // 32
+    assert lay.codes.size == wa + ((m - m_a) // 16) * (n // 16) * 128 * kv_b // 32
+    top = dataclasses.replace(lay, m=m_a, kv=kv, kv_b=0, m_a=0, codes=lay.codes[:wa].copy())
+    bot = dataclasses.replace(lay, m=m - m_a, kv=kv_b, kv_b=0, m_a=0, codes=lay.codes[wa:].copy())
+    W = oracle.decode_dense(lay)
+    assert np.array_equal(W[:m_a], oracle.decode_dense(top))
+    assert np.array_equal(W[m_a:], oracle.decode_dense(bot))
+    st = oracle.decode_tiles_storage(lay, 0, lay.n_tiles)
+    ta = top.n_tiles
+    assert np.array_equal(st[:ta], oracle.decode_tiles_storage(top, 0, ta))
+    assert np.array_equal(st[ta:], oracle.decode_tiles_storage(bot, 0, bot.n_tiles))
+
+
+def test_fractional_validate_rejects():
+    good = _frac_layer(5, kv_b=6, m_a=128)
+    assert oracle.validate(good)
+    for bad in [dict(k=2), dict(m_a=100), dict(m_a=256), dict(kv_b=0), dict(kv=17),
+                dict(m_a=0), dict(kv_b=20)]:
+        assert not oracle.validate(dataclasses.replace(good, **bad)), bad
+    nuq = synth.make_layer(synth.NUQ, 128, 128, 3, tag="valnuq")
+    assert not oracle.validate(dataclasses.replace(nuq, kv=3, k=0))
+    assert not oracle.validate(dataclasses.replace(nuq, kv_b=3, m_a=0))
+
+
+@pytest.mark.parametrize("kv,kv_b,m_a", [(5, 0, 0), (7, 0, 0), (5, 6, 128)])
+def test_forward_fractional_matches_numpy(kv, kv_b, m_a):
+    lay = _frac_layer(kv, kv_b=kv_b, m_a=m_a, m=256, n=96, tag="fwdfrac%d%d" % (kv, kv_b))
+    lay = dataclasses.replace(lay, had_out=256)      # the output RHT spans both parts
+    x = synth.activations("fwdfracx", 2, 96)
+    got = oracle.forward(lay, x)
+    want = _numpy_forward(lay, x)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
