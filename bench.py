@@ -99,7 +99,8 @@ def make_pool_layers(q, torch, dev, code, m, n, k, count, tag, **kw):
     import synth
     g = torch.Generator(device=dev)
     g.manual_seed(int.from_bytes(tag.encode()[:8].ljust(8, b"\0"), "little") & 0x7FFFFFFF)
-    words = m * n * k // 32
+    words = synth.code_words(code, m, n, k, kw.get("V"), kw.get("kv", 0), kw.get("kv_b", 0),
+                             kw.get("m_a", 0))
     pool = torch.randint(-(1 << 31), (1 << 31) - 1, (count, words), dtype=torch.int32, device=dev,
                          generator=g)
     host = synth.make_layer(code, m, n, k, tag=tag, codes=np.zeros(words, dtype=np.uint32), **kw)
@@ -110,7 +111,7 @@ def make_pool_layers(q, torch, dev, code, m, n, k, count, tag, **kw):
                               codes=pool[i], lut=base.lut, group_scale=base.group_scale,
                               group=base.group, layer_scale=base.layer_scale,
                               sign_in=base.sign_in, sign_out=base.sign_out, had_in=base.had_in,
-                              had_out=base.had_out))
+                              had_out=base.had_out, kv=base.kv, kv_b=base.kv_b, m_a=base.m_a))
     return layers, pool, base
 
 
@@ -263,6 +264,7 @@ def main():
         detail.update(bench_llama_layer(q, torch, dev, stream, "llama3_8b_layer_fused"))
         detail.update(bench_gemm(q, torch, dev, stream))
         detail.update(bench_code_variants(q, torch, dev))
+        detail.update(bench_fractional(q, torch, dev))
 
     if not args.no_detail and not args.only:
         ceil = measured_ceilings(torch, dev)
@@ -378,18 +380,18 @@ def bench_llama_layer(q, torch, dev, stream, name="llama3_8b_layer"):
     return out
 
 
-def bench_code_variants(q, torch, dev):
-    """The table-size knob of the trellis codes on one 4096x4096 k=2 layer at
-    b=1 and b=64: HYB with 2^9 pairs (V=2), HYB with a 2^6-value codebook
-    (V=1) and the pure lookup of 2^16 values (a 128 KiB table in LDS)."""
+def time_4096_variants(q, torch, dev, variants, tagbase):
+    """Graph-replayed time per call of 4096x4096 layers (16 distinct code
+    sets in rotation) at b=1 (qdec_gemv) and b=64 (qdec_gemm) for each
+    (name, code, k, make_layer keywords) variant."""
     import synth
     out = {}
-    for name, code, kw in (("HYB_V2_Q9", synth.HYB, dict(V=2, Q=9)), ("HYB_V1_Q6", synth.HYB, dict(V=1, Q=6)),
-                           ("LUT_L16", synth.LUT, {})):
-        layers, pool, base = make_pool_layers(q, torch, dev, code, 4096, 4096, 2, 16, "bench/var/" + name, **kw)
+    for name, code, k, kw in variants:
+        layers, pool, base = make_pool_layers(q, torch, dev, code, 4096, 4096, k, 16, tagbase + name, **kw)
+        nbytes = base.code_bytes
         res = {}
         for b in (1, 64):
-            x = torch.from_numpy(synth.activations("bench/var/x", b, 4096).view(np.int16)).to(dev)
+            x = torch.from_numpy(synth.activations(tagbase + "x", b, 4096).view(np.int16)).to(dev)
             y = torch.empty((b, 4096), dtype=torch.float16, device=dev)
             op = q.QDEC_OP_GEMV if b == 1 else q.QDEC_OP_GEMM
             ws = q.workspace(base, b, op, dev)
@@ -412,14 +414,39 @@ def bench_code_variants(q, torch, dev):
             us = e0.elapsed_time(e1) * 1e3 / 80
             res["b%d_us" % b] = round(us, 2)
             if b == 1:
-                res["b1_packed_GBps"] = round(4096 * 4096 * 2 / 8 / (us * 1e-6) / 1e9, 1)
+                res["b1_packed_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
             else:
                 res["b64_TFLOPs"] = round(2 * 4096 * 4096 * 64 / (us * 1e-6) / 1e12, 1)
             del g
         out[name] = res
         del layers, pool
+    return out
+
+
+def bench_code_variants(q, torch, dev):
+    """The table-size knob of the trellis codes on one 4096x4096 k=2 layer at
+    b=1 and b=64: HYB with 2^9 pairs (V=2), HYB with a 2^6-value codebook
+    (V=1) and the pure lookup of 2^16 values (a 128 KiB table in LDS)."""
+    import synth
+    out = time_4096_variants(q, torch, dev, (
+        ("HYB_V2_Q9", synth.HYB, 2, dict(V=2, Q=9)), ("HYB_V1_Q6", synth.HYB, 2, dict(V=1, Q=6)),
+        ("LUT_L16", synth.LUT, 2, {})), "bench/var/")
     log("code variants (4096x4096 k=2):", out)
     return {"code_variants_4096_k2": out}
+
+
+def bench_fractional(q, torch, dev):
+    """Bit widths of one 4096x4096 HYB layer (V=2, Q=9) at b=1 and b=64:
+    2 to 4 bits per weight in half-bit steps (kV = 4 .. 8 bits per trellis
+    step), and half-TCQ with the rows cut in two halves at 2.5 and 3 bits
+    (2.75 on average)."""
+    import synth
+    H = synth.HYB
+    out = time_4096_variants(q, torch, dev, (
+        ("k2.0", H, 2, {}), ("k2.5", H, 0, dict(kv=5)), ("k3.0", H, 3, {}), ("k3.5", H, 0, dict(kv=7)),
+        ("k4.0", H, 4, {}), ("half_k2.5_k3.0", H, 0, dict(kv=5, kv_b=6, m_a=2048))), "bench/frac/")
+    log("bit widths (4096x4096 HYB):", out)
+    return {"bit_widths_4096_hyb": out}
 
 
 def bench_gemm(q, torch, dev, stream):

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libqdec.so")
 QDEC_OK, QDEC_EINVAL, QDEC_EUNSUPPORTED, QDEC_EWORKSPACE, QDEC_EHIP, QDEC_ENODEV = 0, -1, -2, -3, -4, -5
 QDEC_CODE_HYB, QDEC_CODE_1MAD, QDEC_CODE_3INST, QDEC_CODE_NUQ, QDEC_CODE_VQ, QDEC_CODE_LUT = 1, 2, 3, 4, 5, 6
 QDEC_OP_GEMV, QDEC_OP_GEMM = 1, 2
-QDEC_ABI_VERSION = 1
+QDEC_ABI_VERSION = 2
 
 # The exported symbols, as declared in include/qdec.h.
 EXPORTS = ("qdec_abi_version", "qdec_status_string", "qdec_last_error", "qdec_workspace_bytes",
@@ -41,6 +41,7 @@ class qdec_layer(ctypes.Structure):
     _fields_ = [
         ("abi_version", ctypes.c_uint32), ("code", ctypes.c_int32),
         ("L", ctypes.c_int32), ("k", ctypes.c_int32), ("V", ctypes.c_int32), ("Q", ctypes.c_int32),
+        ("kv", ctypes.c_int32), ("kv_b", ctypes.c_int32), ("m_a", ctypes.c_int64),
         ("m", ctypes.c_int64), ("n", ctypes.c_int64),
         ("codes", ctypes.c_void_p), ("lut", ctypes.c_void_p), ("group_scale", ctypes.c_void_p),
         ("group", ctypes.c_int32), ("layer_scale", ctypes.c_float),
@@ -124,11 +125,15 @@ class Layer:
     sign_out: object = None
     had_in: int = 1
     had_out: int = 1
+    kv: int = 0       # bits per trellis step of rows [0, m_a) (0: k * V)
+    kv_b: int = 0     # half-TCQ: bits per step of rows [m_a, m)
+    m_a: int = 0      # half-TCQ: rows of the first part (0: one part)
     _desc: qdec_layer = field(default=None, repr=False)
 
     def desc(self) -> qdec_layer:
         if self._desc is None:
             self._desc = qdec_layer(QDEC_ABI_VERSION, self.code, self.L, self.k, self.V, self.Q,
+                                    self.kv, self.kv_b, self.m_a,
                                     self.m, self.n, _ptr(self.codes), _ptr(self.lut),
                                     _ptr(self.group_scale), self.group, self.layer_scale,
                                     _ptr(self.sign_in), _ptr(self.sign_out), self.had_in, self.had_out)
@@ -140,7 +145,12 @@ class Layer:
 
     @property
     def code_bytes(self) -> int:
-        return self.m * self.n * self.k // 8
+        kva = self.kv if self.kv else self.k * self.V
+        rows_a = self.m_a if self.m_a else self.m
+        bits = rows_a * self.n * kva // self.V
+        if self.m_a:
+            bits += (self.m - self.m_a) * self.n * self.kv_b // self.V
+        return bits // 8
 
 
 def qdec_workspace_bytes(layer: Layer, batch: int, op: int) -> int:
@@ -192,7 +202,8 @@ def upload_layer(host, device="cuda") -> Layer:
     return Layer(code=host.code, L=host.L, k=host.k, V=host.V, Q=host.Q, m=host.m, n=host.n,
                  codes=codes, lut=t(host.lut, np.int32), group_scale=t(host.gscale, np.int16),
                  group=host.group, layer_scale=host.scale, sign_in=t(host.sign_in, np.int32),
-                 sign_out=t(host.sign_out, np.int32), had_in=host.had_in, had_out=host.had_out)
+                 sign_out=t(host.sign_out, np.int32), had_in=host.had_in, had_out=host.had_out,
+                 kv=getattr(host, "kv", 0), kv_b=getattr(host, "kv_b", 0), m_a=getattr(host, "m_a", 0))
 
 
 def workspace(layer: Layer, batch: int, op: int, device="cuda"):

@@ -31,10 +31,6 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
 }
-
-bool gemv_supported(int code, int k, int b) {
-  return code >= HYB && code <= HYB1 && k >= 2 && k <= 4 && b >= 1 && b <= 8;
-}
 }  // namespace qdec
 
 using namespace qdec;
@@ -46,11 +42,30 @@ constexpr int kMaxHadamard = 16384;
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+bool is_trellis(int code) {
+  return code == QDEC_CODE_HYB || code == QDEC_CODE_1MAD || code == QDEC_CODE_3INST || code == QDEC_CODE_LUT;
+}
+
 // Format-level validation; EUNSUPPORTED for valid combinations not built.
-int check_layer(const qdec_layer* L, LayerArgs* out) {
+// On success *out describes the whole layer with the first part's width and
+// *parts the row parts (one, or two for half-TCQ).
+int check_layer(const qdec_layer* L, LayerArgs* out, LayerParts* parts = nullptr) {
   if (!L || L->abi_version != QDEC_ABI_VERSION) return QDEC_EINVAL;
   if (L->m <= 0 || L->n <= 0 || (L->m % 128) || (L->n % 16)) return QDEC_EINVAL;
-  if (L->k < 1 || L->k > 8) return QDEC_EINVAL;
+  if (L->kv == 0) {
+    if (L->k < 1 || L->k > 8) return QDEC_EINVAL;
+  } else if (L->k != 0 || !is_trellis(L->code)) {
+    return QDEC_EINVAL;
+  }
+  if (L->m_a) {
+    if (!is_trellis(L->code) || L->m_a < 0 || L->m_a >= L->m || (L->m_a % 128) || L->kv_b < 1)
+      return QDEC_EINVAL;
+  } else if (L->kv_b) {
+    return QDEC_EINVAL;
+  }
+  const int kv_a = L->kv ? L->kv : L->k * L->V;
+  const int kv_b = L->m_a ? L->kv_b : kv_a;
+  if (kv_a < 1 || kv_b < 1 || kv_a > L->L || kv_b > L->L) return QDEC_EINVAL;
   if (!L->codes || !aligned(L->codes, 16)) return QDEC_EINVAL;
   if (!is_pow2(L->had_in) || L->n % L->had_in) return QDEC_EINVAL;
   if (!is_pow2(L->had_out) || L->m % L->had_out) return QDEC_EINVAL;
@@ -58,7 +73,6 @@ int check_layer(const qdec_layer* L, LayerArgs* out) {
   switch (L->code) {
     case QDEC_CODE_HYB:
       if (L->L != 16 || (L->V != 1 && L->V != 2) || L->Q < 1 || L->Q > 15 || !L->lut) return QDEC_EINVAL;
-      if (L->k * L->V > L->L) return QDEC_EINVAL;
       if (L->Q > 11) return QDEC_EUNSUPPORTED;   // LDS table would exceed the budget
       break;
     case QDEC_CODE_LUT:
@@ -78,7 +92,8 @@ int check_layer(const qdec_layer* L, LayerArgs* out) {
     default:
       return QDEC_EINVAL;
   }
-  if (L->k < 2 || L->k > 4) return QDEC_EUNSUPPORTED;
+  const int kcode = (L->code == QDEC_CODE_HYB && L->V == 1) ? HYB1 : L->code;
+  if (!kv_built(kcode, kv_a) || !kv_built(kcode, kv_b)) return QDEC_EUNSUPPORTED;
   if (L->had_in > kMaxHadamard || L->had_out > kMaxHadamard) return QDEC_EUNSUPPORTED;
   if (out) {
     out->codes = L->codes;
@@ -88,14 +103,32 @@ int check_layer(const qdec_layer* L, LayerArgs* out) {
     out->sign_out = L->sign_out;
     out->m = L->m;
     out->n = L->n;
-    out->code = (L->code == QDEC_CODE_HYB && L->V == 1) ? HYB1 : L->code;
-    out->k = L->k;
+    out->code = kcode;
+    out->kv = kv_a;
     out->Q = L->code == QDEC_CODE_HYB ? L->Q : 0;   // both V = 1 and V = 2
     out->qshift = L->code == QDEC_CODE_HYB ? 15 - L->Q : 0;
     out->group = L->code == QDEC_CODE_NUQ ? L->group : 1;
     out->had_in = L->had_in;
     out->had_out = L->had_out;
     out->scale = L->layer_scale;
+    if (parts) {
+      // a tile holds (256/V) steps of kV bits: 8 kV / V words
+      const int64_t m_a = L->m_a ? L->m_a : L->m;
+      parts->count = L->m_a ? 2 : 1;
+      parts->part[0] = *out;
+      parts->part[0].m = m_a;
+      parts->row0[0] = 0;
+      parts->tile0[0] = 0;
+      if (L->m_a) {
+        const int64_t tiles_a = (m_a / 16) * (L->n / 16);
+        parts->part[1] = *out;
+        parts->part[1].m = L->m - m_a;
+        parts->part[1].kv = kv_b;
+        parts->part[1].codes = L->codes + tiles_a * (8 * kv_a / L->V);
+        parts->row0[1] = m_a;
+        parts->tile0[1] = tiles_a;
+      }
+    }
   }
   return QDEC_OK;
 }
@@ -242,7 +275,8 @@ int qdec_rht(const void* in, int32_t in_dtype, void* out, int32_t out_dtype, int
 int qdec_gemv(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t batch, void* ws,
               size_t ws_bytes, void* stream) {
   LayerArgs L;
-  int st = check_layer(layer, &L);
+  LayerParts parts;
+  int st = check_layer(layer, &L, &parts);
   if (st) return st;
   if (!x || !y || !aligned(x, 16) || !aligned(y, 4)) return QDEC_EINVAL;
   if (batch < 1) return QDEC_EINVAL;
@@ -262,6 +296,8 @@ int qdec_gemv(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
   a.y = y;
   a.b = (int)batch;
   a.z = (float*)((char*)ws + wl.z);
+  a.row0 = 0;
+  a.mz = L.m;
   a.xr = nullptr;
   a.Kc = Kc;
   a.nchunks = (int)((L.n + a.Kc - 1) / a.Kc);
@@ -290,13 +326,23 @@ int qdec_gemv(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
     if (e != hipSuccess) return status_of(e);
     a.xr = xr;
   }
-  return status_of(launch_gemv(a, (hipStream_t)stream));
+  // the decode-and-multiply kernel per row part (each adds into z), then the
+  // output side over the whole layer
+  for (int p = 0; p < parts.count; ++p) {
+    GemvArgs ap = a;
+    ap.L = parts.part[p];
+    ap.row0 = parts.row0[p];
+    const hipError_t e = launch_gemv(ap, (hipStream_t)stream);
+    if (e != hipSuccess) return status_of(e);
+  }
+  return status_of(launch_gemv_finish(a, (hipStream_t)stream));
 }
 
 int qdec_gemm(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t batch, void* ws,
               size_t ws_bytes, void* stream) {
   LayerArgs L;
-  int st = check_layer(layer, &L);
+  LayerParts parts;
+  int st = check_layer(layer, &L, &parts);
   if (st) return st;
   if (!x || !y || !aligned(x, 16) || !aligned(y, 4)) return QDEC_EINVAL;
   if (batch < 1) return QDEC_EINVAL;
@@ -327,14 +373,18 @@ int qdec_gemm(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
   if (e != hipSuccess) return status_of(e);
   // 2. Z[split] = W_hat X'^T over each K split (fp32 slices, plain stores)
   GemmArgs g;
-  g.L = L;
   g.xr = xr;
   g.z = z;
+  g.mz = L.m;
   g.b = (int)batch;
   const int64_t ks = gemm_ksplit(L.m, L.n, batch);
   g.ksplit = (int)ks;
-  e = launch_gemm(g, s);
-  if (e != hipSuccess) return status_of(e);
+  for (int p = 0; p < parts.count; ++p) {   // each row part writes its rows of every slice
+    g.L = parts.part[p];
+    g.row0 = parts.row0[p];
+    e = launch_gemm(g, s);
+    if (e != hipSuccess) return status_of(e);
+  }
   // 3. Y = s_out .* (scale/sqrt(B) H sum_split Z[split]), fp16
   e = launch_rht_out_f32(z, g.ksplit, y, batch, L.m, L.had_out, L.sign_out,
                          (float)((double)L.scale / sqrt((double)L.had_out)), s);
@@ -344,7 +394,8 @@ int qdec_gemm(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
 int qdec_decode_tile(const qdec_layer* layer, int64_t first_tile, int64_t n_tiles, uint16_t* out,
                      void* stream) {
   LayerArgs L;
-  int st = check_layer(layer, &L);
+  LayerParts parts;
+  int st = check_layer(layer, &L, &parts);
   if (st) return st;
   const int64_t total = (L.m / 16) * (L.n / 16);
   if (first_tile < 0 || n_tiles < 0 || first_tile + n_tiles > total) return QDEC_EINVAL;
@@ -352,12 +403,22 @@ int qdec_decode_tile(const qdec_layer* layer, int64_t first_tile, int64_t n_tile
   if (n_tiles == 0) return QDEC_OK;
   const int d = check_device();
   if (d) return d;
-  DecodeArgs a;
-  a.L = L;
-  a.first = first_tile;
-  a.count = n_tiles;
-  a.out = out;
-  return status_of(launch_decode_tile(a, (hipStream_t)stream));
+  // the requested storage range, cut at the part boundary
+  for (int p = 0; p < parts.count; ++p) {
+    const int64_t t0 = parts.tile0[p];
+    const int64_t t1 = t0 + (parts.part[p].m / 16) * (L.n / 16);
+    const int64_t lo = first_tile > t0 ? first_tile : t0;
+    const int64_t hi = first_tile + n_tiles < t1 ? first_tile + n_tiles : t1;
+    if (lo >= hi) continue;
+    DecodeArgs a;
+    a.L = parts.part[p];
+    a.first = lo - t0;
+    a.count = hi - lo;
+    a.out = out + (lo - first_tile) * 256;
+    const hipError_t e = launch_decode_tile(a, (hipStream_t)stream);
+    if (e != hipSuccess) return status_of(e);
+  }
+  return QDEC_OK;
 }
 
 }  // extern "C"

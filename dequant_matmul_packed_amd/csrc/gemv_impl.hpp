@@ -48,20 +48,20 @@ struct GemvTable {
   static constexpr int COPIES = (CODE == HYB || CODE == HYB1 || CODE == VQ) ? 8 : 1;
 };
 
-template <int CODE, int K>
+template <int CODE, int KV>
 __host__ __device__ constexpr int gemv_table_words(int Q) {
   return (CODE == HYB || CODE == HYB1) ? (2 << Q) * GemvTable<CODE>::COPIES
-       : CODE == VQ ? (1 << (2 * K)) * GemvTable<CODE>::COPIES
-       : CODE == NUQ ? (1 << K)
+       : CODE == VQ ? (1 << KV) * GemvTable<CODE>::COPIES
+       : CODE == NUQ ? (1 << KV)
        : CODE == LUT ? (1 << 15) : 0;   // LUT: 2^16 fp16 values, two per word
 }
 
 // LDS of one workgroup: region A (lookup table; also the scratch of the
 // input RHT, the wave reduction and the output RHT), then x' as fp16 pairs,
 // then (3INST) x' duplicated into (x, x) pairs.
-template <int CODE, int K, int NB>
+template <int CODE, int KV, int NB>
 __host__ __device__ inline size_t gemv_regA_bytes(int Q, int Kc, int U) {
-  size_t tab = (size_t)gemv_table_words<CODE, K>(Q) * 4;
+  size_t tab = (size_t)gemv_table_words<CODE, KV>(Q) * 4;
   size_t rht = (size_t)(GEMV_THREADS * 8 + NB * padded_words(Kc)) * 4;
   size_t red = (size_t)4 * 128 * NB * 4;
   (void)U;
@@ -82,32 +82,18 @@ template <int NB>
 __host__ __device__ inline size_t gemv_wred_bytes(int Kc) {
   return (NB == 1 && Kc <= GEMV_WRED_SEP_MAX) ? (size_t)4 * Kc * 4 : 0;
 }
-template <int CODE, int K, int NB>
+template <int CODE, int KV, int NB>
 __host__ __device__ inline size_t gemv_lds_bytes(int Q, int Kc, int U) {
-  return gemv_regA_bytes<CODE, K, NB>(Q, Kc, U) + (size_t)NB * Kc * 2 +
+  return gemv_regA_bytes<CODE, KV, NB>(Q, Kc, U) + (size_t)NB * Kc * 2 +
          (CODE == INST3 ? (size_t)NB * Kc * 4 : 0) + gemv_wred_bytes<NB>(Kc);
 }
 
-// K consecutive code words of one lane (16-byte aligned tile blocks).
-template <int K>
-__device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint32_t* w) {
-  if constexpr (K == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    w[0] = v.x; w[1] = v.y;
-  } else if constexpr (K == 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  } else {
-#pragma unroll
-    for (int i = 0; i < K; ++i) w[i] = p[i];
-  }
-}
-
-template <int CODE, int K, int NB, int PF, bool SL>
+template <int CODE, int KV, int NB, int PF, bool SL>
 __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
-  constexpr int V = code_V(CODE);
-  constexpr int L = code_L(CODE, K);
-  constexpr int KV = K * V;
+  using G = LaneGeom<CODE, KV>;
+  constexpr int V = G::V;
+  constexpr int L = G::L;
+  constexpr int NW = G::NW;
   constexpr int COPIES = GemvTable<CODE>::COPIES;
   extern __shared__ __align__(16) uint32_t smem[];
 
@@ -127,7 +113,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   tc_count = tc_count < 0 ? 0 : (tc_count > tpw ? tpw : tc_count);
 
   // LDS carve-up
-  const size_t regA_words = gemv_regA_bytes<CODE, K, NB>(a.L.Q, Kc, a.U) / 4;
+  const size_t regA_words = gemv_regA_bytes<CODE, KV, NB>(a.L.Q, Kc, a.U) / 4;
   uint32_t* regA = smem;
   float* fA = reinterpret_cast<float*>(smem);
   uint32_t* xh = smem + regA_words;                 // [NB][Kc/2] fp16 pairs
@@ -154,7 +140,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   // (HYB: 2^Q <= 256 TW words; VQ 2^(2k) <= 256; NUQ 2^k <= 16)
   constexpr int TW = (CODE == HYB || CODE == HYB1) ? (SL ? 2 : 8) : 1;
   const int nlut = (CODE == HYB || CODE == HYB1) ? (1 << a.L.Q)
-                 : CODE == VQ ? (1 << (2 * K)) : CODE == NUQ ? (1 << K) : 0;   // LUT: filled below
+                 : (CODE == VQ || CODE == NUQ) ? (1 << KV) : 0;   // LUT: filled below
   uint32_t lw[TW];
   {
     const auto lrs = make_rsrc(a.L.lut, (uint32_t)nlut * 4u);
@@ -184,23 +170,25 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   }
 
   // ---- 1. issue the code loads ------------------------------------------
-  // A buffer over this panel's tile columns of the chunk (each 8 tiles x 8
-  // lanes x K words); the wave's tile columns tc_begin .. tc_begin+tc_count-1
-  // stream through an 8-deep ring of registers, the first 8 requested here.
+  // A buffer over this panel's tile columns of the chunk (each 8 tiles of
+  // TILE_WORDS words); the wave's tile columns tc_begin .. tc_begin+tc_count-1
+  // stream through a PF-deep ring of registers, the first PF requested here.
+  // Lane q of tile row tl loads NW words from word lane_word(q) of its tile.
+  constexpr uint32_t TCB = 8u * 4u * G::TILE_WORDS;   // bytes per tile column
   const int64_t tiles_row = n >> 4;
-  const uint32_t* pchunk = a.L.codes + ((int64_t)panel * tiles_row + (c0 >> 4)) * (64 * K);
-  const auto crs = make_rsrc(pchunk, (uint32_t)ntc * (256u * K));
-  const uint32_t lane_off = (uint32_t)lane * (4 * K);
+  const uint32_t* pchunk = a.L.codes + ((int64_t)panel * tiles_row + (c0 >> 4)) * (8 * G::TILE_WORDS);
+  const auto crs = make_rsrc(pchunk, (uint32_t)ntc * TCB);
+  const uint32_t lane_off = (uint32_t)(lane >> 3) * (4u * G::TILE_WORDS) + 4u * G::lane_word(lane & 7);
   auto code_off = [&](int j) -> uint32_t {
-    return j < tc_count ? (uint32_t)(tc_begin + j) * (256u * K) + lane_off : BUF_OFF;
+    return j < tc_count ? (uint32_t)(tc_begin + j) * TCB + lane_off : BUF_OFF;
   };
-  uint32_t buf[PF][K];
+  uint32_t buf[PF][NW];
 #pragma unroll
-  for (int j = 0; j < PF; ++j) buf_load_words<K>(crs, code_off(j), buf[j]);
+  for (int j = 0; j < PF; ++j) buf_load_words<NW>(crs, code_off(j), buf[j]);
   // NUQ: the fp16 group scales of the lane's two rows ride in the same ring
   const int64_t gstride = CODE == NUQ ? n / a.L.group : 0;
-  const int64_t grow0 = (int64_t)panel * 128 + (lane >> 3) * 16 + 2 * (lane & 7);
-  const auto grs = make_rsrc(a.L.gscale, CODE == NUQ ? (uint32_t)(m * gstride * 2) : 0u);
+  const int64_t grow0 = a.row0 + (int64_t)panel * 128 + (lane >> 3) * 16 + 2 * (lane & 7);
+  const auto grs = make_rsrc(a.L.gscale, CODE == NUQ ? (uint32_t)(a.mz * gstride * 2) : 0u);
   uint32_t gsr[PF][2];
   auto gs_load = [&](int j, uint32_t* g) {
     if constexpr (CODE == NUQ) {
@@ -452,18 +440,18 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
 #pragma unroll
   for (int jj = 0; jj < PF; ++jj) {
     const int j = j0 + jj;
-    uint32_t w[K + 1];
+    uint32_t w[NW + 1];
 #pragma unroll
-    for (int i = 0; i < K; ++i) w[i] = buf[jj][i];
+    for (int i = 0; i < NW; ++i) w[i] = buf[jj][i];
     const uint32_t g0 = gsr[jj][0], g1 = gsr[jj][1];
     (void)g0; (void)g1;
-    // refill this ring slot with the tile column 8 ahead (unconditionally:
+    // refill this ring slot with the tile column PF ahead (unconditionally:
     // past the wave's last column the load is switched off by its offset)
-    buf_load_words<K>(crs, code_off(j + PF), buf[jj]);
+    buf_load_words<NW>(crs, code_off(j + PF), buf[jj]);
     gs_load(j + PF, gsr[jj]);
     if (j < tc_count) {
       const int tcl = tc_begin + j;   // tile column within the chunk
-      w[K] = next_lane_word(w[0], lane);
+      lane_words_ready<CODE, KV>(w, lane);
       if constexpr (CODE == INST3) {
 #pragma unroll
         for (int t = 0; t < 32; ++t) {
@@ -597,54 +585,60 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
         v0 = hi ? o0 - v0 : v0 + o0;
         v1 = hi ? o1 - v1 : v1 + o1;
       }
-      float* zr = a.z + (int64_t)c * m + (int64_t)panel * 128 + 2 * lane;
+      float* zr = a.z + (int64_t)c * a.mz + a.row0 + (int64_t)panel * 128 + 2 * lane;
       __hip_atomic_fetch_add(zr, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_fetch_add(zr + 1, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
-template <int CODE, int K, int NB, int PF, bool SL>
+template <int CODE, int KV, int NB, int PF, bool SL>
 hipError_t launch_gemv_v(const GemvArgs& a, hipStream_t stream) {
-  const size_t lds = gemv_lds_bytes<CODE, K, NB>(a.L.Q, a.Kc, a.U);
+  const size_t lds = gemv_lds_bytes<CODE, KV, NB>(a.L.Q, a.Kc, a.U);
   static size_t have = 0;
   const hipError_t e =
-      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<CODE, K, NB, PF, SL>), lds, &have);
+      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<CODE, KV, NB, PF, SL>), lds, &have);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((a.L.m / 128) * a.nchunks);
-  hipLaunchKernelGGL((gemv_kernel<CODE, K, NB, PF, SL>), dim3(grid), dim3(GEMV_THREADS), lds, stream, a);
-  const hipError_t e1 = hipGetLastError();
-  if (e1 != hipSuccess) return e1;
-  return launch_gemv_finish(a, stream);
+  hipLaunchKernelGGL((gemv_kernel<CODE, KV, NB, PF, SL>), dim3(grid), dim3(GEMV_THREADS), lds, stream, a);
+  return hipGetLastError();
 }
 
-template <int CODE, int K, int NB>
+template <int CODE, int KV, int NB>
 hipError_t launch_gemv_t(const GemvArgs& a, hipStream_t stream) {
   const bool sl = (NB > 1 || a.L.had_in <= 4096) && ((CODE != HYB && CODE != HYB1) || a.L.Q <= 9);
   if constexpr (NB == 1) {
-    if (a.Kc <= 128 && sl) return launch_gemv_v<CODE, K, NB, 2, true>(a, stream);
-    if (a.Kc <= 256 && sl) return launch_gemv_v<CODE, K, NB, 4, true>(a, stream);
+    if (a.Kc <= 128 && sl) return launch_gemv_v<CODE, KV, NB, 2, true>(a, stream);
+    if (a.Kc <= 256 && sl) return launch_gemv_v<CODE, KV, NB, 4, true>(a, stream);
   }
-  if (sl) return launch_gemv_v<CODE, K, NB, 8, true>(a, stream);
-  return launch_gemv_v<CODE, K, NB, 8, false>(a, stream);
+  if (sl) return launch_gemv_v<CODE, KV, NB, 8, true>(a, stream);
+  return launch_gemv_v<CODE, KV, NB, 8, false>(a, stream);
 }
 
-template <int CODE, int K>
+template <int CODE, int KV>
 hipError_t launch_gemv_k(const GemvArgs& a, hipStream_t stream) {
-  if (a.b <= 1) return launch_gemv_t<CODE, K, 1>(a, stream);
-  if (a.b <= 2) return launch_gemv_t<CODE, K, 2>(a, stream);
-  if (a.b <= 4) return launch_gemv_t<CODE, K, 4>(a, stream);
-  return launch_gemv_t<CODE, K, 8>(a, stream);
+  if (a.b <= 1) return launch_gemv_t<CODE, KV, 1>(a, stream);
+  if (a.b <= 2) return launch_gemv_t<CODE, KV, 2>(a, stream);
+  if (a.b <= 4) return launch_gemv_t<CODE, KV, 4>(a, stream);
+  return launch_gemv_t<CODE, KV, 8>(a, stream);
 }
 
-template <int CODE>
+// The kernels of one code for the step widths in [KV_LO, KV_HI] that it is
+// built for (one source file may take a sub-range).
+template <int CODE, int KV_LO = 2, int KV_HI = 8>
 hipError_t launch_gemv_code(const GemvArgs& a, hipStream_t stream) {
-  switch (a.L.k) {
-    case 2: return launch_gemv_k<CODE, 2>(a, stream);
-    case 3: return launch_gemv_k<CODE, 3>(a, stream);
-    case 4: return launch_gemv_k<CODE, 4>(a, stream);
-    default: return hipErrorInvalidValue;
+#define QDEC_GEMV_KV(KV)                                                          \
+  case KV:                                                                       \
+    if constexpr (kv_built(CODE, KV) && KV >= KV_LO && KV <= KV_HI)             \
+      return launch_gemv_k<CODE, KV>(a, stream);                                 \
+    break;
+  switch (a.L.kv) {
+    QDEC_GEMV_KV(2) QDEC_GEMV_KV(3) QDEC_GEMV_KV(4) QDEC_GEMV_KV(5)
+    QDEC_GEMV_KV(6) QDEC_GEMV_KV(7) QDEC_GEMV_KV(8)
+    default: break;
   }
+#undef QDEC_GEMV_KV
+  return hipErrorInvalidValue;
 }
 
 }  // namespace qdec

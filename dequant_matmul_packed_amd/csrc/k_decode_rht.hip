@@ -9,25 +9,28 @@ namespace qdec {
 // Tile decode (the bit-exact parity surface).  32 tiles per workgroup, one
 // 8-lane group per tile, the same window extraction and value maps the
 // matmul kernels use.
-template <int CODE, int K>
+template <int CODE, int KV>
 __global__ __launch_bounds__(256) void decode_tile_kernel(DecodeArgs a) {
+  using G = LaneGeom<CODE, KV>;
+  constexpr int NW = G::NW;
   constexpr int COPIES = GemvTable<CODE>::COPIES;
   extern __shared__ __align__(16) uint32_t tab[];
   const int tid = threadIdx.x, lane = tid & 63, q = tid & 7;
   if constexpr (CODE == HYB) fill_signed_table<COPIES>(tab, a.L.lut, a.L.Q, tid, 256);
   if constexpr (CODE == HYB1) fill_signed_table<COPIES, 0x8000u>(tab, a.L.lut, a.L.Q, tid, 256);
   if constexpr (CODE == LUT) fill_plain_table<1>(tab, a.L.lut, 1 << 15, tid, 256);
-  if constexpr (CODE == VQ) fill_plain_table<COPIES>(tab, a.L.lut, 1 << (2 * K), tid, 256);
-  if constexpr (CODE == NUQ) fill_plain_table<1>(tab, a.L.lut, 1 << K, tid, 256);
+  if constexpr (CODE == VQ) fill_plain_table<COPIES>(tab, a.L.lut, 1 << KV, tid, 256);
+  if constexpr (CODE == NUQ) fill_plain_table<1>(tab, a.L.lut, 1 << KV, tid, 256);
   __syncthreads();
 
+  // tiles [first, first + count) of this part; lane q of a tile reads NW
+  // words from word lane_word(q) (a switched-off load past the range)
   const int64_t tile = a.first + (int64_t)blockIdx.x * 32 + (tid >> 3);
   const bool valid = tile < a.first + a.count;
-  uint32_t w[K + 1];
-#pragma unroll
-  for (int i = 0; i <= K; ++i) w[i] = 0u;
-  if (valid) load_words<K>(a.L.codes + tile * (8 * K) + q * K, w);
-  w[K] = next_lane_word(w[0], lane);
+  const auto crs = make_rsrc(a.L.codes + a.first * G::TILE_WORDS, (uint32_t)(a.count * G::TILE_WORDS * 4));
+  uint32_t w[NW + 1];
+  buf_load_words<NW>(crs, valid ? (uint32_t)((tile - a.first) * G::TILE_WORDS + G::lane_word(q)) * 4u : BUF_OFF, w);
+  lane_words_ready<CODE, KV>(w, lane);
   if (!valid) return;
 
   float gs[2] = {0.f, 0.f};
@@ -42,33 +45,36 @@ __global__ __launch_bounds__(256) void decode_tile_kernel(DecodeArgs a) {
     for (int r = 0; r < 2; ++r) gs[r] = h2f(a.L.gscale[(R * 16 + 2 * q + r) * gstride + g]);
   }
   uint32_t out[16];
-  lane_decode_exact<CODE, K, COPIES>(w, tab + (lane & (COPIES - 1)), a.L.qshift, gs, out);
+  lane_decode_exact<CODE, KV, COPIES>(w, tab + (lane & (COPIES - 1)), a.L.qshift, gs, out);
   uint4* dst = reinterpret_cast<uint4*>(a.out + (tile - a.first) * 256 + q * 32);
 #pragma unroll
   for (int i = 0; i < 4; ++i) dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
 }
 
-template <int CODE, int K>
+template <int CODE, int KV>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int COPIES = GemvTable<CODE>::COPIES;
-  const size_t lds = (size_t)gemv_table_words<CODE, K>(a.L.Q) * 4 + 16;
-  (void)COPIES;
+  const size_t lds = (size_t)gemv_table_words<CODE, KV>(a.L.Q) * 4 + 16;
   static size_t have = 0;
-  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&decode_tile_kernel<CODE, K>), lds, &have);
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&decode_tile_kernel<CODE, KV>), lds, &have);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((a.count + 31) / 32);
-  hipLaunchKernelGGL((decode_tile_kernel<CODE, K>), dim3(grid), dim3(256), lds, stream, a);
+  hipLaunchKernelGGL((decode_tile_kernel<CODE, KV>), dim3(grid), dim3(256), lds, stream, a);
   return hipGetLastError();
 }
 
 template <int CODE>
 static hipError_t launch_decode_code(const DecodeArgs& a, hipStream_t stream) {
-  switch (a.L.k) {
-    case 2: return launch_decode_t<CODE, 2>(a, stream);
-    case 3: return launch_decode_t<CODE, 3>(a, stream);
-    case 4: return launch_decode_t<CODE, 4>(a, stream);
-    default: return hipErrorInvalidValue;
+#define QDEC_DEC_KV(KV)                                                          \
+  case KV:                                                                      \
+    if constexpr (kv_built(CODE, KV)) return launch_decode_t<CODE, KV>(a, stream); \
+    break;
+  switch (a.L.kv) {
+    QDEC_DEC_KV(2) QDEC_DEC_KV(3) QDEC_DEC_KV(4) QDEC_DEC_KV(5)
+    QDEC_DEC_KV(6) QDEC_DEC_KV(7) QDEC_DEC_KV(8)
+    default: break;
   }
+#undef QDEC_DEC_KV
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_tile(const DecodeArgs& a, hipStream_t stream) {
@@ -83,10 +89,6 @@ hipError_t launch_decode_tile(const DecodeArgs& a, hipStream_t stream) {
     case LUT: return launch_decode_code<LUT>(a, stream);
     default: return hipErrorInvalidValue;
   }
-}
-
-bool decode_supported(int code, int k) {
-  return code >= HYB && code <= HYB1 && k >= 2 && k <= 4;
 }
 
 // ---------------------------------------------------------------------------

@@ -31,21 +31,23 @@ __device__ __forceinline__ int gemm_swz(int r, int k) {
 }
 
 // LDS: lookup table, then B[2][64 batch][64 k] fp16 (double buffered).
-template <int CODE, int K>
+template <int CODE, int KV>
 __host__ __device__ inline size_t gemm_table_bytes(int Q) {
-  return ((size_t)gemv_table_words<CODE, K>(Q) * 4 + 15) & ~(size_t)15;
+  return ((size_t)gemv_table_words<CODE, KV>(Q) * 4 + 15) & ~(size_t)15;
 }
-template <int CODE, int K>
+template <int CODE, int KV>
 __host__ __device__ inline size_t gemm_lds_bytes(int Q) {
-  return gemm_table_bytes<CODE, K>(Q) + 2 * (64 * 128);
+  return gemm_table_bytes<CODE, KV>(Q) + 2 * (64 * 128);
 }
 
-template <int CODE, int K>
+template <int CODE, int KV>
 __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
+  using G = LaneGeom<CODE, KV>;
+  constexpr int NW = G::NW;
   constexpr int COPIES = GemvTable<CODE>::COPIES;
   extern __shared__ __align__(16) uint32_t smem[];
   uint32_t* tab = smem;
-  char* Bs = reinterpret_cast<char*>(smem) + gemm_table_bytes<CODE, K>(a.L.Q);
+  char* Bs = reinterpret_cast<char*>(smem) + gemm_table_bytes<CODE, KV>(a.L.Q);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -66,8 +68,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   if constexpr (CODE == HYB) fill_signed_table<COPIES>(tab, a.L.lut, a.L.Q, tid, GEMM_THREADS);
   if constexpr (CODE == HYB1) fill_signed_table<COPIES, 0x8000u>(tab, a.L.lut, a.L.Q, tid, GEMM_THREADS);
   if constexpr (CODE == LUT) fill_plain_table<1>(tab, a.L.lut, 1 << 15, tid, GEMM_THREADS);
-  if constexpr (CODE == VQ) fill_plain_table<COPIES>(tab, a.L.lut, 1 << (2 * K), tid, GEMM_THREADS);
-  if constexpr (CODE == NUQ) fill_plain_table<1>(tab, a.L.lut, 1 << K, tid, GEMM_THREADS);
+  if constexpr (CODE == VQ) fill_plain_table<COPIES>(tab, a.L.lut, 1 << KV, tid, GEMM_THREADS);
+  if constexpr (CODE == NUQ) fill_plain_table<1>(tab, a.L.lut, 1 << KV, tid, GEMM_THREADS);
   const uint32_t* tabc = tab + (lane & (COPIES - 1));
 
   // Every global load goes through a buffer resource and is issued
@@ -78,23 +80,25 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   // while it is below the lane's limit (32-bit offsets: a panel's codes and
   // X' stay far below 4 GiB).
   // Code words of this lane: tile (row 2*wave + tr, column 4*it + tc) of the
-  // panel; a panel's tile column is 8 tiles of 8K words.
-  const auto crs = make_rsrc(a.L.codes + (int64_t)panel * ntc * (64 * K), (uint32_t)ntc * (256u * K));
+  // panel; a panel's tile column is 8 tiles of TILE_WORDS words, and lane q
+  // reads NW words from word lane_word(q) of its tile.
+  constexpr uint32_t TB = 4u * G::TILE_WORDS;       // bytes per tile
+  const auto crs = make_rsrc(a.L.codes + (int64_t)panel * ntc * (8 * G::TILE_WORDS), (uint32_t)ntc * (8u * TB));
   const int itc = (ntc - tc + 3) >> 2 < it1 ? (ntc - tc + 3) >> 2 : it1;   // 4 it + tc < ntc
-  const uint32_t cbase = (uint32_t)tc * (256u * K) + (uint32_t)((2 * wave + tr) * (32 * K) + q * (4 * K));
+  const uint32_t cbase = (uint32_t)tc * (8u * TB) + (uint32_t)(2 * wave + tr) * TB + 4u * G::lane_word(q);
   // NUQ group scales of the lane's rows 2q, 2q+1 (fp16 [m][n/group]); a
   // group spans gpt tile columns
   const int gstride = CODE == NUQ ? (int)(n / a.L.group) : 0;
   const int gpt = CODE == NUQ ? a.L.group >> 4 : 1;
-  const int grow0 = panel * 128 + (2 * wave + tr) * 16 + 2 * q;
-  const auto grs = make_rsrc(a.L.gscale, CODE == NUQ ? (uint32_t)(m * gstride * 2) : 0u);
+  const int grow0 = (int)a.row0 + panel * 128 + (2 * wave + tr) * 16 + 2 * q;
+  const auto grs = make_rsrc(a.L.gscale, CODE == NUQ ? (uint32_t)(a.mz * gstride * 2) : 0u);
   auto load_codes = [&](int it, uint32_t* w) {
     const bool ok = it < itc;
-    buf_load_words<K>(crs, ok ? cbase + (uint32_t)it * (1024u * K) : BUF_OFF, w);
+    buf_load_words<NW>(crs, ok ? cbase + (uint32_t)it * (32u * TB) : BUF_OFF, w);
     if constexpr (CODE == NUQ) {
       const int g = (it * 4 + tc) / gpt;
-      w[K] = buf_load_u16(grs, ok ? (uint32_t)((grow0 * gstride + g) * 2) : BUF_OFF);
-      w[K + 1] = buf_load_u16(grs, ok ? (uint32_t)(((grow0 + 1) * gstride + g) * 2) : BUF_OFF);
+      w[NW] = buf_load_u16(grs, ok ? (uint32_t)((grow0 * gstride + g) * 2) : BUF_OFF);
+      w[NW + 1] = buf_load_u16(grs, ok ? (uint32_t)(((grow0 + 1) * gstride + g) * 2) : BUF_OFF);
     }
   };
   // X' chunks of this thread: batch row n0 + (c >> 3), k chunk c & 7, for
@@ -136,17 +140,17 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   // A tile column beyond n (only in the last step) is decoded from zero
   // words and then zeroed, so no value of the table can leak into the sums.
   auto decode = [&](int it, const uint32_t* wc, uint4* A) {
-    uint32_t w[K + 1];
+    uint32_t w[NW + 1];
 #pragma unroll
-    for (int i = 0; i < K; ++i) w[i] = wc[i];
-    w[K] = next_lane_word(w[0], lane);
+    for (int i = 0; i < NW; ++i) w[i] = wc[i];
+    lane_words_ready<CODE, KV>(w, lane);
     float gs[2] = {0.f, 0.f};
     if constexpr (CODE == NUQ) {
-      gs[0] = h2f((uint16_t)wc[K]);
-      gs[1] = h2f((uint16_t)wc[K + 1]);
+      gs[0] = h2f((uint16_t)wc[NW]);
+      gs[1] = h2f((uint16_t)wc[NW + 1]);
     }
     uint32_t out[16];
-    lane_decode_exact<CODE, K, COPIES>(w, tabc, a.L.qshift, gs, out);
+    lane_decode_exact<CODE, KV, COPIES>(w, tabc, a.L.qshift, gs, out);
     if (it * 4 + 3 >= ntc || it >= it1) {             // wave-uniform: the ragged or padding step
       const bool live = it < it1 && it * 4 + tc < ntc;
 #pragma unroll
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   // x[(s + 1) % 2] holds X'(s + 1).  A step multiplies s, then decodes s+1
   // (its VALU work overlaps the MFMAs in flight), stages X'(s+1) in the other
   // LDS buffer and refills the freed registers with steps s+5 and s+3.
-  constexpr int CW = CODE == NUQ ? K + 2 : K;        // code words (+ NUQ scales) per step
+  constexpr int CW = CODE == NUQ ? NW + 2 : NW;      // code words (+ NUQ scales) per step
   uint32_t c0[CW], c1[CW], c2[CW], c3[CW];
   uint4 x0[2], x1[2];
   uint4 A0[4], A1[4];
@@ -220,12 +224,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   // MFMA row i is weight row 16*(i/8) + 2*(i%8) + ra of the wave's 32 rows.
   // Each K split writes its own slice of the workspace (no atomics); the
   // output-RHT kernel sums the slices.
-  float* zs = a.z + (int64_t)split * a.b * m;
+  float* zs = a.z + (int64_t)split * a.b * a.mz;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int bb = n0 + nb * 16 + (lane & 15);
     if (bb >= a.b) continue;
-    float* zrow = zs + (int64_t)bb * m + (int64_t)panel * 128 + 32 * wave;
+    float* zrow = zs + (int64_t)bb * a.mz + a.row0 + (int64_t)panel * 128 + 32 * wave;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * (lane >> 4) + e;
@@ -235,26 +239,31 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   }
 }
 
-template <int CODE, int K>
+template <int CODE, int KV>
 static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t stream) {
-  const size_t lds = gemm_lds_bytes<CODE, K>(a.L.Q);
+  const size_t lds = gemm_lds_bytes<CODE, KV>(a.L.Q);
   static size_t have = 0;
   const hipError_t e =
-      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_kernel<CODE, K>), lds, &have);
+      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_kernel<CODE, KV>), lds, &have);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)((a.L.m / 128) * a.ksplit), (unsigned)((a.b + 63) / 64));
-  hipLaunchKernelGGL((gemm_kernel<CODE, K>), grid, dim3(GEMM_THREADS), lds, stream, a);
+  hipLaunchKernelGGL((gemm_kernel<CODE, KV>), grid, dim3(GEMM_THREADS), lds, stream, a);
   return hipGetLastError();
 }
 
 template <int CODE>
 static hipError_t launch_gemm_code(const GemmArgs& a, hipStream_t stream) {
-  switch (a.L.k) {
-    case 2: return launch_gemm_t<CODE, 2>(a, stream);
-    case 3: return launch_gemm_t<CODE, 3>(a, stream);
-    case 4: return launch_gemm_t<CODE, 4>(a, stream);
-    default: return hipErrorInvalidValue;
+#define QDEC_GEMM_KV(KV)                                                       \
+  case KV:                                                                    \
+    if constexpr (kv_built(CODE, KV)) return launch_gemm_t<CODE, KV>(a, stream); \
+    break;
+  switch (a.L.kv) {
+    QDEC_GEMM_KV(2) QDEC_GEMM_KV(3) QDEC_GEMM_KV(4) QDEC_GEMM_KV(5)
+    QDEC_GEMM_KV(6) QDEC_GEMM_KV(7) QDEC_GEMM_KV(8)
+    default: break;
   }
+#undef QDEC_GEMM_KV
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
@@ -269,7 +278,5 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
 }
-
-bool gemm_supported(int code, int k) { return code >= HYB && code <= HYB1 && k >= 2 && k <= 4; }
 
 }  // namespace qdec

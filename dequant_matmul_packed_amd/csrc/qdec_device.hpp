@@ -1,14 +1,18 @@
 // Device-side building blocks shared by the qdec kernels (gfx950, wave64).
 //
 // Packed format, lane layout and code rules are those of include/qdec.h:
-// a 16x16 tile is a 256*k-bit stream; 8 consecutive lanes handle one tile and
-// lane q of the group holds stream words [q*k, q*k + k), i.e. stream bits
-// [32kq, 32k(q+1)) = weights 32q .. 32q+31 = tile rows 2q and 2q+1.  The
-// state of a step is an L-bit window that may run into the first word of the
-// next lane (the last lane wraps to the first: the tail-biting stream), which
-// a cross-lane permute supplies ("QTIP: Quantization with Trellises and
-// Incoherence Processing", "Figure 2 (Q4)": the bitshift trellis decodes any
-// step from its own window, so all lanes decode in parallel).
+// a 16x16 tile is a stream of 256/V steps of kV bits; 8 consecutive lanes
+// handle one tile and lane q of the group decodes weights 32q .. 32q+31 (tile
+// rows 2q and 2q+1), the steps whose windows start in stream bits
+// [q*LB, (q+1)*LB), LB = (32/V)*kV.  The state of a step is an L-bit window
+// that may run past the lane's own bits into the next lane's first word (the
+// last lane wraps to the first: the tail-biting stream), which a cross-lane
+// permute supplies ("QTIP: Quantization with Trellises and Incoherence
+// Processing", "Figure 2 (Q4)": the bitshift trellis decodes any step from
+// its own window, so all lanes decode in parallel).  Every kernel takes kV,
+// the bits per trellis step, as its width parameter: k = kV/V bits per
+// weight, 2.5 at V = 2 and kV = 5 (the fractional widths of the "Q-Palette"
+// summary).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,9 +29,41 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 enum { HYB = 1, MAD1 = 2, INST3 = 3, NUQ = 4, VQ = 5, LUT = 6, HYB1 = 7 };
 
 __host__ __device__ constexpr int code_V(int code) { return (code == HYB || code == VQ) ? 2 : 1; }
-__host__ __device__ constexpr int code_L(int code, int k) {
-  return code == NUQ ? k : (code == VQ ? 2 * k : 16);
+// State bits: kV for the scalar and vector quantizers (L = kV: plain
+// indices), 16 for the trellis codes.
+__host__ __device__ constexpr int code_L(int code, int kv) {
+  return (code == NUQ || code == VQ) ? kv : 16;
 }
+// The (code, kV) pairs the kernels are built for: HYB at V = 2 takes kV 4 to
+// 8 (2 to 4 bits per weight in half-bit steps), VQ 4, 6, 8 (k = 2, 3, 4),
+// the V = 1 codes 2 to 4.
+__host__ __device__ constexpr bool kv_built(int code, int kv) {
+  return code == HYB ? (kv >= 4 && kv <= 8)
+       : code == VQ ? (kv == 4 || kv == 6 || kv == 8)
+       : (kv >= 2 && kv <= 4);
+}
+
+// Where a lane's bits sit for a code with KV bits per step: LANE_BITS =
+// (32/V)*KV stream bits per lane (its 32 weights), loaded as NW words from
+// word lane_word(q) of the tile; TILE_WORDS per tile.  When LANE_BITS is an
+// odd multiple of 16 (V = 2 and odd KV), odd lanes start 16 bits into their
+// first word (HALF).
+template <int CODE, int KV>
+struct LaneGeom {
+  static constexpr int V = code_V(CODE);
+  static constexpr int L = code_L(CODE, KV);
+  static constexpr int LANE_BITS = (32 / V) * KV;
+  static constexpr int NW = (LANE_BITS + 31) / 32;
+  static constexpr int TILE_WORDS = LANE_BITS / 4;
+  static constexpr bool HALF = (LANE_BITS % 32) != 0;
+  static_assert(LANE_BITS % 16 == 0, "lane segments start on 16-bit boundaries");
+  // every window of the lane (the last one starts at bit LANE_BITS - KV)
+  // ends within its NW words plus one more
+  static_assert(LANE_BITS - KV + L <= 32 * (NW + 1), "windows reach one word past the lane");
+  // shifted odd lanes have no valid word past their own NW
+  static_assert(!HALF || LANE_BITS - KV + L <= 32 * NW, "half-word lanes stay within NW words");
+  __host__ __device__ static constexpr uint32_t lane_word(int q) { return (uint32_t)(q * LANE_BITS) >> 5; }
+};
 
 // Computed-code constants (this library's own; the pages give none).
 constexpr uint32_t MAD1_A = 0x00EA4F79u, MAD1_C = 0xC2AA9973u;
@@ -107,6 +143,25 @@ __device__ __forceinline__ uint32_t next_lane_word(uint32_t v, int lane) {
   return (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)v);
 }
 
+// Completes a lane's word array w[0..NW] for window extraction: w[NW] is the
+// next lane's first word, and with HALF the odd lanes, whose words were
+// loaded from 16 bits before their segment, shift them into place (the next
+// lane is even there, so its first word starts exactly where the lane's
+// segment ends).  Called by all lanes (the permute reads every lane).
+template <int CODE, int KV>
+__device__ __forceinline__ void lane_words_ready(uint32_t* w, int lane) {
+  using G = LaneGeom<CODE, KV>;
+  w[G::NW] = next_lane_word(w[0], lane);
+  if constexpr (G::HALF) {
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int i = 0; i < G::NW; ++i) {
+      const uint32_t sh = __builtin_amdgcn_alignbit(w[i], w[i + 1], 16);
+      w[i] = odd ? sh : w[i];
+    }
+  }
+}
+
 // HYB hash: h = s*s + s (mod 2^16); the signed table index is h >> (15 - Q)
 // (Q index bits plus the sign bit 15).
 // Only bits below 16 of h are used, and they depend only on the low 16 bits
@@ -169,16 +224,15 @@ __device__ __forceinline__ void fill_plain_table(uint32_t* tab, const uint32_t* 
 // ---------------------------------------------------------------------------
 // Exact decode of a lane's 32 weights into 16 fp16 pairs:
 // out[i] = (weight 32q + 2i, weight 32q + 2i + 1), i.e. tile row 2q + (i >> 3),
-// columns 2(i & 7) and 2(i & 7) + 1.  w[0..K) are the lane's words and w[K]
-// the next lane's first word.  tabc points at this lane's copy of the table
+// columns 2(i & 7) and 2(i & 7) + 1.  w[0..NW] are the lane's words as
+// lane_words_ready leaves them.  tabc points at this lane's copy of the table
 // (HYB/VQ) or at the NUQ levels; gs[r] is the NUQ group scale of the lane's
 // row 2q + r (unused otherwise).
-template <int CODE, int K, int COPIES>
+template <int CODE, int KV, int COPIES>
 __device__ __forceinline__ void lane_decode_exact(const uint32_t* w, const uint32_t* tabc,
                                                   int qshift, const float* gs, uint32_t* out) {
   constexpr int V = code_V(CODE);
-  constexpr int L = code_L(CODE, K);
-  constexpr int KV = K * V;
+  constexpr int L = code_L(CODE, KV);
   if constexpr (V == 2) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) {

@@ -9,17 +9,27 @@
 
 namespace qdec {
 
-// A validated layer, as the kernels see it.
+// A validated layer, as the kernels see it: one part of rows (a half-TCQ
+// layer is launched part by part, each with its own codes, rows and kV).
 struct LayerArgs {
   const uint32_t* codes;
   const uint32_t* lut;
   const uint16_t* gscale;
   const uint32_t* sign_in;
   const uint32_t* sign_out;
-  int64_t m, n;
-  int code, k, Q, qshift, group;
+  int64_t m, n;        // rows of this part, columns
+  int code, kv, Q, qshift, group;   // kv: bits per trellis step (or index bits)
   int had_in, had_out;
   float scale;
+};
+
+// The row parts of a layer: rows [0, m_a) at kv, then [m_a, m) at kv_b
+// (half-TCQ), each a panel-ordered tile array of its own.
+struct LayerParts {
+  int count;
+  LayerArgs part[2];
+  int64_t row0[2];     // first output row of each part
+  int64_t tile0[2];    // storage index of each part's first tile
 };
 
 struct GemvArgs {
@@ -28,7 +38,9 @@ struct GemvArgs {
   uint16_t* y;         // [b][m] fp16
   int b;
   const uint16_t* xr;  // precomputed x' = RHT_in(x), fp16 [b][n], or NULL
-  float* z;            // [b][m] fp32 split-K accumulator (workspace; zero on entry, left zero)
+  float* z;            // [b][mz] fp32 split-K accumulator (workspace; zero on entry, left zero)
+  int64_t row0;        // first row of L (a part of the layer) in the layer
+  int64_t mz;          // rows of the whole layer (z's row stride)
   int Kc;              // columns per chunk (power of two, 64 .. 2048; Kc * b <= 4096)
   int nchunks;         // ceil(n / Kc)
   int U;               // rows per output block = max(had_out, 128)
@@ -57,7 +69,9 @@ struct RhtArgs {
 struct GemmArgs {
   LayerArgs L;
   const uint16_t* xr;  // [b][n] fp16, input RHT already applied
-  float* z;            // [ksplit][b][m] fp32 partial sums, one slice per K split
+  float* z;            // [ksplit][b][mz] fp32 partial sums, one slice per K split
+  int64_t row0;        // first row of L (a part of the layer) in the layer
+  int64_t mz;          // rows of the whole layer
   int b;
   int ksplit;          // K split factor
 };
@@ -97,6 +111,8 @@ inline hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes, size_t* h
 }
 
 // Kernel launchers (return hipSuccess or the launch error).
+// launch_gemv: the decode-and-multiply kernel of one part (adds into z);
+// launch_gemv_finish: the output side over the whole layer.
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 hipError_t launch_gemv_finish(const GemvArgs& a, hipStream_t stream);
 hipError_t launch_decode_tile(const DecodeArgs& a, hipStream_t stream);
@@ -105,10 +121,5 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 // Output side of the batched path: y = fp16(s_out .* (mult * H z)); z zeroed.
 hipError_t launch_rht_out_f32(const float* z, int nsum, uint16_t* y, int64_t rows, int64_t m, int block,
                               const uint32_t* signs, float mult, hipStream_t stream);
-
-// Which (code, k) pairs and batch sizes the kernels are built for.
-bool gemv_supported(int code, int k, int b);
-bool decode_supported(int code, int k);
-bool gemm_supported(int code, int k);
 
 }  // namespace qdec

@@ -51,11 +51,20 @@
  *                    state itself indexes a table of 2^16 fp16 values
  *                    (16 x 2^L bits = 128 KiB, held in LDS).
  *
- * Packed format (version 1).
+ * Bit widths.  A trellis step (or a NUQ/VQ index) takes kV bits for V
+ * weights: k = kV/V bits per weight.  The trellis codes may give kV directly
+ * (field kv), which allows fractional widths at V = 2: kV = 5 is 2.5 bits
+ * per weight, kV = 7 is 3.5 ("Q-Palette" summary: fractional-bit
+ * quantizers).  Half-TCQ ("Q-Palette" summary: two trellis widths in one
+ * layer, 2.5 and 3 bits averaging 2.75) cuts the rows at m_a, a multiple of
+ * 128: rows [0, m_a) take kv, rows [m_a, m) take kv_b.
+ *
+ * Packed format (version 2).
  *  - W_hat is cut into 16x16 tiles; tile (R, C) covers rows 16R..16R+15 and
  *    columns 16C..16C+15; weight j of a tile sits at (j >> 4, j & 15).
- *  - Each tile is a stream of 256*k bits held in 8k little-endian uint32
- *    words; stream bit p is bit 31 - (p & 31) of word p >> 5 (MSB first).
+ *  - Each tile is a stream of (256/V)*kV bits held in (256/V)*kV/32
+ *    little-endian uint32 words; stream bit p is bit 31 - (p & 31) of word
+ *    p >> 5 (MSB first).
  *  - Step t (t = 0 .. 256/V - 1) covers weights tV .. tV+V-1.  Its state is
  *    the L-bit window starting at stream bit t*kV, read MSB first, wrapping
  *    around the end of the tile's stream (tail-biting): the last L-kV bits of
@@ -64,6 +73,9 @@
  *  - Tiles are stored in panels of 8 tile-rows (128 output rows); inside a
  *    panel, column by column: storage index of tile (R, C) is
  *      ((R / 8) * (n / 16) + C) * 8 + (R % 8).
+ *    A half-TCQ layer stores the tiles of rows [0, m_a) this way, then those
+ *    of rows [m_a, m), indexed as a layer of their own (R counted from m_a/16),
+ *    at their own width; storage indices run on across the two parts.
  *  - HYB LUT: 2^Q uint32 words, each an fp16 pair (low half = first weight);
  *    at V = 1, each word's low half is the value (the high half is ignored).
  *    NUQ table: 2^k uint32 words, fp16 level in the low half.  VQ table:
@@ -96,7 +108,7 @@
 extern "C" {
 #endif
 
-#define QDEC_ABI_VERSION 1u
+#define QDEC_ABI_VERSION 2u
 
 typedef enum {
   QDEC_OK = 0,
@@ -117,21 +129,27 @@ typedef enum {
 } qdec_code;
 
 /* One quantized linear layer.  Plain data; all pointers are device pointers
- * owned by the caller.  Supported combinations:
- *   HYB    L = 16, V = 2 or 1, k in {2, 3, 4}, Q in [1, 11]
- *   1MAD   L = 16, V = 1, k in {2, 3, 4}
- *   3INST  L = 16, V = 1, k in {2, 3, 4}
+ * owned by the caller.  Supported combinations (kV = k*V, or kv):
+ *   HYB    L = 16, V = 2, kV in {4, 5, 6, 7, 8}; or V = 1, kV in {2, 3, 4};
+ *          Q in [1, 11]
+ *   1MAD   L = 16, V = 1, kV in {2, 3, 4}
+ *   3INST  L = 16, V = 1, kV in {2, 3, 4}
  *   NUQ    L = k,  V = 1, k in {2, 3, 4}, group a multiple of 16 dividing n
  *   VQ     L = 2k, V = 2, k in {2, 3, 4}
- *   LUT    L = 16, V = 1, k in {2, 3, 4}
+ *   LUT    L = 16, V = 1, kV in {2, 3, 4}
+ * The trellis codes (HYB, 1MAD, 3INST, LUT) may set kv (then k = 0) and a
+ * second part (m_a, kv_b), each width one of the above.
  * m % 128 == 0, n % 16 == 0; had_in (had_out) a power of two dividing n (m),
  * at most 16384; codes 16-byte aligned.                                      */
 typedef struct qdec_layer {
   uint32_t abi_version;          /* QDEC_ABI_VERSION                          */
   int32_t code;                  /* qdec_code                                 */
   int32_t L, k, V, Q;            /* state bits, bits/weight, weights/step, HYB index bits */
+  int32_t kv;                    /* trellis bits per step of rows [0, m_a); 0 = k*V */
+  int32_t kv_b;                  /* bits per step of rows [m_a, m); 0 when m_a = 0 */
+  int64_t m_a;                   /* half-TCQ: rows of the first part; 0 = one part */
   int64_t m, n;                  /* W_hat is m (out) x n (in)                 */
-  const uint32_t *codes;         /* m*n*k/32 words, packed format above       */
+  const uint32_t *codes;         /* m*n*kV/(32V) words (summed over the parts) */
   const uint32_t *lut;           /* HYB / NUQ / VQ / LUT table (see format), else NULL */
   const uint16_t *group_scale;   /* NUQ: fp16 [m][n/group]; else NULL         */
   int32_t group;                 /* NUQ group length along a row; else 0      */

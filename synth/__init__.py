@@ -97,6 +97,20 @@ class HostLayer:
         return b
 
 
+def code_words(code: int, m: int, n: int, k: int, V: Optional[int] = None, kv: int = 0,
+               kv_b: int = 0, m_a: int = 0) -> int:
+    """uint32 words of packed codes: per 256-weight tile, 256/V steps of kV
+    bits (kV = kv, or k * V), the rows split at m_a when kv_b is given."""
+    if V is None:
+        V = 2 if code in (HYB, VQ) else 1
+    kva = kv if kv else k * V
+    rows_a = m_a if m_a else m
+    words = (rows_a // 16) * (n // 16) * (256 // V) * kva // 32
+    if m_a:
+        words += ((m - m_a) // 16) * (n // 16) * (256 // V) * kv_b // 32
+    return words
+
+
 def make_layer(code: int, m: int, n: int, k: int, *, tag: str, V: Optional[int] = None,
                Q: int = 9, scale: float = 0.02, signs: bool = True,
                had_in: Optional[int] = None, had_out: Optional[int] = None,
@@ -120,12 +134,7 @@ def make_layer(code: int, m: int, n: int, k: int, *, tag: str, V: Optional[int] 
         V, L = 2, 2 * k
     else:
         raise ValueError("unknown code %r" % code)
-    spt = 256 // V                       # trellis steps (or indices) per tile
-    kva = kv if kv else k * V
-    rows_a = m_a if m_a else m
-    nwords = (rows_a // 16) * (n // 16) * spt * kva // 32
-    if m_a:
-        nwords += ((m - m_a) // 16) * (n // 16) * spt * kv_b // 32
+    nwords = code_words(code, m, n, k, V, kv, kv_b, m_a)
     if codes is None:
         codes = random_words(rng_for(tag, "codes"), nwords)
     assert codes.size == nwords

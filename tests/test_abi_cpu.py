@@ -57,6 +57,10 @@ def test_workspace_sizes(q):
     gm = q.qdec_workspace_bytes(lay, 64, q.QDEC_OP_GEMM)
     # X' (b x n fp16), then one fp32 b x m slice per K split (here 2: n/64)
     assert gm == 64 * 128 * 2 + 2 * 64 * 256 * 4
+    # a half-TCQ layer needs the same workspace as one of a single width
+    half = _layer(q, k=0, kv=5, m_a=128, kv_b=6)
+    assert q.qdec_workspace_bytes(half, 1, q.QDEC_OP_GEMV) == gv
+    assert q.qdec_workspace_bytes(half, 64, q.QDEC_OP_GEMM) == gm
     assert q.qdec_workspace_bytes(lay, 9, q.QDEC_OP_GEMV) == 0
     assert q.qdec_workspace_bytes(lay, 0, q.QDEC_OP_GEMM) == 0
     assert q.qdec_workspace_bytes(lay, 1, 99) == 0
@@ -70,6 +74,11 @@ BAD_LAYERS = [
     dict(lut=None), dict(code=9), dict(code=4, L=3, k=3, V=1, group=128, group_scale=None),
     dict(code=4, L=3, k=3, V=1, group=24, group_scale=FAKE), dict(code=5, L=6, k=2, V=2),
     dict(code=2, V=2), dict(layer_scale=float("nan")),
+    # bits per step and half-TCQ parts
+    dict(kv=5), dict(k=0, kv=17), dict(k=0, kv=5, m_a=100, kv_b=6), dict(k=0, kv=5, m_a=256, kv_b=6),
+    dict(kv_b=6), dict(k=0, kv=5, m_a=128, kv_b=0), dict(m_a=-128, kv_b=4),
+    dict(code=4, L=3, k=0, kv=3, V=1, group=128, group_scale=FAKE),
+    dict(code=5, L=4, k=2, V=2, m_a=128, kv_b=4),
 ]
 
 
@@ -86,11 +95,11 @@ def test_invalid_layers_rejected(q, kw):
         q.QDEC_EINVAL, q.QDEC_EUNSUPPORTED)
 
 
-def test_unsupported_but_valid(q):
-    lay = _layer(q, k=5)
-    d = ctypes.byref(lay.desc())
-    assert q.raw_status("qdec_decode_tile", d, 0, 1, FAKE + (1 << 24), None) == q.QDEC_EUNSUPPORTED
-    lay = _layer(q, Q=13)
+@pytest.mark.parametrize("kw", [dict(k=5), dict(Q=13), dict(k=0, kv=9), dict(k=0, kv=3),
+                                dict(k=0, kv=5, m_a=128, kv_b=9), dict(code=2, V=1, k=0, kv=5),
+                                dict(code=2, V=1, k=2, m_a=128, kv_b=6)])
+def test_unsupported_but_valid(q, kw):
+    lay = _layer(q, **kw)
     d = ctypes.byref(lay.desc())
     assert q.raw_status("qdec_decode_tile", d, 0, 1, FAKE + (1 << 24), None) == q.QDEC_EUNSUPPORTED
 

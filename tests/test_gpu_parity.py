@@ -411,3 +411,89 @@ def test_gemm_agrees_with_gemv(q, dev):
     g = _to_f64(q.gemm(lay, xt))
     torch.cuda.synchronize()
     assert _rel(g, a) < REL_TOL
+
+
+# ---------------------------------------------------------------------------
+# Fractional widths (kV = 5, 7 at V = 2: 2.5 and 3.5 bits per weight) and
+# half-TCQ (rows split at a panel boundary into two widths): decode, GEMV,
+# GEMM.  Lanes of odd kV start mid-word, and the parts have their own tile
+# arrays, so every case is checked on whole small layers and on a decode
+# range that crosses the part boundary.
+FRAC_CASES = [(synth.HYB, 5, 0, 0), (synth.HYB, 7, 0, 0), (synth.HYB, 5, 6, 128),
+              (synth.HYB, 7, 4, 256), (synth.HYB, 4, 5, 128), (synth.HYB, 8, 7, 384),
+              (synth.MAD1, 2, 3, 128), (synth.LUT, 4, 2, 256)]
+
+
+@pytest.mark.parametrize("code,kv,kv_b,m_a", FRAC_CASES,
+                         ids=["%s_kv%d_%d_ma%d" % (synth.CODE_NAMES[c], a, b_, ma) for c, a, b_, ma in FRAC_CASES])
+def test_fractional_and_half_tcq(q, dev, code, kv, kv_b, m_a):
+    import torch
+    for (m, n) in [(384, 160), (512, 592), (1024, 1024)]:
+        if m_a >= m:
+            continue
+        host = synth.make_layer(code, m, n, 0, kv=kv, kv_b=kv_b, m_a=m_a,
+                                tag="fr%d_%d_%d_%d_%d" % (code, kv, kv_b, m_a, n))
+        lay = q.upload_layer(host, dev)
+        _say("frac decode", synth.CODE_NAMES[code], kv, kv_b, m_a, m, n)
+        want = oracle.decode_tiles_storage(host, 0, host.n_tiles)
+        out = torch.zeros((host.n_tiles, 256), dtype=torch.int16, device=dev)
+        q.qdec_decode_tile(lay, 0, host.n_tiles, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), want)
+        if m_a:
+            ta = (m_a // 16) * (n // 16)
+            first, cnt = ta - 10, 37
+            out2 = torch.zeros((cnt, 256), dtype=torch.int16, device=dev)
+            q.qdec_decode_tile(lay, first, cnt, out2)
+            torch.cuda.synchronize()
+            assert np.array_equal(out2.cpu().numpy().view(np.uint16), want[first:first + cnt])
+        for b in (1, 3, 8):
+            _say("frac gemv", b)
+            x16 = synth.activations("frx%d_%d" % (b, n), b, n)
+            y = q.gemv(lay, _f16_tensor(x16, dev))
+            torch.cuda.synchronize()
+            assert _rel(_to_f64(y), oracle.forward(host, x16)) < REL_TOL, (m, n, b)
+        _say("frac gemm")
+        x16 = synth.activations("frx70_%d" % n, 70, n)
+        y = q.gemm(lay, _f16_tensor(x16, dev))
+        torch.cuda.synchronize()
+        assert _rel(_to_f64(y), oracle.forward(host, x16)) < REL_TOL, (m, n)
+
+
+FRAC_FULL = [(4096, 4096, 5, 0, 0, 1), (4096, 4096, 7, 0, 0, 1), (4096, 4096, 5, 6, 2048, 1),
+             (28672, 8192, 5, 6, 14336, 64)]
+
+
+@pytest.mark.parametrize("m,n,kv,kv_b,m_a,b", FRAC_FULL,
+                         ids=["%dx%d_kv%d_%d_b%d" % (m, n, a, b_, bb) for m, n, a, b_, ma, bb in FRAC_FULL])
+def test_fractional_full_size_sampled(q, dev, m, n, kv, kv_b, m_a, b):
+    """Full-size fractional and half-TCQ layers in the launch configuration
+    the bench times (GEMV at b = 1, GEMM at b = 64), sampled output blocks
+    on both sides of the part boundary; the decode of every tile."""
+    import torch
+    had_in = 8192 if n == 8192 else None
+    had_out = 4096 if m == 28672 else None
+    host = synth.make_layer(synth.HYB, m, n, 0, kv=kv, kv_b=kv_b, m_a=m_a, had_in=had_in,
+                            had_out=had_out, tag="frfull%d_%d_%d" % (m, kv, kv_b))
+    x16 = synth.activations("frfullx%d" % n, b, n)
+    lay = q.upload_layer(host, dev)
+    _say("frac full", m, n, kv, kv_b, m_a, b)
+    fn = q.gemv if b <= 8 else q.gemm
+    y = _to_f64(fn(lay, _f16_tensor(x16, dev)))
+    torch.cuda.synchronize()
+    nblk = host.m // host.had_out
+    cols = sorted({0, b - 1})
+    # the first and last blocks, and those holding the last row of the first
+    # part and the first row of the second
+    blks = sorted({0, nblk - 1} | ({(m_a - 1) // host.had_out, m_a // host.had_out} if m_a else set()))
+    for blk in blks:
+        ref = oracle.forward_block(host, x16, cols, blk)
+        got = y[cols][:, blk * host.had_out:(blk + 1) * host.had_out]
+        assert _rel(got, ref) < REL_TOL, blk
+    out = torch.empty((host.n_tiles, 256), dtype=torch.int16, device=dev)
+    q.qdec_decode_tile(lay, 0, host.n_tiles, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    want = oracle.decode_tiles_storage(host, 0, host.n_tiles)
+    bad = np.nonzero((got != want).any(1))[0]
+    assert bad.size == 0, "first mismatching tiles %s" % bad[:8]
