@@ -28,6 +28,15 @@ Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``
                              tile the cyclic walk of its 128 kV-bit stream
                              (numpy slicing); even kV equals the integer k;
                              a two-part layer decodes as two layers stacked
+  viterbi / encode_stream    pinned: brute force over every bit string of
+                             tiny trellises (free ends, constrained ends,
+                             tail-biting with every wrap tried); L = kV is
+                             the nearest codeword; the returned stream's
+                             cyclic walk is the returned path
+  encode_layer               pinned: MSE on N(0,1) between the rate-
+                             distortion limit 2^(-2k) and the Lloyd-Max
+                             scalar MSE (2 and 3 bits); the decoded layer's
+                             error equals the reported cost
   rht                        pinned: H H^T = B I, Kronecker recursion,
                              Parseval, round trip, numpy's matrix product
   forward / forward_block    pinned: a small layer against an independent
@@ -96,6 +105,12 @@ def lib():
         L.orc_forward_block.argtypes = [P, P, i64, P, i64, i64, P]
         L.orc_state_value.argtypes = [i32, i32, i32, P, ctypes.c_uint32, P]
         L.orc_lloyd_max_gauss.argtypes = [i32, i32, P, P]
+        f32 = ctypes.c_float
+        L.orc_viterbi.restype = f32
+        L.orc_viterbi.argtypes = [i32, i32, i32, i32, P, P, f32, i32, i64, i64, P]
+        L.orc_encode_stream.restype = f32
+        L.orc_encode_stream.argtypes = [i32, i32, i32, i32, P, P, f32, i32, P, P]
+        L.orc_encode_layer.argtypes = [P, P, P, i32, P]
         L.orc_omp_threads.restype = i32
         L.orc_set_threads.argtypes = [i32]
         L.orc_set_threads.restype = None
@@ -266,6 +281,47 @@ def state_values_all(code: int, L: int = 16, Q: int = 9, lut=None, V: int = 2) -
     """Values of all 2^L states as fp16 bit patterns, shape (2^L, V)."""
     rows = [state_value(code, s, Q, lut, V) for s in range(1 << L)]
     return np.array(rows, dtype=np.uint16)
+
+
+def viterbi(L: int, kV: int, V: int, vals, x, scale: float = 1.0, r: int = 0,
+            start_P: int = -1, end_P: int = -1) -> tuple:
+    """Best path of the bitshift trellis for the targets x (T x V): returns
+    (fp32 cost, states).  vals: 2^L x V code values."""
+    vals = np.ascontiguousarray(vals, dtype=np.float32).reshape(-1)
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    T = x.size // V
+    st = np.zeros(T, dtype=np.uint32)
+    c = lib().orc_viterbi(L, kV, V, T, _ptr(vals), _ptr(x), scale, r, start_P, end_P, _ptr(st))
+    return float(c), st
+
+
+def encode_stream(L: int, kV: int, V: int, vals, x, scale: float = 1.0, exact: bool = False) -> tuple:
+    """Tail-biting encode of the targets x (T x V) into T*kV stream bits:
+    returns (fp32 cost, words, states)."""
+    vals = np.ascontiguousarray(vals, dtype=np.float32).reshape(-1)
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    T = x.size // V
+    words = np.zeros((T * kV + 31) // 32, dtype=np.uint32)
+    st = np.zeros(T, dtype=np.uint32)
+    c = lib().orc_encode_stream(L, kV, V, T, _ptr(vals), _ptr(x), scale, int(exact), _ptr(words), _ptr(st))
+    if np.isnan(c):
+        raise ValueError("encode_stream: invalid arguments")
+    return float(c), words, st
+
+
+def encode_layer(layer, W, exact: bool = False) -> tuple:
+    """Codes of the layer's format (its code, V, Q, lut, widths and scale)
+    that minimise each tile's squared error against W (m x n): returns
+    (codes, sum of the tiles' fp32 costs).  layer.codes only sizes the
+    output."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    assert W.shape == (layer.m, layer.n)
+    out = np.zeros_like(np.asarray(layer.codes, dtype=np.uint32))
+    s, keep = _struct(layer)
+    sse = ctypes.c_double()
+    if lib().orc_encode_layer(ctypes.byref(s), _ptr(W), _ptr(out), int(exact), ctypes.byref(sse)):
+        raise ValueError("encode_layer: invalid layer")
+    return out, sse.value
 
 
 def lloyd_max_gauss(nlev: int, iters: int = 2000) -> tuple:

@@ -59,7 +59,18 @@
  *    e in the low half of word e/2 when e is even, the high half when odd);
  *  - 1MAD / 3INST constants are this library's own (not on the pages);
  *  - Sylvester-ordered Hadamard, 1/sqrt(B) normalisation, signs before H on
- *    the input and after H on the output, sign bit set means -1.
+ *    the input and after H on the output, sign bit set means -1;
+ *  - the encoder (the step before the path) minimises the squared error of a
+ *    tile over all tail-biting streams with the Viterbi algorithm on the
+ *    bitshift trellis ("Figure 2 (Q4)": the trellis lives in the state
+ *    numbering; "Why does TCQ work? (Q5)": TCQ searches a 2^(kV)-sized part
+ *    of the 2^L-state space at every step).  The pages do not say how the
+ *    wrap of a tail-biting stream is chosen; here a first pass over the
+ *    sequence rotated by half its length picks the L-kV wrap bits (the top
+ *    bits of the first state), and a second pass is the exact Viterbi
+ *    given them.  Path costs are accumulated in fp32 in a fixed order (no
+ *    fused multiply-add), ties going to the smaller index, so that a GPU
+ *    encoder with the same arithmetic takes the same decisions.
  *
  * Floating point: fp64 throughout; conversion to fp16 by this file's own
  * round-to-nearest-even (orc_f16_from_double).  Build with -ffp-contract=off
@@ -640,6 +651,166 @@ int orc_lloyd_max_gauss(int nlev, int iters, double *levels, double *mse) {
     *mse = acc;
   }
   return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The encoder: Viterbi on the bitshift trellis.                              */
+
+/* Squared error of one step: targets x[0..V) against scale * values c[0..V),
+ * in fp32, products and differences rounded one by one (the build forbids
+ * contraction into fused multiply-adds).                                     */
+static float orc_step_dist(const float *x, const float *c, float scale, int V) {
+  float d = 0.0f;
+  for (int i = 0; i < V; i++) {
+    float p = scale * c[i];
+    float e = x[i] - p;
+    float sq = e * e;
+    d = (i == 0) ? sq : d + sq;
+  }
+  return d;
+}
+
+/* Viterbi over the bitshift trellis (L state bits, kV new bits per step) for
+ * T steps of V targets: state s_t is reached from the 2^kV states whose low
+ * L-kV bits are the high L-kV bits of s_t, and the path cost is the fp32
+ * sum over t of the squared error of step (t + r) mod T against value(s_t)
+ * (vals: 2^L x V floats).  start_P >= 0 admits only first states with high
+ * L-kV bits start_P; end_P >= 0 only last states with low L-kV bits end_P.
+ * Among equal costs the smaller predecessor, and the smaller last state, win.
+ * Writes the best path's states; returns its cost (INFINITY if none).       */
+float orc_viterbi(int L, int kV, int V, int T, const float *vals, const float *x, float scale,
+                  int r, int64_t start_P, int64_t end_P, uint32_t *states) {
+  if (L < 1 || L > 24 || kV < 1 || kV > L || T < 1 || (V != 1 && V != 2)) return NAN;
+  const int64_t S = (int64_t)1 << L, G = (int64_t)1 << (L - kV), U = (int64_t)1 << kV;
+  float *cost = (float *)malloc(sizeof(float) * (size_t)S);
+  float *next = (float *)malloc(sizeof(float) * (size_t)S);
+  uint8_t *bp = (uint8_t *)malloc((size_t)(T * G));
+  if (!cost || !next || !bp) { free(cost); free(next); free(bp); return NAN; }
+  const float *x0 = x + (size_t)(r % T) * V;
+  for (int64_t st = 0; st < S; st++) {
+    int ok = start_P < 0 || (st >> kV) == start_P;
+    cost[st] = ok ? orc_step_dist(x0, vals + st * V, scale, V) : INFINITY;
+  }
+  for (int t = 1; t < T; t++) {
+    const float *xt = x + (size_t)((t + r) % T) * V;
+    for (int64_t g = 0; g < G; g++) {
+      /* predecessors of the states g * 2^kV + v: u * G + g, u = 0 .. 2^kV-1 */
+      float best = cost[g];
+      int bu = 0;
+      for (int64_t u = 1; u < U; u++) {
+        float c = cost[u * G + g];
+        if (c < best) { best = c; bu = (int)u; }
+      }
+      bp[(int64_t)t * G + g] = (uint8_t)bu;
+      for (int64_t v = 0; v < U; v++) {
+        int64_t st = g * U + v;
+        next[st] = best + orc_step_dist(xt, vals + st * V, scale, V);
+      }
+    }
+    float *tmp = cost; cost = next; next = tmp;
+  }
+  float best = INFINITY;
+  int64_t bs = -1;
+  for (int64_t st = 0; st < S; st++) {
+    if (end_P >= 0 && (st & (G - 1)) != end_P) continue;
+    if (bs < 0 || cost[st] < best) { best = cost[st]; bs = st; }
+  }
+  if (bs >= 0 && !isinf(best)) {
+    states[T - 1] = (uint32_t)bs;
+    for (int t = T - 1; t >= 1; t--) {
+      int64_t g = states[t] >> kV;
+      states[t - 1] = (uint32_t)((int64_t)bp[(int64_t)t * G + g] * G + g);
+    }
+  } else {
+    best = INFINITY;
+  }
+  free(cost); free(next); free(bp);
+  return best;
+}
+
+/* Tail-biting encode of T steps into a stream of T*kV bits (MSB first in
+ * words): the first state's L bits, then the kV new bits of every later
+ * state.  exact = 0: the wrap bits P (high L-kV bits of the first state)
+ * come from a first pass over the sequence rotated by T/2, whose best path
+ * passes through some state at the original step 0; exact = 1: every P is
+ * tried (tiny trellises only).  The second pass is the Viterbi with the
+ * first state's high bits and the last state's low bits both P, which is
+ * exactly the set of tail-biting streams with those wrap bits.  Returns the
+ * cost; states (T entries) receives the path.                               */
+float orc_encode_stream(int L, int kV, int V, int T, const float *vals, const float *x, float scale,
+                        int exact, uint32_t *words, uint32_t *states) {
+  const int64_t nbits = (int64_t)T * kV;
+  if (nbits < L) return NAN;
+  const int64_t G = (int64_t)1 << (L - kV);
+  float best;
+  if (!exact) {
+    const int r = T / 2;
+    uint32_t *rot = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)T);
+    if (!rot) return NAN;
+    float c1 = orc_viterbi(L, kV, V, T, vals, x, scale, r, -1, -1, rot);
+    int64_t P = (int64_t)(rot[(T - r) % T] >> kV);
+    free(rot);
+    if (isnan(c1)) return NAN;
+    best = orc_viterbi(L, kV, V, T, vals, x, scale, 0, P, P, states);
+  } else {
+    uint32_t *tmp = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)T);
+    if (!tmp) return NAN;
+    best = INFINITY;
+    for (int64_t P = 0; P < G; P++) {
+      float c = orc_viterbi(L, kV, V, T, vals, x, scale, 0, P, P, tmp);
+      if (c < best) { best = c; memcpy(states, tmp, sizeof(uint32_t) * (size_t)T); }
+    }
+    free(tmp);
+  }
+  if (isnan(best) || isinf(best)) return best;
+  const int64_t nwords = (nbits + 31) / 32;
+  memset(words, 0, sizeof(uint32_t) * (size_t)nwords);
+  int64_t pos = 0;
+  for (int i = L - 1; i >= 0 && pos < nbits; i--, pos++)
+    if ((states[0] >> i) & 1u) words[pos >> 5] |= 1u << (31 - (pos & 31));
+  for (int t = 1; t < T; t++)
+    for (int i = kV - 1; i >= 0 && pos < nbits; i--, pos++)
+      if ((states[t] >> i) & 1u) words[pos >> 5] |= 1u << (31 - (pos & 31));
+  return best;
+}
+
+/* Encode a whole layer: W (m x n fp32, row-major) -> codes_out in the
+ * layer's packed format (both parts of a half-TCQ layer), each tile
+ * minimising its squared error against layer_scale x value.  The layer's
+ * code, V, Q, lut and widths select the trellis; its codes pointer is not
+ * read.  sse_out (optional): the sum of the tiles' path costs.              */
+int orc_encode_layer(const orc_layer *Lr, const float *W, uint32_t *codes_out, int exact,
+                     double *sse_out) {
+  if (orc_validate(Lr) || !orc_is_trellis(Lr->code) || Lr->L != 16) return -1;
+  const int V = Lr->V, T = 256 / V;
+  const int64_t S = (int64_t)1 << Lr->L;
+  float *vals = (float *)malloc(sizeof(float) * (size_t)(S * V));
+  if (!vals) return -1;
+  for (int64_t st = 0; st < S; st++) {
+    uint16_t o[2];
+    orc_state_value(Lr->code, V, Lr->Q, Lr->lut, (uint32_t)st, o);
+    for (int i = 0; i < V; i++) vals[st * V + i] = (float)orc_f16_to_double(o[i]);
+  }
+  const int64_t tiles = (Lr->m / 16) * (Lr->n / 16);
+  double sse = 0.0;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : sse)
+  for (int64_t i = 0; i < tiles; i++) {
+    int64_t R, C;
+    int kV;
+    orc_storage_coords(Lr, i, &R, &C);
+    const uint32_t *w = orc_tile_words(Lr, R, C, &kV);
+    float x[256];
+    uint32_t st[256];
+    for (int j = 0; j < 256; j++) x[j] = W[(R * 16 + (j >> 4)) * Lr->n + C * 16 + (j & 15)];
+    float c = orc_encode_stream(Lr->L, kV, V, T, vals, x, Lr->scale, exact,
+                                codes_out + (w - Lr->codes), st);
+    if (isnan(c) || isinf(c)) bad = 1;
+    else sse += c;
+  }
+  free(vals);
+  if (sse_out) *sse_out = sse;
+  return bad ? -1 : 0;
 }
 
 int orc_omp_threads(void) {

@@ -610,3 +610,142 @@ def test_forward_fractional_matches_numpy(kv, kv_b, m_a):
     got = oracle.forward(lay, x)
     want = _numpy_forward(lay, x)
     assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# The encoder (Viterbi on the bitshift trellis)
+
+def _path_cost(vals, x, st, V, scale=1.0):
+    """fp64 squared error of a state path (independent of the encoder)."""
+    T = st.size
+    return float(((x.reshape(T, V).astype(np.float64) -
+                   scale * vals.reshape(-1, V)[st].astype(np.float64)) ** 2).sum())
+
+
+def _all_streams(nbits):
+    for v in range(1 << nbits):
+        yield np.array([(v >> (nbits - 1 - i)) & 1 for i in range(nbits)], np.uint8)
+
+
+TINY = [(4, 1, 1, 8), (6, 2, 1, 6), (6, 3, 2, 4), (5, 2, 2, 5)]
+
+
+@pytest.mark.parametrize("L,kV,V,T", TINY)
+def test_viterbi_linear_equals_brute_force(L, kV, V, T):
+    """Free start and end: the Viterbi optimum is the minimum over every bit
+    string of L + (T-1) kV bits, walked by the (pinned) shift register."""
+    rng = np.random.default_rng(L * 1000 + kV * 10 + V)
+    for trial in range(3):
+        vals = rng.standard_normal((1 << L, V)).astype(np.float32)
+        x = rng.standard_normal(T * V).astype(np.float32)
+        best = min(_path_cost(vals, x, oracle.walk_bits(b, L, kV, T, False), V)
+                   for b in _all_streams(L + (T - 1) * kV))
+        c, st = oracle.viterbi(L, kV, V, vals, x)
+        assert abs(c - best) <= 1e-5 * best
+        assert abs(_path_cost(vals, x, st, V) - best) <= 1e-5 * best
+        # consecutive states share L - kV bits
+        G = 1 << (L - kV)
+        assert all((st[t] & (G - 1)) == (st[t + 1] >> kV) for t in range(T - 1))
+
+
+@pytest.mark.parametrize("L,kV,V,T", TINY)
+def test_tailbiting_encoder_equals_brute_force(L, kV, V, T):
+    """Trying every wrap P gives the minimum over all T*kV-bit tail-biting
+    streams; the two-pass encoder returns a valid stream (so never below the
+    minimum) whose cyclic walk is the path it reports."""
+    rng = np.random.default_rng(L * 1000 + kV * 10 + V + 7)
+    for trial in range(3):
+        vals = rng.standard_normal((1 << L, V)).astype(np.float32)
+        x = rng.standard_normal(T * V).astype(np.float32)
+        costs = [_path_cost(vals, x, oracle.walk_bits(b, L, kV, T, True), V)
+                 for b in _all_streams(T * kV)]
+        best = min(costs)
+        for exact in (True, False):
+            c, words, st = oracle.encode_stream(L, kV, V, vals, x, exact=exact)
+            bits = np.unpackbits(words.astype(">u4").view(np.uint8))[:T * kV]
+            walk = oracle.walk_bits(bits, L, kV, T, True)
+            assert np.array_equal(walk, st)
+            assert abs(_path_cost(vals, x, walk, V) - c) <= 1e-5 * c
+            if exact:
+                assert abs(c - best) <= 1e-5 * best
+            else:
+                assert c >= best * (1 - 1e-6)
+
+
+def test_viterbi_constraints_equal_brute_force():
+    """start_P / end_P restrict the first state's high and the last state's
+    low L - kV bits."""
+    L, kV, V, T = 6, 2, 1, 5
+    rng = np.random.default_rng(99)
+    vals = rng.standard_normal((1 << L, V)).astype(np.float32)
+    x = rng.standard_normal(T * V).astype(np.float32)
+    G = 1 << (L - kV)
+    for P0, P1 in [(3, 3), (0, 15), (9, -1), (-1, 5)]:
+        best = None
+        for b in _all_streams(L + (T - 1) * kV):
+            st = oracle.walk_bits(b, L, kV, T, False)
+            if P0 >= 0 and (st[0] >> kV) != P0:
+                continue
+            if P1 >= 0 and (st[-1] & (G - 1)) != P1:
+                continue
+            c = _path_cost(vals, x, st, V)
+            best = c if best is None else min(best, c)
+        c, st = oracle.viterbi(L, kV, V, vals, x, start_P=P0, end_P=P1)
+        assert abs(c - best) <= 1e-5 * best, (P0, P1)
+
+
+def test_encoder_L_equals_kV_is_nearest_neighbour():
+    """L = kV: no overlap between steps, so each step takes its nearest
+    codeword (plain kV-bit V-dim VQ, "Ablations and fast inference")."""
+    rng = np.random.default_rng(3)
+    for L, V in [(4, 1), (6, 2)]:
+        T = 32
+        vals = rng.standard_normal((1 << L, V)).astype(np.float32)
+        x = rng.standard_normal(T * V).astype(np.float32)
+        c, words, st = oracle.encode_stream(L, L, V, vals, x)
+        d = ((x.reshape(T, 1, V).astype(np.float64) - vals[None].astype(np.float64)) ** 2).sum(2)
+        assert np.array_equal(st, d.argmin(1))
+
+
+@pytest.mark.parametrize("code,kV,V,lo,hi", [
+    (synth.MAD1, 2, 1, "rd_limit_2bit", "lloyd_max_mse_2bit"),
+    (synth.MAD1, 3, 1, "rd_limit_3bit", "lloyd_max_mse_3bit"),
+    (synth.HYB, 4, 2, "rd_limit_2bit", "lloyd_max_mse_2bit")])
+def test_encoder_mse_between_rate_distortion_and_lloyd_max(code, kV, V, lo, hi):
+    """L = 16 trellis on i.i.d. N(0,1): the MSE per weight lies above the
+    rate-distortion limit 2^(-2k) and well below the optimal scalar
+    quantizer at the same rate; the tail-biting stream costs at most a few
+    percent over the free-ended Viterbi optimum (a lower bound)."""
+    g = _read_golden("bit_accounting.txt")
+    k = kV / V
+    lay = synth.make_layer(code, 128, 64, 0, kv=kV, V=V, tag="encmse%d%d" % (code, kV), scale=1.0)
+    vals = oracle.state_values_all(code, 16, lay.Q, lay.lut, V).view(np.float16).astype(np.float32)
+    rng = np.random.default_rng(kV)
+    W = rng.standard_normal((lay.m, lay.n)).astype(np.float32)
+    codes, sse = oracle.encode_layer(lay, W)
+    mse = sse / W.size
+    assert float(g[lo]) < mse < 0.7 * float(g[hi]), mse
+    assert mse < float(g[lo]) * (1.25 if k == 2 else 1.3)
+    # the reported cost is the error of the decoded layer
+    What = oracle.decode_dense(dataclasses.replace(lay, codes=codes))
+    assert abs(((W - What) ** 2).sum() - sse) <= 1e-4 * sse
+    # a few tiles against the free-ended optimum
+    for i in range(3):
+        x = W[16 * i:16 * i + 16, :16].reshape(-1)
+        c, _, _ = oracle.encode_stream(16, kV, V, vals, x)
+        cl, _ = oracle.viterbi(16, kV, V, vals, x)
+        assert cl <= c <= 1.12 * cl
+
+
+def test_encode_layer_half_tcq_round_trip():
+    """A half-TCQ layer encodes part by part at its own widths; decoding the
+    codes gives back the reported error."""
+    lay = synth.make_layer(synth.HYB, 256, 32, 0, kv=5, kv_b=6, m_a=128, tag="enchalf", scale=0.5)
+    rng = np.random.default_rng(11)
+    W = (0.5 * rng.standard_normal((256, 32))).astype(np.float32)
+    codes, sse = oracle.encode_layer(lay, W)
+    What = oracle.decode_dense(dataclasses.replace(lay, codes=codes))
+    err = ((W - What) ** 2)
+    assert abs(err.sum() - sse) <= 1e-4 * sse
+    # more bits per weight, less error: the 3-bit half beats the 2.5-bit half
+    assert err[128:].mean() < err[:128].mean()
