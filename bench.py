@@ -265,6 +265,7 @@ def main():
         detail.update(bench_gemm(q, torch, dev, stream))
         detail.update(bench_code_variants(q, torch, dev))
         detail.update(bench_fractional(q, torch, dev))
+        detail.update(bench_encoder(q, torch, dev, cpu=not args.no_cpu_baseline))
 
     if not args.no_detail and not args.only:
         ceil = measured_ceilings(torch, dev)
@@ -433,6 +434,55 @@ def bench_code_variants(q, torch, dev):
         ("LUT_L16", synth.LUT, 2, {})), "bench/var/")
     log("code variants (4096x4096 k=2):", out)
     return {"code_variants_4096_k2": out}
+
+
+def bench_encoder(q, torch, dev, cpu=True):
+    """The tail-biting trellis encoder on a 4096x4096 HYB layer at 2 bits
+    (65536 tiles) of i.i.d. N(0,1) x 0.02 targets: tiles/s on the GPU, the
+    MSE per weight relative to the target variance, and (cpu) the oracle's
+    one-thread time on a few tiles of the same layer."""
+    import synth
+    m = n = 4096
+    host = synth.make_layer(synth.HYB, m, n, 2, tag="bench/enc", codes=np.zeros(m * n * 2 // 32, np.uint32))
+    lay = q.upload_layer(host, dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    W = torch.randn((m, n), generator=g, device=dev, dtype=torch.float32) * 0.02
+    ws = q.workspace(lay, 1, q.QDEC_OP_ENCODE, dev)
+    codes = torch.empty(m * n * 2 // 32, dtype=torch.int32, device=dev)
+    q.encode(lay, W, codes, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    q.encode(lay, W, codes, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3
+    ntiles = (m // 16) * (n // 16)
+    # error of the decoded layer, tiles in storage order
+    lay2 = q.Layer(code=lay.code, L=lay.L, k=lay.k, V=lay.V, Q=lay.Q, m=m, n=n, codes=codes, lut=lay.lut,
+                   layer_scale=lay.layer_scale, had_in=lay.had_in, had_out=lay.had_out)
+    dec = torch.empty((ntiles, 256), dtype=torch.float16, device=dev)
+    q.qdec_decode_tile(lay2, 0, ntiles, dec)
+    Wt = W.view(m // 128, 8, 16, n // 16, 16).permute(0, 3, 1, 2, 4).reshape(ntiles, 256)
+    mse = ((Wt - dec.float() * np.float32(host.scale)) ** 2).mean().item() / 0.02 ** 2
+    out = {"layer": "4096x4096 HYB k=2 V=2 Q=9", "tiles": ntiles, "seconds": round(sec, 4),
+           "tiles_per_s": round(ntiles / sec), "mse_rel": round(mse, 5)}
+    if cpu:
+        import oracle
+        threads = oracle.omp_threads()
+        oracle.set_threads(1)
+        Wh = W[:16, :64].cpu().numpy()
+        vals = oracle.state_values_all(synth.HYB, 16, host.Q, host.lut, 2).view(np.float16).astype(np.float32)
+        t0 = time.time()
+        for c in range(4):
+            oracle.encode_stream(16, 4, 2, vals, Wh[:, 16 * c:16 * c + 16].reshape(-1), host.scale)
+        cpu_tile = (time.time() - t0) / 4
+        oracle.set_threads(threads)
+        out["oracle_one_thread_s_per_tile"] = round(cpu_tile, 4)
+        out["gpu_vs_oracle_one_thread"] = round(ntiles / sec * cpu_tile, 1)
+    log("encoder:", out)
+    return {"encoder_4096_hyb_k2": out}
 
 
 def bench_fractional(q, torch, dev):

@@ -19,12 +19,12 @@ LIB_PATH = os.path.join(_PKG, "libqdec.so")
 
 QDEC_OK, QDEC_EINVAL, QDEC_EUNSUPPORTED, QDEC_EWORKSPACE, QDEC_EHIP, QDEC_ENODEV = 0, -1, -2, -3, -4, -5
 QDEC_CODE_HYB, QDEC_CODE_1MAD, QDEC_CODE_3INST, QDEC_CODE_NUQ, QDEC_CODE_VQ, QDEC_CODE_LUT = 1, 2, 3, 4, 5, 6
-QDEC_OP_GEMV, QDEC_OP_GEMM = 1, 2
+QDEC_OP_GEMV, QDEC_OP_GEMM, QDEC_OP_ENCODE = 1, 2, 3
 QDEC_ABI_VERSION = 2
 
 # The exported symbols, as declared in include/qdec.h.
 EXPORTS = ("qdec_abi_version", "qdec_status_string", "qdec_last_error", "qdec_workspace_bytes",
-           "qdec_rht", "qdec_gemv", "qdec_gemm", "qdec_decode_tile")
+           "qdec_rht", "qdec_gemv", "qdec_gemm", "qdec_decode_tile", "qdec_encode")
 
 
 class QdecError(RuntimeError):
@@ -71,6 +71,8 @@ def _load():
         fn.argtypes = [P, P, P, i64, P, ctypes.c_size_t, P]
     lib.qdec_decode_tile.restype = ctypes.c_int
     lib.qdec_decode_tile.argtypes = [P, i64, i64, P, P]
+    lib.qdec_encode.restype = ctypes.c_int
+    lib.qdec_encode.argtypes = [P, P, P, P, ctypes.c_size_t, P]
     if lib.qdec_abi_version() != QDEC_ABI_VERSION:
         raise ImportError("libqdec.so ABI version mismatch")
     return lib
@@ -178,6 +180,11 @@ def qdec_decode_tile(layer: Layer, first_tile: int, n_tiles: int, out, stream=No
                                  _stream(stream)), "qdec_decode_tile")
 
 
+def qdec_encode(layer: Layer, w, codes, ws, ws_bytes: int, stream=None) -> None:
+    _check(_lib.qdec_encode(ctypes.byref(layer.desc()), _ptr(w), _ptr(codes), _ptr(ws), ws_bytes,
+                            _stream(stream)), "qdec_encode")
+
+
 def raw_status(fn_name: str, *args) -> int:
     """Call an entry point with raw ctypes arguments and return its status
     (for error-path tests)."""
@@ -237,3 +244,15 @@ def gemm(layer: Layer, x, ws=None, y=None):
         y = torch.empty((b, layer.m), dtype=torch.float16, device=x.device)
     qdec_gemm(layer, x, y, b, ws, ws.numel())
     return y
+
+
+def encode(layer: Layer, w, codes=None, ws=None):
+    """Codes of the layer's format for the fp32 matrix w [m, n] (the
+    tail-biting trellis encoder); returns the int32 tensor of code words."""
+    import torch
+    if codes is None:
+        codes = torch.empty(layer.code_bytes // 4, dtype=torch.int32, device=w.device)
+    if ws is None:
+        ws = workspace(layer, 1, QDEC_OP_ENCODE, w.device)
+    qdec_encode(layer, w, codes, ws, ws.numel())
+    return codes

@@ -240,6 +240,11 @@ size_t qdec_workspace_bytes(const qdec_layer* layer, int64_t batch, int32_t op) 
     if (batch < 1 || batch > 256) return 0;
     return gemm_ws_bytes(L.m, L.n, batch);
   }
+  if (op == QDEC_OP_ENCODE) {
+    if (batch != 1) return 0;
+    if (L.code != HYB && L.code != HYB1 && L.code != MAD1 && L.code != INST3) return 0;
+    return encode_ws_bytes(code_V(L.code));
+  }
   return 0;
 }
 
@@ -389,6 +394,39 @@ int qdec_gemm(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
   e = launch_rht_out_f32(z, g.ksplit, y, batch, L.m, L.had_out, L.sign_out,
                          (float)((double)L.scale / sqrt((double)L.had_out)), s);
   return status_of(e);
+}
+
+int qdec_encode(const qdec_layer* layer, const float* w, uint32_t* codes, void* ws, size_t ws_bytes,
+                void* stream) {
+  LayerArgs L;
+  LayerParts parts;
+  int st = check_layer(layer, &L, &parts);
+  if (st) return st;
+  if (L.code != HYB && L.code != HYB1 && L.code != MAD1 && L.code != INST3) return QDEC_EUNSUPPORTED;
+  if (!w || !codes || !aligned(w, 4) || !aligned(codes, 16)) return QDEC_EINVAL;
+  const int V = code_V(L.code);
+  const size_t wbytes = (size_t)(L.m * L.n) * 4;
+  const int64_t last = parts.count - 1;
+  const size_t cbytes = (size_t)((parts.part[last].codes - L.codes) +
+                                 (parts.part[last].m / 16) * (L.n / 16) * (8 * parts.part[last].kv / V)) * 4;
+  if (overlap(w, wbytes, codes, cbytes)) return QDEC_EINVAL;
+  const size_t need = encode_ws_bytes(V);
+  if (!ws || !aligned(ws, 256) || ws_bytes < need) return QDEC_EWORKSPACE;
+  if (overlap(ws, need, w, wbytes) || overlap(ws, need, codes, cbytes)) return QDEC_EINVAL;
+  const int d = check_device();
+  if (d) return d;
+  for (int p = 0; p < parts.count; ++p) {
+    EncodeArgs a;
+    a.L = parts.part[p];
+    a.w = w;
+    a.row0 = parts.row0[p];
+    a.codes = codes + (parts.part[p].codes - L.codes);
+    a.bp = (uint32_t*)ws;
+    a.ntiles = (parts.part[p].m / 16) * (L.n / 16);
+    const hipError_t e = launch_encode(a, (hipStream_t)stream);
+    if (e != hipSuccess) return status_of(e);
+  }
+  return QDEC_OK;
 }
 
 int qdec_decode_tile(const qdec_layer* layer, int64_t first_tile, int64_t n_tiles, uint16_t* out,

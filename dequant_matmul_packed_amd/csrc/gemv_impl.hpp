@@ -427,7 +427,6 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   }
 
   // ---- 4. stream the tiles ------------------------------------------------
-  const int q = lane & 7, tl = lane >> 3;
   const uint32_t* tabc = regA + (lane & (COPIES - 1));
   const int qshift = a.L.qshift;
   float acc[2][NB];

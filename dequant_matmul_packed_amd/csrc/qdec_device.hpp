@@ -180,6 +180,7 @@ __device__ __forceinline__ uint32_t inst3_bits(uint32_t s) {
 
 // Exact fp16 value of 1MAD: fp16(fp32((sigma - 510) * fp32(1/sqrt(21845)))).
 __device__ __forceinline__ uint16_t mad1_value_bits(uint32_t s) {
+#pragma clang fp contract(off)   // the fp32 product is rounded before the fp16 conversion
   const int sigma = (int)__builtin_amdgcn_sad_u8(mad1_lcg(s), 0u, 0u);
   return f2h_bits((float)(sigma - 510) * mad1_norm());
 }

@@ -76,6 +76,19 @@ struct GemmArgs {
   int ksplit;          // K split factor
 };
 
+// The encoder: one part of a layer, its targets and its output codes.
+struct EncodeArgs {
+  LayerArgs L;         // the part (its kv, rows m and tile count)
+  const float* w;      // [layer m][n] fp32 targets (row-major, whole layer)
+  int64_t row0;        // first row of the part in w
+  uint32_t* codes;     // the part's output code words
+  uint32_t* bp;        // workspace: [ENCODE_GRID][256/V][1024] backpointer words
+  int64_t ntiles;      // tiles of the part
+};
+// Workgroups of the encoder (one tile each at a time, 1024 threads).
+constexpr int ENCODE_GRID = 256;
+inline size_t encode_ws_bytes(int V) { return (size_t)ENCODE_GRID * (256 / V) * 1024 * 4; }
+
 // Workspace layout of qdec_gemv: the fp32 accumulator z [b][m] (must start
 // at zero; left zero), then the fp16 x' [b][n] of the separate-RHT path.
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -118,6 +131,7 @@ hipError_t launch_gemv_finish(const GemvArgs& a, hipStream_t stream);
 hipError_t launch_decode_tile(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_rht(const RhtArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_encode(const EncodeArgs& a, hipStream_t stream);
 // Output side of the batched path: y = fp16(s_out .* (mult * H z)); z zeroed.
 hipError_t launch_rht_out_f32(const float* z, int nsum, uint16_t* y, int64_t rows, int64_t m, int block,
                               const uint32_t* signs, float mult, hipStream_t stream);

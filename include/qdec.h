@@ -162,10 +162,11 @@ typedef struct qdec_layer {
 /* Operation selector for qdec_workspace_bytes.                               */
 #define QDEC_OP_GEMV 1
 #define QDEC_OP_GEMM 2
+#define QDEC_OP_ENCODE 3
 
-/* Bytes of workspace qdec_gemv (op = QDEC_OP_GEMV) or qdec_gemm
- * (op = QDEC_OP_GEMM) needs for this layer at this batch.  0 on a bad
- * argument.                                                                  */
+/* Bytes of workspace qdec_gemv (op = QDEC_OP_GEMV), qdec_gemm
+ * (op = QDEC_OP_GEMM) or qdec_encode (op = QDEC_OP_ENCODE, batch = 1) needs
+ * for this layer at this batch.  0 on a bad argument.                        */
 size_t qdec_workspace_bytes(const qdec_layer *layer, int64_t batch, int32_t op);
 
 /* Randomized Hadamard transform of `rows` rows of length n, block-diagonal
@@ -193,6 +194,25 @@ int qdec_gemv(const qdec_layer *layer, const uint16_t *x, uint16_t *y,
  * 256-byte aligned; its contents on entry do not matter.                    */
 int qdec_gemm(const qdec_layer *layer, const uint16_t *x, uint16_t *y,
               int64_t batch, void *ws, size_t ws_bytes, void *stream);
+
+/* Tail-biting trellis encoder, the step before the matmuls: writes into
+ * `codes` (the layer's code words in the packed format, both parts of a
+ * half-TCQ layer) the streams that minimise, tile by tile, the squared error
+ * sum (w - layer_scale x value)^2 against w (fp32 [m][n], row-major, device;
+ * finite values).  The search is the Viterbi algorithm on the bitshift
+ * trellis ("Figure 2 (Q4)": the predecessors of a state are the 2^kV states
+ * whose low L-kV bits are its high L-kV bits; "Why does TCQ work? (Q5)").
+ * The wrap of a tail-biting stream is chosen by a first, free-ended pass
+ * over the step sequence rotated by half its length (the high L-kV bits of
+ * the state its best path takes at step 0); the second pass is the exact
+ * Viterbi over the streams with that wrap.  Path costs are fp32 sums in a
+ * fixed order, ties to the smaller predecessor and last state, so the codes
+ * are a deterministic function of w.  Codes HYB (V = 1, 2), 1MAD and 3INST
+ * (QDEC_EUNSUPPORTED otherwise); layer->codes is not read.  ws:
+ * qdec_workspace_bytes(layer, 1, QDEC_OP_ENCODE) bytes, 256-byte aligned;
+ * its contents do not matter.  codes: 16-byte aligned, not overlapping w.  */
+int qdec_encode(const qdec_layer *layer, const float *w, uint32_t *codes, void *ws,
+                size_t ws_bytes, void *stream);
 
 /* Decode tiles [first_tile, first_tile + n_tiles) in storage order into
  * out[n_tiles][256] fp16, tile-local row-major.  Values are the code values

@@ -151,3 +151,33 @@ def test_valid_call_without_device_reports_enodev(q):
     need = q.qdec_workspace_bytes(lay, 1, q.QDEC_OP_GEMV)
     st = q.raw_status("qdec_gemv", d, FAKE + (1 << 24), FAKE + (1 << 25), 1, FAKE + (1 << 26), need, None)
     assert st == q.QDEC_ENODEV
+
+
+def test_encode_workspace_and_argument_errors(q):
+    lay = _layer(q)
+    # one [256/V][1024] word array of backpointers per encoder workgroup (256)
+    assert q.qdec_workspace_bytes(lay, 1, q.QDEC_OP_ENCODE) == 256 * 128 * 1024 * 4
+    mad = _layer(q, code=q.QDEC_CODE_1MAD, V=1)
+    assert q.qdec_workspace_bytes(mad, 1, q.QDEC_OP_ENCODE) == 256 * 256 * 1024 * 4
+    assert q.qdec_workspace_bytes(lay, 2, q.QDEC_OP_ENCODE) == 0
+    lut = _layer(q, code=q.QDEC_CODE_LUT, V=1)
+    assert q.qdec_workspace_bytes(lut, 1, q.QDEC_OP_ENCODE) == 0
+    d = ctypes.byref(lay.desc())
+    W, C, WS = FAKE + (1 << 24), FAKE + (1 << 26), FAKE + (1 << 28)
+    need = q.qdec_workspace_bytes(lay, 1, q.QDEC_OP_ENCODE)
+    E = q.QDEC_EINVAL
+    assert q.raw_status("qdec_encode", d, None, C, WS, need, None) == E
+    assert q.raw_status("qdec_encode", d, W, None, WS, need, None) == E
+    assert q.raw_status("qdec_encode", d, W + 2, C, WS, need, None) == E        # misaligned w
+    assert q.raw_status("qdec_encode", d, W, C + 4, WS, need, None) == E        # misaligned codes
+    assert q.raw_status("qdec_encode", d, W, W + 64, WS, need, None) == E       # codes overlap w
+    assert q.raw_status("qdec_encode", d, W, C, None, need, None) == q.QDEC_EWORKSPACE
+    assert q.raw_status("qdec_encode", d, W, C, WS, need - 4, None) == q.QDEC_EWORKSPACE
+    assert q.raw_status("qdec_encode", d, W, C, WS + 16, need, None) == q.QDEC_EWORKSPACE
+    assert q.raw_status("qdec_encode", d, W, C, W, need, None) == E             # ws overlaps w
+    dl = ctypes.byref(lut.desc())
+    assert q.raw_status("qdec_encode", dl, W, C, WS, need, None) == q.QDEC_EUNSUPPORTED
+    for kw in BAD_LAYERS[:6]:
+        bad = _layer(q, **kw)
+        assert q.raw_status("qdec_encode", ctypes.byref(bad.desc()), W, C, WS, need, None) in (
+            q.QDEC_EINVAL, q.QDEC_EUNSUPPORTED)

@@ -497,3 +497,53 @@ def test_fractional_full_size_sampled(q, dev, m, n, kv, kv_b, m_a, b):
     want = oracle.decode_tiles_storage(host, 0, host.n_tiles)
     bad = np.nonzero((got != want).any(1))[0]
     assert bad.size == 0, "first mismatching tiles %s" % bad[:8]
+
+
+# ---------------------------------------------------------------------------
+# The encoder: codes bit-exact against the oracle's Viterbi (same fp32 path
+# costs and tie rules), on layers of more tiles than the encoder's 256
+# workgroups, for every state layout (kV = 2 .. 8) and code.
+ENC_CASES = [(synth.HYB, 2, 4, 9, 0, 0), (synth.HYB, 2, 5, 9, 0, 0), (synth.HYB, 2, 6, 9, 0, 0),
+             (synth.HYB, 2, 7, 9, 0, 0), (synth.HYB, 2, 8, 9, 0, 0), (synth.HYB, 1, 3, 6, 0, 0),
+             (synth.MAD1, 1, 2, 9, 0, 0), (synth.MAD1, 1, 4, 9, 0, 0), (synth.INST3, 1, 3, 9, 0, 0),
+             (synth.HYB, 2, 5, 9, 6, 128)]
+
+
+@pytest.mark.parametrize("code,V,kv,Q,kv_b,m_a", ENC_CASES,
+                         ids=["%s_V%d_kv%d_%d" % (synth.CODE_NAMES[c], v, k, kb) for c, v, k, qq, kb, ma in ENC_CASES])
+def test_encode_matches_oracle(q, dev, code, V, kv, Q, kv_b, m_a):
+    import torch
+    m, n = 256, 288                      # 288 tiles: more than one per workgroup
+    host = synth.make_layer(code, m, n, 0, V=V, Q=Q, kv=kv, kv_b=kv_b, m_a=m_a,
+                            tag="enc%d_%d_%d_%d" % (code, V, kv, kv_b))
+    rng = synth.rng_for("encw", code, kv)
+    W = (host.scale * rng.standard_normal((m, n))).astype(np.float32)
+    _say("encode", synth.CODE_NAMES[code], V, kv, kv_b, m_a)
+    want, sse = oracle.encode_layer(host, W)
+    lay = q.upload_layer(host, dev)
+    got = q.encode(lay, torch.from_numpy(W).to(dev))
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().view(np.uint32)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, "first differing code words %s of %d" % (bad[:8], got.size)
+    # the codes decode (on the GPU) to a layer with the reported error
+    lay2 = q.upload_layer(synth.with_codes(host, got), dev)
+    out = torch.empty((host.n_tiles, 256), dtype=torch.int16, device=dev)
+    q.qdec_decode_tile(lay2, 0, host.n_tiles, out)
+    torch.cuda.synchronize()
+    tiles = out.cpu().numpy().view(np.float16).astype(np.float64) * np.float32(host.scale)
+    W2 = np.zeros((m, n))
+    for i in range(host.n_tiles):
+        R, C = _storage_coords(host, i)
+        W2[R * 16:R * 16 + 16, C * 16:C * 16 + 16] = tiles[i].reshape(16, 16)
+    assert abs(((W - W2) ** 2).sum() - sse) <= 1e-3 * sse
+
+
+def _storage_coords(host, i):
+    """Grid coordinates of storage index i (the part boundary of a
+    half-TCQ layer included)."""
+    tpr = host.n // 16
+    ta = (host.m_a // 16) * tpr if host.m_a else host.n_tiles
+    j = i if i < ta else i - ta
+    R, C = (j >> 3) // tpr * 8 + (j & 7), (j >> 3) % tpr
+    return (R if i < ta else R + host.m_a // 16), C
