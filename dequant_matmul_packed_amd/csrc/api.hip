@@ -186,6 +186,21 @@ int gemm_ksplit(int64_t m, int64_t n, int64_t b) {
   return (int)ks;
 }
 
+// Whether a one-column GEMV takes the separate input transform: every
+// workgroup of the fused path transforms its own chunk, reading all B_in
+// values of x for it.  Tuning override QDEC_GEMV_XR = 0 / 1.
+bool gemv_separate_rht(int64_t m, int64_t n, int64_t b, int had_in) {
+  static int forced = -2;
+  if (forced == -2) {
+    const char* e = getenv("QDEC_GEMV_XR");
+    forced = e ? (atoi(e) != 0) : -1;
+  }
+  if (b > 1) return true;
+  if (forced >= 0) return forced != 0;
+  (void)m; (void)n; (void)had_in;
+  return false;
+}
+
 int gemv_chunk(int64_t m, int64_t n, int64_t b) {
   static int forced = -1;
   if (forced < 0) {
@@ -311,10 +326,10 @@ int qdec_gemv(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
   // the 1MAD matmul path multiplies by the fp32 normaliser, as the decode does
   const double f32norm = (double)(float)factor;
   a.out_mult = (float)((double)L.scale * f32norm / sqrt((double)L.had_out));
-  if (batch > 1) {
+  if (gemv_separate_rht(L.m, L.n, batch, L.had_in)) {
     // x' = RHT_in(x) once, by the RHT kernel into the workspace, then the
-    // GEMV loads its slices (with one batch column the GEMV's workgroups
-    // transform their own chunks: no extra launch)
+    // GEMV loads its slices (otherwise, with one batch column, the GEMV's
+    // workgroups transform their own chunks: no extra launch)
     uint16_t* xr = (uint16_t*)((char*)ws + wl.xr);
     RhtArgs r;
     r.in = x;

@@ -88,7 +88,7 @@ __host__ __device__ inline size_t gemv_lds_bytes(int Q, int Kc, int U) {
          (CODE == INST3 ? (size_t)NB * Kc * 4 : 0) + gemv_wred_bytes<NB>(Kc);
 }
 
-template <int CODE, int KV, int NB, int PF, bool SL>
+template <int CODE, int KV, int NB, int PF, bool SL, bool XR>
 __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   using G = LaneGeom<CODE, KV>;
   constexpr int V = G::V;
@@ -126,7 +126,6 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   // RHT's wait on them does not also wait on the (slower) code loads --
   // vector-memory counters drain in issue order.  With b > 1, x' comes
   // precomputed (args.xr) and step 2 loads the chunk's slice of it instead.
-  constexpr bool XR = NB > 1;
   const int Bi = a.L.had_in;
   const int arows = Kc < Bi ? Bi / Kc : 1;
   const int64_t rbase = Kc < Bi ? (c0 / Bi) * Bi : c0;
@@ -591,27 +590,36 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   }
 }
 
-template <int CODE, int KV, int NB, int PF, bool SL>
+template <int CODE, int KV, int NB, int PF, bool SL, bool XR>
 hipError_t launch_gemv_v(const GemvArgs& a, hipStream_t stream) {
   const size_t lds = gemv_lds_bytes<CODE, KV, NB>(a.L.Q, a.Kc, a.U);
   static size_t have = 0;
   const hipError_t e =
-      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<CODE, KV, NB, PF, SL>), lds, &have);
+      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<CODE, KV, NB, PF, SL, XR>), lds, &have);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((a.L.m / 128) * a.nchunks);
-  hipLaunchKernelGGL((gemv_kernel<CODE, KV, NB, PF, SL>), dim3(grid), dim3(GEMV_THREADS), lds, stream, a);
+  hipLaunchKernelGGL((gemv_kernel<CODE, KV, NB, PF, SL, XR>), dim3(grid), dim3(GEMV_THREADS), lds, stream, a);
   return hipGetLastError();
+}
+
+// XR: x' comes precomputed (args.xr, always with more than one batch
+// column; with one column for layers whose chunk transforms would cost
+// more than the separate transform's launch).
+template <int CODE, int KV, int NB, bool XR>
+hipError_t launch_gemv_x(const GemvArgs& a, hipStream_t stream) {
+  const bool sl = (XR || a.L.had_in <= 4096) && ((CODE != HYB && CODE != HYB1) || a.L.Q <= 9);
+  if (a.Kc <= 128 && sl) return launch_gemv_v<CODE, KV, NB, 2, true, XR>(a, stream);
+  if (a.Kc <= 256 && sl) return launch_gemv_v<CODE, KV, NB, 4, true, XR>(a, stream);
+  if (sl) return launch_gemv_v<CODE, KV, NB, 8, true, XR>(a, stream);
+  return launch_gemv_v<CODE, KV, NB, 8, false, XR>(a, stream);
 }
 
 template <int CODE, int KV, int NB>
 hipError_t launch_gemv_t(const GemvArgs& a, hipStream_t stream) {
-  const bool sl = (NB > 1 || a.L.had_in <= 4096) && ((CODE != HYB && CODE != HYB1) || a.L.Q <= 9);
   if constexpr (NB == 1) {
-    if (a.Kc <= 128 && sl) return launch_gemv_v<CODE, KV, NB, 2, true>(a, stream);
-    if (a.Kc <= 256 && sl) return launch_gemv_v<CODE, KV, NB, 4, true>(a, stream);
+    if (!a.xr) return launch_gemv_x<CODE, KV, 1, false>(a, stream);
   }
-  if (sl) return launch_gemv_v<CODE, KV, NB, 8, true>(a, stream);
-  return launch_gemv_v<CODE, KV, NB, 8, false>(a, stream);
+  return launch_gemv_x<CODE, KV, NB, true>(a, stream);
 }
 
 template <int CODE, int KV>

@@ -242,6 +242,113 @@ __global__ __launch_bounds__(256) void rht_kernel(RhtArgs a) {
   }
 }
 
+// fp16 input with few (row, block) pairs: each block is cut over S
+// workgroups.  With Sylvester ordering H_B = H_S (x) H_Bs (Bs = B / S), so
+// outputs [j Bs, (j+1) Bs) of a block are H_Bs applied to u = sum over a of
+// H_S[j][a] x_a, x_a the a-th Bs-slice (input signs applied): every
+// workgroup reads the whole block, forms its own +/- combination and runs a
+// Bs-point transform.  Chunks of 8 values as in rht_kernel, J per thread.
+template <int S, int J>
+__global__ __launch_bounds__(256) void rht_split_kernel(RhtArgs a) {
+  extern __shared__ __align__(16) float buf[];
+  const int tid = threadIdx.x;
+  const int B = a.block, Bs = B / S;
+  const int64_t nblk = a.n / B;
+  const int jpart = (int)(blockIdx.x % S);
+  const int64_t rb = blockIdx.x / S;
+  const int64_t row = rb / nblk;
+  const int64_t c0 = (rb % nblk) * B;
+  const int64_t off = row * a.n + c0;
+  const int nch = Bs >> 3;
+  const auto srs = make_rsrc(a.signs, a.signs ? (uint32_t)(((a.n + 31) >> 5) * 4) : 0u);
+  const auto irs = make_rsrc((const uint16_t*)a.in + off, (uint32_t)B * 2u);
+  uint4 p[S][J];
+  uint32_t sw[S][J];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int ch = tid + 256 * j;
+      const bool ok = ch < nch;
+      p[s][j] = buf_load_u4(irs, ok ? (uint32_t)(s * Bs + 8 * ch) * 2u : BUF_OFF);
+      sw[s][j] = buf_load_u32(srs, ok && a.mode == 0 ? (uint32_t)(((c0 + s * Bs + 8 * ch) >> 5) * 4) : BUF_OFF);
+    }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int ch = tid + 256 * j;
+    if (ch < nch) {
+      float u[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) u[e] = 0.f;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const uint32_t r[4] = {p[s][j].x, p[s][j].y, p[s][j].z, p[s][j].w};
+        const uint32_t sg = sw[s][j] >> ((c0 + s * Bs + 8 * ch) & 31);
+        const bool neg_s = __builtin_popcount((unsigned)(jpart & s)) & 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = h2f((uint16_t)(r[e >> 1] >> (16 * (e & 1))));
+          const bool neg = (((sg >> e) & 1u) != 0) != neg_s;
+          u[e] += neg ? -v : v;
+        }
+      }
+      fwht_regs<8>(u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) buf[pad_index(8 * ch + e)] = u[e];
+    }
+  }
+  __syncthreads();
+  fwht_bits(buf, Bs, 3, 31 - __builtin_clz((unsigned)Bs), tid, 256);
+  const int64_t o0 = off + (int64_t)jpart * Bs;
+  const auto ors = make_rsrc(a.signs, a.signs ? (uint32_t)(((a.n + 31) >> 5) * 4) : 0u);
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int ch = tid + 256 * j;
+    if (ch < nch) {
+      const uint32_t sg = a.mode == 1 ? buf_load_u32(ors, (uint32_t)(((c0 + jpart * Bs + 8 * ch) >> 5) * 4)) >>
+                                            ((c0 + jpart * Bs + 8 * ch) & 31)
+                                      : 0u;
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o[e] = buf[pad_index(8 * ch + e)] * a.mult;
+        if ((sg >> e) & 1u) o[e] = -o[e];
+      }
+      const int64_t e0 = o0 + 8 * (int64_t)ch;
+      if (a.out_f32) {
+        float* dst = (float*)a.out + e0;
+        *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+      } else {
+        uint32_t r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = f2h_bits(o[2 * e]) | ((uint32_t)f2h_bits(o[2 * e + 1]) << 16);
+        *reinterpret_cast<uint4*>((uint16_t*)a.out + e0) = make_uint4(r[0], r[1], r[2], r[3]);
+      }
+    }
+  }
+}
+
+template <int S>
+static hipError_t launch_rht_split(const RhtArgs& a, hipStream_t stream) {
+  const int Bs = a.block / S;
+  const size_t lds = (size_t)padded_words(Bs) * 4;
+  const unsigned grid = (unsigned)(a.rows * (a.n / a.block) * S);
+  const int nch = Bs >> 3;
+#define QDEC_SPLIT_J(JJ)                                                                            \
+  {                                                                                                 \
+    static size_t have = 0;                                                                         \
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&rht_split_kernel<S, JJ>), lds, &have); \
+    if (e != hipSuccess) return e;                                                                  \
+    hipLaunchKernelGGL((rht_split_kernel<S, JJ>), dim3(grid), dim3(256), lds, stream, a);           \
+    return hipGetLastError();                                                                       \
+  }
+  if (nch <= 256) QDEC_SPLIT_J(1)
+  if (nch <= 512) QDEC_SPLIT_J(2)
+  QDEC_SPLIT_J(4)
+#undef QDEC_SPLIT_J
+}
+
 template <bool IN_F32, int J>
 static hipError_t launch_rht_j(const RhtArgs& a, hipStream_t stream) {
   static size_t have = 0;
@@ -262,12 +369,28 @@ static hipError_t launch_rht_in(const RhtArgs& a, hipStream_t stream) {
   return launch_rht_j<IN_F32, 8>(a, stream);
 }
 
+// Blocks cut over S workgroups (fp16 input): S grows while there are
+// fewer than 256 workgroups and the pieces keep at least 512 values.
+int rht_split_factor(const RhtArgs& a) {
+  if (a.in_f32 || a.block < 1024) return 1;
+  const int64_t wg = a.rows * (a.n / a.block);
+  int S = 1;
+  while (S < 8 && wg * S < 256 && a.block / (2 * S) >= 512) S *= 2;
+  return S;
+}
+
 static hipError_t launch_rht_impl(const RhtArgs& a, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
   if (a.block < 8) {
     const size_t lds = (size_t)padded_words(a.block) * 4;
     hipLaunchKernelGGL(rht_tiny_kernel, dim3((unsigned)(a.rows * (a.n / a.block))), dim3(256), lds, stream, a);
     return hipGetLastError();
+  }
+  switch (rht_split_factor(a)) {
+    case 2: return launch_rht_split<2>(a, stream);
+    case 4: return launch_rht_split<4>(a, stream);
+    case 8: return launch_rht_split<8>(a, stream);
+    default: break;
   }
   return a.in_f32 ? launch_rht_in<true>(a, stream) : launch_rht_in<false>(a, stream);
 }

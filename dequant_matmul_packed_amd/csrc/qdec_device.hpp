@@ -166,9 +166,16 @@ __device__ __forceinline__ void lane_words_ready(uint32_t* w, int lane) {
 // (Q index bits plus the sign bit 15).
 // Only bits below 16 of h are used, and they depend only on the low 16 bits
 // of s, so the 24-bit multiply-add (full rate) is exact here whatever the
-// bits of s above 16; a 32-bit product would be a quarter-rate instruction.
+// bits of s above 16.  It is written as the instruction itself: from the
+// plain expression the compiler forms a 64-bit multiply-add when it knows
+// the high bits of s are zero, a slower instruction.
+__device__ __forceinline__ uint32_t hyb_hash(uint32_t s) {
+  uint32_t h;
+  asm("v_mad_u32_u24 %0, %1, %1, %1" : "=v"(h) : "v"(s));
+  return h;
+}
 __device__ __forceinline__ uint32_t hyb_signed_index(uint32_t s, int qshift) {
-  return ((__umul24(s, s) + s) & 0xFFFFu) >> qshift;
+  return (hyb_hash(s) & 0xFFFFu) >> qshift;
 }
 
 // 1MAD: LCG output for a state.
