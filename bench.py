@@ -342,7 +342,8 @@ def measured_traffic(spec, us):
 def bench_llama_layer(q, torch, dev, stream, name="llama3_8b_layer"):
     """Llama-3-8B-shaped decoder layer (one fused GEMV per projection: 7, or
     4 with QKV and gate+up fused), microseconds per layer at batch 1 and 8,
-    rotating through distinct layer instances."""
+    rotating through distinct layer instances; the layers launched directly
+    and replayed from HIP graphs, the faster of the two reported."""
     import synth
     wl = synth.WORKLOADS[name]
     layer_bytes = wl.code_bytes
@@ -352,6 +353,7 @@ def bench_llama_layer(q, torch, dev, stream, name="llama3_8b_layer"):
     for b in wl.batches:
         x = {}
         calls = []
+        direct = []
         for s in wl.layers:
             layers, pool, base = make_pool_layers(q, torch, dev, s.code, s.m, s.n, s.k, P,
                                                   "bench/llama/" + s.name)
@@ -361,6 +363,7 @@ def bench_llama_layer(q, torch, dev, stream, name="llama3_8b_layer"):
             ws = q.workspace(base, b, q.QDEC_OP_GEMV, dev)
             y = torch.empty((b, s.m), dtype=torch.float16, device=dev)
             calls.append([LazyLaunch(q, "qdec_gemv", L, x[s.n], y, b, ws) for L in layers])
+            direct.append([Launch(q, "qdec_gemv", L, x[s.n], y, b, ws, stream) for L in layers])
         for c in calls:
             c[0]()
         torch.cuda.synchronize()
@@ -379,13 +382,25 @@ def bench_llama_layer(q, torch, dev, stream, name="llama3_8b_layer"):
         for i in range(reps):
             graphs[i % P].replay()
         torch.cuda.synchronize()
-        us = (time.perf_counter() - t0) / reps * 1e6
+        us_graph = (time.perf_counter() - t0) / reps * 1e6
         del graphs
+        for i in range(P):
+            for c in direct:
+                c[i]()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(reps):
+            for c in direct:
+                c[i % P]()
+        torch.cuda.synchronize()
+        us_direct = (time.perf_counter() - t0) / reps * 1e6
+        us = min(us_graph, us_direct)
         out["%s_b%d" % (name, b)] = {"us_per_layer": round(us, 2),
                                      "packed_GBps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
-                                     "gemv_calls": len(wl.layers)}
-        log("%s b=%d: %.2f us/layer" % (name, b, us))
-        del calls
+                                     "gemv_calls": len(wl.layers),
+                                     "direct_us": round(us_direct, 2), "graph_us": round(us_graph, 2)}
+        log("%s b=%d: %.2f us/layer (direct %.2f, graph %.2f)" % (name, b, us, us_direct, us_graph))
+        del calls, direct
         pools.clear()
         torch.cuda.empty_cache()
     return out
@@ -536,11 +551,19 @@ def bench_gemm(q, torch, dev, stream):
         g.replay()
     e1.record()
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / 32
+    us_graph = e0.elapsed_time(e1) * 1e3 / 32
     del g
+    direct = [Launch(q, "qdec_gemm", L, x, y, b, ws, stream) for L in layers]
+    e0.record()
+    for i in range(32):
+        direct[i % P]()
+    e1.record()
+    torch.cuda.synchronize()
+    us_direct = e0.elapsed_time(e1) * 1e3 / 32
+    us = min(us_graph, us_direct)
     flops = 2.0 * s.m * s.n * b
     tf = flops / (us * 1e-6) / 1e12
-    log("gemm b=64: %.1f us, %.1f TFLOP/s" % (us, tf))
+    log("gemm b=64: %.1f us, %.1f TFLOP/s (direct %.1f us, graph %.1f us)" % (us, tf, us_direct, us_graph))
     del calls, pool
     torch.cuda.empty_cache()
     return {"gemm_b64_up70b": {"us_per_call": round(us, 2), "TFLOPs": round(tf, 1),
