@@ -51,6 +51,9 @@ def parse():
                     help="replay the step's other GEMVs from HIP graphs instead of launching them directly")
     ap.add_argument("--event-every", type=int, default=8,
                     help="bracket the dominant call with HIP events on every N-th timed step")
+    ap.add_argument("--layer", default="",
+                    help="only run 8 direct calls of one layer, CODE:M:N:K:B (e.g. HYB:28672:8192:2:1; "
+                         "B > 8 takes qdec_gemm), for counter collection; prints no JSON line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, copy this many MiB device-to-device 5 times "
                          "(a plain copy of known size to scale HBM counters by)")
@@ -119,6 +122,25 @@ def make_pool_layers(q, torch, dev, code, m, n, k, count, tag, **kw):
     return layers, pool, base
 
 
+def run_one_layer(q, torch, dev, stream, spec):
+    """8 direct calls of one layer (4 distinct code sets), for counters."""
+    import synth
+    name, m, n, k, b = spec.split(":")
+    code = {v: c for c, v in synth.CODE_NAMES.items()}[name]
+    m, n, k, b = int(m), int(n), int(k), int(b)
+    kw = dict(had_in=8192, had_out=4096) if (m, n) == (28672, 8192) and b > 8 else {}
+    layers, pool, base = make_pool_layers(q, torch, dev, code, m, n, k, 4, "bench/layer", **kw)
+    x = torch.from_numpy(synth.activations("bench/layer/x", b, n).view(np.int16)).to(dev)
+    y = torch.empty((b, m), dtype=torch.float16, device=dev)
+    op, fn = (q.QDEC_OP_GEMV, "qdec_gemv") if b <= 8 else (q.QDEC_OP_GEMM, "qdec_gemm")
+    ws = q.workspace(base, b, op, dev)
+    calls = [Launch(q, fn, L, x, y, b, ws, stream) for L in layers]
+    for i in range(8):
+        calls[i % 4]()
+    torch.cuda.synchronize()
+    log("layer %s: 8 calls done" % spec)
+
+
 def time_events(torch, fn, reps):
     """Average device time of fn() over reps launches, one event pair each."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -144,6 +166,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream().cuda_stream
+    if args.layer:
+        run_one_layer(q, torch, dev, stream, args.layer)
+        return
 
     # ---- the headline workload: 4096x4096 computed codes, b = 1 -----------
     wl = synth.WORKLOADS["computed4096"]

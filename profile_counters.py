@@ -1,19 +1,24 @@
 #!/usr/bin/env python3
-"""Summarise two rocprofv3 --pmc runs of the bench (SQ counters, eight per
-run) into profiles/sq_counters_bench.md.
+"""Summarise two rocprofv3 --pmc runs (SQ counters, eight per run) of the
+bench, or of one layer of it, into a markdown table under profiles/.
 
 Usage (from the repository root R, after `cd /tmp && export TMPDIR=/tmp`):
   rocprofv3 --pmc SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU \\
-      SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM SQ_VALU_MFMA_BUSY_CYCLES -d $R/gpurun_out/sq2/p1 -o run -- \\
-      python3 $R/bench.py --eager --steps 20 --warmup 5 --no-cpu-baseline
+      SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM SQ_VALU_MFMA_BUSY_CYCLES -d <dir1> -o run -- python3 $R/bench.py ARGS
   rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS \\
-      SQ_ACTIVE_INST_ANY SQ_INSTS_SALU SQ_LDS_ADDR_CONFLICT -d $R/gpurun_out/sq2/p2 -o run -- (same command)
-  python3 profile_counters.py gpurun_out/sq2/p1/run_results.db gpurun_out/sq2/p2/run_results.db
+      SQ_ACTIVE_INST_ANY SQ_INSTS_SALU SQ_LDS_ADDR_CONFLICT -d <dir2> -o run -- python3 $R/bench.py ARGS
+  python3 profile_counters.py <dir1>/run_results.db <dir2>/run_results.db OUT.md "ARGS" [WEIGHTS]
+
+ARGS is the bench's argument string (it goes into the summary's command
+line): `--steps 20 --warmup 5 --no-cpu-baseline` for the bench, or
+`--layer CODE:M:N:K:B` for one layer.  With WEIGHTS (the layer's m x n) the
+table gives VALU and LDS lane-instructions per weight for the layer's
+decode kernel (the gemv_kernel or gemm_kernel dispatches).  Without it, the
+bench's two known shapes are recognised by their grids (the 4096x4096 b=1
+GEMV and the 28672x8192 b=64 GEMM).
 
 Counters are per dispatch, summed over the chip; instruction counts are per
-wave (64 lanes).  For the two kernels the bench names (the 4096x4096 b=1
-GEMV of the headline, and the 28672x8192 b=64 GEMM) the script also gives
-VALU and LDS wave-instructions per weight.
+wave (64 lanes).
 """
 import os
 import sqlite3
@@ -38,12 +43,17 @@ def load(db):
 
 def main():
     a, b = load(sys.argv[1]), load(sys.argv[2])
+    out = sys.argv[3]
+    bench_args = sys.argv[4]
+    weights = int(sys.argv[5]) if len(sys.argv) > 5 else 0
     keys = [k for k in a if k in b and k[0].startswith("qdec::")]
     keys.sort(key=lambda k: -a[k].get("SQ_WAVE_CYCLES", (0, 0))[0] * a[k].get("SQ_WAVE_CYCLES", (0, 1))[1])
-    lines = ["# SQ counters of the bench's kernels", "",
-             "Commands: two `rocprofv3 --pmc` runs of `python3 $R/bench.py --eager --steps 20 --warmup 5 "
-             "--no-cpu-baseline`, eight SQ counters each (the lists are in `profile_counters.py`), "
-             "summarised by `python3 profile_counters.py <pass 1 db> <pass 2 db>`.", "",
+    title = "the bench's kernels" if not weights else "one layer (`%s`)" % bench_args
+    lines = ["# SQ counters of %s" % title, "",
+             "Commands: two `rocprofv3 --pmc` runs of `python3 $R/bench.py %s`, eight SQ counters each "
+             "(the lists are in `profile_counters.py`), summarised by `python3 profile_counters.py "
+             "<pass 1 db> <pass 2 db> %s \"%s\"%s`." % (bench_args, os.path.relpath(out, ROOT), bench_args,
+                                                       (" %d" % weights) if weights else ""), "",
              "Per dispatch, averaged over dispatches.  wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave time "
              "waiting on a dependency); LDS wait = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES; bank = "
              "SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS (conflict cycles per LDS issue cycle).", "",
@@ -55,9 +65,13 @@ def main():
         g = lambda c: d.get(c, (0.0, 0))[0]
         wc = g("SQ_WAVE_CYCLES") or 1.0
         wts = None
-        for (pre, grid), w in KNOWN.items():
-            if k[0].startswith(pre) and k[1] == grid:
-                wts = w
+        if weights:
+            if k[0].startswith(("qdec::gemv_kernel<", "qdec::gemm_kernel<")):
+                wts = weights
+        else:
+            for (pre, grid), w in KNOWN.items():
+                if k[0].startswith(pre) and k[1] == grid:
+                    wts = w
         vpw = "%.3f" % (g("SQ_INSTS_VALU") * 64 / wts) if wts else ""
         lpw = "%.3f" % (g("SQ_INSTS_LDS") * 64 / wts) if wts else ""
         lines.append("| `%s` | %d | %d | %.0f | %.0f | %.0f | %.2f | %.2f | %.2f | %s | %s |" % (
@@ -65,10 +79,8 @@ def main():
             g("SQ_INSTS_MFMA"), g("SQ_WAIT_INST_ANY") / wc, g("SQ_WAIT_INST_LDS") / wc,
             g("SQ_LDS_BANK_CONFLICT") / (g("SQ_ACTIVE_INST_LDS") or 1.0), vpw, lpw))
     lines += ["", "VALU/weight and LDS/weight are lane-instructions per weight (wave instructions x 64 / "
-              "weights) for the two dispatches whose shape is known from the grid: the b=1 GEMV counts "
-              "the decode and the dot products (v_dot2, one per two weights); the b=64 GEMM counts the "
-              "decode only (the products are MFMA instructions)."]
-    out = os.path.join(ROOT, "profiles", "sq_counters_bench.md")
+              "weights) of the decode kernels: a GEMV counts the decode and the dot products (v_dot2, one "
+              "per two weights); a GEMM counts the decode only (the products are MFMA instructions)."]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
