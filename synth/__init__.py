@@ -20,10 +20,14 @@ import numpy as np
 HYB, MAD1, INST3, NUQ, VQ, LUT = 1, 2, 3, 4, 5, 6
 CODE_NAMES = {HYB: "HYB", MAD1: "1MAD", INST3: "3INST", NUQ: "NUQ", VQ: "VQ", LUT: "LUT"}
 
-# Optimal 8-level quantizer for a unit Gaussian (J. Max, "Quantizing for
-# minimum distortion", IRE Trans. IT-6, 1960, the N = 8 Gaussian row):
-# output levels +/-0.2451, 0.7560, 1.344, 2.152.  Stored as data.
+# Optimal 4-, 8- and 16-level quantizers for a unit Gaussian (J. Max,
+# "Quantizing for minimum distortion", IRE Trans. IT-6, 1960, the Gaussian
+# rows N = 4, 8, 16): the output levels, stored as data.
+LLOYD_MAX_4 = (-1.510, -0.4528, 0.4528, 1.510)
 LLOYD_MAX_8 = (-2.152, -1.344, -0.7560, -0.2451, 0.2451, 0.7560, 1.344, 2.152)
+LLOYD_MAX_16 = (-2.733, -2.069, -1.618, -1.256, -0.9424, -0.6568, -0.3881, -0.1284,
+                0.1284, 0.3881, 0.6568, 0.9424, 1.256, 1.618, 2.069, 2.733)
+LLOYD_MAX = {2: LLOYD_MAX_4, 3: LLOYD_MAX_8, 4: LLOYD_MAX_16}
 
 
 def rng_for(*tags) -> np.random.Generator:
@@ -147,9 +151,9 @@ def make_layer(code: int, m: int, n: int, k: int, *, tag: str, V: Optional[int] 
     elif code == LUT:        # 2^16 fp16 values, two per word
         lut = normal_f16(rng_for(tag, "lut"), 1 << 16).view(np.uint32).copy()
     elif code == NUQ:
-        if k != 3:
-            raise ValueError("the textbook table here is the 8-level one (k = 3)")
-        lv = f16_bits(np.array(LLOYD_MAX_8)).astype(np.uint32)
+        if k not in LLOYD_MAX:
+            raise ValueError("the textbook tables here have 4, 8 and 16 levels (k = 2, 3, 4)")
+        lv = f16_bits(np.array(LLOYD_MAX[k])).astype(np.uint32)
         lut = lv
         grp = group
         gscale = f16_bits(rng_for(tag, "gscale").uniform(0.01, 0.03, size=(m, n // group)))

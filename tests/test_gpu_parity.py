@@ -68,7 +68,7 @@ DECODE_CASES = [
     (synth.HYB, 2), (synth.HYB, 3), (synth.HYB, 4),
     (synth.MAD1, 2), (synth.MAD1, 3), (synth.MAD1, 4),
     (synth.INST3, 2), (synth.INST3, 3), (synth.INST3, 4),
-    (synth.NUQ, 3), (synth.VQ, 2), (synth.VQ, 3), (synth.VQ, 4),
+    (synth.NUQ, 2), (synth.NUQ, 3), (synth.NUQ, 4), (synth.VQ, 2), (synth.VQ, 3), (synth.VQ, 4),
 ]
 
 
@@ -154,7 +154,8 @@ GEMV_SHAPES = [(256, 96), (384, 592), (1024, 1024), (128, 16), (640, 2048)]
 
 @pytest.mark.parametrize("code,k", [(synth.HYB, 2), (synth.HYB, 3), (synth.MAD1, 2), (synth.MAD1, 4),
                                     (synth.INST3, 3), (synth.NUQ, 3), (synth.VQ, 4), (synth.HYB, 4),
-                                    (synth.INST3, 2), (synth.MAD1, 3)])
+                                    (synth.INST3, 2), (synth.MAD1, 3), (synth.NUQ, 2), (synth.NUQ, 4),
+                                    (synth.VQ, 2), (synth.VQ, 3)])
 @pytest.mark.parametrize("b", [1, 3, 8])
 def test_gemv_small_matches_oracle(q, dev, code, k, b):
     import torch
@@ -362,7 +363,9 @@ def test_gemv_wide_chunks_sampled(q, dev, n, b, k):
 @pytest.mark.parametrize("code,k,m,n,b", [
     (synth.HYB, 3, 256, 512, 64), (synth.HYB, 2, 384, 592, 5), (synth.HYB, 3, 128, 80, 70),
     (synth.MAD1, 2, 256, 256, 64), (synth.INST3, 4, 256, 256, 33), (synth.NUQ, 3, 256, 512, 64),
-    (synth.VQ, 4, 256, 256, 64), (synth.HYB, 4, 1024, 1024, 64)])
+    (synth.VQ, 4, 256, 256, 64), (synth.HYB, 4, 1024, 1024, 64), (synth.NUQ, 2, 256, 512, 64),
+    (synth.NUQ, 4, 384, 256, 40), (synth.VQ, 2, 256, 256, 64), (synth.VQ, 3, 128, 160, 64),
+    (synth.MAD1, 4, 256, 256, 64), (synth.INST3, 2, 256, 512, 64)])
 def test_gemm_small_matches_oracle(q, dev, code, k, m, n, b):
     import torch
     _say("gemm small", synth.CODE_NAMES[code], k, m, n, b)

@@ -430,6 +430,11 @@ def test_lloyd_max_textbook():
     assert np.allclose(lv, synth.LLOYD_MAX_8, atol=6e-4)
     assert abs(mse - 0.03454) < 5e-5
     assert np.array_equal(synth.f16_bits(lv), synth.f16_bits(np.array(synth.LLOYD_MAX_8)))
+    # the 4- and 16-level rows of the same table (MSE 0.1175 and 0.0095)
+    lv4, mse4 = oracle.lloyd_max_gauss(4, 3000)
+    assert np.allclose(lv4, synth.LLOYD_MAX_4, atol=6e-4) and abs(mse4 - 0.1175) < 1e-4
+    lv16, mse16 = oracle.lloyd_max_gauss(16, 20000)
+    assert np.allclose(lv16, synth.LLOYD_MAX_16, atol=6e-4) and abs(mse16 - 0.0095) < 1e-5
     lv2, mse2 = oracle.lloyd_max_gauss(2, 200)
     # two levels: +/- sqrt(2/pi), MSE 1 - 2/pi
     assert np.allclose(lv2, [-np.sqrt(2 / np.pi), np.sqrt(2 / np.pi)], atol=1e-12)
