@@ -14,7 +14,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libqdec.so")
 
 SOURCES = ["api.hip", "k_decode_rht.hip", "k_gemm.hip", "k_gemv_hyb.hip", "k_gemv_mad1.hip",
-           "k_gemv_inst3.hip", "k_gemv_nuq.hip", "k_gemv_vq.hip", "k_gemv_hyb1.hip", "k_gemv_lut.hip", "k_encode.hip"]
+           "k_gemv_inst3.hip", "k_gemv_nuq.hip", "k_gemv_vq.hip", "k_gemv_hyb1.hip", "k_gemv_lut.hip", "k_encode.hip", "k_gemv_hyb_half.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -346,8 +346,21 @@ int qdec_gemv(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
     if (e != hipSuccess) return status_of(e);
     a.xr = xr;
   }
-  // the decode-and-multiply kernel per row part (each adds into z), then the
-  // output side over the whole layer
+  // the decode-and-multiply kernel per row part (each adds into z), or both
+  // parts of a half-TCQ layer in one launch where that pair is built, then
+  // the output side over the whole layer
+  if (parts.count == 2 && !a.xr && L.code == HYB) {
+    GemvArgs ah = a;
+    ah.L = parts.part[0];
+    ah.row0 = parts.row0[0];
+    ah.codes_b = parts.part[1].codes;
+    ah.m_b = parts.part[1].m;
+    ah.row0_b = parts.row0[1];
+    ah.grid_a = (int)((parts.part[0].m / 128) * a.nchunks);
+    const hipError_t e = launch_gemv_hyb_two_parts(ah, parts.part[1].kv, (hipStream_t)stream);
+    if (e == hipSuccess) return status_of(launch_gemv_finish(a, (hipStream_t)stream));
+    if (e != hipErrorNotSupported) return status_of(e);
+  }
   for (int p = 0; p < parts.count; ++p) {
     GemvArgs ap = a;
     ap.L = parts.part[p];

@@ -29,6 +29,8 @@
 // read from HBM exactly once and every other operand stays on chip.
 #pragma once
 
+#include <type_traits>
+
 #include "qdec_device.hpp"
 #include "qdec_internal.hpp"
 
@@ -88,21 +90,29 @@ __host__ __device__ inline size_t gemv_lds_bytes(int Q, int Kc, int U) {
          (CODE == INST3 ? (size_t)NB * Kc * 4 : 0) + gemv_wred_bytes<NB>(Kc);
 }
 
-template <int CODE, int KV, int NB, int PF, bool SL, bool XR>
+// KVB > 0: a half-TCQ layer in one launch.  Workgroups [0, grid_a) take the
+// first row part (width KV, codes a.L.codes, a.L.m rows), the others the
+// second (width KVB, a.codes_b, a.m_b rows starting at row a.row0_b); the
+// part is uniform per workgroup, and the tile loop is built for each width.
+template <int CODE, int KV, int NB, int PF, bool SL, bool XR, int KVB = 0>
 __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   using G = LaneGeom<CODE, KV>;
+  using GB = LaneGeom<CODE, KVB ? KVB : KV>;
   constexpr int V = G::V;
   constexpr int L = G::L;
-  constexpr int NW = G::NW;
+  constexpr int NW = G::NW > GB::NW ? G::NW : GB::NW;   // ring words per slot
   constexpr int COPIES = GemvTable<CODE>::COPIES;
   extern __shared__ __align__(16) uint32_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar math
-  const int64_t m = a.L.m, n = a.L.n;
+  const bool second = KVB != 0 && (int)blockIdx.x >= a.grid_a;
+  const int bid = second ? (int)blockIdx.x - a.grid_a : (int)blockIdx.x;
+  const int64_t m = second ? a.m_b : a.L.m, n = a.L.n;
+  const int64_t row0 = second ? a.row0_b : a.row0;
   const int npanels = (int)(m / 128);
-  const int panel = blockIdx.x % npanels;
-  const int chunk = blockIdx.x / npanels;
+  const int panel = bid % npanels;
+  const int chunk = bid / npanels;
   const int Kc = a.Kc;
   const int64_t c0 = (int64_t)chunk * Kc;
   const int kcols = (int)((n - c0) < Kc ? (n - c0) : Kc);   // multiple of 16
@@ -173,11 +183,15 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   // TILE_WORDS words); the wave's tile columns tc_begin .. tc_begin+tc_count-1
   // stream through a PF-deep ring of registers, the first PF requested here.
   // Lane q of tile row tl loads NW words from word lane_word(q) of its tile.
-  constexpr uint32_t TCB = 8u * 4u * G::TILE_WORDS;   // bytes per tile column
+  // (with two parts the ring slots take the wider part's word count; the
+  // narrower one's extra words are unused, or read zero past the buffer)
+  const uint32_t TWS = second ? (uint32_t)GB::TILE_WORDS : (uint32_t)G::TILE_WORDS;
+  const uint32_t TCB = 8u * 4u * TWS;                 // bytes per tile column
   const int64_t tiles_row = n >> 4;
-  const uint32_t* pchunk = a.L.codes + ((int64_t)panel * tiles_row + (c0 >> 4)) * (8 * G::TILE_WORDS);
+  const uint32_t* pchunk = (second ? a.codes_b : a.L.codes) + ((int64_t)panel * tiles_row + (c0 >> 4)) * (8 * TWS);
   const auto crs = make_rsrc(pchunk, (uint32_t)ntc * TCB);
-  const uint32_t lane_off = (uint32_t)(lane >> 3) * (4u * G::TILE_WORDS) + 4u * G::lane_word(lane & 7);
+  const uint32_t lane_off = (uint32_t)(lane >> 3) * (4u * TWS) +
+                            4u * (second ? GB::lane_word(lane & 7) : G::lane_word(lane & 7));
   auto code_off = [&](int j) -> uint32_t {
     return j < tc_count ? (uint32_t)(tc_begin + j) * TCB + lane_off : BUF_OFF;
   };
@@ -186,7 +200,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   for (int j = 0; j < PF; ++j) buf_load_words<NW>(crs, code_off(j), buf[j]);
   // NUQ: the fp16 group scales of the lane's two rows ride in the same ring
   const int64_t gstride = CODE == NUQ ? n / a.L.group : 0;
-  const int64_t grow0 = a.row0 + (int64_t)panel * 128 + (lane >> 3) * 16 + 2 * (lane & 7);
+  const int64_t grow0 = row0 + (int64_t)panel * 128 + (lane >> 3) * 16 + 2 * (lane & 7);
   const auto grs = make_rsrc(a.L.gscale, CODE == NUQ ? (uint32_t)(a.mz * gstride * 2) : 0u);
   uint32_t gsr[PF][2];
   auto gs_load = [&](int j, uint32_t* g) {
@@ -434,112 +448,122 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int c = 0; c < NB; ++c) acc[r][c] = 0.f;
 
-  for (int j0 = 0; j0 < tc_count; j0 += PF) {
+  auto stream_tiles = [&](auto kx) {
+    constexpr int KX = decltype(kx)::value;
+    constexpr int NWX = LaneGeom<CODE, KX>::NW;
+    for (int j0 = 0; j0 < tc_count; j0 += PF) {
 #pragma unroll
-  for (int jj = 0; jj < PF; ++jj) {
-    const int j = j0 + jj;
-    uint32_t w[NW + 1];
+    for (int jj = 0; jj < PF; ++jj) {
+      const int j = j0 + jj;
+      uint32_t w[NWX + 1];
 #pragma unroll
-    for (int i = 0; i < NW; ++i) w[i] = buf[jj][i];
-    const uint32_t g0 = gsr[jj][0], g1 = gsr[jj][1];
-    (void)g0; (void)g1;
-    // refill this ring slot with the tile column PF ahead (unconditionally:
-    // past the wave's last column the load is switched off by its offset)
-    buf_load_words<NW>(crs, code_off(j + PF), buf[jj]);
-    gs_load(j + PF, gsr[jj]);
-    if (j < tc_count) {
-      const int tcl = tc_begin + j;   // tile column within the chunk
-      lane_words_ready<CODE, KV>(w, lane);
-      if constexpr (CODE == INST3) {
+      for (int i = 0; i < NWX; ++i) w[i] = buf[jj][i];
+      const uint32_t g0 = gsr[jj][0], g1 = gsr[jj][1];
+      (void)g0; (void)g1;
+      // refill this ring slot with the tile column PF ahead (unconditionally:
+      // past the wave's last column the load is switched off by its offset)
+      buf_load_words<NW>(crs, code_off(j + PF), buf[jj]);
+      gs_load(j + PF, gsr[jj]);
+      if (j < tc_count) {
+        const int tcl = tc_begin + j;   // tile column within the chunk
+        lane_words_ready<CODE, KX>(w, lane);
+        if constexpr (CODE == INST3) {
 #pragma unroll
-        for (int t = 0; t < 32; ++t) {
-          const uint32_t s = window_at<L>(w, t * KV);
-          const half2v val = as_h2(inst3_bits(s));
-#pragma unroll
-          for (int c = 0; c < NB; ++c)
-            acc[t >> 4][c] = __builtin_amdgcn_fdot2(val, as_h2(xd[c * Kc + tcl * 16 + (t & 15)]),
-                                                    acc[t >> 4][c], false);
-        }
-      } else {
-        uint32_t xp[NB][8];
-#pragma unroll
-        for (int c = 0; c < NB; ++c) {
-          const uint4* px = reinterpret_cast<const uint4*>(xh + c * (Kc / 2) + tcl * 8);
-          const uint4 p0 = px[0], p1 = px[1];
-          xp[c][0] = p0.x; xp[c][1] = p0.y; xp[c][2] = p0.z; xp[c][3] = p0.w;
-          xp[c][4] = p1.x; xp[c][5] = p1.y; xp[c][6] = p1.z; xp[c][7] = p1.w;
-        }
-        if constexpr (V == 2) {
-#pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            const uint32_t s = window_at<L>(w, t * KV);
-            uint32_t pair;
-            if constexpr (CODE == HYB) pair = tabc[hyb_signed_index(s, qshift) * COPIES];
-            else pair = tabc[s * COPIES];
+          for (int t = 0; t < 32; ++t) {
+            const uint32_t s = window_at<L>(w, t * KX);
+            const half2v val = as_h2(inst3_bits(s));
 #pragma unroll
             for (int c = 0; c < NB; ++c)
-              acc[t >> 3][c] = __builtin_amdgcn_fdot2(as_h2(pair), as_h2(xp[c][t & 7]),
-                                                      acc[t >> 3][c], false);
+              acc[t >> 4][c] = __builtin_amdgcn_fdot2(val, as_h2(xd[c * Kc + tcl * 16 + (t & 15)]),
+                                                      acc[t >> 4][c], false);
           }
-        } else if constexpr (CODE == MAD1) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const uint32_t s0 = window_at<L>(w, (2 * i) * KV);
-            const uint32_t s1 = window_at<L>(w, (2 * i + 1) * KV);
-            const uint32_t v0 = __builtin_amdgcn_sad_u8(mad1_lcg(s0), 0u, 0x6400u);
-            const uint32_t v1 = __builtin_amdgcn_sad_u8(mad1_lcg(s1), 0u, 0x6400u);
-            const uint32_t pv = v0 | (v1 << 16);
-#pragma unroll
-            for (int c = 0; c < NB; ++c)
-              acc[i >> 3][c] = __builtin_amdgcn_fdot2(as_h2(pv), as_h2(xp[c][i & 7]),
-                                                      acc[i >> 3][c], false);
-          }
-        } else if constexpr (CODE == HYB1 || CODE == LUT) {
-          // one table value per state (V = 1): two states per fp16 pair
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const uint32_t s0 = window_at<L>(w, (2 * i) * KV);
-            const uint32_t s1 = window_at<L>(w, (2 * i + 1) * KV);
-            uint32_t pv;
-            if constexpr (CODE == HYB1) {
-              pv = (tabc[hyb_signed_index(s0, qshift) * COPIES] & 0xFFFFu) |
-                   (tabc[hyb_signed_index(s1, qshift) * COPIES] << 16);
-            } else {
-              const uint16_t* t16 = reinterpret_cast<const uint16_t*>(regA);
-              pv = (uint32_t)t16[s0] | ((uint32_t)t16[s1] << 16);
-            }
-#pragma unroll
-            for (int c = 0; c < NB; ++c)
-              acc[i >> 3][c] = __builtin_amdgcn_fdot2(as_h2(pv), as_h2(xp[c][i & 7]),
-                                                      acc[i >> 3][c], false);
-          }
-        } else {  // NUQ
-          const float gs0 = h2f((uint16_t)g0);
-          const float gs1 = h2f((uint16_t)g1);
-          float part[2][NB];
-#pragma unroll
-          for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int c = 0; c < NB; ++c) part[r][c] = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const uint32_t s0 = window_at<L>(w, (2 * i) * KV);
-            const uint32_t s1 = window_at<L>(w, (2 * i + 1) * KV);
-            const uint32_t pv = (regA[s0] & 0xFFFFu) | (regA[s1] << 16);
-#pragma unroll
-            for (int c = 0; c < NB; ++c)
-              part[i >> 3][c] = __builtin_amdgcn_fdot2(as_h2(pv), as_h2(xp[c][i & 7]),
-                                                       part[i >> 3][c], false);
-          }
+        } else {
+          uint32_t xp[NB][8];
 #pragma unroll
           for (int c = 0; c < NB; ++c) {
-            acc[0][c] += gs0 * part[0][c];
-            acc[1][c] += gs1 * part[1][c];
+            const uint4* px = reinterpret_cast<const uint4*>(xh + c * (Kc / 2) + tcl * 8);
+            const uint4 p0 = px[0], p1 = px[1];
+            xp[c][0] = p0.x; xp[c][1] = p0.y; xp[c][2] = p0.z; xp[c][3] = p0.w;
+            xp[c][4] = p1.x; xp[c][5] = p1.y; xp[c][6] = p1.z; xp[c][7] = p1.w;
+          }
+          if constexpr (V == 2) {
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+              const uint32_t s = window_at<L>(w, t * KX);
+              uint32_t pair;
+              if constexpr (CODE == HYB) pair = tabc[hyb_signed_index(s, qshift) * COPIES];
+              else pair = tabc[s * COPIES];
+#pragma unroll
+              for (int c = 0; c < NB; ++c)
+                acc[t >> 3][c] = __builtin_amdgcn_fdot2(as_h2(pair), as_h2(xp[c][t & 7]),
+                                                        acc[t >> 3][c], false);
+            }
+          } else if constexpr (CODE == MAD1) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const uint32_t s0 = window_at<L>(w, (2 * i) * KX);
+              const uint32_t s1 = window_at<L>(w, (2 * i + 1) * KX);
+              const uint32_t v0 = __builtin_amdgcn_sad_u8(mad1_lcg(s0), 0u, 0x6400u);
+              const uint32_t v1 = __builtin_amdgcn_sad_u8(mad1_lcg(s1), 0u, 0x6400u);
+              const uint32_t pv = v0 | (v1 << 16);
+#pragma unroll
+              for (int c = 0; c < NB; ++c)
+                acc[i >> 3][c] = __builtin_amdgcn_fdot2(as_h2(pv), as_h2(xp[c][i & 7]),
+                                                        acc[i >> 3][c], false);
+            }
+          } else if constexpr (CODE == HYB1 || CODE == LUT) {
+            // one table value per state (V = 1): two states per fp16 pair
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const uint32_t s0 = window_at<L>(w, (2 * i) * KX);
+              const uint32_t s1 = window_at<L>(w, (2 * i + 1) * KX);
+              uint32_t pv;
+              if constexpr (CODE == HYB1) {
+                pv = (tabc[hyb_signed_index(s0, qshift) * COPIES] & 0xFFFFu) |
+                     (tabc[hyb_signed_index(s1, qshift) * COPIES] << 16);
+              } else {
+                const uint16_t* t16 = reinterpret_cast<const uint16_t*>(regA);
+                pv = (uint32_t)t16[s0] | ((uint32_t)t16[s1] << 16);
+              }
+#pragma unroll
+              for (int c = 0; c < NB; ++c)
+                acc[i >> 3][c] = __builtin_amdgcn_fdot2(as_h2(pv), as_h2(xp[c][i & 7]),
+                                                        acc[i >> 3][c], false);
+            }
+          } else {  // NUQ
+            const float gs0 = h2f((uint16_t)g0);
+            const float gs1 = h2f((uint16_t)g1);
+            float part[2][NB];
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+              for (int c = 0; c < NB; ++c) part[r][c] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const uint32_t s0 = window_at<L>(w, (2 * i) * KX);
+              const uint32_t s1 = window_at<L>(w, (2 * i + 1) * KX);
+              const uint32_t pv = (regA[s0] & 0xFFFFu) | (regA[s1] << 16);
+#pragma unroll
+              for (int c = 0; c < NB; ++c)
+                part[i >> 3][c] = __builtin_amdgcn_fdot2(as_h2(pv), as_h2(xp[c][i & 7]),
+                                                         part[i >> 3][c], false);
+            }
+#pragma unroll
+            for (int c = 0; c < NB; ++c) {
+              acc[0][c] += gs0 * part[0][c];
+              acc[1][c] += gs1 * part[1][c];
+            }
           }
         }
       }
     }
-  }
+    }
+  };
+  if constexpr (KVB == 0) {
+    stream_tiles(std::integral_constant<int, KV>{});
+  } else {
+    if (second) stream_tiles(std::integral_constant<int, KVB>{});
+    else stream_tiles(std::integral_constant<int, KV>{});
   }
 
   // ---- 5. reduce the waves, add into the fp32 accumulator -----------------
@@ -583,35 +607,52 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
         v0 = hi ? o0 - v0 : v0 + o0;
         v1 = hi ? o1 - v1 : v1 + o1;
       }
-      float* zr = a.z + (int64_t)c * a.mz + a.row0 + (int64_t)panel * 128 + 2 * lane;
+      float* zr = a.z + (int64_t)c * a.mz + row0 + (int64_t)panel * 128 + 2 * lane;
       __hip_atomic_fetch_add(zr, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_fetch_add(zr + 1, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
 
-template <int CODE, int KV, int NB, int PF, bool SL, bool XR>
+template <int CODE, int KV, int NB, int PF, bool SL, bool XR, int KVB = 0>
 hipError_t launch_gemv_v(const GemvArgs& a, hipStream_t stream) {
   const size_t lds = gemv_lds_bytes<CODE, KV, NB>(a.L.Q, a.Kc, a.U);
   static size_t have = 0;
   const hipError_t e =
-      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<CODE, KV, NB, PF, SL, XR>), lds, &have);
+      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<CODE, KV, NB, PF, SL, XR, KVB>), lds, &have);
   if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)((a.L.m / 128) * a.nchunks);
-  hipLaunchKernelGGL((gemv_kernel<CODE, KV, NB, PF, SL, XR>), dim3(grid), dim3(GEMV_THREADS), lds, stream, a);
+  const unsigned grid = (unsigned)((a.L.m / 128 + (KVB ? a.m_b / 128 : 0)) * a.nchunks);
+  hipLaunchKernelGGL((gemv_kernel<CODE, KV, NB, PF, SL, XR, KVB>), dim3(grid), dim3(GEMV_THREADS), lds, stream, a);
   return hipGetLastError();
 }
 
 // XR: x' comes precomputed (args.xr, always with more than one batch
 // column; with one column for layers whose chunk transforms would cost
 // more than the separate transform's launch).
-template <int CODE, int KV, int NB, bool XR>
+template <int CODE, int KV, int NB, bool XR, int KVB = 0>
 hipError_t launch_gemv_x(const GemvArgs& a, hipStream_t stream) {
   const bool sl = (XR || a.L.had_in <= 4096) && ((CODE != HYB && CODE != HYB1) || a.L.Q <= 9);
-  if (a.Kc <= 128 && sl) return launch_gemv_v<CODE, KV, NB, 2, true, XR>(a, stream);
-  if (a.Kc <= 256 && sl) return launch_gemv_v<CODE, KV, NB, 4, true, XR>(a, stream);
-  if (sl) return launch_gemv_v<CODE, KV, NB, 8, true, XR>(a, stream);
-  return launch_gemv_v<CODE, KV, NB, 8, false, XR>(a, stream);
+  if (a.Kc <= 128 && sl) return launch_gemv_v<CODE, KV, NB, 2, true, XR, KVB>(a, stream);
+  if (a.Kc <= 256 && sl) return launch_gemv_v<CODE, KV, NB, 4, true, XR, KVB>(a, stream);
+  if (sl) return launch_gemv_v<CODE, KV, NB, 8, true, XR, KVB>(a, stream);
+  return launch_gemv_v<CODE, KV, NB, 8, false, XR, KVB>(a, stream);
+}
+
+// A two-part (half-TCQ) layer at one batch column with its x transform in
+// the workgroups, in one launch: the width pairs one half-bit apart of HYB
+// at V = 2.  Returns hipErrorNotSupported for the pairs not built here.
+template <int CODE>
+hipError_t launch_gemv_two_parts(const GemvArgs& a, int kvb, hipStream_t stream) {
+  if constexpr (CODE == HYB) {
+    const int kv = a.L.kv;
+#define QDEC_GEMV_PAIR(A, B) \
+    if (kv == A && kvb == B) return launch_gemv_x<CODE, A, 1, false, B>(a, stream);
+    QDEC_GEMV_PAIR(4, 5) QDEC_GEMV_PAIR(5, 4) QDEC_GEMV_PAIR(5, 6) QDEC_GEMV_PAIR(6, 5)
+    QDEC_GEMV_PAIR(6, 7) QDEC_GEMV_PAIR(7, 6) QDEC_GEMV_PAIR(7, 8) QDEC_GEMV_PAIR(8, 7)
+#undef QDEC_GEMV_PAIR
+  }
+  (void)a; (void)kvb; (void)stream;
+  return hipErrorNotSupported;
 }
 
 template <int CODE, int KV, int NB>

@@ -41,6 +41,10 @@ struct GemvArgs {
   float* z;            // [b][mz] fp32 split-K accumulator (workspace; zero on entry, left zero)
   int64_t row0;        // first row of L (a part of the layer) in the layer
   int64_t mz;          // rows of the whole layer (z's row stride)
+  // one launch over both parts of a half-TCQ layer: the second part
+  const uint32_t* codes_b = nullptr;
+  int64_t m_b = 0, row0_b = 0;
+  int grid_a = 0;      // workgroups of the first part
   int Kc;              // columns per chunk (power of two, 64 .. 2048; Kc * b <= 4096)
   int nchunks;         // ceil(n / Kc)
   int U;               // rows per output block = max(had_out, 128)
@@ -128,6 +132,9 @@ inline hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes, size_t* h
 // launch_gemv_finish: the output side over the whole layer.
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 hipError_t launch_gemv_finish(const GemvArgs& a, hipStream_t stream);
+// both parts of a half-TCQ layer in one launch (b = 1, transform in the
+// workgroups); hipErrorNotSupported when that width pair is not built
+hipError_t launch_gemv_hyb_two_parts(const GemvArgs& a, int kvb, hipStream_t stream);
 hipError_t launch_decode_tile(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_rht(const RhtArgs& a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
