@@ -489,10 +489,9 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
           if constexpr (V == 2) {
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
-              const uint32_t s = window_at<L>(w, t * KX);
               uint32_t pair;
-              if constexpr (CODE == HYB) pair = tabc[hyb_signed_index(s, qshift) * COPIES];
-              else pair = tabc[s * COPIES];
+              if constexpr (CODE == HYB) pair = tabc[hyb_signed_index(window_raw<L>(w, t * KX), qshift) * COPIES];
+              else pair = tabc[window_at<L>(w, t * KX) * COPIES];
 #pragma unroll
               for (int c = 0; c < NB; ++c)
                 acc[t >> 3][c] = __builtin_amdgcn_fdot2(as_h2(pair), as_h2(xp[c][t & 7]),
@@ -515,8 +514,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
             // one table value per state (V = 1): two states per fp16 pair
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const uint32_t s0 = window_at<L>(w, (2 * i) * KX);
-              const uint32_t s1 = window_at<L>(w, (2 * i + 1) * KX);
+              const uint32_t s0 = CODE == HYB1 ? window_raw<L>(w, (2 * i) * KX) : window_at<L>(w, (2 * i) * KX);
+              const uint32_t s1 = CODE == HYB1 ? window_raw<L>(w, (2 * i + 1) * KX) : window_at<L>(w, (2 * i + 1) * KX);
               uint32_t pv;
               if constexpr (CODE == HYB1) {
                 pv = (tabc[hyb_signed_index(s0, qshift) * COPIES] & 0xFFFFu) |

@@ -95,6 +95,16 @@ __device__ __forceinline__ uint32_t window_at(const uint32_t* w, int o) {
   return __builtin_amdgcn_alignbit(w[i], w[i + 1], 64 - r - L) & mask;
 }
 
+// The same window with the stream bits that precede it left above bit L
+// (not masked off): for the HYB hash, whose 16 used bits depend only on the
+// window's low 16 bits (see hyb_hash).
+template <int L>
+__device__ __forceinline__ uint32_t window_raw(const uint32_t* w, int o) {
+  const int i = o >> 5, r = o & 31;
+  if (r + L <= 32) return w[i] >> (32 - r - L);
+  return __builtin_amdgcn_alignbit(w[i], w[i + 1], 64 - r - L);
+}
+
 // ---------------------------------------------------------------------------
 // Raw buffer loads.  A buffer resource covers `bytes` bytes from a
 // wave-uniform base; a load whose byte offset lies at or beyond that size
@@ -181,8 +191,12 @@ __device__ __forceinline__ uint32_t hyb_signed_index(uint32_t s, int qshift) {
 // 1MAD: LCG output for a state.
 __device__ __forceinline__ uint32_t mad1_lcg(uint32_t s) { return s * MAD1_A + MAD1_C; }
 // 3INST: LCG, then force the high exponent bits of both halves.
+// The pattern is held in a register so that the mask-and-insert is one
+// v_and_or_b32 (an instruction here takes at most one literal constant).
 __device__ __forceinline__ uint32_t inst3_bits(uint32_t s) {
-  return ((s * INST3_A + INST3_C) & INST3_MASK) | INST3_PATTERN;
+  uint32_t pat = INST3_PATTERN;
+  asm("" : "+v"(pat));
+  return ((s * INST3_A + INST3_C) & INST3_MASK) | pat;
 }
 
 // Exact fp16 value of 1MAD: fp16(fp32((sigma - 510) * fp32(1/sqrt(21845)))).
@@ -244,9 +258,8 @@ __device__ __forceinline__ void lane_decode_exact(const uint32_t* w, const uint3
   if constexpr (V == 2) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const uint32_t s = window_at<L>(w, t * KV);
-      if constexpr (CODE == HYB) out[t] = tabc[hyb_signed_index(s, qshift) * COPIES];
-      else out[t] = tabc[s * COPIES];
+      if constexpr (CODE == HYB) out[t] = tabc[hyb_signed_index(window_raw<L>(w, t * KV), qshift) * COPIES];
+      else out[t] = tabc[window_at<L>(w, t * KV) * COPIES];
     }
   } else {
 #pragma unroll
