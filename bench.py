@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 POOL_MIB = 1152
+POOL_BYTES = 1 << 30
 METRIC = "fused dequant-GEMV HBM GB/s + µs/layer (b=1); GEMM TFLOP/s (b=64)"
 
 
@@ -298,8 +299,9 @@ def main():
         detail.update(bench_llama_layer(q, torch, dev, stream))
         detail.update(bench_llama_layer(q, torch, dev, stream, "llama3_8b_layer_fused"))
         detail.update(bench_gemm(q, torch, dev, stream))
-        detail.update(bench_code_variants(q, torch, dev))
-        detail.update(bench_fractional(q, torch, dev))
+        detail.update(bench_configs(q, torch, dev, stream))
+        detail.update(bench_code_variants(q, torch, dev, stream))
+        detail.update(bench_fractional(q, torch, dev, stream))
         detail.update(bench_encoder(q, torch, dev, cpu=not args.no_cpu_baseline))
 
     if not args.no_detail and not args.only:
@@ -309,9 +311,14 @@ def main():
         if g:
             g["frac_of_measured_fp16_matmul"] = round(g["TFLOPs"] / ceil["fp16_matmul_8192_TFLOPs"], 4)
         detail["headline_frac_of_measured_copy"] = round(dom_gbs / ceil["copy_GBps_read_plus_write"], 4)
+        detail["headline_frac_of_measured_read"] = round(dom_gbs / ceil["read_GBps_colsum_1GiB"], 4)
+        for v in detail["configs_b1"].values():
+            v["frac_of_measured_read"] = round(v["algorithmic_GBps"] / ceil["read_GBps_colsum_1GiB"], 4)
     cpu = None
     if not args.no_cpu_baseline:
         cpu, cpu_detail = cpu_baseline(specs, x16)
+        if not args.no_detail and not args.only:
+            cpu_detail["per_config"] = cpu_per_config()
         detail["cpu_oracle"] = cpu_detail
 
     line = {
@@ -431,55 +438,96 @@ def bench_llama_layer(q, torch, dev, stream, name="llama3_8b_layer"):
     return out
 
 
-def time_4096_variants(q, torch, dev, variants, tagbase):
-    """Graph-replayed time per call of 4096x4096 layers (16 distinct code
-    sets in rotation) at b=1 (qdec_gemv) and b=64 (qdec_gemm) for each
-    (name, code, k, make_layer keywords) variant."""
+def time_layer(q, torch, dev, stream, code, m, n, k, b, tag, **kw):
+    """Device microseconds per call of one layer shape at batch b (qdec_gemv
+    up to 8, qdec_gemm above): distinct random code sets in rotation from a
+    pool of at least 1 GiB, four times the 256 MiB Infinity Cache, so no call
+    finds its codes there; 20 warm-up calls, then 5 repeats of 200
+    back-to-back direct launches, each bracketed by one event pair on the
+    launch stream; the median repeat.  Returns (us, the layer's descriptor)."""
     import synth
+    words = synth.code_words(code, m, n, k, kw.get("V"), kw.get("kv", 0), kw.get("kv_b", 0),
+                             kw.get("m_a", 0))
+    P = int(min(512, max(4, -(-POOL_BYTES // (4 * words)))))
+    layers, pool, base = make_pool_layers(q, torch, dev, code, m, n, k, P, tag, **kw)
+    x = torch.from_numpy(synth.activations(tag + "/x", b, n).view(np.int16)).to(dev)
+    y = torch.empty((b, m), dtype=torch.float16, device=dev)
+    op, fn = (q.QDEC_OP_GEMV, "qdec_gemv") if b <= 8 else (q.QDEC_OP_GEMM, "qdec_gemm")
+    ws = q.workspace(base, b, op, dev)
+    calls = [Launch(q, fn, L, x, y, b, ws, stream) for L in layers]
+    for i in range(20):
+        calls[i % P]()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    reps = []
+    j = 0
+    for r in range(5):
+        e0.record()
+        for i in range(200):
+            calls[j % P]()
+            j += 1
+        e1.record()
+        torch.cuda.synchronize()
+        reps.append(e0.elapsed_time(e1) * 1e3 / 200)
+    if not torch.isfinite(y.float()).all():
+        raise RuntimeError("non-finite output in %s" % tag)
+    del calls, layers, pool, ws, x, y
+    torch.cuda.empty_cache()
+    return float(np.median(reps)), base
+
+
+def tensor_bytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def time_4096_variants(q, torch, dev, stream, variants, tagbase):
+    """Time per call of 4096x4096 layers at b=1 (qdec_gemv) and b=64
+    (qdec_gemm) for each (name, code, k, make_layer keywords) variant."""
     out = {}
     for name, code, k, kw in variants:
-        layers, pool, base = make_pool_layers(q, torch, dev, code, 4096, 4096, k, 16, tagbase + name, **kw)
-        nbytes = base.code_bytes
         res = {}
         for b in (1, 64):
-            x = torch.from_numpy(synth.activations(tagbase + "x", b, 4096).view(np.int16)).to(dev)
-            y = torch.empty((b, 4096), dtype=torch.float16, device=dev)
-            op = q.QDEC_OP_GEMV if b == 1 else q.QDEC_OP_GEMM
-            ws = q.workspace(base, b, op, dev)
-            fn = "qdec_gemv" if b == 1 else "qdec_gemm"
-            calls = [LazyLaunch(q, fn, L, x, y, b, ws) for L in layers]
-            calls[0]()
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(16):
-                    calls[i]()
-            g.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for r in range(5):
-                g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / 80
+            us, base = time_layer(q, torch, dev, stream, code, 4096, 4096, k, b, tagbase + name, **kw)
             res["b%d_us" % b] = round(us, 2)
             if b == 1:
-                res["b1_packed_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+                res["b1_packed_GBps"] = round(base.code_bytes / (us * 1e-6) / 1e9, 1)
             else:
                 res["b64_TFLOPs"] = round(2 * 4096 * 4096 * 64 / (us * 1e-6) / 1e12, 1)
-            del g
         out[name] = res
-        del layers, pool
     return out
 
 
-def bench_code_variants(q, torch, dev):
+def bench_configs(q, torch, dev, stream):
+    """The single-layer configurations at batch 1, timed as in time_layer:
+    the 4096x4096 HYB k=2 layer (V=2, Q=9, 512-pair table), and the
+    4096x14336 down-projection shape with the 3-bit non-uniform scalar
+    quantizer (fp16 scale per 128 weights) and with the 2-D vector quantizer
+    (8-bit index per weight pair).  GB/s on the packed codes, and on the
+    algorithmic bytes (codes, x, y, signs, tables and group scales) as a
+    fraction of the 8 TB/s HBM peak."""
+    import synth
+    out = {}
+    for wname in ("hyb4096", "down_nuq", "down_vq"):
+        s = synth.WORKLOADS[wname].layers[0]
+        kw = dict(scale=s.scale)
+        us, base = time_layer(q, torch, dev, stream, s.code, s.m, s.n, s.k, 1, "bench/cfg/" + wname, **kw)
+        alg = (base.code_bytes + 2 * s.n + 2 * s.m + (s.m + s.n) // 8 + tensor_bytes(base.lut)
+               + tensor_bytes(base.group_scale))
+        out[wname] = {"layer": synth.WORKLOADS[wname].description, "us_per_call": round(us, 2),
+                      "packed_bytes": base.code_bytes, "algorithmic_bytes": alg,
+                      "packed_GBps": round(base.code_bytes / (us * 1e-6) / 1e9, 1),
+                      "algorithmic_GBps": round(alg / (us * 1e-6) / 1e9, 1),
+                      "frac_of_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    log("single-layer configs b=1:", {k: (v["us_per_call"], v["algorithmic_GBps"]) for k, v in out.items()})
+    return {"configs_b1": out}
+
+
+def bench_code_variants(q, torch, dev, stream):
     """The table-size knob of the trellis codes on one 4096x4096 k=2 layer at
     b=1 and b=64: HYB with 2^9 pairs (V=2), HYB with a 2^6-value codebook
     (V=1) and the pure lookup of 2^16 values (a 128 KiB table in LDS)."""
     import synth
-    out = time_4096_variants(q, torch, dev, (
+    out = time_4096_variants(q, torch, dev, stream, (
         ("HYB_V2_Q9", synth.HYB, 2, dict(V=2, Q=9)), ("HYB_V1_Q6", synth.HYB, 2, dict(V=1, Q=6)),
         ("LUT_L16", synth.LUT, 2, {})), "bench/var/")
     log("code variants (4096x4096 k=2):", out)
@@ -535,14 +583,14 @@ def bench_encoder(q, torch, dev, cpu=True):
     return {"encoder_4096_hyb_k2": out}
 
 
-def bench_fractional(q, torch, dev):
+def bench_fractional(q, torch, dev, stream):
     """Bit widths of one 4096x4096 HYB layer (V=2, Q=9) at b=1 and b=64:
     2 to 4 bits per weight in half-bit steps (kV = 4 .. 8 bits per trellis
     step), and half-TCQ with the rows cut in two halves at 2.5 and 3 bits
     (2.75 on average)."""
     import synth
     H = synth.HYB
-    out = time_4096_variants(q, torch, dev, (
+    out = time_4096_variants(q, torch, dev, stream, (
         ("k2.0", H, 2, {}), ("k2.5", H, 0, dict(kv=5)), ("k3.0", H, 3, {}), ("k3.5", H, 0, dict(kv=7)),
         ("k4.0", H, 4, {}), ("half_k2.5_k3.0", H, 0, dict(kv=5, kv_b=6, m_a=2048))), "bench/frac/")
     log("bit widths (4096x4096 HYB):", out)
@@ -635,9 +683,52 @@ def cpu_baseline(specs, x16):
     return base, detail
 
 
+def cpu_per_config():
+    """The oracle on each of the other configurations, all threads: decode
+    only (every tile of every layer, bit-serial walk and code lookup) and one
+    full forward (decode, O(B^2) Hadamards on both sides, fp64 matvec) per
+    batch size.  The 28672x8192 batch-64 forward is timed on 8 of its 64
+    batch columns: its decode and weight work are whole, the per-column work
+    is an eighth.  Rates are weights/s and packed code bytes/s."""
+    import oracle
+    import synth
+    threads = oracle.omp_threads()
+    out = {}
+    for wname, cols in (("hyb4096", None), ("llama3_8b_layer", None), ("down_nuq", None),
+                        ("down_vq", None), ("up70b_prefill", 8)):
+        wl = synth.WORKLOADS[wname]
+        hosts = [s.build("cpu_per_config") for s in wl.layers]
+        weights = sum(h.m * h.n for h in hosts)
+        nbytes = sum(h.code_bytes for h in hosts)
+        t0 = time.perf_counter()
+        for h in hosts:
+            oracle.decode_tiles_storage(h, 0, h.n_tiles)
+        t_dec = time.perf_counter() - t0
+        rec = {"layers": len(hosts), "weights": weights, "packed_bytes": nbytes,
+               "decode_s": round(t_dec, 3), "decode_Mweights_per_s": round(weights / t_dec / 1e6, 2),
+               "decode_packed_GBps": round(nbytes / t_dec / 1e9, 5)}
+        for b in wl.batches:
+            bb = min(b, cols) if cols else b
+            t0 = time.perf_counter()
+            for h in hosts:
+                oracle.forward(h, synth.activations("cpu_per_config/x", bb, h.n))
+            t_fwd = time.perf_counter() - t0
+            rec["forward_b%d" % b] = {"columns_timed": bb, "s": round(t_fwd, 3),
+                                      "Mweights_per_s": round(weights / t_fwd / 1e6, 2),
+                                      "packed_GBps": round(nbytes / t_fwd / 1e9, 5)}
+        out[wname] = rec
+        log("cpu oracle %s: decode %.2f s, forward %s" % (
+            wname, t_dec, ", ".join("b=%s %.2f s" % (k[9:], v["s"]) for k, v in rec.items()
+                                    if k.startswith("forward_b"))))
+    return {"threads": threads, "configs": out,
+            "note": "the oracle is a plain correctness reference (bit-serial walk, O(B^2) Hadamard), "
+                    "not a tuned CPU implementation"}
+
+
 def measured_ceilings(torch, dev):
     """What plain library kernels reach on this GPU: a device-to-device copy
-    (HBM read + write) and a large fp16 matmul (hipBLASLt, MFMA)."""
+    (HBM read + write), a reduction that only reads, and a large fp16 matmul
+    (hipBLASLt, MFMA)."""
     nbytes = 512 << 20
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -652,6 +743,21 @@ def measured_ceilings(torch, dev):
     torch.cuda.synchronize()
     copy_gbs = 2 * nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
+    # pure read: column sums of 1 GiB of fp32 seen as 262144 x 1024 (torch's
+    # reduction over the outer dimension, each thread summing one column:
+    # coalesced reads, 4 KiB written); a full reduction to one scalar
+    # measured slower (3.9 TB/s against 5.7)
+    rd = torch.zeros(POOL_BYTES // 4, dtype=torch.float32, device=dev).view(-1, 1024)
+    for r in range(3):
+        s = rd.sum(0)
+    torch.cuda.synchronize()
+    e0.record()
+    for r in range(10):
+        s = rd.sum(0)
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = POOL_BYTES * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del rd, s
     n = 8192
     a = torch.randn(n, n, dtype=torch.float16, device=dev)
     b = torch.randn(n, n, dtype=torch.float16, device=dev)
@@ -666,8 +772,9 @@ def measured_ceilings(torch, dev):
     mm_tf = 2 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
     del a, b, c
     torch.cuda.empty_cache()
-    log("measured ceilings: copy %.0f GB/s (read + write), fp16 matmul %d^3 %.0f TFLOP/s" % (copy_gbs, n, mm_tf))
-    return {"copy_GBps_read_plus_write": round(copy_gbs, 1),
+    log("measured ceilings: copy %.0f GB/s (read + write), read %.0f GB/s, fp16 matmul %d^3 %.0f TFLOP/s"
+        % (copy_gbs, read_gbs, n, mm_tf))
+    return {"copy_GBps_read_plus_write": round(copy_gbs, 1), "read_GBps_colsum_1GiB": round(read_gbs, 1),
             "fp16_matmul_8192_TFLOPs": round(mm_tf, 1)}
 
 

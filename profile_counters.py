@@ -7,7 +7,8 @@ Usage (from the repository root R, after `cd /tmp && export TMPDIR=/tmp`):
       SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM SQ_VALU_MFMA_BUSY_CYCLES -d <dir1> -o run -- python3 $R/bench.py ARGS
   rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS \\
       SQ_ACTIVE_INST_ANY SQ_INSTS_SALU SQ_LDS_ADDR_CONFLICT -d <dir2> -o run -- python3 $R/bench.py ARGS
-  python3 profile_counters.py <dir1>/run_results.db <dir2>/run_results.db OUT.md "ARGS" [WEIGHTS]
+  rocprofv3 --pmc MfmaUtil -d <dir3> -o run -- python3 $R/bench.py ARGS      (optional third pass)
+  python3 profile_counters.py <dir1>/run_results.db <dir2>/run_results.db OUT.md "ARGS" [WEIGHTS [<dir3>/run_results.db]]
 
 ARGS is the bench's argument string (it goes into the summary's command
 line): `--steps 20 --warmup 5 --no-cpu-baseline` for the bench, or
@@ -18,7 +19,9 @@ bench's two known shapes are recognised by their grids (the 4096x4096 b=1
 GEMV and the 28672x8192 b=64 GEMM).
 
 Counters are per dispatch, summed over the chip; instruction counts are per
-wave (64 lanes).
+wave (64 lanes).  With the third pass the table adds MfmaUtil, rocprofv3's
+derived MFMA utilisation: MFMA-busy cycles summed over the SIMDs over
+(GPU-active cycles x SIMD count), in percent.
 """
 import os
 import sqlite3
@@ -46,19 +49,23 @@ def main():
     out = sys.argv[3]
     bench_args = sys.argv[4]
     weights = int(sys.argv[5]) if len(sys.argv) > 5 else 0
+    c = load(sys.argv[6]) if len(sys.argv) > 6 else None
     keys = [k for k in a if k in b and k[0].startswith("qdec::")]
     keys.sort(key=lambda k: -a[k].get("SQ_WAVE_CYCLES", (0, 0))[0] * a[k].get("SQ_WAVE_CYCLES", (0, 1))[1])
     title = "the bench's kernels" if not weights else "one layer (`%s`)" % bench_args
     lines = ["# SQ counters of %s" % title, "",
-             "Commands: two `rocprofv3 --pmc` runs of `python3 $R/bench.py %s`, eight SQ counters each "
-             "(the lists are in `profile_counters.py`), summarised by `python3 profile_counters.py "
-             "<pass 1 db> <pass 2 db> %s \"%s\"%s`." % (bench_args, os.path.relpath(out, ROOT), bench_args,
-                                                       (" %d" % weights) if weights else ""), "",
+             "Commands: %s `rocprofv3 --pmc` runs of `python3 $R/bench.py %s`, eight SQ counters in each "
+             "of the first two%s (the lists are in `profile_counters.py`), summarised by `python3 "
+             "profile_counters.py <pass 1 db> <pass 2 db> %s \"%s\"%s%s`." % (
+                 "three" if c else "two", bench_args, ", MfmaUtil in the third" if c else "",
+                 os.path.relpath(out, ROOT), bench_args, (" %d" % weights) if weights else "",
+                 " <pass 3 db>" if c else ""), "",
              "Per dispatch, averaged over dispatches.  wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave time "
              "waiting on a dependency); LDS wait = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES; bank = "
              "SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS (conflict cycles per LDS issue cycle).", "",
-             "| kernel | grid | dispatches | VALU inst | LDS inst | MFMA inst | wait | LDS wait | bank | VALU/weight | LDS/weight |",
-             "|---|---|---|---|---|---|---|---|---|---|---|"]
+             "| kernel | grid | dispatches | VALU inst | LDS inst | MFMA inst | wait | LDS wait | bank | VALU/weight | "
+             "LDS/weight |%s" % (" MfmaUtil % |" if c else ""),
+             "|---|---|---|---|---|---|---|---|---|---|---|%s" % ("---|" if c else "")]
     for k in keys[:14]:
         d = dict(a[k])
         d.update(b[k])
@@ -74,13 +81,19 @@ def main():
                     wts = w
         vpw = "%.3f" % (g("SQ_INSTS_VALU") * 64 / wts) if wts else ""
         lpw = "%.3f" % (g("SQ_INSTS_LDS") * 64 / wts) if wts else ""
-        lines.append("| `%s` | %d | %d | %.0f | %.0f | %.0f | %.2f | %.2f | %.2f | %s | %s |" % (
+        util = ""
+        if c:
+            util = " %.1f |" % c[k]["MfmaUtil"][0] if k in c and "MfmaUtil" in c[k] else " |"
+        lines.append("| `%s` | %d | %d | %.0f | %.0f | %.0f | %.2f | %.2f | %.2f | %s | %s |%s" % (
             k[0], k[1], d.get("SQ_INSTS_VALU", (0, 0))[1], g("SQ_INSTS_VALU"), g("SQ_INSTS_LDS"),
             g("SQ_INSTS_MFMA"), g("SQ_WAIT_INST_ANY") / wc, g("SQ_WAIT_INST_LDS") / wc,
-            g("SQ_LDS_BANK_CONFLICT") / (g("SQ_ACTIVE_INST_LDS") or 1.0), vpw, lpw))
+            g("SQ_LDS_BANK_CONFLICT") / (g("SQ_ACTIVE_INST_LDS") or 1.0), vpw, lpw, util))
     lines += ["", "VALU/weight and LDS/weight are lane-instructions per weight (wave instructions x 64 / "
               "weights) of the decode kernels: a GEMV counts the decode and the dot products (v_dot2, one "
               "per two weights); a GEMM counts the decode only (the products are MFMA instructions)."]
+    if c:
+        lines += ["", "MfmaUtil is rocprofv3's derived counter: the MFMA-busy cycles of all SIMDs over the "
+                  "GPU-active cycles of the dispatch times the SIMD count (1024), in percent."]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
