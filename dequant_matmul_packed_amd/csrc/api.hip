@@ -168,7 +168,8 @@ int status_of(hipError_t e) {
 }  // namespace
 
 namespace qdec {
-// K-split factor of the batched path: about two workgroups per CU.
+// K-split factor of the batched path: at most as many workgroups as the
+// CUs hold at once (GEMM_WG_PER_CU each).
 int gemm_ksplit(int64_t m, int64_t n, int64_t b) {
   static int forced = -1;
   if (forced < 0) {
@@ -177,9 +178,9 @@ int gemm_ksplit(int64_t m, int64_t n, int64_t b) {
     forced = ev ? atoi(ev) : 0;
     if (forced > 16) forced = 16;
   }
-  const int64_t npanels = m / 128, nbt = (b + 63) / 64;
+  const int64_t groups = (m / 128 + GEMM_PANELS - 1) / GEMM_PANELS, nbt = (b + 63) / 64;
   const int64_t niter = (n / 16 + 3) / 4;
-  int64_t ks = forced > 0 ? forced : (512 + npanels * nbt - 1) / (npanels * nbt);
+  int64_t ks = forced > 0 ? forced : (256 * GEMM_WG_PER_CU) / (groups * nbt);
   if (ks > niter) ks = niter;
   if (ks > 16) ks = 16;
   if (ks < 1) ks = 1;

@@ -1,9 +1,10 @@
 // Batched decode-and-multiply (qdec_gemm): decoded weights feed fp16 MFMA
 // (v_mfma_f32_16x16x32_f16) with fp32 accumulation.
 //
-// A workgroup (4 waves) owns one panel of 128 output rows and 64 batch
+// A workgroup (8 waves) owns two panels of 128 output rows and 64 batch
 // columns and steps through K 64 input columns (4 tile columns) at a time.
-// Wave w owns tile rows 2w, 2w+1 of the panel; per step it decodes the 8
+// Wave w owns tile rows 2(w%4), 2(w%4)+1 of panel w/4 of the pair; per step
+// it decodes the 8
 // tiles (2 tile rows x 4 tile columns) with the same 8-lanes-per-tile layout
 // as the GEMV: lane q of tile t holds 32 weights, rows 2q and 2q+1 of the
 // tile, as four 8-weight chunks of one row each.  Placing tile t at
@@ -14,8 +15,9 @@
 // weights go from the code registers to the matrix cores without touching
 // LDS.  The transformed activations X' (the B operand) are staged once per
 // step in LDS (double buffered, 16-byte chunks XOR-swizzled by row) and read
-// as fragments by the four waves; the lookup table of HYB/VQ/NUQ also lives
-// in LDS.  The loop is software-pipelined: the code words of step i+2 and
+// as fragments by the eight waves; the lookup table of HYB/VQ/NUQ also
+// lives in LDS, one per workgroup, so the two panels share it (and its 16
+// copies: a table per panel left room for half as many).  The loop is software-pipelined: the code words of step i+2 and
 // the X' chunk of step i+2 are in flight while step i is decoded and
 // multiplied.
 #include "gemv_impl.hpp"
@@ -24,39 +26,56 @@
 
 namespace qdec {
 
-constexpr int GEMM_THREADS = 256;
+constexpr int GEMM_THREADS = 64 * GEMM_WAVES;
+static_assert(GEMM_THREADS == 512, "one 16-byte X' chunk per thread and step (64 batch rows x 8 chunks)");
+
+// LDS table copies: lane l reads copy l % COPIES.  HYB and VQ tables take
+// GEMM_COPIES copies while two workgroups still fit a CU, else 8 (HYB with
+// Q = 10 and 11); the NUQ levels and the pure lookup take one.
+__host__ __device__ constexpr bool gemm_tabled(int code) { return code == HYB || code == HYB1 || code == VQ; }
+template <int CODE, int KV, int COPIES>
+__host__ __device__ constexpr int gemm_table_words(int Q) {
+  return (CODE == HYB || CODE == HYB1) ? (2 << Q) * COPIES
+       : CODE == VQ ? (1 << KV) * COPIES
+       : CODE == NUQ ? (1 << KV)
+       : CODE == LUT ? (1 << 15) : 0;   // LUT: 2^16 fp16 values, two per word
+}
 
 __device__ __forceinline__ int gemm_swz(int r, int k) {
   return r * 128 + ((((k >> 3) ^ (r & 7)) << 4) | ((k & 7) << 1));
 }
 
 // LDS: lookup table, then B[2][64 batch][64 k] fp16 (double buffered).
-template <int CODE, int KV>
+template <int CODE, int KV, int COPIES>
 __host__ __device__ inline size_t gemm_table_bytes(int Q) {
-  return ((size_t)gemv_table_words<CODE, KV>(Q) * 4 + 15) & ~(size_t)15;
+  return ((size_t)gemm_table_words<CODE, KV, COPIES>(Q) * 4 + 15) & ~(size_t)15;
 }
-template <int CODE, int KV>
+template <int CODE, int KV, int COPIES>
 __host__ __device__ inline size_t gemm_lds_bytes(int Q) {
-  return gemm_table_bytes<CODE, KV>(Q) + 2 * (64 * 128);
+  return gemm_table_bytes<CODE, KV, COPIES>(Q) + 2 * (64 * 128);
 }
 
-template <int CODE, int KV>
-__global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
+// Two workgroups per CU are four waves per SIMD (at most 128 VGPRs); the pure
+// lookup's 128 KiB table leaves room for one, so it may use twice as many.
+template <int CODE, int KV, int COPIES>
+__global__ __launch_bounds__(GEMM_THREADS, CODE == LUT ? 2 : 4) void gemm_kernel(GemmArgs a) {
   using G = LaneGeom<CODE, KV>;
   constexpr int NW = G::NW;
-  constexpr int COPIES = GemvTable<CODE>::COPIES;
   extern __shared__ __align__(16) uint32_t smem[];
   uint32_t* tab = smem;
-  char* Bs = reinterpret_cast<char*>(smem) + gemm_table_bytes<CODE, KV>(a.L.Q);
+  char* Bs = reinterpret_cast<char*>(smem) + gemm_table_bytes<CODE, KV, COPIES>(a.L.Q);
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = wv & 3;                           // wave within its panel
   const int q = lane & 7, t = lane >> 3;           // tile t of the wave, lane q in it
   const int tr = t & 1, tc = t >> 1;                 // tile row / column within the step
   const int64_t m = a.L.m, n = a.L.n;
   const int npanels = (int)(m / 128);
-  const int panel = blockIdx.x % npanels;
-  const int split = blockIdx.x / npanels;
+  const int ngroups = (npanels + GEMM_PANELS - 1) / GEMM_PANELS;
+  const int panel = (blockIdx.x % ngroups) * GEMM_PANELS + (wv >> 2);
+  const bool panel_ok = panel < npanels;             // wave-uniform: the last group may be short
+  const int split = blockIdx.x / ngroups;
   const int n0 = blockIdx.y * 64;
   const int ntc = (int)(n >> 4);                    // tile columns (steps of 4)
   const int niter = (ntc + 3) >> 2;
@@ -83,7 +102,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   // panel; a panel's tile column is 8 tiles of TILE_WORDS words, and lane q
   // reads NW words from word lane_word(q) of its tile.
   constexpr uint32_t TB = 4u * G::TILE_WORDS;       // bytes per tile
-  const auto crs = make_rsrc(a.L.codes + (int64_t)panel * ntc * (8 * G::TILE_WORDS), (uint32_t)ntc * (8u * TB));
+  const auto crs = make_rsrc(a.L.codes + (int64_t)(panel_ok ? panel : 0) * ntc * (8 * G::TILE_WORDS),
+                             panel_ok ? (uint32_t)ntc * (8u * TB) : 0u);
   const int itc = (ntc - tc + 3) >> 2 < it1 ? (ntc - tc + 3) >> 2 : it1;   // 4 it + tc < ntc
   const uint32_t cbase = (uint32_t)tc * (8u * TB) + (uint32_t)(2 * wave + tr) * TB + 4u * G::lane_word(q);
   // NUQ group scales of the lane's rows 2q, 2q+1 (fp16 [m][n/group]); a
@@ -101,32 +121,18 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
       w[NW + 1] = buf_load_u16(grs, ok ? (uint32_t)(((grow0 + 1) * gstride + g) * 2) : BUF_OFF);
     }
   };
-  // X' chunks of this thread: batch row n0 + (c >> 3), k chunk c & 7, for
-  // c = tid and tid + 256; chunk ch of step it is column 64 it + 8 ch
+  // X' chunk of this thread: batch row n0 + (tid >> 3), k chunk tid & 7;
+  // chunk ch of step it is column 64 it + 8 ch
   const auto xrs = make_rsrc(a.xr, (uint32_t)(a.b * n * 2));
-  int itx[2];
-  uint32_t xbase[2];
-#pragma unroll
-  for (int rep = 0; rep < 2; ++rep) {
-    const int c = tid + rep * GEMM_THREADS;
-    const int row = n0 + (c >> 3), ch = c & 7;
-    const int lim = (int)((n - ch * 8 + 63) >> 6);
-    itx[rep] = row < a.b ? (lim < it1 ? lim : it1) : 0;
-    xbase[rep] = (uint32_t)(((int64_t)(row < a.b ? row : 0) * n + ch * 8) * 2);
-  }
-  auto load_x = [&](int it, uint4* xv) {
-#pragma unroll
-    for (int rep = 0; rep < 2; ++rep)
-      xv[rep] = buf_load_u4(xrs, it < itx[rep] ? xbase[rep] + (uint32_t)it * 128u : BUF_OFF);
+  const int xrow = n0 + (tid >> 3), xch = tid & 7;
+  const int xlim = (int)((n - xch * 8 + 63) >> 6);
+  const int itx = xrow < a.b ? (xlim < it1 ? xlim : it1) : 0;
+  const uint32_t xbase = (uint32_t)(((int64_t)(xrow < a.b ? xrow : 0) * n + xch * 8) * 2);
+  auto load_x = [&](int it, uint4& xv) {
+    xv = buf_load_u4(xrs, it < itx ? xbase + (uint32_t)it * 128u : BUF_OFF);
   };
-  auto store_x = [&](const uint4* xv, int buf) {
-    char* Bt = Bs + buf * (64 * 128);
-#pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      const int c = tid + rep * GEMM_THREADS;
-      const int bb = c >> 3, ch = c & 7;
-      *reinterpret_cast<uint4*>(Bt + gemm_swz(bb, ch * 8)) = xv[rep];
-    }
+  auto store_x = [&](const uint4& xv, int buf) {
+    *reinterpret_cast<uint4*>(Bs + buf * (64 * 128) + gemm_swz(tid >> 3, xch * 8)) = xv;
   };
 
   float4v acc[2][4];
@@ -188,9 +194,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   // LDS buffer and refills the freed registers with steps s+5 and s+3.
   constexpr int CW = CODE == NUQ ? NW + 2 : NW;      // code words (+ NUQ scales) per step
   uint32_t c0[CW], c1[CW], c2[CW], c3[CW];
-  uint4 x0[2], x1[2];
+  uint4 x0, x1;
   uint4 A0[4], A1[4];
-  auto one = [&](int s, const uint4* Acur, uint4* Anext, uint32_t* cnext, uint4* xnext, int buf) {
+  auto one = [&](int s, const uint4* Acur, uint4* Anext, uint32_t* cnext, uint4& xnext, int buf) {
     __syncthreads();
     mma(Acur, buf);
     decode(s + 1, cnext, Anext);          // past the range: decoded, never used
@@ -224,6 +230,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   // MFMA row i is weight row 16*(i/8) + 2*(i%8) + ra of the wave's 32 rows.
   // Each K split writes its own slice of the workspace (no atomics); the
   // output-RHT kernel sums the slices.
+  if (!panel_ok) return;
   float* zs = a.z + (int64_t)split * a.b * a.mz;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
@@ -239,16 +246,28 @@ __global__ __launch_bounds__(GEMM_THREADS, 3) void gemm_kernel(GemmArgs a) {
   }
 }
 
-template <int CODE, int KV>
-static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t stream) {
-  const size_t lds = gemm_lds_bytes<CODE, KV>(a.L.Q);
+template <int CODE, int KV, int COPIES>
+static hipError_t launch_gemm_c(const GemmArgs& a, hipStream_t stream) {
+  const size_t lds = gemm_lds_bytes<CODE, KV, COPIES>(a.L.Q);
   static size_t have = 0;
   const hipError_t e =
-      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_kernel<CODE, KV>), lds, &have);
+      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_kernel<CODE, KV, COPIES>), lds, &have);
   if (e != hipSuccess) return e;
-  dim3 grid((unsigned)((a.L.m / 128) * a.ksplit), (unsigned)((a.b + 63) / 64));
-  hipLaunchKernelGGL((gemm_kernel<CODE, KV>), grid, dim3(GEMM_THREADS), lds, stream, a);
+  const int64_t ngroups = (a.L.m / 128 + GEMM_PANELS - 1) / GEMM_PANELS;
+  dim3 grid((unsigned)(ngroups * a.ksplit), (unsigned)((a.b + 63) / 64));
+  hipLaunchKernelGGL((gemm_kernel<CODE, KV, COPIES>), grid, dim3(GEMM_THREADS), lds, stream, a);
   return hipGetLastError();
+}
+
+template <int CODE, int KV>
+static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t stream) {
+  if constexpr (gemm_tabled(CODE)) {
+    if (gemm_lds_bytes<CODE, KV, GEMM_COPIES>(a.L.Q) <= GEMM_LDS_BYTES / GEMM_WG_PER_CU)
+      return launch_gemm_c<CODE, KV, GEMM_COPIES>(a, stream);
+    return launch_gemm_c<CODE, KV, 8>(a, stream);
+  } else {
+    return launch_gemm_c<CODE, KV, 1>(a, stream);
+  }
 }
 
 template <int CODE>

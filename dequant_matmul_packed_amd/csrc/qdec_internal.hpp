@@ -112,6 +112,15 @@ inline GemvWs gemv_ws_layout(int64_t m, int64_t n, int64_t b) {
 }
 // Workspace layout of qdec_gemm: X' (fp16 [b][n]) then the K-split partial
 // sums Z (fp32 [ksplit][b][m]).  Nothing in it needs initialising.
+// Batched-path geometry: a workgroup of 8 waves covers two panels of 128
+// rows (four waves each) and shares one lookup table of 16 copies and the
+// staged X'; two such workgroups fit a CU (80 KiB of LDS each for a
+// 2^9-pair table).
+constexpr int GEMM_WAVES = 8;
+constexpr int GEMM_PANELS = GEMM_WAVES / 4;
+constexpr int GEMM_COPIES = 16;
+constexpr int GEMM_WG_PER_CU = 2;
+constexpr size_t GEMM_LDS_BYTES = 160 * 1024;      // LDS of one CU
 int gemm_ksplit(int64_t m, int64_t n, int64_t b);
 inline size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t b) {
   return align256((size_t)(b * n) * 2) + align256((size_t)(gemm_ksplit(m, n, b) * b * m) * 4);
