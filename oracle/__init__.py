@@ -87,6 +87,8 @@ def lib():
         i64, i32 = ctypes.c_int64, ctypes.c_int
         L.orc_f16_from_double.restype = ctypes.c_uint16
         L.orc_f16_from_double.argtypes = [ctypes.c_double]
+        L.orc_f16_from_float_array.restype = None
+        L.orc_f16_from_float_array.argtypes = [P, i64, P]
         L.orc_f16_to_double.restype = ctypes.c_double
         L.orc_f16_to_double.argtypes = [ctypes.c_uint16]
         L.orc_walk_bits.argtypes = [P, i64, i32, i32, i64, i32, P]
@@ -172,6 +174,14 @@ def f16_from_double(v) -> np.ndarray:
     v = np.asarray(v, dtype=np.float64)
     f = lib().orc_f16_from_double
     return np.array([f(float(x)) for x in v.ravel()], dtype=np.uint16).reshape(v.shape)
+
+
+def f16_from_float32(v) -> np.ndarray:
+    """fp16 bit patterns (round to nearest even) of an fp32 array, in one call."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.zeros(v.shape, dtype=np.uint16)
+    lib().orc_f16_from_float_array(_ptr(v), v.size, _ptr(out))
+    return out
 
 
 def f16_to_double(h) -> np.ndarray:

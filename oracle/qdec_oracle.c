@@ -155,6 +155,12 @@ uint16_t orc_f16_from_double(double v) {
   return sign | (uint16_t)((e + 15) << 10) | (uint16_t)((int)f - 1024);
 }
 
+/* The same rounding over an array of fp32 values (each converts to fp64
+   exactly), for exhaustive checks over whole binades. */
+void orc_f16_from_float_array(const float* v, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f16_from_double((double)v[i]);
+}
+
 /* Round fp64 to fp32 (C's conversion rounds to nearest-even by default).   */
 static double orc_round_f32(double v) { return (double)(float)v; }
 

@@ -140,6 +140,22 @@ def test_f16_rounding_matches_numpy():
     assert np.array_equal(back, np.arange(0, 0x7C00, 13, dtype=np.uint16).view(np.float16).astype(np.float64))
 
 
+@pytest.mark.parametrize("e", [-26, -25, -15, -14, 0, 15])
+def test_f16_rounding_exhaustive_binades(e):
+    """Every fp32 value of the binade [2^e, 2^(e+1)), both signs, rounds to
+    the fp16 that numpy's float32 -> float16 conversion gives: below half
+    the smallest subnormal (to zero), around the smallest subnormal, the
+    subnormal/normal boundary, the unit binade and the top binade (overflow
+    to infinity from 65520 on)."""
+    m = np.arange(1 << 23, dtype=np.uint32)
+    for sign in (0, 1):
+        bits = (np.uint32(sign) << np.uint32(31)) | (np.uint32(e + 127) << np.uint32(23)) | m
+        v = bits.view(np.float32)
+        with np.errstate(over="ignore"):
+            want = v.astype(np.float16).view(np.uint16)
+        assert np.array_equal(oracle.f16_from_float32(v), want), (e, sign)
+
+
 # ---------------------------------------------------------------------------
 # HYB code
 
