@@ -180,18 +180,24 @@ int qdec_rht(const void *in, int32_t in_dtype, void *out, int32_t out_dtype,
              int64_t rows, int64_t n, int32_t block, const uint32_t *signs,
              int32_t mode, float scale, void *stream);
 
-/* Fused decode-and-multiply for small batches, one launch:
- * Y[b][m] = layer(X[b][n]) as defined above, 1 <= batch <= 8, fp16 in/out,
- * fp32 accumulation.  ws: qdec_workspace_bytes(layer, batch, QDEC_OP_GEMV)
- * bytes, 256-byte aligned, zero-filled before first use (left zeroed).      */
+/* Fused decode-and-multiply for small batches ("QTIP's contribution (W1)":
+ * small-batch inference is memory bound, so the weights are decoded on the
+ * fly): Y[b][m] = layer(X[b][n]) as defined above, 1 <= batch <= 8, fp16
+ * in/out, fp32 accumulation.  One kernel decodes and multiplies (at one
+ * batch column it also applies the input transform), a second applies the
+ * output transform; with more batch columns the input transform runs first
+ * in a kernel of its own.  ws: qdec_workspace_bytes(layer, batch,
+ * QDEC_OP_GEMV) bytes, 256-byte aligned, zero-filled before first use (left
+ * zeroed).                                                                   */
 int qdec_gemv(const qdec_layer *layer, const uint16_t *x, uint16_t *y,
               int64_t batch, void *ws, size_t ws_bytes, void *stream);
 
 /* Batched decode-and-multiply (prefill): same result as qdec_gemv for
- * 1 <= batch <= 256; decoded tiles are staged in LDS and fed to fp16 MFMA
- * with fp32 accumulation.  Three launches on `stream` (input RHT, GEMM,
- * output RHT).  ws: qdec_workspace_bytes(layer, batch, QDEC_OP_GEMM) bytes,
- * 256-byte aligned; its contents on entry do not matter.                    */
+ * 1 <= batch <= 256; decoded weights go from registers straight into fp16
+ * MFMA (the transformed activations are staged in LDS), fp32 accumulation.
+ * Three launches on `stream` (input RHT, GEMM, output RHT).
+ * ws: qdec_workspace_bytes(layer, batch, QDEC_OP_GEMM) bytes, 256-byte
+ * aligned; its contents on entry do not matter.                             */
 int qdec_gemm(const qdec_layer *layer, const uint16_t *x, uint16_t *y,
               int64_t batch, void *ws, size_t ws_bytes, void *stream);
 
