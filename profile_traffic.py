@@ -3,7 +3,7 @@
 
 Usage (from the repository root, R = its path, after `cd /tmp && export TMPDIR=/tmp`):
   rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc/FETCH_SIZE -o run -- \\
-      python3 $R/bench.py --eager --steps 20 --warmup 5 --no-detail --no-cpu-baseline --copy-calibration-mib 256
+      python3 $R/bench.py --steps 20 --warmup 5 --no-detail --no-cpu-baseline --copy-calibration-mib 256
   rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc/WRITE_SIZE -o run -- (same command)
   python3 profile_traffic.py gpurun_out/pmc/FETCH_SIZE/run_results.db gpurun_out/pmc/WRITE_SIZE/run_results.db
 
@@ -57,7 +57,7 @@ def main():
            "calibration": "device-to-device copy of %d MiB (%s)" % (COPY_MIB, ck[0]), "variants": {}}
     lines = ["# HBM traffic of the fused GEMV (bench workload, 4096x4096, b=1)", "",
              "Counters: `FETCH_SIZE` and `WRITE_SIZE` (KiB per dispatch), one rocprofv3 --pmc run each, of",
-             "`python3 $R/bench.py --eager --steps 20 --warmup 5 --no-detail --no-cpu-baseline --copy-calibration-mib 256`,",
+             "`python3 $R/bench.py --steps 20 --warmup 5 --no-detail --no-cpu-baseline --copy-calibration-mib 256`,",
              "summarised by `python3 profile_traffic.py <FETCH db> <WRITE db>`.", "",
              "Calibration: the plain %d MiB copy reads FETCH %.0f KiB and WRITE %.0f KiB per dispatch, so the" % (
                  COPY_MIB, fetch[ck][1], write[ck][1]),
