@@ -404,6 +404,56 @@ def test_gemm_full_size_sampled(q, dev):
         assert _rel(got, ref) < REL_TOL, blk
 
 
+def test_graph_replays_match_eager(q, dev):
+    """Calls captured into a HIP graph (as the bench replays them) and replayed
+    several times, with eager work on the same buffers between the replays:
+    every replay gives the eager result -- bit for bit for the batched path
+    (fixed summation order), within the tolerance of the oracle for the GEMV
+    (its split-K atomic adds may sum in another order)."""
+    import torch
+    m, n = 1024, 2048
+    host = synth.make_layer(synth.HYB, m, n, 2, tag="graph")
+    lay = q.upload_layer(host, dev)
+    x16 = synth.activations("graphx", 64, n)
+    xt = _f16_tensor(x16, dev)
+    ref1 = oracle.forward(host, x16[:1])
+    ref4 = oracle.forward(host, x16[:4])
+    ws1 = q.workspace(lay, 1, q.QDEC_OP_GEMV, dev)
+    ws4 = q.workspace(lay, 4, q.QDEC_OP_GEMV, dev)
+    wsg = q.workspace(lay, 64, q.QDEC_OP_GEMM, dev)
+    y1 = torch.empty((1, m), dtype=torch.float16, device=dev)
+    y4 = torch.empty((4, m), dtype=torch.float16, device=dev)
+    yg = torch.empty((64, m), dtype=torch.float16, device=dev)
+    x1, x4 = xt[:1].contiguous(), xt[:4].contiguous()
+
+    def calls():
+        q.gemv(lay, x1, ws=ws1, y=y1)
+        q.gemv(lay, x4, ws=ws4, y=y4)
+        q.gemm(lay, xt, ws=wsg, y=yg)
+    calls()                                   # eager first (also sets kernel attributes)
+    torch.cuda.synchronize()
+    eager_g = yg.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(3):
+        _say("graph replay", rep)
+        for t in (y1, y4, yg):
+            t.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert _rel(_to_f64(y1), ref1) < REL_TOL, rep
+        assert _rel(_to_f64(y4), ref4) < REL_TOL, rep
+        assert torch.equal(yg, eager_g), rep
+        calls()                               # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(yg, eager_g), rep
+    del g
+    # the GEMV workspaces are back to zero after the replays
+    assert torch.count_nonzero(ws1[:m * 4]).item() == 0
+    assert torch.count_nonzero(ws4[:4 * m * 4]).item() == 0
+
+
 def test_gemm_agrees_with_gemv(q, dev):
     import torch
     host = synth.make_layer(synth.HYB, 512, 1024, 2, tag="gmgv")
