@@ -168,8 +168,27 @@ int status_of(hipError_t e) {
 }  // namespace
 
 namespace qdec {
+// K halves per workgroup of the batched path: 2 (a 16-wave workgroup, one
+// per CU, adding its halves in LDS: half as many K-split slices to write and
+// to sum) where the panel pairs alone come near filling the chip -- at least
+// 32 per 64 batch columns -- and each half still gets 8 steps of 64 columns;
+// else 1 (8-wave workgroups, two per CU).  Tuning override
+// QDEC_GEMM_KSUB = 1 / 2.
+int gemm_ksub(int64_t m, int64_t n, int64_t b) {
+  static int forced = -1;
+  if (forced < 0) {
+    const char* ev = getenv("QDEC_GEMM_KSUB");
+    forced = ev ? atoi(ev) : 0;
+    if (forced != 1 && forced != 2) forced = 0;
+  }
+  if (forced) return forced;
+  const int64_t groups = (m / 128 + GEMM_PANELS - 1) / GEMM_PANELS, nbt = (b + 63) / 64;
+  const int64_t niter = (n / 16 + 3) / 4;
+  return (groups * nbt >= 32 && niter >= 16) ? 2 : 1;
+}
+
 // K-split factor of the batched path: at most as many workgroups as the
-// CUs hold at once (GEMM_WG_PER_CU each).
+// CUs hold at once (two 8-wave or one 16-wave workgroup each).
 int gemm_ksplit(int64_t m, int64_t n, int64_t b) {
   static int forced = -1;
   if (forced < 0) {
@@ -180,8 +199,11 @@ int gemm_ksplit(int64_t m, int64_t n, int64_t b) {
   }
   const int64_t groups = (m / 128 + GEMM_PANELS - 1) / GEMM_PANELS, nbt = (b + 63) / 64;
   const int64_t niter = (n / 16 + 3) / 4;
-  int64_t ks = forced > 0 ? forced : (256 * GEMM_WG_PER_CU) / (groups * nbt);
-  if (ks > niter) ks = niter;
+  const int ksub = gemm_ksub(m, n, b);
+  const int64_t slots = 256 * (ksub == 2 ? 1 : GEMM_WG_PER_CU);
+  int64_t ks = forced > 0 ? forced : slots / (groups * nbt);
+  const int64_t most = ksub == 2 ? niter / 8 : niter;   // a half keeps at least 4 steps
+  if (ks > most) ks = most;
   if (ks > 16) ks = 16;
   if (ks < 1) ks = 1;
   return (int)ks;
@@ -413,6 +435,7 @@ int qdec_gemm(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
   g.b = (int)batch;
   const int64_t ks = gemm_ksplit(L.m, L.n, batch);
   g.ksplit = (int)ks;
+  g.ksub = gemm_ksub(L.m, L.n, batch);
   for (int p = 0; p < parts.count; ++p) {   // each row part writes its rows of every slice
     g.L = parts.part[p];
     g.row0 = parts.row0[p];

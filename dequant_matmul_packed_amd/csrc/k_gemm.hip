@@ -26,8 +26,13 @@
 
 namespace qdec {
 
-constexpr int GEMM_THREADS = 64 * GEMM_WAVES;
-static_assert(GEMM_THREADS == 512, "one 16-byte X' chunk per thread and step (64 batch rows x 8 chunks)");
+// KSUB = 2 doubles the workgroup: two groups of 8 waves run the two halves
+// of the K split's steps over the same two panels (one table, an X' buffer
+// pair each) and add their sums in LDS at the end, so a layer that fills
+// the chip with one such workgroup per CU writes half as many K-split
+// slices (and the output transform reads half as many).
+constexpr int GEMM_SUB_THREADS = 64 * GEMM_WAVES;
+static_assert(GEMM_SUB_THREADS == 512, "one 16-byte X' chunk per thread and step (64 batch rows x 8 chunks)");
 
 // LDS table copies: lane l reads copy l % COPIES.  HYB and VQ tables take
 // GEMM_COPIES copies while two workgroups still fit a CU, else 8 (HYB with
@@ -45,29 +50,38 @@ __device__ __forceinline__ int gemm_swz(int r, int k) {
   return r * 128 + ((((k >> 3) ^ (r & 7)) << 4) | ((k & 7) << 1));
 }
 
-// LDS: lookup table, then B[2][64 batch][64 k] fp16 (double buffered).
+// LDS: lookup table, then B[KSUB][2][64 batch][64 k] fp16 (double
+// buffered per K half); with KSUB = 2 the space is reused at the end for the
+// second half's sums (8 waves x 32 values x 64 lanes fp32).
 template <int CODE, int KV, int COPIES>
 __host__ __device__ inline size_t gemm_table_bytes(int Q) {
   return ((size_t)gemm_table_words<CODE, KV, COPIES>(Q) * 4 + 15) & ~(size_t)15;
 }
-template <int CODE, int KV, int COPIES>
+template <int CODE, int KV, int COPIES, int KSUB>
 __host__ __device__ inline size_t gemm_lds_bytes(int Q) {
-  return gemm_table_bytes<CODE, KV, COPIES>(Q) + 2 * (64 * 128);
+  const size_t main = gemm_table_bytes<CODE, KV, COPIES>(Q) + (size_t)KSUB * 2 * (64 * 128);
+  const size_t red = KSUB > 1 ? (size_t)GEMM_WAVES * 32 * 64 * 4 : 0;
+  return main > red ? main : red;
 }
 
-// Two workgroups per CU are four waves per SIMD (at most 128 VGPRs); the pure
-// lookup's 128 KiB table leaves room for one, so it may use twice as many.
-template <int CODE, int KV, int COPIES>
-__global__ __launch_bounds__(GEMM_THREADS, CODE == LUT ? 2 : 4) void gemm_kernel(GemmArgs a) {
+// Four waves per SIMD (at most 128 VGPRs): two 8-wave workgroups or one of
+// 16 waves per CU; the pure lookup's 128 KiB table leaves room for one
+// 8-wave workgroup, so it may use twice as many.
+template <int CODE, int KV, int COPIES, int KSUB>
+__global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void gemm_kernel(GemmArgs a) {
+  constexpr int GEMM_THREADS = GEMM_SUB_THREADS * KSUB;
   using G = LaneGeom<CODE, KV>;
   constexpr int NW = G::NW;
   extern __shared__ __align__(16) uint32_t smem[];
   uint32_t* tab = smem;
-  char* Bs = reinterpret_cast<char*>(smem) + gemm_table_bytes<CODE, KV, COPIES>(a.L.Q);
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wvall = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ksub = wvall / GEMM_WAVES;               // K half of this wave (0 with KSUB = 1)
+  const int wv = wvall % GEMM_WAVES;                 // wave within its 8-wave group
+  const int stid = tid % GEMM_SUB_THREADS;           // thread within its group
   const int wave = wv & 3;                           // wave within its panel
+  char* Bs = reinterpret_cast<char*>(smem) + gemm_table_bytes<CODE, KV, COPIES>(a.L.Q) + ksub * 2 * (64 * 128);
   const int q = lane & 7, t = lane >> 3;           // tile t of the wave, lane q in it
   const int tr = t & 1, tc = t >> 1;                 // tile row / column within the step
   const int64_t m = a.L.m, n = a.L.n;
@@ -79,10 +93,16 @@ __global__ __launch_bounds__(GEMM_THREADS, CODE == LUT ? 2 : 4) void gemm_kernel
   const int n0 = blockIdx.y * 64;
   const int ntc = (int)(n >> 4);                    // tile columns (steps of 4)
   const int niter = (ntc + 3) >> 2;
-  // steps per K split, a multiple of 4 (the loop's unroll) where possible
+  // steps per K split, a multiple of 4 (the loop's unroll) where possible;
+  // with KSUB = 2 each half takes `steps` of them, also a multiple of 4,
+  // the first half from s0 and the second from s0 + steps (steps past the
+  // split's end read zeros)
   const int per = (((niter + a.ksplit - 1) / a.ksplit) + 3) & ~3;
-  const int it0 = split * per;
-  const int it1 = (it0 + per) < niter ? (it0 + per) : niter;
+  const int sp0 = split * per;
+  const int sp1 = (sp0 + per) < niter ? (sp0 + per) : niter;
+  const int steps = sp0 < sp1 ? ((((sp1 - sp0) + KSUB - 1) / KSUB) + 3) & ~3 : 0;   // workgroup-uniform
+  const int it0 = sp0 + ksub * steps;                // this half's first step
+  const int it1 = (it0 + steps) < sp1 ? (it0 + steps) : sp1;   // its live end (<= it0: none live)
 
   if constexpr (CODE == HYB) fill_signed_table<COPIES>(tab, a.L.lut, a.L.Q, tid, GEMM_THREADS);
   if constexpr (CODE == HYB1) fill_signed_table<COPIES, 0x8000u>(tab, a.L.lut, a.L.Q, tid, GEMM_THREADS);
@@ -121,10 +141,10 @@ __global__ __launch_bounds__(GEMM_THREADS, CODE == LUT ? 2 : 4) void gemm_kernel
       w[NW + 1] = buf_load_u16(grs, ok ? (uint32_t)(((grow0 + 1) * gstride + g) * 2) : BUF_OFF);
     }
   };
-  // X' chunk of this thread: batch row n0 + (tid >> 3), k chunk tid & 7;
+  // X' chunk of this thread: batch row n0 + (stid >> 3), k chunk stid & 7;
   // chunk ch of step it is column 64 it + 8 ch
   const auto xrs = make_rsrc(a.xr, (uint32_t)(a.b * n * 2));
-  const int xrow = n0 + (tid >> 3), xch = tid & 7;
+  const int xrow = n0 + (stid >> 3), xch = stid & 7;
   const int xlim = (int)((n - xch * 8 + 63) >> 6);
   const int itx = xrow < a.b ? (xlim < it1 ? xlim : it1) : 0;
   const uint32_t xbase = (uint32_t)(((int64_t)(xrow < a.b ? xrow : 0) * n + xch * 8) * 2);
@@ -132,7 +152,7 @@ __global__ __launch_bounds__(GEMM_THREADS, CODE == LUT ? 2 : 4) void gemm_kernel
     xv = buf_load_u4(xrs, it < itx ? xbase + (uint32_t)it * 128u : BUF_OFF);
   };
   auto store_x = [&](const uint4& xv, int buf) {
-    *reinterpret_cast<uint4*>(Bs + buf * (64 * 128) + gemm_swz(tid >> 3, xch * 8)) = xv;
+    *reinterpret_cast<uint4*>(Bs + buf * (64 * 128) + gemm_swz(stid >> 3, xch * 8)) = xv;
   };
 
   float4v acc[2][4];
@@ -204,7 +224,7 @@ __global__ __launch_bounds__(GEMM_THREADS, CODE == LUT ? 2 : 4) void gemm_kernel
     store_x(xnext, buf ^ 1);
     load_x(s + 3, xnext);
   };
-  if (it0 < it1) {
+  if (steps > 0) {                                   // workgroup-uniform: every wave meets every barrier
     load_codes(it0, c0);
     load_codes(it0 + 1, c1);
     load_codes(it0 + 2, c2);
@@ -216,9 +236,8 @@ __global__ __launch_bounds__(GEMM_THREADS, CODE == LUT ? 2 : 4) void gemm_kernel
     load_x(it0 + 2, x0);
     decode(it0, c0, A0);
     load_codes(it0 + 4, c0);
-    // whole groups of 4 steps; steps past it1 (at most 3) read zeros and
-    // add nothing
-    for (int s = it0; s < it1; s += 4) {
+    // whole groups of 4 steps; steps past it1 read zeros and add nothing
+    for (int s = it0; s < it0 + steps; s += 4) {
       one(s, A0, A1, c1, x1, 0);
       one(s + 1, A1, A0, c2, x0, 1);
       one(s + 2, A0, A1, c3, x1, 0);
@@ -228,8 +247,29 @@ __global__ __launch_bounds__(GEMM_THREADS, CODE == LUT ? 2 : 4) void gemm_kernel
 
   // ---- epilogue.  acc[ra][nb] holds D[i][j], i = 4*(lane/16) + e, j = lane % 16:
   // MFMA row i is weight row 16*(i/8) + 2*(i%8) + ra of the wave's 32 rows.
-  // Each K split writes its own slice of the workspace (no atomics); the
-  // output-RHT kernel sums the slices.
+  // With KSUB = 2 the second half hands its sums to the first through LDS
+  // (the table and X' are dead by then).  Each K split writes its own slice
+  // of the workspace (no atomics); the output-RHT kernel sums the slices.
+  if constexpr (KSUB > 1) {
+    float* red = reinterpret_cast<float*>(smem) + (wv * 32) * 64 + lane;
+    __syncthreads();
+    if (ksub == 1) {
+#pragma unroll
+      for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) red[((ra * 4 + nb) * 4 + e) * 64] = acc[ra][nb][e];
+    }
+    __syncthreads();
+    if (ksub == 1) return;
+#pragma unroll
+    for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[ra][nb][e] += red[((ra * 4 + nb) * 4 + e) * 64];
+  }
   if (!panel_ok) return;
   float* zs = a.z + (int64_t)split * a.b * a.mz;
 #pragma unroll
@@ -246,23 +286,28 @@ __global__ __launch_bounds__(GEMM_THREADS, CODE == LUT ? 2 : 4) void gemm_kernel
   }
 }
 
-template <int CODE, int KV, int COPIES>
-static hipError_t launch_gemm_c(const GemmArgs& a, hipStream_t stream) {
-  const size_t lds = gemm_lds_bytes<CODE, KV, COPIES>(a.L.Q);
+template <int CODE, int KV, int COPIES, int KSUB>
+static hipError_t launch_gemm_k(const GemmArgs& a, hipStream_t stream) {
+  const size_t lds = gemm_lds_bytes<CODE, KV, COPIES, KSUB>(a.L.Q);
   static size_t have = 0;
   const hipError_t e =
-      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_kernel<CODE, KV, COPIES>), lds, &have);
+      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_kernel<CODE, KV, COPIES, KSUB>), lds, &have);
   if (e != hipSuccess) return e;
   const int64_t ngroups = (a.L.m / 128 + GEMM_PANELS - 1) / GEMM_PANELS;
   dim3 grid((unsigned)(ngroups * a.ksplit), (unsigned)((a.b + 63) / 64));
-  hipLaunchKernelGGL((gemm_kernel<CODE, KV, COPIES>), grid, dim3(GEMM_THREADS), lds, stream, a);
+  hipLaunchKernelGGL((gemm_kernel<CODE, KV, COPIES, KSUB>), grid, dim3(GEMM_SUB_THREADS * KSUB), lds, stream, a);
   return hipGetLastError();
+}
+template <int CODE, int KV, int COPIES>
+static hipError_t launch_gemm_c(const GemmArgs& a, hipStream_t stream) {
+  if (a.ksub == 2) return launch_gemm_k<CODE, KV, COPIES, 2>(a, stream);
+  return launch_gemm_k<CODE, KV, COPIES, 1>(a, stream);
 }
 
 template <int CODE, int KV>
 static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t stream) {
   if constexpr (gemm_tabled(CODE)) {
-    if (gemm_lds_bytes<CODE, KV, GEMM_COPIES>(a.L.Q) <= GEMM_LDS_BYTES / GEMM_WG_PER_CU)
+    if (gemm_lds_bytes<CODE, KV, GEMM_COPIES, 1>(a.L.Q) <= GEMM_LDS_BYTES / GEMM_WG_PER_CU)
       return launch_gemm_c<CODE, KV, GEMM_COPIES>(a, stream);
     return launch_gemm_c<CODE, KV, 8>(a, stream);
   } else {

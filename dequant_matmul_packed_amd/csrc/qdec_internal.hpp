@@ -78,6 +78,7 @@ struct GemmArgs {
   int64_t mz;          // rows of the whole layer
   int b;
   int ksplit;          // K split factor
+  int ksub;            // K halves per workgroup (1 or 2, gemm_ksub)
 };
 
 // The encoder: one part of a layer, its targets and its output codes.
@@ -121,6 +122,7 @@ constexpr int GEMM_PANELS = GEMM_WAVES / 4;
 constexpr int GEMM_COPIES = 16;
 constexpr int GEMM_WG_PER_CU = 2;
 constexpr size_t GEMM_LDS_BYTES = 160 * 1024;      // LDS of one CU
+int gemm_ksub(int64_t m, int64_t n, int64_t b);
 int gemm_ksplit(int64_t m, int64_t n, int64_t b);
 inline size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t b) {
   return align256((size_t)(b * n) * 2) + align256((size_t)(gemm_ksplit(m, n, b) * b * m) * 4);

@@ -384,6 +384,26 @@ def test_gemm_small_matches_oracle(q, dev, code, k, m, n, b):
     assert _rel(_to_f64(y2), ref) < REL_TOL
 
 
+@pytest.mark.parametrize("b", [64, 130])
+def test_gemm_two_k_halves_sampled(q, dev, b):
+    """A layer large enough for the 16-wave GEMM (32 panel pairs per 64
+    columns: two K halves per workgroup, added in LDS) with a ragged K of
+    17 steps of 64 columns: the second split's second half has one live
+    step, whose last tile column is the layer's last.  Sampled batch columns
+    of the whole 8192-row output block against the oracle."""
+    import torch
+    m, n = 8192, 1040
+    host = synth.make_layer(synth.HYB, m, n, 3, tag="ksub")
+    x16 = synth.activations("ksubx", b, n)
+    _say("gemm two K halves", m, n, b)
+    lay = q.upload_layer(host, dev)
+    y = _to_f64(q.gemm(lay, _f16_tensor(x16, dev)))
+    torch.cuda.synchronize()
+    cols = [0, 63, b - 1]
+    ref = oracle.forward_block(host, x16, cols, 0)
+    assert _rel(y[cols], ref) < REL_TOL
+
+
 def test_gemm_full_size_sampled(q, dev):
     """70B-class up-projection, X 64 x 8192: sampled batch columns and
     output blocks against the oracle."""
