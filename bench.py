@@ -757,7 +757,33 @@ def measured_ceilings(torch, dev):
     e1.record()
     torch.cuda.synchronize()
     read_gbs = POOL_BYTES * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del rd, s
+    # the same read on the headline layer's scale: 4 MiB column sums, each
+    # call on the next 4 MiB of the pool (as the GEMV's code slices rotate),
+    # 200 back-to-back calls; and the floor of a two-kernel call: two
+    # one-workgroup fills of a 4 KiB tensor per iteration
+    small = POOL_BYTES // (4 << 20)
+    views = [rd[i * 1024:(i + 1) * 1024] for i in range(small)]
+    for r in range(20):
+        s = views[r % small].sum(0)
+    torch.cuda.synchronize()
+    e0.record()
+    for r in range(200):
+        s = views[r % small].sum(0)
+    e1.record()
+    torch.cuda.synchronize()
+    small_us = e0.elapsed_time(e1) * 1e3 / 200
+    tiny = torch.empty(1024, dtype=torch.float32, device=dev)
+    for r in range(20):
+        tiny.fill_(1.0)
+    torch.cuda.synchronize()
+    e0.record()
+    for r in range(200):
+        tiny.fill_(1.0)
+        tiny.fill_(2.0)
+    e1.record()
+    torch.cuda.synchronize()
+    pair_us = e0.elapsed_time(e1) * 1e3 / 200
+    del rd, s, views, tiny
     n = 8192
     a = torch.randn(n, n, dtype=torch.float16, device=dev)
     b = torch.randn(n, n, dtype=torch.float16, device=dev)
@@ -772,9 +798,13 @@ def measured_ceilings(torch, dev):
     mm_tf = 2 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
     del a, b, c
     torch.cuda.empty_cache()
-    log("measured ceilings: copy %.0f GB/s (read + write), read %.0f GB/s, fp16 matmul %d^3 %.0f TFLOP/s"
-        % (copy_gbs, read_gbs, n, mm_tf))
+    log("measured ceilings: copy %.0f GB/s (read + write), read %.0f GB/s, 4 MiB read %.2f us (%.0f GB/s), "
+        "two empty kernels %.2f us, fp16 matmul %d^3 %.0f TFLOP/s"
+        % (copy_gbs, read_gbs, small_us, (4 << 20) / (small_us * 1e-6) / 1e9, pair_us, n, mm_tf))
     return {"copy_GBps_read_plus_write": round(copy_gbs, 1), "read_GBps_colsum_1GiB": round(read_gbs, 1),
+            "read_4MiB_colsum_us": round(small_us, 2),
+            "read_4MiB_colsum_GBps": round((4 << 20) / (small_us * 1e-6) / 1e9, 1),
+            "two_tiny_kernels_us": round(pair_us, 2),
             "fp16_matmul_8192_TFLOPs": round(mm_tf, 1)}
 
 
