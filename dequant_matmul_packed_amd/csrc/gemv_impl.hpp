@@ -58,12 +58,23 @@ __host__ __device__ constexpr int gemv_table_words(int Q) {
        : CODE == LUT ? (1 << 15) : 0;   // LUT: 2^16 fp16 values, two per word
 }
 
+// The GEMV's NUQ table holds level pairs: with no trellis overlap (L = kV)
+// the indices of weights 2i and 2i + 1 are one 2k-bit field of the stream,
+// so entry e = (s0 << k) | s1 is (level s0, level s1), one lookup per pair,
+// in NUQ_PAIR_COPIES copies; the 2^k levels are staged after it.  (The group
+// scales multiply the pair sums afterwards, so the pairs stay plain levels.)
+constexpr int NUQ_PAIR_COPIES = 8;
+template <int CODE, int KV>
+__host__ __device__ constexpr int gemv_lut_words(int Q) {
+  return CODE == NUQ ? (1 << (2 * KV)) * NUQ_PAIR_COPIES + (1 << KV) : gemv_table_words<CODE, KV>(Q);
+}
+
 // LDS of one workgroup: region A (lookup table; also the scratch of the
 // input RHT, the wave reduction and the output RHT), then x' as fp16 pairs,
 // then (3INST) x' duplicated into (x, x) pairs.
 template <int CODE, int KV, int NB>
 __host__ __device__ inline size_t gemv_regA_bytes(int Q, int Kc, int U) {
-  size_t tab = (size_t)gemv_table_words<CODE, KV>(Q) * 4;
+  size_t tab = (size_t)gemv_lut_words<CODE, KV>(Q) * 4;
   size_t rht = (size_t)(GEMV_THREADS * 8 + NB * padded_words(Kc)) * 4;
   size_t red = (size_t)4 * 128 * NB * 4;
   (void)U;
@@ -223,7 +234,19 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   // e * COPIES + c).  The pure lookup (LUT) copies its 128 KiB as it is, in
   // rounds of 8 x 16 bytes per thread.
   auto fill_table = [&]() {
-    if constexpr (CODE == HYB || CODE == HYB1 || CODE == VQ || CODE == NUQ) {
+    if constexpr (CODE == NUQ) {
+      // the levels (lw[0] of threads below 2^k), then every pair from them
+      constexpr int NP = 1 << (2 * KV);
+      uint32_t* lv = regA + NP * NUQ_PAIR_COPIES;
+      if (tid < nlut) lv[tid] = lw[0];
+      __syncthreads();
+      for (int e = tid; e < NP; e += GEMV_THREADS) {
+        const uint32_t v = (lv[e >> KV] & 0xFFFFu) | (lv[e & ((1 << KV) - 1)] << 16);
+#pragma unroll
+        for (int c = 0; c < NUQ_PAIR_COPIES; ++c) regA[e * NUQ_PAIR_COPIES + c] = v;
+      }
+    }
+    if constexpr (CODE == HYB || CODE == HYB1 || CODE == VQ) {
       constexpr uint32_t FLIP = CODE == HYB ? 0x80008000u : 0x00008000u;
 #pragma unroll
       for (int i = 0; i < TW; ++i) {
@@ -440,7 +463,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   }
 
   // ---- 4. stream the tiles ------------------------------------------------
-  const uint32_t* tabc = regA + (lane & (COPIES - 1));
+  constexpr int TCOPIES = CODE == NUQ ? NUQ_PAIR_COPIES : COPIES;
+  const uint32_t* tabc = regA + (lane & (TCOPIES - 1));
   const int qshift = a.L.qshift;
   float acc[2][NB];
 #pragma unroll
@@ -539,9 +563,9 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
               for (int c = 0; c < NB; ++c) part[r][c] = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const uint32_t s0 = window_at<L>(w, (2 * i) * KX);
-              const uint32_t s1 = window_at<L>(w, (2 * i + 1) * KX);
-              const uint32_t pv = (regA[s0] & 0xFFFFu) | (regA[s1] << 16);
+              // the 2k-bit field of weights 2i, 2i + 1 indexes their level pair
+              const uint32_t e = window_at<2 * L>(w, (2 * i) * KX);
+              const uint32_t pv = tabc[e * NUQ_PAIR_COPIES];
 #pragma unroll
               for (int c = 0; c < NB; ++c)
                 part[i >> 3][c] = __builtin_amdgcn_fdot2(as_h2(pv), as_h2(xp[c][i & 7]),
