@@ -365,7 +365,7 @@ def test_gemv_wide_chunks_sampled(q, dev, n, b, k):
     (synth.MAD1, 2, 256, 256, 64), (synth.INST3, 4, 256, 256, 33), (synth.NUQ, 3, 256, 512, 64),
     (synth.VQ, 4, 256, 256, 64), (synth.HYB, 4, 1024, 1024, 64), (synth.NUQ, 2, 256, 512, 64),
     (synth.NUQ, 4, 384, 256, 40), (synth.VQ, 2, 256, 256, 64), (synth.VQ, 3, 128, 160, 64),
-    (synth.MAD1, 4, 256, 256, 64), (synth.INST3, 2, 256, 512, 64)])
+    (synth.MAD1, 4, 256, 256, 64), (synth.INST3, 2, 256, 512, 64), (synth.HYB, 2, 256, 256, 256)])
 def test_gemm_small_matches_oracle(q, dev, code, k, m, n, b):
     import torch
     _say("gemm small", synth.CODE_NAMES[code], k, m, n, b)
@@ -382,6 +382,24 @@ def test_gemm_small_matches_oracle(q, dev, code, k, m, n, b):
     y2 = q.gemm(lay, xt, ws=ws)
     torch.cuda.synchronize()
     assert _rel(_to_f64(y2), ref) < REL_TOL
+
+
+def test_gemm_two_k_halves_half_tcq_sampled(q, dev):
+    """A half-TCQ layer (rows [0, 4096) at kV = 5, [4096, 8192) at kV = 6)
+    large enough for two K halves per workgroup: each part is launched with
+    the whole layer's K split and halves, writing its rows of the shared
+    slices.  Sampled batch columns of the output block against the oracle."""
+    import torch
+    m, n, b = 8192, 1040, 64
+    host = synth.make_layer(synth.HYB, m, n, 0, kv=5, kv_b=6, m_a=4096, tag="ksubhalf")
+    x16 = synth.activations("ksubhalfx", b, n)
+    _say("gemm two K halves, half-TCQ", m, n, b)
+    lay = q.upload_layer(host, dev)
+    y = _to_f64(q.gemm(lay, _f16_tensor(x16, dev)))
+    torch.cuda.synchronize()
+    cols = [0, 37, b - 1]
+    ref = oracle.forward_block(host, x16, cols, 0)
+    assert _rel(y[cols], ref) < REL_TOL
 
 
 @pytest.mark.parametrize("b", [64, 130])
