@@ -1,25 +1,27 @@
 // Batched decode-and-multiply (qdec_gemm): decoded weights feed fp16 MFMA
 // (v_mfma_f32_16x16x32_f16) with fp32 accumulation.
 //
-// A workgroup (8 waves) owns two panels of 128 output rows and 64 batch
+// A workgroup of 8 waves owns two panels of 128 output rows and 64 batch
 // columns and steps through K 64 input columns (4 tile columns) at a time.
 // Wave w owns tile rows 2(w%4), 2(w%4)+1 of panel w/4 of the pair; per step
-// it decodes the 8
-// tiles (2 tile rows x 4 tile columns) with the same 8-lanes-per-tile layout
-// as the GEMV: lane q of tile t holds 32 weights, rows 2q and 2q+1 of the
-// tile, as four 8-weight chunks of one row each.  Placing tile t at
-// (tile row t % 2, tile column t / 2) makes lanes l, l+16, l+32, l+48 hold
-// the same weight row at four different k offsets -- exactly the shape of an
-// MFMA A fragment (lane l: row l % 16, k 8*(l/16) .. +8) under a fixed row
-// permutation.  So chunk a of every lane is an A operand as decoded: the
+// it decodes its 8 tiles (2 tile rows x 4 tile columns) with the same
+// 8-lanes-per-tile layout as the GEMV: lane q of tile t holds 32 weights,
+// rows 2q and 2q+1 of the tile, as four 8-weight chunks of one row each.
+// Placing tile t at (tile row t % 2, tile column t / 2) makes lanes l, l+16,
+// l+32, l+48 hold the same weight row at four different k offsets -- the
+// shape of an MFMA A fragment (lane l: row l % 16, k 8*(l/16) .. +8) under a
+// fixed row permutation.  So every chunk is an A operand as decoded: the
 // weights go from the code registers to the matrix cores without touching
 // LDS.  The transformed activations X' (the B operand) are staged once per
 // step in LDS (double buffered, 16-byte chunks XOR-swizzled by row) and read
-// as fragments by the eight waves; the lookup table of HYB/VQ/NUQ also
-// lives in LDS, one per workgroup, so the two panels share it (and its 16
-// copies: a table per panel left room for half as many).  The loop is software-pipelined: the code words of step i+2 and
-// the X' chunk of step i+2 are in flight while step i is decoded and
-// multiplied.
+// as fragments by every wave.  The lookup table of HYB/VQ/NUQ lives in LDS
+// too, one per workgroup: the two panels share it, which leaves room for 16
+// copies (a table per panel left room for half as many).
+//
+// The loop is software-pipelined: while step s is multiplied and step s+1
+// decoded, the code words of steps s+2 .. s+5 and the X' of steps s+2 and
+// s+3 are in flight.  With KSUB = 2 the workgroup holds two such 8-wave
+// groups, each over one half of the K split's steps (see below).
 #include "gemv_impl.hpp"
 #include "qdec_device.hpp"
 #include "qdec_internal.hpp"

@@ -11,11 +11,13 @@ Each counter (KiB per dispatch) is scaled by what it reads for the bench's
 plain device-to-device copy of 256 MiB (bytes read and written are known), so
 the figures are HBM bytes.  Writes profiles/gemv_hbm_traffic.md and
 profiles/gemv_hbm_traffic.json; the JSON carries a hash of the kernel sources
-so the bench reports the traffic only while the kernels are unchanged.
+(comments and blank lines left out) so the bench reports the traffic only
+while the kernels are unchanged.
 """
 import hashlib
 import json
 import os
+import re
 import sqlite3
 import sys
 
@@ -25,13 +27,21 @@ COPY_MIB = 256
 CODES = {1: "HYB", 2: "1MAD", 3: "3INST", 4: "NUQ", 5: "VQ"}
 
 
-def kernel_source_hash() -> str:
+def code_only(text: str) -> str:
+    """The source without comments, trailing spaces and blank lines: what the
+    compiler sees (a comment edit does not change the profiled kernels)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
+def kernel_source_hash(csrc: str = CSRC) -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".hpp", ".h")):
             h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
