@@ -92,7 +92,7 @@ def main():
             name, codes / 2 ** 20, fb / 2 ** 20, wb / 1024, (fin_f + fin_w) / 1024, total / algo))
     lines += ["", "The decode kernel's writes are its split-K fp32 atomic adds (each reaches HBM as its own",
               "4-byte write); the reads are the packed codes plus x, signs and the tables.",
-              "Kernel source hash: `%s`." % out["kernel_source_hash"]]
+              "Kernel source hash (comments and blank lines left out): `%s`." % out["kernel_source_hash"]]
     with open(os.path.join(ROOT, "profiles", "gemv_hbm_traffic.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     with open(os.path.join(ROOT, "profiles", "gemv_hbm_traffic.json"), "w") as f:
