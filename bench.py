@@ -305,6 +305,7 @@ def main():
         detail.update(bench_encoder(q, torch, dev, cpu=not args.no_cpu_baseline))
 
     if not args.no_detail and not args.only:
+        detail["pages_context"] = pages_context()
         ceil = measured_ceilings(torch, dev)
         detail["measured_ceilings"] = ceil
         g = detail.get("gemm_b64_up70b")
@@ -727,6 +728,31 @@ def cpu_per_config():
     return {"threads": threads, "configs": out,
             "note": "the oracle is a plain correctness reference (bit-serial walk, O(B^2) Hadamard), "
                     "not a tuned CPU implementation"}
+
+
+def pages_context():
+    """The pages' own decode-cost figures, beside the VALU lane-instructions
+    per weight measured on this chip (read from the committed SQ-counter
+    summaries; a GEMV counts decode plus one v_dot2 per weight pair, a GEMM
+    the decode alone)."""
+    out = {"pages": {"hyb_int32_ops_per_weight": "~2 (LUT decompress 0.5 + trellis unpack and index ~1.5)",
+                     "e8p_int32_ops_per_weight": "~3 (QuIP# E8P, the pages' comparator)",
+                     "hardware": "NVIDIA GPUs, as stated on the pages",
+                     "source": "QTIP OpenReview discussion, untitled ALU-op comment"},
+           "measured_valu_per_weight": {}}
+    for name, path in (("gemv_hyb_k2_b1_28672x8192", "sq_counters_gemv_hyb_28672x8192_b1.md"),
+                       ("gemm_hyb_k3_b64_28672x8192", "sq_counters_gemm_hyb_28672x8192_b64.md")):
+        f = os.path.join(ROOT, "profiles", path)
+        if not os.path.exists(f):
+            continue
+        with open(f) as fh:
+            for line in fh:
+                cells = [c.strip() for c in line.split("|")]
+                if len(cells) > 11 and cells[1].startswith("`qdec::gem") and cells[10]:
+                    out["measured_valu_per_weight"][name] = float(cells[10])
+                    break
+    out["measured_source"] = "profiles/sq_counters_*.md (SQ_INSTS_VALU x 64 / weights)"
+    return out
 
 
 def measured_ceilings(torch, dev):
