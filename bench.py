@@ -66,11 +66,15 @@ def log(*a):
 
 
 class Launch:
-    """One pre-marshalled C call: avoids per-call Python work in timed loops."""
+    """One pre-marshalled C call: avoids per-call Python work in timed loops.
+    It holds the layer and the tensors whose device pointers it passes, so
+    their memory cannot be freed (and, by torch.cuda.empty_cache, which every
+    graph capture calls, unmapped) while the call can still run."""
 
     def __init__(self, q, fn, layer, x, y, b, ws, stream):
         import ctypes
         self.fn = getattr(q._lib, fn)
+        self.keep = (layer, x, y, ws)
         self.args = (ctypes.byref(layer.desc()), x.data_ptr(), y.data_ptr(), b, ws.data_ptr(),
                      ws.numel(), stream)
 
