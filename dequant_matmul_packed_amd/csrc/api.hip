@@ -168,12 +168,26 @@ int status_of(hipError_t e) {
 }  // namespace
 
 namespace qdec {
+// Batch columns per workgroup of the batched path: 16 up to 16 columns (a
+// quarter of the X' staging, B-fragment reads and MFMAs of a 64-column
+// tile), else 64.  Tuning override QDEC_GEMM_NBT = 16 / 64.
+int gemm_batch_tile(int64_t b) {
+  static int forced = -1;
+  if (forced < 0) {
+    const char* ev = getenv("QDEC_GEMM_NBT");
+    forced = ev ? atoi(ev) : 0;
+    if (forced != 16 && forced != 64) forced = 0;
+  }
+  if (forced) return forced;
+  return b <= 16 ? 16 : 64;
+}
+
 // K halves per workgroup of the batched path: 2 (a 16-wave workgroup, one
 // per CU, adding its halves in LDS: half as many K-split slices to write and
 // to sum) where the panel pairs alone come near filling the chip -- at least
-// 32 per 64 batch columns -- and each half still gets 8 steps of 64 columns;
-// else 1 (8-wave workgroups, two per CU).  Tuning override
-// QDEC_GEMM_KSUB = 1 / 2.
+// 32 per batch tile -- and each half still gets 8 steps of 64 columns; else
+// 1 (8-wave workgroups, two per CU).  Only the 64-column tile is built with
+// two halves.  Tuning override QDEC_GEMM_KSUB = 1 / 2.
 int gemm_ksub(int64_t m, int64_t n, int64_t b) {
   static int forced = -1;
   if (forced < 0) {
@@ -181,8 +195,10 @@ int gemm_ksub(int64_t m, int64_t n, int64_t b) {
     forced = ev ? atoi(ev) : 0;
     if (forced != 1 && forced != 2) forced = 0;
   }
+  const int64_t tile = gemm_batch_tile(b);
+  if (tile != 64) return 1;
   if (forced) return forced;
-  const int64_t groups = (m / 128 + GEMM_PANELS - 1) / GEMM_PANELS, nbt = (b + 63) / 64;
+  const int64_t groups = (m / 128 + GEMM_PANELS - 1) / GEMM_PANELS, nbt = (b + tile - 1) / tile;
   const int64_t niter = (n / 16 + 3) / 4;
   return (groups * nbt >= 32 && niter >= 16) ? 2 : 1;
 }
@@ -197,7 +213,8 @@ int gemm_ksplit(int64_t m, int64_t n, int64_t b) {
     forced = ev ? atoi(ev) : 0;
     if (forced > 16) forced = 16;
   }
-  const int64_t groups = (m / 128 + GEMM_PANELS - 1) / GEMM_PANELS, nbt = (b + 63) / 64;
+  const int64_t tile = gemm_batch_tile(b);
+  const int64_t groups = (m / 128 + GEMM_PANELS - 1) / GEMM_PANELS, nbt = (b + tile - 1) / tile;
   const int64_t niter = (n / 16 + 3) / 4;
   const int ksub = gemm_ksub(m, n, b);
   const int64_t slots = 256 * (ksub == 2 ? 1 : GEMM_WG_PER_CU);
@@ -207,6 +224,32 @@ int gemm_ksplit(int64_t m, int64_t n, int64_t b) {
   if (ks > 16) ks = 16;
   if (ks < 1) ks = 1;
   return (int)ks;
+}
+
+// Whether qdec_gemv runs a product of 4 to 8 columns on the batched MFMA
+// path (input RHT, gemm_kernel with 16-column tiles, output RHT): once the
+// GEMV's per-column dot products (one v_dot2 per weight pair and column)
+// outweigh the batched path's fixed costs, measured at b * m * n >= 4e8
+// (14336x4096 and 4096x14336 from 8 columns, 28672x4096 from 4).  Tuning
+// override QDEC_GEMV_MFMA = 0 / 1 (1: every call of 2 or more columns).
+bool gemv_via_gemm(int64_t m, int64_t n, int64_t b) {
+  static int forced = -2;
+  if (forced == -2) {
+    const char* e = getenv("QDEC_GEMV_MFMA");
+    forced = e ? (atoi(e) != 0) : -1;
+  }
+  if (b < 2) return false;
+  if (forced >= 0) return forced != 0;
+  return b >= 4 && (double)b * (double)m * (double)n >= 4e8;
+}
+
+// Workspace of qdec_gemv: the GEMV's accumulator and x' slot, then (on the
+// MFMA path) the K-split slices, after the accumulator so that it stays
+// zero for later calls of other batches on the same workspace.
+size_t gemv_ws_bytes(int64_t m, int64_t n, int64_t b) {
+  const size_t base = gemv_ws_layout(m, n, b).total;
+  if (!gemv_via_gemm(m, n, b)) return base;
+  return base + align256((size_t)(gemm_ksplit(m, n, b) * b * m) * 4);
 }
 
 // Whether a one-column GEMV takes the separate input transform: every
@@ -272,7 +315,7 @@ size_t qdec_workspace_bytes(const qdec_layer* layer, int64_t batch, int32_t op) 
   if (check_layer(layer, &L) != QDEC_OK) return 0;
   if (op == QDEC_OP_GEMV) {
     if (batch < 1 || batch > 8) return 0;
-    return gemv_ws_layout(L.m, L.n, batch).total;
+    return gemv_ws_bytes(L.m, L.n, batch);
   }
   if (op == QDEC_OP_GEMM) {
     if (batch < 1 || batch > 256) return 0;
@@ -315,6 +358,9 @@ int qdec_rht(const void* in, int32_t in_dtype, void* out, int32_t out_dtype, int
   return status_of(launch_rht(a, (hipStream_t)stream));
 }
 
+static int run_batched(const LayerArgs& L, const LayerParts& parts, const uint16_t* x, uint16_t* y,
+                       int64_t batch, uint16_t* xr, float* z, hipStream_t s);
+
 int qdec_gemv(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t batch, void* ws,
               size_t ws_bytes, void* stream) {
   LayerArgs L;
@@ -327,12 +373,15 @@ int qdec_gemv(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
   if (overlap(x, (size_t)(batch * L.n) * 2, y, (size_t)(batch * L.m) * 2)) return QDEC_EINVAL;
   const int Kc = gemv_chunk(L.m, L.n, batch);
   const GemvWs wl = gemv_ws_layout(L.m, L.n, batch);
-  const size_t need = wl.total;
+  const size_t need = gemv_ws_bytes(L.m, L.n, batch);
   if (!ws || !aligned(ws, 256) || ws_bytes < need) return QDEC_EWORKSPACE;
   if (overlap(ws, need, x, (size_t)(batch * L.n) * 2) || overlap(ws, need, y, (size_t)(batch * L.m) * 2))
     return QDEC_EINVAL;
   const int d = check_device();
   if (d) return d;
+  if (gemv_via_gemm(L.m, L.n, batch))
+    return run_batched(L, parts, x, y, batch, (uint16_t*)((char*)ws + wl.xr),
+                       (float*)((char*)ws + wl.total), (hipStream_t)stream);
   GemvArgs a;
   a.L = L;
   a.x = x;
@@ -410,9 +459,14 @@ int qdec_gemm(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
     return QDEC_EINVAL;
   const int d = check_device();
   if (d) return d;
-  hipStream_t s = (hipStream_t)stream;
-  uint16_t* xr = (uint16_t*)ws;
-  float* z = (float*)((char*)ws + align256((size_t)(batch * L.n) * 2));
+  return run_batched(L, parts, x, y, batch, (uint16_t*)ws,
+                     (float*)((char*)ws + align256((size_t)(batch * L.n) * 2)), (hipStream_t)stream);
+}
+
+// The batched path: X' = RHT_in(X) into xr, the K-split partial sums into
+// z, then Y = RHT_out(sum of the slices).
+static int run_batched(const LayerArgs& L, const LayerParts& parts, const uint16_t* x, uint16_t* y,
+                       int64_t batch, uint16_t* xr, float* z, hipStream_t s) {
   // 1. X' = RHT_in(X), fp16
   RhtArgs r;
   r.in = x;
@@ -436,6 +490,7 @@ int qdec_gemm(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
   const int64_t ks = gemm_ksplit(L.m, L.n, batch);
   g.ksplit = (int)ks;
   g.ksub = gemm_ksub(L.m, L.n, batch);
+  g.nbt = gemm_batch_tile(batch);
   for (int p = 0; p < parts.count; ++p) {   // each row part writes its rows of every slice
     g.L = parts.part[p];
     g.row0 = parts.row0[p];

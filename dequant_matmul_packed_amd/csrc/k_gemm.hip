@@ -1,8 +1,9 @@
 // Batched decode-and-multiply (qdec_gemm): decoded weights feed fp16 MFMA
 // (v_mfma_f32_16x16x32_f16) with fp32 accumulation.
 //
-// A workgroup of 8 waves owns two panels of 128 output rows and 64 batch
-// columns and steps through K 64 input columns (4 tile columns) at a time.
+// A workgroup of 8 waves owns two panels of 128 output rows and NBT = 64
+// batch columns (16 for small batches) and steps through K 64 input columns
+// (4 tile columns) at a time.
 // Wave w owns tile rows 2(w%4), 2(w%4)+1 of panel w/4 of the pair; per step
 // it decodes its 8 tiles (2 tile rows x 4 tile columns) with the same
 // 8-lanes-per-tile layout as the GEMV: lane q of tile t holds 32 weights,
@@ -34,7 +35,7 @@ namespace qdec {
 // the chip with one such workgroup per CU writes half as many K-split
 // slices (and the output transform reads half as many).
 constexpr int GEMM_SUB_THREADS = 64 * GEMM_WAVES;
-static_assert(GEMM_SUB_THREADS == 512, "one 16-byte X' chunk per thread and step (64 batch rows x 8 chunks)");
+static_assert(GEMM_SUB_THREADS == 512, "at most one 16-byte X' chunk per thread and step (64 batch rows x 8 chunks)");
 
 // LDS table copies: lane l reads copy l % COPIES.  HYB and VQ tables take
 // GEMM_COPIES copies while two workgroups still fit a CU, else 8 (HYB with
@@ -52,26 +53,28 @@ __device__ __forceinline__ int gemm_swz(int r, int k) {
   return r * 128 + ((((k >> 3) ^ (r & 7)) << 4) | ((k & 7) << 1));
 }
 
-// LDS: lookup table, then B[KSUB][2][64 batch][64 k] fp16 (double
+// LDS: lookup table, then B[KSUB][2][NBT batch][64 k] fp16 (double
 // buffered per K half); with KSUB = 2 the space is reused at the end for the
-// second half's sums (8 waves x 32 values x 64 lanes fp32).
+// second half's sums (8 waves x 2 NBT / 4 values x 64 lanes fp32).
 template <int CODE, int KV, int COPIES>
 __host__ __device__ inline size_t gemm_table_bytes(int Q) {
   return ((size_t)gemm_table_words<CODE, KV, COPIES>(Q) * 4 + 15) & ~(size_t)15;
 }
-template <int CODE, int KV, int COPIES, int KSUB>
+template <int CODE, int KV, int COPIES, int KSUB, int NBT>
 __host__ __device__ inline size_t gemm_lds_bytes(int Q) {
-  const size_t main = gemm_table_bytes<CODE, KV, COPIES>(Q) + (size_t)KSUB * 2 * (64 * 128);
-  const size_t red = KSUB > 1 ? (size_t)GEMM_WAVES * 32 * 64 * 4 : 0;
+  const size_t main = gemm_table_bytes<CODE, KV, COPIES>(Q) + (size_t)KSUB * 2 * (NBT * 128);
+  const size_t red = KSUB > 1 ? (size_t)GEMM_WAVES * (NBT / 2) * 64 * 4 : 0;
   return main > red ? main : red;
 }
 
 // Four waves per SIMD (at most 128 VGPRs): two 8-wave workgroups or one of
 // 16 waves per CU; the pure lookup's 128 KiB table leaves room for one
 // 8-wave workgroup, so it may use twice as many.
-template <int CODE, int KV, int COPIES, int KSUB>
+template <int CODE, int KV, int COPIES, int KSUB, int NBT>
 __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void gemm_kernel(GemmArgs a) {
+  static_assert(NBT == 16 || NBT == 64, "batch tile of 16 or 64 columns");
   constexpr int GEMM_THREADS = GEMM_SUB_THREADS * KSUB;
+  constexpr int NB4 = NBT / 16;                      // 16-column MFMA blocks
   using G = LaneGeom<CODE, KV>;
   constexpr int NW = G::NW;
   extern __shared__ __align__(16) uint32_t smem[];
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void 
   const int wv = wvall % GEMM_WAVES;                 // wave within its 8-wave group
   const int stid = tid % GEMM_SUB_THREADS;           // thread within its group
   const int wave = wv & 3;                           // wave within its panel
-  char* Bs = reinterpret_cast<char*>(smem) + gemm_table_bytes<CODE, KV, COPIES>(a.L.Q) + ksub * 2 * (64 * 128);
+  char* Bs = reinterpret_cast<char*>(smem) + gemm_table_bytes<CODE, KV, COPIES>(a.L.Q) + ksub * 2 * (NBT * 128);
   const int q = lane & 7, t = lane >> 3;           // tile t of the wave, lane q in it
   const int tr = t & 1, tc = t >> 1;                 // tile row / column within the step
   const int64_t m = a.L.m, n = a.L.n;
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void 
   const int panel = (blockIdx.x % ngroups) * GEMM_PANELS + (wv >> 2);
   const bool panel_ok = panel < npanels;             // wave-uniform: the last group may be short
   const int split = blockIdx.x / ngroups;
-  const int n0 = blockIdx.y * 64;
+  const int n0 = blockIdx.y * NBT;
   const int ntc = (int)(n >> 4);                    // tile columns (steps of 4)
   const int niter = (ntc + 3) >> 2;
   // steps per K split, a multiple of 4 (the loop's unroll) where possible;
@@ -144,24 +147,27 @@ __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void 
     }
   };
   // X' chunk of this thread: batch row n0 + (stid >> 3), k chunk stid & 7;
-  // chunk ch of step it is column 64 it + 8 ch
+  // chunk ch of step it is column 64 it + 8 ch.  A 16-row tile has 128
+  // chunks: the group's waves 2 .. 7 stage nothing.
+  const bool xmine = stid < NBT * 8;                 // wave-uniform
   const auto xrs = make_rsrc(a.xr, (uint32_t)(a.b * n * 2));
   const int xrow = n0 + (stid >> 3), xch = stid & 7;
   const int xlim = (int)((n - xch * 8 + 63) >> 6);
-  const int itx = xrow < a.b ? (xlim < it1 ? xlim : it1) : 0;
+  const int itx = (xmine && xrow < a.b) ? (xlim < it1 ? xlim : it1) : 0;
   const uint32_t xbase = (uint32_t)(((int64_t)(xrow < a.b ? xrow : 0) * n + xch * 8) * 2);
   auto load_x = [&](int it, uint4& xv) {
     xv = buf_load_u4(xrs, it < itx ? xbase + (uint32_t)it * 128u : BUF_OFF);
   };
   auto store_x = [&](const uint4& xv, int buf) {
-    *reinterpret_cast<uint4*>(Bs + buf * (64 * 128) + gemm_swz(stid >> 3, xch * 8)) = xv;
+    if (!xmine) return;
+    *reinterpret_cast<uint4*>(Bs + buf * (NBT * 128) + gemm_swz(stid >> 3, xch * 8)) = xv;
   };
 
-  float4v acc[2][4];
+  float4v acc[2][NB4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NB4; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
 
   // Decode step `it` (the lane's 32 weights) into the four A operands:
   // operand 2*ra + h is the chunk (tile row 2q + ra, columns 8h .. 8h+7).
@@ -187,15 +193,15 @@ __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void 
 #pragma unroll
     for (int j = 0; j < 4; ++j) A[j] = make_uint4(out[4 * j], out[4 * j + 1], out[4 * j + 2], out[4 * j + 3]);
   };
-  // B fragments of the step in LDS buffer `buf`, then the 16 MFMAs: the B
-  // operand for column half h holds X'[batch][16*(l/16) + 8h .. +8].
+  // B fragments of the step in LDS buffer `buf`, then the 4 NB4 MFMAs: the
+  // B operand for column half h holds X'[batch][16*(l/16) + 8h .. +8].
   auto mma = [&](const uint4* A, int buf) {
-    const char* Bt = Bs + buf * (64 * 128);
-    half8v bf[2][4];
+    const char* Bt = Bs + buf * (NBT * 128);
+    half8v bf[2][NB4];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < NB4; ++nb)
         bf[h][nb] = *reinterpret_cast<const half8v*>(Bt + gemm_swz(nb * 16 + (lane & 15), 16 * (lane >> 4) + 8 * h));
 #pragma unroll
     for (int ra = 0; ra < 2; ++ra)
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void 
       for (int h = 0; h < 2; ++h) {
         const half8v af = __builtin_bit_cast(half8v, A[2 * ra + h]);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < NB4; ++nb)
           acc[ra][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[h][nb], acc[ra][nb], 0, 0, 0);
       }
   };
@@ -253,29 +259,29 @@ __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void 
   // (the table and X' are dead by then).  Each K split writes its own slice
   // of the workspace (no atomics); the output-RHT kernel sums the slices.
   if constexpr (KSUB > 1) {
-    float* red = reinterpret_cast<float*>(smem) + (wv * 32) * 64 + lane;
+    float* red = reinterpret_cast<float*>(smem) + (wv * (8 * NB4)) * 64 + lane;
     __syncthreads();
     if (ksub == 1) {
 #pragma unroll
       for (int ra = 0; ra < 2; ++ra)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < NB4; ++nb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) red[((ra * 4 + nb) * 4 + e) * 64] = acc[ra][nb][e];
+          for (int e = 0; e < 4; ++e) red[((ra * NB4 + nb) * 4 + e) * 64] = acc[ra][nb][e];
     }
     __syncthreads();
     if (ksub == 1) return;
 #pragma unroll
     for (int ra = 0; ra < 2; ++ra)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < NB4; ++nb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[ra][nb][e] += red[((ra * 4 + nb) * 4 + e) * 64];
+        for (int e = 0; e < 4; ++e) acc[ra][nb][e] += red[((ra * NB4 + nb) * 4 + e) * 64];
   }
   if (!panel_ok) return;
   float* zs = a.z + (int64_t)split * a.b * a.mz;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < NB4; ++nb) {
     const int bb = n0 + nb * 16 + (lane & 15);
     if (bb >= a.b) continue;
     float* zrow = zs + (int64_t)bb * a.mz + a.row0 + (int64_t)panel * 128 + 32 * wave;
@@ -288,28 +294,32 @@ __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void 
   }
 }
 
-template <int CODE, int KV, int COPIES, int KSUB>
+template <int CODE, int KV, int COPIES, int KSUB, int NBT>
 static hipError_t launch_gemm_k(const GemmArgs& a, hipStream_t stream) {
-  const size_t lds = gemm_lds_bytes<CODE, KV, COPIES, KSUB>(a.L.Q);
+  const size_t lds = gemm_lds_bytes<CODE, KV, COPIES, KSUB, NBT>(a.L.Q);
   static size_t have = 0;
   const hipError_t e =
-      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_kernel<CODE, KV, COPIES, KSUB>), lds, &have);
+      ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_kernel<CODE, KV, COPIES, KSUB, NBT>), lds, &have);
   if (e != hipSuccess) return e;
   const int64_t ngroups = (a.L.m / 128 + GEMM_PANELS - 1) / GEMM_PANELS;
-  dim3 grid((unsigned)(ngroups * a.ksplit), (unsigned)((a.b + 63) / 64));
-  hipLaunchKernelGGL((gemm_kernel<CODE, KV, COPIES, KSUB>), grid, dim3(GEMM_SUB_THREADS * KSUB), lds, stream, a);
+  dim3 grid((unsigned)(ngroups * a.ksplit), (unsigned)((a.b + NBT - 1) / NBT));
+  hipLaunchKernelGGL((gemm_kernel<CODE, KV, COPIES, KSUB, NBT>), grid, dim3(GEMM_SUB_THREADS * KSUB), lds, stream,
+                     a);
   return hipGetLastError();
 }
+// built: 64-column tiles with one or two K halves, 16-column tiles with one
 template <int CODE, int KV, int COPIES>
 static hipError_t launch_gemm_c(const GemmArgs& a, hipStream_t stream) {
-  if (a.ksub == 2) return launch_gemm_k<CODE, KV, COPIES, 2>(a, stream);
-  return launch_gemm_k<CODE, KV, COPIES, 1>(a, stream);
+  if (a.nbt == 16) return a.ksub == 1 ? launch_gemm_k<CODE, KV, COPIES, 1, 16>(a, stream) : hipErrorInvalidValue;
+  if (a.nbt != 64) return hipErrorInvalidValue;
+  if (a.ksub == 2) return launch_gemm_k<CODE, KV, COPIES, 2, 64>(a, stream);
+  return launch_gemm_k<CODE, KV, COPIES, 1, 64>(a, stream);
 }
 
 template <int CODE, int KV>
 static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t stream) {
   if constexpr (gemm_tabled(CODE)) {
-    if (gemm_lds_bytes<CODE, KV, GEMM_COPIES, 1>(a.L.Q) <= GEMM_LDS_BYTES / GEMM_WG_PER_CU)
+    if (gemm_lds_bytes<CODE, KV, GEMM_COPIES, 1, 64>(a.L.Q) <= GEMM_LDS_BYTES / GEMM_WG_PER_CU)
       return launch_gemm_c<CODE, KV, GEMM_COPIES>(a, stream);
     return launch_gemm_c<CODE, KV, 8>(a, stream);
   } else {

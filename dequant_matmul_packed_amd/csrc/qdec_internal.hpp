@@ -79,6 +79,7 @@ struct GemmArgs {
   int b;
   int ksplit;          // K split factor
   int ksub;            // K halves per workgroup (1 or 2, gemm_ksub)
+  int nbt;             // batch columns per workgroup: 16 or 64 (gemm_batch_tile)
 };
 
 // The encoder: one part of a layer, its targets and its output codes.
@@ -94,9 +95,13 @@ struct EncodeArgs {
 constexpr int ENCODE_GRID = 256;
 inline size_t encode_ws_bytes(int V) { return (size_t)ENCODE_GRID * (256 / V) * 1024 * 4; }
 
-// Workspace layout of qdec_gemv: the fp32 accumulator z [b][m] (must start
-// at zero; left zero), then the fp16 x' [b][n] of the separate-RHT path.
+// Workspace layout of qdec_gemv: the fp32 accumulator z (must start at zero;
+// left zero), sized for the largest batch (8 columns) whatever the call's
+// batch, so that no call's scratch (x', K-split slices) lands where a call of
+// another batch expects zeros; then the fp16 x' [b][n] of the separate-RHT
+// path.
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+constexpr int GEMV_MAX_BATCH = 8;
 inline int gemv_unit_rows(int had_out) { return had_out > 128 ? had_out : 128; }
 // Input-chunk width of the fused GEMV: about two (panel, chunk) workgroups
 // per CU, chunks a power of two in [64, 2048].
@@ -107,7 +112,7 @@ struct GemvWs {
 inline GemvWs gemv_ws_layout(int64_t m, int64_t n, int64_t b) {
   GemvWs l;
   l.z = 0;
-  l.xr = align256((size_t)(b * m) * 4);
+  l.xr = align256((size_t)(GEMV_MAX_BATCH * m) * 4);
   l.total = l.xr + align256((size_t)(b * n) * 2);
   return l;
 }
@@ -122,6 +127,7 @@ constexpr int GEMM_PANELS = GEMM_WAVES / 4;
 constexpr int GEMM_COPIES = 16;
 constexpr int GEMM_WG_PER_CU = 2;
 constexpr size_t GEMM_LDS_BYTES = 160 * 1024;      // LDS of one CU
+int gemm_batch_tile(int64_t b);
 int gemm_ksub(int64_t m, int64_t n, int64_t b);
 int gemm_ksplit(int64_t m, int64_t n, int64_t b);
 inline size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t b) {

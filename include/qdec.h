@@ -186,9 +186,12 @@ int qdec_rht(const void *in, int32_t in_dtype, void *out, int32_t out_dtype,
  * in/out, fp32 accumulation.  One kernel decodes and multiplies (at one
  * batch column it also applies the input transform), a second applies the
  * output transform; with more batch columns the input transform runs first
- * in a kernel of its own.  ws: qdec_workspace_bytes(layer, batch,
- * QDEC_OP_GEMV) bytes, 256-byte aligned, zero-filled before first use (left
- * zeroed).                                                                   */
+ * in a kernel of its own.  From 4 batch columns on a large layer
+ * (batch * m * n >= 4e8) the call runs the batched path of qdec_gemm
+ * instead, whose MFMAs then cost less than per-column dot products.
+ * ws: qdec_workspace_bytes(layer, batch, QDEC_OP_GEMV) bytes, 256-byte
+ * aligned, zero-filled before first use (left zeroed).  A workspace sized
+ * for a batch serves every smaller batch of the same layer.                 */
 int qdec_gemv(const qdec_layer *layer, const uint16_t *x, uint16_t *y,
               int64_t batch, void *ws, size_t ws_bytes, void *stream);
 

@@ -51,9 +51,13 @@ def _layer(q, **kw):
 def test_workspace_sizes(q):
     lay = _layer(q)
     gv = q.qdec_workspace_bytes(lay, 1, q.QDEC_OP_GEMV)
-    # fp32 accumulator b x m, then fp16 x' b x n; each 256-byte aligned
-    assert gv == 1 * 256 * 4 + 1 * 128 * 2
+    # fp32 accumulator 8 x m (the largest batch, whatever the call's), then
+    # fp16 x' b x n; each 256-byte aligned
+    assert gv == 8 * 256 * 4 + 1 * 128 * 2
     assert q.qdec_workspace_bytes(lay, 8, q.QDEC_OP_GEMV) == 8 * 256 * 4 + 8 * 128 * 2
+    # a workspace for a batch covers every smaller one
+    sizes = [q.qdec_workspace_bytes(lay, b, q.QDEC_OP_GEMV) for b in range(1, 9)]
+    assert sizes == sorted(sizes)
     gm = q.qdec_workspace_bytes(lay, 64, q.QDEC_OP_GEMM)
     # X' (b x n fp16), then one fp32 b x m slice per K split (here 2: n/64)
     assert gm == 64 * 128 * 2 + 2 * 64 * 256 * 4

@@ -223,11 +223,12 @@ def test_hyb1_and_lut_codes(q, dev, code, V, Q, k):
             y = q.gemv(lay, _f16_tensor(x16, dev))
             torch.cuda.synchronize()
             assert _rel(_to_f64(y), oracle.forward(host, x16)) < REL_TOL, (m, n, b)
-        _say("new code gemm")
-        x16 = synth.activations("ncx64_%d" % n, 70, n)
-        y = q.gemm(lay, _f16_tensor(x16, dev))
-        torch.cuda.synchronize()
-        assert _rel(_to_f64(y), oracle.forward(host, x16)) < REL_TOL, (m, n)
+        for b in (70, 9):    # 64- and 16-column batch tiles
+            _say("new code gemm", b)
+            x16 = synth.activations("ncx64_%d" % n, b, n)
+            y = q.gemm(lay, _f16_tensor(x16, dev))
+            torch.cuda.synchronize()
+            assert _rel(_to_f64(y), oracle.forward(host, x16)) < REL_TOL, (m, n, b)
 
 
 @pytest.mark.parametrize("code,V,Q", [(synth.HYB, 1, 6), (synth.LUT, None, 9)])
@@ -276,6 +277,62 @@ def test_gemv_edge_cases(q, dev):
     for yy in ys:
         assert _rel(_to_f64(yy), ref) < REL_TOL
     assert torch.count_nonzero(ws[:2 * m * 4]).item() == 0
+
+
+def test_gemv_mixed_batches_one_workspace(q, dev):
+    """One workspace sized for 8 columns serves calls of every batch in any
+    order: on a 14336x4096 layer 8 columns take the batched MFMA path
+    (8 * m * n >= 4e8) and 1-3 columns the fused GEMV, whose accumulator
+    must stay zero across the others' scratch."""
+    import torch
+    m, n = 14336, 4096
+    host = synth.make_layer(synth.HYB, m, n, 2, tag="mixws")
+    lay = q.upload_layer(host, dev)
+    ws = q.workspace(lay, 8, q.QDEC_OP_GEMV, dev)
+    x16 = synth.activations("mixwsx", 8, n)
+    xt = _f16_tensor(x16, dev)
+    last = m // host.had_out - 1
+    for b in (8, 3, 1, 8, 2, 8, 1):
+        _say("gemv mixed batches", b)
+        y = _to_f64(q.gemv(lay, xt[:b], ws=ws))
+        torch.cuda.synchronize()
+        cols = sorted({0, b - 1})
+        for blk in (0, last):
+            ref = oracle.forward_block(host, x16[:b], cols, blk)
+            got = y[cols][:, blk * host.had_out:(blk + 1) * host.had_out]
+            assert _rel(got, ref) < REL_TOL, (b, blk)
+    assert torch.count_nonzero(ws[:8 * m * 4]).item() == 0
+
+
+# qdec_gemv calls of 4 to 8 columns on large layers (batch * m * n >= 4e8)
+# run the batched MFMA path with 16-column tiles: other codes, a half-TCQ
+# layer (two row parts sharing the K-split slices) and the smallest batch
+# that takes the path.
+ROUTED_CASES = [(synth.NUQ, 3, 0, 0, 4096, 14336, 8), (synth.VQ, 4, 0, 0, 4096, 14336, 7),
+                (synth.HYB, 0, 5, 7168, 14336, 4096, 8), (synth.MAD1, 2, 0, 0, 28672, 4096, 4)]
+
+
+@pytest.mark.parametrize("code,k,kv_b,m_a,m,n,b", ROUTED_CASES,
+                         ids=["%s_k%d_%dx%d_b%d" % (synth.CODE_NAMES[c], k, m, n, b)
+                              for c, k, _, _, m, n, b in ROUTED_CASES])
+def test_gemv_routed_to_mfma_sampled(q, dev, code, k, kv_b, m_a, m, n, b):
+    import torch
+    kw = dict(kv=6, kv_b=kv_b, m_a=m_a) if m_a else {}
+    host = synth.make_layer(code, m, n, k, tag="routed%d_%d_%d" % (code, m, n), **kw)
+    x16 = synth.activations("routedx%d" % n, b, n)
+    _say("gemv routed", synth.CODE_NAMES[code], k, m, n, b, kw)
+    lay = q.upload_layer(host, dev)
+    ws = q.workspace(lay, b, q.QDEC_OP_GEMV, dev)
+    y = _to_f64(q.gemv(lay, _f16_tensor(x16, dev), ws=ws))
+    torch.cuda.synchronize()
+    cols = sorted({0, b - 1})
+    last = m // host.had_out - 1
+    for blk in (0, last):
+        ref = oracle.forward_block(host, x16, cols, blk)
+        got = y[cols][:, blk * host.had_out:(blk + 1) * host.had_out]
+        assert _rel(got, ref) < REL_TOL, blk
+    # the accumulator stays zero for a later fused call on this workspace
+    assert torch.count_nonzero(ws[:8 * m * 4]).item() == 0
 
 
 @pytest.mark.parametrize("m,had_out", [(1280, 256), (4096, 4096), (8192, 8192), (16384, 16384)])
@@ -365,7 +422,10 @@ def test_gemv_wide_chunks_sampled(q, dev, n, b, k):
     (synth.MAD1, 2, 256, 256, 64), (synth.INST3, 4, 256, 256, 33), (synth.NUQ, 3, 256, 512, 64),
     (synth.VQ, 4, 256, 256, 64), (synth.HYB, 4, 1024, 1024, 64), (synth.NUQ, 2, 256, 512, 64),
     (synth.NUQ, 4, 384, 256, 40), (synth.VQ, 2, 256, 256, 64), (synth.VQ, 3, 128, 160, 64),
-    (synth.MAD1, 4, 256, 256, 64), (synth.INST3, 2, 256, 512, 64), (synth.HYB, 2, 256, 256, 256)])
+    (synth.MAD1, 4, 256, 256, 64), (synth.INST3, 2, 256, 512, 64), (synth.HYB, 2, 256, 256, 256),
+    # 16-column batch tiles (batch <= 16): full, ragged and one-column tiles
+    (synth.HYB, 3, 384, 592, 16), (synth.MAD1, 2, 256, 256, 1), (synth.INST3, 4, 256, 256, 12),
+    (synth.NUQ, 3, 256, 512, 9), (synth.VQ, 4, 256, 256, 16), (synth.HYB, 4, 1024, 1040, 17)])
 def test_gemm_small_matches_oracle(q, dev, code, k, m, n, b):
     import torch
     _say("gemm small", synth.CODE_NAMES[code], k, m, n, b)
