@@ -552,6 +552,44 @@ def test_graph_replays_match_eager(q, dev):
     assert torch.count_nonzero(ws4[:4 * m * 4]).item() == 0
 
 
+def test_graph_replays_routed_gemv(q, dev):
+    """An 8-column qdec_gemv on a 14336x4096 layer (the batched MFMA path:
+    input RHT, 16-column GEMM tiles, output RHT over the K-split slices)
+    captured into a HIP graph: every replay equals the eager call bit for
+    bit (fixed summation order), with an eager one-column call on the same
+    workspace between the replays; the sampled block matches the oracle."""
+    import torch
+    m, n, b = 14336, 4096, 8
+    host = synth.make_layer(synth.HYB, m, n, 2, tag="graphrouted")
+    lay = q.upload_layer(host, dev)
+    x16 = synth.activations("graphroutedx", b, n)
+    xt = _f16_tensor(x16, dev)
+    ws = q.workspace(lay, b, q.QDEC_OP_GEMV, dev)
+    y = torch.empty((b, m), dtype=torch.float16, device=dev)
+    y1 = torch.empty((1, m), dtype=torch.float16, device=dev)
+    x1 = xt[:1].contiguous()
+    q.gemv(lay, xt, ws=ws, y=y)
+    torch.cuda.synchronize()
+    eager = y.clone()
+    ref = oracle.forward_block(host, x16, [0, b - 1], 0)
+    assert _rel(_to_f64(eager)[[0, b - 1]][:, :host.had_out], ref) < REL_TOL
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.gemv(lay, xt, ws=ws, y=y)
+    for rep in range(3):
+        _say("routed graph replay", rep)
+        y.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), rep
+        q.gemv(lay, x1, ws=ws, y=y1)          # the fused GEMV on the same workspace
+        torch.cuda.synchronize()
+    del g
+    ref1 = oracle.forward_block(host, x16[:1], [0], 0)
+    assert _rel(_to_f64(y1)[:, :host.had_out], ref1) < REL_TOL
+    assert torch.count_nonzero(ws[:8 * m * 4]).item() == 0
+
+
 def test_gemm_agrees_with_gemv(q, dev):
     import torch
     host = synth.make_layer(synth.HYB, 512, 1024, 2, tag="gmgv")
