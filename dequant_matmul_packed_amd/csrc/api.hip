@@ -226,12 +226,15 @@ int gemm_ksplit(int64_t m, int64_t n, int64_t b) {
   return (int)ks;
 }
 
-// Whether qdec_gemv runs a product of 4 to 8 columns on the batched MFMA
-// path (input RHT, gemm_kernel with 16-column tiles, output RHT): once the
-// GEMV's per-column dot products (one v_dot2 per weight pair and column)
-// outweigh the batched path's fixed costs, measured at b * m * n >= 4e8
-// (14336x4096 and 4096x14336 from 8 columns, 28672x4096 from 4).  Tuning
-// override QDEC_GEMV_MFMA = 0 / 1 (1: every call of 2 or more columns).
+// Whether qdec_gemv runs a product of 2 to 8 columns on the batched MFMA
+// path (input RHT, gemm_kernel with 16-column tiles, output RHT) instead of
+// the fused GEMV.  The GEMV's time grows with its batch-column template NB
+// (the batch rounded up to 2, 4 or 8: one v_dot2 per weight pair and
+// column), the batched path's hardly at all up to 16 columns; measured over
+// the Llama-8B shapes at b = 2 .. 8, the batched path wins where
+// NB * m * n >= 4e8: 14336x4096 and 4096x14336 from 5 columns, 28672x4096
+// from 3, 6144x4096 and 4096x4096 never.  Tuning override
+// QDEC_GEMV_MFMA = 0 / 1 (1: every call of 2 or more columns).
 bool gemv_via_gemm(int64_t m, int64_t n, int64_t b) {
   static int forced = -2;
   if (forced == -2) {
@@ -240,7 +243,8 @@ bool gemv_via_gemm(int64_t m, int64_t n, int64_t b) {
   }
   if (b < 2) return false;
   if (forced >= 0) return forced != 0;
-  return b >= 4 && (double)b * (double)m * (double)n >= 4e8;
+  const int64_t nb = b <= 2 ? 2 : b <= 4 ? 4 : 8;   // the GEMV's column template
+  return (double)nb * (double)m * (double)n >= 4e8;
 }
 
 // Workspace of qdec_gemv: the GEMV's accumulator and x' slot, then (on the

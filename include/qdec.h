@@ -186,9 +186,10 @@ int qdec_rht(const void *in, int32_t in_dtype, void *out, int32_t out_dtype,
  * in/out, fp32 accumulation.  One kernel decodes and multiplies (at one
  * batch column it also applies the input transform), a second applies the
  * output transform; with more batch columns the input transform runs first
- * in a kernel of its own.  From 4 batch columns on a large layer
- * (batch * m * n >= 4e8) the call runs the batched path of qdec_gemm
- * instead, whose MFMAs then cost less than per-column dot products.
+ * in a kernel of its own.  On large layers with several batch columns
+ * (NB * m * n >= 4e8, NB = batch rounded up to 2, 4 or 8) the call runs the
+ * batched path of qdec_gemm instead, whose MFMAs then cost less than the
+ * per-column dot products.
  * ws: qdec_workspace_bytes(layer, batch, QDEC_OP_GEMV) bytes, 256-byte
  * aligned, zero-filled before first use (left zeroed).  A workspace sized
  * for a batch serves every smaller batch of the same layer.                 */

@@ -70,6 +70,30 @@ def test_workspace_sizes(q):
     assert q.qdec_workspace_bytes(lay, 1, 99) == 0
 
 
+def test_gemv_routing_rule_in_workspace_sizes(q):
+    """qdec_gemv runs a call on the batched MFMA path when NB * m * n >= 4e8,
+    NB the GEMV's batch-column template (the batch rounded up to 2, 4 or 8);
+    such a call's workspace carries the K-split slices (fp32 b x m each) after
+    the GEMV's own (8 x m accumulator, then x')."""
+    def plain(m, n, b):
+        return 8 * m * 4 + b * n * 2
+
+    cases = [  # m, n, batches on the GEMV, batches on the batched path
+        (28672, 4096, [1, 2], [3, 4, 5, 8]),
+        (14336, 4096, [1, 2, 3, 4], [5, 6, 8]),
+        (4096, 14336, [1, 4], [5, 8]),
+        (6144, 4096, [1, 2, 4, 8], []),
+        (4096, 4096, [1, 8], []),
+    ]
+    for m, n, gemv_b, routed_b in cases:
+        lay = _layer(q, m=m, n=n, had_in=min(n & -n, 16384), had_out=min(m & -m, 16384))
+        for b in gemv_b:
+            assert q.qdec_workspace_bytes(lay, b, q.QDEC_OP_GEMV) == plain(m, n, b), (m, n, b)
+        for b in routed_b:
+            extra = q.qdec_workspace_bytes(lay, b, q.QDEC_OP_GEMV) - plain(m, n, b)
+            assert extra > 0 and extra % (b * m * 4) == 0, (m, n, b, extra)
+
+
 BAD_LAYERS = [
     dict(m=100), dict(n=40), dict(m=0), dict(k=0), dict(k=9), dict(Q=0), dict(V=3), dict(L=12),
     dict(code=6, L=12, V=1), dict(code=6, L=16, V=2), dict(code=6, L=16, V=1, lut=None),

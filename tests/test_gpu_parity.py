@@ -304,12 +304,13 @@ def test_gemv_mixed_batches_one_workspace(q, dev):
     assert torch.count_nonzero(ws[:8 * m * 4]).item() == 0
 
 
-# qdec_gemv calls of 4 to 8 columns on large layers (batch * m * n >= 4e8)
-# run the batched MFMA path with 16-column tiles: other codes, a half-TCQ
-# layer (two row parts sharing the K-split slices) and the smallest batch
-# that takes the path.
+# qdec_gemv calls of several columns on large layers (NB * m * n >= 4e8, NB
+# the batch rounded up to 2, 4 or 8) run the batched MFMA path with
+# 16-column tiles: other codes, a half-TCQ layer (two row parts sharing the
+# K-split slices) and the smallest batches that take the path.
 ROUTED_CASES = [(synth.NUQ, 3, 0, 0, 4096, 14336, 8), (synth.VQ, 4, 0, 0, 4096, 14336, 7),
-                (synth.HYB, 0, 5, 7168, 14336, 4096, 8), (synth.MAD1, 2, 0, 0, 28672, 4096, 4)]
+                (synth.HYB, 0, 5, 7168, 14336, 4096, 8), (synth.MAD1, 2, 0, 0, 28672, 4096, 3),
+                (synth.HYB, 2, 0, 0, 14336, 4096, 5)]
 
 
 @pytest.mark.parametrize("code,k,kv_b,m_a,m,n,b", ROUTED_CASES,
