@@ -161,7 +161,7 @@ def time_events(torch, fn, reps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU; this build has no multi-GPU path "
+        print("bench.py measures one GPU; the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch

@@ -1,11 +1,12 @@
 #!/usr/bin/env python3
 """Turn two rocprofv3 counter runs of the bench into HBM-traffic summaries.
 
-Usage (from the repository root, R = its path, after `cd /tmp && export TMPDIR=/tmp`):
-  rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc/FETCH_SIZE -o run -- \\
+Usage (R = the repository root, P = a scratch folder for the raw counter
+databases, after `cd /tmp && export TMPDIR=/tmp`):
+  rocprofv3 --pmc FETCH_SIZE -d $P/FETCH_SIZE -o run -- \\
       python3 $R/bench.py --steps 20 --warmup 5 --no-detail --no-cpu-baseline --copy-calibration-mib 256
-  rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc/WRITE_SIZE -o run -- (same command)
-  python3 profile_traffic.py gpurun_out/pmc/FETCH_SIZE/run_results.db gpurun_out/pmc/WRITE_SIZE/run_results.db
+  rocprofv3 --pmc WRITE_SIZE -d $P/WRITE_SIZE -o run -- (same command)
+  python3 $R/profile_traffic.py $P/FETCH_SIZE/run_results.db $P/WRITE_SIZE/run_results.db
 
 Each counter (KiB per dispatch) is scaled by what it reads for the bench's
 plain device-to-device copy of 256 MiB (bytes read and written are known), so
