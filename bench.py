@@ -307,6 +307,7 @@ def main():
         detail.update(bench_code_variants(q, torch, dev, stream))
         detail.update(bench_fractional(q, torch, dev, stream))
         detail.update(bench_encoder(q, torch, dev, cpu=not args.no_cpu_baseline))
+        detail.update(bench_rht(q, torch, dev, stream))
 
     if not args.no_detail and not args.only:
         detail["pages_context"] = pages_context()
@@ -757,6 +758,63 @@ def pages_context():
                     break
     out["measured_source"] = "profiles/sq_counters_*.md (SQ_INSTS_VALU x 64 / weights)"
     return out
+
+
+def bench_rht(q, torch, dev, stream):
+    """qdec_rht on its own, at the shapes the batched path runs it on and on a
+    large input: the time per call (200 back-to-back launches between one
+    event pair, inputs rotating through a pool of at least 1 GiB so that no
+    call finds its input in the caches; the median of 5 repeats) and its
+    rate against HBM: bytes = input + output + the sign bits."""
+    import ctypes
+    cases = [  # name, rows, n, block, input dtype (0 fp16, 1 fp32), output dtype, mode
+        ("input_64x8192_B8192_f16", 64, 8192, 8192, 0, 0, 0),
+        ("output_64x28672_B4096_f32_to_f16", 64, 28672, 4096, 1, 0, 1),
+        ("output_8x14336_B2048_f32_to_f16", 8, 14336, 2048, 1, 0, 1),
+        ("input_4096x4096_B4096_f16", 4096, 4096, 4096, 0, 0, 0),
+    ]
+    fn = q._lib.qdec_rht
+    out = {}
+    for name, rows, n, block, idt, odt, mode in cases:
+        ib, ob = (4 if idt else 2), (4 if odt else 2)
+        in_bytes = rows * n * ib
+        P = int(min(512, max(4, -(-POOL_BYTES // in_bytes))))
+        g = torch.Generator(device=dev)
+        g.manual_seed(rows * 7919 + n)
+        dt = torch.float32 if idt else torch.float16
+        pool = torch.randn((P, rows, n), generator=g, device=dev).to(dt)
+        signs = torch.randint(-(1 << 31), (1 << 31) - 1, ((n + 31) // 32,), dtype=torch.int32, device=dev,
+                              generator=g)
+        y = torch.empty((rows, n), dtype=torch.float32 if odt else torch.float16, device=dev)
+        scale = ctypes.c_float(1.0)
+
+        def call(i):
+            st = fn(pool[i % P].data_ptr(), idt, y.data_ptr(), odt, rows, n, block, signs.data_ptr(), mode,
+                    scale, stream)
+            if st != 0:
+                raise RuntimeError("qdec_rht failed: %d" % st)
+        for i in range(20):
+            call(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps, j = [], 0
+        for r in range(5):
+            e0.record()
+            for i in range(200):
+                call(j)
+                j += 1
+            e1.record()
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1) * 1e3 / 200)
+        us = sorted(reps)[2]
+        nbytes = in_bytes + rows * n * ob + (n + 7) // 8
+        gbs = nbytes / us / 1e3
+        out[name] = {"us": round(us, 2), "bytes": nbytes, "GBps": round(gbs, 1),
+                     "frac_of_8TBps": round(gbs / 8000.0, 4)}
+        del pool
+        torch.cuda.empty_cache()
+    log("qdec_rht alone:", {k: (v["us"], v["GBps"]) for k, v in out.items()})
+    return {"rht_alone": out}
 
 
 def measured_ceilings(torch, dev):
