@@ -511,14 +511,18 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
             xp[c][4] = p1.x; xp[c][5] = p1.y; xp[c][6] = p1.z; xp[c][7] = p1.w;
           }
           if constexpr (V == 2) {
+            uint32_t pairs[16];
+            if constexpr (CODE == HYB) {
+              hyb_lane_pairs<KX, COPIES>(w, tabc, qshift, pairs);
+            } else {
+#pragma unroll
+              for (int t = 0; t < 16; ++t) pairs[t] = tabc[window_at<L>(w, t * KX) * COPIES];
+            }
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
-              uint32_t pair;
-              if constexpr (CODE == HYB) pair = tabc[hyb_signed_index(window_raw<L>(w, t * KX), qshift) * COPIES];
-              else pair = tabc[window_at<L>(w, t * KX) * COPIES];
 #pragma unroll
               for (int c = 0; c < NB; ++c)
-                acc[t >> 3][c] = __builtin_amdgcn_fdot2(as_h2(pair), as_h2(xp[c][t & 7]),
+                acc[t >> 3][c] = __builtin_amdgcn_fdot2(as_h2(pairs[t]), as_h2(xp[c][t & 7]),
                                                         acc[t >> 3][c], false);
             }
           } else if constexpr (CODE == MAD1) {

@@ -188,6 +188,19 @@ __device__ __forceinline__ uint32_t hyb_signed_index(uint32_t s, int qshift) {
   return (hyb_hash(s) & 0xFFFFu) >> qshift;
 }
 
+// Two states 16 bits apart in the stream (steps t and t + 16/kV when kV
+// divides 16) are the two halves of one 32-bit window: the high half is the
+// state at the window's first bit, the low half the one 16 bits later.  The
+// packed 16-bit multiply-add then hashes both at once, each half of its
+// result being (s*s + s) mod 2^16 of its state, which is all the index uses.
+__device__ __forceinline__ void hyb_index_pair(uint32_t win32, int qshift, uint32_t& idx_first,
+                                               uint32_t& idx_second) {
+  uint32_t h2;
+  asm("v_pk_mad_u16 %0, %1, %1, %1" : "=v"(h2) : "v"(win32));
+  idx_first = h2 >> (16 + qshift);
+  idx_second = (h2 & 0xFFFFu) >> qshift;
+}
+
 // 1MAD: LCG output for a state.
 __device__ __forceinline__ uint32_t mad1_lcg(uint32_t s) { return s * MAD1_A + MAD1_C; }
 // 3INST: LCG, then force the high exponent bits of both halves.
@@ -250,16 +263,39 @@ __device__ __forceinline__ void fill_plain_table(uint32_t* tab, const uint32_t* 
 // lane_words_ready leaves them.  tabc points at this lane's copy of the table
 // (HYB/VQ) or at the NUQ levels; gs[r] is the NUQ group scale of the lane's
 // row 2q + r (unused otherwise).
+// HYB at V = 2: the lane's 16 table pairs, out[t] for step t.  Where kV
+// divides 16, steps t and t + 16/kV come from one window and one packed hash.
+template <int KV, int COPIES>
+__device__ __forceinline__ void hyb_lane_pairs(const uint32_t* w, const uint32_t* tabc, int qshift,
+                                               uint32_t* out) {
+  if constexpr (16 % KV == 0) {
+    constexpr int D = 16 / KV;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      if ((t / D) & 1) continue;                       // the second of a pair
+      uint32_t i0, i1;
+      hyb_index_pair(window_raw<32>(w, t * KV), qshift, i0, i1);
+      out[t] = tabc[i0 * COPIES];
+      out[t + D] = tabc[i1 * COPIES];
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) out[t] = tabc[hyb_signed_index(window_raw<16>(w, t * KV), qshift) * COPIES];
+  }
+}
+
 template <int CODE, int KV, int COPIES>
 __device__ __forceinline__ void lane_decode_exact(const uint32_t* w, const uint32_t* tabc,
                                                   int qshift, const float* gs, uint32_t* out) {
   constexpr int V = code_V(CODE);
   constexpr int L = code_L(CODE, KV);
-  if constexpr (V == 2) {
+  if constexpr (CODE == HYB) {
+    static_assert(V == 2 && L == 16, "HYB: two weights per step, 16-bit states");
+    hyb_lane_pairs<KV, COPIES>(w, tabc, qshift, out);
+  } else if constexpr (V == 2) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      if constexpr (CODE == HYB) out[t] = tabc[hyb_signed_index(window_raw<L>(w, t * KV), qshift) * COPIES];
-      else out[t] = tabc[window_at<L>(w, t * KV) * COPIES];
+      out[t] = tabc[window_at<L>(w, t * KV) * COPIES];
     }
   } else {
 #pragma unroll
