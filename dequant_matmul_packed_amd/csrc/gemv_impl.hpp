@@ -315,6 +315,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
     for (int e = 0; e < 8; ++e) part[e] = 0.f;
 #pragma unroll
     for (int r = 0; r < MAXR; ++r) {
+      if (r * RG >= arows) break;                    // uniform: no thread has row r (its loads read zeros)
       const int ih = tid / CG + r * RG;
       const uint32_t chi = (uint32_t)__builtin_popcount((unsigned)(jhi & ih)) & 1u;
       const uint32_t rw[4] = {xraw[r].x, xraw[r].y, xraw[r].z, xraw[r].w};
@@ -405,6 +406,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
       for (int e = 0; e < 8; ++e) part[e] = 0.f;
 #pragma unroll
       for (int r = 0; r < MAXR; ++r) {
+        if (r * RG >= arows) break;                  // uniform: no thread has row r (its loads read zeros)
         const int ih = rg + r * RG;
         const uint32_t chi = (uint32_t)__builtin_popcount((unsigned)(jhi & ih)) & 1u;
         const uint32_t rw[4] = {xraw[r].x, xraw[r].y, xraw[r].z, xraw[r].w};
