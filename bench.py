@@ -608,50 +608,22 @@ def bench_fractional(q, torch, dev, stream):
 
 
 def bench_gemm(q, torch, dev, stream):
-    """28672x8192 HYB k=3 up-projection with X of 64x8192: TFLOP/s of the
-    three-launch batched path and of the MFMA kernel alone."""
+    """28672x8192 HYB k=3 up-projection with X of 64x8192: time per call and
+    TFLOP/s of the three-launch batched path, with the per-layer protocol
+    (time_layer: code sets rotating through a pool of at least 1 GiB, 20
+    warm-up calls, 5 repeats of 200 back-to-back calls, the median)."""
     import synth
     wl = synth.WORKLOADS["up70b_prefill"]
     s = wl.layers[0]
     b = wl.batches[0]
-    P = 4
-    layers, pool, base = make_pool_layers(q, torch, dev, s.code, s.m, s.n, s.k, P, "bench/up70b")
-    x = torch.from_numpy(synth.activations("bench/up70b/x", b, s.n).view(np.int16)).to(dev)
-    ws = q.workspace(base, b, q.QDEC_OP_GEMM, dev)
-    y = torch.empty((b, s.m), dtype=torch.float16, device=dev)
-    calls = [LazyLaunch(q, "qdec_gemm", L, x, y, b, ws) for L in layers]
-    calls[0]()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(8):
-            calls[i % P]()
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for r in range(4):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    us_graph = e0.elapsed_time(e1) * 1e3 / 32
-    del g
-    direct = [Launch(q, "qdec_gemm", L, x, y, b, ws, stream) for L in layers]
-    e0.record()
-    for i in range(32):
-        direct[i % P]()
-    e1.record()
-    torch.cuda.synchronize()
-    us_direct = e0.elapsed_time(e1) * 1e3 / 32
-    us = min(us_graph, us_direct)
+    us, _ = time_layer(q, torch, dev, stream, s.code, s.m, s.n, s.k, b, "bench/up70b",
+                       had_in=s.had_in, had_out=s.had_out)
     flops = 2.0 * s.m * s.n * b
     tf = flops / (us * 1e-6) / 1e12
-    log("gemm b=64: %.1f us, %.1f TFLOP/s (direct %.1f us, graph %.1f us)" % (us, tf, us_direct, us_graph))
-    del calls, pool
-    torch.cuda.empty_cache()
+    log("gemm b=64: %.1f us, %.1f TFLOP/s" % (us, tf))
     return {"gemm_b64_up70b": {"us_per_call": round(us, 2), "TFLOPs": round(tf, 1),
                                "frac_of_fp16_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                               "launches": "rht_in + gemm + rht_out"}}
+                               "launches": "rht_in + gemm + rht_out", "protocol": "time_layer"}}
 
 
 def cpu_baseline(specs, x16):
