@@ -370,9 +370,12 @@ static hipError_t launch_rht_in(const RhtArgs& a, hipStream_t stream) {
 }
 
 // Blocks cut over S workgroups (fp16 input): S grows while there are
-// fewer than 256 workgroups and the pieces keep at least 512 values.
+// fewer than 256 workgroups and the pieces keep at least 512 values.  Never
+// in place: every workgroup of a cut block reads the whole block but writes
+// only its own slice, so a workgroup that finishes first would overwrite
+// inputs that the others have not read yet.
 int rht_split_factor(const RhtArgs& a) {
-  if (a.in_f32 || a.block < 1024) return 1;
+  if (a.in_f32 || a.block < 1024 || a.in == a.out) return 1;
   const int64_t wg = a.rows * (a.n / a.block);
   int S = 1;
   while (S < 8 && wg * S < 256 && a.block / (2 * S) >= 512) S *= 2;

@@ -3,10 +3,11 @@ the same seeded inputs.
 
 Bars: decoded weights bit-exact (qdec_decode_tile, every tile); outputs of
 qdec_rht / qdec_gemv / qdec_gemm within ||y - y_ref|| / ||y_ref|| <= 2e-3 per
-batch column (fp32 accumulation, fp16 in and out).  Small layers are checked
-whole (several tiles, ragged chunking, odd shapes); the full-size workloads
-are checked on every tile for the decode and on sampled output blocks (whole
-Hadamard blocks the oracle computes from their own rows) for the matmuls.
+batch column (fp32 accumulation, fp16 in and out).  Every output is also held to an
+element-wise bound (|y - y_ref| <= 2e-3 rms(y_ref) + 1 fp16 ulp).  Small
+layers (several tiles, ragged chunking, odd shapes) and the full-size
+workloads alike are checked whole: every tile of the decode, every output of
+every batch column of the matmuls.
 """
 import os
 import sys
@@ -59,6 +60,28 @@ def _rel(y, ref):
         d = np.linalg.norm(ref[c])
         errs.append(np.linalg.norm(y[c] - ref[c]) / (d if d > 0 else 1.0))
     return max(errs)
+
+
+def _elementwise(y, ref, tol=REL_TOL):
+    """Every output against the bound |y - y_ref| <= tol * rms(column of
+    y_ref) + 1 fp16 ulp of y_ref (the last term is the output rounding), so a
+    single wrong element cannot hide in a column norm.  Returns the largest
+    ratio |y - y_ref| / bound (must be <= 1)."""
+    y = np.atleast_2d(np.asarray(y, dtype=np.float64))
+    ref = np.atleast_2d(np.asarray(ref, dtype=np.float64))
+    assert y.shape == ref.shape, (y.shape, ref.shape)
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+    bound = tol * rms + ulp
+    return float(np.max(np.abs(y - ref) / bound))
+
+
+def _check_output(y, ref, what=""):
+    """Both bars: per-column relative L2 error and the element-wise bound."""
+    rel = _rel(y, ref)
+    ew = _elementwise(y, ref)
+    assert rel < REL_TOL and ew <= 1.0, (what, rel, ew)
+    return rel, ew
 
 
 # ---------------------------------------------------------------------------
@@ -139,9 +162,14 @@ def test_rht_matches_oracle(q, dev, B, n, rows, mode):
     # fp32 in place, back to the input
     inplace = out32.clone()
     q.qdec_rht(inplace, 1, inplace, 1, rows, n, B, st, 1 - mode, 2.0)
+    # fp16 in place (where the out-of-place call cuts a block over several
+    # workgroups, an in-place call must not)
+    ip16 = xt.clone()
+    q.qdec_rht(ip16, 0, ip16, 0, rows, n, B, st, mode, 0.5)
     torch.cuda.synchronize()
     assert _rel(out32.cpu().numpy().astype(np.float64), ref) < 1e-5
-    assert _rel(_to_f64(out16), ref) < REL_TOL
+    _check_output(_to_f64(out16), ref, "fp16 out")
+    _check_output(_to_f64(ip16), ref, "fp16 in place")
     back = inplace.cpu().numpy().astype(np.float64)
     assert _rel(back, x16.view(np.float16).astype(np.float64)) < 1e-5
 
@@ -169,8 +197,7 @@ def test_gemv_small_matches_oracle(q, dev, code, k, b):
         lay = q.upload_layer(host, dev)
         y = q.gemv(lay, _f16_tensor(x16, dev))
         torch.cuda.synchronize()
-        err = _rel(_to_f64(y), ref)
-        assert err < REL_TOL, (m, n, err)
+        _check_output(_to_f64(y), ref, (m, n))
 
 
 @pytest.mark.parametrize("Q", [6, 10, 11])
@@ -187,12 +214,12 @@ def test_hyb_table_sizes(q, dev, Q):
         x16 = synth.activations("qx%d" % b, b, n)
         y = q.gemv(lay, _f16_tensor(x16, dev))
         torch.cuda.synchronize()
-        assert _rel(_to_f64(y), oracle.forward(host, x16)) < REL_TOL, b
+        _check_output(_to_f64(y), oracle.forward(host, x16), b)
     _say("hyb Q", Q, "gemm")
     x16 = synth.activations("qx64", 64, n)
     y = q.gemm(lay, _f16_tensor(x16, dev))
     torch.cuda.synchronize()
-    assert _rel(_to_f64(y), oracle.forward(host, x16)) < REL_TOL
+    _check_output(_to_f64(y), oracle.forward(host, x16))
     out = torch.zeros((host.n_tiles, 256), dtype=torch.int16, device=dev)
     q.qdec_decode_tile(lay, 0, host.n_tiles, out)
     torch.cuda.synchronize()
@@ -222,17 +249,17 @@ def test_hyb1_and_lut_codes(q, dev, code, V, Q, k):
             x16 = synth.activations("ncx%d_%d" % (b, n), b, n)
             y = q.gemv(lay, _f16_tensor(x16, dev))
             torch.cuda.synchronize()
-            assert _rel(_to_f64(y), oracle.forward(host, x16)) < REL_TOL, (m, n, b)
+            _check_output(_to_f64(y), oracle.forward(host, x16), (m, n, b))
         for b in (70, 9):    # 64- and 16-column batch tiles
             _say("new code gemm", b)
             x16 = synth.activations("ncx64_%d" % n, b, n)
             y = q.gemm(lay, _f16_tensor(x16, dev))
             torch.cuda.synchronize()
-            assert _rel(_to_f64(y), oracle.forward(host, x16)) < REL_TOL, (m, n, b)
+            _check_output(_to_f64(y), oracle.forward(host, x16), (m, n, b))
 
 
 @pytest.mark.parametrize("code,V,Q", [(synth.HYB, 1, 6), (synth.LUT, None, 9)])
-def test_hyb1_and_lut_full_size_sampled(q, dev, code, V, Q):
+def test_hyb1_and_lut_full_size_whole(q, dev, code, V, Q):
     """4096 x 4096 at k = 2, b = 1 (the launch the bench would time)."""
     import torch
     host = synth.make_layer(code, 4096, 4096, 2, V=V, Q=Q, tag="ncfull%d" % code)
@@ -241,8 +268,7 @@ def test_hyb1_and_lut_full_size_sampled(q, dev, code, V, Q):
     _say("new code full", synth.CODE_NAMES[code], V)
     y = _to_f64(q.gemv(lay, _f16_tensor(x16, dev)))
     torch.cuda.synchronize()
-    ref = oracle.forward_block(host, x16, [0], 0)
-    assert _rel(y[[0]][:, :4096], ref) < REL_TOL
+    _check_output(y, oracle.forward(host, x16))
 
 
 def test_gemv_edge_cases(q, dev):
@@ -261,7 +287,7 @@ def test_gemv_edge_cases(q, dev):
             _say("gemv edge", kw, "b", b)
             y = q.gemv(lay, _f16_tensor(x16[:b], dev))
             torch.cuda.synchronize()
-            assert _rel(_to_f64(y), oracle.forward(h2, x16[:b])) < REL_TOL, (kw, b)
+            _check_output(_to_f64(y), oracle.forward(h2, x16[:b]), (kw, b))
     # zero input gives exactly zero output
     lay = q.upload_layer(host, dev)
     z = q.gemv(lay, torch.zeros((1, n), dtype=torch.float16, device=dev))
@@ -275,7 +301,7 @@ def test_gemv_edge_cases(q, dev):
     ys = [q.gemv(lay, xt, ws=ws).clone() for rep in range(5)]
     torch.cuda.synchronize()
     for yy in ys:
-        assert _rel(_to_f64(yy), ref) < REL_TOL
+        _check_output(_to_f64(yy), ref)
     assert torch.count_nonzero(ws[:2 * m * 4]).item() == 0
 
 
@@ -291,16 +317,12 @@ def test_gemv_mixed_batches_one_workspace(q, dev):
     ws = q.workspace(lay, 8, q.QDEC_OP_GEMV, dev)
     x16 = synth.activations("mixwsx", 8, n)
     xt = _f16_tensor(x16, dev)
-    last = m // host.had_out - 1
+    ref = oracle.forward(host, x16)
     for b in (8, 3, 1, 8, 2, 8, 1):
         _say("gemv mixed batches", b)
         y = _to_f64(q.gemv(lay, xt[:b], ws=ws))
         torch.cuda.synchronize()
-        cols = sorted({0, b - 1})
-        for blk in (0, last):
-            ref = oracle.forward_block(host, x16[:b], cols, blk)
-            got = y[cols][:, blk * host.had_out:(blk + 1) * host.had_out]
-            assert _rel(got, ref) < REL_TOL, (b, blk)
+        _check_output(y, ref[:b], b)
     assert torch.count_nonzero(ws[:8 * m * 4]).item() == 0
 
 
@@ -316,7 +338,7 @@ ROUTED_CASES = [(synth.NUQ, 3, 0, 0, 4096, 14336, 8), (synth.VQ, 4, 0, 0, 4096, 
 @pytest.mark.parametrize("code,k,kv_b,m_a,m,n,b", ROUTED_CASES,
                          ids=["%s_k%d_%dx%d_b%d" % (synth.CODE_NAMES[c], k, m, n, b)
                               for c, k, _, _, m, n, b in ROUTED_CASES])
-def test_gemv_routed_to_mfma_sampled(q, dev, code, k, kv_b, m_a, m, n, b):
+def test_gemv_routed_to_mfma_whole(q, dev, code, k, kv_b, m_a, m, n, b):
     import torch
     kw = dict(kv=6, kv_b=kv_b, m_a=m_a) if m_a else {}
     host = synth.make_layer(code, m, n, k, tag="routed%d_%d_%d" % (code, m, n), **kw)
@@ -326,12 +348,7 @@ def test_gemv_routed_to_mfma_sampled(q, dev, code, k, kv_b, m_a, m, n, b):
     ws = q.workspace(lay, b, q.QDEC_OP_GEMV, dev)
     y = _to_f64(q.gemv(lay, _f16_tensor(x16, dev), ws=ws))
     torch.cuda.synchronize()
-    cols = sorted({0, b - 1})
-    last = m // host.had_out - 1
-    for blk in (0, last):
-        ref = oracle.forward_block(host, x16, cols, blk)
-        got = y[cols][:, blk * host.had_out:(blk + 1) * host.had_out]
-        assert _rel(got, ref) < REL_TOL, blk
+    _check_output(y, oracle.forward(host, x16))
     # the accumulator stays zero for a later fused call on this workspace
     assert torch.count_nonzero(ws[:8 * m * 4]).item() == 0
 
@@ -354,7 +371,7 @@ def test_gemv_output_blocks(q, dev, m, had_out):
         for rep in range(2):
             y = q.gemv(lay, xt, ws=ws)
             torch.cuda.synchronize()
-            assert _rel(_to_f64(y), ref) < REL_TOL, (b, rep)
+            _check_output(_to_f64(y), ref, (b, rep))
         assert torch.count_nonzero(ws[:b * m * 4]).item() == 0
 
 
@@ -370,10 +387,10 @@ def _full_gemv_cases():
 
 @pytest.mark.parametrize("wname,spec,b", _full_gemv_cases(),
                          ids=["%s/%s/b%d" % (w, s.name, b) for w, s, b in _full_gemv_cases()])
-def test_gemv_full_size_sampled(q, dev, wname, spec, b):
-    """Full-size layer in the launch configuration the bench times; the
-    oracle computes the first and last output Hadamard blocks for the first
-    and last batch column from their own rows."""
+def test_gemv_full_size_whole(q, dev, wname, spec, b):
+    """Full-size layer in the launch configuration the bench times: every
+    output of every batch column against the oracle's full forward pass
+    (all output Hadamard blocks, all panels and input chunks)."""
     import torch
     _say("gemv full", wname, spec.name, b)
     host = spec.build(wname)
@@ -381,13 +398,8 @@ def test_gemv_full_size_sampled(q, dev, wname, spec, b):
     lay = q.upload_layer(host, dev)
     y = _to_f64(q.gemv(lay, _f16_tensor(x16, dev)))
     torch.cuda.synchronize()
-    nblk = host.m // host.had_out
-    cols = sorted({0, b - 1})
-    for blk in sorted({0, nblk - 1}):
-        ref = oracle.forward_block(host, x16, cols, blk)
-        got = y[cols][:, blk * host.had_out:(blk + 1) * host.had_out]
-        err = _rel(got, ref)
-        assert err < REL_TOL, (blk, err)
+    ref = oracle.forward(host, x16)
+    _check_output(y, ref, (wname, spec.name, b))
 
 
 # Wide input chunks: 224 row panels make the GEMV pick 2048-column chunks at
@@ -398,7 +410,7 @@ WIDE_CASES = [(8192, 1, 3), (8192, 3, 3), (5136, 1, 2), (5136, 2, 2)]
 
 
 @pytest.mark.parametrize("n,b,k", WIDE_CASES, ids=["n%d_b%d_k%d" % c for c in WIDE_CASES])
-def test_gemv_wide_chunks_sampled(q, dev, n, b, k):
+def test_gemv_wide_chunks_whole(q, dev, n, b, k):
     import torch
     m = 28672
     _say("gemv wide", m, n, b, k)
@@ -407,12 +419,7 @@ def test_gemv_wide_chunks_sampled(q, dev, n, b, k):
     lay = q.upload_layer(host, dev)
     y = _to_f64(q.gemv(lay, _f16_tensor(x16, dev)))
     torch.cuda.synchronize()
-    nblk = host.m // host.had_out
-    cols = sorted({0, b - 1})
-    for blk in (0, nblk - 1):
-        ref = oracle.forward_block(host, x16, cols, blk)
-        got = y[cols][:, blk * host.had_out:(blk + 1) * host.had_out]
-        assert _rel(got, ref) < REL_TOL, blk
+    _check_output(y, oracle.forward(host, x16), (n, b, k))
 
 
 # ---------------------------------------------------------------------------
@@ -438,18 +445,18 @@ def test_gemm_small_matches_oracle(q, dev, code, k, m, n, b):
     xt = _f16_tensor(x16, dev)
     y = q.gemm(lay, xt, ws=ws)
     torch.cuda.synchronize()
-    assert _rel(_to_f64(y), ref) < REL_TOL
+    _check_output(_to_f64(y), ref)
     # the workspace accumulator is left zeroed: a second call agrees
     y2 = q.gemm(lay, xt, ws=ws)
     torch.cuda.synchronize()
-    assert _rel(_to_f64(y2), ref) < REL_TOL
+    _check_output(_to_f64(y2), ref)
 
 
-def test_gemm_two_k_halves_half_tcq_sampled(q, dev):
+def test_gemm_two_k_halves_half_tcq_whole(q, dev):
     """A half-TCQ layer (rows [0, 4096) at kV = 5, [4096, 8192) at kV = 6)
     large enough for two K halves per workgroup: each part is launched with
     the whole layer's K split and halves, writing its rows of the shared
-    slices.  Sampled batch columns of the output block against the oracle."""
+    slices.  Every output against the oracle."""
     import torch
     m, n, b = 8192, 1040, 64
     host = synth.make_layer(synth.HYB, m, n, 0, kv=5, kv_b=6, m_a=4096, tag="ksubhalf")
@@ -458,18 +465,16 @@ def test_gemm_two_k_halves_half_tcq_sampled(q, dev):
     lay = q.upload_layer(host, dev)
     y = _to_f64(q.gemm(lay, _f16_tensor(x16, dev)))
     torch.cuda.synchronize()
-    cols = [0, 37, b - 1]
-    ref = oracle.forward_block(host, x16, cols, 0)
-    assert _rel(y[cols], ref) < REL_TOL
+    _check_output(y, oracle.forward(host, x16))
 
 
 @pytest.mark.parametrize("b", [64, 130])
-def test_gemm_two_k_halves_sampled(q, dev, b):
+def test_gemm_two_k_halves_whole(q, dev, b):
     """A layer large enough for the 16-wave GEMM (32 panel pairs per 64
     columns: two K halves per workgroup, added in LDS) with a ragged K of
     17 steps of 64 columns: the second split's second half has one live
-    step, whose last tile column is the layer's last.  Sampled batch columns
-    of the whole 8192-row output block against the oracle."""
+    step, whose last tile column is the layer's last.  Every output of every
+    batch column against the oracle."""
     import torch
     m, n = 8192, 1040
     host = synth.make_layer(synth.HYB, m, n, 3, tag="ksub")
@@ -478,14 +483,13 @@ def test_gemm_two_k_halves_sampled(q, dev, b):
     lay = q.upload_layer(host, dev)
     y = _to_f64(q.gemm(lay, _f16_tensor(x16, dev)))
     torch.cuda.synchronize()
-    cols = [0, 63, b - 1]
-    ref = oracle.forward_block(host, x16, cols, 0)
-    assert _rel(y[cols], ref) < REL_TOL
+    _check_output(y, oracle.forward(host, x16), b)
 
 
-def test_gemm_full_size_sampled(q, dev):
-    """70B-class up-projection, X 64 x 8192: sampled batch columns and
-    output blocks against the oracle."""
+def test_gemm_full_size_whole(q, dev):
+    """70B-class up-projection, X 64 x 8192 (the batch-64 workload as the
+    bench times it): all 64 batch columns x all 28672 outputs (every output
+    Hadamard block, every panel pair and K split) against the oracle."""
     import torch
     wl = synth.WORKLOADS["up70b_prefill"]
     spec = wl.layers[0]
@@ -496,11 +500,7 @@ def test_gemm_full_size_sampled(q, dev):
     lay = q.upload_layer(host, dev)
     y = _to_f64(q.gemm(lay, _f16_tensor(x16, dev)))
     torch.cuda.synchronize()
-    cols = [0, 31, 63]
-    for blk in (0, host.m // host.had_out - 1):
-        ref = oracle.forward_block(host, x16, cols, blk)
-        got = y[cols][:, blk * host.had_out:(blk + 1) * host.had_out]
-        assert _rel(got, ref) < REL_TOL, blk
+    _check_output(y, oracle.forward(host, x16), "up70b b=64")
 
 
 def test_graph_replays_match_eager(q, dev):
@@ -541,8 +541,8 @@ def test_graph_replays_match_eager(q, dev):
             t.fill_(0)
         g.replay()
         torch.cuda.synchronize()
-        assert _rel(_to_f64(y1), ref1) < REL_TOL, rep
-        assert _rel(_to_f64(y4), ref4) < REL_TOL, rep
+        _check_output(_to_f64(y1), ref1, rep)
+        _check_output(_to_f64(y4), ref4, rep)
         assert torch.equal(yg, eager_g), rep
         calls()                               # eager work between the replays
         torch.cuda.synchronize()
@@ -573,7 +573,7 @@ def test_graph_replays_routed_gemv(q, dev):
     torch.cuda.synchronize()
     eager = y.clone()
     ref = oracle.forward_block(host, x16, [0, b - 1], 0)
-    assert _rel(_to_f64(eager)[[0, b - 1]][:, :host.had_out], ref) < REL_TOL
+    _check_output(_to_f64(eager)[[0, b - 1]][:, :host.had_out], ref)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         q.gemv(lay, xt, ws=ws, y=y)
@@ -587,7 +587,7 @@ def test_graph_replays_routed_gemv(q, dev):
         torch.cuda.synchronize()
     del g
     ref1 = oracle.forward_block(host, x16[:1], [0], 0)
-    assert _rel(_to_f64(y1)[:, :host.had_out], ref1) < REL_TOL
+    _check_output(_to_f64(y1)[:, :host.had_out], ref1)
     assert torch.count_nonzero(ws[:8 * m * 4]).item() == 0
 
 
@@ -642,12 +642,12 @@ def test_fractional_and_half_tcq(q, dev, code, kv, kv_b, m_a):
             x16 = synth.activations("frx%d_%d" % (b, n), b, n)
             y = q.gemv(lay, _f16_tensor(x16, dev))
             torch.cuda.synchronize()
-            assert _rel(_to_f64(y), oracle.forward(host, x16)) < REL_TOL, (m, n, b)
+            _check_output(_to_f64(y), oracle.forward(host, x16), (m, n, b))
         _say("frac gemm")
         x16 = synth.activations("frx70_%d" % n, 70, n)
         y = q.gemm(lay, _f16_tensor(x16, dev))
         torch.cuda.synchronize()
-        assert _rel(_to_f64(y), oracle.forward(host, x16)) < REL_TOL, (m, n)
+        _check_output(_to_f64(y), oracle.forward(host, x16), (m, n))
 
 
 FRAC_FULL = [(4096, 4096, 5, 0, 0, 1), (4096, 4096, 7, 0, 0, 1), (4096, 4096, 5, 6, 2048, 1),
@@ -656,10 +656,10 @@ FRAC_FULL = [(4096, 4096, 5, 0, 0, 1), (4096, 4096, 7, 0, 0, 1), (4096, 4096, 5,
 
 @pytest.mark.parametrize("m,n,kv,kv_b,m_a,b", FRAC_FULL,
                          ids=["%dx%d_kv%d_%d_b%d" % (m, n, a, b_, bb) for m, n, a, b_, ma, bb in FRAC_FULL])
-def test_fractional_full_size_sampled(q, dev, m, n, kv, kv_b, m_a, b):
+def test_fractional_full_size_whole(q, dev, m, n, kv, kv_b, m_a, b):
     """Full-size fractional and half-TCQ layers in the launch configuration
-    the bench times (GEMV at b = 1, GEMM at b = 64), sampled output blocks
-    on both sides of the part boundary; the decode of every tile."""
+    the bench times (GEMV at b = 1, GEMM at b = 64): every output against the
+    oracle (both sides of the part boundary); the decode of every tile."""
     import torch
     had_in = 8192 if n == 8192 else None
     had_out = 4096 if m == 28672 else None
@@ -671,15 +671,7 @@ def test_fractional_full_size_sampled(q, dev, m, n, kv, kv_b, m_a, b):
     fn = q.gemv if b <= 8 else q.gemm
     y = _to_f64(fn(lay, _f16_tensor(x16, dev)))
     torch.cuda.synchronize()
-    nblk = host.m // host.had_out
-    cols = sorted({0, b - 1})
-    # the first and last blocks, and those holding the last row of the first
-    # part and the first row of the second
-    blks = sorted({0, nblk - 1} | ({(m_a - 1) // host.had_out, m_a // host.had_out} if m_a else set()))
-    for blk in blks:
-        ref = oracle.forward_block(host, x16, cols, blk)
-        got = y[cols][:, blk * host.had_out:(blk + 1) * host.had_out]
-        assert _rel(got, ref) < REL_TOL, blk
+    _check_output(y, oracle.forward(host, x16), (m, n, kv, kv_b, b))
     out = torch.empty((host.n_tiles, 256), dtype=torch.int16, device=dev)
     q.qdec_decode_tile(lay, 0, host.n_tiles, out)
     torch.cuda.synchronize()

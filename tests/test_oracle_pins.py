@@ -227,6 +227,57 @@ def test_hyb_hash_of_single_states(s, Q, idx, negative):
     assert (lo, hi) == (int(lut2[idx] & 0xFFFF) ^ flip, int(lut2[idx] >> 16) ^ flip)
 
 
+# Single states of the computed codes, worked by hand from the code rules
+# (1MAD: one multiply-add of a 32-bit LCG, then the sum of the four bytes;
+# 3INST: the LCG, a bit-field insert of the exponent pattern, one fp16 add;
+# computed-codes reply and "LCG citation (O2)"; the constants are this
+# library's own).  A wrong constant, byte, mask or insert order changes these
+# values, while it could keep the statistical pins above.
+#
+# 1MAD, u = 0x00EA4F79 * s + 0xC2AA9973 (mod 2^32), C = fp32(1/sqrt(21845)):
+#   s = 0:      u = 0xC2AA9973; bytes 0x73 0x99 0xAA 0xC2 = 115+153+170+194
+#               = 632; 632 - 510 = 122; fp32(122 C) = 0.82543677; in [0.5, 1)
+#               the fp16 step is 2^-11: 0.82543677 * 2048 = 1690.495, which
+#               rounds down to 1690 (0.8251953) -- a near tie; bits 0x3800 |
+#               (1690 - 1024) = 0x3A9A.
+#   s = 1:      u = 0xC2AA9973 + 0x00EA4F79 = 0xC394E8EC (no carry out of the
+#               low half: 0x9973 + 0x4F79 = 0xE8EC); bytes 0xEC 0xE8 0x94 0xC3
+#               = 236+232+148+195 = 811; 811 - 510 = 301; fp32(301 C) =
+#               2.0365283; in [2, 4) the step is 2^-9: 2.0365283 * 512 =
+#               1042.70 -> 1043 (2.0371094); bits 0x4000 | (1043 - 1024) = 0x4013.
+#   s = 0x1234: u = 0x6BD94007; bytes 0x07 0x40 0xD9 0x6B = 7+64+217+107 =
+#               395; 395 - 510 = -115; fp32(-115 C) = -0.77807564;
+#               0.77807564 * 2048 = 1593.50 -> 1593 (0.7778320, below the tie:
+#               1593.4989); bits 0x8000 | 0x3800 | 569 = 0xBA39.
+# 3INST, u = 0x00E77B2B * s + 0xEACB81D7, u' = (u & 0x8FFF8FFF) | 0x30003000,
+# value = fp16(f16(low half of u') + f16(high half)):
+#   s = 0:      u = 0xEACB81D7 -> & 0x8FFF8FFF = 0x8ACB81D7 -> | 0x30003000 =
+#               0xBACBB1D7; low 0xB1D7 = -(1 + 471/1024) 2^-3 = -0.18249512,
+#               high 0xBACB = -(1 + 715/1024) 2^-1 = -0.84912109; sum
+#               -1.03161621; in [1, 2) the step is 2^-10: 1056.375 -> 1056
+#               (1.03125); bits 0x8000 | 0x3C00 | 32 = 0xBC20.
+#   s = 1:      u = 0xEACB81D7 + 0x00E77B2B = 0xEBB2FD02 -> u' = 0xBBB2BD02;
+#               low 0xBD02 = -(1 + 258/1024) = -1.25195313, high 0xBBB2 =
+#               -(1 + 946/1024) 2^-1 = -0.96191406; sum -2.21386719; in [2, 4)
+#               the step is 2^-9: 1133.5 exactly, a tie, to even 1134
+#               (2.21484375); bits 0x8000 | 0x4000 | 110 = 0xC06E.
+#   s = 0xFFFF: u = 0x650F06AC -> u' = 0x350F36AC; low 0x36AC = (1 + 684/1024)
+#               2^-2 = 0.41699219, high 0x350F = (1 + 271/1024) 2^-2 =
+#               0.31616211; sum 0.73315430 = 1501.5 * 2^-11, a tie, to even
+#               1502 (0.73339844); bits 0x3800 | (1502 - 1024) = 0x39DE.
+COMPUTED_HAND = [
+    (2, 0x0000, 0x3A9A), (2, 0x0001, 0x4013), (2, 0x1234, 0xBA39),
+    (3, 0x0000, 0xBC20), (3, 0x0001, 0xC06E), (3, 0xFFFF, 0x39DE),
+]
+
+
+@pytest.mark.parametrize("code,s,bits", COMPUTED_HAND,
+                         ids=["%s_%04x" % ("1MAD" if c == 2 else "3INST", s) for c, s, _ in COMPUTED_HAND])
+def test_computed_code_single_states(code, s, bits):
+    (v,) = oracle.state_value(code, s, V=1)
+    assert v == bits, "state %#06x: oracle %#06x, worked by hand %#06x" % (s, v, bits)
+
+
 @pytest.mark.parametrize("k", [2, 3])
 def test_lut_code_decodes_the_states(k):
     """Pure-lookup code (L = 16, V = 1; "Ablations and fast inference",
