@@ -24,7 +24,9 @@ QDEC_ABI_VERSION = 2
 
 # The exported symbols, as declared in include/qdec.h.
 EXPORTS = ("qdec_abi_version", "qdec_status_string", "qdec_last_error", "qdec_workspace_bytes",
-           "qdec_rht", "qdec_gemv", "qdec_gemm", "qdec_decode_tile", "qdec_encode")
+           "qdec_rht", "qdec_gemv", "qdec_gemm", "qdec_decode_tile", "qdec_encode",
+           "qdec_gemv_group", "qdec_gemv_group_workspace_bytes")
+GEMV_GROUP_MAX = 8
 
 
 class QdecError(RuntimeError):
@@ -73,6 +75,10 @@ def _load():
     lib.qdec_decode_tile.argtypes = [P, i64, i64, P, P]
     lib.qdec_encode.restype = ctypes.c_int
     lib.qdec_encode.argtypes = [P, P, P, P, ctypes.c_size_t, P]
+    lib.qdec_gemv_group.restype = ctypes.c_int
+    lib.qdec_gemv_group.argtypes = [P, i32, P, P, P, ctypes.c_size_t, P]
+    lib.qdec_gemv_group_workspace_bytes.restype = ctypes.c_size_t
+    lib.qdec_gemv_group_workspace_bytes.argtypes = [P, i32]
     if lib.qdec_abi_version() != QDEC_ABI_VERSION:
         raise ImportError("libqdec.so ABI version mismatch")
     return lib
@@ -185,6 +191,32 @@ def qdec_encode(layer: Layer, w, codes, ws, ws_bytes: int, stream=None) -> None:
                             _stream(stream)), "qdec_encode")
 
 
+class GroupCall:
+    """The host-side pointer arrays of one qdec_gemv_group call (built once,
+    so a call only passes them by reference)."""
+
+    def __init__(self, layers, xs, ys):
+        count = len(layers)
+        self.count = count
+        self.layers = list(layers)
+        self.keep = (list(xs), list(ys))
+        self._descs = [l.desc() for l in self.layers]
+        self.lp = (ctypes.c_void_p * count)(*[ctypes.addressof(d) for d in self._descs])
+        self.xp = (ctypes.c_void_p * count)(*[_ptr(x) for x in xs])
+        self.yp = (ctypes.c_void_p * count)(*[_ptr(y) for y in ys])
+
+
+def qdec_gemv_group_workspace_bytes(layers) -> int:
+    descs = [l.desc() for l in layers]
+    arr = (ctypes.c_void_p * len(descs))(*[ctypes.addressof(d) for d in descs])
+    return int(_lib.qdec_gemv_group_workspace_bytes(arr, len(descs)))
+
+
+def qdec_gemv_group(call: GroupCall, ws, ws_bytes: int, stream=None) -> None:
+    _check(_lib.qdec_gemv_group(call.lp, call.count, call.xp, call.yp, _ptr(ws), ws_bytes,
+                                _stream(stream)), "qdec_gemv_group")
+
+
 def raw_status(fn_name: str, *args) -> int:
     """Call an entry point with raw ctypes arguments and return its status
     (for error-path tests)."""
@@ -214,7 +246,8 @@ def upload_layer(host, device="cuda") -> Layer:
 
 
 def workspace(layer: Layer, batch: int, op: int, device="cuda"):
-    """A zero-filled workspace tensor for qdec_gemv / qdec_gemm."""
+    """A workspace tensor for qdec_gemv / qdec_gemm (zero-filled, although
+    no call depends on its contents)."""
     import torch
     nbytes = qdec_workspace_bytes(layer, batch, op)
     if nbytes == 0:
@@ -232,6 +265,22 @@ def gemv(layer: Layer, x, ws=None, y=None):
         y = torch.empty((b, layer.m), dtype=torch.float16, device=x.device)
     qdec_gemv(layer, x, y, b, ws, ws.numel())
     return y
+
+
+def gemv_group(layers, xs, ws=None, ys=None):
+    """ys[l] = layers[l](xs[l]) for one-column inputs xs[l] of shape [n_l] or
+    [1, n_l] (fp16), in one grouped call (two launches)."""
+    import torch
+    dev = xs[0].device
+    if ys is None:
+        ys = [torch.empty((1, l.m), dtype=torch.float16, device=dev) for l in layers]
+    if ws is None:
+        nbytes = qdec_gemv_group_workspace_bytes(layers)
+        if nbytes == 0:
+            raise QdecError(QDEC_EINVAL, "qdec_gemv_group_workspace_bytes")
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    qdec_gemv_group(GroupCall(layers, xs, ys), ws, ws.numel())
+    return ys
 
 
 def gemm(layer: Layer, x, ws=None, y=None):

@@ -11,14 +11,16 @@
 //   3. build the LDS lookup table (HYB / VQ / NUQ);
 //   4. stream the tiles: each 8-lane group decodes one 16x16 tile per step,
 //      each lane 32 weights of two rows, accumulating with v_dot2_f32_f16;
-//   5. reduce the four waves in LDS and add the panel's partial sums into
-//      the fp32 accumulator z with device-scope atomic adds.
-// A second, small kernel (gemv_finish_kernel) then applies the output RHT,
-// the scale and the signs to z, writes fp16 y and re-zeroes z.  Splitting
-// there keeps every cross-workgroup dependency at a kernel boundary: an
-// in-kernel "last workgroup finishes" scheme needs an agent-scope release
-// (an L2 write-back) in every workgroup, which measured far more expensive
-// than the second launch.  With more than one batch column the input RHT
+//   5. reduce the four waves in LDS and store the panel's partial sums (after
+//      the output-Hadamard stages inside the panel) into the chunk's own fp32
+//      slice of the workspace: plain stores, no atomics.
+// A second, small kernel (gemv_finish_kernel) then adds the slices in chunk
+// order -- a fixed summation order, so the output is reproducible bit for
+// bit -- applies the rest of the output RHT, the scale and the signs, and
+// writes fp16 y.  Splitting there keeps every cross-workgroup dependency at
+// a kernel boundary: an in-kernel "last workgroup finishes" scheme needs an
+// agent-scope release (an L2 write-back) in every workgroup, which measured
+// far more expensive than the second launch.  With more than one batch column the input RHT
 // runs once, in the RHT kernel, and step 2 is a plain load of the chunk's
 // slice of x' (args.xr): the chunk transform costs b x B_in loads and adds
 // in every workgroup, which at b = 8 outweighs the extra launch.  All
@@ -595,13 +597,13 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
     else stream_tiles(std::integral_constant<int, KV>{});
   }
 
-  // ---- 5. reduce the waves, add into the fp32 accumulator -----------------
+  // ---- 5. reduce the waves, store the chunk's slice -------------------------
   // Lane l of every wave holds partial sums of panel rows 2l and 2l + 1.
-  // One wave per batch column adds the four waves' partials, scales them and
-  // applies the output Hadamard stages that stay inside the panel
+  // One wave per batch column adds the four waves' partials (in wave order)
+  // and applies the output Hadamard stages that stay inside the panel
   // (H_min(Bo,128) on the 128 rows: row bit 0 in registers, bits 1-6 across
-  // lanes), then adds the panel's sums into z; the cross-panel stages are
-  // the finisher's.
+  // lanes), then stores the panel's sums into the chunk's slice of z; the
+  // cross-panel stages, the scale and the signs are the finisher's.
   __syncthreads();   // the table region becomes the reduction buffer
   float* red = fA;   // [4 waves][NB][128 rows]
 #pragma unroll
@@ -623,8 +625,6 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
         v0 -= MAD1_BIAS * sx_sum[c];
         v1 -= MAD1_BIAS * sx_sum[c];
       }
-      v0 *= a.out_mult;
-      v1 *= a.out_mult;
       if (hbits > 0) {
         const float t = v0 + v1;
         v1 = v0 - v1;
@@ -636,9 +636,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
         v0 = hi ? o0 - v0 : v0 + o0;
         v1 = hi ? o1 - v1 : v1 + o1;
       }
-      float* zr = a.z + (int64_t)c * a.mz + row0 + (int64_t)panel * 128 + 2 * lane;
-      __hip_atomic_fetch_add(zr, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(zr + 1, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      float* zr = a.z + ((int64_t)chunk * a.b + c) * a.mz + row0 + (int64_t)panel * 128 + 2 * lane;
+      *reinterpret_cast<float2*>(zr) = make_float2(v0, v1);
     }
   }
 }
@@ -646,7 +645,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
 template <int CODE, int KV, int NB, int PF, bool SL, bool XR, int KVB = 0>
 hipError_t launch_gemv_v(const GemvArgs& a, hipStream_t stream) {
   const size_t lds = gemv_lds_bytes<CODE, KV, NB>(a.L.Q, a.Kc, a.U);
-  static size_t have = 0;
+  static LdsLimit have;
   const hipError_t e =
       ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<CODE, KV, NB, PF, SL, XR, KVB>), lds, &have);
   if (e != hipSuccess) return e;

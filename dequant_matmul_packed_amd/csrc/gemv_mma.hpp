@@ -1,0 +1,460 @@
+// Decode-and-multiply of one batch column on the matrix cores (qdec_gemv at
+// b = 1, and every launch of qdec_gemv_group).
+//
+// Small-batch inference is memory bound, so the codes are streamed from HBM
+// once and decoded on chip ("QTIP: Quantization with Trellises and
+// Incoherence Processing", "QTIP's contribution (W1)").  On gfx950 the decode
+// of a HYB weight pair is a handful of VALU instructions and one random LDS
+// read, and at 2 bits per weight the LDS would have to serve one read per two
+// weights at more than half its peak to keep up with HBM: the table layout
+// and the issue slots decide the speed, not the multiply.  So this kernel
+//  - keeps 32 copies of the signed HYB table (128 KiB at Q = 9), lane l
+//    reading copy l % 32: every bank serves exactly two lanes of a wave, the
+//    least a 64-lane read can cost;
+//  - hands the multiply to the matrix cores: a lane's decoded weights are
+//    directly the A operands of v_mfma_f32_16x16x32_f16 (the layout of the
+//    batched kernel), and x' is the B operand; only column 0 of each 16x16
+//    product is used, which costs matrix-core time the VALU does not pay;
+//  - runs one 16-wave workgroup per CU that computes x' = RHT_in(x) for the
+//    whole row once and builds the table once, then walks its units of work,
+//    so that those fixed costs are paid once per CU and layer instead of once
+//    per (panel, chunk) as in the dot-product kernel.
+//
+// Work decomposition.  A unit is one panel of 128 output rows x one range of
+// KR input columns.  Wave w takes row group rg = w % 4 (tile rows 2rg, 2rg+1
+// of the panel: 32 rows) and quarter ks = w / 4 of the range (KR/4 columns,
+// S = KR/256 steps of 64 columns).  Lane q of tile t = lane / 8 decodes the
+// 32 weights of its tile (rows 2q, 2q+1) at tile (row tr = t % 2, column
+// tc = t / 2) of the step, which makes lanes l, l+16, l+32, l+48 hold one
+// weight row at four column offsets: the MFMA A-operand shape under a fixed
+// row permutation.  Code words stream through a PF-deep register ring that
+// runs on across unit boundaries.  At the end of a unit the four quarters'
+// sums meet in LDS (double buffered by unit), the output-Hadamard stages
+// inside the panel are applied, and the panel's 128 sums are stored (plain
+// stores) into the range's fp32 slice; gemv_finish_kernel adds the slices
+// in range order.
+//
+// A launch may hold several layers of one code and width (a grouped call):
+// workgroups [wg0, wg0 + nwg) take the units of layer l, unit u = local
+// workgroup + i * nwg.  Every wave of a workgroup runs the same number of
+// steps and meets every barrier; every global load is a buffer load issued
+// unconditionally (switched off by its offset), and the unit stores are
+// buffer stores switched off the same way, so no branch holds a memory
+// operation.
+#pragma once
+
+#include "gemv_impl.hpp"
+#include "qdec_device.hpp"
+#include "qdec_internal.hpp"
+
+namespace qdec {
+
+constexpr int MMA_THREADS = 1024;
+
+// Table copies of the codes other than HYB (HYB takes MmaArgs::copies).
+template <int CODE>
+struct MmaTable {
+  static constexpr int COPIES = (CODE == VQ || CODE == HYB1) ? 8 : 1;
+};
+
+// HYB at V = 2 with the table at a run-time stride: entry e of the lane's
+// copy at byte e << cshift of tabl.  Where kV divides 16, steps t and
+// t + 16/kV share one 32-bit window and one packed hash (hyb_index_pair).
+template <int KV>
+__device__ __forceinline__ void hyb_pairs_strided(const uint32_t* w, const char* tabl, int cshift, int qshift,
+                                                  uint32_t* out) {
+  auto rd = [&](uint32_t e) { return *reinterpret_cast<const uint32_t*>(tabl + (e << cshift)); };
+  if constexpr (16 % KV == 0) {
+    constexpr int D = 16 / KV;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      if ((t / D) & 1) continue;
+      uint32_t i0, i1;
+      hyb_index_pair(window_raw<32>(w, t * KV), qshift, i0, i1);
+      out[t] = rd(i0);
+      out[t + D] = rd(i1);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) out[t] = rd(hyb_signed_index(window_raw<16>(w, t * KV), qshift));
+  }
+}
+
+// 1MAD on the matrix cores: the byte sum sigma of each state's LCG output is
+// formed as the fp16 number 1024 + sigma (exponent 10 holds the integers
+// exactly), and one packed fp16 subtraction of 1534 gives sigma - 510 exactly
+// for two states.  The fp32 normaliser 1/sqrt(21845) multiplies the finished
+// sums (in the finisher), so the weights differ from the decoded values only
+// by the fp16 rounding of each product, as in the dot-product kernel.
+template <int KV>
+__device__ __forceinline__ void mad1_pairs_centred(const uint32_t* w, uint32_t* out) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t v0 = __builtin_amdgcn_sad_u8(mad1_lcg(window_at<16>(w, (2 * i) * KV)), 0u, 0x6400u);
+    const uint32_t v1 = __builtin_amdgcn_sad_u8(mad1_lcg(window_at<16>(w, (2 * i + 1) * KV)), 0u, 0x6400u);
+    const half2v c = as_h2(v0 | (v1 << 16)) - half2v{(_Float16)1534.0f, (_Float16)1534.0f};
+    out[i] = __builtin_bit_cast(uint32_t, c);
+  }
+}
+
+template <int CODE, int KV, int PF>
+__global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
+  using G = LaneGeom<CODE, KV>;
+  constexpr int NW = G::NW;
+  constexpr int CW = CODE == NUQ ? NW + 2 : NW;          // ring words per slot (+ NUQ scales)
+  constexpr uint32_t TB = 4u * G::TILE_WORDS;            // bytes per tile
+  extern __shared__ __align__(16) uint32_t smem[];
+  char* lds = reinterpret_cast<char*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave & 3, ks = wave >> 2;
+  const int q = lane & 7, t8 = lane >> 3, tr = t8 & 1, tc = t8 >> 1;
+
+  // ---- this workgroup's layer (workgroup-uniform) ---------------------------
+  int li = 0;
+#pragma unroll
+  for (int i = 1; i < GEMV_GROUP_MAX; ++i)
+    if (i < a.nl && (int)blockIdx.x >= a.lay[i].wg0) li = i;
+  const uint32_t* codes = a.lay[li].L.codes;
+  const uint32_t* lut = a.lay[li].L.lut;
+  const uint16_t* gscale = a.lay[li].L.gscale;
+  const uint32_t* sign_in = a.lay[li].L.sign_in;
+  const int64_t mpart = a.lay[li].L.m;
+  const int n = (int)a.lay[li].L.n;
+  const int qshift = a.lay[li].L.qshift, Q = a.lay[li].L.Q, group = a.lay[li].L.group;
+  const int Bi = a.lay[li].L.had_in, Bo = a.lay[li].L.had_out;
+  const uint16_t* xg = a.lay[li].x;
+  float* zl = a.lay[li].z;
+  const int64_t sstride = a.lay[li].slice_stride, row0 = a.lay[li].row0;
+  const int nr = a.lay[li].nr, KR = a.lay[li].KR;
+  const int bl = (int)blockIdx.x - a.lay[li].wg0, nwg = a.lay[li].nwg, units = a.lay[li].units;
+
+  const int ntc = n >> 4;                 // tile columns
+  const int npanels = (int)(mpart >> 7);
+  const int Kw = KR >> 2, S = Kw >> 6;    // columns and steps of a quarter
+  const int my_units = bl < units ? (units - bl + nwg - 1) / nwg : 0;
+  const int T = my_units * S;             // steps of every wave (a multiple of PF)
+  const int dp = nwg % npanels, dr = nwg / npanels;   // unit stride in (panel, range)
+
+  // ---- 0. every global load the set-up needs, and the first PF code steps ----
+  const int nch8 = n >> 3;                // 8-value chunks of x (n <= 16384: 2 per thread)
+  uint4 xv[2];
+  uint32_t sw[2];
+  {
+    const auto xrs = make_rsrc(xg, (uint32_t)n * 2u);
+    const auto srs = make_rsrc(sign_in, sign_in ? (uint32_t)(((n + 31) >> 5) * 4) : 0u);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = tid + MMA_THREADS * j;
+      const bool ok = c < nch8;
+      xv[j] = buf_load_u4(xrs, ok ? (uint32_t)c * 16u : BUF_OFF);
+      sw[j] = buf_load_u32(srs, ok ? (uint32_t)((8 * c) >> 5) * 4u : BUF_OFF);
+    }
+  }
+  const int nlut = CODE == HYB ? (1 << Q) : 0;   // staged through LDS below
+  uint32_t lw[2];
+  {
+    const auto lrs = make_rsrc(lut, (uint32_t)nlut * 4u);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + MMA_THREADS * i;
+      lw[i] = buf_load_u32(lrs, e < nlut ? (uint32_t)e * 4u : BUF_OFF);
+    }
+  }
+  // codes of the whole part through one resource (format sizes below 4 GiB)
+  const auto crs = make_rsrc(codes, (uint32_t)((mpart >> 4) * ntc * (int64_t)TB));
+  const uint32_t lane_part = (uint32_t)(tc * 8 + 2 * rg + tr) * TB + 4u * G::lane_word(q);
+  // NUQ group scales of the lane's rows 2q, 2q+1 (fp16 [rows of the layer][n / group])
+  const int gstride = CODE == NUQ ? n / group : 0;
+  const auto grs = make_rsrc(gscale, CODE == NUQ ? (uint32_t)((row0 + mpart) * gstride * 2) : 0u);
+  const int64_t grow_l = row0 + (2 * rg + tr) * 16 + 2 * q;   // + panel * 128
+
+  // the prefetch pointer: unit k of this workgroup, step s in it, its panel
+  // and range (scalar, advanced one step at a time)
+  int pk = 0, ps = 0, pp = bl % npanels, pr = bl / npanels;
+  auto load_step = [&](uint32_t* slot) {
+    const int cbase = ((pr * KR + ks * Kw) >> 4) + 4 * ps;   // tile column of tc = 0
+    const bool ok = pk < my_units && cbase + tc < ntc;
+    const uint32_t off = (uint32_t)((pp * ntc + cbase) * 8) * TB + lane_part;
+    buf_load_words<NW>(crs, ok ? off : BUF_OFF, slot);
+    if constexpr (CODE == NUQ) {
+      const int64_t gr = grow_l + (int64_t)pp * 128;
+      const int g = ((cbase + tc) * 16) / group;
+      slot[NW] = buf_load_u16(grs, ok ? (uint32_t)((gr * gstride + g) * 2) : BUF_OFF);
+      slot[NW + 1] = buf_load_u16(grs, ok ? (uint32_t)(((gr + 1) * gstride + g) * 2) : BUF_OFF);
+    }
+    if (++ps == S) {
+      ps = 0;
+      ++pk;
+      pp += dp;
+      pr += dr;
+      if (pp >= npanels) { pp -= npanels; ++pr; }
+    }
+  };
+  uint32_t ring[PF][CW];
+#pragma unroll
+  for (int j = 0; j < PF; ++j) load_step(ring[j]);
+  __builtin_amdgcn_sched_barrier(0);   // all requests out before any wait
+
+  // ---- 1. the lookup table ---------------------------------------------------
+  auto build_table = [&]() {
+    if constexpr (CODE == HYB) {
+      // the LUT words are staged in the reduction area, then every thread
+      // writes 16-byte runs of consecutive copies (conflict-free writes),
+      // all its reads first (at most 8 runs per thread: 128 KiB)
+      uint32_t* stg = reinterpret_cast<uint32_t*>(lds + a.red_off);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int e = tid + MMA_THREADS * i;
+        if (e < nlut) stg[e] = lw[i];
+      }
+      __syncthreads();
+      const int lc = 31 - __builtin_clz((unsigned)a.copies);
+      const int W4 = (a.copies << (Q + 1)) >> 2;      // at most 8192
+      uint4* tab4 = reinterpret_cast<uint4*>(lds);
+      uint32_t v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int w4 = tid + MMA_THREADS * k;
+        const int e = (w4 << 2) >> lc;
+        v[k] = w4 < W4 ? stg[e & (nlut - 1)] ^ (((e >> Q) & 1) ? 0x80008000u : 0u) : 0u;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int w4 = tid + MMA_THREADS * k;
+        if (w4 < W4) tab4[w4] = make_uint4(v[k], v[k], v[k], v[k]);
+      }
+    } else {
+      constexpr int C = MmaTable<CODE>::COPIES;
+      uint32_t* tab = smem;
+      if constexpr (CODE == HYB1) fill_signed_table<C, 0x8000u>(tab, lut, Q, tid, MMA_THREADS);
+      if constexpr (CODE == LUT) fill_plain_table<1>(tab, lut, 1 << 15, tid, MMA_THREADS);
+      if constexpr (CODE == VQ) fill_plain_table<C>(tab, lut, 1 << KV, tid, MMA_THREADS);
+      if constexpr (CODE == NUQ) fill_plain_table<1>(tab, lut, 1 << KV, tid, MMA_THREADS);
+    }
+  };
+
+  // ---- 2. x' = RHT_in(x) of the whole row, fp16 in LDS ----------------------
+  // Chunks of 8 consecutive values: the butterfly stages inside a chunk in
+  // registers, the rest in padded LDS in passes of 3 index bits (512 groups of
+  // 8 values on a 4096-value row: every thread busy).
+  _Float16* xs = reinterpret_cast<_Float16*>(lds + a.xs_off);
+  auto x_transform = [&](float* scr) {
+    const int hb_in = 31 - __builtin_clz((unsigned)Bi);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = tid + MMA_THREADS * j;
+      if (c < nch8) {
+        const uint32_t r[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
+        const uint32_t sg = sw[j] >> ((8 * c) & 31);
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = h2f((uint16_t)(r[e >> 1] >> (16 * (e & 1))));
+          v[e] = ((sg >> e) & 1u) ? -f : f;
+        }
+#pragma unroll
+        for (int h = 1; h < 8; h <<= 1) {
+          if (h < Bi) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              if (!(e & h)) {
+                const float x0 = v[e], x1 = v[e + h];
+                v[e] = x0 + x1;
+                v[e + h] = x0 - x1;
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) scr[pad_index(8 * c + e)] = v[e];
+      }
+    }
+    __syncthreads();
+    if (hb_in > 3) fwht_bits<3>(scr, n, 3, hb_in, tid, MMA_THREADS);   // ends with a barrier
+    const float rs = 1.0f / sqrtf((float)Bi);
+    const int npad8 = (nr * KR) >> 3;     // x' is zero past n, to the end of the last range
+    for (int c = tid; c < npad8; c += MMA_THREADS) {
+      uint32_t p[4] = {0u, 0u, 0u, 0u};
+      if (c < nch8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          p[e] = f2h_bits(scr[pad_index(8 * c + 2 * e)] * rs) |
+                 ((uint32_t)f2h_bits(scr[pad_index(8 * c + 2 * e + 1)] * rs) << 16);
+      }
+      *reinterpret_cast<uint4*>(xs + 8 * c) = make_uint4(p[0], p[1], p[2], p[3]);
+    }
+  };
+
+  // Where LDS allows, the transform has a scratch area of its own and the
+  // table is built first, while x is still on its way; otherwise the
+  // transform borrows the table's area and the table follows it.
+  if (a.scr_off) {                        // workgroup-uniform
+    build_table();
+    x_transform(reinterpret_cast<float*>(lds + a.scr_off));
+  } else {
+    x_transform(reinterpret_cast<float*>(lds));
+    __syncthreads();                      // the scratch is read; the table overwrites it
+    build_table();
+  }
+  __syncthreads();
+
+  // ---- 3. the units ----------------------------------------------------------
+  const int cshift = a.cshift;
+  const char* tabl = lds + (lane & (a.copies - 1)) * 4;                          // HYB
+  const uint32_t* tabc = smem + (lane & (MmaTable<CODE>::COPIES - 1));          // other codes
+  const auto zrs = make_rsrc(zl, (uint32_t)(nr * sstride * 4));
+  const int hbits = Bo >= 128 ? 7 : 31 - __builtin_clz((unsigned)Bo);
+  float4v acc[2] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
+  // the current step: unit ck (panel cp, range cr), step cs in it
+  int ck = 0, cs = 0, cp = bl % npanels, cr = bl / npanels;
+
+  auto compute = [&](const uint32_t* wc) {
+    uint32_t w[NW + 1];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w[i] = wc[i];
+    lane_words_ready<CODE, KV>(w, lane);
+    uint32_t out[16];
+    if constexpr (CODE == HYB) {
+      hyb_pairs_strided<KV>(w, tabl, cshift, qshift, out);
+    } else if constexpr (CODE == MAD1) {
+      mad1_pairs_centred<KV>(w, out);
+    } else {
+      float gs[2] = {0.f, 0.f};
+      if constexpr (CODE == NUQ) {
+        gs[0] = h2f((uint16_t)wc[NW]);
+        gs[1] = h2f((uint16_t)wc[NW + 1]);
+      }
+      lane_decode_exact<CODE, KV, MmaTable<CODE>::COPIES>(w, tabc, qshift, gs, out);
+    }
+    const int col = cr * KR + ks * Kw + 64 * cs;   // first input column of the step
+    if (col + 64 > n) {                              // wave-uniform: a ragged step
+      const bool live = col + 16 * tc < n;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) out[i] = live ? out[i] : 0u;
+    }
+    const _Float16* xb = xs + col + 16 * (lane >> 4);
+    const half8v b0 = *reinterpret_cast<const half8v*>(xb);
+    const half8v b1 = *reinterpret_cast<const half8v*>(xb + 8);
+#pragma unroll
+    for (int ra = 0; ra < 2; ++ra) {
+      const half8v a0 = __builtin_bit_cast(half8v, make_uint4(out[8 * ra], out[8 * ra + 1], out[8 * ra + 2], out[8 * ra + 3]));
+      const half8v a1 =
+          __builtin_bit_cast(half8v, make_uint4(out[8 * ra + 4], out[8 * ra + 5], out[8 * ra + 6], out[8 * ra + 7]));
+      acc[ra] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, acc[ra], 0, 0, 0);
+      acc[ra] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc[ra], 0, 0, 0);
+    }
+  };
+
+  // The end of a unit: lanes 0, 16, 32, 48 hold column 0 of the products,
+  // D[i][0] for i = 4 (lane / 16) + e, MFMA row i being row
+  // 16 (i / 8) + 2 (i % 8) + ra of the wave's 32.  Every wave then adds the
+  // four quarters of the panel (quarter order), applies the in-panel
+  // Hadamard stages, and wave 0's store goes out (the others' are switched
+  // off by their offsets).
+  auto unit_end = [&]() {
+    float* red = reinterpret_cast<float*>(lds + a.red_off) + (ck & 1) * 512;
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * (lane >> 4) + e;
+          red[ks * 128 + 32 * rg + 16 * (i >> 3) + 2 * (i & 7) + ra] = acc[ra][e];
+        }
+    }
+    acc[0] = float4v{0.f, 0.f, 0.f, 0.f};
+    acc[1] = float4v{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
+    float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const float2 p = *reinterpret_cast<const float2*>(red + k4 * 128 + 2 * lane);
+      v0 += p.x;
+      v1 += p.y;
+    }
+    if (hbits > 0) {
+      const float s = v0 + v1;
+      v1 = v0 - v1;
+      v0 = s;
+    }
+    for (int msk = 1; msk < (1 << (hbits > 0 ? hbits - 1 : 0)); msk <<= 1) {
+      const float o0 = __shfl_xor(v0, msk, 64), o1 = __shfl_xor(v1, msk, 64);
+      const bool hi = lane & msk;
+      v0 = hi ? o0 - v0 : v0 + o0;
+      v1 = hi ? o1 - v1 : v1 + o1;
+    }
+    const uint32_t off = (uint32_t)(((int64_t)cr * sstride + row0 + (int64_t)cp * 128 + 2 * lane) * 4);
+    __builtin_amdgcn_raw_buffer_store_b64(
+        __builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t,
+                           make_uint2(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1))),
+        zrs, wave == 0 ? off : BUF_OFF, 0, 0);
+    ++ck;
+    cs = 0;
+    cp += dp;
+    cr += dr;
+    if (cp >= npanels) { cp -= npanels; ++cr; }
+  };
+
+  // PF divides S, so a unit ends only after the last step of a group of PF.
+  // A slot is refilled (with the step PF ahead, switched off past the end)
+  // right after its step has read it, into the same registers: refilling
+  // first would give the new words other registers and make the compiler
+  // rotate the ring at the loop's back edge, after waiting for every load.
+  for (int j0 = 0; j0 < T; j0 += PF) {
+#pragma unroll
+    for (int jj = 0; jj < PF; ++jj) {
+      compute(ring[jj]);
+      load_step(ring[jj]);
+      ++cs;
+    }
+    if (cs == S) unit_end();
+  }
+}
+
+// PF = min(S, 8): the ring depth divides the steps of a unit (S is 2, 4 or a
+// multiple of 8: KR is 512, 1024 or a multiple of 2048).
+template <int CODE, int KV, int PF>
+hipError_t launch_gemv_mma_p(const MmaArgs& a, unsigned grid, size_t lds, hipStream_t stream) {
+  static LdsLimit have;
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_mma_kernel<CODE, KV, PF>), lds, &have);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemv_mma_kernel<CODE, KV, PF>), dim3(grid), dim3(MMA_THREADS), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int CODE, int KV>
+hipError_t launch_gemv_mma_k(const MmaArgs& a, hipStream_t stream) {
+  unsigned grid = 0;
+  int S = 1 << 30;
+  for (int l = 0; l < a.nl; ++l) {
+    if (a.lay[l].wg0 != (int)grid) return hipErrorInvalidValue;
+    grid += (unsigned)a.lay[l].nwg;
+    const int s = a.lay[l].KR >> 8;
+    if (s < S) S = s;
+  }
+  if (grid == 0) return hipSuccess;
+  const size_t lds = (size_t)a.lds_bytes;
+  if (lds < (size_t)a.red_off + MMA_RED_BYTES || lds > (size_t)LDS_MAX_BYTES) return hipErrorInvalidValue;
+  if (S == 2) return launch_gemv_mma_p<CODE, KV, 2>(a, grid, lds, stream);
+  if (S == 4) return launch_gemv_mma_p<CODE, KV, 4>(a, grid, lds, stream);
+  return launch_gemv_mma_p<CODE, KV, 8>(a, grid, lds, stream);
+}
+
+template <int CODE>
+hipError_t launch_gemv_mma_code(const MmaArgs& a, int kv, hipStream_t stream) {
+#define QDEC_MMA_KV(KV)                                                              \
+  case KV:                                                                           \
+    if constexpr (kv_built(CODE, KV)) return launch_gemv_mma_k<CODE, KV>(a, stream); \
+    break;
+  switch (kv) {
+    QDEC_MMA_KV(2) QDEC_MMA_KV(3) QDEC_MMA_KV(4) QDEC_MMA_KV(5)
+    QDEC_MMA_KV(6) QDEC_MMA_KV(7) QDEC_MMA_KV(8)
+    default: break;
+  }
+#undef QDEC_MMA_KV
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qdec

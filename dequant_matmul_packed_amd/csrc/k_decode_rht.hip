@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void decode_tile_kernel(DecodeArgs a) {
 template <int CODE, int KV>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const size_t lds = (size_t)gemv_table_words<CODE, KV>(a.L.Q) * 4 + 16;
-  static size_t have = 0;
+  static LdsLimit have;
   const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&decode_tile_kernel<CODE, KV>), lds, &have);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((a.count + 31) / 32);
@@ -337,7 +337,7 @@ static hipError_t launch_rht_split(const RhtArgs& a, hipStream_t stream) {
   const int nch = Bs >> 3;
 #define QDEC_SPLIT_J(JJ)                                                                            \
   {                                                                                                 \
-    static size_t have = 0;                                                                         \
+    static LdsLimit have;                                                                         \
     const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&rht_split_kernel<S, JJ>), lds, &have); \
     if (e != hipSuccess) return e;                                                                  \
     hipLaunchKernelGGL((rht_split_kernel<S, JJ>), dim3(grid), dim3(256), lds, stream, a);           \
@@ -351,7 +351,7 @@ static hipError_t launch_rht_split(const RhtArgs& a, hipStream_t stream) {
 
 template <bool IN_F32, int J>
 static hipError_t launch_rht_j(const RhtArgs& a, hipStream_t stream) {
-  static size_t have = 0;
+  static LdsLimit have;
   const size_t lds = (size_t)padded_words(a.block) * 4;
   const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&rht_kernel<IN_F32, J>), lds, &have);
   if (e != hipSuccess) return e;
@@ -425,59 +425,128 @@ hipError_t launch_rht_out_f32(const float* z, int nsum, uint16_t* y, int64_t row
 }  // namespace qdec
 
 namespace qdec {
-// Output side of qdec_gemv.  z (fp32 [b][m]) holds, for every 128-row panel,
-// the scaled sums already multiplied by H_min(Bo,128) (the stages inside a
-// panel, done by the GEMV workgroups).  With Sylvester ordering
-// H_Bo = H_P (x) H_128 for P = Bo/128, so the stages left are P-point
-// transforms across the P panels of a block at a fixed row offset i: one
-// thread per (block, i, batch column), the P values in registers.  The
-// thread then applies the output signs, writes fp16 y and re-zeroes z.
-template <int P>
-__global__ __launch_bounds__(128) void gemv_finish_kernel(float* z, uint16_t* y, int64_t m,
-                                                        const uint32_t* sign_out) {
-  const int i = threadIdx.x;
-  const int64_t blk = blockIdx.x;
-  const int64_t c = blockIdx.y;
-  const int64_t row0 = blk * (P * 128) + i;
-  float* zc = z + c * m + row0;
-  float v[P];
-  uint32_t sg[P];
-  // sign words through a buffer that is empty without output signs (its
-  // loads read zero): no branch, so all 2P loads are in flight together
-  const auto srs = make_rsrc(sign_out, sign_out ? (uint32_t)(((m + 31) >> 5) * 4) : 0u);
+// Output side of qdec_gemv, one launch for every layer of a call.  Each
+// layer's K slices hold, per 128-row panel, partial sums already multiplied
+// by H_min(Bo,128) (the stages inside a panel, done by the GEMV
+// workgroups).  With Sylvester ordering H_Bo = H_P (x) H_128 (P = Bo/128), so
+// what is left are the index bits 7 .. log2(Bo) of the transform.  One
+// workgroup per (rows_wg rows, batch column): its threads add the slices in
+// slice order (a fixed order: the output is reproducible bit for bit), run
+// the remaining stages in LDS, scale, apply the output signs and write fp16.
+template <int J>   // float4 chunks per thread: rows_wg <= 4096 J
+__global__ __launch_bounds__(1024) void gemv_finish_kernel(FinishArgs a) {
+  extern __shared__ __align__(16) float buf[];
+  constexpr int SU = 8 / J;                       // slices per round of loads
+  int li = 0;
 #pragma unroll
-  for (int j = 0; j < P; ++j) sg[j] = buf_load_u32(srs, (uint32_t)(((row0 + j * 128) >> 5) * 4));
+  for (int i = 1; i < GEMV_GROUP_MAX; ++i)
+    if (i < a.nl && (int)blockIdx.x >= a.lay[i].wg0) li = i;
+  const float* z = a.lay[li].z;
+  const int64_t sstride = a.lay[li].slice_stride, m = a.lay[li].m;
+  const int nsl = a.lay[li].nslices, Bo = a.lay[li].Bo, R = a.lay[li].rows_wg;
+  const int lw = (int)blockIdx.x - a.lay[li].wg0;
+  const int nseg = (int)(m / R);
+  const int seg = lw % nseg, c = lw / nseg;
+  const int tid = threadIdx.x, nch = R >> 2;
+  const int64_t r0 = (int64_t)seg * R;
+  // the workgroup's rows of every slice, through one buffer resource
+  const auto zrs = make_rsrc(z + (int64_t)c * m + r0, (uint32_t)(((int64_t)(nsl - 1) * sstride + R) * 4));
+  // the sign words (the 4 rows of a chunk share one word: 4-row groups never
+  // straddle one), requested with the first slices
+  const uint32_t* sg = a.lay[li].sign_out;
+  const auto srs = make_rsrc(sg, sg ? (uint32_t)(((m + 31) >> 5) * 4) : 0u);
+  uint32_t sw[J];
 #pragma unroll
-  for (int j = 0; j < P; ++j) v[j] = zc[j * 128];
+  for (int j = 0; j < J; ++j) {
+    const int ch = tid + 1024 * j;
+    sw[j] = buf_load_u32(srs, ch < nch ? (uint32_t)(((r0 + 4 * ch) >> 5) * 4) : BUF_OFF);
+  }
+  float acc[J][4];
 #pragma unroll
-  for (int j = 0; j < P; ++j) sg[j] = (sg[j] >> ((row0 + j * 128) & 31)) & 1u;
+  for (int j = 0; j < J; ++j)
 #pragma unroll
-  for (int j = 0; j < P; ++j) zc[j * 128] = 0.f;
-  fwht_regs<P>(v);
-  uint16_t* yc = y + c * m + row0;
+    for (int e = 0; e < 4; ++e) acc[j][e] = 0.f;
+  for (int s0 = 0; s0 < nsl; s0 += SU) {
+    uint4 v[SU][J];
 #pragma unroll
-  for (int j = 0; j < P; ++j) yc[j * 128] = f2h_bits(sg[j] ? -v[j] : v[j]);
+    for (int su = 0; su < SU; ++su)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int ch = tid + 1024 * j;
+        const bool ok = ch < nch && s0 + su < nsl;
+        v[su][j] = buf_load_u4(zrs, ok ? (uint32_t)(((int64_t)(s0 + su) * sstride + 4 * ch) * 4) : BUF_OFF);
+      }
+#pragma unroll
+    for (int su = 0; su < SU; ++su)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        acc[j][0] += __builtin_bit_cast(float, v[su][j].x);
+        acc[j][1] += __builtin_bit_cast(float, v[su][j].y);
+        acc[j][2] += __builtin_bit_cast(float, v[su][j].z);
+        acc[j][3] += __builtin_bit_cast(float, v[su][j].w);
+      }
+  }
+  if (Bo > 128) {                                  // workgroup-uniform
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int ch = tid + 1024 * j;
+      if (ch < nch) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) buf[pad_index(4 * ch + e)] = acc[j][e];
+      }
+    }
+    __syncthreads();
+    fwht_bits<3>(buf, R, 7, 31 - __builtin_clz((unsigned)Bo), tid, 1024);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int ch = tid + 1024 * j;
+      if (ch < nch) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[j][e] = buf[pad_index(4 * ch + e)];
+      }
+    }
+  }
+  const float mult = a.lay[li].mult;
+  uint16_t* yc = a.lay[li].y + (int64_t)c * m + r0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int ch = tid + 1024 * j;
+    const uint32_t swj = sw[j] >> ((r0 + 4 * ch) & 31);
+    if (ch < nch) {
+      uint32_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = acc[j][e] * mult;
+        h[e] = f2h_bits(((swj >> e) & 1u) ? -v : v);
+      }
+      *reinterpret_cast<uint2*>(yc + 4 * ch) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    }
+  }
 }
 
-template <int P>
-static hipError_t launch_finish_p(const GemvArgs& a, hipStream_t stream) {
-  dim3 grid((unsigned)(a.L.m / (P * 128)), (unsigned)a.b);
-  hipLaunchKernelGGL((gemv_finish_kernel<P>), grid, dim3(128), 0, stream, a.z, a.y, a.L.m, a.L.sign_out);
+template <int J>
+static hipError_t launch_finish_j(const FinishArgs& a, unsigned grid, size_t lds, hipStream_t stream) {
+  static LdsLimit have;
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_finish_kernel<J>), lds, &have);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemv_finish_kernel<J>), dim3(grid), dim3(1024), lds, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_finish(const GemvArgs& a, hipStream_t stream) {
-  const int P = a.L.had_out > 128 ? a.L.had_out / 128 : 1;
-  switch (P) {
-    case 1: return launch_finish_p<1>(a, stream);
-    case 2: return launch_finish_p<2>(a, stream);
-    case 4: return launch_finish_p<4>(a, stream);
-    case 8: return launch_finish_p<8>(a, stream);
-    case 16: return launch_finish_p<16>(a, stream);
-    case 32: return launch_finish_p<32>(a, stream);
-    case 64: return launch_finish_p<64>(a, stream);
-    case 128: return launch_finish_p<128>(a, stream);
-    default: return hipErrorInvalidValue;
+hipError_t launch_gemv_finish(const FinishArgs& a, hipStream_t stream) {
+  unsigned grid = 0;
+  size_t lds = 0;
+  int rmax = 0;
+  for (int l = 0; l < a.nl; ++l) {
+    const FinishLayer& f = a.lay[l];
+    if (f.wg0 != (int)grid) return hipErrorInvalidValue;
+    grid += (unsigned)((f.m / f.rows_wg) * f.b);
+    if (f.Bo > 128 && (size_t)padded_words(f.rows_wg) * 4 > lds) lds = (size_t)padded_words(f.rows_wg) * 4;
+    if (f.rows_wg > rmax) rmax = f.rows_wg;
   }
+  if (grid == 0) return hipSuccess;
+  if (rmax <= 4096) return launch_finish_j<1>(a, grid, lds, stream);
+  if (rmax <= 8192) return launch_finish_j<2>(a, grid, lds, stream);
+  return launch_finish_j<4>(a, grid, lds, stream);
 }
 }  // namespace qdec

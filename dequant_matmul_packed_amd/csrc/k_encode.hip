@@ -287,7 +287,7 @@ static hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t stream) {
   using E = EncGeom<KV>;
   const size_t tabw = (CODE == HYB || CODE == HYB1) ? (size_t)(2 << a.L.Q) : 0;
   const size_t lds = ((size_t)E::AREA + 256 + 64 + tabw) * 4;
-  static size_t have = 0;
+  static LdsLimit have;
   const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&encode_kernel<CODE, KV>), lds, &have);
   if (e != hipSuccess) return e;
   const int64_t grid = a.ntiles < ENCODE_GRID ? a.ntiles : ENCODE_GRID;

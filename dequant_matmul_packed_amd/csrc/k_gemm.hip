@@ -297,7 +297,7 @@ __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void 
 template <int CODE, int KV, int COPIES, int KSUB, int NBT>
 static hipError_t launch_gemm_k(const GemmArgs& a, hipStream_t stream) {
   const size_t lds = gemm_lds_bytes<CODE, KV, COPIES, KSUB, NBT>(a.L.Q);
-  static size_t have = 0;
+  static LdsLimit have;
   const hipError_t e =
       ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_kernel<CODE, KV, COPIES, KSUB, NBT>), lds, &have);
   if (e != hipSuccess) return e;

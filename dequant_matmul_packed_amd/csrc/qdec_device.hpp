@@ -363,14 +363,18 @@ __device__ __forceinline__ void fwht_pass(float* buf, int total, int b0, int tid
 }
 
 // Stages on index bits [bit_lo, bit_hi) only; `total` a multiple of 2^bit_hi.
+// Passes of up to R bits: R = 4 (16 values per thread) suits 256-thread
+// blocks; 1024-thread blocks take R = 3, which keeps all their threads busy
+// on a 4096-value transform (512 groups of 8 instead of 256 of 16).
+template <int R = 4>
 __device__ inline void fwht_bits(float* buf, int total, int bit_lo, int bit_hi, int tid, int nthreads) {
-  for (int b0 = bit_lo; b0 < bit_hi; b0 += 4) {
-    const int e = (bit_hi - b0) < 4 ? (bit_hi - b0) : 4;
+  for (int b0 = bit_lo; b0 < bit_hi; b0 += R) {
+    const int e = (bit_hi - b0) < R ? (bit_hi - b0) : R;
     switch (e) {
       case 1: fwht_pass<1>(buf, total, b0, tid, nthreads); break;
       case 2: fwht_pass<2>(buf, total, b0, tid, nthreads); break;
       case 3: fwht_pass<3>(buf, total, b0, tid, nthreads); break;
-      default: fwht_pass<4>(buf, total, b0, tid, nthreads); break;
+      default: fwht_pass<R < 4 ? R : 4>(buf, total, b0, tid, nthreads); break;
     }
     __syncthreads();
   }

@@ -92,11 +92,19 @@
  *  - Argument errors are found on the host before any launch and return a
  *    negative status with no device work queued.  A failed launch returns
  *    QDEC_EHIP.  No exception crosses this interface.
- *  - Workspaces: size them with qdec_workspace_bytes; a workspace must be
- *    zero-filled before its first use; every successful call leaves the
- *    parts it relies on zero again, so it can be reused without clearing.
+ *  - Workspaces: size them with qdec_workspace_bytes (or
+ *    qdec_gemv_group_workspace_bytes); their contents on entry do not
+ *    matter -- every part of it a call reads, the same call has written.
  *    Calls that share one workspace must be ordered (same stream).
- *  - x and y must not overlap.  The library is reentrant.
+ *  - Results are reproducible bit for bit: every split of the K dimension
+ *    writes a slice of its own (plain stores, no atomics) and the slices
+ *    are added in a fixed order.
+ *  - x and y must not overlap.  The library is reentrant: its only state is
+ *    per-device kernel attributes and device checks, set with atomic
+ *    operations, and per-thread call plans.
+ *  - Sizes: m, n <= 2^20 and code bytes below 2^31 per layer
+ *    (QDEC_EUNSUPPORTED beyond): kernels address a layer through 32-bit
+ *    buffer offsets.
  */
 #ifndef QDEC_H
 #define QDEC_H
@@ -183,18 +191,38 @@ int qdec_rht(const void *in, int32_t in_dtype, void *out, int32_t out_dtype,
 /* Fused decode-and-multiply for small batches ("QTIP's contribution (W1)":
  * small-batch inference is memory bound, so the weights are decoded on the
  * fly): Y[b][m] = layer(X[b][n]) as defined above, 1 <= batch <= 8, fp16
- * in/out, fp32 accumulation.  One kernel decodes and multiplies (at one
- * batch column it also applies the input transform), a second applies the
- * output transform; with more batch columns the input transform runs first
- * in a kernel of its own.  On large layers with several batch columns
- * (NB * m * n >= 4e8, NB = batch rounded up to 2, 4 or 8) the call runs the
- * batched path of qdec_gemm instead, whose MFMAs then cost less than the
- * per-column dot products.
+ * in/out, fp32 accumulation.  Two launches: one kernel decodes and
+ * multiplies, the finisher adds its K slices and applies the output
+ * transform.  At one batch column the decode kernel also applies the input
+ * transform: on layers of at least 5e7 weights it is the MFMA kernel (one
+ * workgroup per CU; the decoded weights are MFMA operands), on smaller ones
+ * the dot-product kernel.  With more batch columns the input transform runs
+ * first in a kernel of its own, and on large layers (NB * m * n >= 4e8,
+ * NB = batch rounded up to 2, 4 or 8) the call runs the batched path of
+ * qdec_gemm instead.  x 16-byte and y 8-byte aligned.
  * ws: qdec_workspace_bytes(layer, batch, QDEC_OP_GEMV) bytes, 256-byte
- * aligned, zero-filled before first use (left zeroed).  A workspace sized
- * for a batch serves every smaller batch of the same layer.                 */
+ * aligned; its contents on entry do not matter.  A workspace sized for a
+ * batch serves every smaller batch of the same layer.                       */
 int qdec_gemv(const qdec_layer *layer, const uint16_t *x, uint16_t *y,
               int64_t batch, void *ws, size_t ws_bytes, void *stream);
+
+/* Several independent one-column products in one call (the projections of
+ * a decoder layer that read the same activations, e.g. q, k and v, or gate
+ * and up): y[l] = layers[l](x[l]) for l < count <= 8, each as qdec_gemv at
+ * batch 1.  The row parts of all layers that share a code and width run in
+ * one launch of the one-column MFMA kernel, and one finisher launch serves
+ * every layer, so a group costs two launches instead of two per layer.
+ * x[l]: [n_l] fp16, 16-byte aligned; y[l]: [m_l] fp16, 8-byte aligned, no
+ * y overlapping any x or another y (x may be shared).  ws:
+ * qdec_gemv_group_workspace_bytes(layers, count) bytes, 256-byte aligned;
+ * its contents on entry do not matter.  QDEC_EUNSUPPORTED when a layer's
+ * row or lookup table does not fit the kernel's LDS (rows wider than 16384
+ * columns).                                                                   */
+int qdec_gemv_group(const qdec_layer *const *layers, int32_t count, const uint16_t *const *x,
+                    uint16_t *const *y, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of qdec_gemv_group for these layers (0 on a bad argument). */
+size_t qdec_gemv_group_workspace_bytes(const qdec_layer *const *layers, int32_t count);
 
 /* Batched decode-and-multiply (prefill): same result as qdec_gemv for
  * 1 <= batch <= 256; decoded weights go from registers straight into fp16

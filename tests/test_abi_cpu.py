@@ -49,15 +49,26 @@ def _layer(q, **kw):
 
 
 def test_workspace_sizes(q):
-    lay = _layer(q)
+    """qdec_gemv's workspace: fp16 x' (b x n), then the fp32 K slices of the
+    largest set any call of up to b columns writes, each part 256-byte
+    aligned; nothing in it needs initialising."""
+    lay = _layer(q)                        # 256 x 128
+    # b = 1: x' 128 * 2 = 256 B.  Slices: the MFMA GEMV's ranges of 512
+    # columns (one range: 1 x 256 rows x 4 B = 1024) and the dot-product
+    # GEMV's chunks (256 columns: one chunk, 1024 B) -> 1024.
     gv = q.qdec_workspace_bytes(lay, 1, q.QDEC_OP_GEMV)
-    # fp32 accumulator 8 x m (the largest batch, whatever the call's), then
-    # fp16 x' b x n; each 256-byte aligned
-    assert gv == 8 * 256 * 4 + 1 * 128 * 2
-    assert q.qdec_workspace_bytes(lay, 8, q.QDEC_OP_GEMV) == 8 * 256 * 4 + 8 * 128 * 2
+    assert gv == 256 + 1024
+    # b = 8: x' 8 * 128 * 2 = 2048; the dot-product GEMV takes 64-column
+    # chunks at b > 1 (two chunks: 2 x 8 x 256 x 4 = 16384 B)
+    assert q.qdec_workspace_bytes(lay, 8, q.QDEC_OP_GEMV) == 2048 + 16384
+    # a 4096 x 4096 layer at b = 1: x' 8192 B; 16 chunks of 256 columns
+    # (16 x 4096 x 4 = 262144) cover the MFMA GEMV's 8 ranges of 512
+    big = _layer(q, m=4096, n=4096, had_in=4096, had_out=4096)
+    assert q.qdec_workspace_bytes(big, 1, q.QDEC_OP_GEMV) == 8192 + 262144
     # a workspace for a batch covers every smaller one
-    sizes = [q.qdec_workspace_bytes(lay, b, q.QDEC_OP_GEMV) for b in range(1, 9)]
-    assert sizes == sorted(sizes)
+    for l in (lay, big, _layer(q, m=28672, n=4096, had_in=4096, had_out=4096)):
+        sizes = [q.qdec_workspace_bytes(l, b, q.QDEC_OP_GEMV) for b in range(1, 9)]
+        assert sizes == sorted(sizes)
     gm = q.qdec_workspace_bytes(lay, 64, q.QDEC_OP_GEMM)
     # X' (b x n fp16), then one fp32 b x m slice per K split (here 2: n/64)
     assert gm == 64 * 128 * 2 + 2 * 64 * 256 * 4
@@ -70,28 +81,23 @@ def test_workspace_sizes(q):
     assert q.qdec_workspace_bytes(lay, 1, 99) == 0
 
 
-def test_gemv_routing_rule_in_workspace_sizes(q):
-    """qdec_gemv runs a call on the batched MFMA path when NB * m * n >= 4e8,
-    NB the GEMV's batch-column template (the batch rounded up to 2, 4 or 8);
-    such a call's workspace carries the K-split slices (fp32 b x m each) after
-    the GEMV's own (8 x m accumulator, then x')."""
-    def plain(m, n, b):
-        return 8 * m * 4 + b * n * 2
-
-    cases = [  # m, n, batches on the GEMV, batches on the batched path
-        (28672, 4096, [1, 2], [3, 4, 5, 8]),
-        (14336, 4096, [1, 2, 3, 4], [5, 6, 8]),
-        (4096, 14336, [1, 4], [5, 8]),
-        (6144, 4096, [1, 2, 4, 8], []),
-        (4096, 4096, [1, 8], []),
-    ]
-    for m, n, gemv_b, routed_b in cases:
-        lay = _layer(q, m=m, n=n, had_in=min(n & -n, 16384), had_out=min(m & -m, 16384))
-        for b in gemv_b:
-            assert q.qdec_workspace_bytes(lay, b, q.QDEC_OP_GEMV) == plain(m, n, b), (m, n, b)
-        for b in routed_b:
-            extra = q.qdec_workspace_bytes(lay, b, q.QDEC_OP_GEMV) - plain(m, n, b)
-            assert extra > 0 and extra % (b * m * 4) == 0, (m, n, b, extra)
+def test_group_workspace_sizes(q):
+    """qdec_gemv_group: one set of fp32 range slices per layer (m rows each,
+    256-byte aligned), with one column range for the whole group."""
+    # q, k, v of the Llama-8B layer: 48 panels of 128 rows; ranges of 1024
+    # columns give 192 units (one round of 256 workgroups, 4 steps per
+    # quarter); 4 slices per layer
+    qq = _layer(q, m=4096, n=4096, had_in=4096, had_out=4096)
+    kk = _layer(q, m=1024, n=4096, had_in=4096, had_out=1024)
+    vv = _layer(q, m=1024, n=4096, had_in=4096, had_out=1024)
+    assert q.qdec_gemv_group_workspace_bytes([qq, kk, vv]) == 4 * 4 * (4096 + 1024 + 1024)
+    # gate and up: 224 panels, one range of 4096 columns (224 units)
+    g = _layer(q, m=14336, n=4096, had_in=4096, had_out=2048)
+    assert q.qdec_gemv_group_workspace_bytes([g, g]) == 2 * 14336 * 4
+    # a bad layer, no layers, too many layers: 0
+    assert q.qdec_gemv_group_workspace_bytes([qq, _layer(q, m=100)]) == 0
+    assert q.qdec_gemv_group_workspace_bytes([]) == 0
+    assert q.qdec_gemv_group_workspace_bytes([qq] * 9) == 0
 
 
 BAD_LAYERS = [
@@ -209,3 +215,39 @@ def test_encode_workspace_and_argument_errors(q):
         bad = _layer(q, **kw)
         assert q.raw_status("qdec_encode", ctypes.byref(bad.desc()), W, C, WS, need, None) in (
             q.QDEC_EINVAL, q.QDEC_EUNSUPPORTED)
+
+
+def test_group_call_errors_before_any_launch(q):
+    """qdec_gemv_group rejects bad arguments on the host; with valid
+    arguments and no device it returns ENODEV (nothing is dereferenced)."""
+    import ctypes as C
+    a = _layer(q, m=256, n=128)
+    b = _layer(q, m=384, n=128, had_out=128)
+    layers = [a, b]
+    descs = [l.desc() for l in layers]
+    lp = (C.c_void_p * 2)(*[C.addressof(d) for d in descs])
+    X0, X1 = FAKE + (1 << 24), FAKE + (1 << 24) + 4096
+    Y0, Y1 = FAKE + (1 << 25), FAKE + (1 << 25) + 4096
+    WS = FAKE + (1 << 26)
+    need = q.qdec_gemv_group_workspace_bytes(layers)
+    assert need > 0
+    xp = (C.c_void_p * 2)(X0, X1)
+    yp = (C.c_void_p * 2)(Y0, Y1)
+    E, EW = q.QDEC_EINVAL, q.QDEC_EWORKSPACE
+    st = lambda *args: q.raw_status("qdec_gemv_group", *args)
+    assert st(None, 2, xp, yp, WS, need, None) == E
+    assert st(lp, 0, xp, yp, WS, need, None) == E
+    assert st(lp, 9, xp, yp, WS, need, None) == q.QDEC_EUNSUPPORTED
+    assert st(lp, 2, None, yp, WS, need, None) == E
+    assert st(lp, 2, (C.c_void_p * 2)(X0 + 2, X1), yp, WS, need, None) == E        # misaligned x
+    assert st(lp, 2, xp, (C.c_void_p * 2)(Y0, Y1 + 2), WS, need, None) == E        # misaligned y
+    assert st(lp, 2, xp, (C.c_void_p * 2)(Y0, Y0 + 256), WS, need, None) == E      # outputs overlap
+    assert st(lp, 2, xp, (C.c_void_p * 2)(X0, Y1), WS, need, None) == E            # output on an input
+    assert st(lp, 2, xp, yp, WS, need - 256, None) == EW                          # too small
+    assert st(lp, 2, xp, yp, WS + 16, need, None) == EW                           # misaligned
+    assert st(lp, 2, xp, yp, None, need, None) == EW
+    bad = [_layer(q, m=100).desc(), descs[1]]
+    assert st((C.c_void_p * 2)(*[C.addressof(d) for d in bad]), 2, xp, yp, WS, need, None) == E
+    # inputs may be shared (q, k and v read one x)
+    assert st(lp, 2, (C.c_void_p * 2)(X0, X0), yp, WS, need, None) == q.QDEC_ENODEV
+    assert st(lp, 2, xp, yp, WS, need, None) == q.QDEC_ENODEV
