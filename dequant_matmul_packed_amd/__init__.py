@@ -25,7 +25,8 @@ QDEC_ABI_VERSION = 2
 # The exported symbols, as declared in include/qdec.h.
 EXPORTS = ("qdec_abi_version", "qdec_status_string", "qdec_last_error", "qdec_workspace_bytes",
            "qdec_rht", "qdec_gemv", "qdec_gemm", "qdec_decode_tile", "qdec_encode",
-           "qdec_gemv_group", "qdec_gemv_group_workspace_bytes")
+           "qdec_gemv_group", "qdec_gemv_group_workspace_bytes", "qdec_gemv_noalloc",
+           "qdec_noalloc_scratch_bytes")
 GEMV_GROUP_MAX = 8
 
 
@@ -79,6 +80,10 @@ def _load():
     lib.qdec_gemv_group.argtypes = [P, i32, P, P, P, ctypes.c_size_t, P]
     lib.qdec_gemv_group_workspace_bytes.restype = ctypes.c_size_t
     lib.qdec_gemv_group_workspace_bytes.argtypes = [P, i32]
+    lib.qdec_gemv_noalloc.restype = ctypes.c_int
+    lib.qdec_gemv_noalloc.argtypes = [P, P, P, i64, P]
+    lib.qdec_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.qdec_noalloc_scratch_bytes.argtypes = []
     if lib.qdec_abi_version() != QDEC_ABI_VERSION:
         raise ImportError("libqdec.so ABI version mismatch")
     return lib
@@ -174,6 +179,15 @@ def qdec_rht(inp, in_dtype: int, out, out_dtype: int, rows: int, n: int, block: 
 def qdec_gemv(layer: Layer, x, y, batch: int, ws, ws_bytes: int, stream=None) -> None:
     _check(_lib.qdec_gemv(ctypes.byref(layer.desc()), _ptr(x), _ptr(y), batch, _ptr(ws), ws_bytes,
                           _stream(stream)), "qdec_gemv")
+
+
+def qdec_gemv_noalloc(layer: Layer, x, y, batch: int, stream=None) -> None:
+    _check(_lib.qdec_gemv_noalloc(ctypes.byref(layer.desc()), _ptr(x), _ptr(y), batch, _stream(stream)),
+           "qdec_gemv_noalloc")
+
+
+def qdec_noalloc_scratch_bytes() -> int:
+    return int(_lib.qdec_noalloc_scratch_bytes())
 
 
 def qdec_gemm(layer: Layer, x, y, batch: int, ws, ws_bytes: int, stream=None) -> None:

@@ -719,6 +719,61 @@ int qdec_gemv(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
   return status_of(launch_gemv_finish(f, s));
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// qdec_gemv_noalloc: qdec_gemv with its workspace in a static device array of
+// this file, for callers that cannot allocate.  Each device the library runs
+// on holds its own copy of the array until the process ends; its address on
+// a device is looked up once (hipGetSymbolAddress, with that device current)
+// and kept per device.  Host code never passes the array's name itself to a
+// kernel or a copy: on the host that name is only a stand-in, not a device
+// address.
+namespace {
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::atomic<void*> g_scratch_ptr[64];
+
+// The device address of this device's scratch, or nullptr (status in *st).
+void* scratch_address(int* st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    *st = QDEC_ENODEV;
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    *st = status_of(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    return nullptr;
+  }
+  // concurrent first calls store the same address
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+}  // namespace
+
+extern "C" {
+
+size_t qdec_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int qdec_gemv_noalloc(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t batch, void* stream) {
+  LayerArgs L;
+  const int st = check_layer(layer, &L);
+  if (st) return st;
+  if (batch < 1) return QDEC_EINVAL;
+  if (batch > 8) return QDEC_EUNSUPPORTED;
+  if (gemv_ws_bytes(L.m, L.n, batch) > kNoAllocScratchBytes) return QDEC_EWORKSPACE;
+  const int d = check_device();
+  if (d) return d;
+  int ast = QDEC_OK;
+  void* ws = scratch_address(&ast);
+  if (!ws) return ast;
+  return qdec_gemv(layer, x, y, batch, ws, kNoAllocScratchBytes, stream);
+}
+
 size_t qdec_gemv_group_workspace_bytes(const qdec_layer* const* layers, int32_t count) {
   if (!layers || count < 1 || count > GEMV_GROUP_MAX) return 0;
   int64_t pm[2 * GEMV_GROUP_MAX], pn[2 * GEMV_GROUP_MAX];

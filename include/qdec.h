@@ -206,6 +206,22 @@ int qdec_rht(const void *in, int32_t in_dtype, void *out, int32_t out_dtype,
 int qdec_gemv(const qdec_layer *layer, const uint16_t *x, uint16_t *y,
               int64_t batch, void *ws, size_t ws_bytes, void *stream);
 
+/* qdec_gemv without a caller-provided workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static device array
+ * of qdec_noalloc_scratch_bytes() = 8 MiB inside the library: each device
+ * holds its own copy until the process ends; the call itself allocates and
+ * frees nothing.  Layers whose qdec_gemv workspace at this batch exceeds it
+ * return QDEC_EWORKSPACE before any launch.  Every call on one device shares
+ * that device's array: calls that overlap in time on one device (other
+ * streams, other threads) race and must be ordered by the caller.  Nothing in
+ * the array needs to start at zero.  Otherwise as qdec_gemv.                 */
+int qdec_gemv_noalloc(const qdec_layer *layer, const uint16_t *x, uint16_t *y, int64_t batch,
+                      void *stream);
+
+/* Bytes of the static workspace of qdec_gemv_noalloc.                         */
+size_t qdec_noalloc_scratch_bytes(void);
+
 /* Several independent one-column products in one call (the projections of
  * a decoder layer that read the same activations, e.g. q, k and v, or gate
  * and up): y[l] = layers[l](x[l]) for l < count <= 8, each as qdec_gemv at

@@ -251,3 +251,19 @@ def test_group_call_errors_before_any_launch(q):
     # inputs may be shared (q, k and v read one x)
     assert st(lp, 2, (C.c_void_p * 2)(X0, X0), yp, WS, need, None) == q.QDEC_ENODEV
     assert st(lp, 2, xp, yp, WS, need, None) == q.QDEC_ENODEV
+
+
+def test_noalloc_entry_point_rejects_before_any_launch(q):
+    """qdec_gemv_noalloc: its static workspace is 8 MiB; a call whose
+    qdec_gemv workspace would exceed it returns QDEC_EWORKSPACE, and bad
+    descriptors or batches are rejected, all before touching a device."""
+    assert q.qdec_noalloc_scratch_bytes() == 8 << 20
+    big = _layer(q, m=128, n=1 << 20, had_in=16384, had_out=128)
+    assert q.qdec_workspace_bytes(big, 8, q.QDEC_OP_GEMV) > q.qdec_noalloc_scratch_bytes()
+    X, Y = FAKE + (1 << 24), FAKE + (1 << 25)
+    st = lambda lay, b: q.raw_status("qdec_gemv_noalloc", ctypes.byref(lay.desc()), X, Y, b, None)
+    assert st(big, 8) == q.QDEC_EWORKSPACE
+    assert st(_layer(q, m=100), 1) == q.QDEC_EINVAL
+    assert st(_layer(q), 0) == q.QDEC_EINVAL
+    assert st(_layer(q), 9) == q.QDEC_EUNSUPPORTED
+    assert st(_layer(q), 1) == q.QDEC_ENODEV          # valid: no device here
