@@ -1,27 +1,35 @@
 #!/usr/bin/env python3
 """Benchmark of the fused dequant-GEMV (batch 1) and the MFMA GEMM (batch 64).
 
-Headline (one JSON line on stdout): packed-code HBM GB/s of the fused GEMV
-on the 4096x4096 computed-code layer set -- 1MAD and 3INST, k = 2, 3, 4,
-V = 1, RHT 4096 with random signs, x ~ N(0,1) fp16, batch 1.  One step runs
-one fused GEMV per layer of the set (six launches); consecutive steps use
-different, equally random code buffers from a pool larger than the 256 MiB
-Infinity Cache, so every step reads its codes from HBM.  Inputs are resident
-in HBM before the timed region.  The line also carries:
-  roofline      the dominant kernel's achieved algorithmic bytes per launch
-                over its average launch duration (HIP events on its stream),
-                against the 8 TB/s HBM peak
+Headline (one JSON line on stdout): packed-code HBM GB/s, and microseconds
+per layer, of the seven linear layers of a Llama-3-8B-shaped decoder layer
+(q, o 4096x4096; k, v 1024x4096; gate, up 14336x4096; down 4096x14336), HYB
+trellis codes at 2 bits per weight (L = 16, V = 2, Q = 9), RHT on both sides,
+batch 1.  One step is one pass through a stack of 64 such layers, each with
+codes of its own (3.49 GB per step, 13.6 times the 256 MiB Infinity Cache,
+so every layer reads its codes from HBM), in the order a decoder layer runs
+them: q, k and v in one grouped call (they read the same activations), o,
+gate and up in one grouped call, down.  Inputs are resident in HBM before the
+timed region.  The line also carries:
+  roofline      the dominant call of a layer -- the grouped gate+up call
+                (its MFMA GEMV kernel and its finisher) -- as algorithmic
+                bytes per call over its event-timed duration, against the
+                8 TB/s HBM peak
+  roofline_b64  the batch-64 GEMM on the 28672x8192 up-projection (HYB k=3):
+                TFLOP/s per call against the 2.5 PFLOP/s fp16 MFMA peak
   cpu_baseline  the CPU oracle (decode, O(B^2) Hadamard, fp64 matvec) on a
                 bounded sample of the same workload, on the host cores
-  detail        per-variant kernel times, the Llama-3-8B-shaped decoder layer
-                (microseconds per layer at batch 1 and 8) and the batch-64
-                GEMM on the 28672x8192 up-projection (TFLOP/s vs fp16 MFMA peak)
+  detail        per-projection times, the layer at batch 8 and with fused
+                projections, the single-layer configurations, the measured
+                ceilings of this GPU and the pages' decode-cost figures
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -31,27 +39,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_F16_PEAK_TFLOPS = 2500.0
-POOL_MIB = 1152
+MFMA_F16_PEAK_TFLOPS = 2516.6          # 256 CUs x 2.4 GHz x 4096 fp16 flop per clock, dense
 POOL_BYTES = 1 << 30
+STACK_LAYERS = 64
 METRIC = "fused dequant-GEMV HBM GB/s + µs/layer (b=1); GEMM TFLOP/s (b=64)"
+CSRC = os.path.join(ROOT, "dequant_matmul_packed_amd", "csrc")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--pool-mib", type=int, default=POOL_MIB)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=STACK_LAYERS,
+                    help="distinct Llama-3-8B-shaped layers per step (codes of their own each)")
+    ap.add_argument("--launch", choices=("auto", "graph", "direct"), default="auto",
+                    help="replay each step from one HIP graph, launch its calls directly, or time "
+                         "both before the timed region and take the faster")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-detail", action="store_true")
-    ap.add_argument("--only", default="", help="restrict the step to one variant, e.g. 3INST_k4")
-    ap.add_argument("--eager", action="store_true",
-                    help="(the default) launch every GEMV of a step directly")
-    ap.add_argument("--graphs", action="store_true",
-                    help="replay the step's other GEMVs from HIP graphs instead of launching them directly")
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="bracket the dominant call with HIP events on every N-th timed step")
+    ap.add_argument("--full-detail", action="store_true",
+                    help="add the encoder, bit-width and code-variant tables (several minutes)")
     ap.add_argument("--layer", default="",
                     help="only run 8 direct calls of one layer, CODE:M:N:K:B (e.g. HYB:28672:8192:2:1; "
                          "B > 8 takes qdec_gemm), for counter collection; prints no JSON line")
@@ -59,6 +67,27 @@ def parse():
                     help="after the timed region, copy this many MiB device-to-device 5 times "
                          "(a plain copy of known size to scale HBM counters by)")
     return ap.parse_args()
+
+
+def code_only(text: str) -> str:
+    """The source without comments, trailing spaces and blank lines: what the
+    compiler sees (a comment edit does not change the profiled kernels)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
+def kernel_source_hash(csrc: str = CSRC) -> str:
+    """Hash of the kernel sources (code only), stored with counter summaries
+    so that the bench reports HBM traffic only while the kernels are the
+    ones that were profiled."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                h.update(code_only(f.read()).encode())
+    return h.hexdigest()[:16]
 
 
 def log(*a):
@@ -158,15 +187,171 @@ def time_events(torch, fn, reps):
     return sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3  # us
 
 
+
+class GroupLaunch:
+    """One pre-marshalled qdec_gemv_group call (its pointer arrays built
+    once).  It holds the layers and tensors it passes by pointer, so their
+    memory stays mapped while the call can run; it takes torch's current
+    stream at call time, so it can be captured into a graph."""
+
+    def __init__(self, q, layers, xs, ys, ws):
+        self.fn = q._lib.qdec_gemv_group
+        self.call = q.GroupCall(layers, xs, ys)
+        self.keep = (list(layers), list(xs), list(ys), ws)
+        self.ws, self.nbytes = ws.data_ptr(), ws.numel()
+
+    def __call__(self):
+        import torch
+        st = self.fn(self.call.lp, self.call.count, self.call.xp, self.call.yp, self.ws, self.nbytes,
+                     torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError("qdec_gemv_group failed with status %d" % st)
+
+
+def call_bytes(layers, b=1):
+    """Algorithmic HBM bytes of one call over these layers at batch b: packed
+    codes, fp16 x and y, both sign vectors and the code tables."""
+    return sum(L.code_bytes + 2 * b * (L.n + L.m) + (L.m + L.n) // 8 + tensor_bytes(L.lut)
+               + tensor_bytes(L.group_scale) for L in layers)
+
+
+def time_calls(torch, calls, reps=5, ncalls=200):
+    """Median over reps of the event-timed average of ncalls back-to-back
+    calls (rotating through `calls`), on the current stream, in us."""
+    for i in range(20):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out, j = [], 0
+    for r in range(reps):
+        e0.record()
+        for i in range(ncalls):
+            calls[j % len(calls)]()
+            j += 1
+        e1.record()
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3 / ncalls)
+    return float(np.median(out))
+
+
+def llama_stack(q, torch, dev, args):
+    """The headline: a stack of Llama-3-8B-shaped layers at batch 1, each layer
+    with codes of its own.  Returns the JSON fields."""
+    import synth
+    wl = synth.WORKLOADS["llama3_8b_layer"]
+    specs = {s.name: s for s in wl.layers}
+    L = args.layers
+    pools, lay = [], {}
+    for name, s in specs.items():
+        layers, pool, base = make_pool_layers(q, torch, dev, s.code, s.m, s.n, s.k, L, "bench/stack/" + name)
+        pools.append(pool)
+        lay[name] = layers
+    layer_bytes = sum(lay[nm][0].code_bytes for nm in specs)
+    step_bytes = layer_bytes * L
+    # each group reads its own activations (in a model: the normed residual,
+    # the attention output, the normed residual, the gated product)
+    xt = {g: torch.from_numpy(synth.activations("bench/stack/x_" + g, 1, n).view(np.int16)).to(dev)
+          for g, n in (("qkv", 4096), ("o", 4096), ("gate_up", 4096), ("down", 14336))}
+    ys = {nm: torch.empty((1, s.m), dtype=torch.float16, device=dev) for nm, s in specs.items()}
+    ws_qkv = torch.empty(q.qdec_gemv_group_workspace_bytes([lay[n][0] for n in ("q", "k", "v")]),
+                         dtype=torch.uint8, device=dev)
+    ws_gu = torch.empty(q.qdec_gemv_group_workspace_bytes([lay[n][0] for n in ("gate", "up")]),
+                        dtype=torch.uint8, device=dev)
+    ws_o = q.workspace(lay["o"][0], 1, q.QDEC_OP_GEMV, dev)
+    ws_d = q.workspace(lay["down"][0], 1, q.QDEC_OP_GEMV, dev)
+    calls = {"qkv": [], "o": [], "gate_up": [], "down": []}
+    for l in range(L):
+        calls["qkv"].append(GroupLaunch(q, [lay[n][l] for n in ("q", "k", "v")], [xt["qkv"]] * 3,
+                                        [ys["q"], ys["k"], ys["v"]], ws_qkv))
+        calls["o"].append(LazyLaunch(q, "qdec_gemv", lay["o"][l], xt["o"], ys["o"], 1, ws_o))
+        calls["gate_up"].append(GroupLaunch(q, [lay[n][l] for n in ("gate", "up")], [xt["gate_up"]] * 2,
+                                            [ys["gate"], ys["up"]], ws_gu))
+        calls["down"].append(LazyLaunch(q, "qdec_gemv", lay["down"][l], xt["down"], ys["down"], 1, ws_d))
+
+    def step():
+        for l in range(L):
+            calls["qkv"][l]()
+            calls["o"][l]()
+            calls["gate_up"][l]()
+            calls["down"][l]()
+
+    step()                                   # eager first (sets kernel attributes)
+    torch.cuda.synchronize()
+    graph = None
+    if args.launch in ("auto", "graph"):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+
+    def run_graph():
+        graph.replay()
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n
+
+    mode = args.launch
+    probe = {}
+    if mode == "auto":
+        probe["graph_ms_per_step"] = round(timed(run_graph, 2) * 1e3, 3)
+        probe["direct_ms_per_step"] = round(timed(step, 2) * 1e3, 3)
+        mode = "graph" if probe["graph_ms_per_step"] <= probe["direct_ms_per_step"] else "direct"
+    run = run_graph if mode == "graph" else step
+    for i in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    # ---- timed region: exactly `steps` steps --------------------------------
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    for nm, y in ys.items():
+        if not torch.isfinite(y.float()).all():
+            raise RuntimeError("non-finite output in %s" % nm)
+    ms_per_step = elapsed / args.steps * 1e3
+    gbs = step_bytes * args.steps / elapsed / 1e9
+    us_layer = elapsed / (args.steps * L) * 1e6
+    log("stack of %d layers: %d steps in %.4f s (%s): %.1f GB/s packed, %.2f us/layer"
+        % (L, args.steps, elapsed, mode, gbs, us_layer))
+    if args.copy_calibration_mib > 0:
+        nb = args.copy_calibration_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for r in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 5 device-to-device copies of %d MiB" % args.copy_calibration_mib)
+        del src, dst
+    del graph
+    # ---- the calls of a layer, each alone: event-timed, rotating layers ----
+    per_call = {}
+    for g, cs in calls.items():
+        us = time_calls(torch, cs)
+        nb = call_bytes(cs[0].keep[0] if isinstance(cs[0], GroupLaunch) else [cs[0].keep[0]])
+        per_call[g] = {"us": round(us, 2), "algorithmic_bytes": nb, "GBps": round(nb / us / 1e3, 1)}
+    dom_name = max(per_call, key=lambda g: per_call[g]["us"])
+    dom = per_call[dom_name]
+    log("calls of a layer (us):", {g: v["us"] for g, v in per_call.items()})
+    return {"gbs": gbs, "elapsed": elapsed, "ms_per_step": ms_per_step, "us_per_layer": us_layer,
+            "step_bytes": step_bytes, "layer_bytes": layer_bytes, "mode": mode, "probe": probe,
+            "per_call": per_call, "dominant": dom_name, "dom": dom}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU; the library has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU: every GPU box here has one, and the library's calls run on one "
+              "device (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
     import dequant_matmul_packed_amd as q
-    import synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -174,211 +359,113 @@ def main():
     if args.layer:
         run_one_layer(q, torch, dev, stream, args.layer)
         return
-
-    # ---- the headline workload: 4096x4096 computed codes, b = 1 -----------
-    wl = synth.WORKLOADS["computed4096"]
-    specs = [s for s in wl.layers if not args.only or s.name == args.only]
-    step_bytes = sum(s.m * s.n * s.k // 8 for s in specs)
-    P = max(2, int(args.pool_mib * 2 ** 20 // step_bytes))
-    log("workload %s: %d layers per step, %.1f MiB codes per step, pool of %d steps"
-        % (wl.name, len(specs), step_bytes / 2 ** 20, P))
-    x16 = synth.activations(wl.name + "/x", 1, 4096)
-    x = torch.from_numpy(x16.view(np.int16)).to(dev)
-    variants = []
-    keep = []
-    for s in specs:
-        layers, pool, base = make_pool_layers(q, torch, dev, s.code, s.m, s.n, s.k, P, wl.name + "/" + s.name)
-        keep.append(pool)
-        ws = q.workspace(base, 1, q.QDEC_OP_GEMV, dev)
-        y = torch.empty((1, s.m), dtype=torch.float16, device=dev)
-        launches = [LazyLaunch(q, "qdec_gemv", L, x, y, 1, ws) for L in layers]
-        variants.append(dict(spec=s, launches=launches, layers=layers, y=y, ws=ws,
-                             bytes=algorithmic_bytes(s.m, s.n, s.k, 1)))
-    torch.cuda.synchronize()
-
-    # One step = the six fused GEMVs on one pool slot, launched directly
-    # (replaying the step from HIP graphs measured slower on this stack:
-    # 74 against 70 us per step).  On every N-th timed step the dominant
-    # variant's call is bracketed by two HIP events (created before the timed
-    # region) on the stream it runs on; an event pair costs the GPU about 9 us
-    # per step (it waits for the queue to drain), so it is sampled, not taken
-    # on every step.
-    def capture(fn):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn()
-        return g
-
-
-    for v in variants:          # warm the launch paths once, eagerly
-        v["launches"][0]()
-    torch.cuda.synchronize()
-    per_variant = {}
-    for v in variants:          # per-variant GEMV time, graph of 20 calls
-        g = capture(lambda v=v: [v["launches"][j % P]() for j in range(20)])
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for r in range(5):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        per_variant[v["spec"].name] = e0.elapsed_time(e1) * 1e3 / 100
-        del g
-    # the dominant variant: the longest call; variants within 2 % of it are
-    # the same time within noise, and among them the one moving most bytes
-    longest = max(per_variant.values())
-    dom = max((v for v in variants if per_variant[v["spec"].name] >= 0.98 * longest),
-              key=lambda v: v["bytes"])
-    log("per-variant us per GEMV (graph replay):", {k: round(t, 2) for k, t in per_variant.items()})
-    others = [v for v in variants if v is not dom]
-    if not args.graphs:
-        graphs = None
-        direct = [[Launch(q, "qdec_gemv", L, x, v["y"], 1, v["ws"], stream) for L in v["layers"]]
-                  for v in others]
-
-        def eager_others(i):
-            for d in direct:
-                d[i % P]()
-    else:
-        graphs = [capture(lambda i=i: [v["launches"][i]() for v in others]) for i in range(P)] if others else None
-    dom_launch = [Launch(q, "qdec_gemv", L, x, dom["y"], 1, dom["ws"], stream)
-                  for L in dom["layers"]]
-    dom_call = dom_launch
-
-    def step(i, ev=None):
-        if graphs is not None:
-            graphs[i % P].replay()
-        else:
-            eager_others(i)
-        if ev is not None:
-            ev[0].record()
-            dom_call[i % P]()
-            ev[1].record()
-        else:
-            dom_call[i % P]()
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # ---- timed region: exactly `steps` steps ---------------------------------
-    every = max(1, args.event_every)
-    dom_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for i in range(0, args.steps, every)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i + args.warmup, dom_events[i // every] if i % every == 0 else None)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
-    ms_per_step = elapsed / args.steps * 1e3
-    gbs = step_bytes * args.steps / elapsed / 1e9
-    dom_us = sum(a.elapsed_time(b) for a, b in dom_events) / len(dom_events) * 1e3
-    dom_gbs = dom["bytes"] / (dom_us * 1e-6) / 1e9
-    log("timed %d steps in %.4f s: %.1f GB/s packed, %.2f us/layer; dominant %s %.2f us"
-        % (args.steps, elapsed, gbs, ms_per_step * 1e3 / len(variants), dom["spec"].name, dom_us))
-
-    if args.copy_calibration_mib > 0:
-        nbytes = args.copy_calibration_mib << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for r in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("copy calibration: 5 device-to-device copies of %d MiB" % args.copy_calibration_mib)
-        del src, dst
-
-    # sanity: outputs are finite
-    for v in variants:
-        if not torch.isfinite(v["y"].float()).all():
-            raise RuntimeError("non-finite output in %s" % v["spec"].name)
-
-    detail = {"per_variant_kernel_us": {k: round(t, 3) for k, t in per_variant.items()},
-              "us_per_layer": round(ms_per_step * 1e3 / len(variants), 3),
-              "pool_steps": P}
-    if not args.no_detail and not args.only:
+    H = llama_stack(q, torch, dev, args)
+    torch.cuda.empty_cache()
+    G = bench_gemm(q, torch, dev, stream)
+    dom = H["dom"]
+    kernels = {"gate_up": "qdec_gemv_group over gate and up (gemv_mma_kernel + gemv_finish_kernel)",
+               "qkv": "qdec_gemv_group over q, k, v (gemv_mma_kernel + gemv_finish_kernel)",
+               "down": "qdec_gemv 4096x14336 (gemv_mma_kernel + gemv_finish_kernel)",
+               "o": "qdec_gemv 4096x4096 (gemv_kernel + gemv_finish_kernel)"}
+    traffic = measured_traffic(H["dominant"])
+    detail = {"per_call_of_a_layer": H["per_call"], "launch_probe": H["probe"],
+              "gemm_b64_up70b": G}
+    if not args.no_detail:
+        detail.update(bench_projections(q, torch, dev, stream))
         detail.update(bench_llama_layer(q, torch, dev, stream))
         detail.update(bench_llama_layer(q, torch, dev, stream, "llama3_8b_layer_fused"))
-        detail.update(bench_gemm(q, torch, dev, stream))
         detail.update(bench_configs(q, torch, dev, stream))
-        detail.update(bench_code_variants(q, torch, dev, stream))
-        detail.update(bench_fractional(q, torch, dev, stream))
-        detail.update(bench_encoder(q, torch, dev, cpu=not args.no_cpu_baseline))
         detail.update(bench_rht(q, torch, dev, stream))
-
-    if not args.no_detail and not args.only:
         detail["pages_context"] = pages_context()
         ceil = measured_ceilings(torch, dev)
         detail["measured_ceilings"] = ceil
-        g = detail.get("gemm_b64_up70b")
-        if g:
-            g["frac_of_measured_fp16_matmul"] = round(g["TFLOPs"] / ceil["fp16_matmul_8192_TFLOPs"], 4)
-        detail["headline_frac_of_measured_copy"] = round(dom_gbs / ceil["copy_GBps_read_plus_write"], 4)
-        detail["headline_frac_of_measured_read"] = round(dom_gbs / ceil["read_GBps_colsum_1GiB"], 4)
-        for v in detail["configs_b1"].values():
-            v["frac_of_measured_read"] = round(v["algorithmic_GBps"] / ceil["read_GBps_colsum_1GiB"], 4)
+        G["frac_of_measured_fp16_matmul"] = round(G["TFLOPs"] / ceil["fp16_matmul_8192_TFLOPs"], 4)
+        detail["dominant_frac_of_measured_read"] = round(dom["GBps"] / ceil["read_GBps_colsum_1GiB"], 4)
+    if args.full_detail:
+        detail.update(bench_code_variants(q, torch, dev, stream))
+        detail.update(bench_fractional(q, torch, dev, stream))
+        detail.update(bench_encoder(q, torch, dev, cpu=not args.no_cpu_baseline))
     cpu = None
     if not args.no_cpu_baseline:
-        cpu, cpu_detail = cpu_baseline(specs, x16)
-        if not args.no_detail and not args.only:
+        cpu, cpu_detail = cpu_baseline()
+        if not args.no_detail:
             cpu_detail["per_config"] = cpu_per_config()
         detail["cpu_oracle"] = cpu_detail
-
-    # HBM bytes per call of the dominant variant from the committed counter
-    # summary (None once the kernel sources differ from the profiled ones)
-    traffic = measured_traffic(dom["spec"], dom_us)
     line = {
         "metric": METRIC,
-        "value": round(gbs, 2),
+        "value": round(H["gbs"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(H["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16 (codes k=2,3,4 bit; fp32 accumulate)",
-        "data": "synthetic: seeded random code words, N(0,1) fp16 activations, random signs",
-        "config": {"workload": "4096x4096 linear, 1MAD and 3INST computed codes, k=2,3,4, V=1, "
-                               "RHT 4096/4096, batch 1 (six fused GEMVs per step)",
-                   "global_batch": 1, "layers_per_step": len(variants),
-                   "packed_bytes_per_step": step_bytes, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "qdec_gemv %s k=%d b=1 (gemv_kernel + gemv_finish_kernel)"
-                     % (synth.CODE_NAMES[dom["spec"].code], dom["spec"].k),
-                     "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+        "dtype": "fp16 in/out, fp32 accumulate; 2-bit HYB codes",
+        "data": "synthetic: seeded random code words (every word stream is a valid trellis walk), "
+                "N(0,1) fp16 activations, random signs; no trained weights",
+        "us_per_layer": round(H["us_per_layer"], 2),
+        "config": {"workload": "Llama-3-8B-shaped decoder layers (q, o 4096x4096; k, v 1024x4096; gate, up "
+                               "14336x4096; down 4096x14336), HYB k=2 V=2 Q=9, RHT both sides, batch 1; "
+                               "one step = %d distinct layers, each as qkv group, o, gate+up group, down"
+                               % args.layers,
+                   "global_batch": 1, "layers_per_step": args.layers,
+                   "packed_bytes_per_layer": H["layer_bytes"], "packed_bytes_per_step": H["step_bytes"],
+                   "launch": H["mode"], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": kernels.get(H["dominant"], H["dominant"]),
+                     "achieved": dom["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom["GBps"] / HBM_PEAK_GBS, 4),
                      "traffic": traffic["bytes_per_call"] if traffic else None,
                      "traffic_detail": traffic,
-                     "bytes_per_launch": dom["bytes"], "avg_launch_us": round(dom_us, 3)},
+                     "bytes_per_launch": dom["algorithmic_bytes"], "avg_launch_us": dom["us"],
+                     "timing": "HIP events around 200 back-to-back calls on the launch stream (codes "
+                               "rotating over the stack's layers), median of 5; a call is two kernels"},
+        "roofline_b64": {"bound": "mfma", "kernel": "qdec_gemm 28672x8192 HYB k=3, X 64x8192 "
+                                                    "(rht_split_kernel + gemm_kernel + rht_kernel)",
+                         "achieved": G["TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(G["TFLOPs"] / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                         "flops_per_launch": G["flops"], "avg_launch_us": G["us_per_call"],
+                         "timing": G["protocol"]},
         "cpu_baseline": cpu,
         "detail": detail,
     }
     print(json.dumps(line), flush=True)
 
 
-def measured_traffic(spec, us):
-    """HBM bytes per call of this variant from the committed counter summary
-    (profiles/gemv_hbm_traffic.json), as GB/s over the measured call time;
-    None when the kernels changed since the counters were taken."""
-    import synth
-    path = os.path.join(ROOT, "profiles", "gemv_hbm_traffic.json")
+def measured_traffic(call):
+    """HBM bytes per call of the dominant call from the committed counter
+    summary (profiles/traffic.json), or None when there is none for it or the
+    kernel sources differ from the profiled ones."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    import profile_traffic
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != profile_traffic.kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    v = rec["variants"].get("%s_k%d" % (synth.CODE_NAMES[spec.code], spec.k))
+    v = rec.get("calls", {}).get(call)
     if v is None:
         return None
-    return {"bytes_per_call": int(v["bytes_per_call"]), "GBps": round(v["bytes_per_call"] / (us * 1e-6) / 1e9, 2),
-            "over_algorithmic": round(v["bytes_per_call"] / v["algorithmic"], 3),
-            "source": "profiles/gemv_hbm_traffic.md (FETCH_SIZE, WRITE_SIZE scaled by a 256 MiB copy)"}
+    return {"bytes_per_call": int(v["bytes_per_call"]), "over_algorithmic": round(v["over_algorithmic"], 3),
+            "source": "profiles/traffic.md (FETCH_SIZE, WRITE_SIZE scaled by a 256 MiB copy)"}
+
+
+def bench_projections(q, torch, dev, stream):
+    """Each projection shape of the Llama-3-8B layer alone at batch 1, timed
+    as in time_layer (codes rotating through a pool of at least 1 GiB)."""
+    import synth
+    out = {}
+    seen = set()
+    for s in synth.WORKLOADS["llama3_8b_layer"].layers:
+        if (s.m, s.n) in seen:
+            continue
+        seen.add((s.m, s.n))
+        us, base = time_layer(q, torch, dev, stream, s.code, s.m, s.n, s.k, 1, "bench/proj/%dx%d" % (s.m, s.n))
+        out["%dx%d" % (s.m, s.n)] = {"us_per_call": round(us, 2),
+                                     "packed_GBps": round(base.code_bytes / (us * 1e-6) / 1e9, 1)}
+    log("projections b=1:", {k: v["us_per_call"] for k, v in out.items()})
+    return {"projections_b1": out}
 
 
 def bench_llama_layer(q, torch, dev, stream, name="llama3_8b_layer"):
@@ -509,7 +596,8 @@ def time_4096_variants(q, torch, dev, stream, variants, tagbase):
 
 def bench_configs(q, torch, dev, stream):
     """The single-layer configurations at batch 1, timed as in time_layer:
-    the 4096x4096 HYB k=2 layer (V=2, Q=9, 512-pair table), and the
+    the 4096x4096 HYB k=2 layer (V=2, Q=9, 512-pair table), the same shape
+    with the computed codes (1MAD, 3INST at k = 2, 3, 4), and the
     4096x14336 down-projection shape with the 3-bit non-uniform scalar
     quantizer (fp16 scale per 128 weights) and with the 2-D vector quantizer
     (8-bit index per weight pair).  GB/s on the packed codes, and on the
@@ -517,13 +605,15 @@ def bench_configs(q, torch, dev, stream):
     fraction of the 8 TB/s HBM peak."""
     import synth
     out = {}
-    for wname in ("hyb4096", "down_nuq", "down_vq"):
-        s = synth.WORKLOADS[wname].layers[0]
+    cases = [("hyb4096", synth.WORKLOADS["hyb4096"].layers[0])]
+    cases += [("computed4096/" + s.name, s) for s in synth.WORKLOADS["computed4096"].layers]
+    cases += [("down_nuq", synth.WORKLOADS["down_nuq"].layers[0]), ("down_vq", synth.WORKLOADS["down_vq"].layers[0])]
+    for wname, s in cases:
         kw = dict(scale=s.scale)
         us, base = time_layer(q, torch, dev, stream, s.code, s.m, s.n, s.k, 1, "bench/cfg/" + wname, **kw)
         alg = (base.code_bytes + 2 * s.n + 2 * s.m + (s.m + s.n) // 8 + tensor_bytes(base.lut)
                + tensor_bytes(base.group_scale))
-        out[wname] = {"layer": synth.WORKLOADS[wname].description, "us_per_call": round(us, 2),
+        out[wname] = {"layer": synth.WORKLOADS[wname.split("/")[0]].description, "us_per_call": round(us, 2),
                       "packed_bytes": base.code_bytes, "algorithmic_bytes": alg,
                       "packed_GBps": round(base.code_bytes / (us * 1e-6) / 1e9, 1),
                       "algorithmic_GBps": round(alg / (us * 1e-6) / 1e9, 1),
@@ -621,47 +711,55 @@ def bench_gemm(q, torch, dev, stream):
     flops = 2.0 * s.m * s.n * b
     tf = flops / (us * 1e-6) / 1e12
     log("gemm b=64: %.1f us, %.1f TFLOP/s" % (us, tf))
-    return {"gemm_b64_up70b": {"us_per_call": round(us, 2), "TFLOPs": round(tf, 1),
-                               "frac_of_fp16_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                               "launches": "rht_in + gemm + rht_out", "protocol": "time_layer"}}
+    return {"us_per_call": round(us, 2), "TFLOPs": round(tf, 1), "flops": int(flops),
+            "frac_of_fp16_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+            "launches": "rht_in + gemm + rht_out",
+            "protocol": "HIP events around 200 back-to-back calls on the launch stream (codes rotating "
+                        "through a 1 GiB pool), median of 5; a call is three kernels"}
 
 
-def cpu_baseline(specs, x16):
-    """The oracle as it stands, on the host cores: one full forward per layer
-    of the step (decode of every tile, O(B^2) Hadamards, fp64 matvec) with
-    all threads; then, for the detail, decode-only on all threads and both
-    on one thread over the first layer.  It is a correctness reference, not
-    a tuned CPU competitor."""
+def cpu_baseline(min_seconds=10.0, max_reps=8):
+    """The oracle as it stands, on the host cores: full forwards (decode of
+    every tile, O(B^2) Hadamards, fp64 matvec) of the seven projections of one
+    Llama-3-8B-shaped layer at batch 1, repeated until about 10 s of CPU work;
+    then, for the detail, decode-only on all threads and both on one thread
+    over the q projection.  It is a correctness reference, not a tuned CPU
+    competitor."""
     import oracle
     import synth
     threads = oracle.omp_threads()
-    hosts = [s.build("cpu_baseline") for s in specs]
-    nbytes = [s.m * s.n * s.k // 8 for s in specs]
-    nweights = [s.m * s.n for s in specs]
-
-    def timed(fn):
+    wl = synth.WORKLOADS["llama3_8b_layer"]
+    hosts = [s.build("cpu_baseline") for s in wl.layers]
+    xs = {n: synth.activations("cpu_baseline/x%d" % n, 1, n) for n in {h.n for h in hosts}}
+    nbytes = sum(h.code_bytes for h in hosts)
+    nweights = sum(h.m * h.n for h in hosts)
+    reps, t_fwd = 0, 0.0
+    while reps < max_reps and (reps == 0 or t_fwd < min_seconds):
         t0 = time.perf_counter()
-        fn()
-        return time.perf_counter() - t0
-    t_fwd = sum(timed(lambda h=h: oracle.forward(h, x16)) for h in hosts)
-    t_dec = sum(timed(lambda h=h: oracle.decode_tiles_storage(h, 0, h.n_tiles)) for h in hosts)
+        for h in hosts:
+            oracle.forward(h, xs[h.n])
+        t_fwd += time.perf_counter() - t0
+        reps += 1
+    t0 = time.perf_counter()
+    for h in hosts:
+        oracle.decode_tiles_storage(h, 0, h.n_tiles)
+    t_dec = time.perf_counter() - t0
     oracle.set_threads(1)
-    t_fwd1 = timed(lambda: oracle.forward(hosts[0], x16))
-    t_dec1 = timed(lambda: oracle.decode_tiles_storage(hosts[0], 0, hosts[0].n_tiles))
+    t0 = time.perf_counter()
+    oracle.forward(hosts[0], xs[hosts[0].n])
+    t_fwd1 = time.perf_counter() - t0
     oracle.set_threads(threads)
-    gbs = sum(nbytes) / t_fwd / 1e9
-    log("cpu oracle: forward %.2f s for %d layers (%.4f GB/s, %d threads); one thread, one layer: "
-        "forward %.2f s, decode %.2f s" % (t_fwd, len(specs), gbs, threads, t_fwd1, t_dec1))
+    gbs = nbytes * reps / t_fwd / 1e9
+    log("cpu oracle: %d forwards of the 7 projections in %.2f s (%.4f GB/s, %d threads)"
+        % (reps, t_fwd, gbs, threads))
     base = {"value": round(gbs, 5), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "one full forward of each of the %d layers of one step (%.1f MiB of codes), "
-                      "%.2f s" % (len(specs), sum(nbytes) / 2 ** 20, t_fwd)}
+            "sample": "%d full forwards (batch 1) of the 7 projections of one Llama-3-8B-shaped layer "
+                      "(%.1f MiB of codes each), %.1f s" % (reps, nbytes / 2 ** 20, t_fwd),
+            "us_per_layer": round(t_fwd / reps * 1e6, 1)}
     detail = {"affinity_cores": len(os.sched_getaffinity(0)), "threads": threads,
               "forward_GBps": round(gbs, 5),
-              "decode_Mweights_per_s": round(sum(nweights) / t_dec / 1e6, 2),
-              "one_thread_forward_GBps": round(nbytes[0] / t_fwd1 / 1e9, 5),
-              "one_thread_decode_Mweights_per_s": round(nweights[0] / t_dec1 / 1e6, 2),
-              "sample": "all threads: forward and decode-only of the %d layers; one thread: the first "
-                        "layer (%s)" % (len(specs), specs[0].name)}
+              "decode_Mweights_per_s": round(nweights / t_dec / 1e6, 2),
+              "one_thread_forward_q_GBps": round(hosts[0].code_bytes / t_fwd1 / 1e9, 5)}
     return base, detail
 
 

@@ -509,10 +509,14 @@ bool plan_mma(const LayerArgs* L, const LayerParts* P, int count, const uint16_t
 // 4096x4096 13.9 / 13.5, 4096x14336 20.6 / 20.4, 14336x4096 17.6 / 19.1,
 // 28672x4096 22.4 / 26.2, 28672x8192 33.6 / 40.1.  Tuning override
 // QDEC_GEMV_MMA = 0 / 1.
-bool gemv_use_mma(int64_t m, int64_t n) {
+// The other codes stay on the dot-product kernel, whose decoders are cheaper
+// there (NUQ and VQ look up a weight pair in one read of a small table; the
+// MFMA operands need each weight as an exact fp16 value): 4096x14336 NUQ
+// 3-bit 29.6 / 21.7, VQ 4-bit 22.6 / 16.3.
+bool gemv_use_mma(int code, int64_t m, int64_t n) {
   const int forced = tuning("QDEC_GEMV_MMA");
   if (forced >= 0) return forced != 0;
-  return (double)m * (double)n >= 5e7;
+  return code == HYB && (double)m * (double)n >= 5e7;
 }
 
 // Bytes of slices any call of up to b columns on an m x n layer writes: the
@@ -637,7 +641,7 @@ int qdec_gemv(const qdec_layer* layer, const uint16_t* x, uint16_t* y, int64_t b
   uint16_t* xr = (uint16_t*)((char*)ws + wl.xr);
   float* z = (float*)((char*)ws + wl.z);
   const hipStream_t s = (hipStream_t)stream;
-  if (batch == 1 && gemv_use_mma(L.m, L.n)) {
+  if (batch == 1 && gemv_use_mma(L.code, L.m, L.n)) {
     thread_local MmaCall call;
     if (plan_mma(&L, &parts, 1, &x, &y, (char*)z, &call)) return run_mma(call, s);
   }

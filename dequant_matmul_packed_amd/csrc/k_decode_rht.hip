@@ -436,7 +436,7 @@ namespace qdec {
 template <int J>   // float4 chunks per thread: rows_wg <= 4096 J
 __global__ __launch_bounds__(1024) void gemv_finish_kernel(FinishArgs a) {
   extern __shared__ __align__(16) float buf[];
-  constexpr int SU = 8 / J;                       // slices per round of loads
+  constexpr int SU = 16 / J;                      // slices per round of loads (16 float4 per thread)
   int li = 0;
 #pragma unroll
   for (int i = 1; i < GEMV_GROUP_MAX; ++i)

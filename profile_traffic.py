@@ -15,7 +15,6 @@ profiles/gemv_hbm_traffic.json; the JSON carries a hash of the kernel sources
 (comments and blank lines left out) so the bench reports the traffic only
 while the kernels are unchanged.
 """
-import hashlib
 import json
 import os
 import re
@@ -23,27 +22,11 @@ import sqlite3
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+from bench import kernel_source_hash  # noqa: E402  (one definition of the hash)
 CSRC = os.path.join(ROOT, "dequant_matmul_packed_amd", "csrc")
 COPY_MIB = 256
 CODES = {1: "HYB", 2: "1MAD", 3: "3INST", 4: "NUQ", 5: "VQ"}
-
-
-def code_only(text: str) -> str:
-    """The source without comments, trailing spaces and blank lines: what the
-    compiler sees (a comment edit does not change the profiled kernels)."""
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", "", text)
-    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
-
-
-def kernel_source_hash(csrc: str = CSRC) -> str:
-    h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(csrc, name), encoding="utf-8") as f:
-                h.update(code_only(f.read()).encode())
-    return h.hexdigest()[:16]
 
 
 def per_kernel(db_path):
