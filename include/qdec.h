@@ -67,8 +67,9 @@
  *    p >> 5 (MSB first).
  *  - Step t (t = 0 .. 256/V - 1) covers weights tV .. tV+V-1.  Its state is
  *    the L-bit window starting at stream bit t*kV, read MSB first, wrapping
- *    around the end of the tile's stream (tail-biting): the last L-kV bits of
- *    a state are the first L-kV bits of the next ("Figure 2 (Q4)"), so every
+ *    around the end of the tile's stream (tail-biting): each state is the
+ *    previous one shifted left by kV bits with kV new bits appended, so two
+ *    neighbours share L-kV bits ("Figure 2 (Q4)"), so every
  *    bit string is a valid walk and storage is exactly k bits per weight.
  *  - Tiles are stored in panels of 8 tile-rows (128 output rows); inside a
  *    panel, column by column: storage index of tile (R, C) is

@@ -57,6 +57,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qdec_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# A sanitizer build of the same source (tests/test_sanitizers.py) is loaded
+# in place of the plain one when this names it.
+_SAN_LIB = os.environ.get("QDEC_ORACLE_SANITIZED_LIB")
 
 HYB, MAD1, INST3, NUQ, VQ, LUT = 1, 2, 3, 4, 5, 6
 CODE_NAMES = {HYB: "HYB", MAD1: "1MAD", INST3: "3INST", NUQ: "NUQ", VQ: "VQ", LUT: "LUT"}
@@ -79,10 +82,13 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or (
-                os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
-            build(force=True)
-        L = ctypes.CDLL(_LIB_PATH)
+        if _SAN_LIB:
+            L = ctypes.CDLL(_SAN_LIB)
+        else:
+            if not os.path.exists(_LIB_PATH) or (
+                    os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+                build(force=True)
+            L = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
         i64, i32 = ctypes.c_int64, ctypes.c_int
         L.orc_f16_from_double.restype = ctypes.c_uint16

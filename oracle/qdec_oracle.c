@@ -11,8 +11,9 @@
  * Sources (web pages; sections named as they appear there):
  *  - "QTIP: Quantization with Trellises and Incoherence Processing"
  *    (OpenReview discussion):
- *      "Figure 2 (Q4)"  -- the bitshift trellis: the last L-kV bits of a state
- *        are the first L-kV bits of the next, so only kV new bits are stored
+ *      "Figure 2 (Q4)"  -- the bitshift trellis: a state is its predecessor
+ *        shifted by kV bits with kV fresh bits at the low end (the two share
+ *        L-kV bits), so only kV new bits are stored
  *        per step; the worked example 0010110 -> 00,01,10,01,11,10.
  *      "Ablations and fast inference (W1 and W2)" -- L = kV makes the trellis
  *        plain k-bit V-dim VQ; the bitshift trellis needs no stored graph and
