@@ -326,15 +326,14 @@ int mma_krange(const int64_t* m, const int64_t* n, int count) {
 
 // LDS carve-up of one launch: the table (or, before it is built, the x
 // transform's fp32 scratch), x' of the widest row padded to whole ranges,
-// and the cross-wave sums (or the staged HYB LUT).  HYB takes 32 table copies
+// and the cross-wave sums.  HYB takes 32 table copies
 // where they fit, else fewer (at least 4).  false if nothing fits.
 bool mma_lds(int code, int kv, int Qmax, int64_t nmax, int KR, MmaArgs* a) {
   if (nmax > MMA_MAX_N) return false;
   const size_t xs = (size_t)((nmax + KR - 1) / KR) * KR * 2;
   if (xs > (size_t)MMA_MAX_N * 2) return false;
   const size_t scratch = ((size_t)padded_words((int)nmax) * 4 + 15) & ~(size_t)15;
-  const size_t red = code == HYB && (size_t)(4 << Qmax) > (size_t)MMA_RED_BYTES ? (size_t)(4 << Qmax)
-                                                                                : (size_t)MMA_RED_BYTES;
+  const size_t red = (size_t)MMA_RED_BYTES;
   // the transform's scratch gets an area of its own where it fits (the
   // table is then built while x is in flight), else it borrows the table's
   auto fits = [&](size_t table) -> bool {

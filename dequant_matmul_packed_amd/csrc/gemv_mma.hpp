@@ -152,14 +152,20 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
       sw[j] = buf_load_u32(srs, ok ? (uint32_t)((8 * c) >> 5) * 4u : BUF_OFF);
     }
   }
-  const int nlut = CODE == HYB ? (1 << Q) : 0;   // staged through LDS below
-  uint32_t lw[2];
+  // HYB: the LUT word of each 16-byte run of the table this thread writes
+  // (run w4 = tid + 1024 k holds 4 copies of signed entry (4 w4) / copies;
+  // at most 8 runs per thread: 128 KiB), requested with x
+  const int nlut = CODE == HYB ? (1 << Q) : 0;
+  const int lc = 31 - __builtin_clz((unsigned)a.copies);
+  const int W4 = CODE == HYB ? (a.copies << (Q + 1)) >> 2 : 0;
+  uint32_t lw[8];
   {
     const auto lrs = make_rsrc(lut, (uint32_t)nlut * 4u);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = tid + MMA_THREADS * i;
-      lw[i] = buf_load_u32(lrs, e < nlut ? (uint32_t)e * 4u : BUF_OFF);
+    for (int k = 0; k < 8; ++k) {
+      const int w4 = tid + MMA_THREADS * k;
+      const int e = (w4 << 2) >> lc;
+      lw[k] = buf_load_u32(lrs, w4 < W4 ? (uint32_t)(e & (nlut - 1)) * 4u : BUF_OFF);
     }
   }
   // codes of the whole part through one resource (format sizes below 4 GiB)
@@ -200,30 +206,16 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
   // ---- 1. the lookup table ---------------------------------------------------
   auto build_table = [&]() {
     if constexpr (CODE == HYB) {
-      // the LUT words are staged in the reduction area, then every thread
-      // writes 16-byte runs of consecutive copies (conflict-free writes),
-      // all its reads first (at most 8 runs per thread: 128 KiB)
-      uint32_t* stg = reinterpret_cast<uint32_t*>(lds + a.red_off);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int e = tid + MMA_THREADS * i;
-        if (e < nlut) stg[e] = lw[i];
-      }
-      __syncthreads();
-      const int lc = 31 - __builtin_clz((unsigned)a.copies);
-      const int W4 = (a.copies << (Q + 1)) >> 2;      // at most 8192
+      // every thread writes its 16-byte runs of consecutive copies
+      // (conflict-free writes) from the LUT words it loaded at the start;
+      // entries 2^Q and up are the sign-flipped ones
       uint4* tab4 = reinterpret_cast<uint4*>(lds);
-      uint32_t v[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int w4 = tid + MMA_THREADS * k;
         const int e = (w4 << 2) >> lc;
-        v[k] = w4 < W4 ? stg[e & (nlut - 1)] ^ (((e >> Q) & 1) ? 0x80008000u : 0u) : 0u;
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int w4 = tid + MMA_THREADS * k;
-        if (w4 < W4) tab4[w4] = make_uint4(v[k], v[k], v[k], v[k]);
+        const uint32_t v = lw[k] ^ (((e >> Q) & 1) ? 0x80008000u : 0u);
+        if (w4 < W4) tab4[w4] = make_uint4(v, v, v, v);
       }
     } else {
       constexpr int C = MmaTable<CODE>::COPIES;
@@ -307,6 +299,7 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
   const auto zrs = make_rsrc(zl, (uint32_t)(nr * sstride * 4));
   const int hbits = Bo >= 128 ? 7 : 31 - __builtin_clz((unsigned)Bo);
   float4v acc[2] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
+  half8v b0 = {}, b1 = {};   // the B operands (x'), set in lanes 0, 16, 32, 48 each step
   // the current step: unit ck (panel cp, range cr), step cs in it
   int ck = 0, cs = 0, cp = bl % npanels, cr = bl / npanels;
 
@@ -334,9 +327,14 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) out[i] = live ? out[i] : 0u;
     }
-    const _Float16* xb = xs + col + 16 * (lane >> 4);
-    const half8v b0 = *reinterpret_cast<const half8v*>(xb);
-    const half8v b1 = *reinterpret_cast<const half8v*>(xb + 8);
+    // only column 0 of the products is used: only lanes 0, 16, 32, 48 (the
+    // B operand's column 0) read x' -- a sixteenth of the LDS return traffic;
+    // the other lanes keep zeros
+    if ((lane & 15) == 0) {
+      const _Float16* xb = xs + col + 16 * (lane >> 4);
+      b0 = *reinterpret_cast<const half8v*>(xb);
+      b1 = *reinterpret_cast<const half8v*>(xb + 8);
+    }
 #pragma unroll
     for (int ra = 0; ra < 2; ++ra) {
       const half8v a0 = __builtin_bit_cast(half8v, make_uint4(out[8 * ra], out[8 * ra + 1], out[8 * ra + 2], out[8 * ra + 3]));

@@ -98,7 +98,7 @@ struct MmaArgs {
   int nl;
   int tab_bytes;           // LDS: table (and the x transform's scratch) [0, tab_bytes)
   int xs_off;              // x' fp16 [npad] from here
-  int red_off;             // the cross-wave sums (and the staged LUT) from here
+  int red_off;             // the cross-wave sums from here
   int scr_off;             // the x transform's fp32 scratch, or 0: it borrows the table's area
   int lds_bytes;           // the whole carve-up
   int cshift;              // HYB: log2(4 x table copies)
