@@ -325,14 +325,14 @@ int mma_krange(const int64_t* m, const int64_t* n, int count) {
 }
 
 // LDS carve-up of one launch: the table (or, before it is built, the x
-// transform's fp32 scratch), x' of the widest row padded to whole ranges,
-// and the cross-wave sums.  HYB takes 32 table copies
-// where they fit, else fewer (at least 4).  false if nothing fits.
-bool mma_lds(int code, int kv, int Qmax, int64_t nmax, int KR, MmaArgs* a) {
-  if (nmax > MMA_MAX_N) return false;
-  const size_t xs = (size_t)((nmax + KR - 1) / KR) * KR * 2;
-  if (xs > (size_t)MMA_MAX_N * 2) return false;
-  const size_t scratch = ((size_t)padded_words((int)nmax) * 4 + 15) & ~(size_t)15;
+// transform's fp32 scratch), x' (xs_elems fp16: the widest row padded to
+// whole ranges, or one range), and the cross-wave sums; the scratch holds
+// scr_elems fp32.  HYB takes 32 table copies where they fit, else fewer (at
+// least 4).  false if nothing fits.
+bool mma_lds(int code, int kv, int Qmax, int64_t xs_elems, int64_t scr_elems, MmaArgs* a) {
+  if (xs_elems > MMA_MAX_N || scr_elems > MMA_MAX_N) return false;
+  const size_t xs = (size_t)xs_elems * 2;
+  const size_t scratch = ((size_t)padded_words((int)scr_elems) * 4 + 15) & ~(size_t)15;
   const size_t red = (size_t)MMA_RED_BYTES;
   // the transform's scratch gets an area of its own where it fits (the
   // table is then built while x is in flight), else it borrows the table's
@@ -439,7 +439,7 @@ bool plan_mma(const LayerArgs* L, const LayerParts* P, int count, const uint16_t
       MmaArgs& a = c->launch[c->nlaunch];
       a.nl = 0;
       int Qmax = 0;
-      int64_t nmax = 0;
+      int64_t xs_elems = 0, scr_elems = 0;
       for (int l = l0; l < count; ++l)
         for (int p = 0; p < P[l].count; ++p) {
           if (used[l][p] || P[l].part[p].code != code || P[l].part[p].kv != kv || a.nl == GEMV_GROUP_MAX)
@@ -454,12 +454,18 @@ bool plan_mma(const LayerArgs* L, const LayerParts* P, int count, const uint16_t
           ml.nr = (int)((ml.L.n + KR - 1) / KR);
           ml.KR = KR;
           ml.units = (int)(ml.L.m / 128) * ml.nr;
+          // x' of one range per workgroup where the range is whole
+          // Hadamard blocks: each workgroup transforms KR values, not n
+          ml.xmode = ml.nr > 1 && KR % ml.L.had_in == 0 ? 1 : 0;
+          const int64_t xe = ml.xmode ? KR : (int64_t)ml.nr * KR, se = ml.xmode ? KR : ml.L.n;
           if (ml.L.Q > Qmax) Qmax = ml.L.Q;
-          if (ml.L.n > nmax) nmax = ml.L.n;
+          if (xe > xs_elems) xs_elems = xe;
+          if (se > scr_elems) scr_elems = se;
         }
-      if (!mma_lds(code, kv, Qmax, nmax, KR, &a)) return false;
+      if (!mma_lds(code, kv, Qmax, xs_elems, scr_elems, &a)) return false;
       // workgroups: one per unit when they fit one round, else shared out
-      // in proportion to the units (at least one per part)
+      // in proportion to the units (at least one per part; a multiple of
+      // the ranges where each workgroup keeps one range)
       int64_t U = 0;
       for (int i = 0; i < a.nl; ++i) U += a.lay[i].units;
       int wg = 0;
@@ -472,8 +478,10 @@ bool plan_mma(const LayerArgs* L, const LayerParts* P, int count, const uint16_t
       } else {
         int nw[GEMV_GROUP_MAX], tot = 0;
         for (int i = 0; i < a.nl; ++i) {
+          const int g = a.lay[i].xmode ? a.lay[i].nr : 1;
           nw[i] = (int)((int64_t)MMA_CUS * a.lay[i].units / U);
-          if (nw[i] < 1) nw[i] = 1;
+          nw[i] -= nw[i] % g;
+          if (nw[i] < g) nw[i] = g;
           if (nw[i] > a.lay[i].units) nw[i] = a.lay[i].units;
           tot += nw[i];
         }
@@ -481,12 +489,14 @@ bool plan_mma(const LayerArgs* L, const LayerParts* P, int count, const uint16_t
           int bi = -1;
           int64_t br = 0;
           for (int i = 0; i < a.nl; ++i) {
+            const int g = a.lay[i].xmode ? a.lay[i].nr : 1;
             const int64_t r = (a.lay[i].units + nw[i] - 1) / nw[i];
-            if (nw[i] < a.lay[i].units && r > br) { br = r; bi = i; }
+            if (nw[i] + g <= a.lay[i].units && tot + g <= MMA_CUS && r > br) { br = r; bi = i; }
           }
           if (bi < 0) break;
-          ++nw[bi];
-          ++tot;
+          const int g = a.lay[bi].xmode ? a.lay[bi].nr : 1;
+          nw[bi] += g;
+          tot += g;
         }
         for (int i = 0; i < a.nl; ++i) {
           a.lay[i].wg0 = wg;

@@ -15,8 +15,9 @@
 //    directly the A operands of v_mfma_f32_16x16x32_f16 (the layout of the
 //    batched kernel), and x' is the B operand; only column 0 of each 16x16
 //    product is used, which costs matrix-core time the VALU does not pay;
-//  - runs one 16-wave workgroup per CU that computes x' = RHT_in(x) for the
-//    whole row once and builds the table once, then walks its units of work,
+//  - runs one 16-wave workgroup per CU that computes x' = RHT_in(x) once
+//    (of the whole row, or, where all its units share one K range, of that
+//    range only) and builds the table once, then walks its units of work,
 //    so that those fixed costs are paid once per CU and layer instead of once
 //    per (panel, chunk) as in the dot-product kernel.
 //
@@ -130,15 +131,37 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
   const int nr = a.lay[li].nr, KR = a.lay[li].KR;
   const int bl = (int)blockIdx.x - a.lay[li].wg0, nwg = a.lay[li].nwg, units = a.lay[li].units;
 
+  const int xmode = a.lay[li].xmode;
   const int ntc = n >> 4;                 // tile columns
   const int npanels = (int)(mpart >> 7);
   const int Kw = KR >> 2, S = Kw >> 6;    // columns and steps of a quarter
-  const int my_units = bl < units ? (units - bl + nwg - 1) / nwg : 0;
+  // the units: with the whole row in LDS, unit u = bl + i nwg (panel u %
+  // npanels, range u / npanels); with one range per workgroup (xmode 1; nwg
+  // a multiple of nr), range bl % nr and panels bl / nr + i (nwg / nr)
+  int my_units, dp, dr, cp0, cr0;
+  if (xmode == 0) {
+    my_units = bl < units ? (units - bl + nwg - 1) / nwg : 0;
+    dp = nwg % npanels;
+    dr = nwg / npanels;
+    cp0 = bl % npanels;
+    cr0 = bl / npanels;
+  } else {
+    dp = nwg / nr;
+    dr = 0;
+    cp0 = bl / nr;
+    cr0 = bl % nr;
+    my_units = cp0 < npanels ? (npanels - cp0 + dp - 1) / dp : 0;
+  }
   const int T = my_units * S;             // steps of every wave (a multiple of PF)
-  const int dp = nwg % npanels, dr = nwg / npanels;   // unit stride in (panel, range)
+  // x' in LDS: the whole row (xmode 0) or the workgroup's range only, local
+  // column 0 being column xbase of the row
+  const int xbase = xmode == 0 ? 0 : cr0 * KR;
+  const int NL = xmode == 0 ? n : KR;     // x' values kept (zero past n)
 
   // ---- 0. every global load the set-up needs, and the first PF code steps ----
-  const int nch8 = n >> 3;                // 8-value chunks of x (n <= 16384: 2 per thread)
+  // x in 8-value chunks: local chunk c = tid + 1024 j of the row or the
+  // range (at most 16384 values: 2 per thread)
+  const int nch8 = n >> 3;
   uint4 xv[2];
   uint32_t sw[2];
   {
@@ -147,9 +170,10 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int c = tid + MMA_THREADS * j;
-      const bool ok = c < nch8;
-      xv[j] = buf_load_u4(xrs, ok ? (uint32_t)c * 16u : BUF_OFF);
-      sw[j] = buf_load_u32(srs, ok ? (uint32_t)((8 * c) >> 5) * 4u : BUF_OFF);
+      const int gc = (xbase >> 3) + c;
+      const bool ok = c < (NL >> 3) && gc < nch8;
+      xv[j] = buf_load_u4(xrs, ok ? (uint32_t)gc * 16u : BUF_OFF);
+      sw[j] = buf_load_u32(srs, ok ? (uint32_t)((8 * gc) >> 5) * 4u : BUF_OFF);
     }
   }
   // HYB: the LUT word of each 16-byte run of the table this thread writes
@@ -178,7 +202,7 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
 
   // the prefetch pointer: unit k of this workgroup, step s in it, its panel
   // and range (scalar, advanced one step at a time)
-  int pk = 0, ps = 0, pp = bl % npanels, pr = bl / npanels;
+  int pk = 0, ps = 0, pp = cp0, pr = cr0;
   auto load_step = [&](uint32_t* slot) {
     const int cbase = ((pr * KR + ks * Kw) >> 4) + 4 * ps;   // tile column of tc = 0
     const bool ok = pk < my_units && cbase + tc < ntc;
@@ -227,7 +251,7 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
     }
   };
 
-  // ---- 2. x' = RHT_in(x) of the whole row, fp16 in LDS ----------------------
+  // ---- 2. x' = RHT_in(x) of the row or of the range, fp16 in LDS -----------
   // Chunks of 8 consecutive values: the butterfly stages inside a chunk in
   // registers, the rest in padded LDS in passes of 3 index bits (512 groups of
   // 8 values on a 4096-value row: every thread busy).
@@ -236,10 +260,11 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
     const int hb_in = 31 - __builtin_clz((unsigned)Bi);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int c = tid + MMA_THREADS * j;
-      if (c < nch8) {
+      const int c = tid + MMA_THREADS * j;          // local chunk
+      const int gc = (xbase >> 3) + c;
+      if (c < (NL >> 3) && gc < nch8) {
         const uint32_t r[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
-        const uint32_t sg = sw[j] >> ((8 * c) & 31);
+        const uint32_t sg = sw[j] >> ((8 * gc) & 31);
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -264,12 +289,14 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
       }
     }
     __syncthreads();
-    if (hb_in > 3) fwht_bits<3>(scr, n, 3, hb_in, tid, MMA_THREADS);   // ends with a barrier
+    if (hb_in > 3) fwht_bits<3>(scr, NL, 3, hb_in, tid, MMA_THREADS);   // ends with a barrier
     const float rs = 1.0f / sqrtf((float)Bi);
-    const int npad8 = (nr * KR) >> 3;     // x' is zero past n, to the end of the last range
+    // x' is zero past n, to the end of the last range
+    const int npad8 = (xmode == 0 ? nr * KR : KR) >> 3;
+    const int nval8 = (n - xbase < NL ? n - xbase : NL) >> 3;
     for (int c = tid; c < npad8; c += MMA_THREADS) {
       uint32_t p[4] = {0u, 0u, 0u, 0u};
-      if (c < nch8) {
+      if (c < nval8) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           p[e] = f2h_bits(scr[pad_index(8 * c + 2 * e)] * rs) |
@@ -301,7 +328,7 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
   float4v acc[2] = {float4v{0.f, 0.f, 0.f, 0.f}, float4v{0.f, 0.f, 0.f, 0.f}};
   half8v b0 = {}, b1 = {};   // the B operands (x'), set in lanes 0, 16, 32, 48 each step
   // the current step: unit ck (panel cp, range cr), step cs in it
-  int ck = 0, cs = 0, cp = bl % npanels, cr = bl / npanels;
+  int ck = 0, cs = 0, cp = cp0, cr = cr0;
 
   auto compute = [&](const uint32_t* wc) {
     uint32_t w[NW + 1];
@@ -331,7 +358,7 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
     // B operand's column 0) read x' -- a sixteenth of the LDS return traffic;
     // the other lanes keep zeros
     if ((lane & 15) == 0) {
-      const _Float16* xb = xs + col + 16 * (lane >> 4);
+      const _Float16* xb = xs + (col - xbase) + 16 * (lane >> 4);
       b0 = *reinterpret_cast<const half8v*>(xb);
       b1 = *reinterpret_cast<const half8v*>(xb + 8);
     }

@@ -533,7 +533,81 @@ static hipError_t launch_finish_j(const FinishArgs& a, unsigned grid, size_t lds
   return hipGetLastError();
 }
 
+// The same finish with the cross-panel stages between lanes, for blocks of
+// P <= 32 panels (P = Bo / 128, 1 below): thread t of a (layer, column)
+// takes row blk Rb + p 128 + i of block blk (Rb = 128 P rows) with
+// p = t mod P, i = (t mod Rb) / P, so the P rows at one in-panel index sit
+// in P neighbouring lanes and stage h of H_P pairs lanes t and t ^ h (one
+// ds_swizzle each: no LDS buffer, no barrier).  256 threads per workgroup,
+// rows past m idle; each layer's workgroups are ceil(m / 256) per column,
+// column major.  Slices are added in slice order, as above.
+// One butterfly stage between lanes t and t ^ H (H < 32): ds_swizzle in
+// bit-mask mode (offset bit 15 clear: within each 32 lanes, lane j reads
+// lane ((j & 31) | 0) ^ H).  The lower lane keeps the sum, the upper one the
+// difference.
+template <int H>
+__device__ __forceinline__ void lane_butterfly(float& v, int lane) {
+  const float o = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x1F | (H << 10)));
+  v = (lane & H) ? o - v : v + o;
+}
+
+__global__ __launch_bounds__(256) void gemv_finish_lanes_kernel(FinishArgs a) {
+  int li = 0;
+#pragma unroll
+  for (int i = 1; i < GEMV_GROUP_MAX; ++i)
+    if (i < a.nl && (int)blockIdx.x >= a.lay[i].wg0) li = i;
+  const int64_t m = a.lay[li].m;
+  const int P = a.lay[li].Bo >= 128 ? a.lay[li].Bo >> 7 : 1;   // workgroup-uniform
+  const int wpc = (int)((m + 255) >> 8);            // workgroups per column
+  const int lw = (int)blockIdx.x - a.lay[li].wg0;
+  const int c = lw / wpc;
+  const int64_t g = (int64_t)(lw % wpc) * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int Rb = 128 * P;
+  const int t = (int)(g % Rb);
+  const int64_t row = (g / Rb) * Rb + (int64_t)(t % P) * 128 + t / P;
+  const bool live = g < m;
+  const int nsl = a.lay[li].nslices;
+  const int64_t sstride = a.lay[li].slice_stride;
+  const float* zc = a.lay[li].z + (int64_t)c * m + row;
+  float acc = 0.f;
+  for (int s0 = 0; s0 < nsl; s0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int su = 0; su < 16; ++su) v[su] = live && s0 + su < nsl ? zc[(int64_t)(s0 + su) * sstride] : 0.f;
+#pragma unroll
+    for (int su = 0; su < 16; ++su)
+      if (s0 + su < nsl) acc += v[su];
+  }
+  if (P > 1) lane_butterfly<1>(acc, lane);
+  if (P > 2) lane_butterfly<2>(acc, lane);
+  if (P > 4) lane_butterfly<4>(acc, lane);
+  if (P > 8) lane_butterfly<8>(acc, lane);
+  if (P > 16) lane_butterfly<16>(acc, lane);
+  if (live) {
+    const uint32_t* sg = a.lay[li].sign_out;
+    const bool neg = sg && ((sg[row >> 5] >> (row & 31)) & 1u);
+    const float v = acc * a.lay[li].mult;
+    a.lay[li].y[(int64_t)c * m + row] = f2h_bits(neg ? -v : v);
+  }
+}
+
 hipError_t launch_gemv_finish(const FinishArgs& a, hipStream_t stream) {
+  // the lane finisher where every block is at most 32 panels
+  bool lanes = a.nl > 0;
+  for (int l = 0; l < a.nl; ++l)
+    if (a.lay[l].Bo > 32 * 128) lanes = false;
+  if (lanes) {
+    FinishArgs b = a;
+    unsigned grid = 0;
+    for (int l = 0; l < b.nl; ++l) {
+      b.lay[l].wg0 = (int)grid;
+      grid += (unsigned)(((b.lay[l].m + 255) >> 8) * b.lay[l].b);
+    }
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(gemv_finish_lanes_kernel, dim3(grid), dim3(256), 0, stream, b);
+    return hipGetLastError();
+  }
   unsigned grid = 0;
   size_t lds = 0;
   int rmax = 0;

@@ -80,8 +80,9 @@ struct FinishArgs {
 // The MFMA GEMV of one batch column (gemv_mma_kernel): one 16-wave
 // workgroup per CU.  A unit of work is one 128-row panel x one range of KR
 // input columns; the 16 waves are 4 row groups (32 rows) x 4 quarters of
-// the range.  Each workgroup works on one layer of the launch: x' of the
-// whole row and the layer's table stay in LDS while it walks its units.
+// the range.  Each workgroup works on one layer of the launch: x' (of the
+// whole row, or of the one range all its units share) and the layer's
+// table stay in LDS while it walks its units.
 struct MmaLayer {
   LayerArgs L;             // one row part of a layer
   const uint16_t* x;       // [n] fp16
@@ -91,6 +92,8 @@ struct MmaLayer {
   int nr, KR;              // K ranges of KR columns (the last may be ragged)
   int wg0, nwg;            // workgroups [wg0, wg0 + nwg) of the launch work on this layer
   int units;               // (m / 128) x nr
+  int xmode;               // x' in LDS: 0 the whole row; 1 one range per workgroup
+                           // (nwg a multiple of nr; the range is whole Hadamard blocks)
 };
 constexpr int MMA_RED_BYTES = 2 * 4 * 128 * 4;   // two buffers: 4 quarters x 128 rows fp32
 constexpr int MMA_MAX_N = 16384;                  // x' of a whole row in LDS (fp16)

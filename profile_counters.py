@@ -14,9 +14,9 @@ ARGS is the bench's argument string (it goes into the summary's command
 line): `--steps 20 --warmup 5 --no-cpu-baseline` for the bench, or
 `--layer CODE:M:N:K:B` for one layer.  With WEIGHTS (the layer's m x n) the
 table gives VALU and LDS lane-instructions per weight for the layer's
-decode kernel (the gemv_kernel or gemm_kernel dispatches).  Without it, the
-bench's two known shapes are recognised by their grids (the 4096x4096 b=1
-GEMV and the 28672x8192 b=64 GEMM).
+decode kernel (the gemv_kernel, gemv_mma_kernel or gemm_kernel dispatches).
+Rows are kept apart by kernel, grid and LDS size; every qdec kernel gets a
+row.
 
 Counters are per dispatch, summed over the chip; instruction counts are per
 wave (64 lanes).  With the third pass the table adds MfmaUtil, rocprofv3's
@@ -28,18 +28,17 @@ import sqlite3
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-# (kernel name prefix, grid size in threads) -> weights per dispatch
-KNOWN = {("qdec::gemv_kernel<", 131072): 4096 * 4096,     # 4096x4096, b=1: 32 panels x 16 chunks
-         ("qdec::gemm_kernel<", 172032): 28672 * 8192}     # 28672x8192, b=64: 224 panels x 3 K splits
+DECODE = ("qdec::gemv_kernel<", "qdec::gemv_mma_kernel<", "qdec::gemm_kernel<")
 
 
 def load(db):
     c = sqlite3.connect(db)
-    rows = c.execute("select kernel_name, grid_size, counter_name, avg(value), count(*) "
-                     "from counters_collection group by kernel_name, grid_size, counter_name").fetchall()
+    rows = c.execute("select kernel_name, grid_size, lds_block_size, counter_name, avg(value), count(*) "
+                     "from counters_collection group by kernel_name, grid_size, lds_block_size, "
+                     "counter_name").fetchall()
     out = {}
-    for kn, gs, cn, v, n in rows:
-        k = (kn.split("(")[0].replace("void ", ""), gs)
+    for kn, gs, lds, cn, v, n in rows:
+        k = (kn.split("(")[0].replace("void ", ""), gs, lds)
         out.setdefault(k, {})[cn] = (v, n)
     return out
 
@@ -63,34 +62,29 @@ def main():
              "Per dispatch, averaged over dispatches.  wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave time "
              "waiting on a dependency); LDS wait = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES; bank = "
              "SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS (conflict cycles per LDS issue cycle).", "",
-             "| kernel | grid | dispatches | VALU inst | LDS inst | MFMA inst | wait | LDS wait | bank | VALU/weight | "
-             "LDS/weight |%s" % (" MfmaUtil % |" if c else ""),
-             "|---|---|---|---|---|---|---|---|---|---|---|%s" % ("---|" if c else "")]
-    for k in keys[:14]:
+             "| kernel | grid | LDS bytes | dispatches | VALU inst | LDS inst | MFMA inst | wait | LDS wait | bank | "
+             "VALU/weight | LDS/weight |%s" % (" MfmaUtil % |" if c else ""),
+             "|---|---|---|---|---|---|---|---|---|---|---|---|%s" % ("---|" if c else "")]
+    for k in keys:
         d = dict(a[k])
         d.update(b[k])
         g = lambda c: d.get(c, (0.0, 0))[0]
         wc = g("SQ_WAVE_CYCLES") or 1.0
-        wts = None
-        if weights:
-            if k[0].startswith(("qdec::gemv_kernel<", "qdec::gemm_kernel<")):
-                wts = weights
-        else:
-            for (pre, grid), w in KNOWN.items():
-                if k[0].startswith(pre) and k[1] == grid:
-                    wts = w
+        wts = weights if weights and k[0].startswith(DECODE) else None
         vpw = "%.3f" % (g("SQ_INSTS_VALU") * 64 / wts) if wts else ""
         lpw = "%.3f" % (g("SQ_INSTS_LDS") * 64 / wts) if wts else ""
         util = ""
         if c:
             util = " %.1f |" % c[k]["MfmaUtil"][0] if k in c and "MfmaUtil" in c[k] else " |"
-        lines.append("| `%s` | %d | %d | %.0f | %.0f | %.0f | %.2f | %.2f | %.2f | %s | %s |%s" % (
-            k[0], k[1], d.get("SQ_INSTS_VALU", (0, 0))[1], g("SQ_INSTS_VALU"), g("SQ_INSTS_LDS"),
+        lines.append("| `%s` | %d | %d | %d | %.0f | %.0f | %.0f | %.2f | %.2f | %.2f | %s | %s |%s" % (
+            k[0], k[1], k[2], d.get("SQ_INSTS_VALU", (0, 0))[1], g("SQ_INSTS_VALU"), g("SQ_INSTS_LDS"),
             g("SQ_INSTS_MFMA"), g("SQ_WAIT_INST_ANY") / wc, g("SQ_WAIT_INST_LDS") / wc,
             g("SQ_LDS_BANK_CONFLICT") / (g("SQ_ACTIVE_INST_LDS") or 1.0), vpw, lpw, util))
     lines += ["", "VALU/weight and LDS/weight are lane-instructions per weight (wave instructions x 64 / "
-              "weights) of the decode kernels: a GEMV counts the decode and the dot products (v_dot2, one "
-              "per two weights); a GEMM counts the decode only (the products are MFMA instructions)."]
+              "weights) of the decode kernels: gemv_kernel counts the decode and the dot products (v_dot2, "
+              "one per two weights); gemv_mma_kernel and gemm_kernel count the decode only (the products "
+              "are MFMA instructions).  The decode kernels also carry their start-up work (the input "
+              "Hadamard transform and the table fill)."]
     if c:
         lines += ["", "MfmaUtil is rocprofv3's derived counter: the MFMA-busy cycles of all SIMDs over the "
                   "GPU-active cycles of the dispatch times the SIMD count (1024), in percent."]
