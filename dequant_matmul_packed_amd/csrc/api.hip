@@ -512,12 +512,12 @@ bool plan_mma(const LayerArgs* L, const LayerParts* P, int count, const uint16_t
 }
 
 // Whether a one-column qdec_gemv takes the MFMA GEMV.  Its workgroups pay a
-// fixed start (the x transform of the whole row, a 128 KiB table) that the
-// dot-product kernel's smaller workgroups do not, and win it back on large
-// layers: measured at 2 bits per weight (us per call, MFMA / dot product)
-// 4096x4096 13.9 / 13.5, 4096x14336 20.6 / 20.4, 14336x4096 17.6 / 19.1,
-// 28672x4096 22.4 / 26.2, 28672x8192 33.6 / 40.1.  Tuning override
-// QDEC_GEMV_MMA = 0 / 1.
+// fixed start (the x transform, a 128 KiB table) that the dot-product
+// kernel's smaller workgroups do not, and win it back on layers from about
+// 4096x4096 up: measured at 2 bits per weight (us per call, MFMA / dot
+// product) 4096x4096 12.1 / 12.3, 4096x14336 15.9 / 20.4, 14336x4096
+// 17.6 / 19.1, 28672x4096 22.4 / 26.2, 28672x8192 33.6 / 40.1.  Tuning
+// override QDEC_GEMV_MMA = 0 / 1.
 // The other codes stay on the dot-product kernel, whose decoders are cheaper
 // there (NUQ and VQ look up a weight pair in one read of a small table; the
 // MFMA operands need each weight as an exact fp16 value): 4096x14336 NUQ
@@ -525,7 +525,7 @@ bool plan_mma(const LayerArgs* L, const LayerParts* P, int count, const uint16_t
 bool gemv_use_mma(int code, int64_t m, int64_t n) {
   const int forced = tuning("QDEC_GEMV_MMA");
   if (forced >= 0) return forced != 0;
-  return code == HYB && (double)m * (double)n >= 5e7;
+  return code == HYB && (double)m * (double)n >= 1.6e7;
 }
 
 // Bytes of slices any call of up to b columns on an m x n layer writes: the

@@ -195,9 +195,9 @@ int qdec_rht(const void *in, int32_t in_dtype, void *out, int32_t out_dtype,
  * in/out, fp32 accumulation.  Two launches: one kernel decodes and
  * multiplies, the finisher adds its K slices and applies the output
  * transform.  At one batch column the decode kernel also applies the input
- * transform: on layers of at least 5e7 weights it is the MFMA kernel (one
- * workgroup per CU; the decoded weights are MFMA operands), on smaller ones
- * the dot-product kernel.  With more batch columns the input transform runs
+ * transform: for HYB codes (V = 2) on layers of at least 1.6e7 weights
+ * (4096 x 4096 and up) it is the MFMA kernel (one workgroup per CU; the
+ * decoded weights are MFMA operands), otherwise the dot-product kernel.  With more batch columns the input transform runs
  * first in a kernel of its own, and on large layers (NB * m * n >= 4e8,
  * NB = batch rounded up to 2, 4 or 8) the call runs the batched path of
  * qdec_gemm instead.  x 16-byte and y 8-byte aligned.
