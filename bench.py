@@ -43,6 +43,7 @@ MFMA_F16_PEAK_TFLOPS = 2516.6          # 256 CUs x 2.4 GHz x 4096 fp16 flop per 
 POOL_BYTES = 1 << 30
 STACK_LAYERS = 64
 METRIC = "fused dequant-GEMV HBM GB/s + µs/layer (b=1); GEMM TFLOP/s (b=64)"
+GEMM_LAYER = "HYB:28672:8192:3:64"     # the b=64 GEMM of the headline, as a --layer spec
 CSRC = os.path.join(ROOT, "dequant_matmul_packed_amd", "csrc")
 
 
@@ -63,6 +64,10 @@ def parse():
     ap.add_argument("--layer", default="",
                     help="only run 8 direct calls of one layer, CODE:M:N:K:B (e.g. HYB:28672:8192:2:1; "
                          "B > 8 takes qdec_gemm), for counter collection; prints no JSON line")
+    ap.add_argument("--call", default="", choices=("", "qkv", "o", "gate_up", "down", "gemm"),
+                    help="only run 8 direct calls of one call of the headline (a call of the Llama layer "
+                         "stack, or the b=64 GEMM), then the copy calibration if asked, for counter "
+                         "collection; prints no JSON line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, copy this many MiB device-to-device 5 times "
                          "(a plain copy of known size to scale HBM counters by)")
@@ -234,6 +239,19 @@ def time_calls(torch, calls, reps=5, ncalls=200):
     return float(np.median(out))
 
 
+def copy_calibration(torch, dev, mib):
+    """5 device-to-device copies of mib MiB: a plain copy of known size that
+    HBM counters (FETCH_SIZE, WRITE_SIZE) are scaled by."""
+    if mib <= 0:
+        return
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for r in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: 5 device-to-device copies of %d MiB" % mib)
+
+
 def llama_stack(q, torch, dev, args):
     """The headline: a stack of Llama-3-8B-shaped layers at batch 1, each layer
     with codes of its own.  Returns the JSON fields."""
@@ -274,6 +292,14 @@ def llama_stack(q, torch, dev, args):
             calls["o"][l]()
             calls["gate_up"][l]()
             calls["down"][l]()
+
+    if args.call:                            # counter collection: one call only
+        for i in range(8):
+            calls[args.call][i % L]()
+        torch.cuda.synchronize()
+        log("call %s: 8 calls done" % args.call)
+        copy_calibration(torch, dev, args.copy_calibration_mib)
+        return None
 
     step()                                   # eager first (sets kernel attributes)
     torch.cuda.synchronize()
@@ -320,15 +346,7 @@ def llama_stack(q, torch, dev, args):
     us_layer = elapsed / (args.steps * L) * 1e6
     log("stack of %d layers: %d steps in %.4f s (%s): %.1f GB/s packed, %.2f us/layer"
         % (L, args.steps, elapsed, mode, gbs, us_layer))
-    if args.copy_calibration_mib > 0:
-        nb = args.copy_calibration_mib << 20
-        src = torch.empty(nb, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for r in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("copy calibration: 5 device-to-device copies of %d MiB" % args.copy_calibration_mib)
-        del src, dst
+    copy_calibration(torch, dev, args.copy_calibration_mib)
     del graph
     # ---- the calls of a layer, each alone: event-timed, rotating layers ----
     per_call = {}
@@ -359,6 +377,14 @@ def main():
     if args.layer:
         run_one_layer(q, torch, dev, stream, args.layer)
         return
+    if args.call == "gemm":
+        run_one_layer(q, torch, dev, stream, GEMM_LAYER)
+        copy_calibration(torch, dev, args.copy_calibration_mib)
+        return
+    if args.call:
+        args.layers = min(args.layers, 8)
+        llama_stack(q, torch, dev, args)
+        return
     H = llama_stack(q, torch, dev, args)
     torch.cuda.empty_cache()
     G = bench_gemm(q, torch, dev, stream)
@@ -367,7 +393,8 @@ def main():
                "qkv": "qdec_gemv_group over q, k, v (gemv_mma_kernel + gemv_finish_kernel)",
                "down": "qdec_gemv 4096x14336 (gemv_mma_kernel + gemv_finish_kernel)",
                "o": "qdec_gemv 4096x4096 (gemv_kernel + gemv_finish_kernel)"}
-    traffic = measured_traffic(H["dominant"])
+    traffic = measured_traffic(H["dominant"], dom["algorithmic_bytes"])
+    traffic_b64 = measured_traffic("gemm", G["algorithmic_bytes"])
     detail = {"per_call_of_a_layer": H["per_call"], "launch_probe": H["probe"],
               "gemm_b64_up70b": G}
     if not args.no_detail:
@@ -424,7 +451,9 @@ def main():
         "roofline_b64": {"bound": "mfma", "kernel": "qdec_gemm 28672x8192 HYB k=3, X 64x8192 "
                                                     "(rht_split_kernel + gemm_kernel + rht_kernel)",
                          "achieved": G["TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(G["TFLOPs"] / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                         "frac": round(G["TFLOPs"] / MFMA_F16_PEAK_TFLOPS, 4),
+                         "traffic": traffic_b64["bytes_per_call"] if traffic_b64 else None,
+                         "traffic_detail": traffic_b64, "algorithmic_bytes": G["algorithmic_bytes"],
                          "flops_per_launch": G["flops"], "avg_launch_us": G["us_per_call"],
                          "timing": G["protocol"]},
         "cpu_baseline": cpu,
@@ -433,10 +462,10 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def measured_traffic(call):
-    """HBM bytes per call of the dominant call from the committed counter
-    summary (profiles/traffic.json), or None when there is none for it or the
-    kernel sources differ from the profiled ones."""
+def measured_traffic(call, algorithmic):
+    """HBM bytes per call of `call` from the committed counter summary
+    (profiles/traffic.json), or None when there is none for it or the kernel
+    sources differ from the profiled ones."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -447,7 +476,9 @@ def measured_traffic(call):
     v = rec.get("calls", {}).get(call)
     if v is None:
         return None
-    return {"bytes_per_call": int(v["bytes_per_call"]), "over_algorithmic": round(v["over_algorithmic"], 3),
+    return {"bytes_per_call": int(v["bytes_per_call"]), "read_bytes": int(v["read_bytes"]),
+            "write_bytes": int(v["write_bytes"]),
+            "over_algorithmic": round(v["bytes_per_call"] / algorithmic, 3),
             "source": "profiles/traffic.md (FETCH_SIZE, WRITE_SIZE scaled by a 256 MiB copy)"}
 
 
@@ -711,7 +742,10 @@ def bench_gemm(q, torch, dev, stream):
     flops = 2.0 * s.m * s.n * b
     tf = flops / (us * 1e-6) / 1e12
     log("gemm b=64: %.1f us, %.1f TFLOP/s" % (us, tf))
+    # codes, X and Y in fp16, both sign vectors, the 2^Q-entry table
+    nbytes = s.m * s.n * s.k // 8 + 2 * b * (s.n + s.m) + (s.m + s.n) // 8 + 4 * 512
     return {"us_per_call": round(us, 2), "TFLOPs": round(tf, 1), "flops": int(flops),
+            "algorithmic_bytes": int(nbytes),
             "frac_of_fp16_mfma_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
             "launches": "rht_in + gemm + rht_out",
             "protocol": "HIP events around 200 back-to-back calls on the launch stream (codes rotating "
