@@ -570,6 +570,9 @@ __global__ __launch_bounds__(256) void gemv_finish_lanes_kernel(FinishArgs a) {
   const int nsl = a.lay[li].nslices;
   const int64_t sstride = a.lay[li].slice_stride;
   const float* zc = a.lay[li].z + (int64_t)c * m + row;
+  // the sign word first: issued with the slices, not after the butterflies
+  const uint32_t* sg = a.lay[li].sign_out;
+  const uint32_t sgw = live && sg ? sg[row >> 5] : 0u;
   float acc = 0.f;
   for (int s0 = 0; s0 < nsl; s0 += 16) {
     float v[16];
@@ -585,8 +588,7 @@ __global__ __launch_bounds__(256) void gemv_finish_lanes_kernel(FinishArgs a) {
   if (P > 8) lane_butterfly<8>(acc, lane);
   if (P > 16) lane_butterfly<16>(acc, lane);
   if (live) {
-    const uint32_t* sg = a.lay[li].sign_out;
-    const bool neg = sg && ((sg[row >> 5] >> (row & 31)) & 1u);
+    const bool neg = (sgw >> (row & 31)) & 1u;
     const float v = acc * a.lay[li].mult;
     a.lay[li].y[(int64_t)c * m + row] = f2h_bits(neg ? -v : v);
   }
