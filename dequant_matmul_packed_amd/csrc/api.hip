@@ -327,9 +327,10 @@ int mma_krange(const int64_t* m, const int64_t* n, int count) {
 // LDS carve-up of one launch: the table (or, before it is built, the x
 // transform's fp32 scratch), x' (xs_elems fp16: the widest row padded to
 // whole ranges, or one range), and the cross-wave sums; the scratch holds
-// scr_elems fp32.  HYB takes 32 table copies where they fit, else fewer (at
-// least 4).  false if nothing fits.
-bool mma_lds(int code, int kv, int Qmax, int64_t xs_elems, int64_t scr_elems, MmaArgs* a) {
+// scr_elems fp32.  HYB takes 32 table copies where they fit, else fewer, but
+// at least 2^(13 - Q) (and 4) for the decode's table addresses (more than
+// 32 below Q = 8: a 64 KiB table).  false if nothing fits.
+bool mma_lds(int code, int kv, int Qmin, int Qmax, int64_t xs_elems, int64_t scr_elems, MmaArgs* a) {
   if (xs_elems > MMA_MAX_N || scr_elems > MMA_MAX_N) return false;
   const size_t xs = (size_t)xs_elems * 2;
   const size_t scratch = ((size_t)padded_words((int)scr_elems) * 4 + 15) & ~(size_t)15;
@@ -356,7 +357,10 @@ bool mma_lds(int code, int kv, int Qmax, int64_t xs_elems, int64_t scr_elems, Mm
     return true;
   };
   if (code == HYB) {
-    for (int c = 32; c >= 4; c /= 2) {
+    // at least 2^(13 - Q) copies for every layer: entry stride 4 c >= 2^(15 - Q),
+    // the decode's table address being the masked hash times 4 c / 2^(15 - Q)
+    const int cmin = Qmin >= 11 ? 4 : 1 << (13 - Qmin);
+    for (int c = cmin > 32 ? cmin : 32; c >= 4 && c >= cmin; c /= 2) {
       if (fits((size_t)c * (2u << Qmax) * 4)) {
         a->copies = c;
         a->cshift = 31 - __builtin_clz((unsigned)(4 * c));
@@ -438,7 +442,7 @@ bool plan_mma(const LayerArgs* L, const LayerParts* P, int count, const uint16_t
       const int code = P[l0].part[p0].code, kv = P[l0].part[p0].kv;
       MmaArgs& a = c->launch[c->nlaunch];
       a.nl = 0;
-      int Qmax = 0;
+      int Qmax = 0, Qmin = 16;
       int64_t xs_elems = 0, scr_elems = 0;
       for (int l = l0; l < count; ++l)
         for (int p = 0; p < P[l].count; ++p) {
@@ -459,10 +463,11 @@ bool plan_mma(const LayerArgs* L, const LayerParts* P, int count, const uint16_t
           ml.xmode = ml.nr > 1 && KR % ml.L.had_in == 0 ? 1 : 0;
           const int64_t xe = ml.xmode ? KR : (int64_t)ml.nr * KR, se = ml.xmode ? KR : ml.L.n;
           if (ml.L.Q > Qmax) Qmax = ml.L.Q;
+          if (ml.L.Q < Qmin) Qmin = ml.L.Q;
           if (xe > xs_elems) xs_elems = xe;
           if (se > scr_elems) scr_elems = se;
         }
-      if (!mma_lds(code, kv, Qmax, xs_elems, scr_elems, &a)) return false;
+      if (!mma_lds(code, kv, Qmin, Qmax, xs_elems, scr_elems, &a)) return false;
       // workgroups: one per unit when they fit one round, else shared out
       // in proportion to the units (at least one per part; a multiple of
       // the ranges where each workgroup keeps one range)

@@ -59,25 +59,41 @@ struct MmaTable {
 };
 
 // HYB at V = 2 with the table at a run-time stride: entry e of the lane's
-// copy at byte e << cshift of tabl.  Where kV divides 16, steps t and
-// t + 16/kV share one 32-bit window and one packed hash (hyb_index_pair).
+// copy at byte e << cshift of the table, which starts at LDS address 0
+// (gemv_mma_kernel has no static LDS, so its dynamic block starts there);
+// lb is the lane's copy, 4 (lane mod copies) bytes.  The signed index is
+// h >> qshift of the 16-bit hash h, and cshift >= qshift (the host keeps at
+// least 2^(qshift - 2) copies), so the address is (h & mask) * 2^(cshift -
+// qshift) + lb: one v_mad_u32_u16 of the masked hash.  Where kV divides 16,
+// steps t and t + 16/kV share one 32-bit window and one packed hash, both
+// halves are masked by one v_and_b32, and the two mads take the high and
+// the low half (op_sel).  Four VALU per two states besides the window.
+typedef __attribute__((address_space(3))) const uint32_t lds_cu32;
 template <int KV>
-__device__ __forceinline__ void hyb_pairs_strided(const uint32_t* w, const char* tabl, int cshift, int qshift,
+__device__ __forceinline__ void hyb_pairs_strided(const uint32_t* w, uint32_t lb, uint32_t mul, uint32_t mask2,
                                                   uint32_t* out) {
-  auto rd = [&](uint32_t e) { return *reinterpret_cast<const uint32_t*>(tabl + (e << cshift)); };
+  auto rd = [&](uint32_t addr) { return *reinterpret_cast<lds_cu32*>((uintptr_t)addr); };
   if constexpr (16 % KV == 0) {
     constexpr int D = 16 / KV;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       if ((t / D) & 1) continue;
-      uint32_t i0, i1;
-      hyb_index_pair(window_raw<32>(w, t * KV), qshift, i0, i1);
-      out[t] = rd(i0);
-      out[t + D] = rd(i1);
+      uint32_t h2, a_first, a_second;
+      asm("v_pk_mad_u16 %0, %1, %1, %1" : "=v"(h2) : "v"(window_raw<32>(w, t * KV)));
+      const uint32_t hm = h2 & mask2;
+      asm("v_mad_u32_u16 %0, %1, %2, %3 op_sel:[1,0,0,0]" : "=v"(a_first) : "v"(hm), "s"(mul), "v"(lb));
+      asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(a_second) : "v"(hm), "s"(mul), "v"(lb));
+      out[t] = rd(a_first);
+      out[t + D] = rd(a_second);
     }
   } else {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) out[t] = rd(hyb_signed_index(window_raw<16>(w, t * KV), qshift));
+    for (int t = 0; t < 16; ++t) {
+      uint32_t a;
+      const uint32_t hm = hyb_hash(window_raw<16>(w, t * KV)) & mask2;
+      asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(a) : "v"(hm), "s"(mul), "v"(lb));
+      out[t] = rd(a);
+    }
   }
 }
 
@@ -321,7 +337,10 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
 
   // ---- 3. the units ----------------------------------------------------------
   const int cshift = a.cshift;
-  const char* tabl = lds + (lane & (a.copies - 1)) * 4;                          // HYB
+  // HYB: the lane's copy, the stride factor and the index mask (both halves)
+  const uint32_t hlb = 4u * (uint32_t)(lane & (a.copies - 1));
+  const uint32_t hmul = 1u << (cshift - qshift);
+  const uint32_t hmask = (0xFFFFu & ~((1u << qshift) - 1u)) * 0x10001u;
   const uint32_t* tabc = smem + (lane & (MmaTable<CODE>::COPIES - 1));          // other codes
   const auto zrs = make_rsrc(zl, (uint32_t)(nr * sstride * 4));
   const int hbits = Bo >= 128 ? 7 : 31 - __builtin_clz((unsigned)Bo);
@@ -337,7 +356,7 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
     lane_words_ready<CODE, KV>(w, lane);
     uint32_t out[16];
     if constexpr (CODE == HYB) {
-      hyb_pairs_strided<KV>(w, tabl, cshift, qshift, out);
+      hyb_pairs_strided<KV>(w, hlb, hmul, hmask, out);
     } else if constexpr (CODE == MAD1) {
       mad1_pairs_centred<KV>(w, out);
     } else {
