@@ -322,10 +322,96 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
     }
   };
 
+  // 4096 values (the whole row of a 4096-column layer, or a 4096-column
+  // range): threads 0 .. 511 hold chunks of 8, index 8 t + e.  Index bits
+  // 0-2 are in registers, bits 3-8 are lane bits 0-5 (butterflies between
+  // lanes: DPP quad permutes for lanes ^1 and ^2, ds_swizzle for ^4, ^8,
+  // ^16, ds_bpermute for ^32), then one exchange through LDS gives thread a
+  // the indices a + 512 k, k < 8, whose bits 9-11 are again in registers;
+  // the results go to x' as fp16.  Two barriers instead of five.
+  auto x_transform_4096 = [&](float* scr) {
+    const int hb_in = 31 - __builtin_clz((unsigned)Bi);
+    const int c = tid;                             // local chunk (threads < 512)
+    const int gc = (xbase >> 3) + c;
+    float v[8];
+    if (c < 512) {
+      const bool ok = gc < nch8;
+      const uint32_t r[4] = {xv[0].x, xv[0].y, xv[0].z, xv[0].w};
+      const uint32_t sg = sw[0] >> ((8 * gc) & 31);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = ok ? h2f((uint16_t)(r[e >> 1] >> (16 * (e & 1)))) : 0.f;
+        v[e] = ((sg >> e) & 1u) ? -f : f;
+      }
+#pragma unroll
+      for (int h = 1; h < 8; h <<= 1) {
+        if (h < Bi) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (!(e & h)) {
+              const float x0 = v[e], x1 = v[e + h];
+              v[e] = x0 + x1;
+              v[e + h] = x0 - x1;
+            }
+          }
+        }
+      }
+      // bits 3-8 between lanes: the lower lane keeps the sum, the upper
+      // one the difference
+      auto stage = [&](int hbit, auto&& partner) {
+        if (hb_in > hbit) {                        // workgroup-uniform
+          const float sgn = (lane >> (hbit - 3)) & 1 ? -1.f : 1.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(v[e], sgn, partner(v[e]));
+        }
+      };
+      stage(3, [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true)); });
+      stage(4, [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true)); });
+      stage(5, [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F | (4 << 10))); });
+      stage(6, [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F | (8 << 10))); });
+      stage(7, [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F | (16 << 10))); });
+      stage(8, [](float x) { return __shfl_xor(x, 32, 64); });
+#pragma unroll
+      for (int e = 0; e < 8; ++e) scr[pad_index(8 * c + e)] = v[e];
+    }
+    __syncthreads();
+    if (c < 512) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = scr[pad_index(c + 512 * k)];
+#pragma unroll
+      for (int h = 1; h < 8; h <<= 1) {
+        if ((h << 9) < Bi) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            if (!(k & h)) {
+              const float x0 = v[k], x1 = v[k + h];
+              v[k] = x0 + x1;
+              v[k + h] = x0 - x1;
+            }
+          }
+        }
+      }
+      const float rs = 1.0f / sqrtf((float)Bi);
+      const int nval = n - xbase < NL ? n - xbase : NL;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = c + 512 * k;
+        xs[i] = i < nval ? (_Float16)(v[k] * rs) : (_Float16)0.f;
+      }
+    }
+    // x' is zero past the 4096 values, to the end of the last range
+    const int npad8 = (xmode == 0 ? nr * KR : KR) >> 3;
+    for (int c8 = 512 + tid; c8 < npad8; c8 += MMA_THREADS)
+      *reinterpret_cast<uint4*>(xs + 8 * c8) = make_uint4(0u, 0u, 0u, 0u);
+  };
+
   // Where LDS allows, the transform has a scratch area of its own and the
   // table is built first, while x is still on its way; otherwise the
   // transform borrows the table's area and the table follows it.
-  if (a.scr_off) {                        // workgroup-uniform
+  if (a.scr_off && NL == 4096) {          // workgroup-uniform
+    build_table();
+    x_transform_4096(reinterpret_cast<float*>(lds + a.scr_off));
+  } else if (a.scr_off) {
     build_table();
     x_transform(reinterpret_cast<float*>(lds + a.scr_off));
   } else {
