@@ -322,19 +322,21 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
     }
   };
 
-  // 4096 values (the whole row of a 4096-column layer, or a 4096-column
-  // range): threads 0 .. 511 hold chunks of 8, index 8 t + e.  Index bits
-  // 0-2 are in registers, bits 3-8 are lane bits 0-5 (butterflies between
-  // lanes: DPP quad permutes for lanes ^1 and ^2, ds_swizzle for ^4, ^8,
-  // ^16, ds_bpermute for ^32), then one exchange through LDS gives thread a
-  // the indices a + 512 k, k < 8, whose bits 9-11 are again in registers;
-  // the results go to x' as fp16.  Two barriers instead of five.
-  auto x_transform_4096 = [&](float* scr) {
+  // NL = 1024, 2048 or 4096 values (the whole row of such a layer, or such
+  // a range): threads t < NL / 8 hold chunks of 8, index 8 t + e.  Index
+  // bits 0-2 are in registers, bits 3-8 are lane bits 0-5 (butterflies
+  // between lanes: DPP quad permutes for lanes ^1 and ^2, ds_swizzle for ^4,
+  // ^8, ^16, ds_bpermute for ^32), then one exchange through LDS gives thread
+  // a < 512 the indices a + 512 k, k < NL / 512, whose bits 9 and up are
+  // again in registers; the results go to x' as fp16.  Two barriers instead
+  // of five.
+  auto x_transform_fast = [&](float* scr) {
     const int hb_in = 31 - __builtin_clz((unsigned)Bi);
-    const int c = tid;                             // local chunk (threads < 512)
+    const int c = tid;                             // local chunk (threads < NL / 8)
     const int gc = (xbase >> 3) + c;
+    const int KK = NL >> 9;                        // values per thread after the exchange
     float v[8];
-    if (c < 512) {
+    if (c < (NL >> 3)) {                           // whole waves
       const bool ok = gc < nch8;
       const uint32_t r[4] = {xv[0].x, xv[0].y, xv[0].z, xv[0].w};
       const uint32_t sg = sw[0] >> ((8 * gc) & 31);
@@ -377,10 +379,10 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
     __syncthreads();
     if (c < 512) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = scr[pad_index(c + 512 * k)];
+      for (int k = 0; k < 8; ++k) v[k] = k < KK ? scr[pad_index(c + 512 * k)] : 0.f;
 #pragma unroll
       for (int h = 1; h < 8; h <<= 1) {
-        if ((h << 9) < Bi) {
+        if ((h << 9) < Bi && h < KK) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             if (!(k & h)) {
@@ -396,21 +398,21 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int i = c + 512 * k;
-        xs[i] = i < nval ? (_Float16)(v[k] * rs) : (_Float16)0.f;
+        if (k < KK) xs[i] = i < nval ? (_Float16)(v[k] * rs) : (_Float16)0.f;
       }
     }
-    // x' is zero past the 4096 values, to the end of the last range
+    // x' is zero past the NL values, to the end of the last range
     const int npad8 = (xmode == 0 ? nr * KR : KR) >> 3;
-    for (int c8 = 512 + tid; c8 < npad8; c8 += MMA_THREADS)
+    for (int c8 = (NL >> 3) + tid; c8 < npad8; c8 += MMA_THREADS)
       *reinterpret_cast<uint4*>(xs + 8 * c8) = make_uint4(0u, 0u, 0u, 0u);
   };
 
   // Where LDS allows, the transform has a scratch area of its own and the
   // table is built first, while x is still on its way; otherwise the
   // transform borrows the table's area and the table follows it.
-  if (a.scr_off && NL == 4096) {          // workgroup-uniform
+  if (a.scr_off && (NL == 1024 || NL == 2048 || NL == 4096)) {   // workgroup-uniform
     build_table();
-    x_transform_4096(reinterpret_cast<float*>(lds + a.scr_off));
+    x_transform_fast(reinterpret_cast<float*>(lds + a.scr_off));
   } else if (a.scr_off) {
     build_table();
     x_transform(reinterpret_cast<float*>(lds + a.scr_off));
