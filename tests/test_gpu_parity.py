@@ -705,6 +705,12 @@ GROUP_CASES = {
                  (synth.MAD1, 768, 2048, 0, dict(kv=2, kv_b=3, m_a=256))],
     # inputs of different lengths in one launch
     "widths": [(synth.HYB, 256, 512, 2, {}), (synth.HYB, 640, 4096, 2, {}), (synth.HYB, 128, 2064, 2, {})],
+    # input Hadamard blocks smaller than the row (1024-, 2048- and 4096-value
+    # transforms whose upper stages are skipped) beside a tiny block
+    "small_blocks": [(synth.HYB, 512, 4096, 2, dict(had_in=2048)), (synth.HYB, 256, 2048, 2, dict(had_in=1024)),
+                     (synth.HYB, 384, 1024, 2, dict(had_in=8))],
+    # one K range per workgroup (1024-column ranges of 256-column blocks)
+    "range_blocks": [(synth.HYB, 8192, 4096, 2, dict(had_in=256))],
 }
 
 
