@@ -439,14 +439,17 @@ bool plan_mma(const LayerArgs* L, const LayerParts* P, int count, const uint16_t
   for (int l0 = 0; l0 < count; ++l0)
     for (int p0 = 0; p0 < P[l0].count; ++p0) {
       if (used[l0][p0]) continue;
-      const int code = P[l0].part[p0].code, kv = P[l0].part[p0].kv;
+      // one launch per (code, width, Q): a HYB launch's table copies must
+      // suit every Q in it (mma_lds)
+      const int code = P[l0].part[p0].code, kv = P[l0].part[p0].kv, Q0 = P[l0].part[p0].Q;
       MmaArgs& a = c->launch[c->nlaunch];
       a.nl = 0;
       int Qmax = 0, Qmin = 16;
       int64_t xs_elems = 0, scr_elems = 0;
       for (int l = l0; l < count; ++l)
         for (int p = 0; p < P[l].count; ++p) {
-          if (used[l][p] || P[l].part[p].code != code || P[l].part[p].kv != kv || a.nl == GEMV_GROUP_MAX)
+          if (used[l][p] || P[l].part[p].code != code || P[l].part[p].kv != kv || P[l].part[p].Q != Q0 ||
+              a.nl == GEMV_GROUP_MAX)
             continue;
           used[l][p] = true;
           MmaLayer& ml = a.lay[a.nl++];

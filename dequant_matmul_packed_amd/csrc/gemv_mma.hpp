@@ -35,7 +35,7 @@
 // stores) into the range's fp32 slice; gemv_finish_kernel adds the slices
 // in range order.
 //
-// A launch may hold several layers of one code and width (a grouped call):
+// A launch may hold several layers of one code, width and Q (a grouped call):
 // workgroups [wg0, wg0 + nwg) take the units of layer l, unit u = local
 // workgroup + i * nwg.  Every wave of a workgroup runs the same number of
 // steps and meets every barrier; every global load is a buffer load issued

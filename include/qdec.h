@@ -226,7 +226,7 @@ size_t qdec_noalloc_scratch_bytes(void);
 /* Several independent one-column products in one call (the projections of
  * a decoder layer that read the same activations, e.g. q, k and v, or gate
  * and up): y[l] = layers[l](x[l]) for l < count <= 8, each as qdec_gemv at
- * batch 1.  The row parts of all layers that share a code and width run in
+ * batch 1.  The row parts of all layers that share a code, width and Q run in
  * one launch of the one-column MFMA kernel, and one finisher launch serves
  * every layer, so a group costs two launches instead of two per layer.
  * x[l]: [n_l] fp16, 16-byte aligned; y[l]: [m_l] fp16, 8-byte aligned, no

@@ -711,6 +711,10 @@ GROUP_CASES = {
                      (synth.HYB, 384, 1024, 2, dict(had_in=8))],
     # one K range per workgroup (1024-column ranges of 256-column blocks)
     "range_blocks": [(synth.HYB, 8192, 4096, 2, dict(had_in=256))],
+    # HYB tables of different sizes (Q = 6: 128 table copies; Q = 10, 11:
+    # fewer): one launch per Q
+    "table_sizes": [(synth.HYB, 256, 1024, 2, dict(Q=6)), (synth.HYB, 384, 2048, 2, dict(Q=10)),
+                    (synth.HYB, 128, 4096, 2, dict(Q=11)), (synth.HYB, 256, 1024, 2, {})],
 }
 
 
