@@ -194,19 +194,24 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
   }
   // HYB: the LUT word of each 16-byte run of the table this thread writes
   // (run w4 = tid + 1024 k holds 4 copies of signed entry (4 w4) / copies;
-  // at most 8 runs per thread: 128 KiB), requested with x
+  // K8 = W4 / 1024 <= 8 runs per thread: at most 128 KiB), requested with x.
+  // The host keeps copies * 2^Q >= 8192, so W4 is a multiple of 1024 and
+  // run k's entry is e0 + step k with e0 = 4 tid / copies < step = 4096 /
+  // copies <= 2^Q: its LUT word is e0 + (step k mod 2^Q), and whether it is
+  // a sign-flipped entry (bit Q) does not depend on the thread.  One vector
+  // offset and scalar offsets: no per-run address arithmetic.
   const int nlut = CODE == HYB ? (1 << Q) : 0;
   const int lc = 31 - __builtin_clz((unsigned)a.copies);
   const int W4 = CODE == HYB ? (a.copies << (Q + 1)) >> 2 : 0;
+  const int K8 = W4 >> 10;
+  const int step = 4096 >> lc;
   uint32_t lw[8];
   {
     const auto lrs = make_rsrc(lut, (uint32_t)nlut * 4u);
+    const uint32_t vo = (uint32_t)((tid << 2) >> lc) * 4u;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int w4 = tid + MMA_THREADS * k;
-      const int e = (w4 << 2) >> lc;
-      lw[k] = buf_load_u32(lrs, w4 < W4 ? (uint32_t)(e & (nlut - 1)) * 4u : BUF_OFF);
-    }
+    for (int k = 0; k < 8; ++k)
+      lw[k] = __builtin_amdgcn_raw_buffer_load_b32(lrs, vo, (uint32_t)((step * k) & (nlut - 1)) * 4u, 0);
   }
   // codes of the whole part through one resource (format sizes below 4 GiB)
   const auto crs = make_rsrc(codes, (uint32_t)((mpart >> 4) * ntc * (int64_t)TB));
@@ -249,13 +254,13 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
       // every thread writes its 16-byte runs of consecutive copies
       // (conflict-free writes) from the LUT words it loaded at the start;
       // entries 2^Q and up are the sign-flipped ones
-      uint4* tab4 = reinterpret_cast<uint4*>(lds);
+      uint4* tab4 = reinterpret_cast<uint4*>(lds) + tid;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int w4 = tid + MMA_THREADS * k;
-        const int e = (w4 << 2) >> lc;
-        const uint32_t v = lw[k] ^ (((e >> Q) & 1) ? 0x80008000u : 0u);
-        if (w4 < W4) tab4[w4] = make_uint4(v, v, v, v);
+        if (k < K8) {                              // workgroup-uniform
+          const uint32_t v = lw[k] ^ ((((step * k) >> Q) & 1) ? 0x80008000u : 0u);
+          tab4[MMA_THREADS * k] = make_uint4(v, v, v, v);
+        }
       }
     } else {
       constexpr int C = MmaTable<CODE>::COPIES;
@@ -481,10 +486,12 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
 
   // The end of a unit: lanes 0, 16, 32, 48 hold column 0 of the products,
   // D[i][0] for i = 4 (lane / 16) + e, MFMA row i being row
-  // 16 (i / 8) + 2 (i % 8) + ra of the wave's 32.  Every wave then adds the
+  // 16 (i / 8) + 2 (i % 8) + ra of the wave's 32.  Wave 0 then adds the
   // four quarters of the panel (quarter order), applies the in-panel
-  // Hadamard stages, and wave 0's store goes out (the others' are switched
-  // off by their offsets).
+  // Hadamard stages (row bit 0 in registers, bits 1-6 between lanes: DPP
+  // quad permutes, ds_swizzle, one ds_bpermute; the upper lane of a pair
+  // keeps the difference, fma(v, -1, o) = o - v exactly) and stores the
+  // panel; the other waves go on to their next unit.
   auto unit_end = [&]() {
     float* red = reinterpret_cast<float*>(lds + a.red_off) + (ck & 1) * 512;
     if ((lane & 15) == 0) {
@@ -499,29 +506,39 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
     acc[0] = float4v{0.f, 0.f, 0.f, 0.f};
     acc[1] = float4v{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
-    float v0 = 0.f, v1 = 0.f;
+    if (wave == 0) {
+      float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const float2 p = *reinterpret_cast<const float2*>(red + k4 * 128 + 2 * lane);
-      v0 += p.x;
-      v1 += p.y;
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const float2 p = *reinterpret_cast<const float2*>(red + k4 * 128 + 2 * lane);
+        v0 += p.x;
+        v1 += p.y;
+      }
+      if (hbits > 0) {
+        const float s = v0 + v1;
+        v1 = v0 - v1;
+        v0 = s;
+      }
+      // row bit b (b >= 1) is lane bit b - 1
+      auto stage = [&](int b, auto&& partner) {
+        if (hbits > b) {                          // workgroup-uniform
+          const float sg = (lane >> (b - 1)) & 1 ? -1.f : 1.f;
+          v0 = __builtin_fmaf(v0, sg, partner(v0));
+          v1 = __builtin_fmaf(v1, sg, partner(v1));
+        }
+      };
+      stage(1, [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true)); });
+      stage(2, [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true)); });
+      stage(3, [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F | (4 << 10))); });
+      stage(4, [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F | (8 << 10))); });
+      stage(5, [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F | (16 << 10))); });
+      stage(6, [](float x) { return __shfl_xor(x, 32, 64); });
+      const uint32_t off = (uint32_t)(((int64_t)cr * sstride + row0 + (int64_t)cp * 128 + 2 * lane) * 4);
+      __builtin_amdgcn_raw_buffer_store_b64(
+          __builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t,
+                             make_uint2(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1))),
+          zrs, off, 0, 0);
     }
-    if (hbits > 0) {
-      const float s = v0 + v1;
-      v1 = v0 - v1;
-      v0 = s;
-    }
-    for (int msk = 1; msk < (1 << (hbits > 0 ? hbits - 1 : 0)); msk <<= 1) {
-      const float o0 = __shfl_xor(v0, msk, 64), o1 = __shfl_xor(v1, msk, 64);
-      const bool hi = lane & msk;
-      v0 = hi ? o0 - v0 : v0 + o0;
-      v1 = hi ? o1 - v1 : v1 + o1;
-    }
-    const uint32_t off = (uint32_t)(((int64_t)cr * sstride + row0 + (int64_t)cp * 128 + 2 * lane) * 4);
-    __builtin_amdgcn_raw_buffer_store_b64(
-        __builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t,
-                           make_uint2(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1))),
-        zrs, wave == 0 ? off : BUF_OFF, 0, 0);
     ++ck;
     cs = 0;
     cp += dp;

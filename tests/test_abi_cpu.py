@@ -267,3 +267,9 @@ def test_noalloc_entry_point_rejects_before_any_launch(q):
     assert st(_layer(q), 0) == q.QDEC_EINVAL
     assert st(_layer(q), 9) == q.QDEC_EUNSUPPORTED
     assert st(_layer(q), 1) == q.QDEC_ENODEV          # valid: no device here
+
+
+def test_header_abi_version_matches_binding(q):
+    """The binding's copy of the header's ABI version."""
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "qdec.h")).read()
+    assert int(re.search(r"#define QDEC_ABI_VERSION (\d+)u", hdr).group(1)) == q.QDEC_ABI_VERSION
