@@ -62,7 +62,12 @@ def main():
         if not (os.path.exists(fp) and os.path.exists(wp)):
             continue
         fetch, write = per_kernel(fp), per_kernel(wp)
-        ck = max(write, key=lambda k: write[k][1])          # the copy: the largest write
+        # the copy: the blit kernel, else the kernel whose writes come
+        # closest to its size (the largest write can be the code pool's
+        # random fill, which writes 1 GiB and reads nothing)
+        copies = [k for k in write if "copyBuffer" in k[0]]
+        ck = (max(copies, key=lambda k: write[k][1]) if copies
+              else min(write, key=lambda k: abs(write[k][1] - (COPY_MIB << 10))))
         f_scale = (COPY_MIB << 20) / (fetch[ck][1] * 1024)
         w_scale = (COPY_MIB << 20) / (write[ck][1] * 1024)
         ks = [k for k in fetch if k[0].startswith("qdec::") and k in write]

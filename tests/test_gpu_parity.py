@@ -715,6 +715,9 @@ GROUP_CASES = {
     # fewer): one launch per Q
     "table_sizes": [(synth.HYB, 256, 1024, 2, dict(Q=6)), (synth.HYB, 384, 2048, 2, dict(Q=10)),
                     (synth.HYB, 128, 4096, 2, dict(Q=11)), (synth.HYB, 256, 1024, 2, {})],
+    # more units than workgroups (448 panels on 256 workgroups): some
+    # workgroups walk two units, each unit's slice rows written once
+    "several_units": [(synth.HYB, 28672, 4096, 2, {}), (synth.HYB, 28672, 4096, 2, {})],
 }
 
 
