@@ -242,6 +242,135 @@ __global__ __launch_bounds__(256) void rht_kernel(RhtArgs a) {
   }
 }
 
+// Blocks of 2048 J values (J = 1, 2, 4): the chunks, loads and signs of
+// rht_kernel, but one barrier.  Index 8 (tid + 256 j) + e: bits 0-2 (e) are
+// butterflies in registers, bits 3-8 (lane bits 0-5) butterflies between
+// lanes (DPP quad permutes for lanes ^1 and ^2, ds_swizzle for ^4, ^8, ^16,
+// ds_bpermute for ^32); one exchange through LDS then gives thread t the
+// indices t + 256 k (k < 8 J), whose bits 9 and up are butterflies in
+// registers again, and the results are stored from there (one store of a
+// wave covers 64 consecutive entries).  The stages run in ascending bit
+// order, as rht_kernel's, and each is the same sum or difference, so both
+// kernels give the same bits.  A workgroup reads its whole block before it
+// writes: in place is safe.
+template <bool IN_F32, int J>
+__global__ __launch_bounds__(256) void rht_lanes_kernel(RhtArgs a) {
+  extern __shared__ __align__(16) float buf[];
+  constexpr int SU = IN_F32 ? (J >= 4 ? 1 : 4 / J) : 1;   // fp32 slices per round
+  constexpr int K = 8 * J;                                 // values per thread
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int B = 2048 * J;
+  const int64_t nblk = a.n / B;
+  const int64_t row = blockIdx.x / nblk;
+  const int64_t c0 = (blockIdx.x % nblk) * B;
+  const int64_t off = row * a.n + c0;
+  const bool out_signs = a.mode == 1;
+  // sign words: on the input side those of the thread's chunks (8 tid +
+  // 2048 j), on the output side those of its outputs (tid + 256 k)
+  const auto srs = make_rsrc(a.signs, a.signs ? (uint32_t)(((a.n + 31) >> 5) * 4) : 0u);
+  uint32_t sw[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t i = out_signs ? c0 + tid + 256 * k : c0 + 8 * (tid + 256 * k);
+    sw[k] = buf_load_u32(srs, (out_signs || k < J) ? (uint32_t)((i >> 5) * 4) : BUF_OFF);
+  }
+  float v[J][8];
+  if constexpr (IN_F32) {
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+    const float* base = (const float*)a.in + off;
+    const auto irs = make_rsrc(base, (uint32_t)(((a.nsum - 1) * a.sum_stride + B) * 4));
+    for (int s0 = 0; s0 < a.nsum; s0 += SU) {
+      uint4 p[SU][J][2];
+#pragma unroll
+      for (int su = 0; su < SU; ++su)
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const int ch = tid + 256 * j;
+          const bool ok = s0 + su < a.nsum;
+          const uint32_t o = (uint32_t)(((s0 + su) * a.sum_stride + 8 * ch) * 4);
+          p[su][j][0] = buf_load_u4(irs, ok ? o : BUF_OFF);
+          p[su][j][1] = buf_load_u4(irs, ok ? o + 16u : BUF_OFF);
+        }
+#pragma unroll
+      for (int su = 0; su < SU; ++su)
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const uint32_t r[8] = {p[su][j][0].x, p[su][j][0].y, p[su][j][0].z, p[su][j][0].w,
+                                 p[su][j][1].x, p[su][j][1].y, p[su][j][1].z, p[su][j][1].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[j][e] += __builtin_bit_cast(float, r[e]);
+        }
+    }
+  } else {
+    const auto irs = make_rsrc((const uint16_t*)a.in + off, (uint32_t)B * 2u);
+    uint4 p[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) p[j] = buf_load_u4(irs, (uint32_t)(tid + 256 * j) * 16u);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint32_t r[4] = {p[j].x, p[j].y, p[j].z, p[j].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[j][e] = h2f((uint16_t)(r[e >> 1] >> (16 * (e & 1))));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (!out_signs) {
+      const uint32_t sg = sw[j] >> ((c0 + 8 * (tid + 256 * j)) & 31);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if ((sg >> e) & 1u) v[j][e] = -v[j][e];
+    }
+    fwht_regs<8>(v[j]);
+  }
+  // bits 3-8 between lanes: the lower lane keeps the sum, the upper one the
+  // difference (fma(v, -1, o) = o - v exactly)
+  auto stage = [&](int lbit, auto&& partner) {
+    const float sgn = (lane >> lbit) & 1 ? -1.f : 1.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[j][e] = __builtin_fmaf(v[j][e], sgn, partner(v[j][e]));
+  };
+  stage(0, [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true)); });
+  stage(1, [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true)); });
+  stage(2, [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F | (4 << 10))); });
+  stage(3, [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F | (8 << 10))); });
+  stage(4, [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F | (16 << 10))); });
+  stage(5, [](float x) { return __shfl_xor(x, 32, 64); });
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) buf[pad_index(8 * (tid + 256 * j) + e)] = v[j][e];
+  __syncthreads();
+  float w[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) w[k] = buf[pad_index(tid + 256 * k)];
+  // bits 9 and up: k bits 1 and up
+#pragma unroll
+  for (int h = 2; h < K; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      if (!(i & h)) {
+        const float x0 = w[i], x1 = w[i + h];
+        w[i] = x0 + x1;
+        w[i + h] = x0 - x1;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t i = c0 + tid + 256 * k;
+    float o = w[k] * a.mult;
+    if (out_signs && ((sw[k] >> (i & 31)) & 1u)) o = -o;
+    if (a.out_f32) ((float*)a.out)[row * a.n + i] = o;
+    else ((uint16_t*)a.out)[row * a.n + i] = f2h_bits(o);
+  }
+}
+
 // fp16 input with few (row, block) pairs: each block is cut over S
 // workgroups.  With Sylvester ordering H_B = H_S (x) H_Bs (Bs = B / S), so
 // outputs [j Bs, (j+1) Bs) of a block are H_Bs applied to u = sum over a of
@@ -360,8 +489,23 @@ static hipError_t launch_rht_j(const RhtArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <bool IN_F32, int J>
+static hipError_t launch_rht_lanes(const RhtArgs& a, hipStream_t stream) {
+  static LdsLimit have;
+  const size_t lds = (size_t)padded_words(a.block) * 4;
+  const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&rht_lanes_kernel<IN_F32, J>), lds, &have);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((rht_lanes_kernel<IN_F32, J>), dim3((unsigned)(a.rows * (a.n / a.block))), dim3(256), lds,
+                     stream, a);
+  return hipGetLastError();
+}
+
 template <bool IN_F32>
 static hipError_t launch_rht_in(const RhtArgs& a, hipStream_t stream) {
+  // blocks of 2048, 4096 and 8192 values: one barrier (rht_lanes_kernel)
+  if (a.block == 2048) return launch_rht_lanes<IN_F32, 1>(a, stream);
+  if (a.block == 4096) return launch_rht_lanes<IN_F32, 2>(a, stream);
+  if (a.block == 8192) return launch_rht_lanes<IN_F32, 4>(a, stream);
   const int nch = a.block >> 3;
   if (nch <= 256) return launch_rht_j<IN_F32, 1>(a, stream);
   if (nch <= 512) return launch_rht_j<IN_F32, 2>(a, stream);
