@@ -139,6 +139,15 @@ def algorithmic_bytes(m, n, k, b, lut_bytes=0, gscale_bytes=0):
     return m * n * k // 8 + 2 * b * n + 2 * b * m + (m + n) // 8 + lut_bytes + gscale_bytes
 
 
+def sha256_tensor(torch, t, chunk=1 << 26):
+    """SHA-256 of a tensor's bytes (copied to the host 64 MiB at a time)."""
+    h = hashlib.sha256()
+    flat = t.reshape(-1).view(torch.uint8)
+    for i in range(0, flat.numel(), chunk):
+        h.update(flat[i:i + chunk].cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
 def make_pool_layers(q, torch, dev, code, m, n, k, count, tag, **kw):
     """`count` layers sharing signs/LUT but with distinct random codes (extra
     keyword arguments go to synth.make_layer, e.g. V and Q)."""
@@ -271,6 +280,19 @@ def llama_stack(q, torch, dev, args):
     xt = {g: torch.from_numpy(synth.activations("bench/stack/x_" + g, 1, n).view(np.int16)).to(dev)
           for g, n in (("qkv", 4096), ("o", 4096), ("gate_up", 4096), ("down", 14336))}
     ys = {nm: torch.empty((1, s.m), dtype=torch.float16, device=dev) for nm, s in specs.items()}
+    # the generated buffers, by SHA-256 (each projection's code pool, table
+    # and sign vectors; the activations): the inputs are fixed by the seeds
+    inputs = {"generator": "codes: torch.randint on the device (uniform int32 words), seeded by the tag; "
+                           "tables, signs and activations: synth (SHA-256-seeded numpy generators)",
+              "sha256": {}}
+    for nm in (specs if not args.call else ()):     # not in counter runs (no extra copies)
+        b0 = lay[nm][0]
+        inputs["sha256"]["codes/" + nm] = sha256_tensor(torch, pools[list(specs).index(nm)])
+        for part in ("lut", "sign_in", "sign_out"):
+            if getattr(b0, part) is not None:
+                inputs["sha256"]["%s/%s" % (part, nm)] = sha256_tensor(torch, getattr(b0, part))
+    for g, t in (xt.items() if not args.call else ()):
+        inputs["sha256"]["x/" + g] = sha256_tensor(torch, t)
     ws_qkv = torch.empty(q.qdec_gemv_group_workspace_bytes([lay[n][0] for n in ("q", "k", "v")]),
                          dtype=torch.uint8, device=dev)
     ws_gu = torch.empty(q.qdec_gemv_group_workspace_bytes([lay[n][0] for n in ("gate", "up")]),
@@ -359,7 +381,7 @@ def llama_stack(q, torch, dev, args):
     log("calls of a layer (us):", {g: v["us"] for g, v in per_call.items()})
     return {"gbs": gbs, "elapsed": elapsed, "ms_per_step": ms_per_step, "us_per_layer": us_layer,
             "step_bytes": step_bytes, "layer_bytes": layer_bytes, "mode": mode, "probe": probe,
-            "per_call": per_call, "dominant": dom_name, "dom": dom}
+            "per_call": per_call, "dominant": dom_name, "dom": dom, "inputs": inputs}
 
 
 def main():
@@ -389,10 +411,10 @@ def main():
     torch.cuda.empty_cache()
     G = bench_gemm(q, torch, dev, stream)
     dom = H["dom"]
-    kernels = {"gate_up": "qdec_gemv_group over gate and up (gemv_mma_kernel + gemv_finish_kernel)",
-               "qkv": "qdec_gemv_group over q, k, v (gemv_mma_kernel + gemv_finish_kernel)",
-               "down": "qdec_gemv 4096x14336 (gemv_mma_kernel + gemv_finish_kernel)",
-               "o": "qdec_gemv 4096x4096 (gemv_kernel + gemv_finish_kernel)"}
+    kernels = {"gate_up": "qdec_gemv_group over gate and up (gemv_mma_kernel + gemv_finish_lanes_kernel)",
+               "qkv": "qdec_gemv_group over q, k, v (gemv_mma_kernel + gemv_finish_lanes_kernel)",
+               "down": "qdec_gemv 4096x14336 (gemv_mma_kernel + gemv_finish_lanes_kernel)",
+               "o": "qdec_gemv 4096x4096 (gemv_mma_kernel + gemv_finish_lanes_kernel)"}
     traffic = measured_traffic(H["dominant"], dom["algorithmic_bytes"])
     traffic_b64 = measured_traffic("gemm", G["algorithmic_bytes"])
     detail = {"per_call_of_a_layer": H["per_call"], "launch_probe": H["probe"],
@@ -449,7 +471,7 @@ def main():
                      "timing": "HIP events around 200 back-to-back calls on the launch stream (codes "
                                "rotating over the stack's layers), median of 5; a call is two kernels"},
         "roofline_b64": {"bound": "mfma", "kernel": "qdec_gemm 28672x8192 HYB k=3, X 64x8192 "
-                                                    "(rht_split_kernel + gemm_kernel + rht_kernel)",
+                                                    "(rht_split_kernel + gemm_kernel + rht_lanes_kernel)",
                          "achieved": G["TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(G["TFLOPs"] / MFMA_F16_PEAK_TFLOPS, 4),
                          "traffic": traffic_b64["bytes_per_call"] if traffic_b64 else None,
@@ -457,6 +479,7 @@ def main():
                          "flops_per_launch": G["flops"], "avg_launch_us": G["us_per_call"],
                          "timing": G["protocol"]},
         "cpu_baseline": cpu,
+        "inputs": H["inputs"],
         "detail": detail,
     }
     print(json.dumps(line), flush=True)

@@ -26,7 +26,7 @@ QDEC_ABI_VERSION = 2
 EXPORTS = ("qdec_abi_version", "qdec_status_string", "qdec_last_error", "qdec_workspace_bytes",
            "qdec_rht", "qdec_gemv", "qdec_gemm", "qdec_decode_tile", "qdec_encode",
            "qdec_gemv_group", "qdec_gemv_group_workspace_bytes", "qdec_gemv_noalloc",
-           "qdec_noalloc_scratch_bytes")
+           "qdec_noalloc_scratch_bytes", "qdec_debug_fail_launches")
 GEMV_GROUP_MAX = 8
 
 
@@ -61,6 +61,8 @@ def _load():
     P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.qdec_abi_version.restype = ctypes.c_uint32
     lib.qdec_abi_version.argtypes = []
+    lib.qdec_debug_fail_launches.restype = ctypes.c_int
+    lib.qdec_debug_fail_launches.argtypes = [ctypes.c_int32]
     lib.qdec_status_string.restype = ctypes.c_char_p
     lib.qdec_status_string.argtypes = [ctypes.c_int]
     lib.qdec_last_error.restype = ctypes.c_char_p

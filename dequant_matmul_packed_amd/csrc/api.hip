@@ -172,6 +172,12 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 // The current device must be a gfx950 part; checked once per device.
+// Test hook (qdec_debug_fail_launches): calls that reach the launch stage
+// while it is positive take one from it and return QDEC_EHIP, launching
+// nothing.
+std::atomic<int> g_fail_launches{0};
+int injected_failure();
+
 int check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
@@ -183,7 +189,7 @@ int check_device() {
   static std::atomic<int> state[64];
   if (dev < 64) {
     const int st = state[dev].load(std::memory_order_relaxed);
-    if (st) return st > 0 ? QDEC_OK : QDEC_ENODEV;
+    if (st) return st > 0 ? injected_failure() : QDEC_ENODEV;
   }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
@@ -192,10 +198,21 @@ int check_device() {
   }
   const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
   if (dev < 64) state[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
-  return ok ? QDEC_OK : QDEC_ENODEV;
+  return ok ? injected_failure() : QDEC_ENODEV;
 }
 
 thread_local char g_last_error[256] = "no error";
+
+int injected_failure() {
+  int n = g_fail_launches.load(std::memory_order_relaxed);
+  while (n > 0) {
+    if (g_fail_launches.compare_exchange_weak(n, n - 1, std::memory_order_relaxed)) {
+      snprintf(g_last_error, sizeof g_last_error, "injected launch failure (qdec_debug_fail_launches)");
+      return QDEC_EHIP;
+    }
+  }
+  return QDEC_OK;
+}
 
 int status_of(hipError_t e) {
   if (e == hipSuccess) return QDEC_OK;
@@ -562,6 +579,12 @@ size_t gemv_ws_bytes(int64_t m, int64_t n, int64_t b) { return gemv_ws_layout(m,
 extern "C" {
 
 uint32_t qdec_abi_version(void) { return QDEC_ABI_VERSION; }
+
+int qdec_debug_fail_launches(int32_t count) {
+  if (count < 0) return QDEC_EINVAL;
+  g_fail_launches.store(count, std::memory_order_relaxed);
+  return QDEC_OK;
+}
 
 const char* qdec_last_error(void) { return g_last_error; }
 

@@ -277,6 +277,13 @@ int qdec_encode(const qdec_layer *layer, const float *w, uint32_t *codes, void *
 int qdec_decode_tile(const qdec_layer *layer, int64_t first_tile,
                      int64_t n_tiles, uint16_t *out, void *stream);
 
+/* Test hook for callers' error paths: the next `count` calls (of any entry
+ * point) that pass their argument checks and find a gfx950 device return
+ * QDEC_EHIP without launching anything, and qdec_last_error names the hook.
+ * count = 0 clears it.  QDEC_EINVAL for a negative count.  The count is
+ * shared by every thread of the process.                                    */
+int qdec_debug_fail_launches(int32_t count);
+
 /* Human-readable name of a status code (static storage).                    */
 const char *qdec_status_string(int status);
 

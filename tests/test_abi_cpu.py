@@ -273,3 +273,24 @@ def test_header_abi_version_matches_binding(q):
     """The binding's copy of the header's ABI version."""
     hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "qdec.h")).read()
     assert int(re.search(r"#define QDEC_ABI_VERSION (\d+)u", hdr).group(1)) == q.QDEC_ABI_VERSION
+
+
+def test_fail_launches_hook_arguments(q):
+    """qdec_debug_fail_launches: a negative count is rejected; a pending
+    injected failure is taken only by a call that reaches the launch stage,
+    so argument errors (and, with no device, ENODEV) come first."""
+    assert q._lib.qdec_debug_fail_launches(-1) == q.QDEC_EINVAL
+    assert q._lib.qdec_debug_fail_launches(1) == q.QDEC_OK
+    try:
+        lay = _layer(q)
+        d = ctypes.byref(lay.desc())
+        need = q.qdec_workspace_bytes(lay, 1, q.QDEC_OP_GEMV)
+        # an argument error wins over the pending failure
+        assert q.raw_status("qdec_gemv", d, FAKE + 2, FAKE + (1 << 25), 1, FAKE + (1 << 26), need,
+                            None) == q.QDEC_EINVAL
+        if not _has_gpu():
+            st = q.raw_status("qdec_gemv", d, FAKE + (1 << 24), FAKE + (1 << 25), 1, FAKE + (1 << 26), need,
+                              None)
+            assert st == q.QDEC_ENODEV
+    finally:
+        assert q._lib.qdec_debug_fail_launches(0) == q.QDEC_OK

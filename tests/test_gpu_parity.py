@@ -307,6 +307,36 @@ def test_gemv_edge_cases(q, dev):
             assert torch.equal(yy, ys[0]), b                 # fixed summation order
 
 
+def test_injected_launch_failure(q, dev):
+    """qdec_debug_fail_launches(1): the next call returns QDEC_EHIP, names the
+    hook in qdec_last_error and launches nothing (its output keeps a
+    sentinel); the call after it runs normally and matches the oracle."""
+    import ctypes
+    import torch
+    host = synth.make_layer(synth.HYB, 256, 512, 2, tag="inject")
+    x16 = synth.activations("inject/x", 1, 512)
+    lay = q.upload_layer(host, dev)
+    xt = _f16_tensor(x16, dev)
+    y = torch.full((1, 256), 7.0, dtype=torch.float16, device=dev)
+    ws = q.workspace(lay, 1, q.QDEC_OP_GEMV, dev)
+    torch.cuda.synchronize()
+    _say("injected launch failure")
+    assert q._lib.qdec_debug_fail_launches(1) == q.QDEC_OK
+    try:
+        st = q.raw_status("qdec_gemv", ctypes.byref(lay.desc()), xt.data_ptr(), y.data_ptr(), 1,
+                          ws.data_ptr(), ws.numel(), None)
+        msg = q._lib.qdec_last_error()
+    finally:
+        q._lib.qdec_debug_fail_launches(0)
+    assert st == q.QDEC_EHIP
+    assert b"injected" in msg
+    torch.cuda.synchronize()
+    assert bool(torch.all(y == 7.0))
+    y2 = q.gemv(lay, xt, ws=ws, y=y)
+    torch.cuda.synchronize()
+    _check_output(_to_f64(y2), oracle.forward(host, x16))
+
+
 def test_gemv_mixed_batches_one_workspace(q, dev):
     """One workspace sized for 8 columns serves calls of every batch in any
     order: on a 14336x4096 layer 8 columns take the batched MFMA path
