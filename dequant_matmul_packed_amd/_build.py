@@ -22,6 +22,9 @@ HIPCC_FLAGS = [
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=fast", "-Wall", "-Wno-unused-function",
+    # preload the leading scalar kernel arguments (up to 16) into SGPRs at
+    # wave launch: the GEMV kernels pass their layer bounds there
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -115,7 +115,8 @@ __device__ __forceinline__ void mad1_pairs_centred(const uint32_t* w, uint32_t* 
 }
 
 template <int CODE, int KV, int PF>
-__global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
+__global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(QDEC_BOUNDS_PARAMS, int xs_off_, int red_off_, int scr_off_, int cshift_,
+                                                                 int copies_, MmaArgs a) {
   using G = LaneGeom<CODE, KV>;
   constexpr int NW = G::NW;
   constexpr int CW = CODE == NUQ ? NW + 2 : NW;          // ring words per slot (+ NUQ scales)
@@ -129,10 +130,8 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
   const int q = lane & 7, t8 = lane >> 3, tr = t8 & 1, tc = t8 >> 1;
 
   // ---- this workgroup's layer (workgroup-uniform) ---------------------------
-  int li = 0;
-#pragma unroll
-  for (int i = 1; i < GEMV_GROUP_MAX; ++i)
-    if (i < a.nl && (int)blockIdx.x >= a.lay[i].wg0) li = i;
+  (void)nl_;
+  const int li = QDEC_LAYER_OF((int)blockIdx.x);
   const uint32_t* codes = a.lay[li].L.codes;
   const uint32_t* lut = a.lay[li].L.lut;
   const uint16_t* gscale = a.lay[li].L.gscale;
@@ -148,6 +147,13 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
   const int bl = (int)blockIdx.x - a.lay[li].wg0, nwg = a.lay[li].nwg, units = a.lay[li].units;
 
   const int xmode = a.lay[li].xmode;
+  // the layer's fields in one round of scalar loads (the compiler would
+  // otherwise issue some only where they are first used, after the first
+  // round has returned); the launch's LDS carve-up and table geometry come
+  // preloaded with the layer bounds
+  asm volatile("" ::"s"(codes), "s"(lut), "s"(gscale), "s"(sign_in), "s"(mpart), "s"(n), "s"(qshift), "s"(Q),
+               "s"(group), "s"(Bi), "s"(Bo), "s"(xg), "s"(zl), "s"(sstride), "s"(row0), "s"(nr), "s"(KR), "s"(bl),
+               "s"(nwg), "s"(units), "s"(xmode));
   const int ntc = n >> 4;                 // tile columns
   const int npanels = (int)(mpart >> 7);
   const int Kw = KR >> 2, S = Kw >> 6;    // columns and steps of a quarter
@@ -201,8 +207,8 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
   // a sign-flipped entry (bit Q) does not depend on the thread.  One vector
   // offset and scalar offsets: no per-run address arithmetic.
   const int nlut = CODE == HYB ? (1 << Q) : 0;
-  const int lc = 31 - __builtin_clz((unsigned)a.copies);
-  const int W4 = CODE == HYB ? (a.copies << (Q + 1)) >> 2 : 0;
+  const int lc = 31 - __builtin_clz((unsigned)copies_);
+  const int W4 = CODE == HYB ? (copies_ << (Q + 1)) >> 2 : 0;
   const int K8 = W4 >> 10;
   const int step = 4096 >> lc;
   uint32_t lw[8];
@@ -276,7 +282,7 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
   // Chunks of 8 consecutive values: the butterfly stages inside a chunk in
   // registers, the rest in padded LDS in passes of 3 index bits (512 groups of
   // 8 values on a 4096-value row: every thread busy).
-  _Float16* xs = reinterpret_cast<_Float16*>(lds + a.xs_off);
+  _Float16* xs = reinterpret_cast<_Float16*>(lds + xs_off_);
   auto x_transform = [&](float* scr) {
     const int hb_in = 31 - __builtin_clz((unsigned)Bi);
 #pragma unroll
@@ -415,12 +421,12 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
   // Where LDS allows, the transform has a scratch area of its own and the
   // table is built first, while x is still on its way; otherwise the
   // transform borrows the table's area and the table follows it.
-  if (a.scr_off && (NL == 1024 || NL == 2048 || NL == 4096)) {   // workgroup-uniform
+  if (scr_off_ && (NL == 1024 || NL == 2048 || NL == 4096)) {   // workgroup-uniform
     build_table();
-    x_transform_fast(reinterpret_cast<float*>(lds + a.scr_off));
-  } else if (a.scr_off) {
+    x_transform_fast(reinterpret_cast<float*>(lds + scr_off_));
+  } else if (scr_off_) {
     build_table();
-    x_transform(reinterpret_cast<float*>(lds + a.scr_off));
+    x_transform(reinterpret_cast<float*>(lds + scr_off_));
   } else {
     x_transform(reinterpret_cast<float*>(lds));
     __syncthreads();                      // the scratch is read; the table overwrites it
@@ -429,9 +435,9 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
   __syncthreads();
 
   // ---- 3. the units ----------------------------------------------------------
-  const int cshift = a.cshift;
+  const int cshift = cshift_;
   // HYB: the lane's copy, the stride factor and the index mask (both halves)
-  const uint32_t hlb = 4u * (uint32_t)(lane & (a.copies - 1));
+  const uint32_t hlb = 4u * (uint32_t)(lane & (copies_ - 1));
   const uint32_t hmul = 1u << (cshift - qshift);
   const uint32_t hmask = (0xFFFFu & ~((1u << qshift) - 1u)) * 0x10001u;
   const uint32_t* tabc = smem + (lane & (MmaTable<CODE>::COPIES - 1));          // other codes
@@ -493,7 +499,7 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(MmaArgs a) {
   // keeps the difference, fma(v, -1, o) = o - v exactly) and stores the
   // panel; the other waves go on to their next unit.
   auto unit_end = [&]() {
-    float* red = reinterpret_cast<float*>(lds + a.red_off) + (ck & 1) * 512;
+    float* red = reinterpret_cast<float*>(lds + red_off_) + (ck & 1) * 512;
     if ((lane & 15) == 0) {
 #pragma unroll
       for (int ra = 0; ra < 2; ++ra)
@@ -569,7 +575,11 @@ hipError_t launch_gemv_mma_p(const MmaArgs& a, unsigned grid, size_t lds, hipStr
   static LdsLimit have;
   const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_mma_kernel<CODE, KV, PF>), lds, &have);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemv_mma_kernel<CODE, KV, PF>), dim3(grid), dim3(MMA_THREADS), lds, stream, a);
+  LayerBounds b;
+  b.w[0] = a.nl;
+  for (int i = 1; i < GEMV_GROUP_MAX; ++i) b.w[i] = i < a.nl ? a.lay[i].wg0 : INT_MAX;
+  hipLaunchKernelGGL((gemv_mma_kernel<CODE, KV, PF>), dim3(grid), dim3(MMA_THREADS), lds, stream,
+                     QDEC_BOUNDS_ARGS(b), a.xs_off, a.red_off, a.scr_off, a.cshift, a.copies, a);
   return hipGetLastError();
 }
 

@@ -578,13 +578,11 @@ namespace qdec {
 // slice order (a fixed order: the output is reproducible bit for bit), run
 // the remaining stages in LDS, scale, apply the output signs and write fp16.
 template <int J>   // float4 chunks per thread: rows_wg <= 4096 J
-__global__ __launch_bounds__(1024) void gemv_finish_kernel(FinishArgs a) {
+__global__ __launch_bounds__(1024) void gemv_finish_kernel(QDEC_BOUNDS_PARAMS, FinishArgs a) {
   extern __shared__ __align__(16) float buf[];
   constexpr int SU = 16 / J;                      // slices per round of loads (16 float4 per thread)
-  int li = 0;
-#pragma unroll
-  for (int i = 1; i < GEMV_GROUP_MAX; ++i)
-    if (i < a.nl && (int)blockIdx.x >= a.lay[i].wg0) li = i;
+  (void)nl_;
+  const int li = QDEC_LAYER_OF((int)blockIdx.x);
   const float* z = a.lay[li].z;
   const int64_t sstride = a.lay[li].slice_stride, m = a.lay[li].m;
   const int nsl = a.lay[li].nslices, Bo = a.lay[li].Bo, R = a.lay[li].rows_wg;
@@ -668,12 +666,20 @@ __global__ __launch_bounds__(1024) void gemv_finish_kernel(FinishArgs a) {
   }
 }
 
+static LayerBounds finish_bounds(const FinishArgs& a) {
+  LayerBounds b;
+  b.w[0] = a.nl;
+  for (int i = 1; i < GEMV_GROUP_MAX; ++i) b.w[i] = i < a.nl ? a.lay[i].wg0 : INT_MAX;
+  return b;
+}
+
 template <int J>
 static hipError_t launch_finish_j(const FinishArgs& a, unsigned grid, size_t lds, hipStream_t stream) {
   static LdsLimit have;
   const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_finish_kernel<J>), lds, &have);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gemv_finish_kernel<J>), dim3(grid), dim3(1024), lds, stream, a);
+  hipLaunchKernelGGL((gemv_finish_kernel<J>), dim3(grid), dim3(1024), lds, stream, QDEC_BOUNDS_ARGS(finish_bounds(a)),
+                     a);
   return hipGetLastError();
 }
 
@@ -695,27 +701,31 @@ __device__ __forceinline__ void lane_butterfly(float& v, int lane) {
   v = (lane & H) ? o - v : v + o;
 }
 
-__global__ __launch_bounds__(256) void gemv_finish_lanes_kernel(FinishArgs a) {
-  int li = 0;
-#pragma unroll
-  for (int i = 1; i < GEMV_GROUP_MAX; ++i)
-    if (i < a.nl && (int)blockIdx.x >= a.lay[i].wg0) li = i;
+__global__ __launch_bounds__(256) void gemv_finish_lanes_kernel(QDEC_BOUNDS_PARAMS, FinishArgs a) {
+  (void)nl_;
+  const int li = QDEC_LAYER_OF((int)blockIdx.x);
   const int64_t m = a.lay[li].m;
-  const int P = a.lay[li].Bo >= 128 ? a.lay[li].Bo >> 7 : 1;   // workgroup-uniform
+  const int Bo = a.lay[li].Bo, wg0 = a.lay[li].wg0, nsl = a.lay[li].nslices;
+  const int64_t sstride = a.lay[li].slice_stride;
+  const float* zl = a.lay[li].z;
+  const uint32_t* sg = a.lay[li].sign_out;
+  const float mult = a.lay[li].mult;
+  uint16_t* yl = a.lay[li].y;
+  // the layer's fields in one round of scalar loads
+  asm volatile("" ::"s"(m), "s"(Bo), "s"(wg0), "s"(nsl), "s"(sstride), "s"(zl), "s"(sg), "s"(mult), "s"(yl));
+  const int P = Bo >= 128 ? Bo >> 7 : 1;           // workgroup-uniform, a power of two
+  const int lp = 31 - __builtin_clz((unsigned)P);
   const int wpc = (int)((m + 255) >> 8);            // workgroups per column
-  const int lw = (int)blockIdx.x - a.lay[li].wg0;
+  const int lw = (int)blockIdx.x - wg0;
   const int c = lw / wpc;
-  const int64_t g = (int64_t)(lw % wpc) * 256 + threadIdx.x;
+  const int64_t g = (int64_t)(lw - c * wpc) * 256 + threadIdx.x;
   const int lane = threadIdx.x & 63;
   const int Rb = 128 * P;
-  const int t = (int)(g % Rb);
-  const int64_t row = (g / Rb) * Rb + (int64_t)(t % P) * 128 + t / P;
+  const int t = (int)(g & (Rb - 1));
+  const int64_t row = (g & ~(int64_t)(Rb - 1)) + (int64_t)(t & (P - 1)) * 128 + (t >> lp);
   const bool live = g < m;
-  const int nsl = a.lay[li].nslices;
-  const int64_t sstride = a.lay[li].slice_stride;
-  const float* zc = a.lay[li].z + (int64_t)c * m + row;
+  const float* zc = zl + (int64_t)c * m + row;
   // the sign word first: issued with the slices, not after the butterflies
-  const uint32_t* sg = a.lay[li].sign_out;
   const uint32_t sgw = live && sg ? sg[row >> 5] : 0u;
   float acc = 0.f;
   for (int s0 = 0; s0 < nsl; s0 += 16) {
@@ -733,8 +743,8 @@ __global__ __launch_bounds__(256) void gemv_finish_lanes_kernel(FinishArgs a) {
   if (P > 16) lane_butterfly<16>(acc, lane);
   if (live) {
     const bool neg = (sgw >> (row & 31)) & 1u;
-    const float v = acc * a.lay[li].mult;
-    a.lay[li].y[(int64_t)c * m + row] = f2h_bits(neg ? -v : v);
+    const float v = acc * mult;
+    yl[(int64_t)c * m + row] = f2h_bits(neg ? -v : v);
   }
 }
 
@@ -751,7 +761,8 @@ hipError_t launch_gemv_finish(const FinishArgs& a, hipStream_t stream) {
       grid += (unsigned)(((b.lay[l].m + 255) >> 8) * b.lay[l].b);
     }
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(gemv_finish_lanes_kernel, dim3(grid), dim3(256), 0, stream, b);
+    hipLaunchKernelGGL(gemv_finish_lanes_kernel, dim3(grid), dim3(256), 0, stream, QDEC_BOUNDS_ARGS(finish_bounds(b)),
+                       b);
     return hipGetLastError();
   }
   unsigned grid = 0;

@@ -72,6 +72,21 @@ struct FinishLayer {
   float mult;
   int wg0;                 // first workgroup of this layer: (m / rows_wg) x b of them
 };
+// The layer bounds of a grouped launch, passed as the kernel's first eight
+// arguments: the build preloads them into SGPRs at wave launch (kernarg
+// preloading), so a workgroup finds its layer without a memory round trip
+// and reads that layer's fields in one.  w[0] = the layer count, w[i] =
+// the first workgroup of layer i (INT_MAX for i >= the count).
+struct LayerBounds {
+  int w[GEMV_GROUP_MAX];
+};
+#define QDEC_BOUNDS_PARAMS int nl_, int w1_, int w2_, int w3_, int w4_, int w5_, int w6_, int w7_
+#define QDEC_BOUNDS_ARGS(b) (b).w[0], (b).w[1], (b).w[2], (b).w[3], (b).w[4], (b).w[5], (b).w[6], (b).w[7]
+// the layer of workgroup bx: the count of layers 1 .. 7 starting at or below it
+#define QDEC_LAYER_OF(bx)                                                                        \
+  ((int)((bx) >= w1_) + (int)((bx) >= w2_) + (int)((bx) >= w3_) + (int)((bx) >= w4_) +           \
+   (int)((bx) >= w5_) + (int)((bx) >= w6_) + (int)((bx) >= w7_))
+
 struct FinishArgs {
   int nl;
   FinishLayer lay[GEMV_GROUP_MAX];
