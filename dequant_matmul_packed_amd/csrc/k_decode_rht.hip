@@ -242,6 +242,16 @@ __global__ __launch_bounds__(256) void rht_kernel(RhtArgs a) {
   }
 }
 
+// The RHT arguments as plain leading kernel arguments (13 dwords): the
+// build preloads them into SGPRs at wave launch, so a workgroup issues its
+// loads without a round trip to the argument segment.  Element counts stay
+// below 2^30 (the boundary limits rows x n x 4 bytes below 2^32).
+#define QDEC_RHT_PARAMS                                                                          \
+  const void *ain, void *aout, const uint32_t *asg, int n32, int blk, int mode, int out_f32, int nsum, \
+      int sum_stride, float mult
+#define QDEC_RHT_ARGS(a)                                                                         \
+  (a).in, (a).out, (a).signs, (int)(a).n, (a).block, (a).mode, (a).out_f32, (a).nsum, (int)(a).sum_stride, (a).mult
+
 // Blocks of 2048 J values (J = 1, 2, 4): the chunks, loads and signs of
 // rht_kernel, but one barrier.  Index 8 (tid + 256 j) + e: bits 0-2 (e) are
 // butterflies in registers, bits 3-8 (lane bits 0-5) butterflies between
@@ -254,20 +264,21 @@ __global__ __launch_bounds__(256) void rht_kernel(RhtArgs a) {
 // kernels give the same bits.  A workgroup reads its whole block before it
 // writes: in place is safe.
 template <bool IN_F32, int J>
-__global__ __launch_bounds__(256) void rht_lanes_kernel(RhtArgs a) {
+__global__ __launch_bounds__(256) void rht_lanes_kernel(QDEC_RHT_PARAMS) {
   extern __shared__ __align__(16) float buf[];
   constexpr int SU = IN_F32 ? (J >= 4 ? 1 : 4 / J) : 1;   // fp32 slices per round
   constexpr int K = 8 * J;                                 // values per thread
   const int tid = threadIdx.x, lane = tid & 63;
   const int B = 2048 * J;
-  const int64_t nblk = a.n / B;
-  const int64_t row = blockIdx.x / nblk;
-  const int64_t c0 = (blockIdx.x % nblk) * B;
-  const int64_t off = row * a.n + c0;
-  const bool out_signs = a.mode == 1;
+  (void)blk;
+  const int nblk = n32 / B;
+  const int row = (int)blockIdx.x / nblk;
+  const int c0 = ((int)blockIdx.x - row * nblk) * B;
+  const int64_t off = (int64_t)row * n32 + c0;
+  const bool out_signs = mode == 1;
   // sign words: on the input side those of the thread's chunks (8 tid +
   // 2048 j), on the output side those of its outputs (tid + 256 k)
-  const auto srs = make_rsrc(a.signs, a.signs ? (uint32_t)(((a.n + 31) >> 5) * 4) : 0u);
+  const auto srs = make_rsrc(asg, asg ? (uint32_t)(((n32 + 31) >> 5) * 4) : 0u);
   uint32_t sw[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
@@ -280,17 +291,17 @@ __global__ __launch_bounds__(256) void rht_lanes_kernel(RhtArgs a) {
     for (int j = 0; j < J; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
-    const float* base = (const float*)a.in + off;
-    const auto irs = make_rsrc(base, (uint32_t)(((a.nsum - 1) * a.sum_stride + B) * 4));
-    for (int s0 = 0; s0 < a.nsum; s0 += SU) {
+    const float* base = (const float*)ain + off;
+    const auto irs = make_rsrc(base, (uint32_t)(((nsum - 1) * (int64_t)sum_stride + B) * 4));
+    for (int s0 = 0; s0 < nsum; s0 += SU) {
       uint4 p[SU][J][2];
 #pragma unroll
       for (int su = 0; su < SU; ++su)
 #pragma unroll
         for (int j = 0; j < J; ++j) {
           const int ch = tid + 256 * j;
-          const bool ok = s0 + su < a.nsum;
-          const uint32_t o = (uint32_t)(((s0 + su) * a.sum_stride + 8 * ch) * 4);
+          const bool ok = s0 + su < nsum;
+          const uint32_t o = (uint32_t)(((int64_t)(s0 + su) * sum_stride + 8 * ch) * 4);
           p[su][j][0] = buf_load_u4(irs, ok ? o : BUF_OFF);
           p[su][j][1] = buf_load_u4(irs, ok ? o + 16u : BUF_OFF);
         }
@@ -305,7 +316,7 @@ __global__ __launch_bounds__(256) void rht_lanes_kernel(RhtArgs a) {
         }
     }
   } else {
-    const auto irs = make_rsrc((const uint16_t*)a.in + off, (uint32_t)B * 2u);
+    const auto irs = make_rsrc((const uint16_t*)ain + off, (uint32_t)B * 2u);
     uint4 p[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) p[j] = buf_load_u4(irs, (uint32_t)(tid + 256 * j) * 16u);
@@ -364,10 +375,10 @@ __global__ __launch_bounds__(256) void rht_lanes_kernel(RhtArgs a) {
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int64_t i = c0 + tid + 256 * k;
-    float o = w[k] * a.mult;
+    float o = w[k] * mult;
     if (out_signs && ((sw[k] >> (i & 31)) & 1u)) o = -o;
-    if (a.out_f32) ((float*)a.out)[row * a.n + i] = o;
-    else ((uint16_t*)a.out)[row * a.n + i] = f2h_bits(o);
+    if (out_f32) ((float*)aout)[(int64_t)row * n32 + i] = o;
+    else ((uint16_t*)aout)[(int64_t)row * n32 + i] = f2h_bits(o);
   }
 }
 
@@ -378,19 +389,21 @@ __global__ __launch_bounds__(256) void rht_lanes_kernel(RhtArgs a) {
 // workgroup reads the whole block, forms its own +/- combination and runs a
 // Bs-point transform.  Chunks of 8 values as in rht_kernel, J per thread.
 template <int S, int J>
-__global__ __launch_bounds__(256) void rht_split_kernel(RhtArgs a) {
+__global__ __launch_bounds__(256) void rht_split_kernel(QDEC_RHT_PARAMS) {
   extern __shared__ __align__(16) float buf[];
   const int tid = threadIdx.x;
-  const int B = a.block, Bs = B / S;
-  const int64_t nblk = a.n / B;
+  (void)nsum;
+  (void)sum_stride;
+  const int B = blk, Bs = B / S;
+  const int nblk = n32 / B;
   const int jpart = (int)(blockIdx.x % S);
-  const int64_t rb = blockIdx.x / S;
-  const int64_t row = rb / nblk;
-  const int64_t c0 = (rb % nblk) * B;
-  const int64_t off = row * a.n + c0;
+  const int rb = (int)(blockIdx.x / S);
+  const int row = rb / nblk;
+  const int c0 = (rb - row * nblk) * B;
+  const int64_t off = (int64_t)row * n32 + c0;
   const int nch = Bs >> 3;
-  const auto srs = make_rsrc(a.signs, a.signs ? (uint32_t)(((a.n + 31) >> 5) * 4) : 0u);
-  const auto irs = make_rsrc((const uint16_t*)a.in + off, (uint32_t)B * 2u);
+  const auto srs = make_rsrc(asg, asg ? (uint32_t)(((n32 + 31) >> 5) * 4) : 0u);
+  const auto irs = make_rsrc((const uint16_t*)ain + off, (uint32_t)B * 2u);
   uint4 p[S][J];
   uint32_t sw[S][J];
 #pragma unroll
@@ -400,7 +413,7 @@ __global__ __launch_bounds__(256) void rht_split_kernel(RhtArgs a) {
       const int ch = tid + 256 * j;
       const bool ok = ch < nch;
       p[s][j] = buf_load_u4(irs, ok ? (uint32_t)(s * Bs + 8 * ch) * 2u : BUF_OFF);
-      sw[s][j] = buf_load_u32(srs, ok && a.mode == 0 ? (uint32_t)(((c0 + s * Bs + 8 * ch) >> 5) * 4) : BUF_OFF);
+      sw[s][j] = buf_load_u32(srs, ok && mode == 0 ? (uint32_t)(((c0 + s * Bs + 8 * ch) >> 5) * 4) : BUF_OFF);
     }
 #pragma unroll
   for (int j = 0; j < J; ++j) {
@@ -429,30 +442,30 @@ __global__ __launch_bounds__(256) void rht_split_kernel(RhtArgs a) {
   __syncthreads();
   fwht_bits(buf, Bs, 3, 31 - __builtin_clz((unsigned)Bs), tid, 256);
   const int64_t o0 = off + (int64_t)jpart * Bs;
-  const auto ors = make_rsrc(a.signs, a.signs ? (uint32_t)(((a.n + 31) >> 5) * 4) : 0u);
+  const auto ors = make_rsrc(asg, asg ? (uint32_t)(((n32 + 31) >> 5) * 4) : 0u);
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int ch = tid + 256 * j;
     if (ch < nch) {
-      const uint32_t sg = a.mode == 1 ? buf_load_u32(ors, (uint32_t)(((c0 + jpart * Bs + 8 * ch) >> 5) * 4)) >>
+      const uint32_t sg = mode == 1 ? buf_load_u32(ors, (uint32_t)(((c0 + jpart * Bs + 8 * ch) >> 5) * 4)) >>
                                             ((c0 + jpart * Bs + 8 * ch) & 31)
                                       : 0u;
       float o[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        o[e] = buf[pad_index(8 * ch + e)] * a.mult;
+        o[e] = buf[pad_index(8 * ch + e)] * mult;
         if ((sg >> e) & 1u) o[e] = -o[e];
       }
       const int64_t e0 = o0 + 8 * (int64_t)ch;
-      if (a.out_f32) {
-        float* dst = (float*)a.out + e0;
+      if (out_f32) {
+        float* dst = (float*)aout + e0;
         *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
         *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
       } else {
         uint32_t r[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) r[e] = f2h_bits(o[2 * e]) | ((uint32_t)f2h_bits(o[2 * e + 1]) << 16);
-        *reinterpret_cast<uint4*>((uint16_t*)a.out + e0) = make_uint4(r[0], r[1], r[2], r[3]);
+        *reinterpret_cast<uint4*>((uint16_t*)aout + e0) = make_uint4(r[0], r[1], r[2], r[3]);
       }
     }
   }
@@ -469,7 +482,7 @@ static hipError_t launch_rht_split(const RhtArgs& a, hipStream_t stream) {
     static LdsLimit have;                                                                         \
     const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&rht_split_kernel<S, JJ>), lds, &have); \
     if (e != hipSuccess) return e;                                                                  \
-    hipLaunchKernelGGL((rht_split_kernel<S, JJ>), dim3(grid), dim3(256), lds, stream, a);           \
+    hipLaunchKernelGGL((rht_split_kernel<S, JJ>), dim3(grid), dim3(256), lds, stream, QDEC_RHT_ARGS(a)); \
     return hipGetLastError();                                                                       \
   }
   if (nch <= 256) QDEC_SPLIT_J(1)
@@ -496,7 +509,7 @@ static hipError_t launch_rht_lanes(const RhtArgs& a, hipStream_t stream) {
   const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&rht_lanes_kernel<IN_F32, J>), lds, &have);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((rht_lanes_kernel<IN_F32, J>), dim3((unsigned)(a.rows * (a.n / a.block))), dim3(256), lds,
-                     stream, a);
+                     stream, QDEC_RHT_ARGS(a));
   return hipGetLastError();
 }
 

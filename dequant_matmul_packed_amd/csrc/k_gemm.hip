@@ -71,7 +71,17 @@ __host__ __device__ inline size_t gemm_lds_bytes(int Q) {
 // 16 waves per CU; the pure lookup's 128 KiB table leaves room for one
 // 8-wave workgroup, so it may use twice as many.
 template <int CODE, int KV, int COPIES, int KSUB, int NBT>
-__global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void gemm_kernel(GemmArgs a) {
+// The hot scalar arguments lead (16 dwords, preloaded into SGPRs at wave
+// launch: the table fill and the first code loads need no round trip to
+// the argument segment); the NUQ group scales stay in the struct.
+#define QDEC_GEMM_PARAMS                                                                            \
+  const uint32_t *codes_, const uint32_t *lut_, const uint16_t *xr_, float *z_, int m_, int n_, int Q_, \
+      int qshift_, int b_, int ksplit_, int mz_, int row0_
+#define QDEC_GEMM_ARGS(a)                                                                        \
+  (a).L.codes, (a).L.lut, (a).xr, (a).z, (int)(a).L.m, (int)(a).L.n, (a).L.Q, (a).L.qshift, (a).b, (a).ksplit, \
+      (int)(a).mz, (int)(a).row0
+__global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void gemm_kernel(QDEC_GEMM_PARAMS,
+                                                                                         GemmArgs a) {
   static_assert(NBT == 16 || NBT == 64, "batch tile of 16 or 64 columns");
   constexpr int GEMM_THREADS = GEMM_SUB_THREADS * KSUB;
   constexpr int NB4 = NBT / 16;                      // 16-column MFMA blocks
@@ -86,10 +96,10 @@ __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void 
   const int wv = wvall % GEMM_WAVES;                 // wave within its 8-wave group
   const int stid = tid % GEMM_SUB_THREADS;           // thread within its group
   const int wave = wv & 3;                           // wave within its panel
-  char* Bs = reinterpret_cast<char*>(smem) + gemm_table_bytes<CODE, KV, COPIES>(a.L.Q) + ksub * 2 * (NBT * 128);
+  char* Bs = reinterpret_cast<char*>(smem) + gemm_table_bytes<CODE, KV, COPIES>(Q_) + ksub * 2 * (NBT * 128);
   const int q = lane & 7, t = lane >> 3;           // tile t of the wave, lane q in it
   const int tr = t & 1, tc = t >> 1;                 // tile row / column within the step
-  const int64_t m = a.L.m, n = a.L.n;
+  const int64_t m = (int64_t)m_, n = (int64_t)n_;
   const int npanels = (int)(m / 128);
   const int ngroups = (npanels + GEMM_PANELS - 1) / GEMM_PANELS;
   const int panel = (blockIdx.x % ngroups) * GEMM_PANELS + (wv >> 2);
@@ -102,18 +112,18 @@ __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void 
   // with KSUB = 2 each half takes `steps` of them, also a multiple of 4,
   // the first half from s0 and the second from s0 + steps (steps past the
   // split's end read zeros)
-  const int per = (((niter + a.ksplit - 1) / a.ksplit) + 3) & ~3;
+  const int per = (((niter + ksplit_ - 1) / ksplit_) + 3) & ~3;
   const int sp0 = split * per;
   const int sp1 = (sp0 + per) < niter ? (sp0 + per) : niter;
   const int steps = sp0 < sp1 ? ((((sp1 - sp0) + KSUB - 1) / KSUB) + 3) & ~3 : 0;   // workgroup-uniform
   const int it0 = sp0 + ksub * steps;                // this half's first step
   const int it1 = (it0 + steps) < sp1 ? (it0 + steps) : sp1;   // its live end (<= it0: none live)
 
-  if constexpr (CODE == HYB) fill_signed_table<COPIES>(tab, a.L.lut, a.L.Q, tid, GEMM_THREADS);
-  if constexpr (CODE == HYB1) fill_signed_table<COPIES, 0x8000u>(tab, a.L.lut, a.L.Q, tid, GEMM_THREADS);
-  if constexpr (CODE == LUT) fill_plain_table<1>(tab, a.L.lut, 1 << 15, tid, GEMM_THREADS);
-  if constexpr (CODE == VQ) fill_plain_table<COPIES>(tab, a.L.lut, 1 << KV, tid, GEMM_THREADS);
-  if constexpr (CODE == NUQ) fill_plain_table<1>(tab, a.L.lut, 1 << KV, tid, GEMM_THREADS);
+  if constexpr (CODE == HYB) fill_signed_table<COPIES>(tab, lut_, Q_, tid, GEMM_THREADS);
+  if constexpr (CODE == HYB1) fill_signed_table<COPIES, 0x8000u>(tab, lut_, Q_, tid, GEMM_THREADS);
+  if constexpr (CODE == LUT) fill_plain_table<1>(tab, lut_, 1 << 15, tid, GEMM_THREADS);
+  if constexpr (CODE == VQ) fill_plain_table<COPIES>(tab, lut_, 1 << KV, tid, GEMM_THREADS);
+  if constexpr (CODE == NUQ) fill_plain_table<1>(tab, lut_, 1 << KV, tid, GEMM_THREADS);
   const uint32_t* tabc = tab + (lane & (COPIES - 1));
 
   // Every global load goes through a buffer resource and is issued
@@ -127,7 +137,7 @@ __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void 
   // panel; a panel's tile column is 8 tiles of TILE_WORDS words, and lane q
   // reads NW words from word lane_word(q) of its tile.
   constexpr uint32_t TB = 4u * G::TILE_WORDS;       // bytes per tile
-  const auto crs = make_rsrc(a.L.codes + (int64_t)(panel_ok ? panel : 0) * ntc * (8 * G::TILE_WORDS),
+  const auto crs = make_rsrc(codes_ + (int64_t)(panel_ok ? panel : 0) * ntc * (8 * G::TILE_WORDS),
                              panel_ok ? (uint32_t)ntc * (8u * TB) : 0u);
   const int itc = (ntc - tc + 3) >> 2 < it1 ? (ntc - tc + 3) >> 2 : it1;   // 4 it + tc < ntc
   const uint32_t cbase = (uint32_t)tc * (8u * TB) + (uint32_t)(2 * wave + tr) * TB + 4u * G::lane_word(q);
@@ -135,8 +145,8 @@ __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void 
   // group spans gpt tile columns
   const int gstride = CODE == NUQ ? (int)(n / a.L.group) : 0;
   const int gpt = CODE == NUQ ? a.L.group >> 4 : 1;
-  const int grow0 = (int)a.row0 + panel * 128 + (2 * wave + tr) * 16 + 2 * q;
-  const auto grs = make_rsrc(a.L.gscale, CODE == NUQ ? (uint32_t)(a.mz * gstride * 2) : 0u);
+  const int grow0 = (int)(int64_t)row0_ + panel * 128 + (2 * wave + tr) * 16 + 2 * q;
+  const auto grs = make_rsrc(a.L.gscale, CODE == NUQ ? (uint32_t)((int64_t)mz_ * gstride * 2) : 0u);
   auto load_codes = [&](int it, uint32_t* w) {
     const bool ok = it < itc;
     buf_load_words<NW>(crs, ok ? cbase + (uint32_t)it * (32u * TB) : BUF_OFF, w);
@@ -150,11 +160,11 @@ __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void 
   // chunk ch of step it is column 64 it + 8 ch.  A 16-row tile has 128
   // chunks: the group's waves 2 .. 7 stage nothing.
   const bool xmine = stid < NBT * 8;                 // wave-uniform
-  const auto xrs = make_rsrc(a.xr, (uint32_t)(a.b * n * 2));
+  const auto xrs = make_rsrc(xr_, (uint32_t)(b_ * n * 2));
   const int xrow = n0 + (stid >> 3), xch = stid & 7;
   const int xlim = (int)((n - xch * 8 + 63) >> 6);
-  const int itx = (xmine && xrow < a.b) ? (xlim < it1 ? xlim : it1) : 0;
-  const uint32_t xbase = (uint32_t)(((int64_t)(xrow < a.b ? xrow : 0) * n + xch * 8) * 2);
+  const int itx = (xmine && xrow < b_) ? (xlim < it1 ? xlim : it1) : 0;
+  const uint32_t xbase = (uint32_t)(((int64_t)(xrow < b_ ? xrow : 0) * n + xch * 8) * 2);
   auto load_x = [&](int it, uint4& xv) {
     xv = buf_load_u4(xrs, it < itx ? xbase + (uint32_t)it * 128u : BUF_OFF);
   };
@@ -184,7 +194,7 @@ __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void 
       gs[1] = h2f((uint16_t)wc[NW + 1]);
     }
     uint32_t out[16];
-    lane_decode_exact<CODE, KV, COPIES>(w, tabc, a.L.qshift, gs, out);
+    lane_decode_exact<CODE, KV, COPIES>(w, tabc, qshift_, gs, out);
     if (it * 4 + 3 >= ntc || it >= it1) {             // wave-uniform: the ragged or padding step
       const bool live = it < it1 && it * 4 + tc < ntc;
 #pragma unroll
@@ -279,12 +289,12 @@ __global__ __launch_bounds__(GEMM_SUB_THREADS * KSUB, CODE == LUT ? 2 : 4) void 
         for (int e = 0; e < 4; ++e) acc[ra][nb][e] += red[((ra * NB4 + nb) * 4 + e) * 64];
   }
   if (!panel_ok) return;
-  float* zs = a.z + (int64_t)split * a.b * a.mz;
+  float* zs = z_ + (int64_t)split * b_ * (int64_t)mz_;
 #pragma unroll
   for (int nb = 0; nb < NB4; ++nb) {
     const int bb = n0 + nb * 16 + (lane & 15);
-    if (bb >= a.b) continue;
-    float* zrow = zs + (int64_t)bb * a.mz + a.row0 + (int64_t)panel * 128 + 32 * wave;
+    if (bb >= b_) continue;
+    float* zrow = zs + (int64_t)bb * (int64_t)mz_ + (int64_t)row0_ + (int64_t)panel * 128 + 32 * wave;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * (lane >> 4) + e;
@@ -304,7 +314,7 @@ static hipError_t launch_gemm_k(const GemmArgs& a, hipStream_t stream) {
   const int64_t ngroups = (a.L.m / 128 + GEMM_PANELS - 1) / GEMM_PANELS;
   dim3 grid((unsigned)(ngroups * a.ksplit), (unsigned)((a.b + NBT - 1) / NBT));
   hipLaunchKernelGGL((gemm_kernel<CODE, KV, COPIES, KSUB, NBT>), grid, dim3(GEMM_SUB_THREADS * KSUB), lds, stream,
-                     a);
+                     QDEC_GEMM_ARGS(a), a);
   return hipGetLastError();
 }
 // built: 64-column tiles with one or two K halves, 16-column tiles with one
