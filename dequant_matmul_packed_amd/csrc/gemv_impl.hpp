@@ -107,8 +107,16 @@ __host__ __device__ inline size_t gemv_lds_bytes(int Q, int Kc, int U) {
 // first row part (width KV, codes a.L.codes, a.L.m rows), the others the
 // second (width KVB, a.codes_b, a.m_b rows starting at row a.row0_b); the
 // part is uniform per workgroup, and the tile loop is built for each width.
+// The hot scalar arguments lead (14 dwords, preloaded into SGPRs at wave
+// launch, so the table, activation and code loads need no round trip to the
+// argument segment); the rest stay in the struct.
+#define QDEC_GEMV_PARAMS                                                                              \
+  const uint32_t *lut_, const uint32_t *codes_, const uint16_t *x_, const uint32_t *sgin_, int n_, int m_, \
+      int Kc_, int Q_, int hin_, int grida_
+#define QDEC_GEMV_ARGS(a)                                                                             \
+  (a).L.lut, (a).L.codes, (a).x, (a).L.sign_in, (int)(a).L.n, (int)(a).L.m, (a).Kc, (a).L.Q, (a).L.had_in, (a).grid_a
 template <int CODE, int KV, int NB, int PF, bool SL, bool XR, int KVB = 0>
-__global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(QDEC_GEMV_PARAMS, GemvArgs a) {
   using G = LaneGeom<CODE, KV>;
   using GB = LaneGeom<CODE, KVB ? KVB : KV>;
   constexpr int V = G::V;
@@ -119,15 +127,16 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar math
-  const bool second = KVB != 0 && (int)blockIdx.x >= a.grid_a;
-  const int bid = second ? (int)blockIdx.x - a.grid_a : (int)blockIdx.x;
-  const int64_t m = second ? a.m_b : a.L.m, n = a.L.n;
+  const bool second = KVB != 0 && (int)blockIdx.x >= grida_;
+  const int bid = second ? (int)blockIdx.x - grida_ : (int)blockIdx.x;
+  // 32-bit index math (m, n <= 2^20): no 64-bit division in the prologue
+  const int m = second ? (int)a.m_b : m_, n = n_;
   const int64_t row0 = second ? a.row0_b : a.row0;
-  const int npanels = (int)(m / 128);
+  const int npanels = m >> 7;
   const int panel = bid % npanels;
   const int chunk = bid / npanels;
-  const int Kc = a.Kc;
-  const int64_t c0 = (int64_t)chunk * Kc;
+  const int Kc = Kc_;
+  const int c0 = chunk * Kc;
   const int kcols = (int)((n - c0) < Kc ? (n - c0) : Kc);   // multiple of 16
   const int ntc = kcols >> 4;                                  // tile columns in chunk
   const int tpw = (ntc + 3) >> 2;
@@ -136,7 +145,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   tc_count = tc_count < 0 ? 0 : (tc_count > tpw ? tpw : tc_count);
 
   // LDS carve-up
-  const size_t regA_words = gemv_regA_bytes<CODE, KV, NB>(a.L.Q, Kc, a.U) / 4;
+  const size_t regA_words = gemv_regA_bytes<CODE, KV, NB>(Q_, Kc, a.U) / 4;
   uint32_t* regA = smem;
   float* fA = reinterpret_cast<float*>(smem);
   uint32_t* xh = smem + regA_words;                 // [NB][Kc/2] fp16 pairs
@@ -149,10 +158,10 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   // RHT's wait on them does not also wait on the (slower) code loads --
   // vector-memory counters drain in issue order.  With b > 1, x' comes
   // precomputed (args.xr) and step 2 loads the chunk's slice of it instead.
-  const int Bi = a.L.had_in;
+  const int Bi = hin_;
   const int arows = Kc < Bi ? Bi / Kc : 1;
-  const int64_t rbase = Kc < Bi ? (c0 / Bi) * Bi : c0;
-  const int jhi = Kc < Bi ? (int)((c0 - rbase) / Kc) : 0;
+  const int rbase = Kc < Bi ? (c0 / Bi) * Bi : c0;
+  const int jhi = Kc < Bi ? (c0 - rbase) / Kc : 0;
   const int CG = kcols >> 3;                       // groups of 8 columns
   const int RG = CG >= GEMV_THREADS ? 1 : GEMV_THREADS / CG;
   constexpr int MAXR = XR ? 1 : (SL ? 2 : 8);   // arows / RG = B_in / 2048 (B_in <= 16384)
@@ -161,11 +170,11 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   // the lookup table's words, requested up front too: word tid + 256 i
   // (HYB: 2^Q <= 256 TW words; VQ 2^(2k) <= 256; NUQ 2^k <= 16)
   constexpr int TW = (CODE == HYB || CODE == HYB1) ? (SL ? 2 : 8) : 1;
-  const int nlut = (CODE == HYB || CODE == HYB1) ? (1 << a.L.Q)
+  const int nlut = (CODE == HYB || CODE == HYB1) ? (1 << Q_)
                  : (CODE == VQ || CODE == NUQ) ? (1 << KV) : 0;   // LUT: filled below
   uint32_t lw[TW];
   {
-    const auto lrs = make_rsrc(a.L.lut, (uint32_t)nlut * 4u);
+    const auto lrs = make_rsrc(lut_, (uint32_t)nlut * 4u);
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
       const int e = tid + i * GEMV_THREADS;
@@ -177,8 +186,8 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
     // the layer has no input signs (its loads then read zero: all signs +1).
     // xsb[r] is the whole sign word: the group's 8 signs start at bit
     // (cg * 8) & 31, as rbase and Kc are multiples of 64.
-    const auto xrs = make_rsrc(a.x, (uint32_t)(n * 2));
-    const auto srs = make_rsrc(a.L.sign_in, a.L.sign_in ? (uint32_t)(((n + 31) >> 5) * 4) : 0u);
+    const auto xrs = make_rsrc(x_, (uint32_t)(n * 2));
+    const auto srs = make_rsrc(sgin_, sgin_ ? (uint32_t)(((n + 31) >> 5) * 4) : 0u);
     const int cg = tid % CG, rg = tid / CG;
 #pragma unroll
     for (int r = 0; r < MAXR; ++r) {
@@ -201,7 +210,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
   const uint32_t TWS = second ? (uint32_t)GB::TILE_WORDS : (uint32_t)G::TILE_WORDS;
   const uint32_t TCB = 8u * 4u * TWS;                 // bytes per tile column
   const int64_t tiles_row = n >> 4;
-  const uint32_t* pchunk = (second ? a.codes_b : a.L.codes) + ((int64_t)panel * tiles_row + (c0 >> 4)) * (8 * TWS);
+  const uint32_t* pchunk = (second ? a.codes_b : codes_) + ((int64_t)panel * tiles_row + (c0 >> 4)) * (8 * TWS);
   const auto crs = make_rsrc(pchunk, (uint32_t)ntc * TCB);
   const uint32_t lane_off = (uint32_t)(lane >> 3) * (4u * TWS) +
                             4u * (second ? GB::lane_word(lane & 7) : G::lane_word(lane & 7));
@@ -212,14 +221,14 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
 #pragma unroll
   for (int j = 0; j < PF; ++j) buf_load_words<NW>(crs, code_off(j), buf[j]);
   // NUQ: the fp16 group scales of the lane's two rows ride in the same ring
-  const int64_t gstride = CODE == NUQ ? n / a.L.group : 0;
+  const int gstride = CODE == NUQ ? n / a.L.group : 0;
   const int64_t grow0 = row0 + (int64_t)panel * 128 + (lane >> 3) * 16 + 2 * (lane & 7);
   const auto grs = make_rsrc(a.L.gscale, CODE == NUQ ? (uint32_t)(a.mz * gstride * 2) : 0u);
   uint32_t gsr[PF][2];
   auto gs_load = [&](int j, uint32_t* g) {
     if constexpr (CODE == NUQ) {
       const bool ok = j < tc_count;
-      const int64_t gcol = (c0 + (int64_t)(tc_begin + j) * 16) / a.L.group;
+      const int gcol = (c0 + (tc_begin + j) * 16) / a.L.group;
       g[0] = buf_load_u16(grs, ok ? (uint32_t)((grow0 * gstride + gcol) * 2) : BUF_OFF);
       g[1] = buf_load_u16(grs, ok ? (uint32_t)(((grow0 + 1) * gstride + gcol) * 2) : BUF_OFF);
     } else {
@@ -263,7 +272,7 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_kernel(GemvArgs a) {
       }
     }
     if constexpr (CODE == LUT) {
-      const auto trs = make_rsrc(a.L.lut, (1u << 15) * 4u);
+      const auto trs = make_rsrc(lut_, (1u << 15) * 4u);
       for (int r0 = 0; r0 < (1 << 13); r0 += 8 * GEMV_THREADS) {   // 2^13 chunks of 16 bytes
         uint4 v[8];
 #pragma unroll
@@ -650,7 +659,8 @@ hipError_t launch_gemv_v(const GemvArgs& a, hipStream_t stream) {
       ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_kernel<CODE, KV, NB, PF, SL, XR, KVB>), lds, &have);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((a.L.m / 128 + (KVB ? a.m_b / 128 : 0)) * a.nchunks);
-  hipLaunchKernelGGL((gemv_kernel<CODE, KV, NB, PF, SL, XR, KVB>), dim3(grid), dim3(GEMV_THREADS), lds, stream, a);
+  hipLaunchKernelGGL((gemv_kernel<CODE, KV, NB, PF, SL, XR, KVB>), dim3(grid), dim3(GEMV_THREADS), lds, stream,
+                     QDEC_GEMV_ARGS(a), a);
   return hipGetLastError();
 }
 
