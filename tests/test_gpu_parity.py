@@ -748,6 +748,9 @@ GROUP_CASES = {
     # more units than workgroups (448 panels on 256 workgroups): some
     # workgroups walk two units, each unit's slice rows written once
     "several_units": [(synth.HYB, 28672, 4096, 2, {}), (synth.HYB, 28672, 4096, 2, {})],
+    # the largest group, one code, width and Q: one launch whose eight layers
+    # use every layer bound the kernels take as leading arguments
+    "eight_layers": [(synth.HYB, 128 * (i + 1), 1024 if i % 2 else 2048, 2, {}) for i in range(8)],
 }
 
 
