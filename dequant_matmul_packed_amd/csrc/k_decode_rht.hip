@@ -701,8 +701,8 @@ static hipError_t launch_finish_j(const FinishArgs& a, unsigned grid, size_t lds
 // takes row blk Rb + p 128 + i of block blk (Rb = 128 P rows) with
 // p = t mod P, i = (t mod Rb) / P, so the P rows at one in-panel index sit
 // in P neighbouring lanes and stage h of H_P pairs lanes t and t ^ h (one
-// ds_swizzle each: no LDS buffer, no barrier).  256 threads per workgroup,
-// rows past m idle; each layer's workgroups are ceil(m / 256) per column,
+// ds_swizzle each: no LDS buffer, no barrier).  One wave per workgroup,
+// rows past m idle; each layer's workgroups are ceil(m / 64) per column,
 // column major.  Slices are added in slice order, as above.
 // One butterfly stage between lanes t and t ^ H (H < 32): ds_swizzle in
 // bit-mask mode (offset bit 15 clear: within each 32 lanes, lane j reads
@@ -714,7 +714,10 @@ __device__ __forceinline__ void lane_butterfly(float& v, int lane) {
   v = (lane & H) ? o - v : v + o;
 }
 
-__global__ __launch_bounds__(256) void gemv_finish_lanes_kernel(QDEC_BOUNDS_PARAMS, FinishArgs a) {
+// One wave per workgroup: the slice loads (each wave load spans up to 32
+// cache lines) spread over as many CUs as there are waves.
+constexpr int FIN_LANES_THREADS = 64;
+__global__ __launch_bounds__(FIN_LANES_THREADS) void gemv_finish_lanes_kernel(QDEC_BOUNDS_PARAMS, FinishArgs a) {
   (void)nl_;
   const int li = QDEC_LAYER_OF((int)blockIdx.x);
   const int64_t m = a.lay[li].m;
@@ -728,10 +731,10 @@ __global__ __launch_bounds__(256) void gemv_finish_lanes_kernel(QDEC_BOUNDS_PARA
   asm volatile("" ::"s"(m), "s"(Bo), "s"(wg0), "s"(nsl), "s"(sstride), "s"(zl), "s"(sg), "s"(mult), "s"(yl));
   const int P = Bo >= 128 ? Bo >> 7 : 1;           // workgroup-uniform, a power of two
   const int lp = 31 - __builtin_clz((unsigned)P);
-  const int wpc = (int)((m + 255) >> 8);            // workgroups per column
+  const int wpc = (int)((m + FIN_LANES_THREADS - 1) / FIN_LANES_THREADS);   // workgroups per column
   const int lw = (int)blockIdx.x - wg0;
   const int c = lw / wpc;
-  const int64_t g = (int64_t)(lw - c * wpc) * 256 + threadIdx.x;
+  const int64_t g = (int64_t)(lw - c * wpc) * FIN_LANES_THREADS + threadIdx.x;
   const int lane = threadIdx.x & 63;
   const int Rb = 128 * P;
   const int t = (int)(g & (Rb - 1));
@@ -771,10 +774,11 @@ hipError_t launch_gemv_finish(const FinishArgs& a, hipStream_t stream) {
     unsigned grid = 0;
     for (int l = 0; l < b.nl; ++l) {
       b.lay[l].wg0 = (int)grid;
-      grid += (unsigned)(((b.lay[l].m + 255) >> 8) * b.lay[l].b);
+      grid += (unsigned)(((b.lay[l].m + FIN_LANES_THREADS - 1) / FIN_LANES_THREADS) * b.lay[l].b);
     }
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(gemv_finish_lanes_kernel, dim3(grid), dim3(256), 0, stream, QDEC_BOUNDS_ARGS(finish_bounds(b)),
+    hipLaunchKernelGGL(gemv_finish_lanes_kernel, dim3(grid), dim3(FIN_LANES_THREADS), 0, stream,
+                       QDEC_BOUNDS_ARGS(finish_bounds(b)),
                        b);
     return hipGetLastError();
   }
