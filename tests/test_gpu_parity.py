@@ -144,7 +144,8 @@ def test_decode_tile_bit_exact_full_size(q, dev, wname, spec):
 # RHT
 
 @pytest.mark.parametrize("B,n,rows", [(1, 64, 3), (16, 592, 2), (256, 1024, 5), (4096, 4096, 2),
-                                      (2048, 14336, 1), (8192, 8192, 2), (16384, 16384, 1)])
+                                      (2048, 14336, 1), (8192, 8192, 2), (16384, 16384, 1),
+                                      (8192, 8192, 64), (4096, 4096, 160)])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_rht_matches_oracle(q, dev, B, n, rows, mode):
     import torch
