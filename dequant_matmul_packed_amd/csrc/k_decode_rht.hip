@@ -721,18 +721,26 @@ __global__ __launch_bounds__(FIN_LANES_THREADS) void gemv_finish_lanes_kernel(QD
   (void)nl_;
   const int li = QDEC_LAYER_OF((int)blockIdx.x);
   const int64_t m = a.lay[li].m;
-  const int Bo = a.lay[li].Bo, wg0 = a.lay[li].wg0, nsl = a.lay[li].nslices;
+  const int Bo = a.lay[li].Bo, wg0 = a.lay[li].wg0, nsl = a.lay[li].nslices, ncol = a.lay[li].b;
   const int64_t sstride = a.lay[li].slice_stride;
   const float* zl = a.lay[li].z;
   const uint32_t* sg = a.lay[li].sign_out;
   const float mult = a.lay[li].mult;
   uint16_t* yl = a.lay[li].y;
   // the layer's fields in one round of scalar loads
-  asm volatile("" ::"s"(m), "s"(Bo), "s"(wg0), "s"(nsl), "s"(sstride), "s"(zl), "s"(sg), "s"(mult), "s"(yl));
+  asm volatile("" ::"s"(m), "s"(Bo), "s"(wg0), "s"(nsl), "s"(ncol), "s"(sstride), "s"(zl), "s"(sg), "s"(mult),
+               "s"(yl));
   const int P = Bo >= 128 ? Bo >> 7 : 1;           // workgroup-uniform, a power of two
   const int lp = 31 - __builtin_clz((unsigned)P);
   const int wpc = (int)((m + FIN_LANES_THREADS - 1) / FIN_LANES_THREADS);   // workgroups per column
-  const int lw = (int)blockIdx.x - wg0;
+  // Workgroups are dealt to the 8 XCDs in turn, and one wave holds only
+  // 64 / P consecutive rows of each panel, so the workgroups that share a
+  // cache line of a slice are logical neighbours: the layer's first
+  // 8 floor(nwg / 8) workgroups take their logical index in XCD-major
+  // order, which puts logical neighbours on one XCD and its L2.
+  const int nq = (wpc * ncol) & ~7;
+  int lw = (int)blockIdx.x - wg0;
+  if (lw < nq) lw = (lw & 7) * (nq >> 3) + (lw >> 3);
   const int c = lw / wpc;
   const int64_t g = (int64_t)(lw - c * wpc) * FIN_LANES_THREADS + threadIdx.x;
   const int lane = threadIdx.x & 63;
