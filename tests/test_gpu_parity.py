@@ -386,13 +386,14 @@ def test_gemv_routed_to_mfma_whole(q, dev, code, k, kv_b, m_a, m, n, b):
 @pytest.mark.parametrize("m,had_out", [(1280, 256), (4096, 4096), (8192, 8192), (16384, 16384)])
 def test_gemv_output_blocks(q, dev, m, had_out):
     """Output Hadamard blocks of 256 to 16384 rows (2 to 128 panels per block
-    in the finisher's cross-panel transform), at one and three batch
-    columns, twice on one workspace (bit-identical results)."""
+    in the finisher's cross-panel transform), at one, three and eight batch
+    columns (the finisher's workgroups of several columns in one XCD-major
+    order), twice on one workspace (bit-identical results)."""
     import torch
     n = 256
     host = synth.make_layer(synth.HYB, m, n, 2, had_out=had_out, tag="ob%d" % m)
     lay = q.upload_layer(host, dev)
-    for b in (1, 3):
+    for b in (1, 3, 8):
         _say("gemv output blocks", m, had_out, "b", b)
         x16 = synth.activations("obx%d" % b, b, n)
         ref = oracle.forward(host, x16)
