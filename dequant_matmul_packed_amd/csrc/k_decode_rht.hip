@@ -717,29 +717,19 @@ __device__ __forceinline__ void lane_butterfly(float& v, int lane) {
 // One wave per workgroup: the slice loads (each wave load spans up to 32
 // cache lines) spread over as many CUs as there are waves.
 constexpr int FIN_LANES_THREADS = 64;
-__global__ __launch_bounds__(FIN_LANES_THREADS) void gemv_finish_lanes_kernel(QDEC_BOUNDS_PARAMS, FinishArgs a) {
-  (void)nl_;
-  const int li = QDEC_LAYER_OF((int)blockIdx.x);
-  const int64_t m = a.lay[li].m;
-  const int Bo = a.lay[li].Bo, wg0 = a.lay[li].wg0, nsl = a.lay[li].nslices, ncol = a.lay[li].b;
-  const int64_t sstride = a.lay[li].slice_stride;
-  const float* zl = a.lay[li].z;
-  const uint32_t* sg = a.lay[li].sign_out;
-  const float mult = a.lay[li].mult;
-  uint16_t* yl = a.lay[li].y;
-  // the layer's fields in one round of scalar loads
-  asm volatile("" ::"s"(m), "s"(Bo), "s"(wg0), "s"(nsl), "s"(ncol), "s"(sstride), "s"(zl), "s"(sg), "s"(mult),
-               "s"(yl));
+
+// The work of one lane-finisher workgroup, lw its index within the layer.
+__device__ __forceinline__ void finish_lanes(int lw, const float* zl, uint16_t* yl, const uint32_t* sg, int m,
+                                             int Bo, int nsl, int ncol, int64_t sstride, float mult) {
   const int P = Bo >= 128 ? Bo >> 7 : 1;           // workgroup-uniform, a power of two
   const int lp = 31 - __builtin_clz((unsigned)P);
-  const int wpc = (int)((m + FIN_LANES_THREADS - 1) / FIN_LANES_THREADS);   // workgroups per column
+  const int wpc = (m + FIN_LANES_THREADS - 1) / FIN_LANES_THREADS;   // workgroups per column
   // Workgroups are dealt to the 8 XCDs in turn, and one wave holds only
   // 64 / P consecutive rows of each panel, so the workgroups that share a
   // cache line of a slice are logical neighbours: the layer's first
   // 8 floor(nwg / 8) workgroups take their logical index in XCD-major
   // order, which puts logical neighbours on one XCD and its L2.
   const int nq = (wpc * ncol) & ~7;
-  int lw = (int)blockIdx.x - wg0;
   if (lw < nq) lw = (lw & 7) * (nq >> 3) + (lw >> 3);
   const int c = lw / wpc;
   const int64_t g = (int64_t)(lw - c * wpc) * FIN_LANES_THREADS + threadIdx.x;
@@ -772,6 +762,32 @@ __global__ __launch_bounds__(FIN_LANES_THREADS) void gemv_finish_lanes_kernel(QD
   }
 }
 
+// Several layers: the layer bounds are preloaded, the layer's fields come
+// from the argument struct in one round of scalar loads.
+__global__ __launch_bounds__(FIN_LANES_THREADS) void gemv_finish_lanes_kernel(QDEC_BOUNDS_PARAMS, FinishArgs a) {
+  (void)nl_;
+  const int li = QDEC_LAYER_OF((int)blockIdx.x);
+  const int m = (int)a.lay[li].m;
+  const int Bo = a.lay[li].Bo, wg0 = a.lay[li].wg0, nsl = a.lay[li].nslices, ncol = a.lay[li].b;
+  const int64_t sstride = a.lay[li].slice_stride;
+  const float* zl = a.lay[li].z;
+  const uint32_t* sg = a.lay[li].sign_out;
+  const float mult = a.lay[li].mult;
+  uint16_t* yl = a.lay[li].y;
+  asm volatile("" ::"s"(m), "s"(Bo), "s"(wg0), "s"(nsl), "s"(ncol), "s"(sstride), "s"(zl), "s"(sg), "s"(mult),
+               "s"(yl));
+  finish_lanes((int)blockIdx.x - wg0, zl, yl, sg, m, Bo, nsl, ncol, sstride, mult);
+}
+
+// One layer: every field is a leading scalar argument, all preloaded into
+// SGPRs at wave launch (12 of them), so no argument is loaded from memory.
+__global__ __launch_bounds__(FIN_LANES_THREADS) void gemv_finish_lanes1_kernel(const float* z, uint16_t* y,
+                                                                               const uint32_t* sg, int m, int Bo,
+                                                                               int nsl, int ncol, int sstride,
+                                                                               float mult) {
+  finish_lanes((int)blockIdx.x, z, y, sg, m, Bo, nsl, ncol, sstride, mult);
+}
+
 hipError_t launch_gemv_finish(const FinishArgs& a, hipStream_t stream) {
   // the lane finisher where every block is at most 32 panels
   bool lanes = a.nl > 0;
@@ -785,6 +801,12 @@ hipError_t launch_gemv_finish(const FinishArgs& a, hipStream_t stream) {
       grid += (unsigned)(((b.lay[l].m + FIN_LANES_THREADS - 1) / FIN_LANES_THREADS) * b.lay[l].b);
     }
     if (grid == 0) return hipSuccess;
+    const FinishLayer& f = b.lay[0];
+    if (b.nl == 1 && f.slice_stride <= INT32_MAX) {
+      hipLaunchKernelGGL(gemv_finish_lanes1_kernel, dim3(grid), dim3(FIN_LANES_THREADS), 0, stream, f.z, f.y,
+                         f.sign_out, (int)f.m, f.Bo, f.nslices, f.b, (int)f.slice_stride, f.mult);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL(gemv_finish_lanes_kernel, dim3(grid), dim3(FIN_LANES_THREADS), 0, stream,
                        QDEC_BOUNDS_ARGS(finish_bounds(b)),
                        b);
