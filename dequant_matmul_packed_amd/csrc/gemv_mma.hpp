@@ -114,9 +114,14 @@ __device__ __forceinline__ void mad1_pairs_centred(const uint32_t* w, uint32_t* 
   }
 }
 
-template <int CODE, int KV, int PF>
-__global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(QDEC_BOUNDS_PARAMS, int xs_off_, int red_off_, int scr_off_, int cshift_,
-                                                                 int copies_, MmaArgs a) {
+// The kernel body for layer li of the launch.  X0: a launch of one layer
+// whose x' is the whole row, with the table, x, the input signs, n and Q
+// passed as leading (preloaded) arguments, so that the x and table loads
+// issue before the layer's other fields have been read from memory.
+template <int CODE, int KV, int PF, bool X0>
+__device__ __forceinline__ void gemv_mma_body(int li, const uint32_t* lut_p, const uint16_t* x_p,
+                                              const uint32_t* sgin_p, int n_p, int Q_p, int xs_off_, int red_off_,
+                                              int scr_off_, int cshift_, int copies_, const MmaArgs& a) {
   using G = LaneGeom<CODE, KV>;
   constexpr int NW = G::NW;
   constexpr int CW = CODE == NUQ ? NW + 2 : NW;          // ring words per slot (+ NUQ scales)
@@ -129,24 +134,63 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(QDEC_BOUNDS_PA
   const int rg = wave & 3, ks = wave >> 2;
   const int q = lane & 7, t8 = lane >> 3, tr = t8 & 1, tc = t8 >> 1;
 
+  // x in 8-value chunks: local chunk c = tid + 1024 j of the row or the
+  // range (at most 16384 values: 2 per thread)
+  uint4 xv[2];
+  uint32_t sw[2];
+  auto issue_x = [&](const uint16_t* xg_, const uint32_t* sg_, int n_, int xbase_, int NL_) {
+    const int nch8_ = n_ >> 3;
+    const auto xrs = make_rsrc(xg_, (uint32_t)n_ * 2u);
+    const auto srs = make_rsrc(sg_, sg_ ? (uint32_t)(((n_ + 31) >> 5) * 4) : 0u);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = tid + MMA_THREADS * j;
+      const int gc = (xbase_ >> 3) + c;
+      const bool ok = c < (NL_ >> 3) && gc < nch8_;
+      xv[j] = buf_load_u4(xrs, ok ? (uint32_t)gc * 16u : BUF_OFF);
+      sw[j] = buf_load_u32(srs, ok ? (uint32_t)((8 * gc) >> 5) * 4u : BUF_OFF);
+    }
+  };
+  // HYB: the LUT word of each 16-byte run of the table this thread writes
+  // (run w4 = tid + 1024 k holds 4 copies of signed entry (4 w4) / copies;
+  // K8 = W4 / 1024 <= 8 runs per thread: at most 128 KiB), requested with x.
+  // The host keeps copies * 2^Q >= 8192, so W4 is a multiple of 1024 and
+  // run k's entry is e0 + step k with e0 = 4 tid / copies < step = 4096 /
+  // copies <= 2^Q: its LUT word is e0 + (step k mod 2^Q), and whether it is
+  // a sign-flipped entry (bit Q) does not depend on the thread.  One vector
+  // offset and scalar offsets: no per-run address arithmetic.
+  uint32_t lw[8];
+  auto issue_lut = [&](const uint32_t* lut_, int Q_) {
+    const int nlut_ = CODE == HYB ? (1 << Q_) : 0;
+    const int lc_ = 31 - __builtin_clz((unsigned)copies_);
+    const int step_ = 4096 >> lc_;
+    const auto lrs = make_rsrc(lut_, (uint32_t)nlut_ * 4u);
+    const uint32_t vo = (uint32_t)((tid << 2) >> lc_) * 4u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      lw[k] = __builtin_amdgcn_raw_buffer_load_b32(lrs, vo, (uint32_t)((step_ * k) & (nlut_ - 1)) * 4u, 0);
+  };
+  if constexpr (X0) {
+    issue_x(x_p, sgin_p, n_p, 0, n_p);
+    issue_lut(lut_p, Q_p);
+  }
+
   // ---- this workgroup's layer (workgroup-uniform) ---------------------------
-  (void)nl_;
-  const int li = QDEC_LAYER_OF((int)blockIdx.x);
   const uint32_t* codes = a.lay[li].L.codes;
-  const uint32_t* lut = a.lay[li].L.lut;
+  const uint32_t* lut = X0 ? lut_p : a.lay[li].L.lut;
   const uint16_t* gscale = a.lay[li].L.gscale;
-  const uint32_t* sign_in = a.lay[li].L.sign_in;
+  const uint32_t* sign_in = X0 ? sgin_p : a.lay[li].L.sign_in;
   const int64_t mpart = a.lay[li].L.m;
-  const int n = (int)a.lay[li].L.n;
-  const int qshift = a.lay[li].L.qshift, Q = a.lay[li].L.Q, group = a.lay[li].L.group;
+  const int n = X0 ? n_p : (int)a.lay[li].L.n;
+  const int qshift = a.lay[li].L.qshift, Q = X0 ? Q_p : a.lay[li].L.Q, group = a.lay[li].L.group;
   const int Bi = a.lay[li].L.had_in, Bo = a.lay[li].L.had_out;
-  const uint16_t* xg = a.lay[li].x;
+  const uint16_t* xg = X0 ? x_p : a.lay[li].x;
   float* zl = a.lay[li].z;
   const int64_t sstride = a.lay[li].slice_stride, row0 = a.lay[li].row0;
   const int nr = a.lay[li].nr, KR = a.lay[li].KR;
   const int bl = (int)blockIdx.x - a.lay[li].wg0, nwg = a.lay[li].nwg, units = a.lay[li].units;
 
-  const int xmode = a.lay[li].xmode;
+  const int xmode = X0 ? 0 : a.lay[li].xmode;
   // the layer's fields in one round of scalar loads (the compiler would
   // otherwise issue some only where they are first used, after the first
   // round has returned); the launch's LDS carve-up and table geometry come
@@ -181,44 +225,15 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(QDEC_BOUNDS_PA
   const int NL = xmode == 0 ? n : KR;     // x' values kept (zero past n)
 
   // ---- 0. every global load the set-up needs, and the first PF code steps ----
-  // x in 8-value chunks: local chunk c = tid + 1024 j of the row or the
-  // range (at most 16384 values: 2 per thread)
-  const int nch8 = n >> 3;
-  uint4 xv[2];
-  uint32_t sw[2];
-  {
-    const auto xrs = make_rsrc(xg, (uint32_t)n * 2u);
-    const auto srs = make_rsrc(sign_in, sign_in ? (uint32_t)(((n + 31) >> 5) * 4) : 0u);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = tid + MMA_THREADS * j;
-      const int gc = (xbase >> 3) + c;
-      const bool ok = c < (NL >> 3) && gc < nch8;
-      xv[j] = buf_load_u4(xrs, ok ? (uint32_t)gc * 16u : BUF_OFF);
-      sw[j] = buf_load_u32(srs, ok ? (uint32_t)((8 * gc) >> 5) * 4u : BUF_OFF);
-    }
+  if constexpr (!X0) {
+    issue_x(xg, sign_in, n, xbase, NL);
+    issue_lut(lut, Q);
   }
-  // HYB: the LUT word of each 16-byte run of the table this thread writes
-  // (run w4 = tid + 1024 k holds 4 copies of signed entry (4 w4) / copies;
-  // K8 = W4 / 1024 <= 8 runs per thread: at most 128 KiB), requested with x.
-  // The host keeps copies * 2^Q >= 8192, so W4 is a multiple of 1024 and
-  // run k's entry is e0 + step k with e0 = 4 tid / copies < step = 4096 /
-  // copies <= 2^Q: its LUT word is e0 + (step k mod 2^Q), and whether it is
-  // a sign-flipped entry (bit Q) does not depend on the thread.  One vector
-  // offset and scalar offsets: no per-run address arithmetic.
-  const int nlut = CODE == HYB ? (1 << Q) : 0;
+  const int nch8 = n >> 3;
   const int lc = 31 - __builtin_clz((unsigned)copies_);
   const int W4 = CODE == HYB ? (copies_ << (Q + 1)) >> 2 : 0;
   const int K8 = W4 >> 10;
   const int step = 4096 >> lc;
-  uint32_t lw[8];
-  {
-    const auto lrs = make_rsrc(lut, (uint32_t)nlut * 4u);
-    const uint32_t vo = (uint32_t)((tid << 2) >> lc) * 4u;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      lw[k] = __builtin_amdgcn_raw_buffer_load_b32(lrs, vo, (uint32_t)((step * k) & (nlut - 1)) * 4u, 0);
-  }
   // codes of the whole part through one resource (format sizes below 4 GiB)
   const auto crs = make_rsrc(codes, (uint32_t)((mpart >> 4) * ntc * (int64_t)TB));
   const uint32_t lane_part = (uint32_t)(tc * 8 + 2 * rg + tr) * TB + 4u * G::lane_word(q);
@@ -568,6 +583,24 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(QDEC_BOUNDS_PA
   }
 }
 
+template <int CODE, int KV, int PF>
+__global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(QDEC_BOUNDS_PARAMS, int xs_off_, int red_off_,
+                                                                 int scr_off_, int cshift_, int copies_, MmaArgs a) {
+  (void)nl_;
+  gemv_mma_body<CODE, KV, PF, false>(QDEC_LAYER_OF((int)blockIdx.x), nullptr, nullptr, nullptr, 0, 0, xs_off_,
+                                     red_off_, scr_off_, cshift_, copies_, a);
+}
+
+// One layer whose x' is the whole row: the first loads' pointers and sizes
+// lead the arguments (13 preloaded SGPRs with the LDS carve-up).
+template <int CODE, int KV, int PF>
+__global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma1_kernel(const uint32_t* lut_, const uint16_t* x_,
+                                                                  const uint32_t* sgin_, int n_, int Q_, int xs_off_,
+                                                                  int red_off_, int scr_off_, int cshift_,
+                                                                  int copies_, MmaArgs a) {
+  gemv_mma_body<CODE, KV, PF, true>(0, lut_, x_, sgin_, n_, Q_, xs_off_, red_off_, scr_off_, cshift_, copies_, a);
+}
+
 // PF = min(S, 8): the ring depth divides the steps of a unit (S is 2, 4 or a
 // multiple of 8: KR is 512, 1024 or a multiple of 2048).
 template <int CODE, int KV, int PF>
@@ -575,6 +608,18 @@ hipError_t launch_gemv_mma_p(const MmaArgs& a, unsigned grid, size_t lds, hipStr
   static LdsLimit have;
   const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_mma_kernel<CODE, KV, PF>), lds, &have);
   if (e != hipSuccess) return e;
+  if constexpr (CODE == HYB) {
+    if (a.nl == 1 && a.lay[0].xmode == 0) {
+      static LdsLimit have1;
+      const hipError_t e1 = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_mma1_kernel<CODE, KV, PF>), lds,
+                                               &have1);
+      if (e1 != hipSuccess) return e1;
+      const MmaLayer& l0 = a.lay[0];
+      hipLaunchKernelGGL((gemv_mma1_kernel<CODE, KV, PF>), dim3(grid), dim3(MMA_THREADS), lds, stream, l0.L.lut, l0.x,
+                         l0.L.sign_in, (int)l0.L.n, l0.L.Q, a.xs_off, a.red_off, a.scr_off, a.cshift, a.copies, a);
+      return hipGetLastError();
+    }
+  }
   LayerBounds b;
   b.w[0] = a.nl;
   for (int i = 1; i < GEMV_GROUP_MAX; ++i) b.w[i] = i < a.nl ? a.lay[i].wg0 : INT_MAX;
