@@ -40,7 +40,7 @@ def call_spans(db):
     while i < len(rows):
         nm = short(rows[i][0])
         key = (nm, rows[i][1] // max(rows[i][2], 1), rows[i][3])
-        if nm.startswith("qdec::gemv_mma_kernel") and i + 1 < len(rows) and \
+        if nm.startswith("qdec::gemv_mma") and i + 1 < len(rows) and \
                 short(rows[i + 1][0]).startswith("qdec::gemv_finish"):
             last, n = i + 1, 2
         elif nm.startswith("qdec::rht_split_kernel") and i + 2 < len(rows) and \
