@@ -112,7 +112,7 @@ class Launch:
         self.args = (ctypes.byref(layer.desc()), x.data_ptr(), y.data_ptr(), b, ws.data_ptr(),
                      ws.numel(), stream)
 
-    def __call__(self):
+    def __call__(self, stream=None):
         st = self.fn(*self.args)
         if st != 0:
             raise RuntimeError("launch failed with status %d" % st)
@@ -120,14 +120,16 @@ class Launch:
 
 class LazyLaunch(Launch):
     """A Launch that picks up the current stream at call time (so it can be
-    captured into a graph on torch's capture stream)."""
+    captured into a graph on torch's capture stream), or takes the stream
+    handle from its caller (a timed loop looks it up once: the lookup costs
+    about as much host time as the library's launch itself)."""
 
     def __init__(self, q, fn, layer, x, y, b, ws):
         super().__init__(q, fn, layer, x, y, b, ws, None)
 
-    def __call__(self):
+    def __call__(self, stream=None):
         import torch
-        args = self.args[:-1] + (torch.cuda.current_stream().cuda_stream,)
+        args = self.args[:-1] + (stream if stream is not None else torch.cuda.current_stream().cuda_stream,)
         st = self.fn(*args)
         if st != 0:
             raise RuntimeError("launch failed with status %d" % st)
@@ -214,10 +216,10 @@ class GroupLaunch:
         self.keep = (list(layers), list(xs), list(ys), ws)
         self.ws, self.nbytes = ws.data_ptr(), ws.numel()
 
-    def __call__(self):
+    def __call__(self, stream=None):
         import torch
         st = self.fn(self.call.lp, self.call.count, self.call.xp, self.call.yp, self.ws, self.nbytes,
-                     torch.cuda.current_stream().cuda_stream)
+                     stream if stream is not None else torch.cuda.current_stream().cuda_stream)
         if st != 0:
             raise RuntimeError("qdec_gemv_group failed with status %d" % st)
 
@@ -232,15 +234,16 @@ def call_bytes(layers, b=1):
 def time_calls(torch, calls, reps=5, ncalls=200):
     """Median over reps of the event-timed average of ncalls back-to-back
     calls (rotating through `calls`), on the current stream, in us."""
+    s = torch.cuda.current_stream().cuda_stream
     for i in range(20):
-        calls[i % len(calls)]()
+        calls[i % len(calls)](s)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     out, j = [], 0
     for r in range(reps):
         e0.record()
         for i in range(ncalls):
-            calls[j % len(calls)]()
+            calls[j % len(calls)](s)
             j += 1
         e1.record()
         e1.synchronize()
@@ -308,12 +311,15 @@ def llama_stack(q, torch, dev, args):
                                             [ys["gate"], ys["up"]], ws_gu))
         calls["down"].append(LazyLaunch(q, "qdec_gemv", lay["down"][l], xt["down"], ys["down"], 1, ws_d))
 
-    def step():
+    def step(stream=None):
         for l in range(L):
-            calls["qkv"][l]()
-            calls["o"][l]()
-            calls["gate_up"][l]()
-            calls["down"][l]()
+            calls["qkv"][l](stream)
+            calls["o"][l](stream)
+            calls["gate_up"][l](stream)
+            calls["down"][l](stream)
+
+    def run_direct():
+        step(torch.cuda.current_stream().cuda_stream)
 
     if args.call:                            # counter collection: one call only
         for i in range(8):
@@ -348,9 +354,9 @@ def llama_stack(q, torch, dev, args):
     probe = {}
     if mode == "auto":
         probe["graph_ms_per_step"] = round(timed(run_graph, 2) * 1e3, 3)
-        probe["direct_ms_per_step"] = round(timed(step, 2) * 1e3, 3)
+        probe["direct_ms_per_step"] = round(timed(run_direct, 2) * 1e3, 3)
         mode = "graph" if probe["graph_ms_per_step"] <= probe["direct_ms_per_step"] else "direct"
-    run = run_graph if mode == "graph" else step
+    run = run_graph if mode == "graph" else run_direct
     for i in range(args.warmup):
         run()
     torch.cuda.synchronize()

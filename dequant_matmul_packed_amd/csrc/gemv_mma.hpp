@@ -601,6 +601,22 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma1_kernel(const uint32_
   gemv_mma_body<CODE, KV, PF, true>(0, lut_, x_, sgin_, n_, Q_, xs_off_, red_off_, scr_off_, cshift_, copies_, a);
 }
 
+// Two layers with one x (the same n and Q), both x' the whole row: both
+// tables, both sign vectors, x, the second layer's first workgroup and, in
+// three packed words, n and Q, the LDS carve-up (offsets in 16-byte units),
+// the table shift and the copies lead the arguments (14 preloaded SGPRs).
+template <int CODE, int KV, int PF>
+__global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma2_kernel(const uint32_t* lut0_, const uint32_t* lut1_,
+                                                                  const uint32_t* sg0_, const uint32_t* sg1_,
+                                                                  const uint16_t* x_, int w1_, uint32_t nq_,
+                                                                  uint32_t off0_, uint32_t off1_, MmaArgs a) {
+  const int li = (int)blockIdx.x >= w1_ ? 1 : 0;
+  gemv_mma_body<CODE, KV, PF, true>(li, li ? lut1_ : lut0_, x_, li ? sg1_ : sg0_, (int)(nq_ & 0xFFFFFFu),
+                                    (int)(nq_ >> 24), (int)((off0_ & 0xFFFFu) << 4), (int)((off0_ >> 16) << 4),
+                                    (int)((off1_ & 0xFFFFu) << 4), (int)((off1_ >> 16) & 0xFFu), (int)(off1_ >> 24),
+                                    a);
+}
+
 // PF = min(S, 8): the ring depth divides the steps of a unit (S is 2, 4 or a
 // multiple of 8: KR is 512, 1024 or a multiple of 2048).
 template <int CODE, int KV, int PF>
@@ -617,6 +633,24 @@ hipError_t launch_gemv_mma_p(const MmaArgs& a, unsigned grid, size_t lds, hipStr
       const MmaLayer& l0 = a.lay[0];
       hipLaunchKernelGGL((gemv_mma1_kernel<CODE, KV, PF>), dim3(grid), dim3(MMA_THREADS), lds, stream, l0.L.lut, l0.x,
                          l0.L.sign_in, (int)l0.L.n, l0.L.Q, a.xs_off, a.red_off, a.scr_off, a.cshift, a.copies, a);
+      return hipGetLastError();
+    }
+    const MmaLayer& l0 = a.lay[0];
+    const MmaLayer& l1 = a.lay[1];
+    const bool packs = ((a.xs_off | a.red_off | a.scr_off) & 15) == 0 && a.xs_off < (1 << 20) &&
+                       a.red_off < (1 << 20) && a.scr_off < (1 << 20) && a.cshift < 256 && a.copies < 256 &&
+                       l0.L.n < (1 << 24) && l0.L.Q < 256;
+    if (a.nl == 2 && packs && l0.xmode == 0 && l1.xmode == 0 && l0.x == l1.x && l0.L.n == l1.L.n &&
+        l0.L.Q == l1.L.Q) {
+      static LdsLimit have2;
+      const hipError_t e2 = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_mma2_kernel<CODE, KV, PF>), lds,
+                                               &have2);
+      if (e2 != hipSuccess) return e2;
+      const uint32_t nq = (uint32_t)l0.L.n | ((uint32_t)l0.L.Q << 24);
+      const uint32_t off0 = ((uint32_t)a.xs_off >> 4) | (((uint32_t)a.red_off >> 4) << 16);
+      const uint32_t off1 = ((uint32_t)a.scr_off >> 4) | ((uint32_t)a.cshift << 16) | ((uint32_t)a.copies << 24);
+      hipLaunchKernelGGL((gemv_mma2_kernel<CODE, KV, PF>), dim3(grid), dim3(MMA_THREADS), lds, stream, l0.L.lut,
+                         l1.L.lut, l0.L.sign_in, l1.L.sign_in, l0.x, l1.wg0, nq, off0, off1, a);
       return hipGetLastError();
     }
   }
