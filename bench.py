@@ -417,7 +417,7 @@ def main():
     torch.cuda.empty_cache()
     G = bench_gemm(q, torch, dev, stream)
     dom = H["dom"]
-    kernels = {"gate_up": "qdec_gemv_group over gate and up (gemv_mma_kernel + gemv_finish_lanes_kernel)",
+    kernels = {"gate_up": "qdec_gemv_group over gate and up (gemv_mma2_kernel + gemv_finish_lanes_kernel)",
                "qkv": "qdec_gemv_group over q, k, v (gemv_mma_kernel + gemv_finish_lanes_kernel)",
                "down": "qdec_gemv 4096x14336 (gemv_mma_kernel + gemv_finish_lanes1_kernel)",
                "o": "qdec_gemv 4096x4096 (gemv_mma1_kernel + gemv_finish_lanes1_kernel)"}
