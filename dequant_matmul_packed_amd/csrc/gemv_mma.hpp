@@ -120,8 +120,9 @@ __device__ __forceinline__ void mad1_pairs_centred(const uint32_t* w, uint32_t* 
 // issue before the layer's other fields have been read from memory.
 template <int CODE, int KV, int PF, bool X0>
 __device__ __forceinline__ void gemv_mma_body(int li, const uint32_t* lut_p, const uint16_t* x_p,
-                                              const uint32_t* sgin_p, int n_p, int Q_p, int xs_off_, int red_off_,
-                                              int scr_off_, int cshift_, int copies_, const MmaArgs& a) {
+                                              const uint32_t* sgin_p, int n_p, int Q_p, int xmode_p, int xb_p,
+                                              int NL_p, int xs_off_, int red_off_, int scr_off_, int cshift_,
+                                              int copies_, const MmaArgs& a) {
   using G = LaneGeom<CODE, KV>;
   constexpr int NW = G::NW;
   constexpr int CW = CODE == NUQ ? NW + 2 : NW;          // ring words per slot (+ NUQ scales)
@@ -171,7 +172,7 @@ __device__ __forceinline__ void gemv_mma_body(int li, const uint32_t* lut_p, con
       lw[k] = __builtin_amdgcn_raw_buffer_load_b32(lrs, vo, (uint32_t)((step_ * k) & (nlut_ - 1)) * 4u, 0);
   };
   if constexpr (X0) {
-    issue_x(x_p, sgin_p, n_p, 0, n_p);
+    issue_x(x_p, sgin_p, n_p, xb_p, NL_p);
     issue_lut(lut_p, Q_p);
   }
 
@@ -190,7 +191,7 @@ __device__ __forceinline__ void gemv_mma_body(int li, const uint32_t* lut_p, con
   const int nr = a.lay[li].nr, KR = a.lay[li].KR;
   const int bl = (int)blockIdx.x - a.lay[li].wg0, nwg = a.lay[li].nwg, units = a.lay[li].units;
 
-  const int xmode = X0 ? 0 : a.lay[li].xmode;
+  const int xmode = X0 ? xmode_p : a.lay[li].xmode;
   // the layer's fields in one round of scalar loads (the compiler would
   // otherwise issue some only where they are first used, after the first
   // round has returned); the launch's LDS carve-up and table geometry come
@@ -587,8 +588,8 @@ template <int CODE, int KV, int PF>
 __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma_kernel(QDEC_BOUNDS_PARAMS, int xs_off_, int red_off_,
                                                                  int scr_off_, int cshift_, int copies_, MmaArgs a) {
   (void)nl_;
-  gemv_mma_body<CODE, KV, PF, false>(QDEC_LAYER_OF((int)blockIdx.x), nullptr, nullptr, nullptr, 0, 0, xs_off_,
-                                     red_off_, scr_off_, cshift_, copies_, a);
+  gemv_mma_body<CODE, KV, PF, false>(QDEC_LAYER_OF((int)blockIdx.x), nullptr, nullptr, nullptr, 0, 0, 0, 0, 0,
+                                     xs_off_, red_off_, scr_off_, cshift_, copies_, a);
 }
 
 // One layer whose x' is the whole row: the first loads' pointers and sizes
@@ -598,7 +599,25 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma1_kernel(const uint32_
                                                                   const uint32_t* sgin_, int n_, int Q_, int xs_off_,
                                                                   int red_off_, int scr_off_, int cshift_,
                                                                   int copies_, MmaArgs a) {
-  gemv_mma_body<CODE, KV, PF, true>(0, lut_, x_, sgin_, n_, Q_, xs_off_, red_off_, scr_off_, cshift_, copies_, a);
+  gemv_mma_body<CODE, KV, PF, true>(0, lut_, x_, sgin_, n_, Q_, 0, 0, n_, xs_off_, red_off_, scr_off_, cshift_,
+                                    copies_, a);
+}
+
+// One layer with one K range per workgroup (x' of the range only): the
+// table, x and the input signs, then n with Q, the LDS carve-up (offsets in
+// 16-byte units) with the table shift and the copies, and the ranges (x'
+// mode, count, KR / 512), packed in four words (10 preloaded SGPRs).
+template <int CODE, int KV, int PF>
+__global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma1r_kernel(const uint32_t* lut_, const uint16_t* x_,
+                                                                   const uint32_t* sgin_, uint32_t nq_,
+                                                                   uint32_t off0_, uint32_t off1_, uint32_t rk_,
+                                                                   MmaArgs a) {
+  const int n = (int)(nq_ & 0xFFFFFFu), nr = (int)((rk_ >> 1) & 0x7FFFu), KR = (int)(rk_ >> 16) << 9;
+  const int xb = ((int)blockIdx.x % nr) * KR;   // one layer: range blockIdx mod nr
+  gemv_mma_body<CODE, KV, PF, true>(0, lut_, x_, sgin_, n, (int)(nq_ >> 24), 1, xb, KR,
+                                    (int)((off0_ & 0xFFFFu) << 4), (int)((off0_ >> 16) << 4),
+                                    (int)((off1_ & 0xFFFFu) << 4), (int)((off1_ >> 16) & 0xFFu), (int)(off1_ >> 24),
+                                    a);
 }
 
 // Two layers with one x (the same n and Q), both x' the whole row: both
@@ -612,7 +631,8 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma2_kernel(const uint32_
                                                                   uint32_t off0_, uint32_t off1_, MmaArgs a) {
   const int li = (int)blockIdx.x >= w1_ ? 1 : 0;
   gemv_mma_body<CODE, KV, PF, true>(li, li ? lut1_ : lut0_, x_, li ? sg1_ : sg0_, (int)(nq_ & 0xFFFFFFu),
-                                    (int)(nq_ >> 24), (int)((off0_ & 0xFFFFu) << 4), (int)((off0_ >> 16) << 4),
+                                    (int)(nq_ >> 24), 0, 0, (int)(nq_ & 0xFFFFFFu), (int)((off0_ & 0xFFFFu) << 4),
+                                    (int)((off0_ >> 16) << 4),
                                     (int)((off1_ & 0xFFFFu) << 4), (int)((off1_ >> 16) & 0xFFu), (int)(off1_ >> 24),
                                     a);
 }
@@ -640,15 +660,26 @@ hipError_t launch_gemv_mma_p(const MmaArgs& a, unsigned grid, size_t lds, hipStr
     const bool packs = ((a.xs_off | a.red_off | a.scr_off) & 15) == 0 && a.xs_off < (1 << 20) &&
                        a.red_off < (1 << 20) && a.scr_off < (1 << 20) && a.cshift < 256 && a.copies < 256 &&
                        l0.L.n < (1 << 24) && l0.L.Q < 256;
+    const uint32_t nq = (uint32_t)l0.L.n | ((uint32_t)l0.L.Q << 24);
+    const uint32_t off0 = ((uint32_t)a.xs_off >> 4) | (((uint32_t)a.red_off >> 4) << 16);
+    const uint32_t off1 = ((uint32_t)a.scr_off >> 4) | ((uint32_t)a.cshift << 16) | ((uint32_t)a.copies << 24);
+    if (a.nl == 1 && packs && l0.xmode == 1 && l0.nr >= 1 && l0.nr < (1 << 15) && l0.KR % 512 == 0 &&
+        (l0.KR >> 9) < (1 << 16)) {
+      static LdsLimit have1r;
+      const hipError_t e1 = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_mma1r_kernel<CODE, KV, PF>), lds,
+                                               &have1r);
+      if (e1 != hipSuccess) return e1;
+      const uint32_t rk = 1u | ((uint32_t)l0.nr << 1) | ((uint32_t)(l0.KR >> 9) << 16);
+      hipLaunchKernelGGL((gemv_mma1r_kernel<CODE, KV, PF>), dim3(grid), dim3(MMA_THREADS), lds, stream, l0.L.lut,
+                         l0.x, l0.L.sign_in, nq, off0, off1, rk, a);
+      return hipGetLastError();
+    }
     if (a.nl == 2 && packs && l0.xmode == 0 && l1.xmode == 0 && l0.x == l1.x && l0.L.n == l1.L.n &&
         l0.L.Q == l1.L.Q) {
       static LdsLimit have2;
       const hipError_t e2 = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_mma2_kernel<CODE, KV, PF>), lds,
                                                &have2);
       if (e2 != hipSuccess) return e2;
-      const uint32_t nq = (uint32_t)l0.L.n | ((uint32_t)l0.L.Q << 24);
-      const uint32_t off0 = ((uint32_t)a.xs_off >> 4) | (((uint32_t)a.red_off >> 4) << 16);
-      const uint32_t off1 = ((uint32_t)a.scr_off >> 4) | ((uint32_t)a.cshift << 16) | ((uint32_t)a.copies << 24);
       hipLaunchKernelGGL((gemv_mma2_kernel<CODE, KV, PF>), dim3(grid), dim3(MMA_THREADS), lds, stream, l0.L.lut,
                          l1.L.lut, l0.L.sign_in, l1.L.sign_in, l0.x, l1.wg0, nq, off0, off1, a);
       return hipGetLastError();
