@@ -788,6 +788,21 @@ __global__ __launch_bounds__(FIN_LANES_THREADS) void gemv_finish_lanes1_kernel(c
   finish_lanes((int)blockIdx.x, z, y, sg, m, Bo, nsl, ncol, sstride, mult);
 }
 
+// Two layers of one shape (gate and up): the slices and sign vectors of
+// both, the second layer's first workgroup, the shape (m and log2 B_out;
+// slices and columns) and the slice stride are preloaded (12 SGPRs); the
+// outputs and scales, needed only at the store, come from the struct.
+__global__ __launch_bounds__(FIN_LANES_THREADS) void gemv_finish_lanes2_kernel(const float* z0, const float* z1,
+                                                                               const uint32_t* sg0,
+                                                                               const uint32_t* sg1, int w1,
+                                                                               uint32_t shape0, uint32_t shape1,
+                                                                               int sstride, FinishArgs a) {
+  const int li = (int)blockIdx.x >= w1 ? 1 : 0;
+  finish_lanes((int)blockIdx.x - (li ? w1 : 0), li ? z1 : z0, a.lay[li].y, li ? sg1 : sg0,
+               (int)(shape0 & 0xFFFFFFu), 1 << (shape0 >> 24), (int)(shape1 & 0xFFFFu), (int)(shape1 >> 16), sstride,
+               a.lay[li].mult);
+}
+
 hipError_t launch_gemv_finish(const FinishArgs& a, hipStream_t stream) {
   // the lane finisher where every block is at most 32 panels
   bool lanes = a.nl > 0;
@@ -805,6 +820,16 @@ hipError_t launch_gemv_finish(const FinishArgs& a, hipStream_t stream) {
     if (b.nl == 1 && f.slice_stride <= INT32_MAX) {
       hipLaunchKernelGGL(gemv_finish_lanes1_kernel, dim3(grid), dim3(FIN_LANES_THREADS), 0, stream, f.z, f.y,
                          f.sign_out, (int)f.m, f.Bo, f.nslices, f.b, (int)f.slice_stride, f.mult);
+      return hipGetLastError();
+    }
+    const FinishLayer& g = b.lay[1];
+    if (b.nl == 2 && f.m == g.m && f.Bo == g.Bo && f.nslices == g.nslices && f.b == g.b &&
+        f.slice_stride == g.slice_stride && f.slice_stride <= INT32_MAX && f.m < (1 << 24) && f.Bo > 0 &&
+        (f.Bo & (f.Bo - 1)) == 0 && f.nslices < (1 << 16) && f.b < (1 << 16)) {
+      const uint32_t shape0 = (uint32_t)f.m | ((uint32_t)(31 - __builtin_clz((unsigned)f.Bo)) << 24);
+      const uint32_t shape1 = (uint32_t)f.nslices | ((uint32_t)f.b << 16);
+      hipLaunchKernelGGL(gemv_finish_lanes2_kernel, dim3(grid), dim3(FIN_LANES_THREADS), 0, stream, f.z, g.z,
+                         f.sign_out, g.sign_out, g.wg0, shape0, shape1, (int)f.slice_stride, b);
       return hipGetLastError();
     }
     hipLaunchKernelGGL(gemv_finish_lanes_kernel, dim3(grid), dim3(FIN_LANES_THREADS), 0, stream,
