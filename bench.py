@@ -418,7 +418,7 @@ def main():
     G = bench_gemm(q, torch, dev, stream)
     dom = H["dom"]
     kernels = {"gate_up": "qdec_gemv_group over gate and up (gemv_mma2_kernel + gemv_finish_lanes_kernel)",
-               "qkv": "qdec_gemv_group over q, k, v (gemv_mma_kernel + gemv_finish_lanes_kernel)",
+               "qkv": "qdec_gemv_group over q, k, v (gemv_mma3_kernel + gemv_finish_lanes_kernel)",
                "down": "qdec_gemv 4096x14336 (gemv_mma1r_kernel + gemv_finish_lanes1_kernel)",
                "o": "qdec_gemv 4096x4096 (gemv_mma1_kernel + gemv_finish_lanes1_kernel)"}
     traffic = measured_traffic(H["dominant"], dom["algorithmic_bytes"])

@@ -637,6 +637,27 @@ __global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma2_kernel(const uint32_
                                     a);
 }
 
+// Three layers with one x (q, k, v: the same n and Q), x' the whole row:
+// layer 0's table and sign vector, x, the byte offsets of layers 1 and 2's
+// tables and sign vectors from layer 0's, both layer boundaries (16 bits
+// each) and the three packed words of gemv_mma2_kernel (14 preloaded SGPRs).
+template <int CODE, int KV, int PF>
+__global__ __launch_bounds__(MMA_THREADS, 1) void gemv_mma3_kernel(const uint32_t* lut0_, const uint32_t* sg0_,
+                                                                  const uint16_t* x_, int dl1_, int dl2_, int ds1_,
+                                                                  int ds2_, uint32_t w12_, uint32_t nq_,
+                                                                  uint32_t off0_, uint32_t off1_, MmaArgs a) {
+  const int bid = (int)blockIdx.x;
+  const int li = (int)(bid >= (int)(w12_ & 0xFFFFu)) + (int)(bid >= (int)(w12_ >> 16));
+  const int64_t dl = li == 0 ? 0 : li == 1 ? dl1_ : dl2_;
+  const int64_t ds = li == 0 ? 0 : li == 1 ? ds1_ : ds2_;
+  const uint32_t* lut = reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lut0_) + dl);
+  const uint32_t* sg = sg0_ ? reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(sg0_) + ds) : nullptr;
+  gemv_mma_body<CODE, KV, PF, true>(li, lut, x_, sg, (int)(nq_ & 0xFFFFFFu), (int)(nq_ >> 24), 0, 0,
+                                    (int)(nq_ & 0xFFFFFFu), (int)((off0_ & 0xFFFFu) << 4), (int)((off0_ >> 16) << 4),
+                                    (int)((off1_ & 0xFFFFu) << 4), (int)((off1_ >> 16) & 0xFFu), (int)(off1_ >> 24),
+                                    a);
+}
+
 // PF = min(S, 8): the ring depth divides the steps of a unit (S is 2, 4 or a
 // multiple of 8: KR is 512, 1024 or a multiple of 2048).
 template <int CODE, int KV, int PF>
@@ -673,6 +694,30 @@ hipError_t launch_gemv_mma_p(const MmaArgs& a, unsigned grid, size_t lds, hipStr
       hipLaunchKernelGGL((gemv_mma1r_kernel<CODE, KV, PF>), dim3(grid), dim3(MMA_THREADS), lds, stream, l0.L.lut,
                          l0.x, l0.L.sign_in, nq, off0, off1, rk, a);
       return hipGetLastError();
+    }
+    if (a.nl == 3 && packs) {
+      const MmaLayer& l2 = a.lay[2];
+      auto delta = [](const void* p, const void* q, int64_t* d) {
+        *d = (int64_t)((intptr_t)p - (intptr_t)q);
+        return *d >= INT32_MIN && *d <= INT32_MAX;
+      };
+      int64_t dl1, dl2, ds1 = 0, ds2 = 0;
+      const bool signs = l0.L.sign_in && l1.L.sign_in && l2.L.sign_in;
+      const bool nosigns = !l0.L.sign_in && !l1.L.sign_in && !l2.L.sign_in;
+      if (l0.xmode == 0 && l1.xmode == 0 && l2.xmode == 0 && l0.x == l1.x && l0.x == l2.x &&
+          l0.L.n == l1.L.n && l0.L.n == l2.L.n && l0.L.Q == l1.L.Q && l0.L.Q == l2.L.Q && l1.wg0 < (1 << 16) &&
+          l2.wg0 < (1 << 16) && (signs || nosigns) && delta(l1.L.lut, l0.L.lut, &dl1) &&
+          delta(l2.L.lut, l0.L.lut, &dl2) &&
+          (nosigns || (delta(l1.L.sign_in, l0.L.sign_in, &ds1) && delta(l2.L.sign_in, l0.L.sign_in, &ds2)))) {
+        static LdsLimit have3;
+        const hipError_t e3 = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemv_mma3_kernel<CODE, KV, PF>), lds,
+                                                 &have3);
+        if (e3 != hipSuccess) return e3;
+        const uint32_t w12 = (uint32_t)l1.wg0 | ((uint32_t)l2.wg0 << 16);
+        hipLaunchKernelGGL((gemv_mma3_kernel<CODE, KV, PF>), dim3(grid), dim3(MMA_THREADS), lds, stream, l0.L.lut,
+                           l0.L.sign_in, l0.x, (int)dl1, (int)dl2, (int)ds1, (int)ds2, w12, nq, off0, off1, a);
+        return hipGetLastError();
+      }
     }
     if (a.nl == 2 && packs && l0.xmode == 0 && l1.xmode == 0 && l0.x == l1.x && l0.L.n == l1.L.n &&
         l0.L.Q == l1.L.Q) {

@@ -14,8 +14,8 @@ ARGS is the bench's argument string (it goes into the summary's command
 line): `--steps 20 --warmup 5 --no-cpu-baseline` for the bench, or
 `--layer CODE:M:N:K:B` for one layer.  With WEIGHTS (the layer's m x n) the
 table gives VALU and LDS lane-instructions per weight for the layer's
-decode kernel (the gemv_kernel, gemv_mma_kernel, gemv_mma1_kernel, gemv_mma1r_kernel, gemv_mma2_kernel
-or gemm_kernel dispatches).
+decode kernel (the gemv_kernel, gemv_mma_kernel, gemv_mma1_kernel, gemv_mma1r_kernel, gemv_mma2_kernel,
+gemv_mma3_kernel or gemm_kernel dispatches).
 Rows are kept apart by kernel, grid and LDS size; every qdec kernel gets a
 row.
 
@@ -30,7 +30,7 @@ import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 DECODE = ("qdec::gemv_kernel<", "qdec::gemv_mma_kernel<", "qdec::gemv_mma1_kernel<", "qdec::gemv_mma1r_kernel<",
-          "qdec::gemv_mma2_kernel<", "qdec::gemm_kernel<")
+          "qdec::gemv_mma2_kernel<", "qdec::gemv_mma3_kernel<", "qdec::gemm_kernel<")
 
 
 def load(db):
